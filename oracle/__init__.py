@@ -1,0 +1,184 @@
+"""SAS decode-path oracle -- test infrastructure, not product code.
+
+Python face of ``sas_oracle.c``: a plain, slow, fp64 CPU implementation of the
+three SAS stages (key-block pooling -> gate scores + per-KV-head Top-K ->
+attention over the selected 64-token blocks, written as dense softmax
+attention over an explicit token mask).  The passages each step follows are
+cited in the C source.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP path:
+its inputs are plain numpy arrays (bf16 values travel as their uint16 bit
+patterns) and it never calls into the GPU library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sas_oracle.c")
+_LIB = os.path.join(_HERE, "_sas_oracle.so")
+
+BLOCK = 64
+HEAD_DIM = 128
+GATE_DIM = 128
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (OpenMP, IEEE arithmetic, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("page_stride", ctypes.c_int64), ("tok_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64)]
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(build())
+        _lib.sas_oracle_round_bf16.restype = ctypes.c_uint16
+        _lib.sas_oracle_round_bf16.argtypes = [ctypes.c_double]
+        _lib.sas_oracle_select.restype = ctypes.c_int32
+        _lib.sas_oracle_num_threads.restype = ctypes.c_int
+    return _lib
+
+
+def _p(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _shape(batch, n_q_heads, n_kv_heads, max_blocks, strides):
+    ps, ts, hs = strides
+    return _Shape(batch, n_q_heads, n_kv_heads, max_blocks, ps, ts, hs)
+
+
+def num_threads() -> int:
+    return int(_load().sas_oracle_num_threads())
+
+
+def round_bf16(x: float) -> int:
+    """fp64 -> bf16 bit pattern, round to nearest even in one step."""
+    return int(_load().sas_oracle_round_bf16(float(x)))
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns (uint16) as fp64."""
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def rms_norm(v: np.ndarray, w: np.ndarray) -> np.ndarray:
+    out = np.ascontiguousarray(v, dtype=np.float64).copy()
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    _load().sas_oracle_rms_norm(_p(out), _p(w))
+    return out
+
+
+def rope(v: np.ndarray, pos: float, theta: float) -> np.ndarray:
+    out = np.ascontiguousarray(v, dtype=np.float64).copy()
+    _load().sas_oracle_rope(_p(out), ctypes.c_double(pos), ctypes.c_double(theta))
+    return out
+
+
+def pool_stats(k_pool, block_table, strides, max_blocks, n_kv_heads, s, c, kvh) -> np.ndarray:
+    sh = _shape(block_table.shape[0], n_kv_heads, n_kv_heads, max_blocks, strides)
+    out = np.zeros(3 * HEAD_DIM, np.float64)
+    _load().sas_oracle_pool_stats(ctypes.byref(sh), _p(k_pool), _p(block_table), s, c, kvh, _p(out))
+    return out
+
+
+def pool_blocks(k_pool, block_table, strides, n_kv_heads, pool_seq, pool_blk, w_k, w_knorm,
+                theta, gate_keys, want_f64=False):
+    """Fill gate_keys (uint16 [P][Hkv][128], modified in place) for the listed
+    (sequence, block) pairs.  Returns the fp64 keys before rounding
+    ([n][Hkv][128]) when want_f64."""
+    B, max_blocks = block_table.shape
+    sh = _shape(B, n_kv_heads, n_kv_heads, max_blocks, strides)
+    pool_seq = np.ascontiguousarray(pool_seq, np.int32)
+    pool_blk = np.ascontiguousarray(pool_blk, np.int32)
+    n = len(pool_seq)
+    f64 = np.zeros((n, n_kv_heads, GATE_DIM), np.float64) if want_f64 else None
+    _load().sas_oracle_pool_blocks(ctypes.byref(sh), _p(k_pool), _p(block_table), _p(pool_seq),
+                                   _p(pool_blk), ctypes.c_int32(n), _p(w_k), _p(w_knorm),
+                                   ctypes.c_double(theta), _p(gate_keys), _p(f64))
+    return f64
+
+
+def gate_query(q, w_q, w_qnorm, theta, seq_len, s, h) -> np.ndarray:
+    out = np.zeros(GATE_DIM, np.float64)
+    _load().sas_oracle_gate_query(_p(q), ctypes.c_int(q.shape[1]), ctypes.c_int(s), ctypes.c_int(h),
+                                  _p(w_q), _p(w_qnorm), ctypes.c_double(theta),
+                                  ctypes.c_int32(seq_len), _p(out))
+    return out
+
+
+def gate_topk(q, w_q, w_qnorm, gate_keys, block_table, seq_lens, theta, budget_tokens,
+              n_kv_heads):
+    """Gate stage for the batch.  Returns (sel, gates, cnt, scores):
+    sel int32 [B][Hkv][budget/64] (ascending, local block last, -1 padded),
+    gates f32 (same shape; sigmoid(score), 1 for the local block, 0 padding),
+    cnt int32 [B][Hkv], scores f32 [B][Hkv][max_blocks] (-inf for c >= l)."""
+    B, Hq, _ = q.shape
+    max_blocks = block_table.shape[1]
+    sh = _shape(B, Hq, n_kv_heads, max_blocks, (0, 0, 0))
+    n_sel = budget_tokens // BLOCK
+    sel = np.zeros((B, n_kv_heads, n_sel), np.int32)
+    gates = np.zeros((B, n_kv_heads, n_sel), np.float32)
+    cnt = np.zeros((B, n_kv_heads), np.int32)
+    scores = np.zeros((B, n_kv_heads, max_blocks), np.float32)
+    _load().sas_oracle_gate_topk(ctypes.byref(sh), _p(q), _p(w_q), _p(w_qnorm), _p(gate_keys),
+                                 _p(block_table), _p(np.ascontiguousarray(seq_lens, np.int32)),
+                                 ctypes.c_double(theta), ctypes.c_int32(budget_tokens), _p(sel),
+                                 _p(gates), _p(cnt), _p(scores))
+    return sel, gates, cnt, scores
+
+
+def select(scores: np.ndarray, seq_len: int, budget_tokens: int):
+    """Top-K of one (sequence, KV head) from its fp32 block scores."""
+    n_sel = budget_tokens // BLOCK
+    sel = np.zeros(n_sel, np.int32)
+    gates = np.zeros(n_sel, np.float32)
+    sc = np.ascontiguousarray(scores, np.float32)
+    cnt = _load().sas_oracle_select(_p(sc), ctypes.c_int32(seq_len), ctypes.c_int32(budget_tokens),
+                                    _p(sel), _p(gates))
+    return sel, gates, int(cnt)
+
+
+def attend(q, k_pool, v_pool, block_table, strides, n_kv_heads, seq_lens, sel, gates, cnt,
+           sm_scale, pairs=None):
+    """Dense masked softmax attention.  gates=None is plain Top-K mode.
+    pairs: optional int32 [n][2] list of (sequence, query head); default all.
+    Returns fp64 [n][128] (or [B][Hq][128] when pairs is None)."""
+    B, Hq, _ = q.shape
+    max_blocks = block_table.shape[1]
+    sh = _shape(B, Hq, n_kv_heads, max_blocks, strides)
+    n_sel = sel.shape[-1]
+    if pairs is not None:
+        pairs = np.ascontiguousarray(pairs, np.int32).reshape(-1, 2)
+        n = pairs.shape[0]
+    else:
+        n = B * Hq
+    out = np.zeros((n, HEAD_DIM), np.float64)
+    g = None if gates is None else np.ascontiguousarray(gates, np.float32)
+    _load().sas_oracle_attend(ctypes.byref(sh), _p(q), _p(k_pool), _p(v_pool), _p(block_table),
+                              _p(np.ascontiguousarray(seq_lens, np.int32)),
+                              _p(np.ascontiguousarray(sel, np.int32)), _p(g),
+                              _p(np.ascontiguousarray(cnt, np.int32)), ctypes.c_int32(n_sel),
+                              ctypes.c_double(sm_scale), _p(pairs), ctypes.c_int64(n), _p(out))
+    return out if pairs is not None else out.reshape(B, Hq, HEAD_DIM)

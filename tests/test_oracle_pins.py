@@ -1,0 +1,415 @@
+"""Pins of the oracle to things other than itself (CPU only).
+
+Each test checks an oracle function against a library routine, a closed form,
+an invariant, brute force on a tiny input, or a number the SAS pages print.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import oracle
+from harness import SM_SCALE, Host, complete_blocks, oracle_gate_keys, oracle_step
+from learned_block_sparse_tok_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def small_paged(seed=11, lens=(300, 64, 1, 200), Hq=8, Hkv=2, budget=256, random_norms=True):
+    return wl.make(len(lens), Hq, Hkv, list(lens), budget, "paged", seed, "cpu",
+                   max_blocks=8, random_norms=random_norms, extra_pages=5)
+
+
+def small_contig(seed=12, lens=(700, 129), Hq=6, Hkv=2, budget=256):
+    return wl.make(len(lens), Hq, Hkv, list(lens), budget, "contiguous", seed, "cpu",
+                   random_norms=True)
+
+
+def dense_kv(h: Host, pool: np.ndarray, s: int, kvh: int) -> np.ndarray:
+    """Gather sequence s's first L keys/values of one KV head into [L][128] fp64."""
+    w = h.w
+    L = int(h.lens[s])
+    ps, ts, hs = w.strides
+    flat = pool.reshape(-1)
+    tok = np.arange(L)
+    base = h.bt[s, tok // wl.BLOCK].astype(np.int64) * ps + kvh * hs + (tok % wl.BLOCK) * ts
+    idx = base[:, None] + np.arange(wl.HEAD_DIM)[None, :]
+    return oracle.bf16_to_f64(flat[idx])
+
+
+# ---------------------------------------------------------------- bf16 rounding
+def test_round_bf16_ties_and_specials():
+    cases = [(1.0, 0x3F80), (1.0 + 2 ** -8, 0x3F80), (1.0 + 3 * 2 ** -8, 0x3F82), (-2.5, 0xC020),
+             (1.0 + 2 ** -8 + 2 ** -30, 0x3F81), (0.0, 0x0000), (-0.0, 0x8000),
+             (float("inf"), 0x7F80), (float("-inf"), 0xFF80), (3.4e38, 0x7F80),
+             (2.0 ** -133, 0x0001), (2.0 ** -134, 0x0000), (3 * 2.0 ** -134, 0x0002)]
+    for x, bits in cases:
+        assert oracle.round_bf16(x) == bits, (x, hex(oracle.round_bf16(x)), hex(bits))
+
+
+def test_round_bf16_matches_torch_on_fp32_values():
+    # fp32 inputs are exact in fp64, so both roundings are single roundings.
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32),
+                        (rng.standard_normal(2000) * 1e-39).astype(np.float32),
+                        (rng.standard_normal(2000) * 1e37).astype(np.float32)])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.round_bf16(float(v)) for v in x], np.uint16)
+    np.testing.assert_array_equal(got, want)
+
+
+# ---------------------------------------------------------------- norm / rope
+def test_rms_norm_matches_torch():
+    rng = np.random.default_rng(1)
+    for scale in (1e-4, 1.0, 37.0):
+        v = rng.standard_normal(128) * scale
+        w = (1 + 0.1 * rng.standard_normal(128)).astype(np.float32)
+        want = F.rms_norm(torch.from_numpy(v), (128,), torch.from_numpy(w.astype(np.float64)), eps=1e-6)
+        np.testing.assert_allclose(oracle.rms_norm(v, w), want.numpy(), rtol=1e-13, atol=1e-15)
+
+
+def test_rope_is_complex_rotation():
+    rng = np.random.default_rng(2)
+    theta = 1e6
+    for pos in (0.0, 1.0, 63.0, 4095.0, 32767.0, 131071.0):
+        v = rng.standard_normal(128)
+        z = (v[:64] + 1j * v[64:]) * np.exp(1j * pos * theta ** (-np.arange(64) / 64.0))
+        # the angle pos * freq carries fp64 rounding of relative size 1e-16
+        np.testing.assert_allclose(oracle.rope(v, pos, theta), np.concatenate([z.real, z.imag]),
+                                   rtol=1e-12, atol=1e-14 * (1.0 + pos))
+
+
+def test_rope_properties():
+    rng = np.random.default_rng(3)
+    x, y = rng.standard_normal(128), rng.standard_normal(128)
+    np.testing.assert_array_equal(oracle.rope(x, 0.0, 1e6), x)  # position 0 = identity
+    np.testing.assert_allclose(np.linalg.norm(oracle.rope(x, 777.0, 1e6)), np.linalg.norm(x), rtol=1e-14)
+    for a, b, m in ((100.0, 64.0, 4096.0), (32767.0, 0.0, 640.0)):
+        lhs = oracle.rope(x, a, 1e6) @ oracle.rope(y, b, 1e6)
+        rhs = oracle.rope(x, a + m, 1e6) @ oracle.rope(y, b + m, 1e6)
+        assert abs(lhs - rhs) < 1e-9 * (1 + abs(lhs))
+
+
+# ---------------------------------------------------------------- pooling
+def test_pool_stats_direct_scan():
+    w = small_paged()
+    h = Host(w)
+    for s, c in zip(*complete_blocks(h.lens)):
+        for kvh in range(w.n_kv_heads):
+            blk = dense_kv(h, h.k, s, kvh)[c * 64:(c + 1) * 64]
+            got = oracle.pool_stats(h.k, h.bt, w.strides, w.max_blocks, w.n_kv_heads, int(s), int(c), kvh)
+            np.testing.assert_array_equal(got[:128], blk.max(axis=0))
+            np.testing.assert_array_equal(got[128:256], blk.min(axis=0))
+            # a sum of 64 bf16 values is exact in fp64, so the mean is exact
+            np.testing.assert_array_equal(got[256:], blk.sum(axis=0) / 64.0)
+
+
+def _torch_gate_key(blk, w_k, wkn, c, theta):
+    p = torch.cat([blk.max(0).values, blk.min(0).values, blk.mean(0)])
+    u = p @ w_k
+    u = F.rms_norm(u, (128,), wkn, eps=1e-6)
+    z = torch.complex(u[:64], u[64:]) * torch.exp(1j * (c * 64.0) * theta ** (-torch.arange(64, dtype=torch.float64) / 64))
+    return torch.cat([z.real, z.imag])
+
+
+@pytest.mark.parametrize("maker", [small_paged, small_contig])
+def test_gate_key_pipeline_matches_torch(maker):
+    w = maker()
+    h = Host(w)
+    gk, f64, seq, blk = oracle_gate_keys(h, want_f64=True)
+    w_k = torch.from_numpy(oracle.bf16_to_f64(h.w_k))
+    wkn = torch.from_numpy(h.wkn.astype(np.float64))
+    for i, (s, c) in enumerate(zip(seq, blk)):
+        for kvh in range(w.n_kv_heads):
+            kb = torch.from_numpy(dense_kv(h, h.k, s, kvh)[c * 64:(c + 1) * 64])
+            want = _torch_gate_key(kb, w_k[kvh], wkn, int(c), w.theta)
+            np.testing.assert_allclose(f64[i, kvh], want.numpy(), rtol=1e-11, atol=1e-11)
+            page = h.bt[s, c]
+            bits = gk[page, kvh]
+            # stored key = the fp64 key rounded to bf16: within half a bf16 ulp
+            val = oracle.bf16_to_f64(bits)
+            ulp = 2.0 ** (np.floor(np.log2(np.abs(want.numpy()) + 1e-300)) - 7)
+            assert np.all(np.abs(val - want.numpy()) <= 0.5 * ulp + 1e-300)
+
+
+# ---------------------------------------------------------------- gate query / scores
+def test_gate_query_matches_torch():
+    w = small_contig()
+    h = Host(w)
+    w_q = torch.from_numpy(oracle.bf16_to_f64(h.w_q))
+    q = torch.from_numpy(oracle.bf16_to_f64(h.q))
+    wqn = torch.from_numpy(h.wqn.astype(np.float64))
+    for s in range(w.batch):
+        pos = float(h.lens[s] - 1)
+        for hh in range(w.n_q_heads):
+            v = F.rms_norm(q[s, hh] @ w_q[hh], (128,), wqn, eps=1e-6)
+            z = torch.complex(v[:64], v[64:]) * torch.exp(1j * pos * w.theta ** (-torch.arange(64, dtype=torch.float64) / 64))
+            want = torch.cat([z.real, z.imag]).numpy()
+            got = oracle.gate_query(h.q, h.w_q, h.wqn, w.theta, int(h.lens[s]), s, hh)
+            np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-12)
+
+
+def test_scores_equal_dot_of_mean_gate_query():
+    # mean over the group of per-head scores == score of the mean gate query
+    w = small_paged()
+    h = Host(w)
+    gk = oracle_gate_keys(h)
+    sel, gates, cnt, scores = oracle.gate_topk(h.q, h.w_q, h.wqn, gk, h.bt, h.lens, w.theta, w.budget, w.n_kv_heads)
+    G = w.group
+    for s in range(w.batch):
+        local = (int(h.lens[s]) - 1) // 64
+        for kvh in range(w.n_kv_heads):
+            gm = np.mean([oracle.gate_query(h.q, h.w_q, h.wqn, w.theta, int(h.lens[s]), s, kvh * G + g)
+                          for g in range(G)], axis=0)
+            keys = oracle.bf16_to_f64(gk[h.bt[s, :local], kvh])
+            want = (keys @ gm / math.sqrt(128)).astype(np.float32)
+            np.testing.assert_allclose(scores[s, kvh, :local], want, rtol=1e-6, atol=1e-7)
+            assert np.all(np.isneginf(scores[s, kvh, local:]))
+
+
+# ---------------------------------------------------------------- selection
+def _brute_topk(scores, k):
+    """Max-sum subset of size k; equal sums broken by the lexicographically
+    smallest sorted index tuple.  NaN counts as -inf."""
+    s = np.where(np.isnan(scores), -np.inf, scores.astype(np.float64))
+    best, best_sum = None, None
+    for comb in itertools.combinations(range(len(s)), k):
+        tot = sum(s[list(comb)]) if k else 0.0
+        if best is None or tot > best_sum:
+            best, best_sum = comb, tot
+    return list(best)
+
+
+def test_select_brute_force_tiny():
+    rng = np.random.default_rng(4)
+    for trial in range(300):
+        local = int(rng.integers(0, 12))
+        budget = 64 * int(rng.integers(1, 6))
+        kind = trial % 3
+        if kind == 0:
+            sc = rng.standard_normal(local).astype(np.float32)
+        elif kind == 1:  # many exact ties
+            sc = rng.integers(-2, 3, size=local).astype(np.float32)
+        else:  # signed zeros and a NaN
+            sc = rng.choice(np.array([0.0, -0.0, 1.0, -1.0, np.nan], np.float32), size=local)
+        if np.isnan(sc).any() and kind == 2:
+            # -inf sums make max-sum ambiguous; keep NaNs out of the chosen set
+            k_eff = min(budget // 64 - 1, local)
+            if np.count_nonzero(~np.isnan(sc)) < k_eff:
+                continue
+        L = local * 64 + int(rng.integers(1, 65))
+        sel, gates, cnt = oracle.select(sc, L, budget)
+        k_eff = min(budget // 64 - 1, local)
+        assert cnt == k_eff + 1
+        want = sorted(_brute_topk(sc, k_eff)) + [local]
+        assert list(sel[:cnt]) == want, (sc, sel, want)
+        assert np.all(sel[cnt:] == -1)
+
+
+def test_select_matches_lexsort():
+    rng = np.random.default_rng(5)
+    for local, budget in ((511, 2048), (2047, 2048), (1023, 4096), (511, 1024), (20, 4096)):
+        sc = rng.standard_normal(local).astype(np.float32)
+        sc[rng.integers(0, local, 40)] = sc[rng.integers(0, local, 40)]  # duplicates
+        sc[rng.integers(0, local, 5)] = -0.0
+        sc[rng.integers(0, local, 5)] = 0.0
+        L = local * 64 + 7
+        sel, gates, cnt = oracle.select(sc, L, budget)
+        k = min(budget // 64 - 1, local)
+        order = np.lexsort((np.arange(local), -sc.astype(np.float64)))
+        want = np.sort(order[:k])
+        np.testing.assert_array_equal(sel[:k], want)
+        assert sel[k] == local and cnt == k + 1
+        np.testing.assert_allclose(gates[:k], scipy.special.expit(sc[want].astype(np.float64)).astype(np.float32),
+                                   rtol=2e-7)
+        assert gates[k] == 1.0 and np.all(gates[k + 1:] == 0) and np.all(sel[k + 1:] == -1)
+
+
+@pytest.mark.parametrize("budget", [1024, 2048, 4096])
+def test_budget_block_counts(budget):
+    # a budget of B tokens selects exactly B/64 blocks once the context holds them
+    rng = np.random.default_rng(6)
+    for local in (0, 1, 5, budget // 64 - 2, budget // 64 - 1, budget // 64, 511, 2047):
+        sc = rng.standard_normal(max(local, 1)).astype(np.float32)[:local]
+        sel, gates, cnt = oracle.select(sc, local * 64 + 1, budget)
+        assert cnt == (budget // 64 if local >= budget // 64 - 1 else local + 1)
+        assert np.all(np.diff(sel[:cnt]) > 0) and sel[cnt - 1] == local
+        assert np.all(sel[:cnt - 1] < local) and np.all(sel[cnt:] == -1)
+
+
+# ---------------------------------------------------------------- attention
+def _sdpa_reference(h: Host, sel, gates, cnt):
+    """torch scaled-dot-product attention (fp64) with a boolean token mask;
+    gated mode scales each value row by its block's gate."""
+    w = h.w
+    G = w.group
+    out = np.zeros((w.batch, w.n_q_heads, 128))
+    for s in range(w.batch):
+        L = int(h.lens[s])
+        for kvh in range(w.n_kv_heads):
+            K = torch.from_numpy(dense_kv(h, h.k, s, kvh))
+            V = torch.from_numpy(dense_kv(h, h.v, s, kvh))
+            blocks = sel[s, kvh, :cnt[s, kvh]]
+            mask = torch.from_numpy(np.isin(np.arange(L) // 64, blocks))
+            if gates is not None:
+                gmap = dict(zip(blocks.tolist(), gates[s, kvh, :cnt[s, kvh]].tolist()))
+                gt = torch.tensor([gmap.get(j // 64, 0.0) for j in range(L)], dtype=torch.float64)
+                V = V * gt[:, None]
+            qh = torch.from_numpy(oracle.bf16_to_f64(h.q[s, kvh * G:(kvh + 1) * G]))
+            o = F.scaled_dot_product_attention(qh[None, :, None, :], K[None, None].expand(1, G, L, 128),
+                                               V[None, None].expand(1, G, L, 128),
+                                               attn_mask=mask[None, None, None, :], scale=SM_SCALE)
+            out[s, kvh * G:(kvh + 1) * G] = o[0, :, 0].numpy()
+    return out
+
+
+@pytest.mark.parametrize("maker", [small_paged, small_contig])
+@pytest.mark.parametrize("gated", [False, True])
+def test_attention_matches_sdpa(maker, gated):
+    w = maker()
+    h = Host(w)
+    sel, gates, cnt = wl.random_selection(h.lens, w.n_kv_heads, w.budget, seed=7)
+    got = oracle.attend(h.q, h.k, h.v, h.bt, w.strides, w.n_kv_heads, h.lens, sel,
+                        gates if gated else None, cnt, SM_SCALE)
+    want = _sdpa_reference(h, sel, gates if gated else None, cnt)
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+
+
+def test_attention_pairs_subset():
+    w = small_paged()
+    h = Host(w)
+    sel, gates, cnt = wl.random_selection(h.lens, w.n_kv_heads, w.budget, seed=8)
+    full = oracle.attend(h.q, h.k, h.v, h.bt, w.strides, w.n_kv_heads, h.lens, sel, gates, cnt, SM_SCALE)
+    pairs = np.array([[3, 7], [0, 0], [1, 5]], np.int32)
+    part = oracle.attend(h.q, h.k, h.v, h.bt, w.strides, w.n_kv_heads, h.lens, sel, gates, cnt, SM_SCALE,
+                         pairs=pairs)
+    for i, (s, hh) in enumerate(pairs):
+        np.testing.assert_array_equal(part[i], full[s, hh])
+
+
+def test_dense_equivalence_when_budget_covers_context():
+    # budget >= context: every block is selected and the output is plain dense attention
+    w = wl.named("tiny", budget=4096)
+    h = Host(w)
+    res = oracle_step(h, gated=False)
+    assert res["cnt"][0, 0] == 64
+    K = torch.from_numpy(dense_kv(h, h.k, 0, 0))
+    V = torch.from_numpy(dense_kv(h, h.v, 0, 0))
+    q = torch.from_numpy(oracle.bf16_to_f64(h.q[0]))
+    want = F.scaled_dot_product_attention(q[:, None, :], K[None].expand(4, -1, -1), V[None].expand(4, -1, -1),
+                                          scale=SM_SCALE)[:, 0]
+    np.testing.assert_allclose(res["out"][0], want.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_softmax_closed_forms():
+    # one cached token: the output is that token's value row
+    w = wl.make(2, 4, 2, [1, 1], 1024, "paged", 21, "cpu", max_blocks=2)
+    h = Host(w)
+    sel, gates, cnt = wl.random_selection(h.lens, 2, 1024, seed=1)
+    out = oracle.attend(h.q, h.k, h.v, h.bt, w.strides, 2, h.lens, sel, None, cnt, SM_SCALE)
+    for s in range(2):
+        for hh in range(4):
+            np.testing.assert_array_equal(out[s, hh], dense_kv(h, h.v, s, hh // 2)[0])
+    # zero query: equal logits, the output is the mean of the selected rows
+    w = small_paged()
+    w.q.zero_()
+    h = Host(w)
+    sel, gates, cnt = wl.random_selection(h.lens, w.n_kv_heads, w.budget, seed=2)
+    out = oracle.attend(h.q, h.k, h.v, h.bt, w.strides, w.n_kv_heads, h.lens, sel, None, cnt, SM_SCALE)
+    for s in range(w.batch):
+        L = int(h.lens[s])
+        for hh in range(w.n_q_heads):
+            kvh = hh // w.group
+            V = dense_kv(h, h.v, s, kvh)
+            keep = np.isin(np.arange(L) // 64, sel[s, kvh, :cnt[s, kvh]])
+            np.testing.assert_allclose(out[s, hh], V[keep].mean(axis=0), rtol=1e-12, atol=1e-13)
+
+
+def test_gated_mode_is_linear_in_a_common_gate():
+    w = small_paged()
+    h = Host(w)
+    sel, gates, cnt = wl.random_selection(h.lens, w.n_kv_heads, w.budget, seed=3)
+    plain = oracle.attend(h.q, h.k, h.v, h.bt, w.strides, w.n_kv_heads, h.lens, sel, None, cnt, SM_SCALE)
+    for gamma in (0.25, 0.7):
+        g = np.where(sel >= 0, np.float32(gamma), np.float32(0)).astype(np.float32)
+        gated = oracle.attend(h.q, h.k, h.v, h.bt, w.strides, w.n_kv_heads, h.lens, sel, g, cnt, SM_SCALE)
+        np.testing.assert_allclose(gated, gamma * plain, rtol=1e-7, atol=1e-12)
+
+
+# ---------------------------------------------------------------- whole-step invariants
+def test_norm_placement_scale_invariance():
+    # RMSNorm right after each projection: scaling a projection leaves keys and ranking unchanged
+    w = small_paged(random_norms=True)
+    h = Host(w)
+    ref = oracle_step(h, gated=True)
+    _, f64_ref, _, _ = oracle_gate_keys(h, want_f64=True)
+    h.w_k = wl.host((w.w_k.float() * 4).to(torch.bfloat16))  # power of two: exact in bf16
+    h.w_q = wl.host((w.w_q.float() * 0.5).to(torch.bfloat16))
+    _, f64_new, _, _ = oracle_gate_keys(h, want_f64=True)
+    np.testing.assert_allclose(f64_new, f64_ref, rtol=1e-5, atol=1e-6)
+    new = oracle_step(h, gated=True)
+    np.testing.assert_array_equal(new["sel"], ref["sel"])
+
+
+def test_planted_blocks_are_selected_tiny():
+    from planting import plant
+    w = wl.named("tiny")
+    plant(w)
+    h = Host(w)
+    res = oracle_step(h, gated=False)
+    sc = res["scores"][0, 0, :63]
+    chosen = set(res["sel"][0, 0, :res["cnt"][0, 0]].tolist())
+    planted = set(w.planted[0, 0].tolist())
+    assert planted <= chosen
+    others = np.delete(sc, list(planted))
+    assert sc[list(planted)].min() > others.max()  # planted blocks lead the ranking
+
+
+def test_oracle_step_shapes_and_validity():
+    w = small_paged()
+    h = Host(w)
+    res = oracle_step(h, gated=True)
+    for s in range(w.batch):
+        local = (int(h.lens[s]) - 1) // 64
+        for kvh in range(w.n_kv_heads):
+            c = res["cnt"][s, kvh]
+            sel = res["sel"][s, kvh]
+            assert c == min(w.budget // 64 - 1, local) + 1
+            assert sel[c - 1] == local and np.all(np.diff(sel[:c]) > 0)
+            assert np.all((res["gates"][s, kvh, :c - 1] > 0) & (res["gates"][s, kvh, :c - 1] < 1))
+    assert np.all(np.isfinite(res["out"]))
+
+
+# ---------------------------------------------------------------- numbers the pages print
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def test_gate_parameter_count_and_checkpoint_size():
+    # Gate weights as the oracle consumes them: per query head w_q [128][128],
+    # per KV head w_k [384][128], two 128-wide norm vectors, no biases; stored bf16.
+    for name, layers, hq, hkv, params_m, ckpt_mib in _golden_rows("gate_params.txt"):
+        layers, hq, hkv = int(layers), int(hq), int(hkv)
+        per_layer = hq * 128 * 128 + hkv * 384 * 128 + 2 * 128
+        n = layers * per_layer
+        assert round(n / 1e6, 1) == float(params_m), (name, n)
+        mib = n * 2 / 2 ** 20
+        assert math.ceil(mib) == int(ckpt_mib), (name, mib)
+        # neither fp32 storage, nor biases, nor one query projection per KV head
+        # would print these numbers
+        assert math.ceil(n * 4 / 2 ** 20) != int(ckpt_mib)
+        assert round(layers * (per_layer + hq * 128 + hkv * 128) / 1e6, 1) != float(params_m)
+        assert round(layers * (hkv * 128 * 128 + hkv * 384 * 128 + 256) / 1e6, 1) != float(params_m)
