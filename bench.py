@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""SAS sparse-decode benchmark on one MI355X.
+
+One step = one decode query per sequence through one attention layer:
+sas_gate_topk (gate query, block scores, per-KV-head Top-K) followed by
+sas_sparse_decode (block-sparse flash-decode over the selection).  Gate keys
+are pooled once by sas_pool_blocks before timing.  Inputs are synthetic and
+already resident in HBM.  Consecutive steps rotate over --layers independent
+layers (own K/V pools, gate keys, gate weights, queries), as consecutive
+attention calls of a model do, so no step re-reads data a previous step left
+in the 256 MB last-level cache.
+
+Prints one JSON line: queries/s (sequences x steps / wall time of the timed
+steps), the roofline entry of the dominant call (sas_sparse_decode, timed with
+HIP events on its stream) and the oracle timed on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kv_bytes_per_step(cnt, block_bytes):
+    return int(cnt.sum()) * 2 * block_bytes
+
+
+def gk_bytes_per_step(lens, n_kv_heads):
+    return int(sum((int(L) - 1) // 64 for L in lens)) * n_kv_heads * 128 * 2
+
+
+def cpu_baseline(layer, budget, gated, seconds):
+    """The oracle (as it stands) on a bounded sample of the same workload:
+    whole sequences of the first layer, gate stage + dense masked attention,
+    repeated until `seconds` of host time have passed."""
+    import numpy as np
+    import oracle
+    from learned_block_sparse_tok_amd import workloads as wl
+    w = layer["w"]
+    n_s = min(w.batch, 4)
+    bt = wl.host(w.block_table)[:n_s]
+    nblk = bt.shape[1]
+    pages = bt.reshape(-1)
+    import torch
+    idx = torch.as_tensor(pages, device=w.k_pool.device, dtype=torch.int64)
+    # both layouts are arrays of 64-token pages (page p of a contiguous cache is
+    # sequence p // max_blocks, block p % max_blocks), so gather whole pages
+    k = wl.host(w.k_pool.view(w.n_pages, -1).index_select(0, idx))
+    v = wl.host(w.v_pool.view(w.n_pages, -1).index_select(0, idx))
+    bt_sub = np.arange(n_s * nblk, dtype=np.int32).reshape(n_s, nblk)
+    q = wl.host(w.q)[:n_s].copy()
+    lens = wl.host(w.seq_lens)[:n_s].astype(np.int32)
+    gk = np.zeros((n_s * nblk, w.n_kv_heads, 128), np.uint16)
+    seq = np.repeat(np.arange(n_s, dtype=np.int32), [int(L) // 64 for L in lens])
+    blk = np.concatenate([np.arange(int(L) // 64, dtype=np.int32) for L in lens])
+    wk, wq = wl.host(w.w_k), wl.host(w.w_q)
+    wkn, wqn = wl.host(w.w_knorm), wl.host(w.w_qnorm)
+    oracle.pool_blocks(k, bt_sub, w.strides, w.n_kv_heads, seq, blk, wk, wkn, w.theta, gk)  # precomputed, untimed
+    queries, t_total, reps = 0, 0.0, 0
+    while t_total < seconds or reps == 0:
+        t0 = time.perf_counter()
+        sel, gates, cnt, _ = oracle.gate_topk(q, wq, wqn, gk, bt_sub, lens, w.theta, budget, w.n_kv_heads)
+        oracle.attend(q, k, v, bt_sub, w.strides, w.n_kv_heads, lens, sel, gates if gated else None, cnt,
+                      1.0 / math.sqrt(128))
+        t_total += time.perf_counter() - t0
+        queries += n_s
+        reps += 1
+    return dict(value=queries / t_total, unit="queries/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{n_s} of {w.batch} sequences of the same workload ({'gated' if gated else 'plain'} mode), "
+                       f"gate stage + dense masked attention over all {int(lens[0])} tokens, {reps} repetitions, "
+                       f"{t_total:.1f} s; gate keys pooled beforehand (untimed, as on the GPU)")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen3_8b")
+    ap.add_argument("--budget", type=int, default=2048)
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--modes", default="plain,gated")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py: the SAS decode path here runs on one GPU only; multi-GPU runs are not "
+                  f"supported (asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from learned_block_sparse_tok_amd import ops
+    from learned_block_sparse_tok_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ops.lib()
+    t_setup = time.perf_counter()
+    layers = []
+    for l in range(args.layers):
+        w = wl.named(args.workload, seed=100 + l, device=dev, budget=args.budget)
+        shape = ops.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides)
+        gk = torch.zeros((w.n_pages, w.n_kv_heads, 128), dtype=torch.bfloat16, device=dev)
+        lens = wl.host(w.seq_lens)
+        seq = np.repeat(np.arange(w.batch, dtype=np.int32), [int(L) // 64 for L in lens])
+        blk = np.concatenate([np.arange(int(L) // 64, dtype=np.int32) for L in lens])
+        ops.pool_blocks(shape, w.k_pool, w.block_table, torch.as_tensor(seq, device=dev),
+                        torch.as_tensor(blk, device=dev), w.w_k, w.w_knorm, w.theta, gk)
+        layers.append(dict(w=w, gk=gk))
+        torch.cuda.synchronize()
+        log(f"layer {l}: {args.workload} inputs drawn and gate keys pooled")
+    w0 = layers[0]["w"]
+    log(f"setup {time.perf_counter() - t_setup:.1f} s")
+
+    stream = torch.cuda.current_stream()
+    results = {}
+    for mode in args.modes.split(","):
+        gated = mode == "gated"
+        dec = ops.SparseDecoder(w0.batch, w0.n_q_heads, w0.n_kv_heads, w0.max_blocks, w0.strides, args.budget,
+                                w0.theta, gated, device=dev)
+
+        def step(i, ev=None):
+            L = layers[i % len(layers)]
+            w = L["w"]
+            dec.select(w.q, w.w_q, w.w_qnorm, L["gk"], w.block_table, w.seq_lens)
+            if ev is not None:
+                ev[0].record(stream)
+            dec.attend(w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens)
+            if ev is not None:
+                ev[1].record(stream)
+
+        for i in range(args.warmup):
+            step(i)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, evs[i])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        # algorithmic bytes: selected K+V blocks (decode) and every candidate's gate key (gate)
+        cnts = []
+        for l in range(len(layers)):
+            step(l)
+            torch.cuda.synchronize()
+            cnts.append(wl.host(dec.cnt))
+        kv_b = float(np.mean([kv_bytes_per_step(c, 64 * 128 * 2) for c in cnts]))
+        gk_b = float(np.mean([gk_bytes_per_step(wl.host(L["w"].seq_lens), w0.n_kv_heads) for L in layers]))
+        ms = elapsed * 1e3 / args.steps
+        results[mode] = dict(queries_per_s=w0.batch * args.steps / elapsed, ms_per_step=ms,
+                             decode_ms=dec_ms, decode_gbs=kv_b / (dec_ms * 1e-3) / 1e9,
+                             step_gbs=(kv_b + gk_b) / (ms * 1e-3) / 1e9, kv_bytes=kv_b, gk_bytes=gk_b,
+                             attended_tokens_per_query=float(np.mean([c.sum() for c in cnts])) * 64 / (
+                                 w0.batch * w0.n_kv_heads))
+        log(f"{mode}: {results[mode]['queries_per_s']:.0f} queries/s, {ms * 1e3:.1f} us/step, "
+            f"decode {dec_ms * 1e3:.1f} us = {results[mode]['decode_gbs']:.0f} GB/s, "
+            f"step {results[mode]['step_gbs']:.0f} GB/s")
+
+    worst = min(results, key=lambda m: results[m]["queries_per_s"])
+    r = results[worst]
+    line = {
+        "metric": "sparse-decode queries/s + % HBM roofline, Qwen3-8B shape, 32K ctx, 2K budget",
+        "value": round(r["queries_per_s"], 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": w0.batch, "context": int(wl.host(w0.seq_lens).max()),
+                   "n_q_heads": w0.n_q_heads, "n_kv_heads": w0.n_kv_heads, "head_dim": 128,
+                   "budget_tokens": args.budget, "kv_layout": w0.layout, "layers_rotated": len(layers),
+                   "mode": f"{worst} (slower of {','.join(results)})"},
+        "roofline": {"bound": "hbm", "kernel": "sas_sparse_decode (split + merge kernels)",
+                     "achieved": round(r["decode_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(r["decode_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": r["kv_bytes"], "avg_launch_us": round(r["decode_ms"] * 1e3, 2)},
+        "step_hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(r["queries_per_s"], 1),
+        "attended_kv_tokens_per_s": round(r["queries_per_s"] * r["attended_tokens_per_query"], 1),
+        "modes": {m: {k: round(v, 3) for k, v in d.items()} for m, d in results.items()},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(layers[0], args.budget, worst == "gated", args.cpu_seconds)
+        log(f"cpu baseline: {line['cpu_baseline']['value']:.1f} queries/s on {line['cpu_baseline']['cores']} threads")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

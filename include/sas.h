@@ -1,0 +1,165 @@
+/*
+ * sas.h -- C ABI of libsas, the MI355X (gfx950) SAS sparse-decode library.
+ *
+ * Simple-Attention-Sparsification (SAS) decodes with attention over a learned
+ * choice of 64-token KV blocks ("Tencent released Simple-Attention-
+ * Sparsification ...", aigc.news, the paragraph listing the sparse-attention
+ * setup; "Specifications and Configuration Table" of the localmodelwatch
+ * model page): each key block is pooled (max + min + average) into a 128-wide
+ * gate key with Q/K normalisation and gate RoPE; a query projection (Qproj)
+ * of the decode query scores the blocks; a Top-K keeps 31 historical blocks
+ * plus the local block for the default 2,048-token budget (1,024 / 4,096
+ * tokens also, without retraining); attention then reads only those blocks,
+ * optionally scaled by continuous gates on the selected blocks.
+ *
+ * Three calls, in serving order:
+ *   sas_pool_blocks    once per newly completed 64-token block   (pooling)
+ *   sas_gate_topk      once per decode step                      (selection)
+ *   sas_sparse_decode  once per decode step                      (attention)
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is a DEVICE pointer owned by the caller (for
+ *     example a torch tensor's data_ptr()), except `shape`, which is a host
+ *     pointer read during the call.  The library never allocates, frees or
+ *     copies between host and device, and never synchronises: each call only
+ *     enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ *     returns.
+ *   - bf16 tensors hold IEEE bfloat16 bit patterns; all arithmetic inside is
+ *     fp32 (MFMA bf16 x bf16 -> fp32 for the attention tiles); results
+ *     rounded to bf16 use round-to-nearest-even.
+ *   - head_dim = gate_dim = 128 and block = 64 tokens are fixed.
+ *   - Arguments are checked on the host before anything is launched; a failed
+ *     check launches nothing, leaves every output untouched and returns a
+ *     non-zero sas_status.  Device-resident values (sequence lengths, block
+ *     table entries, selections) are trusted: they must be in range.
+ *   - GQA: query head h reads KV head h / (n_q_heads / n_kv_heads).
+ *   - Calls are thread-safe; sas_last_error() is per host thread.
+ */
+#ifndef SAS_H
+#define SAS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAS_HEAD_DIM 128
+#define SAS_GATE_DIM 128
+#define SAS_BLOCK 64
+#define SAS_MAX_GROUP 16       /* n_q_heads / n_kv_heads */
+#define SAS_MAX_BLOCKS 16384   /* blocks per sequence (1,048,576 tokens) */
+
+typedef int32_t sas_status;
+enum {
+  SAS_OK = 0,
+  SAS_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad budget or stride */
+  SAS_ERR_UNSUPPORTED = 2, /* outside the supported envelope (group > 16, misaligned, ...) */
+  SAS_ERR_WORKSPACE = 3,   /* workspace too small */
+  SAS_ERR_HIP = 4          /* a HIP launch failed; detail in sas_last_error() */
+};
+
+/*
+ * Shape of one attention layer's decode batch and of its paged KV pools.
+ * K/V element (page p, kv head h, token-in-block t, dim d) lives at
+ *   pool[p * page_stride + h * head_stride + t * tok_stride + d]   (elements).
+ *   head-major pages [P][Hkv][64][128]:  (Hkv*64*128, 128, 64*128)
+ *   contiguous cache [B][L][Hkv][128] with block_table[s][c] = s*max_blocks+c:
+ *                                       (64*Hkv*128, Hkv*128, 128)
+ * Strides must be multiples of 8 elements and pools 16-byte aligned.
+ */
+typedef struct {
+  int32_t batch;       /* B: sequences in the decode batch */
+  int32_t n_q_heads;   /* Hq */
+  int32_t n_kv_heads;  /* Hkv; Hq % Hkv == 0, Hq / Hkv <= 16 */
+  int32_t max_blocks;  /* columns of block_table, <= SAS_MAX_BLOCKS */
+  int64_t page_stride, tok_stride, head_stride;
+} sas_shape;
+
+/*
+ * sas_pool_blocks -- key-block pooling into gate keys (the pages' "key block
+ * pooling max + min + average", "gate hidden size 128", "Q/K normalization",
+ * "gate RoPE").
+ *
+ * For each listed pair i (s = pool_seq[i], c = pool_blk[i]) and every KV head
+ * h, over the 64 cached keys of block c (all 64 rows must be written):
+ *   p  = [max_t k_t | min_t k_t | mean_t k_t]                     (384 values)
+ *   u  = p @ w_k[h]                       w_k: bf16 [Hkv][384][128], no bias
+ *   n  = u / sqrt(mean(u^2) + 1e-6) * w_knorm                    (RMSNorm)
+ *   gk = RoPE(n, position 64*c, rope_theta)   rotate-half pairs (i, i+64),
+ *        angle position * rope_theta^(-i/64)
+ *   gate_keys[block_table[s][c]][h][:] = bf16(gk)         bf16 [P][Hkv][128]
+ * n == 0 is a no-op returning SAS_OK.  pool_seq / pool_blk: int32 [n].
+ */
+sas_status sas_pool_blocks(const sas_shape *shape, const void *k_pool, const int32_t *block_table,
+                           const int32_t *pool_seq, const int32_t *pool_blk, int32_t n,
+                           const void *w_k, const float *w_knorm, double rope_theta,
+                           void *gate_keys, void *stream);
+
+/*
+ * sas_gate_topk -- gate scores and per-KV-head Top-K block selection (the
+ * pages' "query projection Qproj", "training Top-K 31 historical blocks", the
+ * 1,024 / 2,048 / 4,096-token decode budgets, "continuous gates on selected
+ * KV blocks").
+ *
+ * For sequence s with L = seq_lens[s] >= 1 cached tokens (the current token
+ * included) the local block is l = (L-1)/64 and the candidates are c < l.
+ *   gate query, per query head h: RoPE(RMSNorm(q[s][h] @ w_q[h]) * w_qnorm,
+ *       position L-1)                      w_q: bf16 [Hq][128][128], no bias
+ *   score of c for KV head k: mean over k's query heads of
+ *       <gate query, gate_keys[block_table[s][c]][k]> / sqrt(128)
+ *   Top-K: the min(budget/64 - 1, l) best candidates under (score descending,
+ *       block index ascending; NaN ranks lowest, -0 == +0), then the local
+ *       block.
+ * Outputs ([B][Hkv][budget/64] unless noted; the selection ascending, the
+ * local block last, padded with -1 / 0):
+ *   sel    int32  selected block indices
+ *   gates  fp32   sigmoid(score) per selected historical block, 1 for the
+ *                 local block (nullable: not written)
+ *   cnt    int32  [B][Hkv] number of selected blocks (>= 1)
+ *   scores fp32   [B][Hkv][max_blocks] block scores (entries c >= l are -inf)
+ * workspace: device scratch of at least sas_gate_topk_workspace_bytes(shape).
+ * budget_tokens: a positive multiple of 64, at most 64 * 256.
+ */
+size_t sas_gate_topk_workspace_bytes(const sas_shape *shape);
+sas_status sas_gate_topk(const sas_shape *shape, const void *q, const void *w_q,
+                         const float *w_qnorm, const void *gate_keys, const int32_t *block_table,
+                         const int32_t *seq_lens, double rope_theta, int32_t budget_tokens,
+                         int32_t *sel, float *gates, int32_t *cnt, float *scores,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sas_sparse_decode -- block-sparse flash-decode over the selected blocks
+ * (the pages' block-sparse decoding within the token budget).
+ *
+ * For query head h of sequence s (KV head k = h / G) over the tokens j of the
+ * cnt[s][k] blocks sel[s][k][:] with j <= L-1:
+ *   z_j = sm_scale * <q[s][h], K_j>,   P = softmax(z) over those tokens
+ *   plain mode (gates == NULL):  out = sum_j P_j V_j
+ *   gated mode:                  out = sum_j gates[s][k][i(j)] * P_j V_j
+ *       (each selected block's contribution scaled by its gate; P normalised
+ *        over the whole selection)
+ * q: bf16 [B][Hq][128]; out: bf16 [B][Hq][128]; sel / gates: [B][Hkv][max_sel]
+ * as written by sas_gate_topk with max_sel = budget/64; cnt: [B][Hkv].
+ * workspace: device scratch of at least
+ * sas_sparse_decode_workspace_bytes(shape, max_sel) bytes.
+ */
+size_t sas_sparse_decode_workspace_bytes(const sas_shape *shape, int32_t max_sel);
+sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *k_pool,
+                             const void *v_pool, const int32_t *block_table,
+                             const int32_t *seq_lens, const int32_t *sel, const float *gates,
+                             const int32_t *cnt, int32_t max_sel, float sm_scale, void *out,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Text of a status code (static storage). */
+const char *sas_status_str(sas_status status);
+/* Detail of the last failed call on this host thread ("" if none). */
+const char *sas_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t sas_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAS_H */

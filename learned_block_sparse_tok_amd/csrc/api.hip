@@ -1,0 +1,208 @@
+// C ABI of libsas: argument checks, workspace carving, kernel launches.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/sas.h"
+#include "sas_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+sas_status fail(sas_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+sas_status ok() {
+  g_last_error[0] = '\0';
+  return SAS_OK;
+}
+
+sas_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(SAS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+sas_status check_shape(const sas_shape *sh, bool need_kv_strides) {
+  if (!sh) return fail(SAS_ERR_INVALID_ARG, "shape is NULL");
+  if (sh->batch <= 0 || sh->n_q_heads <= 0 || sh->n_kv_heads <= 0 || sh->max_blocks <= 0)
+    return fail(SAS_ERR_INVALID_ARG, "batch, n_q_heads, n_kv_heads and max_blocks must be positive");
+  if (sh->n_q_heads % sh->n_kv_heads != 0)
+    return fail(SAS_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", sh->n_q_heads,
+                sh->n_kv_heads);
+  if (sh->n_q_heads / sh->n_kv_heads > SAS_MAX_GROUP)
+    return fail(SAS_ERR_UNSUPPORTED, "group size %d exceeds %d", sh->n_q_heads / sh->n_kv_heads, SAS_MAX_GROUP);
+  if (sh->max_blocks > SAS_MAX_BLOCKS)
+    return fail(SAS_ERR_UNSUPPORTED, "max_blocks %d exceeds %d", sh->max_blocks, SAS_MAX_BLOCKS);
+  if (need_kv_strides) {
+    if (sh->page_stride <= 0 || sh->tok_stride <= 0 || sh->head_stride <= 0)
+      return fail(SAS_ERR_INVALID_ARG, "KV strides must be positive");
+    if (sh->page_stride % 8 || sh->tok_stride % 8 || sh->head_stride % 8)
+      return fail(SAS_ERR_UNSUPPORTED, "KV strides must be multiples of 8 elements");
+    if (sh->tok_stride < SAS_HEAD_DIM)
+      return fail(SAS_ERR_INVALID_ARG, "tok_stride must be at least %d", SAS_HEAD_DIM);
+  }
+  return SAS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sas_status_str(sas_status st) {
+  switch (st) {
+    case SAS_OK: return "SAS_OK";
+    case SAS_ERR_INVALID_ARG: return "SAS_ERR_INVALID_ARG";
+    case SAS_ERR_UNSUPPORTED: return "SAS_ERR_UNSUPPORTED";
+    case SAS_ERR_WORKSPACE: return "SAS_ERR_WORKSPACE";
+    case SAS_ERR_HIP: return "SAS_ERR_HIP";
+    default: return "SAS_ERR_UNKNOWN";
+  }
+}
+
+const char *sas_last_error(void) { return g_last_error; }
+
+int32_t sas_version(void) { return 100; }
+
+sas_status sas_pool_blocks(const sas_shape *shape, const void *k_pool, const int32_t *block_table,
+                           const int32_t *pool_seq, const int32_t *pool_blk, int32_t n, const void *w_k,
+                           const float *w_knorm, double rope_theta, void *gate_keys, void *stream) {
+  sas_status st = check_shape(shape, true);
+  if (st) return st;
+  if (n < 0) return fail(SAS_ERR_INVALID_ARG, "n is negative");
+  if (n == 0) return ok();
+  if (!k_pool || !block_table || !pool_seq || !pool_blk || !w_k || !w_knorm || !gate_keys)
+    return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!(rope_theta > 1.0)) return fail(SAS_ERR_INVALID_ARG, "rope_theta must be > 1");
+  if (!aligned16(gate_keys)) return fail(SAS_ERR_UNSUPPORTED, "gate_keys must be 16-byte aligned");
+  sas::PoolParams p;
+  p.k_pool = (const uint16_t *)k_pool;
+  p.block_table = block_table;
+  p.pool_seq = pool_seq;
+  p.pool_blk = pool_blk;
+  p.w_k = (const uint16_t *)w_k;
+  p.w_knorm = w_knorm;
+  p.gate_keys = (uint16_t *)gate_keys;
+  p.page_stride = shape->page_stride;
+  p.tok_stride = shape->tok_stride;
+  p.head_stride = shape->head_stride;
+  p.n = n;
+  p.n_kv_heads = shape->n_kv_heads;
+  p.max_blocks = shape->max_blocks;
+  p.theta = rope_theta;
+  return hip_status(sas::launch_pool(p, (hipStream_t)stream), "sas_pool_blocks launch");
+}
+
+size_t sas_gate_topk_workspace_bytes(const sas_shape *shape) {
+  if (!shape || shape->batch <= 0 || shape->n_q_heads <= 0) return 0;
+  return align256((size_t)shape->batch * shape->n_q_heads * SAS_GATE_DIM * sizeof(float));
+}
+
+sas_status sas_gate_topk(const sas_shape *shape, const void *q, const void *w_q, const float *w_qnorm,
+                         const void *gate_keys, const int32_t *block_table, const int32_t *seq_lens,
+                         double rope_theta, int32_t budget_tokens, int32_t *sel, float *gates, int32_t *cnt,
+                         float *scores, void *workspace, size_t workspace_bytes, void *stream) {
+  sas_status st = check_shape(shape, false);
+  if (st) return st;
+  if (!q || !w_q || !w_qnorm || !gate_keys || !block_table || !seq_lens || !sel || !cnt || !scores || !workspace)
+    return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (budget_tokens < SAS_BLOCK || budget_tokens % SAS_BLOCK)
+    return fail(SAS_ERR_INVALID_ARG, "budget_tokens (%d) must be a positive multiple of %d", budget_tokens,
+                SAS_BLOCK);
+  if (budget_tokens / SAS_BLOCK > 256)
+    return fail(SAS_ERR_UNSUPPORTED, "budget_tokens (%d) exceeds %d", budget_tokens, 256 * SAS_BLOCK);
+  if (!(rope_theta > 1.0)) return fail(SAS_ERR_INVALID_ARG, "rope_theta must be > 1");
+  if (!aligned16(gate_keys) || !aligned16(workspace))
+    return fail(SAS_ERR_UNSUPPORTED, "gate_keys and workspace must be 16-byte aligned");
+  if (workspace_bytes < sas_gate_topk_workspace_bytes(shape))
+    return fail(SAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
+                sas_gate_topk_workspace_bytes(shape));
+  hipStream_t s = (hipStream_t)stream;
+  sas::GateQueryParams gp;
+  gp.q = (const uint16_t *)q;
+  gp.w_q = (const uint16_t *)w_q;
+  gp.w_qnorm = w_qnorm;
+  gp.seq_lens = seq_lens;
+  gp.gq = (float *)workspace;
+  gp.batch = shape->batch;
+  gp.n_q_heads = shape->n_q_heads;
+  gp.theta = rope_theta;
+  hipError_t e = sas::launch_gate_query(gp, s);
+  if (e != hipSuccess) return hip_status(e, "sas_gate_topk gate-query launch");
+  sas::ScoreTopkParams tp;
+  tp.gq = (const float *)workspace;
+  tp.gate_keys = (const uint16_t *)gate_keys;
+  tp.block_table = block_table;
+  tp.seq_lens = seq_lens;
+  tp.sel = sel;
+  tp.gates = gates;
+  tp.cnt = cnt;
+  tp.scores = scores;
+  tp.n_q_heads = shape->n_q_heads;
+  tp.n_kv_heads = shape->n_kv_heads;
+  tp.group = shape->n_q_heads / shape->n_kv_heads;
+  tp.max_blocks = shape->max_blocks;
+  tp.n_sel = budget_tokens / SAS_BLOCK;
+  return hip_status(sas::launch_score_topk(tp, shape->batch, s), "sas_gate_topk score/top-k launch");
+}
+
+size_t sas_sparse_decode_workspace_bytes(const sas_shape *shape, int32_t max_sel) {
+  if (!shape || shape->batch <= 0 || shape->n_kv_heads <= 0 || shape->n_q_heads <= 0 || max_sel <= 0) return 0;
+  sas::DecodeSplit sp = sas::decode_split(shape->batch, shape->n_kv_heads, max_sel);
+  const size_t slots = (size_t)shape->batch * shape->n_q_heads * sp.waves_per_unit;
+  return align256(slots * SAS_HEAD_DIM * sizeof(float)) + align256(slots * 2 * sizeof(float));
+}
+
+sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *k_pool, const void *v_pool,
+                             const int32_t *block_table, const int32_t *seq_lens, const int32_t *sel,
+                             const float *gates, const int32_t *cnt, int32_t max_sel, float sm_scale, void *out,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  sas_status st = check_shape(shape, true);
+  if (st) return st;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !sel || !cnt || !out || !workspace)
+    return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (max_sel <= 0) return fail(SAS_ERR_INVALID_ARG, "max_sel must be positive");
+  if (!(sm_scale > 0.f)) return fail(SAS_ERR_INVALID_ARG, "sm_scale must be positive");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(workspace))
+    return fail(SAS_ERR_UNSUPPORTED, "q, k_pool, v_pool and workspace must be 16-byte aligned");
+  const size_t need = sas_sparse_decode_workspace_bytes(shape, max_sel);
+  if (workspace_bytes < need)
+    return fail(SAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  sas::DecodeSplit sp = sas::decode_split(shape->batch, shape->n_kv_heads, max_sel);
+  const size_t slots = (size_t)shape->batch * shape->n_q_heads * sp.waves_per_unit;
+  sas::DecodeParams p;
+  p.q = (const uint16_t *)q;
+  p.k_pool = (const uint16_t *)k_pool;
+  p.v_pool = (const uint16_t *)v_pool;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.sel = sel;
+  p.cnt = cnt;
+  p.gates = gates;
+  p.part_o = (float *)workspace;
+  p.part_ml = (float *)((char *)workspace + align256(slots * SAS_HEAD_DIM * sizeof(float)));
+  p.out = (uint16_t *)out;
+  p.page_stride = shape->page_stride;
+  p.tok_stride = shape->tok_stride;
+  p.head_stride = shape->head_stride;
+  p.n_q_heads = shape->n_q_heads;
+  p.n_kv_heads = shape->n_kv_heads;
+  p.group = shape->n_q_heads / shape->n_kv_heads;
+  p.max_blocks = shape->max_blocks;
+  p.max_sel = max_sel;
+  p.wg_per_unit = sp.wg_per_unit;
+  p.blocks_per_wave = sp.blocks_per_wave;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  return hip_status(sas::launch_decode(p, shape->batch, (hipStream_t)stream), "sas_sparse_decode launch");
+}
+
+}  // extern "C"

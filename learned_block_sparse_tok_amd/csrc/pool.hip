@@ -1,0 +1,98 @@
+// Key-block pooling -> gate keys.
+//
+// SAS pools each 64-token key block by max, min and average and maps the
+// pooled statistics to a 128-wide gate key with Q/K normalisation and gate
+// RoPE ("Tencent released Simple-Attention-Sparsification ...", aigc.news,
+// the setup paragraph; "Specifications and Configuration Table" of the
+// localmodelwatch model page: KV block size 64, gate hidden size 128, key
+// block pooling max + min + average, Q/K normalization, gate RoPE).
+//
+// One workgroup (256 threads) per (listed block, KV head):
+//   1. a coalesced pass over the 64 x 128 bf16 key rows: per dimension the
+//      running max / min / fp32 sum of 32 rows per thread, halves combined
+//      in LDS -> pooled[384] = [max | min | mean];
+//   2. pooled @ w_k[h] (384 x 128, rows read coalesced), two 192-row halves
+//      per output dimension combined in LDS;
+//   3. wave 0: RMSNorm (eps 1e-6) * w_knorm, rotate-half RoPE at position
+//      64*c with fp64 angles, round to bf16, store.
+// Bytes per (block, KV head): 16 KiB of keys read, 256 B of gate key written
+// (w_k is 96 KiB per KV head and stays in L2).
+#include "sas_device.h"
+#include "sas_kernels.h"
+
+namespace sas {
+
+__global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
+  const int unit = blockIdx.x;
+  const int i = unit / p.n_kv_heads;
+  const int kvh = unit - i * p.n_kv_heads;
+  const int t = threadIdx.x;
+  const int s = p.pool_seq[i], c = p.pool_blk[i];
+  const int32_t page = p.block_table[(int64_t)s * p.max_blocks + c];
+  const uint16_t *kb = p.k_pool + (int64_t)page * p.page_stride + (int64_t)kvh * p.head_stride;
+
+  __shared__ float part[2][3][kHeadDim];
+  __shared__ float pooled[3 * kHeadDim];
+  __shared__ float upart[2][kGateDim];
+
+  {  // 1. pooled statistics
+    const int d = t & (kHeadDim - 1);
+    const int half = t >> 7;
+    float mx = -__builtin_inff(), mn = __builtin_inff(), sum = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < kBlock / 2; ++r) {
+      float x = bf16_to_f32(kb[(int64_t)(half * (kBlock / 2) + r) * p.tok_stride + d]);
+      mx = fmaxf(mx, x);
+      mn = fminf(mn, x);
+      sum += x;
+    }
+    part[half][0][d] = mx;
+    part[half][1][d] = mn;
+    part[half][2][d] = sum;
+  }
+  __syncthreads();
+  if (t < kHeadDim) {
+    pooled[t] = fmaxf(part[0][0][t], part[1][0][t]);
+    pooled[kHeadDim + t] = fminf(part[0][1][t], part[1][1][t]);
+    pooled[2 * kHeadDim + t] = (part[0][2][t] + part[1][2][t]) * (1.0f / kBlock);
+  }
+  __syncthreads();
+  {  // 2. projection to the gate space
+    const int j = t & (kGateDim - 1);
+    const int half = t >> 7;
+    const uint16_t *w = p.w_k + (int64_t)kvh * 3 * kHeadDim * kGateDim;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < 3 * kHeadDim / 2; ++r) {
+      int row = half * (3 * kHeadDim / 2) + r;
+      acc = fmaf(pooled[row], bf16_to_f32(w[row * kGateDim + j]), acc);
+    }
+    upart[half][j] = acc;
+  }
+  __syncthreads();
+  if (t < 64) {  // 3. norm + RoPE on pairs (t, t+64)
+    float a = upart[0][t] + upart[1][t];
+    float b = upart[0][t + 64] + upart[1][t + 64];
+    float ss = wave_sum(a * a + b * b);
+    float inv = 1.0f / sqrtf(ss * (1.0f / kGateDim) + 1e-6f);
+    a = a * inv * p.w_knorm[t];
+    b = b * inv * p.w_knorm[t + 64];
+    double ang = (double)c * kBlock * pow(p.theta, -(double)t / 64.0);
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    float cf = (float)cs, sf = (float)sn;
+    float ra = a * cf - b * sf;
+    float rb = b * cf + a * sf;
+    uint16_t *dst = p.gate_keys + ((int64_t)page * p.n_kv_heads + kvh) * kGateDim;
+    dst[t] = (uint16_t)f32_to_bf16(ra);
+    dst[t + 64] = (uint16_t)f32_to_bf16(rb);
+  }
+}
+
+hipError_t launch_pool(const PoolParams &p, hipStream_t st) {
+  if (p.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(pool_kernel, dim3((unsigned)(p.n * p.n_kv_heads)), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace sas

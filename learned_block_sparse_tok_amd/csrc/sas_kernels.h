@@ -1,0 +1,68 @@
+// Kernel parameter blocks and launchers of libsas (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sas {
+
+struct PoolParams {
+  const uint16_t *k_pool;
+  const int32_t *block_table;
+  const int32_t *pool_seq, *pool_blk;
+  const uint16_t *w_k;      // [Hkv][384][128]
+  const float *w_knorm;     // [128]
+  uint16_t *gate_keys;      // [P][Hkv][128]
+  int64_t page_stride, tok_stride, head_stride;
+  int32_t n, n_kv_heads, max_blocks;
+  double theta;
+};
+
+struct GateQueryParams {
+  const uint16_t *q;        // [B][Hq][128]
+  const uint16_t *w_q;      // [Hq][128][128]
+  const float *w_qnorm;     // [128]
+  const int32_t *seq_lens;  // [B]
+  float *gq;                // [B][Hq][128] workspace
+  int32_t batch, n_q_heads;
+  double theta;
+};
+
+struct ScoreTopkParams {
+  const float *gq;          // [B][Hq][128]
+  const uint16_t *gate_keys;
+  const int32_t *block_table, *seq_lens;
+  int32_t *sel;
+  float *gates;             // nullable
+  int32_t *cnt;
+  float *scores;            // [B][Hkv][max_blocks]
+  int32_t n_q_heads, n_kv_heads, group, max_blocks, n_sel;
+};
+
+struct DecodeParams {
+  const uint16_t *q;
+  const uint16_t *k_pool, *v_pool;
+  const int32_t *block_table, *seq_lens, *sel, *cnt;
+  const float *gates;       // null: plain Top-K mode
+  float *part_o;            // [B*Hkv][W][G][128]
+  float *part_ml;           // [B*Hkv][W][G][2]
+  uint16_t *out;            // [B][Hq][128]
+  int64_t page_stride, tok_stride, head_stride;
+  int32_t n_q_heads, n_kv_heads, group, max_blocks, max_sel;
+  int32_t wg_per_unit;      // workgroups per (sequence, KV head)
+  int32_t blocks_per_wave;  // selected blocks each wave handles
+  float scale_log2;         // sm_scale * log2(e)
+};
+
+// Decode work split: waves per (sequence, KV head) and blocks per wave.
+struct DecodeSplit {
+  int wg_per_unit, waves_per_unit, blocks_per_wave;
+};
+DecodeSplit decode_split(int batch, int n_kv_heads, int max_sel);
+
+hipError_t launch_pool(const PoolParams &p, hipStream_t st);
+hipError_t launch_gate_query(const GateQueryParams &p, hipStream_t st);
+hipError_t launch_score_topk(const ScoreTopkParams &p, int batch, hipStream_t st);
+hipError_t launch_decode(const DecodeParams &p, int batch, hipStream_t st);
+
+}  // namespace sas

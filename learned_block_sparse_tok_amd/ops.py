@@ -1,0 +1,173 @@
+"""Thin Python binding of libsas (include/sas.h) over ctypes.
+
+Argument marshalling only: every step of the SAS decode path runs in the HIP
+kernels of libsas.so.  torch supplies device memory (tensors) and the stream
+(the current torch stream unless one is given).  There is no fallback: if
+libsas.so is missing or cannot load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsas.so")
+BLOCK = 64
+HEAD_DIM = 128
+GATE_DIM = 128
+
+SAS_OK, SAS_ERR_INVALID_ARG, SAS_ERR_UNSUPPORTED, SAS_ERR_WORKSPACE, SAS_ERR_HIP = range(5)
+
+
+class SasError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        super().__init__(f"{fn} failed: {_status_str(status)}: {detail}")
+        self.status = status
+
+
+class SasShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("page_stride", ctypes.c_int64), ("tok_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64)]
+
+
+_lib = None
+_VP, _I32, _F32, _F64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
+_SIGS = {
+    "sas_pool_blocks": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _F64, _VP, _VP]),
+    "sas_gate_topk_workspace_bytes": (_SZ, [_VP]),
+    "sas_gate_topk": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _F64, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "sas_sparse_decode_workspace_bytes": (_SZ, [_VP, _I32]),
+    "sas_sparse_decode": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP, _VP, _SZ, _VP]),
+    "sas_status_str": (ctypes.c_char_p, [_I32]),
+    "sas_last_error": (ctypes.c_char_p, []),
+    "sas_version": (_I32, []),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsas.so (built in-tree by learned_block_sparse_tok_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m learned_block_sparse_tok_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _status_str(st: int) -> str:
+    return lib().sas_status_str(st).decode()
+
+
+def _check(st: int, fn: str):
+    if st != SAS_OK:
+        raise SasError(st, fn, lib().sas_last_error().decode())
+
+
+def _ptr(t: torch.Tensor | None, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_shape(batch, n_q_heads, n_kv_heads, max_blocks, strides=(0, 0, 0)) -> SasShape:
+    ps, ts, hs = strides
+    return SasShape(batch, n_q_heads, n_kv_heads, max_blocks, ps, ts, hs)
+
+
+def gate_topk_workspace_bytes(shape: SasShape) -> int:
+    return int(lib().sas_gate_topk_workspace_bytes(ctypes.byref(shape)))
+
+
+def sparse_decode_workspace_bytes(shape: SasShape, max_sel: int) -> int:
+    return int(lib().sas_sparse_decode_workspace_bytes(ctypes.byref(shape), max_sel))
+
+
+def pool_blocks(shape: SasShape, k_pool, block_table, pool_seq, pool_blk, w_k, w_knorm, theta,
+                gate_keys, stream=None):
+    n = int(pool_seq.numel())
+    st = lib().sas_pool_blocks(ctypes.byref(shape), _ptr(k_pool, torch.bfloat16, "k_pool"),
+                               _ptr(block_table, torch.int32, "block_table"),
+                               _ptr(pool_seq, torch.int32, "pool_seq"), _ptr(pool_blk, torch.int32, "pool_blk"),
+                               n, _ptr(w_k, torch.bfloat16, "w_k"), _ptr(w_knorm, torch.float32, "w_knorm"),
+                               float(theta), _ptr(gate_keys, torch.bfloat16, "gate_keys"), _stream(stream))
+    _check(st, "sas_pool_blocks")
+
+
+def gate_topk(shape: SasShape, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, theta, budget_tokens,
+              sel, gates, cnt, scores, workspace, stream=None):
+    st = lib().sas_gate_topk(ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"), _ptr(w_q, torch.bfloat16, "w_q"),
+                             _ptr(w_qnorm, torch.float32, "w_qnorm"), _ptr(gate_keys, torch.bfloat16, "gate_keys"),
+                             _ptr(block_table, torch.int32, "block_table"), _ptr(seq_lens, torch.int32, "seq_lens"),
+                             float(theta), int(budget_tokens), _ptr(sel, torch.int32, "sel"),
+                             _ptr(gates, torch.float32, "gates"), _ptr(cnt, torch.int32, "cnt"),
+                             _ptr(scores, torch.float32, "scores"), _ptr(workspace, None, "workspace"),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "sas_gate_topk")
+
+
+def sparse_decode(shape: SasShape, q, k_pool, v_pool, block_table, seq_lens, sel, gates, cnt, max_sel,
+                  sm_scale, out, workspace, stream=None):
+    st = lib().sas_sparse_decode(ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"),
+                                 _ptr(k_pool, torch.bfloat16, "k_pool"), _ptr(v_pool, torch.bfloat16, "v_pool"),
+                                 _ptr(block_table, torch.int32, "block_table"),
+                                 _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(sel, torch.int32, "sel"),
+                                 _ptr(gates, torch.float32, "gates"), _ptr(cnt, torch.int32, "cnt"), int(max_sel),
+                                 float(sm_scale), _ptr(out, torch.bfloat16, "out"), _ptr(workspace, None, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "sas_sparse_decode")
+
+
+class SparseDecoder:
+    """Holds the outputs and workspaces of one layer's decode step (allocated
+    once, by torch) and runs sas_gate_topk + sas_sparse_decode on them."""
+
+    def __init__(self, batch, n_q_heads, n_kv_heads, max_blocks, strides, budget, theta, gated,
+                 device="cuda", sm_scale=None):
+        self.shape = make_shape(batch, n_q_heads, n_kv_heads, max_blocks, strides)
+        self.budget, self.theta, self.gated = budget, theta, gated
+        self.n_sel = budget // BLOCK
+        self.sm_scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(HEAD_DIM)
+        dev = torch.device(device)
+        self.sel = torch.empty((batch, n_kv_heads, self.n_sel), dtype=torch.int32, device=dev)
+        self.gates = torch.empty((batch, n_kv_heads, self.n_sel), dtype=torch.float32, device=dev)
+        self.cnt = torch.empty((batch, n_kv_heads), dtype=torch.int32, device=dev)
+        self.scores = torch.empty((batch, n_kv_heads, max_blocks), dtype=torch.float32, device=dev)
+        self.out = torch.empty((batch, n_q_heads, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.ws_gate = torch.empty(gate_topk_workspace_bytes(self.shape), dtype=torch.uint8, device=dev)
+        self.ws_dec = torch.empty(sparse_decode_workspace_bytes(self.shape, self.n_sel), dtype=torch.uint8,
+                                  device=dev)
+
+    def select(self, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, stream=None):
+        gate_topk(self.shape, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, self.theta, self.budget,
+                  self.sel, self.gates, self.cnt, self.scores, self.ws_gate, stream)
+
+    def attend(self, q, k_pool, v_pool, block_table, seq_lens, stream=None):
+        sparse_decode(self.shape, q, k_pool, v_pool, block_table, seq_lens, self.sel,
+                      self.gates if self.gated else None, self.cnt, self.n_sel, self.sm_scale, self.out,
+                      self.ws_dec, stream)
+
+    def step(self, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens, stream=None):
+        self.select(q, w_q, w_qnorm, gate_keys, block_table, seq_lens, stream)
+        self.attend(q, k_pool, v_pool, block_table, seq_lens, stream)
+        return self.out

@@ -160,6 +160,16 @@ def select(scores: np.ndarray, seq_len: int, budget_tokens: int):
     return sel, gates, int(cnt)
 
 
+def block_gates(scores: np.ndarray, sel: np.ndarray, cnt: int) -> np.ndarray:
+    """Gates of a given selection of one (sequence, KV head): sigmoid of the
+    block scores, 1 for the last (local) block, 0 padding."""
+    sc = np.ascontiguousarray(scores, np.float32)
+    sel = np.ascontiguousarray(sel, np.int32)
+    out = np.zeros(len(sel), np.float32)
+    _load().sas_oracle_block_gates(_p(sc), _p(sel), ctypes.c_int32(cnt), ctypes.c_int32(len(sel)), _p(out))
+    return out
+
+
 def attend(q, k_pool, v_pool, block_table, strides, n_kv_heads, seq_lens, sel, gates, cnt,
            sm_scale, pairs=None):
     """Dense masked softmax attention.  gates=None is plain Top-K mode.

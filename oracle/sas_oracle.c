@@ -245,6 +245,19 @@ static int int_cmp(const void *pa, const void *pb) {
   return (a > b) - (a < b);
 }
 
+/* Continuous gates of a selection of cnt blocks (the last one local):
+ * g = sigmoid(score) for the historical blocks, 1 for the local block, 0 for
+ * the padding up to n_sel. */
+void sas_oracle_block_gates(const float *scores, const int32_t *sel, int32_t cnt, int32_t n_sel,
+                            float *gates) {
+  for (int i = 0; i < n_sel; ++i) {
+    if (i < cnt - 1)
+      gates[i] = (float)(1.0 / (1.0 + exp(-(double)scores[sel[i]])));
+    else
+      gates[i] = i == cnt - 1 ? 1.0f : 0.0f;
+  }
+}
+
 /* Top-K of one (s, kvh).  The budget of B tokens is B/64 blocks: the local
  * block (always attended, never a candidate) plus K_hist = B/64 - 1 historical
  * blocks (31 at the default 2,048 tokens).  K_eff = min(K_hist, l).  Output:
@@ -268,18 +281,8 @@ int32_t sas_oracle_select(const float *scores, int32_t seq_len, int32_t budget_t
   for (int i = 0; i < k_eff; ++i) chosen[i] = r[i].block;
   qsort(chosen, (size_t)k_eff, sizeof(int32_t), int_cmp);
   chosen[k_eff] = local;
-  for (int i = 0; i < n_sel; ++i) {
-    if (i <= k_eff) {
-      sel[i] = chosen[i];
-      if (gates) {
-        double sc = i < k_eff ? (double)scores[chosen[i]] : 0.0;
-        gates[i] = i < k_eff ? (float)(1.0 / (1.0 + exp(-sc))) : 1.0f;
-      }
-    } else {
-      sel[i] = -1;
-      if (gates) gates[i] = 0.0f;
-    }
-  }
+  for (int i = 0; i < n_sel; ++i) sel[i] = i <= k_eff ? chosen[i] : -1;
+  if (gates) sas_oracle_block_gates(scores, sel, k_eff + 1, n_sel, gates);
   free(chosen);
   free(r);
   return k_eff + 1;

@@ -1,0 +1,100 @@
+"""The C ABI library loads, exports every entry point include/sas.h declares,
+and rejects bad arguments on the host before any GPU work (CPU only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from learned_block_sparse_tok_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sas.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sas_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        pytest.skip("libsas.so not built")
+    return ops.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"sas_pool_blocks", "sas_gate_topk", "sas_sparse_decode"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.sas_status_str(0) == b"SAS_OK"
+    assert lib.sas_status_str(3) == b"SAS_ERR_WORKSPACE"
+    assert lib.sas_version() >= 100
+
+
+FAKE = ctypes.c_void_p(4096)  # never dereferenced: every call below fails its host-side checks
+
+
+def _shape(**kw):
+    d = dict(batch=2, n_q_heads=8, n_kv_heads=2, max_blocks=16, strides=(2 * 64 * 128, 128, 64 * 128))
+    d.update(kw)
+    return ops.make_shape(d["batch"], d["n_q_heads"], d["n_kv_heads"], d["max_blocks"], d["strides"])
+
+
+def _gate(lib, shape, budget=1024, ws_bytes=1 << 20, null_sel=False):
+    return lib.sas_gate_topk(ctypes.byref(shape) if shape is not None else None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, 1e6, budget, None if null_sel else FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+def _decode(lib, shape, max_sel=16, ws_bytes=1 << 24, scale=0.088):
+    return lib.sas_sparse_decode(ctypes.byref(shape), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, max_sel, scale,
+                                 FAKE, FAKE, ws_bytes, None)
+
+
+def test_gate_topk_rejects_bad_arguments(lib):
+    assert _gate(lib, None) == ops.SAS_ERR_INVALID_ARG
+    assert _gate(lib, _shape(), budget=1000) == ops.SAS_ERR_INVALID_ARG
+    assert _gate(lib, _shape(), budget=0) == ops.SAS_ERR_INVALID_ARG
+    assert _gate(lib, _shape(), budget=64 * 257) == ops.SAS_ERR_UNSUPPORTED
+    assert _gate(lib, _shape(n_q_heads=6, n_kv_heads=4)) == ops.SAS_ERR_INVALID_ARG
+    assert _gate(lib, _shape(n_q_heads=34, n_kv_heads=2)) == ops.SAS_ERR_UNSUPPORTED
+    assert _gate(lib, _shape(batch=0)) == ops.SAS_ERR_INVALID_ARG
+    assert _gate(lib, _shape(max_blocks=16385)) == ops.SAS_ERR_UNSUPPORTED
+    assert _gate(lib, _shape(), null_sel=True) == ops.SAS_ERR_INVALID_ARG
+    assert _gate(lib, _shape(), ws_bytes=16) == ops.SAS_ERR_WORKSPACE
+    assert b"workspace" in lib.sas_last_error()
+
+
+def test_sparse_decode_rejects_bad_arguments(lib):
+    assert _decode(lib, _shape(strides=(0, 128, 8192))) == ops.SAS_ERR_INVALID_ARG
+    assert _decode(lib, _shape(strides=(2 * 64 * 128, 100, 64 * 128))) == ops.SAS_ERR_UNSUPPORTED
+    assert _decode(lib, _shape(), max_sel=0) == ops.SAS_ERR_INVALID_ARG
+    assert _decode(lib, _shape(), scale=0.0) == ops.SAS_ERR_INVALID_ARG
+    assert _decode(lib, _shape(), ws_bytes=100) == ops.SAS_ERR_WORKSPACE
+
+
+def test_pool_rejects_bad_arguments_and_accepts_empty_list(lib):
+    sh = _shape()
+    assert lib.sas_pool_blocks(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, -1, FAKE, FAKE, 1e6, FAKE, None) == \
+        ops.SAS_ERR_INVALID_ARG
+    assert lib.sas_pool_blocks(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, 3, FAKE, FAKE, 0.5, FAKE, None) == \
+        ops.SAS_ERR_INVALID_ARG
+    assert lib.sas_pool_blocks(ctypes.byref(sh), None, FAKE, FAKE, FAKE, 3, FAKE, FAKE, 1e6, FAKE, None) == \
+        ops.SAS_ERR_INVALID_ARG
+    # an empty list enqueues nothing and succeeds
+    assert lib.sas_pool_blocks(ctypes.byref(sh), None, None, None, None, 0, None, None, 1e6, None, None) == ops.SAS_OK
+
+
+def test_workspace_sizes(lib):
+    sh = _shape(batch=32, n_q_heads=32, n_kv_heads=8, max_blocks=512)
+    assert lib.sas_gate_topk_workspace_bytes(ctypes.byref(sh)) >= 32 * 32 * 128 * 4
+    assert lib.sas_sparse_decode_workspace_bytes(ctypes.byref(sh), 32) >= 32 * 32 * 130 * 4
+    assert lib.sas_sparse_decode_workspace_bytes(ctypes.byref(sh), 0) == 0

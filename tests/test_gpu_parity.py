@@ -1,0 +1,271 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, on the GPU.
+
+Stage tests feed both sides the same seeded inputs for one stage; whole-step
+tests run pool -> select -> attend on each side from the same workload and
+compare with tie accounting (selection bit-exact outside the 1e-3 boundary
+band; outputs within max-abs 2e-2 / mean-abs 2e-3 of the fp64 oracle).
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_harness import (assert_out_close, bf16_out, compare_selection, compare_step, gpu_pool, gpu_step,
+                         shape_of)
+from harness import SM_SCALE, Host, complete_blocks, oracle_gate_keys, oracle_step
+from learned_block_sparse_tok_amd import ops
+from learned_block_sparse_tok_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ops.lib()
+
+
+# ------------------------------------------------------------------ pooling
+POOL_CASES = [
+    dict(name="paged_ragged", lens=[300, 64, 1, 4097, 200], Hq=8, Hkv=2, layout="paged", mb=70),
+    dict(name="contig_g4", lens=[4096, 777], Hq=4, Hkv=1, layout="contiguous", mb=None),
+    dict(name="paged_8kv", lens=[2048, 1000, 130], Hq=32, Hkv=8, layout="paged", mb=40),
+]
+
+
+@pytest.mark.parametrize("case", POOL_CASES, ids=lambda c: c["name"])
+def test_pool_blocks_parity(case):
+    say("pool", case["name"])
+    w = wl.make(len(case["lens"]), case["Hq"], case["Hkv"], case["lens"], 1024, case["layout"], 31, DEV,
+                max_blocks=case["mb"], random_norms=True, extra_pages=3)
+    h = Host(w)
+    gk_o, f64, seq, blk = oracle_gate_keys(h, want_f64=True)
+    gk_g = wl.host(gpu_pool(w))
+    # pages outside the list stay untouched (zero)
+    listed = np.zeros(w.n_pages, bool)
+    listed[h.bt[seq, blk]] = True
+    assert np.all(gk_g[~listed] == 0)
+    # each key within one bf16 ulp of the oracle's unrounded fp64 key
+    pages = h.bt[seq, blk]
+    got = oracle.bf16_to_f64(gk_g[pages])
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(f64) + 1e-30)) - 7)
+    assert np.all(np.abs(got - f64) <= ulp), float(np.max(np.abs(got - f64) / ulp))
+    flips = int(np.count_nonzero(gk_g[pages] != gk_o[pages]))
+    say(f"  gate-key bf16 values differing from the oracle's rounding: {flips} of {gk_o[pages].size}")
+    assert flips <= 0.01 * gk_o[pages].size
+
+
+def test_pool_blocks_empty_list_is_noop():
+    w = wl.make(1, 4, 1, 300, 1024, "paged", 32, DEV, max_blocks=5)
+    gk = torch.full((w.n_pages, 1, 128), 7, dtype=torch.bfloat16, device=DEV)
+    e = torch.zeros(0, dtype=torch.int32, device=DEV)
+    ops.pool_blocks(shape_of(w), w.k_pool, w.block_table, e, e, w.w_k, w.w_knorm, w.theta, gk)
+    torch.cuda.synchronize()
+    assert torch.all(gk == 7)
+
+
+# ------------------------------------------------------------------ gate / Top-K
+GATE_CASES = [
+    dict(name="tiny_1024", lens=[4096], Hq=4, Hkv=1, budget=1024, mb=64),
+    dict(name="b64_k0", lens=[1000, 5000], Hq=8, Hkv=2, budget=64, mb=80),
+    dict(name="mixed_2048", lens=[32768, 1, 64, 65, 2048, 2049, 3000], Hq=16, Hkv=4, budget=2048, mb=512),
+    dict(name="long_2047", lens=[131072, 70000], Hq=40, Hkv=8, budget=2048, mb=2048),
+    dict(name="ragged_4096", lens=[4096, 65536, 12345, 40000], Hq=32, Hkv=8, budget=4096, mb=1026),
+    dict(name="g16", lens=[9000, 600], Hq=16, Hkv=1, budget=1024, mb=150),
+]
+
+
+def _gate_inputs(case, seed):
+    w = wl.make(len(case["lens"]), case["Hq"], case["Hkv"], case["lens"], case["budget"], "paged", seed, DEV,
+                max_blocks=case["mb"], random_norms=True)
+    gk = wl.random_gate_keys(w.n_pages, w.n_kv_heads, seed, DEV)
+    return w, gk
+
+
+def _gpu_gate(w, gk, budget):
+    dec = ops.SparseDecoder(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, budget, w.theta, True,
+                            device=DEV)
+    dec.select(w.q, w.w_q, w.w_qnorm, gk, w.block_table, w.seq_lens)
+    torch.cuda.synchronize()
+    return dict(sel=wl.host(dec.sel), gates=wl.host(dec.gates), cnt=wl.host(dec.cnt), scores=wl.host(dec.scores))
+
+
+@pytest.mark.parametrize("case", GATE_CASES, ids=lambda c: c["name"])
+def test_gate_topk_parity(case):
+    say("gate", case["name"])
+    w, gk = _gate_inputs(case, 41)
+    h = Host(w)
+    sel, gates, cnt, scores = oracle.gate_topk(h.q, h.w_q, h.wqn, wl.host(gk), h.bt, h.lens, w.theta,
+                                               case["budget"], w.n_kv_heads)
+    o = dict(sel=sel, gates=gates, cnt=cnt, scores=scores)
+    g = _gpu_gate(w, gk, case["budget"])
+    for s in range(w.batch):
+        n = (int(h.lens[s]) - 1) // 64
+        np.testing.assert_allclose(g["scores"][:, :, :][s, :, :n], scores[s, :, :n], rtol=1e-5, atol=1e-5)
+        assert np.all(np.isneginf(g["scores"][s, :, n:]))
+    ties = compare_selection(g, o, h.lens, case["budget"])
+    say(f"  boundary ties: {len(ties)} of {w.batch * w.n_kv_heads}")
+    tie_set = set(ties)
+    for s in range(w.batch):
+        for k in range(w.n_kv_heads):
+            if (s, k) not in tie_set:
+                c = cnt[s, k]
+                np.testing.assert_allclose(g["gates"][s, k, :c], gates[s, k, :c], rtol=1e-5, atol=1e-6)
+                assert np.all(g["gates"][s, k, c:] == 0)
+
+
+def test_gate_topk_exact_ties_break_by_index():
+    # many candidate blocks share one physical page: identical scores on both
+    # sides, so the lower block index must win every tie, bit-exactly
+    w = wl.make(3, 8, 2, [5000, 3000, 20000], 2048, "paged", 43, DEV, max_blocks=320)
+    n_pages = w.n_pages
+    bt = wl.host(w.block_table).copy()
+    rng = np.random.default_rng(0)
+    bt = rng.integers(0, 12, size=bt.shape).astype(np.int32)  # only 12 distinct pages
+    w.block_table = torch.as_tensor(bt, device=DEV)
+    gk = wl.random_gate_keys(n_pages, 2, 43, DEV)
+    h = Host(w)
+    sel, gates, cnt, scores = oracle.gate_topk(h.q, h.w_q, h.wqn, wl.host(gk), h.bt, h.lens, w.theta, 2048, 2)
+    g = _gpu_gate(w, gk, 2048)
+    for s in range(w.batch):
+        for k in range(2):
+            # the GPU's scores of equal pages are equal, so ties are exact on both sides
+            n = (int(h.lens[s]) - 1) // 64
+            gs = g["scores"][s, k, :n]
+            for page in range(12):
+                vals = gs[bt[s, :n] == page]
+                assert len(set(vals.tolist())) <= 1
+    ties = compare_selection(g, dict(sel=sel, gates=gates, cnt=cnt, scores=scores), h.lens, 2048)
+    # equal-score groups straddle the threshold: the lower indices must win on both sides
+    assert ties == []
+
+
+# ------------------------------------------------------------------ attention
+DEC_CASES = [
+    dict(name="tiny_contig", lens=[4096], Hq=4, Hkv=1, budget=1024, layout="contiguous", mb=None),
+    dict(name="ragged_paged", lens=[300, 64, 1, 4097, 200, 129], Hq=8, Hkv=2, budget=512, layout="paged", mb=70),
+    dict(name="g5", lens=[9000, 20000], Hq=40, Hkv=8, budget=2048, layout="paged", mb=320),
+    dict(name="g1", lens=[3000, 70], Hq=4, Hkv=4, budget=1024, layout="paged", mb=50),
+    dict(name="g16", lens=[5000], Hq=16, Hkv=1, budget=4096, layout="contiguous", mb=None),
+    dict(name="b32_h8", lens=[2500] * 32, Hq=32, Hkv=8, budget=2048, layout="paged", mb=40),
+    dict(name="budget_ge_ctx", lens=[1500, 2000], Hq=8, Hkv=2, budget=4096, layout="paged", mb=32),
+]
+
+
+@pytest.mark.parametrize("gated", [False, True], ids=["plain", "gated"])
+@pytest.mark.parametrize("case", DEC_CASES, ids=lambda c: c["name"])
+def test_sparse_decode_parity(case, gated):
+    say("decode", case["name"], gated)
+    w = wl.make(len(case["lens"]), case["Hq"], case["Hkv"], case["lens"], case["budget"], case["layout"], 51, DEV,
+                max_blocks=case["mb"])
+    h = Host(w)
+    sel, gates, cnt = wl.random_selection(h.lens, w.n_kv_heads, case["budget"], seed=52)
+    want = oracle.attend(h.q, h.k, h.v, h.bt, w.strides, w.n_kv_heads, h.lens, sel, gates if gated else None,
+                         cnt, SM_SCALE)
+    shape = shape_of(w)
+    n_sel = case["budget"] // 64
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(ops.sparse_decode_workspace_bytes(shape, n_sel), dtype=torch.uint8, device=DEV)
+    t_sel = torch.as_tensor(sel, device=DEV)
+    t_gates = torch.as_tensor(gates, device=DEV) if gated else None
+    ops.sparse_decode(shape, w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens, t_sel, t_gates,
+                      torch.as_tensor(cnt, device=DEV), n_sel, SM_SCALE, out, ws)
+    torch.cuda.synchronize()
+    mx, mean = assert_out_close(bf16_out(out), want)
+    say(f"  max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
+def test_sparse_decode_dense_equivalence_and_nan_rows():
+    # budget >= context: every block is selected and the output equals dense
+    # attention; NaN in the unused rows of the local page must not leak in
+    w = wl.make(2, 8, 2, [1000, 63], 2048, "paged", 53, DEV, max_blocks=16)
+    bt = wl.host(w.block_table)
+    ps, ts, hs = w.strides
+    for pool in (w.k_pool, w.v_pool):
+        flat = pool.view(-1)
+        for s, L in enumerate([1000, 63]):
+            page = int(bt[s, (L - 1) // 64])
+            for kvh in range(2):
+                for r in range(L % 64, 64):
+                    base = page * ps + kvh * hs + r * ts
+                    flat[base:base + 128] = float("nan")
+    h = Host(w)
+    sel, gates, cnt = wl.random_selection(h.lens, 2, 2048, seed=1, full=True)
+    want = oracle.attend(h.q, h.k, h.v, h.bt, w.strides, 2, h.lens, sel, None, cnt, SM_SCALE)
+    shape = shape_of(w)
+    out = torch.empty((2, 8, 128), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(ops.sparse_decode_workspace_bytes(shape, 32), dtype=torch.uint8, device=DEV)
+    ops.sparse_decode(shape, w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens, torch.as_tensor(sel, device=DEV),
+                      None, torch.as_tensor(cnt, device=DEV), 32, SM_SCALE, out, ws)
+    torch.cuda.synchronize()
+    assert_out_close(bf16_out(out), want)
+
+
+# ------------------------------------------------------------------ whole step
+STEP_CASES = [
+    dict(name="tiny_planted", named="tiny", budget=1024),
+    dict(name="tiny_dense", named="tiny", budget=4096),
+    dict(name="small_8b_like", lens=[8192] * 4, Hq=32, Hkv=8, budget=2048, layout="paged", mb=128),
+    dict(name="small_4b_like", lens=[6000, 8192], Hq=32, Hkv=8, budget=2048, layout="contiguous", mb=None),
+    dict(name="small_ragged", lens=[4096, 9000, 6543, 5000], Hq=32, Hkv=8, budget=4096, layout="paged", mb=150),
+    dict(name="small_14b_like", lens=[20000], Hq=40, Hkv=8, budget=2048, layout="paged", mb=320, planted=8),
+]
+
+
+def _step_workload(case):
+    if "named" in case:
+        w = wl.named(case["named"], device=DEV, budget=case["budget"])
+    else:
+        w = wl.make(len(case["lens"]), case["Hq"], case["Hkv"], case["lens"], case["budget"], case["layout"], 61,
+                    DEV, max_blocks=case["mb"], n_planted=case.get("planted", 0), plant_delta=3.0)
+    from planting import plant
+    plant(w)
+    return w
+
+
+@pytest.mark.parametrize("gated", [False, True], ids=["plain", "gated"])
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: c["name"])
+def test_step_parity(case, gated):
+    say("step", case["name"], gated)
+    w = _step_workload(case)
+    h = Host(w)
+    o = oracle_step(h, gated, case["budget"])
+    g = gpu_step(w, gpu_pool(w), gated, case["budget"])
+    ties, skipped = compare_step(h, g, o, gated, case["budget"])
+    say(f"  ties {ties} (outputs of {skipped} not enumerated)")
+    if w.planted is not None:
+        for s in range(w.batch):
+            for k in range(w.n_kv_heads):
+                got = set(g["sel"][s, k, :g["cnt"][s, k]].tolist())
+                assert set(w.planted[s, k].tolist()) <= got
+
+
+# ------------------------------------------------------------------ errors
+def test_invalid_arguments_raise():
+    w = wl.make(1, 4, 1, 300, 1024, "paged", 71, DEV, max_blocks=5)
+    shape = shape_of(w)
+    dec = ops.SparseDecoder(1, 4, 1, 5, w.strides, 1024, w.theta, True, device=DEV)
+    gk = torch.zeros((w.n_pages, 1, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ops.SasError) as ei:
+        ops.gate_topk(shape, w.q, w.w_q, w.w_qnorm, gk, w.block_table, w.seq_lens, w.theta, 1000, dec.sel,
+                      dec.gates, dec.cnt, dec.scores, dec.ws_gate)
+    assert ei.value.status == ops.SAS_ERR_INVALID_ARG
+    small = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ops.SasError) as ei:
+        ops.sparse_decode(shape, w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens, dec.sel, None, dec.cnt, 16,
+                          SM_SCALE, dec.out, small)
+    assert ei.value.status == ops.SAS_ERR_WORKSPACE
+    with pytest.raises(TypeError):
+        ops.sparse_decode(shape, w.q.float(), w.k_pool, w.v_pool, w.block_table, w.seq_lens, dec.sel, None,
+                          dec.cnt, 16, SM_SCALE, dec.out, dec.ws_dec)
