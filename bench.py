@@ -10,9 +10,12 @@ layers (own K/V pools, gate keys, gate weights, queries), as consecutive
 attention calls of a model do, so no step re-reads data a previous step left
 in the 256 MB last-level cache.
 
-Prints one JSON line: queries/s (sequences x steps / wall time of the timed
-steps), the roofline entry of the dominant call (sas_sparse_decode, timed with
-HIP events on its stream) and the oracle timed on a bounded sample on the host.
+Each layer's step (both calls) is captured once into a HIP graph and replayed
+(--no-graph launches eagerly).  Prints one JSON line: queries/s (sequences x
+steps / wall time of the timed steps), the roofline entry of the dominant call
+(sas_sparse_decode, launched back to back --steps times on its stream and
+bracketed by HIP events) and the oracle timed on a bounded sample on the
+host.
 """
 from __future__ import annotations
 
@@ -95,6 +98,8 @@ def main():
     ap.add_argument("--modes", default="plain,gated")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="launch each step eagerly instead of replaying a per-layer HIP graph")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -129,40 +134,61 @@ def main():
     w0 = layers[0]["w"]
     log(f"setup {time.perf_counter() - t_setup:.1f} s")
 
-    stream = torch.cuda.current_stream()
     results = {}
     for mode in args.modes.split(","):
         gated = mode == "gated"
-        dec = ops.SparseDecoder(w0.batch, w0.n_q_heads, w0.n_kv_heads, w0.max_blocks, w0.strides, args.budget,
-                                w0.theta, gated, device=dev)
+        # one decoder (outputs + workspaces) per layer, as a model keeps per-layer state
+        decs = [ops.SparseDecoder(w0.batch, w0.n_q_heads, w0.n_kv_heads, w0.max_blocks, w0.strides, args.budget,
+                                  w0.theta, gated, device=dev) for _ in layers]
 
-        def step(i, ev=None):
-            L = layers[i % len(layers)]
+        def step_eager(l):
+            L, dec = layers[l], decs[l]
             w = L["w"]
-            dec.select(w.q, w.w_q, w.w_qnorm, L["gk"], w.block_table, w.seq_lens)
-            if ev is not None:
-                ev[0].record(stream)
-            dec.attend(w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens)
-            if ev is not None:
-                ev[1].record(stream)
+            dec.step(w.q, w.w_q, w.w_qnorm, L["gk"], w.k_pool, w.v_pool, w.block_table, w.seq_lens)
 
+        for i in range(max(args.warmup, len(layers))):
+            step_eager(i % len(layers))
+        torch.cuda.synchronize()
+        graphs = []
+        if args.graph:
+            # one HIP graph per layer holding sas_gate_topk + sas_sparse_decode
+            for l in range(len(layers)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step_eager(l)
+                graphs.append(g)
+            torch.cuda.synchronize()
+            run_step = lambda i: graphs[i % len(layers)].replay()
+        else:
+            run_step = lambda i: step_eager(i % len(layers))
         for i in range(args.warmup):
-            step(i)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+            run_step(i)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step(i, evs[i])
+            run_step(i)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-        dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+        # the dominant call alone: sas_sparse_decode launched back to back on the
+        # current stream (selections from the steps above), bracketed by HIP events
+        stream = torch.cuda.current_stream()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(len(layers)):
+            L = layers[i]
+            decs[i].attend(L["w"].q, L["w"].k_pool, L["w"].v_pool, L["w"].block_table, L["w"].seq_lens)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(args.steps):
+            l = i % len(layers)
+            w = layers[l]["w"]
+            decs[l].attend(w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        dec_ms = ev0.elapsed_time(ev1) / args.steps
+
         # algorithmic bytes: selected K+V blocks (decode) and every candidate's gate key (gate)
-        cnts = []
-        for l in range(len(layers)):
-            step(l)
-            torch.cuda.synchronize()
-            cnts.append(wl.host(dec.cnt))
+        cnts = [wl.host(d.cnt) for d in decs]
         kv_b = float(np.mean([kv_bytes_per_step(c, 64 * 128 * 2) for c in cnts]))
         gk_b = float(np.mean([gk_bytes_per_step(wl.host(L["w"].seq_lens), w0.n_kv_heads) for L in layers]))
         ms = elapsed * 1e3 / args.steps
@@ -193,8 +219,9 @@ def main():
         "config": {"workload": args.workload, "batch": w0.batch, "context": int(wl.host(w0.seq_lens).max()),
                    "n_q_heads": w0.n_q_heads, "n_kv_heads": w0.n_kv_heads, "head_dim": 128,
                    "budget_tokens": args.budget, "kv_layout": w0.layout, "layers_rotated": len(layers),
-                   "mode": f"{worst} (slower of {','.join(results)})"},
-        "roofline": {"bound": "hbm", "kernel": "sas_sparse_decode (split + merge kernels)",
+                   "mode": f"{worst} (slower of {','.join(results)})",
+                   "launch": "hip graph per layer" if args.graph else "eager"},
+        "roofline": {"bound": "hbm", "kernel": "sas_sparse_decode (decode_kernel)",
                      "achieved": round(r["decode_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(r["decode_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": r["kv_bytes"], "avg_launch_us": round(r["decode_ms"] * 1e3, 2)},

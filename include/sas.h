@@ -85,7 +85,8 @@ typedef struct {
  * For each listed pair i (s = pool_seq[i], c = pool_blk[i]) and every KV head
  * h, over the 64 cached keys of block c (all 64 rows must be written):
  *   p  = [max_t k_t | min_t k_t | mean_t k_t]                     (384 values)
- *   u  = p @ w_k[h]                       w_k: bf16 [Hkv][384][128], no bias
+ *   u[j] = sum_i w_k[h][j][i] * p[i]      w_k: bf16 [Hkv][128][384], no bias
+ *                                         (output-major, a Linear weight)
  *   n  = u / sqrt(mean(u^2) + 1e-6) * w_knorm                    (RMSNorm)
  *   gk = RoPE(n, position 64*c, rope_theta)   rotate-half pairs (i, i+64),
  *        angle position * rope_theta^(-i/64)
@@ -105,8 +106,9 @@ sas_status sas_pool_blocks(const sas_shape *shape, const void *k_pool, const int
  *
  * For sequence s with L = seq_lens[s] >= 1 cached tokens (the current token
  * included) the local block is l = (L-1)/64 and the candidates are c < l.
- *   gate query, per query head h: RoPE(RMSNorm(q[s][h] @ w_q[h]) * w_qnorm,
- *       position L-1)                      w_q: bf16 [Hq][128][128], no bias
+ *   gate query, per query head h: RoPE(RMSNorm(u) * w_qnorm, position L-1)
+ *       with u[j] = sum_d w_q[h][j][d] * q[s][h][d]
+ *                                 w_q: bf16 [Hq][128][128] output-major, no bias
  *   score of c for KV head k: mean over k's query heads of
  *       <gate query, gate_keys[block_table[s][c]][k]> / sqrt(128)
  *   Top-K: the min(budget/64 - 1, l) best candidates under (score descending,
@@ -143,7 +145,9 @@ sas_status sas_gate_topk(const sas_shape *shape, const void *q, const void *w_q,
  * q: bf16 [B][Hq][128]; out: bf16 [B][Hq][128]; sel / gates: [B][Hkv][max_sel]
  * as written by sas_gate_topk with max_sel = budget/64; cnt: [B][Hkv].
  * workspace: device scratch of at least
- * sas_sparse_decode_workspace_bytes(shape, max_sel) bytes.
+ * sas_sparse_decode_workspace_bytes(shape, max_sel) bytes (partial results
+ * when a (sequence, KV head) is split across workgroups; no initial contents
+ * needed).  Calls that overlap in time must not share a workspace.
  */
 size_t sas_sparse_decode_workspace_bytes(const sas_shape *shape, int32_t max_sel);
 sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *k_pool,

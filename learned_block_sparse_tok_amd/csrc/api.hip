@@ -4,7 +4,10 @@
 #include <string.h>
 
 #include "../../include/sas.h"
+#include "sas_device.h"
 #include "sas_kernels.h"
+
+static_assert(SAS_MAX_BLOCKS == SAS_MAX_BLOCKS_DEV, "block-table limit mismatch");
 
 namespace {
 
@@ -155,11 +158,24 @@ sas_status sas_gate_topk(const sas_shape *shape, const void *q, const void *w_q,
   return hip_status(sas::launch_score_topk(tp, shape->batch, s), "sas_gate_topk score/top-k launch");
 }
 
+namespace {
+struct DecodeWorkspace {
+  size_t part_o, part_ml, total;  // byte offsets and size
+};
+DecodeWorkspace decode_workspace(const sas_shape *shape, int32_t max_sel) {
+  sas::DecodeSplit sp = sas::decode_split(shape->batch, shape->n_kv_heads, max_sel);
+  const size_t slots = (size_t)shape->batch * shape->n_q_heads * sp.wg_per_unit;
+  DecodeWorkspace w;
+  w.part_o = 0;
+  w.part_ml = w.part_o + align256(slots * SAS_HEAD_DIM * sizeof(float));
+  w.total = w.part_ml + align256(slots * 2 * sizeof(float));
+  return w;
+}
+}  // namespace
+
 size_t sas_sparse_decode_workspace_bytes(const sas_shape *shape, int32_t max_sel) {
   if (!shape || shape->batch <= 0 || shape->n_kv_heads <= 0 || shape->n_q_heads <= 0 || max_sel <= 0) return 0;
-  sas::DecodeSplit sp = sas::decode_split(shape->batch, shape->n_kv_heads, max_sel);
-  const size_t slots = (size_t)shape->batch * shape->n_q_heads * sp.waves_per_unit;
-  return align256(slots * SAS_HEAD_DIM * sizeof(float)) + align256(slots * 2 * sizeof(float));
+  return decode_workspace(shape, max_sel).total;
 }
 
 sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *k_pool, const void *v_pool,
@@ -178,7 +194,7 @@ sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *
   if (workspace_bytes < need)
     return fail(SAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
   sas::DecodeSplit sp = sas::decode_split(shape->batch, shape->n_kv_heads, max_sel);
-  const size_t slots = (size_t)shape->batch * shape->n_q_heads * sp.waves_per_unit;
+  const DecodeWorkspace wl = decode_workspace(shape, max_sel);
   sas::DecodeParams p;
   p.q = (const uint16_t *)q;
   p.k_pool = (const uint16_t *)k_pool;
@@ -188,8 +204,8 @@ sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *
   p.sel = sel;
   p.cnt = cnt;
   p.gates = gates;
-  p.part_o = (float *)workspace;
-  p.part_ml = (float *)((char *)workspace + align256(slots * SAS_HEAD_DIM * sizeof(float)));
+  p.part_o = (float *)((char *)workspace + wl.part_o);
+  p.part_ml = (float *)((char *)workspace + wl.part_ml);
   p.out = (uint16_t *)out;
   p.page_stride = shape->page_stride;
   p.tok_stride = shape->tok_stride;

@@ -8,145 +8,149 @@
 // Configuration Table").  Each selected block gets a continuous gate.
 //
 // Two kernels:
-//   gate_query_kernel   one workgroup per (query head, 8 sequences): q @ w_q[h]
-//                       with w_q[h] read once per workgroup, RMSNorm, RoPE at
-//                       position L-1 (fp64 angles); fp32 result to workspace.
-//   score_topk_kernel   one workgroup per (sequence, KV head): the mean gate
-//                       query of the group against every candidate's gate key
-//                       (16 lanes x 16 B per key, gathered through the block
-//                       table, DPP row reduction), keys kept in LDS as
-//                       order-preserving uint32; exact Top-K by a 4-pass
-//                       8-bit radix select over the whole workgroup; ties at
-//                       the threshold go to the lowest block indices; the
-//                       selection is written in ascending order by two
-//                       workgroup prefix sums.
+//   gate_query_kernel   one workgroup per (query head, 16 sequences): the
+//                       16 x 128 x 128 projection q . w_q[h]^T on MFMA
+//                       (v_mfma_f32_16x16x32_bf16, w_q rows are 16-byte
+//                       operand loads), then RMSNorm and RoPE at position L-1
+//                       (angles formed and reduced in fp64); fp32 result to
+//                       workspace.
+//   score_topk_kernel   one workgroup per (sequence, KV head): the block-table
+//                       row is staged in LDS, every candidate's gate key is
+//                       gathered at once (16 lanes x 16 B per key, up to 512
+//                       keys in flight per workgroup) and dotted with the mean
+//                       gate query of the group (DPP row reduction); scores
+//                       become order-preserving uint32 keys in the same LDS
+//                       slots; an 8-bit radix select (per-wave histograms, one
+//                       wave scans) finds the threshold, usually in two or
+//                       three passes; the selection is marked in an LDS bitmap
+//                       and one wave writes it out in ascending block order,
+//                       ties at the threshold going to the lowest indices.
 // Bytes per (sequence, KV head): 256 B of gate key per candidate block.
 #include "sas_device.h"
 #include "sas_kernels.h"
 
 namespace sas {
 
-constexpr int kGqSeqs = 8;  // sequences per gate-query workgroup
+constexpr int kGqTile = 16;  // sequences per gate-query workgroup (MFMA rows)
 
-__global__ __launch_bounds__(128) void gate_query_kernel(GateQueryParams p) {
+__device__ __forceinline__ bf16x8 as_bf16x8_g(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__global__ __launch_bounds__(256) void gate_query_kernel(GateQueryParams p) {
   const int h = blockIdx.x;
-  const int s0 = blockIdx.y * kGqSeqs;
-  const int ns = min(kGqSeqs, p.batch - s0);
-  const int j = threadIdx.x;  // output dimension
-  __shared__ float qs[kGqSeqs][kHeadDim];
-  __shared__ float vs[kGqSeqs][kGateDim];
-  __shared__ float red[2][kGqSeqs];
+  const int s0 = blockIdx.y * kGqTile;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  __shared__ float g[kGqTile][kGateDim + 4];
+  __shared__ double inv_freq[kGateDim / 2];
+  if (threadIdx.x < kGateDim / 2) inv_freq[threadIdx.x] = pow(p.theta, -(double)threadIdx.x / 64.0);
 
-  for (int i = 0; i < kGqSeqs; ++i)
-    qs[i][j] = i < ns ? bf16_to_f32(p.q[((int64_t)(s0 + i) * p.n_q_heads + h) * kHeadDim + j]) : 0.f;
+  // A operand: q rows of 16 sequences, lane holds q[s0+row][32ks + 8kg .. +7]
+  bf16x8 qa[4];
+  {
+    const bool valid = s0 + row < p.batch;
+    const uint16_t *qrow = p.q + ((int64_t)(s0 + row) * p.n_q_heads + h) * kHeadDim + 8 * kg;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qa[ks] = as_bf16x8_g(valid ? ld16(qrow + 32 * ks) : u32x4{0, 0, 0, 0});
+  }
+  // B operand: w_q[h] is [j][d]; lane holds w_q[h][16nt + row][32ks + 8kg .. +7]
+  const uint16_t *wh = p.w_q + (int64_t)h * kGateDim * kHeadDim;
+#pragma unroll
+  for (int n2 = 0; n2 < 2; ++n2) {
+    const int nt = 2 * wave + n2;
+    const uint16_t *wrow = wh + (int64_t)(16 * nt + row) * kHeadDim + 8 * kg;
+    u32x4 wb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) wb[ks] = ld16(wrow + 32 * ks);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], as_bf16x8_g(wb[ks]), acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) g[4 * kg + r][16 * nt + row] = acc[r];
+  }
   __syncthreads();
 
-  float acc[kGqSeqs];
+  // RMSNorm + RoPE: thread (sequence t/16, pairs 4(t%16) .. +3 with partners +64)
+  const int sq = threadIdx.x >> 4, q4 = threadIdx.x & 15;
+  float a[4], b[4], ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < kGqSeqs; ++i) acc[i] = 0.f;
-  const uint16_t *w = p.w_q + (int64_t)h * kHeadDim * kGateDim + j;
-#pragma unroll 4
-  for (int d = 0; d < kHeadDim; ++d) {
-    float wv = bf16_to_f32(w[d * kGateDim]);
-#pragma unroll
-    for (int i = 0; i < kGqSeqs; ++i) acc[i] = fmaf(qs[i][d], wv, acc[i]);
+  for (int e = 0; e < 4; ++e) {
+    a[e] = g[sq][4 * q4 + e];
+    b[e] = g[sq][4 * q4 + e + 64];
+    ss += a[e] * a[e] + b[e] * b[e];
   }
-  // RMSNorm: sum of squares over the 128 dimensions (two waves)
+  ss = row16_sum(ss);
+  if (s0 + sq < p.batch) {
+    const float inv = 1.0f / sqrtf(ss * (1.0f / kGateDim) + 1e-6f);
+    const double pos = (double)(p.seq_lens[s0 + sq] - 1);
+    float *dst = p.gq + ((int64_t)(s0 + sq) * p.n_q_heads + h) * kGateDim;
 #pragma unroll
-  for (int i = 0; i < kGqSeqs; ++i) {
-    float ss = wave_sum(acc[i] * acc[i]);
-    if ((j & 63) == 0) red[j >> 6][i] = ss;
-  }
-  __syncthreads();
-  const float wn = p.w_qnorm[j];
-#pragma unroll
-  for (int i = 0; i < kGqSeqs; ++i) {
-    float inv = 1.0f / sqrtf((red[0][i] + red[1][i]) * (1.0f / kGateDim) + 1e-6f);
-    vs[i][j] = acc[i] * inv * wn;
-  }
-  __syncthreads();
-  // RoPE at the current token's position: thread j rotates pair (j & 63) of
-  // the sequences i = j >> 6, (j >> 6) + 2, ...
-  const int pj = j & 63;
-  const double inv_freq = pow(p.theta, -(double)pj / 64.0);
-  for (int i = j >> 6; i < ns; i += 2) {
-    double ang = (double)(p.seq_lens[s0 + i] - 1) * inv_freq;
-    double sn, cs;
-    sincos(ang, &sn, &cs);
-    float cf = (float)cs, sf = (float)sn;
-    float a = vs[i][pj], b = vs[i][pj + 64];
-    float *dst = p.gq + ((int64_t)(s0 + i) * p.n_q_heads + h) * kGateDim;
-    dst[pj] = a * cf - b * sf;
-    dst[pj + 64] = b * cf + a * sf;
+    for (int e = 0; e < 4; ++e) {
+      const int pj = 4 * q4 + e;
+      const float av = a[e] * inv * p.w_qnorm[pj];
+      const float bv = b[e] * inv * p.w_qnorm[pj + 64];
+      float cf, sf;
+      rope_cos_sin(pos, inv_freq[pj], cf, sf);
+      dst[pj] = av * cf - bv * sf;
+      dst[pj + 64] = bv * cf + av * sf;
+    }
   }
 }
 
-// Inclusive prefix sum of one uint32 per thread over a 256-thread workgroup.
-__device__ __forceinline__ uint32_t wg_incl_scan(uint32_t v, uint32_t *tmp /* [4] */) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t n = __shfl_up(v, off, 64);
-    if (lane >= off) v += n;
-  }
-  if (lane == 63) tmp[w] = v;
-  __syncthreads();
-  uint32_t add = 0;
-  for (int k = 0; k < w; ++k) add += tmp[k];
-  __syncthreads();
-  return v + add;
-}
-
-constexpr int kScoreUnroll = 8;  // gate keys in flight per 16-lane group
+constexpr int kKeysInFlight = 32;  // gate keys per 16-lane group per pass (512 per workgroup)
+constexpr int kMaxBitWords = SAS_MAX_BLOCKS_DEV / 32;
 
 __global__ __launch_bounds__(256) void score_topk_kernel(ScoreTopkParams p) {
-  extern __shared__ uint32_t keys[];  // [max_blocks]
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t scan_tmp[4];
-  __shared__ uint32_t sh_prefix, sh_krem;
+  extern __shared__ uint32_t slot[];  // [max_blocks]: block-table row, then score keys
+  __shared__ uint32_t hist[4][256];
+  __shared__ uint32_t selbits[kMaxBitWords], eqbits[kMaxBitWords];
+  __shared__ uint32_t sh_T, sh_krem, sh_full;
 
   const int sk = blockIdx.x;
   const int s = sk / p.n_kv_heads;
   const int kvh = sk - s * p.n_kv_heads;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int lane16 = t & 15, grp = t >> 4;
   const int32_t L = p.seq_lens[s];
-  const int n = (L - 1) / kBlock;  // candidates: blocks before the local block
-  const int k_hist = p.n_sel - 1;
-  const int k_eff = min(k_hist, n);
+  const int n = (L - 1) / kBlock;  // candidates: the blocks before the local block
+  const int k_eff = min(p.n_sel - 1, n);
+  const int nwords = (n + 31) >> 5;
 
-  // mean gate query of this KV head's group, dims 8*lane16 .. +7
+  const int32_t *bt = p.block_table + (int64_t)s * p.max_blocks;
+  for (int c = t; c < n; c += 256) slot[c] = (uint32_t)bt[c];
+  for (int i = t; i < nwords; i += 256) {
+    selbits[i] = 0;
+    eqbits[i] = 0;
+  }
+
+  // mean gate query of the group, dims 8*lane16 .. +7
   float gm[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) gm[e] = 0.f;
   for (int g = 0; g < p.group; ++g) {
     const float *src = p.gq + ((int64_t)s * p.n_q_heads + kvh * p.group + g) * kGateDim + 8 * lane16;
-    f32x4 a = *reinterpret_cast<const f32x4 *>(src);
-    f32x4 b = *reinterpret_cast<const f32x4 *>(src + 4);
-    gm[0] += a.x; gm[1] += a.y; gm[2] += a.z; gm[3] += a.w;
-    gm[4] += b.x; gm[5] += b.y; gm[6] += b.z; gm[7] += b.w;
+    const f32x4 x = *reinterpret_cast<const f32x4 *>(src);
+    const f32x4 y = *reinterpret_cast<const f32x4 *>(src + 4);
+    gm[0] += x.x; gm[1] += x.y; gm[2] += x.z; gm[3] += x.w;
+    gm[4] += y.x; gm[5] += y.y; gm[6] += y.z; gm[7] += y.w;
   }
   const float inv_g = 1.0f / (float)p.group;
 #pragma unroll
   for (int e = 0; e < 8; ++e) gm[e] *= inv_g;
+  __syncthreads();
 
   const float inv_sqrt_dg = 0.08838834764831845f;  // 1/sqrt(128)
-  const int32_t *bt = p.block_table + (int64_t)s * p.max_blocks;
   float *scores = p.scores + (int64_t)sk * p.max_blocks;
-  for (int base = 0; base < n; base += 16 * kScoreUnroll) {
-    u32x4 v[kScoreUnroll];
+  const uint16_t *gkh = p.gate_keys + (int64_t)kvh * kGateDim + 8 * lane16;
+  const int64_t page_stride = (int64_t)p.n_kv_heads * kGateDim;
+  for (int base = 0; base < n; base += 16 * kKeysInFlight) {
+    u32x4 v[kKeysInFlight];
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      int c = base + u * 16 + grp;
-      if (c < n) {
-        int32_t page = bt[c];
-        v[u] = ld16(p.gate_keys + ((int64_t)page * p.n_kv_heads + kvh) * kGateDim + 8 * lane16);
-      } else {
-        v[u] = u32x4{0, 0, 0, 0};
-      }
+    for (int u = 0; u < kKeysInFlight; ++u) {
+      const int c = base + 16 * u + grp;
+      v[u] = c < n ? ld16(gkh + (int64_t)slot[c] * page_stride) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
+    for (int u = 0; u < kKeysInFlight; ++u) {
       float d = gm[0] * bf16_lo(v[u].x);
       d = fmaf(gm[1], bf16_hi(v[u].x), d);
       d = fmaf(gm[2], bf16_lo(v[u].y), d);
@@ -156,10 +160,10 @@ __global__ __launch_bounds__(256) void score_topk_kernel(ScoreTopkParams p) {
       d = fmaf(gm[6], bf16_lo(v[u].w), d);
       d = fmaf(gm[7], bf16_hi(v[u].w), d);
       d = row16_sum(d);
-      int c = base + u * 16 + grp;
+      const int c = base + 16 * u + grp;
       if (lane16 == 0 && c < n) {
-        float sc = d * inv_sqrt_dg;
-        keys[c] = score_key(sc);
+        const float sc = d * inv_sqrt_dg;
+        slot[c] = score_key(sc);
         scores[c] = sc;
       }
     }
@@ -167,57 +171,110 @@ __global__ __launch_bounds__(256) void score_topk_kernel(ScoreTopkParams p) {
   for (int c = n + t; c < p.max_blocks; c += 256) scores[c] = -__builtin_inff();
   __syncthreads();
 
-  // ---- exact Top-K: threshold key T and how many keys equal to T to take
-  uint32_t T = 0, krem = 0;  // k_eff >= n: every candidate (all keys > 0)
+  // ---- threshold: take every key > T, and the krem lowest-index keys == T
+  uint32_t T = 0, krem = 0;  // k_eff >= n: every candidate (all keys are > 0)
   if (k_eff > 0 && k_eff < n) {
     uint32_t prefix = 0, mask = 0;
     krem = (uint32_t)k_eff;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[t] = 0;
+      for (int i = t; i < 4 * 256; i += 256) (&hist[0][0])[i] = 0;
       __syncthreads();
       for (int i = t; i < n; i += 256) {
-        uint32_t k = keys[i];
-        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+        const uint32_t k = slot[i];
+        if ((k & mask) == prefix) atomicAdd(&hist[wave][(k >> shift) & 255u], 1u);
       }
       __syncthreads();
-      const uint32_t dig = 255u - (uint32_t)t;
-      const uint32_t hv = hist[dig];
-      const uint32_t ge = wg_incl_scan(hv, scan_tmp);  // keys with digit >= dig
-      if (ge >= krem && ge - hv < krem) {
-        sh_prefix = prefix | (dig << shift);
-        sh_krem = krem - (ge - hv);
+      if (wave == 0) {
+        // lane l owns digits 255-4l .. 252-4l (descending)
+        uint32_t cnt[4], tot = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = 255 - (4 * lane + e);
+          cnt[e] = hist[0][d] + hist[1][d] + hist[2][d] + hist[3][d];
+          tot += cnt[e];
+        }
+        uint32_t incl = tot;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t y = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += y;
+        }
+        uint32_t run = incl - tot;  // keys in higher digits
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (run < krem && run + cnt[e] >= krem) {
+            const uint32_t d = 255u - (uint32_t)(4 * lane + e);
+            sh_T = prefix | (d << shift);
+            sh_krem = krem - run;
+            sh_full = cnt[e] == krem - run;
+          }
+          run += cnt[e];
+        }
       }
       __syncthreads();
-      prefix = sh_prefix;
+      prefix = sh_T;
       krem = sh_krem;
       mask |= 0xFFu << shift;
+      if (sh_full) {  // the whole bin is taken: every key >= prefix
+        T = prefix - 1u;  // prefix > 0 here: some keys lie below the bin
+        krem = 0;
+        break;
+      }
+      T = prefix;
     }
-    T = prefix;
   }
 
-  // ---- ordered compaction: thread t owns candidates [t*m, t*m + m)
+  // ---- mark the selection, then write it in ascending block order
   const int n_sel = p.n_sel;
   int32_t *sel = p.sel + (int64_t)sk * n_sel;
   float *gates = p.gates ? p.gates + (int64_t)sk * n_sel : nullptr;
   if (k_eff > 0) {
-    const int m = (n + 255) / 256;
-    const int lo = min(n, t * m), hi = min(n, lo + m);
-    uint32_t eq = 0;
-    for (int i = lo; i < hi; ++i) eq += keys[i] == T;
-    uint32_t eq_before = wg_incl_scan(eq, scan_tmp) - eq;
-    uint32_t take = 0;
-    for (int i = lo; i < hi; ++i) {
-      uint32_t k = keys[i];
-      if (k > T || (k == T && eq_before++ < krem)) ++take;
+    for (int i = t; i < n; i += 256) {
+      const uint32_t k = slot[i];
+      if (k > T) atomicOr(&selbits[i >> 5], 1u << (i & 31));
+      else if (k == T && krem > 0) atomicOr(&eqbits[i >> 5], 1u << (i & 31));
     }
-    uint32_t pos = wg_incl_scan(take, scan_tmp) - take;
-    eq_before = wg_incl_scan(eq, scan_tmp) - eq;
-    for (int i = lo; i < hi; ++i) {
-      uint32_t k = keys[i];
-      if (k > T || (k == T && eq_before++ < krem)) {
-        sel[pos] = i;
-        if (gates) gates[pos] = 1.0f / (1.0f + expf(-key_score(k)));
-        ++pos;
+    __syncthreads();
+    if (wave == 0) {
+      const int wpl = (nwords + 63) / 64;
+      const int w0 = min(nwords, lane * wpl), w1 = min(nwords, w0 + wpl);
+      if (krem > 0) {  // the krem lowest-index keys equal to T
+        uint32_t c = 0;
+        for (int i = w0; i < w1; ++i) c += __popc(eqbits[i]);
+        uint32_t incl = c;
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t y = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += y;
+        }
+        uint32_t before = incl - c;
+        for (int i = w0; i < w1 && before < krem; ++i) {
+          uint32_t bits = eqbits[i];
+          while (bits && before < krem) {
+            const uint32_t low = bits & (0u - bits);
+            selbits[i] |= low;
+            bits ^= low;
+            ++before;
+          }
+        }
+      }
+      uint32_t c = 0;
+      for (int i = w0; i < w1; ++i) c += __popc(selbits[i]);
+      uint32_t incl = c;
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      uint32_t pos = incl - c;
+      for (int i = w0; i < w1; ++i) {
+        uint32_t bits = selbits[i];
+        while (bits) {
+          const int b = __ffs(bits) - 1;
+          bits &= bits - 1;
+          const int idx = 32 * i + b;
+          sel[pos] = idx;
+          if (gates) gates[pos] = 1.0f / (1.0f + expf(-key_score(slot[idx])));
+          ++pos;
+        }
       }
     }
   }
@@ -229,13 +286,18 @@ __global__ __launch_bounds__(256) void score_topk_kernel(ScoreTopkParams p) {
 }
 
 hipError_t launch_gate_query(const GateQueryParams &p, hipStream_t st) {
-  dim3 grid((unsigned)p.n_q_heads, (unsigned)((p.batch + kGqSeqs - 1) / kGqSeqs));
-  hipLaunchKernelGGL(gate_query_kernel, grid, dim3(128), 0, st, p);
+  dim3 grid((unsigned)p.n_q_heads, (unsigned)((p.batch + kGqTile - 1) / kGqTile));
+  hipLaunchKernelGGL(gate_query_kernel, grid, dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_score_topk(const ScoreTopkParams &p, int batch, hipStream_t st) {
-  size_t lds = sizeof(uint32_t) * (size_t)p.max_blocks;
+  const size_t lds = sizeof(uint32_t) * (size_t)p.max_blocks;
+  // allow the largest block-table row (64 KiB of LDS); set once per process
+  static const hipError_t attr = hipFuncSetAttribute((const void *)score_topk_kernel,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)(sizeof(uint32_t) * SAS_MAX_BLOCKS_DEV));
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(score_topk_kernel, dim3((unsigned)(batch * p.n_kv_heads)), dim3(256), lds, st, p);
   return hipGetLastError();
 }

@@ -11,10 +11,10 @@
 //   1. a coalesced pass over the 64 x 128 bf16 key rows: per dimension the
 //      running max / min / fp32 sum of 32 rows per thread, halves combined
 //      in LDS -> pooled[384] = [max | min | mean];
-//   2. pooled @ w_k[h] (384 x 128, rows read coalesced), two 192-row halves
-//      per output dimension combined in LDS;
+//   2. the 128 x 384 projection w_k[h] . pooled (w_k rows read as 16-byte
+//      chunks), two 192-input halves per output dimension combined in LDS;
 //   3. wave 0: RMSNorm (eps 1e-6) * w_knorm, rotate-half RoPE at position
-//      64*c with fp64 angles, round to bf16, store.
+//      64*c (angles formed and reduced in fp64), round to bf16, store.
 // Bytes per (block, KV head): 16 KiB of keys read, 256 B of gate key written
 // (w_k is 96 KiB per KV head and stays in L2).
 #include "sas_device.h"
@@ -57,15 +57,26 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
     pooled[2 * kHeadDim + t] = (part[0][2][t] + part[1][2][t]) * (1.0f / kBlock);
   }
   __syncthreads();
-  {  // 2. projection to the gate space
+  {  // 2. projection to the gate space; w_k[h] is [j][i], row j read as 16-byte chunks
     const int j = t & (kGateDim - 1);
     const int half = t >> 7;
-    const uint16_t *w = p.w_k + (int64_t)kvh * 3 * kHeadDim * kGateDim;
+    constexpr int kHalf = 3 * kHeadDim / 2;  // 192 inputs per thread
+    const uint16_t *w = p.w_k + ((int64_t)kvh * kGateDim + j) * 3 * kHeadDim + half * kHalf;
+    u32x4 wv[kHalf / 8];
+#pragma unroll
+    for (int c = 0; c < kHalf / 8; ++c) wv[c] = ld16(w + 8 * c);
     float acc = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < 3 * kHeadDim / 2; ++r) {
-      int row = half * (3 * kHeadDim / 2) + r;
-      acc = fmaf(pooled[row], bf16_to_f32(w[row * kGateDim + j]), acc);
+#pragma unroll
+    for (int c = 0; c < kHalf / 8; ++c) {
+      const float *pp = pooled + half * kHalf + 8 * c;
+      acc = fmaf(pp[0], bf16_lo(wv[c].x), acc);
+      acc = fmaf(pp[1], bf16_hi(wv[c].x), acc);
+      acc = fmaf(pp[2], bf16_lo(wv[c].y), acc);
+      acc = fmaf(pp[3], bf16_hi(wv[c].y), acc);
+      acc = fmaf(pp[4], bf16_lo(wv[c].z), acc);
+      acc = fmaf(pp[5], bf16_hi(wv[c].z), acc);
+      acc = fmaf(pp[6], bf16_lo(wv[c].w), acc);
+      acc = fmaf(pp[7], bf16_hi(wv[c].w), acc);
     }
     upart[half][j] = acc;
   }
@@ -77,10 +88,8 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
     float inv = 1.0f / sqrtf(ss * (1.0f / kGateDim) + 1e-6f);
     a = a * inv * p.w_knorm[t];
     b = b * inv * p.w_knorm[t + 64];
-    double ang = (double)c * kBlock * pow(p.theta, -(double)t / 64.0);
-    double sn, cs;
-    sincos(ang, &sn, &cs);
-    float cf = (float)cs, sf = (float)sn;
+    float cf, sf;
+    rope_cos_sin((double)c * kBlock, pow(p.theta, -(double)t / 64.0), cf, sf);
     float ra = a * cf - b * sf;
     float rb = b * cf + a * sf;
     uint16_t *dst = p.gate_keys + ((int64_t)page * p.n_kv_heads + kvh) * kGateDim;

@@ -9,6 +9,7 @@ constexpr int kHeadDim = 128;
 constexpr int kGateDim = 128;
 constexpr int kBlock = 64;
 constexpr int kMaxGroup = 16;
+#define SAS_MAX_BLOCKS_DEV 16384
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -61,6 +62,16 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 }
 __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+// cos and sin of pos * inv_freq for RoPE.  The angle can reach ~1e5 rad, so
+// it is formed and reduced to [-pi, pi] in fp64 (error ~1e-11 rad); the
+// reduced angle's sine and cosine are then taken in fp32.
+__device__ __forceinline__ void rope_cos_sin(double pos, double inv_freq, float &c, float &s) {
+  const double kTwoPi = 6.283185307179586;
+  const double ang = pos * inv_freq;
+  const double r = ang - rint(ang * (1.0 / kTwoPi)) * kTwoPi;
+  sincosf((float)r, &s, &c);
 }
 
 }  // namespace sas

@@ -44,8 +44,8 @@ struct DecodeParams {
   const uint16_t *k_pool, *v_pool;
   const int32_t *block_table, *seq_lens, *sel, *cnt;
   const float *gates;       // null: plain Top-K mode
-  float *part_o;            // [B*Hkv][W][G][128]
-  float *part_ml;           // [B*Hkv][W][G][2]
+  float *part_o;            // [B*Hkv][wg_per_unit][G][128] unnormalised partial outputs
+  float *part_ml;           // [B*Hkv][wg_per_unit][G][2]   (max, sum) per partial
   uint16_t *out;            // [B][Hq][128]
   int64_t page_stride, tok_stride, head_stride;
   int32_t n_q_heads, n_kv_heads, group, max_blocks, max_sel;

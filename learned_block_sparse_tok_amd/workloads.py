@@ -21,7 +21,8 @@ ragged     64     32/8    4K..64K   paged       4,096   128 append steps
 
 Values: q, K, V ~ N(0, 1) drawn in fp32 and rounded to bf16 (RNE, by torch);
 gate weights ~ N(0, 1/sqrt(fan_in)) drawn in fp32 and rounded to bf16; norm
-weights ones (or 1 + 0.1 N(0,1) when ``random_norms``).  Paged pools are
+weights ones (or 1 + 0.1 N(0,1) when ``random_norms``).  Projection weights
+are stored output-major, as torch Linear weights are.  Paged pools are
 head-major ``[P][Hkv][64][128]`` with a seeded random-permutation block table;
 contiguous caches are ``[B][L][Hkv][128]`` with the identity block table.
 Planted blocks are only *chosen* here (seeded); the direction that plants them
@@ -63,8 +64,8 @@ class Workload:
     k_pool: torch.Tensor  # bf16, layout-dependent
     v_pool: torch.Tensor
     block_table: torch.Tensor  # int32 [B][max_blocks]
-    w_q: torch.Tensor  # bf16 [Hq][128][128]
-    w_k: torch.Tensor  # bf16 [Hkv][384][128]
+    w_q: torch.Tensor  # bf16 [Hq][128 out][128 in]  (torch Linear layout)
+    w_k: torch.Tensor  # bf16 [Hkv][128 out][384 in]
     w_qnorm: torch.Tensor  # f32 [128]
     w_knorm: torch.Tensor  # f32 [128]
     strides: tuple  # (page, token, head) strides of the pools, in elements
@@ -138,7 +139,7 @@ def make(batch: int, n_q_heads: int, n_kv_heads: int, seq_lens, budget: int, lay
     else:
         raise ValueError(layout)
     w_q = _normal_bf16((Hq, HEAD_DIM, GATE_DIM), device, seed, _S_WQ, std=1.0 / math.sqrt(HEAD_DIM))
-    w_k = _normal_bf16((Hkv, 3 * HEAD_DIM, GATE_DIM), device, seed, _S_WK, std=1.0 / math.sqrt(3 * HEAD_DIM))
+    w_k = _normal_bf16((Hkv, GATE_DIM, 3 * HEAD_DIM), device, seed, _S_WK, std=1.0 / math.sqrt(3 * HEAD_DIM))
     if random_norms:
         gn = torch.Generator(device="cpu").manual_seed(seed * 1000 + _S_NORM)
         w_qnorm = (1.0 + 0.1 * torch.randn(GATE_DIM, generator=gn)).to(device)

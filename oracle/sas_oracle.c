@@ -130,9 +130,10 @@ void sas_oracle_pool_stats(const oracle_shape *sh, const uint16_t *k_pool,
   }
 }
 
-/* Gate key of block c, KV head kvh.  READING: a bias-free projection of the
+/* Gate key of block c, KV head kvh.  READING: a bias-free linear map of the
  * 384 pooled values to the 128-wide gate space (one weight matrix per KV head,
- * w_k[kvh][i][j], the shape the pages' gate-parameter counts imply), then
+ * stored output-major like a torch Linear weight, w_k[kvh][j][i]; the shape
+ * the pages' gate-parameter counts imply), then
  * RMSNorm with weight w_knorm, then RoPE at the block's first position 64*c.
  * Output: fp64 before rounding (gk_f64, nullable) and bf16 RNE (gk_bf16). */
 void sas_oracle_gate_key(const oracle_shape *sh, const uint16_t *k_pool,
@@ -141,10 +142,10 @@ void sas_oracle_gate_key(const oracle_shape *sh, const uint16_t *k_pool,
                          double *gk_f64, uint16_t *gk_bf16) {
   double pooled[POOLED], u[GATE_DIM];
   sas_oracle_pool_stats(sh, k_pool, block_table, s, c, kvh, pooled);
-  const uint16_t *w = w_k + (int64_t)kvh * POOLED * GATE_DIM;
+  const uint16_t *w = w_k + (int64_t)kvh * GATE_DIM * POOLED;
   for (int j = 0; j < GATE_DIM; ++j) {
     double acc = 0.0;
-    for (int i = 0; i < POOLED; ++i) acc += pooled[i] * bf16_value(w[i * GATE_DIM + j]);
+    for (int i = 0; i < POOLED; ++i) acc += pooled[i] * bf16_value(w[j * POOLED + i]);
     u[j] = acc;
   }
   sas_oracle_rms_norm(u, w_knorm);
@@ -178,8 +179,9 @@ void sas_oracle_pool_blocks(const oracle_shape *sh, const uint16_t *k_pool,
 /* Stage 2: gate query, block scores, Top-K, gates                     */
 /* ------------------------------------------------------------------ */
 /* Gate query of query head h of sequence s ("query projection Qproj").
- * READING: a bias-free 128x128 projection per query head, w_q[h][d][j], then
- * RMSNorm with w_qnorm, then RoPE at the current token's position L-1. */
+ * READING: a bias-free 128x128 linear map per query head, stored
+ * output-major like a torch Linear weight, w_q[h][j][d], then RMSNorm with
+ * w_qnorm, then RoPE at the current token's position L-1. */
 void sas_oracle_gate_query(const uint16_t *q /* [B][Hq][128] */, int n_q_heads, int s,
                            int h, const uint16_t *w_q, const float *w_qnorm,
                            double theta, int32_t seq_len, double *gq /* [128] */) {
@@ -187,7 +189,7 @@ void sas_oracle_gate_query(const uint16_t *q /* [B][Hq][128] */, int n_q_heads, 
   const uint16_t *w = w_q + (int64_t)h * HEAD_DIM * GATE_DIM;
   for (int j = 0; j < GATE_DIM; ++j) {
     double acc = 0.0;
-    for (int d = 0; d < HEAD_DIM; ++d) acc += bf16_value(qh[d]) * bf16_value(w[d * GATE_DIM + j]);
+    for (int d = 0; d < HEAD_DIM; ++d) acc += bf16_value(qh[d]) * bf16_value(w[j * HEAD_DIM + d]);
     gq[j] = acc;
   }
   sas_oracle_rms_norm(gq, w_qnorm);

@@ -8,9 +8,10 @@ and through them the gate key -- move along a known direction.  READING of the
 points along the direction that raises block c's gate score fastest, i.e. the
 gate query mapped back into key space,
 
-    u = unit( (Wk_max + Wk_min + Wk_mean) @ (w_knorm * R(-64c) gq_mean) ),
+    u = unit( (Wk_max + Wk_min + Wk_mean)^T @ (w_knorm * R(-64c) gq_mean) ),
 
-where Wk_* are the three 128-row slices of the pooled-key projection, R the
+where Wk_* are the three 128-column slices of the pooled-key projection
+(output-major, [128 out][384 in]), R the
 gate RoPE rotation and gq_mean the mean gate query of the KV head's group.
 Its per-component RMS is delta (norm delta * sqrt(128)), matching the
 N(0, 1) scale of the keys.  K stays bf16: the offset is added in fp32 and
@@ -31,8 +32,7 @@ def plant(w: wl.Workload) -> None:
         return
     q = wl.host(w.q)
     w_q = wl.host(w.w_q)
-    w_k = wl.host(w.w_k).reshape(w.n_kv_heads, 3, wl.HEAD_DIM, wl.GATE_DIM)
-    w_k = oracle.bf16_to_f64(w_k)
+    w_k = oracle.bf16_to_f64(wl.host(w.w_k)).reshape(w.n_kv_heads, wl.GATE_DIM, 3, wl.HEAD_DIM)
     wqn = wl.host(w.w_qnorm)
     wkn = wl.host(w.w_knorm).astype(np.float64)
     lens = wl.host(w.seq_lens)
@@ -46,10 +46,10 @@ def plant(w: wl.Workload) -> None:
         for kvh in range(w.n_kv_heads):
             gq = np.mean([oracle.gate_query(q, w_q, wqn, w.theta, int(lens[s]), s, kvh * G + g)
                           for g in range(G)], axis=0)
-            wsum = w_k[kvh].sum(axis=0)  # [128 in][128 gate]
+            wsum = w_k[kvh].sum(axis=1)  # [128 gate][128 key dim]
             for c in w.planted[s, kvh]:
                 t = wkn * oracle.rope(gq, -float(c) * wl.BLOCK, w.theta)
-                u = wsum @ t
+                u = wsum.T @ t
                 u = u / np.linalg.norm(u) * (w.plant_delta * np.sqrt(wl.HEAD_DIM))
                 page = int(bt[s, c])
                 idx = page * ps + kvh * hs + rows[:, None] * ts + dims[None, :]

@@ -56,11 +56,15 @@ def test_pool_blocks_parity(case):
     listed = np.zeros(w.n_pages, bool)
     listed[h.bt[seq, blk]] = True
     assert np.all(gk_g[~listed] == 0)
-    # each key within one bf16 ulp of the oracle's unrounded fp64 key
+    # each key within one bf16 ulp of the oracle's unrounded fp64 key, plus the
+    # fp32 error of the 384-term projection and the norm (keys have RMS ~1,
+    # so an absolute 2e-5 bounds it): near-zero elements have ulps far below
+    # that error and may round either way
     pages = h.bt[seq, blk]
     got = oracle.bf16_to_f64(gk_g[pages])
     ulp = 2.0 ** (np.floor(np.log2(np.abs(f64) + 1e-30)) - 7)
-    assert np.all(np.abs(got - f64) <= ulp), float(np.max(np.abs(got - f64) / ulp))
+    excess = np.abs(got - f64) - ulp
+    assert np.all(excess <= 2e-5), float(excess.max())
     flips = int(np.count_nonzero(gk_g[pages] != gk_o[pages]))
     say(f"  gate-key bf16 values differing from the oracle's rounding: {flips} of {gk_o[pages].size}")
     assert flips <= 0.01 * gk_o[pages].size
@@ -176,7 +180,7 @@ def test_sparse_decode_parity(case, gated):
     shape = shape_of(w)
     n_sel = case["budget"] // 64
     out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.bfloat16, device=DEV)
-    ws = torch.empty(ops.sparse_decode_workspace_bytes(shape, n_sel), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(ops.sparse_decode_workspace_bytes(shape, n_sel), dtype=torch.uint8, device=DEV)
     t_sel = torch.as_tensor(sel, device=DEV)
     t_gates = torch.as_tensor(gates, device=DEV) if gated else None
     ops.sparse_decode(shape, w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens, t_sel, t_gates,
@@ -205,7 +209,7 @@ def test_sparse_decode_dense_equivalence_and_nan_rows():
     want = oracle.attend(h.q, h.k, h.v, h.bt, w.strides, 2, h.lens, sel, None, cnt, SM_SCALE)
     shape = shape_of(w)
     out = torch.empty((2, 8, 128), dtype=torch.bfloat16, device=DEV)
-    ws = torch.empty(ops.sparse_decode_workspace_bytes(shape, 32), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(ops.sparse_decode_workspace_bytes(shape, 32), dtype=torch.uint8, device=DEV)
     ops.sparse_decode(shape, w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens, torch.as_tensor(sel, device=DEV),
                       None, torch.as_tensor(cnt, device=DEV), 32, SM_SCALE, out, ws)
     torch.cuda.synchronize()
@@ -269,3 +273,34 @@ def test_invalid_arguments_raise():
     with pytest.raises(TypeError):
         ops.sparse_decode(shape, w.q.float(), w.k_pool, w.v_pool, w.block_table, w.seq_lens, dec.sel, None,
                           dec.cnt, 16, SM_SCALE, dec.out, dec.ws_dec)
+
+
+# ------------------------------------------------------------------ graphs, determinism
+def test_graph_replay_matches_eager():
+    # both calls captured into one HIP graph: every replay, with eager work and
+    # synchronisations in between, reproduces the eager result bit for bit
+    w = wl.make(4, 32, 8, [8192, 5000, 3000, 8192], 2048, "paged", 81, DEV, max_blocks=128)
+    gk = gpu_pool(w)
+    for gated in (False, True):
+        dec = ops.SparseDecoder(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, 2048, w.theta, gated,
+                                device=DEV)
+        args = (w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, w.block_table, w.seq_lens)
+        dec.step(*args)
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in (dec.sel, dec.gates, dec.cnt, dec.out, dec.scores)]
+        dec.step(*args)  # a second eager call: deterministic
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (dec.sel, dec.gates, dec.cnt, dec.out, dec.scores)):
+            assert torch.equal(a, b)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            dec.step(*args)
+        for r in range(4):
+            dec.out.zero_()
+            dec.sel.fill_(-7)
+            dec.gates.fill_(3.0)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for a, b in zip(ref, (dec.sel, dec.gates, dec.cnt, dec.out, dec.scores)):
+                assert torch.equal(a, b), f"replay {r}"

@@ -113,7 +113,7 @@ def test_pool_stats_direct_scan():
 
 def _torch_gate_key(blk, w_k, wkn, c, theta):
     p = torch.cat([blk.max(0).values, blk.min(0).values, blk.mean(0)])
-    u = p @ w_k
+    u = F.linear(p, w_k)  # w_k: [128 out][384 in]
     u = F.rms_norm(u, (128,), wkn, eps=1e-6)
     z = torch.complex(u[:64], u[64:]) * torch.exp(1j * (c * 64.0) * theta ** (-torch.arange(64, dtype=torch.float64) / 64))
     return torch.cat([z.real, z.imag])
@@ -149,7 +149,7 @@ def test_gate_query_matches_torch():
     for s in range(w.batch):
         pos = float(h.lens[s] - 1)
         for hh in range(w.n_q_heads):
-            v = F.rms_norm(q[s, hh] @ w_q[hh], (128,), wqn, eps=1e-6)
+            v = F.rms_norm(F.linear(q[s, hh], w_q[hh]), (128,), wqn, eps=1e-6)
             z = torch.complex(v[:64], v[64:]) * torch.exp(1j * pos * w.theta ** (-torch.arange(64, dtype=torch.float64) / 64))
             want = torch.cat([z.real, z.imag]).numpy()
             got = oracle.gate_query(h.q, h.w_q, h.wqn, w.theta, int(h.lens[s]), s, hh)
@@ -400,7 +400,7 @@ def _golden_rows(name):
 
 def test_gate_parameter_count_and_checkpoint_size():
     # Gate weights as the oracle consumes them: per query head w_q [128][128],
-    # per KV head w_k [384][128], two 128-wide norm vectors, no biases; stored bf16.
+    # per KV head w_k [128][384], two 128-wide norm vectors, no biases; stored bf16.
     for name, layers, hq, hkv, params_m, ckpt_mib in _golden_rows("gate_params.txt"):
         layers, hq, hkv = int(layers), int(hq), int(hkv)
         per_layer = hq * 128 * 128 + hkv * 384 * 128 + 2 * 128
