@@ -121,15 +121,12 @@ sas_status sas_pool_blocks(const sas_shape *shape, const void *k_pool, const int
  *                 local block (nullable: not written)
  *   cnt    int32  [B][Hkv] number of selected blocks (>= 1)
  *   scores fp32   [B][Hkv][max_blocks] block scores (entries c >= l are -inf)
- * workspace: device scratch of at least sas_gate_topk_workspace_bytes(shape).
  * budget_tokens: a positive multiple of 64, at most 64 * 256.
  */
-size_t sas_gate_topk_workspace_bytes(const sas_shape *shape);
 sas_status sas_gate_topk(const sas_shape *shape, const void *q, const void *w_q,
                          const float *w_qnorm, const void *gate_keys, const int32_t *block_table,
                          const int32_t *seq_lens, double rope_theta, int32_t budget_tokens,
-                         int32_t *sel, float *gates, int32_t *cnt, float *scores,
-                         void *workspace, size_t workspace_bytes, void *stream);
+                         int32_t *sel, float *gates, int32_t *cnt, float *scores, void *stream);
 
 /*
  * sas_sparse_decode -- block-sparse flash-decode over the selected blocks

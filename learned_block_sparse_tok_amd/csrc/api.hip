@@ -1,4 +1,5 @@
 // C ABI of libsas: argument checks, workspace carving, kernel launches.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -105,18 +106,13 @@ sas_status sas_pool_blocks(const sas_shape *shape, const void *k_pool, const int
   return hip_status(sas::launch_pool(p, (hipStream_t)stream), "sas_pool_blocks launch");
 }
 
-size_t sas_gate_topk_workspace_bytes(const sas_shape *shape) {
-  if (!shape || shape->batch <= 0 || shape->n_q_heads <= 0) return 0;
-  return align256((size_t)shape->batch * shape->n_q_heads * SAS_GATE_DIM * sizeof(float));
-}
-
 sas_status sas_gate_topk(const sas_shape *shape, const void *q, const void *w_q, const float *w_qnorm,
                          const void *gate_keys, const int32_t *block_table, const int32_t *seq_lens,
                          double rope_theta, int32_t budget_tokens, int32_t *sel, float *gates, int32_t *cnt,
-                         float *scores, void *workspace, size_t workspace_bytes, void *stream) {
+                         float *scores, void *stream) {
   sas_status st = check_shape(shape, false);
   if (st) return st;
-  if (!q || !w_q || !w_qnorm || !gate_keys || !block_table || !seq_lens || !sel || !cnt || !scores || !workspace)
+  if (!q || !w_q || !w_qnorm || !gate_keys || !block_table || !seq_lens || !sel || !cnt || !scores)
     return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
   if (budget_tokens < SAS_BLOCK || budget_tokens % SAS_BLOCK)
     return fail(SAS_ERR_INVALID_ARG, "budget_tokens (%d) must be a positive multiple of %d", budget_tokens,
@@ -124,38 +120,26 @@ sas_status sas_gate_topk(const sas_shape *shape, const void *q, const void *w_q,
   if (budget_tokens / SAS_BLOCK > 256)
     return fail(SAS_ERR_UNSUPPORTED, "budget_tokens (%d) exceeds %d", budget_tokens, 256 * SAS_BLOCK);
   if (!(rope_theta > 1.0)) return fail(SAS_ERR_INVALID_ARG, "rope_theta must be > 1");
-  if (!aligned16(gate_keys) || !aligned16(workspace))
-    return fail(SAS_ERR_UNSUPPORTED, "gate_keys and workspace must be 16-byte aligned");
-  if (workspace_bytes < sas_gate_topk_workspace_bytes(shape))
-    return fail(SAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
-                sas_gate_topk_workspace_bytes(shape));
-  hipStream_t s = (hipStream_t)stream;
-  sas::GateQueryParams gp;
-  gp.q = (const uint16_t *)q;
-  gp.w_q = (const uint16_t *)w_q;
-  gp.w_qnorm = w_qnorm;
-  gp.seq_lens = seq_lens;
-  gp.gq = (float *)workspace;
-  gp.batch = shape->batch;
-  gp.n_q_heads = shape->n_q_heads;
-  gp.theta = rope_theta;
-  hipError_t e = sas::launch_gate_query(gp, s);
-  if (e != hipSuccess) return hip_status(e, "sas_gate_topk gate-query launch");
-  sas::ScoreTopkParams tp;
-  tp.gq = (const float *)workspace;
-  tp.gate_keys = (const uint16_t *)gate_keys;
-  tp.block_table = block_table;
-  tp.seq_lens = seq_lens;
-  tp.sel = sel;
-  tp.gates = gates;
-  tp.cnt = cnt;
-  tp.scores = scores;
-  tp.n_q_heads = shape->n_q_heads;
-  tp.n_kv_heads = shape->n_kv_heads;
-  tp.group = shape->n_q_heads / shape->n_kv_heads;
-  tp.max_blocks = shape->max_blocks;
-  tp.n_sel = budget_tokens / SAS_BLOCK;
-  return hip_status(sas::launch_score_topk(tp, shape->batch, s), "sas_gate_topk score/top-k launch");
+  if (!aligned16(gate_keys) || !aligned16(w_q))
+    return fail(SAS_ERR_UNSUPPORTED, "gate_keys and w_q must be 16-byte aligned");
+  sas::GateParams p;
+  p.q = (const uint16_t *)q;
+  p.w_q = (const uint16_t *)w_q;
+  p.w_qnorm = w_qnorm;
+  p.gate_keys = (const uint16_t *)gate_keys;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.sel = sel;
+  p.gates = gates;
+  p.cnt = cnt;
+  p.scores = scores;
+  p.n_q_heads = shape->n_q_heads;
+  p.n_kv_heads = shape->n_kv_heads;
+  p.group = shape->n_q_heads / shape->n_kv_heads;
+  p.max_blocks = shape->max_blocks;
+  p.n_sel = budget_tokens / SAS_BLOCK;
+  for (int i = 0; i < SAS_GATE_DIM / 2; ++i) p.inv_freq[i] = pow(rope_theta, -(double)i / (SAS_GATE_DIM / 2));
+  return hip_status(sas::launch_gate_topk(p, shape->batch, (hipStream_t)stream), "sas_gate_topk launch");
 }
 
 namespace {

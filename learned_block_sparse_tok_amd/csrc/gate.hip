@@ -1,4 +1,4 @@
-// Gate query, block scores and per-KV-head Top-K.
+// Gate query, block scores and per-KV-head Top-K, fused in one kernel.
 //
 // SAS scores the KV blocks for each decode query through a query projection
 // ("Qproj") with Q/K normalisation and gate RoPE, and keeps a Top-K of 31
@@ -7,147 +7,154 @@
 // ...", aigc.news, setup paragraph; localmodelwatch "Specifications and
 // Configuration Table").  Each selected block gets a continuous gate.
 //
-// Two kernels:
-//   gate_query_kernel   one workgroup per (query head, 16 sequences): the
-//                       16 x 128 x 128 projection q . w_q[h]^T on MFMA
-//                       (v_mfma_f32_16x16x32_bf16, w_q rows are 16-byte
-//                       operand loads), then RMSNorm and RoPE at position L-1
-//                       (angles formed and reduced in fp64); fp32 result to
-//                       workspace.
-//   score_topk_kernel   one workgroup per (sequence, KV head): the block-table
-//                       row is staged in LDS, every candidate's gate key is
-//                       gathered at once (16 lanes x 16 B per key, up to 512
-//                       keys in flight per workgroup) and dotted with the mean
-//                       gate query of the group (DPP row reduction); scores
-//                       become order-preserving uint32 keys in the same LDS
-//                       slots; an 8-bit radix select (per-wave histograms, one
-//                       wave scans) finds the threshold, usually in two or
-//                       three passes; the selection is marked in an LDS bitmap
-//                       and one wave writes it out in ascending block order,
-//                       ties at the threshold going to the lowest indices.
-// Bytes per (sequence, KV head): 256 B of gate key per candidate block.
+// One 256-thread workgroup per (sequence, KV head):
+//   1. the block-table row is staged in LDS while the group's queries and
+//      query-projection rows arrive (w_q rows as 16-byte loads, from L2);
+//   2. gate queries: q . w_q[h]^T per head, RMSNorm, RoPE at position L-1
+//      (angles formed and reduced in fp64 from host-computed frequencies),
+//      averaged over the group (the KV head's score is the mean of its query
+//      heads' scores);
+//   3. every candidate's gate key is gathered (16 lanes x 16 B per key, up to
+//      512 keys in flight) and dotted with the mean gate query (DPP row
+//      reduction); scores become order-preserving uint32 keys in the LDS
+//      slots the block table occupied;
+//   4. one wave selects: an 8-bit radix select (wave-private histogram, DPP
+//      prefix sums, no workgroup barriers) finds the threshold key, usually
+//      in two or three passes; a second sweep writes the selection in
+//      ascending block order, ties at the threshold going to the lowest
+//      block indices.
+// Bytes per (sequence, KV head): 256 B of gate key per candidate block (the
+// projection weights come from L2: 32 KiB per query head).
 #include "sas_device.h"
 #include "sas_kernels.h"
 
 namespace sas {
 
-constexpr int kGqTile = 16;  // sequences per gate-query workgroup (MFMA rows)
+constexpr int kKeysInFlight = 32;  // gate keys per 16-lane group per pass (512 per workgroup)
 
-__device__ __forceinline__ bf16x8 as_bf16x8_g(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-__global__ __launch_bounds__(256) void gate_query_kernel(GateQueryParams p) {
-  const int h = blockIdx.x;
-  const int s0 = blockIdx.y * kGqTile;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = lane & 15, kg = lane >> 4;
-  __shared__ float g[kGqTile][kGateDim + 4];
-  __shared__ double inv_freq[kGateDim / 2];
-  if (threadIdx.x < kGateDim / 2) inv_freq[threadIdx.x] = pow(p.theta, -(double)threadIdx.x / 64.0);
-
-  // A operand: q rows of 16 sequences, lane holds q[s0+row][32ks + 8kg .. +7]
-  bf16x8 qa[4];
-  {
-    const bool valid = s0 + row < p.batch;
-    const uint16_t *qrow = p.q + ((int64_t)(s0 + row) * p.n_q_heads + h) * kHeadDim + 8 * kg;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qa[ks] = as_bf16x8_g(valid ? ld16(qrow + 32 * ks) : u32x4{0, 0, 0, 0});
-  }
-  // B operand: w_q[h] is [j][d]; lane holds w_q[h][16nt + row][32ks + 8kg .. +7]
-  const uint16_t *wh = p.w_q + (int64_t)h * kGateDim * kHeadDim;
-#pragma unroll
-  for (int n2 = 0; n2 < 2; ++n2) {
-    const int nt = 2 * wave + n2;
-    const uint16_t *wrow = wh + (int64_t)(16 * nt + row) * kHeadDim + 8 * kg;
-    u32x4 wb[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) wb[ks] = ld16(wrow + 32 * ks);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], as_bf16x8_g(wb[ks]), acc, 0, 0, 0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) g[4 * kg + r][16 * nt + row] = acc[r];
-  }
-  __syncthreads();
-
-  // RMSNorm + RoPE: thread (sequence t/16, pairs 4(t%16) .. +3 with partners +64)
-  const int sq = threadIdx.x >> 4, q4 = threadIdx.x & 15;
-  float a[4], b[4], ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    a[e] = g[sq][4 * q4 + e];
-    b[e] = g[sq][4 * q4 + e + 64];
-    ss += a[e] * a[e] + b[e] * b[e];
-  }
-  ss = row16_sum(ss);
-  if (s0 + sq < p.batch) {
-    const float inv = 1.0f / sqrtf(ss * (1.0f / kGateDim) + 1e-6f);
-    const double pos = (double)(p.seq_lens[s0 + sq] - 1);
-    float *dst = p.gq + ((int64_t)(s0 + sq) * p.n_q_heads + h) * kGateDim;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int pj = 4 * q4 + e;
-      const float av = a[e] * inv * p.w_qnorm[pj];
-      const float bv = b[e] * inv * p.w_qnorm[pj + 64];
-      float cf, sf;
-      rope_cos_sin(pos, inv_freq[pj], cf, sf);
-      dst[pj] = av * cf - bv * sf;
-      dst[pj + 64] = bv * cf + av * sf;
-    }
-  }
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then the
+// row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
 }
 
-constexpr int kKeysInFlight = 32;  // gate keys per 16-lane group per pass (512 per workgroup)
-constexpr int kMaxBitWords = SAS_MAX_BLOCKS_DEV / 32;
-
-__global__ __launch_bounds__(256) void score_topk_kernel(ScoreTopkParams p) {
-  extern __shared__ uint32_t slot[];  // [max_blocks]: block-table row, then score keys
-  __shared__ uint32_t hist[4][256];
-  __shared__ uint32_t selbits[kMaxBitWords], eqbits[kMaxBitWords];
-  __shared__ uint32_t sh_T, sh_krem, sh_full;
+__global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
+  // [max(max_blocks, 512)]: block-table row, then score keys
+  extern __shared__ __attribute__((aligned(16))) uint32_t slot[];
+  __shared__ float qs[kMaxGroup][kHeadDim];
+  __shared__ float vs[kMaxGroup][kGateDim];
+  __shared__ float part[4][kGateDim];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[256];
 
   const int sk = blockIdx.x;
   const int s = sk / p.n_kv_heads;
   const int kvh = sk - s * p.n_kv_heads;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane16 = t & 15, grp = t >> 4;
+  const int G = p.group;
   const int32_t L = p.seq_lens[s];
   const int n = (L - 1) / kBlock;  // candidates: the blocks before the local block
   const int k_eff = min(p.n_sel - 1, n);
-  const int nwords = (n + 31) >> 5;
 
+  // ---- 1. issue this thread's first two query-projection rows (independent
+  // of everything else; clamped so the loads are unconditional), stage the
+  // block-table row and the group's queries
+  const int n_out_t = (G * kGateDim - t + 255) >> 8;  // projection outputs of this thread
+  u32x4 wv[2][16];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int o = min(t + 256 * k, G * kGateDim - 1);
+    const uint16_t *w = p.w_q + ((int64_t)kvh * G * kGateDim + o) * kHeadDim;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) wv[k][c] = ld16(w + 8 * c);
+  }
   const int32_t *bt = p.block_table + (int64_t)s * p.max_blocks;
   for (int c = t; c < n; c += 256) slot[c] = (uint32_t)bt[c];
-  for (int i = t; i < nwords; i += 256) {
-    selbits[i] = 0;
-    eqbits[i] = 0;
-  }
-
-  // mean gate query of the group, dims 8*lane16 .. +7
-  float gm[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) gm[e] = 0.f;
-  for (int g = 0; g < p.group; ++g) {
-    const float *src = p.gq + ((int64_t)s * p.n_q_heads + kvh * p.group + g) * kGateDim + 8 * lane16;
-    const f32x4 x = *reinterpret_cast<const f32x4 *>(src);
-    const f32x4 y = *reinterpret_cast<const f32x4 *>(src + 4);
-    gm[0] += x.x; gm[1] += x.y; gm[2] += x.z; gm[3] += x.w;
-    gm[4] += y.x; gm[5] += y.y; gm[6] += y.z; gm[7] += y.w;
-  }
-  const float inv_g = 1.0f / (float)p.group;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) gm[e] *= inv_g;
+  const uint16_t *qg = p.q + ((int64_t)s * p.n_q_heads + kvh * G) * kHeadDim;
+  for (int i = t; i < G * kHeadDim; i += 256) qs[i >> 7][i & 127] = bf16_to_f32(qg[i]);
   __syncthreads();
 
-  const float inv_sqrt_dg = 0.08838834764831845f;  // 1/sqrt(128)
-  float *scores = p.scores + (int64_t)sk * p.max_blocks;
+  // ---- 2. issue the first 512 candidates' gate keys, then compute the gate
+  // queries while they are in flight
   const uint16_t *gkh = p.gate_keys + (int64_t)kvh * kGateDim + 8 * lane16;
   const int64_t page_stride = (int64_t)p.n_kv_heads * kGateDim;
-  for (int base = 0; base < n; base += 16 * kKeysInFlight) {
-    u32x4 v[kKeysInFlight];
+  u32x4 v[kKeysInFlight];
 #pragma unroll
-    for (int u = 0; u < kKeysInFlight; ++u) {
-      const int c = base + 16 * u + grp;
-      v[u] = c < n ? ld16(gkh + (int64_t)slot[c] * page_stride) : u32x4{0, 0, 0, 0};
+  for (int u = 0; u < kKeysInFlight; ++u) {
+    const int c = 16 * u + grp;
+    v[u] = c < n ? ld16(gkh + (int64_t)slot[c] * page_stride) : u32x4{0, 0, 0, 0};
+  }
+  for (int k = 0; k < n_out_t; ++k) {  // v[g][j] = sum_d w_q[h][j][d] q[h][d], output o = g*128 + j
+    const int o = t + 256 * k;
+    const int g = o >> 7, jj = o & 127;
+    u32x4 wk[16];
+    if (k < 2) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) wk[c] = wv[k & 1][c];
+    } else {
+      const uint16_t *w = p.w_q + ((int64_t)kvh * G * kGateDim + o) * kHeadDim;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) wk[c] = ld16(w + 8 * c);
+    }
+    const float *qq = qs[g];
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      acc = fmaf(qq[8 * c + 0], bf16_lo(wk[c].x), acc);
+      acc = fmaf(qq[8 * c + 1], bf16_hi(wk[c].x), acc);
+      acc = fmaf(qq[8 * c + 2], bf16_lo(wk[c].y), acc);
+      acc = fmaf(qq[8 * c + 3], bf16_hi(wk[c].y), acc);
+      acc = fmaf(qq[8 * c + 4], bf16_lo(wk[c].z), acc);
+      acc = fmaf(qq[8 * c + 5], bf16_hi(wk[c].z), acc);
+      acc = fmaf(qq[8 * c + 6], bf16_lo(wk[c].w), acc);
+      acc = fmaf(qq[8 * c + 7], bf16_hi(wk[c].w), acc);
+    }
+    vs[g][jj] = acc;
+  }
+  __syncthreads();
+  {  // RMSNorm + RoPE per head (wave w: heads w, w+4, ...; lane i: pair (i, i+64)); sum over heads
+    float cf, sf;
+    rope_cos_sin((double)(L - 1), p.inv_freq[lane], cf, sf);
+    const float wa = p.w_qnorm[lane], wb = p.w_qnorm[lane + 64];
+    float sa = 0.f, sb = 0.f;
+    for (int g = wave; g < G; g += 4) {
+      const float a = vs[g][lane], b = vs[g][lane + 64];
+      const float inv = 1.0f / sqrtf(wave_sum(a * a + b * b) * (1.0f / kGateDim) + 1e-6f);
+      const float na = a * inv * wa, nb = b * inv * wb;
+      sa += na * cf - nb * sf;
+      sb += nb * cf + na * sf;
+    }
+    part[wave][lane] = sa;
+    part[wave][lane + 64] = sb;
+  }
+  __syncthreads();
+  float gm[8];  // mean gate query of the group, dims 8*lane16 .. +7
+  {
+    const float inv_g = 1.0f / (float)G;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * lane16 + e;
+      gm[e] = (part[0][d] + part[1][d] + part[2][d] + part[3][d]) * inv_g;
+    }
+  }
+
+  // ---- 3. scores of every candidate (first 512 already in flight)
+  const float inv_sqrt_dg = 0.08838834764831845f;  // 1/sqrt(128)
+  float *scores = p.scores + (int64_t)sk * p.max_blocks;
+  for (int base = 0; base < n; base += 16 * kKeysInFlight) {
+    if (base > 0) {
+#pragma unroll
+      for (int u = 0; u < kKeysInFlight; ++u) {
+        const int c = base + 16 * u + grp;
+        v[u] = c < n ? ld16(gkh + (int64_t)slot[c] * page_stride) : u32x4{0, 0, 0, 0};
+      }
     }
 #pragma unroll
     for (int u = 0; u < kKeysInFlight; ++u) {
@@ -170,135 +177,129 @@ __global__ __launch_bounds__(256) void score_topk_kernel(ScoreTopkParams p) {
   }
   for (int c = n + t; c < p.max_blocks; c += 256) scores[c] = -__builtin_inff();
   __syncthreads();
+  if (wave != 0) return;
 
-  // ---- threshold: take every key > T, and the krem lowest-index keys == T
+  // ---- 4. one wave selects.  Keys > T are taken, and the krem lowest-index
+  // keys equal to T.  Lane l sweeps keys [512k + 8l, 512k + 8l + 8); the
+  // first 512 stay in registers across the passes.
+  const int n_sel = p.n_sel;
+  int32_t *sel = p.sel + (int64_t)sk * n_sel;
+  float *gates = p.gates ? p.gates + (int64_t)sk * n_sel : nullptr;
+  uint32_t k0[8];  // keys 8l .. 8l+7 (0 past the candidates: keys are > 0)
+  {
+    const u32x4 a = *reinterpret_cast<const u32x4 *>(&slot[8 * lane]);
+    const u32x4 b = *reinterpret_cast<const u32x4 *>(&slot[8 * lane + 4]);
+    const uint32_t r[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) k0[e] = 8 * lane + e < n ? r[e] : 0u;
+  }
+  auto key_at = [&](int c0, int e) -> uint32_t {  // key c0 + e of this lane's sweep
+    return c0 == 8 * lane ? k0[e] : (c0 + e < n ? slot[c0 + e] : 0u);
+  };
   uint32_t T = 0, krem = 0;  // k_eff >= n: every candidate (all keys are > 0)
   if (k_eff > 0 && k_eff < n) {
     uint32_t prefix = 0, mask = 0;
     krem = (uint32_t)k_eff;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = t; i < 4 * 256; i += 256) (&hist[0][0])[i] = 0;
-      __syncthreads();
-      for (int i = t; i < n; i += 256) {
-        const uint32_t k = slot[i];
-        if ((k & mask) == prefix) atomicAdd(&hist[wave][(k >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (wave == 0) {
-        // lane l owns digits 255-4l .. 252-4l (descending)
-        uint32_t cnt[4], tot = 0;
+      *reinterpret_cast<u32x4 *>(&hist[4 * lane]) = u32x4{0, 0, 0, 0};
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int d = 255 - (4 * lane + e);
-          cnt[e] = hist[0][d] + hist[1][d] + hist[2][d] + hist[3][d];
-          tot += cnt[e];
-        }
-        uint32_t incl = tot;
+      for (int e = 0; e < 8; ++e)
+        if (k0[e] != 0u && (k0[e] & mask) == prefix) atomicAdd(&hist[(k0[e] >> shift) & 255u], 1u);
+      for (int c0 = 8 * lane + 512; c0 < n; c0 += 512) {
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t y = __shfl_up(incl, off, 64);
-          if (lane >= off) incl += y;
-        }
-        uint32_t run = incl - tot;  // keys in higher digits
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (run < krem && run + cnt[e] >= krem) {
-            const uint32_t d = 255u - (uint32_t)(4 * lane + e);
-            sh_T = prefix | (d << shift);
-            sh_krem = krem - run;
-            sh_full = cnt[e] == krem - run;
-          }
-          run += cnt[e];
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t k = key_at(c0, e);
+          if (k != 0u && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
         }
       }
-      __syncthreads();
-      prefix = sh_T;
-      krem = sh_krem;
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      // lane l owns digits 255-4l .. 252-4l (descending)
+      const u32x4 h4 = *reinterpret_cast<const u32x4 *>(&hist[252 - 4 * lane]);
+      const uint32_t cnt[4] = {h4.w, h4.z, h4.y, h4.x};
+      const uint32_t tot = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+      uint32_t run = wave_incl_scan(tot) - tot;  // keys in higher digits
+      int found_e = -1;
+      uint32_t found_krem = 0, found_cnt = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (found_e < 0 && run < krem && run + cnt[e] >= krem) {
+          found_e = e;
+          found_krem = krem - run;
+          found_cnt = cnt[e];
+        }
+        run += cnt[e];
+      }
+      const unsigned long long who = __ballot(found_e >= 0);
+      const int leader = (int)__builtin_ctzll(who);  // exactly one lane finds the digit
+      const uint32_t d = 255u - (uint32_t)(4 * leader + __builtin_amdgcn_readlane(found_e, leader));
+      krem = (uint32_t)__builtin_amdgcn_readlane((int)found_krem, leader);
+      const uint32_t bin_cnt = (uint32_t)__builtin_amdgcn_readlane((int)found_cnt, leader);
+      prefix |= d << shift;
       mask |= 0xFFu << shift;
-      if (sh_full) {  // the whole bin is taken: every key >= prefix
-        T = prefix - 1u;  // prefix > 0 here: some keys lie below the bin
+      if (bin_cnt == krem) {  // the whole bin is taken: every key >= prefix
+        T = prefix - 1u;      // prefix > 0 here: some keys lie below the bin
         krem = 0;
         break;
       }
       T = prefix;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
     }
   }
-
-  // ---- mark the selection, then write it in ascending block order
-  const int n_sel = p.n_sel;
-  int32_t *sel = p.sel + (int64_t)sk * n_sel;
-  float *gates = p.gates ? p.gates + (int64_t)sk * n_sel : nullptr;
   if (k_eff > 0) {
-    for (int i = t; i < n; i += 256) {
-      const uint32_t k = slot[i];
-      if (k > T) atomicOr(&selbits[i >> 5], 1u << (i & 31));
-      else if (k == T && krem > 0) atomicOr(&eqbits[i >> 5], 1u << (i & 31));
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const int wpl = (nwords + 63) / 64;
-      const int w0 = min(nwords, lane * wpl), w1 = min(nwords, w0 + wpl);
-      if (krem > 0) {  // the krem lowest-index keys equal to T
-        uint32_t c = 0;
-        for (int i = w0; i < w1; ++i) c += __popc(eqbits[i]);
-        uint32_t incl = c;
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t y = __shfl_up(incl, off, 64);
-          if (lane >= off) incl += y;
-        }
-        uint32_t before = incl - c;
-        for (int i = w0; i < w1 && before < krem; ++i) {
-          uint32_t bits = eqbits[i];
-          while (bits && before < krem) {
-            const uint32_t low = bits & (0u - bits);
-            selbits[i] |= low;
-            bits ^= low;
-            ++before;
-          }
-        }
+    uint32_t pos_base = 0, eq_base = 0;
+    for (int c0 = 0; c0 < n; c0 += 512) {
+      const int cl = c0 + 8 * lane;
+      uint32_t kk[8];
+      uint32_t n_eq = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kk[e] = key_at(cl, e);
+        n_eq += (krem > 0 && kk[e] == T);
       }
-      uint32_t c = 0;
-      for (int i = w0; i < w1; ++i) c += __popc(selbits[i]);
-      uint32_t incl = c;
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
+      const uint32_t eq_incl = wave_incl_scan(n_eq);
+      uint32_t eq_rank = eq_base + eq_incl - n_eq;  // equal keys before this lane's
+      uint32_t take_mask = 0, n_take = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bool take = kk[e] > T;
+        if (krem > 0 && kk[e] == T) take = eq_rank++ < krem;
+        take_mask |= (uint32_t)take << e;
+        n_take += take;
       }
-      uint32_t pos = incl - c;
-      for (int i = w0; i < w1; ++i) {
-        uint32_t bits = selbits[i];
-        while (bits) {
-          const int b = __ffs(bits) - 1;
-          bits &= bits - 1;
-          const int idx = 32 * i + b;
-          sel[pos] = idx;
-          if (gates) gates[pos] = 1.0f / (1.0f + expf(-key_score(slot[idx])));
+      const uint32_t take_incl = wave_incl_scan(n_take);
+      uint32_t pos = pos_base + take_incl - n_take;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (take_mask >> e & 1u) {
+          sel[pos] = cl + e;
+          if (gates) gates[pos] = 1.0f / (1.0f + __expf(-key_score(kk[e])));
           ++pos;
         }
       }
+      pos_base += (uint32_t)__builtin_amdgcn_readlane((int)take_incl, 63);
+      eq_base += (uint32_t)__builtin_amdgcn_readlane((int)eq_incl, 63);
     }
   }
-  for (int i = k_eff + t; i < n_sel; i += 256) {
+  for (int i = k_eff + lane; i < n_sel; i += 64) {
     sel[i] = i == k_eff ? n : -1;
     if (gates) gates[i] = i == k_eff ? 1.0f : 0.0f;
   }
-  if (t == 0) p.cnt[sk] = k_eff + 1;
+  if (lane == 0) p.cnt[sk] = k_eff + 1;
 }
 
-hipError_t launch_gate_query(const GateQueryParams &p, hipStream_t st) {
-  dim3 grid((unsigned)p.n_q_heads, (unsigned)((p.batch + kGqTile - 1) / kGqTile));
-  hipLaunchKernelGGL(gate_query_kernel, grid, dim3(256), 0, st, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_score_topk(const ScoreTopkParams &p, int batch, hipStream_t st) {
-  const size_t lds = sizeof(uint32_t) * (size_t)p.max_blocks;
+hipError_t launch_gate_topk(const GateParams &p, int batch, hipStream_t st) {
+  // the selecting wave reads the first 512 slots as whole vectors
+  const size_t lds = sizeof(uint32_t) * (size_t)(p.max_blocks > 512 ? (p.max_blocks + 7) / 8 * 8 : 512);
   // allow the largest block-table row (64 KiB of LDS); set once per process
-  static const hipError_t attr = hipFuncSetAttribute((const void *)score_topk_kernel,
+  static const hipError_t attr = hipFuncSetAttribute((const void *)gate_topk_kernel,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      (int)(sizeof(uint32_t) * SAS_MAX_BLOCKS_DEV));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(score_topk_kernel, dim3((unsigned)(batch * p.n_kv_heads)), dim3(256), lds, st, p);
+  hipLaunchKernelGGL(gate_topk_kernel, dim3((unsigned)(batch * p.n_kv_heads)), dim3(256), lds, st, p);
   return hipGetLastError();
 }
 

@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "sas_device.h"
+
 namespace sas {
 
 struct PoolParams {
@@ -18,18 +20,10 @@ struct PoolParams {
   double theta;
 };
 
-struct GateQueryParams {
+struct GateParams {
   const uint16_t *q;        // [B][Hq][128]
-  const uint16_t *w_q;      // [Hq][128][128]
+  const uint16_t *w_q;      // [Hq][128 out][128 in]
   const float *w_qnorm;     // [128]
-  const int32_t *seq_lens;  // [B]
-  float *gq;                // [B][Hq][128] workspace
-  int32_t batch, n_q_heads;
-  double theta;
-};
-
-struct ScoreTopkParams {
-  const float *gq;          // [B][Hq][128]
   const uint16_t *gate_keys;
   const int32_t *block_table, *seq_lens;
   int32_t *sel;
@@ -37,6 +31,7 @@ struct ScoreTopkParams {
   int32_t *cnt;
   float *scores;            // [B][Hkv][max_blocks]
   int32_t n_q_heads, n_kv_heads, group, max_blocks, n_sel;
+  double inv_freq[kGateDim / 2];  // rope_theta^(-i/64)
 };
 
 struct DecodeParams {
@@ -61,8 +56,7 @@ struct DecodeSplit {
 DecodeSplit decode_split(int batch, int n_kv_heads, int max_sel);
 
 hipError_t launch_pool(const PoolParams &p, hipStream_t st);
-hipError_t launch_gate_query(const GateQueryParams &p, hipStream_t st);
-hipError_t launch_score_topk(const ScoreTopkParams &p, int batch, hipStream_t st);
+hipError_t launch_gate_topk(const GateParams &p, int batch, hipStream_t st);
 hipError_t launch_decode(const DecodeParams &p, int batch, hipStream_t st);
 
 }  // namespace sas

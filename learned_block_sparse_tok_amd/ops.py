@@ -39,8 +39,7 @@ _lib = None
 _VP, _I32, _F32, _F64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
 _SIGS = {
     "sas_pool_blocks": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _F64, _VP, _VP]),
-    "sas_gate_topk_workspace_bytes": (_SZ, [_VP]),
-    "sas_gate_topk": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _F64, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "sas_gate_topk": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _F64, _I32, _VP, _VP, _VP, _VP, _VP]),
     "sas_sparse_decode_workspace_bytes": (_SZ, [_VP, _I32]),
     "sas_sparse_decode": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP, _VP, _SZ, _VP]),
     "sas_status_str": (ctypes.c_char_p, [_I32]),
@@ -95,10 +94,6 @@ def make_shape(batch, n_q_heads, n_kv_heads, max_blocks, strides=(0, 0, 0)) -> S
     return SasShape(batch, n_q_heads, n_kv_heads, max_blocks, ps, ts, hs)
 
 
-def gate_topk_workspace_bytes(shape: SasShape) -> int:
-    return int(lib().sas_gate_topk_workspace_bytes(ctypes.byref(shape)))
-
-
 def sparse_decode_workspace_bytes(shape: SasShape, max_sel: int) -> int:
     return int(lib().sas_sparse_decode_workspace_bytes(ctypes.byref(shape), max_sel))
 
@@ -115,14 +110,13 @@ def pool_blocks(shape: SasShape, k_pool, block_table, pool_seq, pool_blk, w_k, w
 
 
 def gate_topk(shape: SasShape, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, theta, budget_tokens,
-              sel, gates, cnt, scores, workspace, stream=None):
+              sel, gates, cnt, scores, stream=None):
     st = lib().sas_gate_topk(ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"), _ptr(w_q, torch.bfloat16, "w_q"),
                              _ptr(w_qnorm, torch.float32, "w_qnorm"), _ptr(gate_keys, torch.bfloat16, "gate_keys"),
                              _ptr(block_table, torch.int32, "block_table"), _ptr(seq_lens, torch.int32, "seq_lens"),
                              float(theta), int(budget_tokens), _ptr(sel, torch.int32, "sel"),
                              _ptr(gates, torch.float32, "gates"), _ptr(cnt, torch.int32, "cnt"),
-                             _ptr(scores, torch.float32, "scores"), _ptr(workspace, None, "workspace"),
-                             workspace.numel() * workspace.element_size(), _stream(stream))
+                             _ptr(scores, torch.float32, "scores"), _stream(stream))
     _check(st, "sas_gate_topk")
 
 
@@ -154,13 +148,12 @@ class SparseDecoder:
         self.cnt = torch.empty((batch, n_kv_heads), dtype=torch.int32, device=dev)
         self.scores = torch.empty((batch, n_kv_heads, max_blocks), dtype=torch.float32, device=dev)
         self.out = torch.empty((batch, n_q_heads, HEAD_DIM), dtype=torch.bfloat16, device=dev)
-        self.ws_gate = torch.empty(gate_topk_workspace_bytes(self.shape), dtype=torch.uint8, device=dev)
         self.ws_dec = torch.empty(sparse_decode_workspace_bytes(self.shape, self.n_sel), dtype=torch.uint8,
                                   device=dev)
 
     def select(self, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, stream=None):
         gate_topk(self.shape, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, self.theta, self.budget,
-                  self.sel, self.gates, self.cnt, self.scores, self.ws_gate, stream)
+                  self.sel, self.gates, self.cnt, self.scores, stream)
 
     def attend(self, q, k_pool, v_pool, block_table, seq_lens, stream=None):
         sparse_decode(self.shape, q, k_pool, v_pool, block_table, seq_lens, self.sel,

@@ -263,7 +263,7 @@ def test_invalid_arguments_raise():
     gk = torch.zeros((w.n_pages, 1, 128), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(ops.SasError) as ei:
         ops.gate_topk(shape, w.q, w.w_q, w.w_qnorm, gk, w.block_table, w.seq_lens, w.theta, 1000, dec.sel,
-                      dec.gates, dec.cnt, dec.scores, dec.ws_gate)
+                      dec.gates, dec.cnt, dec.scores)
     assert ei.value.status == ops.SAS_ERR_INVALID_ARG
     small = torch.empty(16, dtype=torch.uint8, device=DEV)
     with pytest.raises(ops.SasError) as ei:
