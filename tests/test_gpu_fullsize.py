@@ -1,0 +1,190 @@
+"""Parity at the benchmark workloads' full sizes, on sampled sequences.
+
+The GPU runs the whole path over the full batch in the launch configuration
+the benchmark times (sas_pool_blocks over every complete block, then
+sas_gate_topk + sas_sparse_decode through SparseDecoder).  The oracle then
+recomputes sampled sequences one by one from host copies of their pages --
+pooling, gate scores, full sort, dense masked attention -- and the two are
+compared with the same tie accounting as the small-size tests.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_harness import assert_out_close, bf16_out, compare_step, gpu_pool
+from harness import SM_SCALE, Host, oracle_step
+from learned_block_sparse_tok_amd import ops
+from learned_block_sparse_tok_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ops.lib()
+
+
+def sub_workload(w: wl.Workload, seqs) -> wl.Workload:
+    """The sampled sequences as a workload of their own: their pages gathered
+    into a compact pool with an identity block table (host-side input
+    marshalling for the oracle; no arithmetic)."""
+    seqs = list(seqs)
+    bt = w.block_table[seqs]  # [n][max_blocks]
+    pages = bt.reshape(-1).long()
+    per_page = w.k_pool.numel() // w.n_pages
+    k = w.k_pool.view(w.n_pages, per_page).index_select(0, pages)
+    v = w.v_pool.view(w.n_pages, per_page).index_select(0, pages)
+    n = len(seqs)
+    if w.layout == "contiguous":
+        shape = (n, w.max_blocks * wl.BLOCK, w.n_kv_heads, wl.HEAD_DIM)
+    else:
+        shape = (n * w.max_blocks, w.n_kv_heads, wl.BLOCK, wl.HEAD_DIM)
+    return wl.Workload(name=w.name + "_sample", batch=n, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+                       max_blocks=w.max_blocks, layout=w.layout, budget=w.budget, theta=w.theta,
+                       seq_lens=w.seq_lens[seqs].clone(), q=w.q[seqs].clone(), k_pool=k.reshape(shape),
+                       v_pool=v.reshape(shape),
+                       block_table=torch.arange(n * w.max_blocks, dtype=torch.int32, device=w.q.device).reshape(
+                           n, w.max_blocks),
+                       w_q=w.w_q, w_k=w.w_k, w_qnorm=w.w_qnorm, w_knorm=w.w_knorm, strides=w.strides)
+
+
+def gpu_full_step(w, gk, gated, budget):
+    dec = ops.SparseDecoder(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, budget, w.theta, gated,
+                            device=DEV)
+    dec.step(w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, w.block_table, w.seq_lens)
+    torch.cuda.synchronize()
+    return dec
+
+
+def gpu_sample(dec, seqs):
+    seqs = list(seqs)
+    return dict(sel=wl.host(dec.sel)[seqs], gates=wl.host(dec.gates)[seqs], cnt=wl.host(dec.cnt)[seqs],
+                scores=wl.host(dec.scores)[seqs], out=bf16_out(dec.out)[seqs])
+
+
+def check_sampled(w, dec, seqs, gated, budget):
+    sub = sub_workload(w, seqs)
+    h = Host(sub)
+    o = oracle_step(h, gated, budget)
+    g = gpu_sample(dec, seqs)
+    return compare_step(h, g, o, gated, budget)
+
+
+FULL = [
+    ("qwen3_4b", 2048, [0, 5]),
+    ("qwen3_8b", 1024, [0, 17, 31]),
+    ("qwen3_8b", 2048, [3, 30]),
+    ("qwen3_8b", 4096, [11, 26]),
+]
+
+
+@pytest.mark.parametrize("name,budget,seqs", FULL, ids=[f"{n}-{b}" for n, b, _ in FULL])
+def test_full_size_sampled_parity(name, budget, seqs):
+    w = wl.named(name, device=DEV, budget=budget)
+    gk = gpu_pool(w)
+    for gated in (False, True):
+        say(f"{name} budget {budget} {'gated' if gated else 'plain'}: sequences {seqs}")
+        dec = gpu_full_step(w, gk, gated, budget)
+        ties, skipped = check_sampled(w, dec, seqs, gated, budget)
+        say(f"  boundary ties {ties}, unenumerated {skipped}")
+        # every unit of the full batch selected exactly budget/64 blocks
+        assert np.all(wl.host(dec.cnt) == budget // 64)
+        assert np.all(np.isfinite(bf16_out(dec.out)))
+
+
+def test_full_size_qwen3_14b_planted_recall():
+    from planting import plant
+    w = wl.named("qwen3_14b", device=DEV)
+    plant(w)
+    gk = gpu_pool(w)
+    dec = gpu_full_step(w, gk, True, 2048)
+    sel, cnt = wl.host(dec.sel), wl.host(dec.cnt)
+    hit = tot = 0
+    for s in range(w.batch):
+        for k in range(w.n_kv_heads):
+            chosen = set(sel[s, k, :cnt[s, k]].tolist())
+            hit += len(chosen & set(w.planted[s, k].tolist()))
+            tot += w.planted.shape[2]
+    say(f"qwen3_14b planted recall {hit}/{tot}")
+    assert hit == tot
+    ties, skipped = check_sampled(w, dec, [1], True, 2048)
+    say(f"  boundary ties {ties}, unenumerated {skipped}")
+
+
+def test_ragged_incremental_serving():
+    """64 ragged sequences, 128 decode steps: append one token per sequence,
+    pool every block the new token completes, select, attend.  Sampled
+    sequences are checked against the oracle at the first, a middle and the
+    last step; the incrementally pooled gate keys against the oracle's pooling
+    of the same blocks."""
+    steps = 128
+    w = wl.named("ragged", device=DEV, steps=steps)
+    shape = ops.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides)
+    gk = gpu_pool(w)
+    q_new, k_new, v_new = wl.append_rows(w, steps, seed=55)
+    lens = wl.host(w.seq_lens).astype(np.int64)
+    bt = wl.host(w.block_table)
+    ps, ts, hs = w.strides
+    dec = ops.SparseDecoder(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, w.budget, w.theta, True,
+                            device=DEV)
+    kflat, vflat = w.k_pool.view(-1), w.v_pool.view(-1)
+    dims = torch.arange(wl.HEAD_DIM, device=DEV)
+    heads = torch.arange(w.n_kv_heads, device=DEV)
+    pooled_seq, pooled_blk = [], []
+    check_at = {0, steps // 2, steps - 1}
+    for step in range(steps):
+        # append the new token at position L (its K/V rows), then L += 1
+        pos = lens.copy()
+        page = bt[np.arange(w.batch), pos // 64].astype(np.int64)
+        base = torch.as_tensor(page * ps + (pos % 64) * ts, device=DEV)
+        idx = base[:, None, None] + heads[None, :, None] * hs + dims[None, None, :]
+        kflat[idx] = k_new[step]
+        vflat[idx] = v_new[step]
+        lens += 1
+        w.seq_lens.copy_(torch.as_tensor(lens.astype(np.int32)))
+        w.q.copy_(q_new[step])
+        done = np.nonzero(lens % 64 == 0)[0].astype(np.int32)
+        if len(done):
+            blk = (lens[done] // 64 - 1).astype(np.int32)
+            ops.pool_blocks(shape, w.k_pool, w.block_table, torch.as_tensor(done, device=DEV),
+                            torch.as_tensor(blk, device=DEV), w.w_k, w.w_knorm, w.theta, gk)
+            pooled_seq += done.tolist()
+            pooled_blk += blk.tolist()
+        dec.step(w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, w.block_table, w.seq_lens)
+        if step in check_at:
+            torch.cuda.synchronize()
+            seqs = [step % 64, (step * 7 + 3) % 64]
+            say(f"ragged step {step}: sequences {seqs} lengths {lens[seqs].tolist()}")
+            ties, skipped = check_sampled(w, dec, seqs, True, w.budget)
+            say(f"  boundary ties {ties}, unenumerated {skipped}")
+    # incrementally pooled keys vs the oracle's pooling of the same blocks
+    # (their pages gathered into a compact pool; block indices kept, since
+    # they set the gate-key RoPE position)
+    assert len(pooled_seq) > 0
+    torch.cuda.synchronize()
+    n = len(pooled_seq)
+    pages = bt[pooled_seq, pooled_blk].astype(np.int64)
+    per_page = w.k_pool.numel() // w.n_pages
+    k_sub = wl.host(w.k_pool.view(w.n_pages, per_page).index_select(0, torch.as_tensor(pages, device=DEV)))
+    bt_sub = np.zeros((n, w.max_blocks), np.int32)
+    bt_sub[np.arange(n), pooled_blk] = np.arange(n)
+    gk_o = np.zeros((n, w.n_kv_heads, 128), np.uint16)
+    oracle.pool_blocks(k_sub, bt_sub, w.strides, w.n_kv_heads, np.arange(n, dtype=np.int32),
+                       np.array(pooled_blk, np.int32), wl.host(w.w_k), wl.host(w.w_knorm), w.theta, gk_o)
+    got = oracle.bf16_to_f64(wl.host(gk)[pages])
+    want = oracle.bf16_to_f64(gk_o)
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(want) + 1e-30)) - 7)
+    assert np.all(np.abs(got - want) <= ulp + 2e-5)
+    say(f"ragged: {n} blocks pooled incrementally")
