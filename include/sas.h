@@ -78,9 +78,9 @@ typedef struct {
 } sas_shape;
 
 /*
- * sas_pool_blocks -- key-block pooling into gate keys (the pages' "key block
- * pooling max + min + average", "gate hidden size 128", "Q/K normalization",
- * "gate RoPE").
+ * sas_pool_blocks -- key-block pooling into gate keys: pooling by max, min and
+ * average, a 128-wide gate space, Q/K normalisation and gate RoPE (settings
+ * table of the localmodelwatch model page; aigc.news release note).
  *
  * For each listed pair i (s = pool_seq[i], c = pool_blk[i]) and every KV head
  * h, over the 64 cached keys of block c (all 64 rows must be written):
@@ -99,10 +99,10 @@ sas_status sas_pool_blocks(const sas_shape *shape, const void *k_pool, const int
                            void *gate_keys, void *stream);
 
 /*
- * sas_gate_topk -- gate scores and per-KV-head Top-K block selection (the
- * pages' "query projection Qproj", "training Top-K 31 historical blocks", the
- * 1,024 / 2,048 / 4,096-token decode budgets, "continuous gates on selected
- * KV blocks").
+ * sas_gate_topk -- gate scores and per-KV-head Top-K block selection: the
+ * Qproj query projection, a Top-K of 31 historical blocks at the default
+ * 2,048-token budget (1,024 / 4,096 also), and a continuous gate per selected
+ * block (aigc.news release note; localmodelwatch settings table).
  *
  * For sequence s with L = seq_lens[s] >= 1 cached tokens (the current token
  * included) the local block is l = (L-1)/64 and the candidates are c < l.

@@ -1,7 +1,7 @@
 // Gate query, block scores and per-KV-head Top-K, fused in one kernel.
 //
 // SAS scores the KV blocks for each decode query through a query projection
-// ("Qproj") with Q/K normalisation and gate RoPE, and keeps a Top-K of 31
+// (Qproj) with Q/K normalisation and gate RoPE, and keeps a Top-K of 31
 // historical blocks plus the local block for the default 2,048-token budget
 // (1,024 / 4,096 also) ("Tencent released Simple-Attention-Sparsification
 // ...", aigc.news, setup paragraph; localmodelwatch "Specifications and

@@ -9,7 +9,7 @@
  *   "Simple-Attention-Sparsification Text Generation Model: 12GB+ VRAM"
  *   (localmodelwatch, EN) and its Japanese twin.
  * Those passages fix: 64-token KV blocks, Top-K of 31 historical blocks, gate
- * hidden size 128, a query projection "Qproj", key-block pooling by
+ * hidden size 128, a query projection named Qproj, key-block pooling by
  * max + min + average, Q/K normalisation, gate RoPE, and a 2,048-token decode
  * budget (1,024 / 4,096 also usable without retraining).  Everything else is a
  * reading of those passages; each reading is named where it is used.
@@ -32,8 +32,8 @@
 #include <string.h>
 
 #define HEAD_DIM 128   /* Qwen3 attention head dimension */
-#define GATE_DIM 128   /* "gate hidden size 128" */
-#define BLOCK 64       /* "KV block size 64 tokens" */
+#define GATE_DIM 128   /* gate hidden size (settings table) */
+#define BLOCK 64       /* KV block size in tokens (settings table) */
 #define HALF_GATE (GATE_DIM / 2)
 #define POOLED (3 * HEAD_DIM) /* [max | min | mean] */
 #define NORM_EPS 1e-6
@@ -69,7 +69,7 @@ uint16_t sas_oracle_round_bf16(double x) {
 /* ------------------------------------------------------------------ */
 /* Q/K normalisation and gate RoPE                                     */
 /* ------------------------------------------------------------------ */
-/* READING (pages say only "Q/K normalization enabled"): RMSNorm with a
+/* READING (the pages only say that Q/K normalisation is on): RMSNorm with a
  * learned weight vector, eps 1e-6, applied after the projection. */
 void sas_oracle_rms_norm(double *v, const float *w) {
   double ss = 0.0;
@@ -78,7 +78,7 @@ void sas_oracle_rms_norm(double *v, const float *w) {
   for (int i = 0; i < GATE_DIM; ++i) v[i] = v[i] * inv * (double)w[i];
 }
 
-/* READING (pages say only "gate RoPE enabled"): rotate-half rotary embedding
+/* READING (the pages only say that a gate RoPE is on): rotate-half rotary embedding
  * over the 128-wide gate vector; pair (i, i+64) turns by pos * theta^(-i/64). */
 void sas_oracle_rope(double *v, double pos, double theta) {
   for (int i = 0; i < HALF_GATE; ++i) {
@@ -109,8 +109,8 @@ static const uint16_t *kv_row(const oracle_shape *sh, const uint16_t *pool,
 /* Stage 1: key-block pooling -> gate key                              */
 /* ------------------------------------------------------------------ */
 /* Pooled statistics of one 64-token key block of one KV head: per dimension
- * the max, the min and the average over the block's 64 cached keys
- * ("key block pooling max + min + average").  READING: the cached keys as
+ * the max, the min and the average over the block's 64 cached keys (the
+ * pooling the settings table lists).  READING: the cached keys as
  * stored are pooled, and the three statistics are concatenated in the order
  * the pages list them. */
 void sas_oracle_pool_stats(const oracle_shape *sh, const uint16_t *k_pool,
@@ -178,7 +178,7 @@ void sas_oracle_pool_blocks(const oracle_shape *sh, const uint16_t *k_pool,
 /* ------------------------------------------------------------------ */
 /* Stage 2: gate query, block scores, Top-K, gates                     */
 /* ------------------------------------------------------------------ */
-/* Gate query of query head h of sequence s ("query projection Qproj").
+/* Gate query of query head h of sequence s (the Qproj query projection).
  * READING: a bias-free 128x128 linear map per query head, stored
  * output-major like a torch Linear weight, w_q[h][j][d], then RMSNorm with
  * w_qnorm, then RoPE at the current token's position L-1. */
@@ -319,7 +319,7 @@ void sas_oracle_gate_topk(const oracle_shape *sh, const uint16_t *q, const uint1
  * an explicit token mask: token j is kept iff its block j/64 is in the
  * selection (and j <= L-1).  z_j = sm_scale * <q, k_j>; P = softmax(z) over
  * the kept tokens.  Plain mode: o = sum_j P_j v_j.  Gated mode (gates given):
- * READING of "continuous gates on selected blocks" -- each selected block's
+ * READING of the continuous gates on selected blocks -- each selected block's
  * contribution is scaled by its gate, o = sum_j g_{block(j)} P_j v_j, with P
  * normalised over the whole selection.  GQA: head h reads KV head h / G. */
 void sas_oracle_attend_head(const oracle_shape *sh, const uint16_t *q, const uint16_t *k_pool,
