@@ -41,6 +41,9 @@ constexpr int kWaves = 8;  // waves per workgroup, one workgroup per CU
 #ifndef SAS_V_NT
 #define SAS_V_NT 1
 #endif
+#ifndef SAS_K_NT
+#define SAS_K_NT 0
+#endif
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 template <bool kNT>
@@ -117,7 +120,7 @@ __device__ __forceinline__ void attend_block(WaveState &w, BlockRegs &b, const B
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) b.k[t][ks] = ld16_kv<false>(nxt.k + t * lo.k_tile + 64 * ks + lo.k);
+      for (int ks = 0; ks < 4; ++ks) b.k[t][ks] = ld16_kv<SAS_K_NT>(nxt.k + t * lo.k_tile + 64 * ks + lo.k);
   }
   float z[4][4];
   float mx = -__builtin_inff();
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) b.k[t][ks] = ld16_kv<false>(cur.k + t * lo.k_tile + 64 * ks + lo.k);
+      for (int ks = 0; ks < 4; ++ks) b.k[t][ks] = ld16_kv<SAS_K_NT>(cur.k + t * lo.k_tile + 64 * ks + lo.k);
     for (int i = i0; i + 1 < i1; ++i) {
       const BlockSrc nxt = source(i + 1);
       attend_block<kGated, true>(ws, b, cur, nxt, qB, lo, vt, p.scale_log2, g, j, tr_e, tr_q);

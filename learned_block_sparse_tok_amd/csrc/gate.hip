@@ -9,7 +9,8 @@
 //
 // One 256-thread workgroup per (sequence, KV head):
 //   1. the block-table row is staged in LDS while the group's queries and
-//      query-projection rows arrive (w_q rows as 16-byte loads, from L2);
+//      query-projection rows arrive (w_q rows from L2, 16 lanes x 16 B per
+//      row, so every load instruction reads whole rows);
 //   2. gate queries: q . w_q[h]^T per head, RMSNorm, RoPE at position L-1
 //      (angles formed and reduced in fp64 from host-computed frequencies),
 //      averaged over the group (the KV head's score is the mean of its query
@@ -63,26 +64,70 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
   const int n = (L - 1) / kBlock;  // candidates: the blocks before the local block
   const int k_eff = min(p.n_sel - 1, n);
 
-  // ---- 1. issue this thread's first two query-projection rows (independent
-  // of everything else; clamped so the loads are unconditional), stage the
-  // block-table row and the group's queries
-  const int n_out_t = (G * kGateDim - t + 255) >> 8;  // projection outputs of this thread
-  u32x4 wv[2][16];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int o = min(t + 256 * k, G * kGateDim - 1);
-    const uint16_t *w = p.w_q + ((int64_t)kvh * G * kGateDim + o) * kHeadDim;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) wv[k][c] = ld16(w + 8 * c);
-  }
-  const int32_t *bt = p.block_table + (int64_t)s * p.max_blocks;
-  for (int c = t; c < n; c += 256) slot[c] = (uint32_t)bt[c];
+  // ---- 1. issue every load the gate-query phase needs before anything
+  // waits (so in-order load counters never hold it behind the gate-key
+  // gather): the group's queries, the RoPE frequency and norm weights of
+  // this lane's pair, the block-table row (its whole width, independent of
+  // the sequence length), and the query-projection rows.  The G*128
+  // projection outputs are split over the 16 lane-groups, 8G rows each; a
+  // group reads a row as 16 x 16 B (so a wave reads 4 whole rows per load)
+  // and reduces it across the group.
   const uint16_t *qg = p.q + ((int64_t)s * p.n_q_heads + kvh * G) * kHeadDim;
-  for (int i = t; i < G * kHeadDim; i += 256) qs[i >> 7][i & 127] = bf16_to_f32(qg[i]);
-  __syncthreads();
+  const bool has_q = 8 * t < G * kHeadDim;  // G <= 16: one 16-byte piece per thread
+  const u32x4 qpiece = ld16(qg + (has_q ? 8 * t : 0));
+  const double inv_freq = p.inv_freq[lane];
+  const float wqn_a = p.w_qnorm[lane], wqn_b = p.w_qnorm[lane + 64];
+  const int32_t *bt = p.block_table + (int64_t)s * p.max_blocks;
+  constexpr int kBtUnroll = 4;  // rows of up to 1,024 blocks staged without a loop
+  int32_t btv[kBtUnroll];
+#pragma unroll
+  for (int k = 0; k < kBtUnroll; ++k) btv[k] = bt[min(t + 256 * k, p.max_blocks - 1)];
+  constexpr int kRowsInFlight = 32;  // all rows of a group for G <= 4
+  const int rows_per_grp = G * (kGateDim / 16);
+  const int64_t row0 = (int64_t)kvh * G * kGateDim + (int64_t)grp * rows_per_grp;
+  const int64_t row_last = (int64_t)kvh * G * kGateDim + G * kGateDim - 1;
+  const uint16_t *wq_lane = p.w_q + 8 * lane16;
+  u32x4 wv[kRowsInFlight];
+#pragma unroll
+  for (int u = 0; u < kRowsInFlight; ++u) wv[u] = ld16(wq_lane + min(row0 + u, row_last) * kHeadDim);
 
-  // ---- 2. issue the first 512 candidates' gate keys, then compute the gate
-  // queries while they are in flight
+  if (has_q) {
+    float *qd = &qs[0][0] + 8 * t;
+    qd[0] = bf16_lo(qpiece.x); qd[1] = bf16_hi(qpiece.x); qd[2] = bf16_lo(qpiece.y); qd[3] = bf16_hi(qpiece.y);
+    qd[4] = bf16_lo(qpiece.z); qd[5] = bf16_hi(qpiece.z); qd[6] = bf16_lo(qpiece.w); qd[7] = bf16_hi(qpiece.w);
+  }
+#pragma unroll
+  for (int k = 0; k < kBtUnroll; ++k)
+    if (t + 256 * k < p.max_blocks) slot[t + 256 * k] = (uint32_t)btv[k];
+  for (int c = t + 256 * kBtUnroll; c < p.max_blocks; c += 256) slot[c] = (uint32_t)bt[c];
+  lds_barrier();
+
+  // ---- 2. gate queries: v[g][j] = sum_d w_q[h][j][d] q[h][d]
+  auto project_row = [&](const u32x4 &w, int r) {
+    const int o = grp * rows_per_grp + r;
+    const int g = o >> 7, jj = o & 127;
+    const float *qq = qs[g] + 8 * lane16;
+    float acc = qq[0] * bf16_lo(w.x);
+    acc = fmaf(qq[1], bf16_hi(w.x), acc);
+    acc = fmaf(qq[2], bf16_lo(w.y), acc);
+    acc = fmaf(qq[3], bf16_hi(w.y), acc);
+    acc = fmaf(qq[4], bf16_lo(w.z), acc);
+    acc = fmaf(qq[5], bf16_hi(w.z), acc);
+    acc = fmaf(qq[6], bf16_lo(w.w), acc);
+    acc = fmaf(qq[7], bf16_hi(w.w), acc);
+    acc = row16_sum(acc);
+    if (lane16 == 0 && r < rows_per_grp) vs[g][jj] = acc;
+  };
+#pragma unroll
+  for (int u = 0; u < kRowsInFlight; ++u) project_row(wv[u], u);  // rows past the group's own are clamped
+  for (int b0 = kRowsInFlight; b0 < rows_per_grp; b0 += kRowsInFlight) {  // G > 4 only
+#pragma unroll
+    for (int u = 0; u < kRowsInFlight; ++u) wv[u] = ld16(wq_lane + min(row0 + b0 + u, row_last) * kHeadDim);
+#pragma unroll
+    for (int u = 0; u < kRowsInFlight; ++u) project_row(wv[u], b0 + u);
+  }
+  // ---- 2b. issue the first 512 candidates' gate keys; they arrive while
+  // the gate queries are normalised and rotated
   const uint16_t *gkh = p.gate_keys + (int64_t)kvh * kGateDim + 8 * lane16;
   const int64_t page_stride = (int64_t)p.n_kv_heads * kGateDim;
   u32x4 v[kKeysInFlight];
@@ -91,38 +136,11 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
     const int c = 16 * u + grp;
     v[u] = c < n ? ld16(gkh + (int64_t)slot[c] * page_stride) : u32x4{0, 0, 0, 0};
   }
-  for (int k = 0; k < n_out_t; ++k) {  // v[g][j] = sum_d w_q[h][j][d] q[h][d], output o = g*128 + j
-    const int o = t + 256 * k;
-    const int g = o >> 7, jj = o & 127;
-    u32x4 wk[16];
-    if (k < 2) {
-#pragma unroll
-      for (int c = 0; c < 16; ++c) wk[c] = wv[k & 1][c];
-    } else {
-      const uint16_t *w = p.w_q + ((int64_t)kvh * G * kGateDim + o) * kHeadDim;
-#pragma unroll
-      for (int c = 0; c < 16; ++c) wk[c] = ld16(w + 8 * c);
-    }
-    const float *qq = qs[g];
-    float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      acc = fmaf(qq[8 * c + 0], bf16_lo(wk[c].x), acc);
-      acc = fmaf(qq[8 * c + 1], bf16_hi(wk[c].x), acc);
-      acc = fmaf(qq[8 * c + 2], bf16_lo(wk[c].y), acc);
-      acc = fmaf(qq[8 * c + 3], bf16_hi(wk[c].y), acc);
-      acc = fmaf(qq[8 * c + 4], bf16_lo(wk[c].z), acc);
-      acc = fmaf(qq[8 * c + 5], bf16_hi(wk[c].z), acc);
-      acc = fmaf(qq[8 * c + 6], bf16_lo(wk[c].w), acc);
-      acc = fmaf(qq[8 * c + 7], bf16_hi(wk[c].w), acc);
-    }
-    vs[g][jj] = acc;
-  }
-  __syncthreads();
+  lds_barrier();
   {  // RMSNorm + RoPE per head (wave w: heads w, w+4, ...; lane i: pair (i, i+64)); sum over heads
     float cf, sf;
-    rope_cos_sin((double)(L - 1), p.inv_freq[lane], cf, sf);
-    const float wa = p.w_qnorm[lane], wb = p.w_qnorm[lane + 64];
+    rope_cos_sin((double)(L - 1), inv_freq, cf, sf);
+    const float wa = wqn_a, wb = wqn_b;
     float sa = 0.f, sb = 0.f;
     for (int g = wave; g < G; g += 4) {
       const float a = vs[g][lane], b = vs[g][lane + 64];
@@ -134,7 +152,7 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
     part[wave][lane] = sa;
     part[wave][lane + 64] = sb;
   }
-  __syncthreads();
+  lds_barrier();
   float gm[8];  // mean gate query of the group, dims 8*lane16 .. +7
   {
     const float inv_g = 1.0f / (float)G;
@@ -176,7 +194,7 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
     }
   }
   for (int c = n + t; c < p.max_blocks; c += 256) scores[c] = -__builtin_inff();
-  __syncthreads();
+  lds_barrier();
   if (wave != 0) return;
 
   // ---- 4. one wave selects.  Keys > T are taken, and the krem lowest-index

@@ -11,8 +11,8 @@
 //   1. a coalesced pass over the 64 x 128 bf16 key rows: per dimension the
 //      running max / min / fp32 sum of 32 rows per thread, halves combined
 //      in LDS -> pooled[384] = [max | min | mean];
-//   2. the 128 x 384 projection w_k[h] . pooled (w_k rows read as 16-byte
-//      chunks), two 192-input halves per output dimension combined in LDS;
+//   2. the 128 x 384 projection w_k[h] . pooled: 16 lanes per w_k row (every
+//      load instruction reads whole rows), reduced across the lanes (DPP);
 //   3. wave 0: RMSNorm (eps 1e-6) * w_knorm, rotate-half RoPE at position
 //      64*c (angles formed and reduced in fp64), round to bf16, store.
 // Bytes per (block, KV head): 16 KiB of keys read, 256 B of gate key written
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
 
   __shared__ float part[2][3][kHeadDim];
   __shared__ float pooled[3 * kHeadDim];
-  __shared__ float upart[2][kGateDim];
+  __shared__ float upart[1][kGateDim];
 
   {  // 1. pooled statistics
     const int d = t & (kHeadDim - 1);
@@ -57,33 +57,39 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
     pooled[2 * kHeadDim + t] = (part[0][2][t] + part[1][2][t]) * (1.0f / kBlock);
   }
   __syncthreads();
-  {  // 2. projection to the gate space; w_k[h] is [j][i], row j read as 16-byte chunks
-    const int j = t & (kGateDim - 1);
-    const int half = t >> 7;
-    constexpr int kHalf = 3 * kHeadDim / 2;  // 192 inputs per thread
-    const uint16_t *w = p.w_k + ((int64_t)kvh * kGateDim + j) * 3 * kHeadDim + half * kHalf;
-    u32x4 wv[kHalf / 8];
+  {  // 2. projection to the gate space: each 16-lane group owns 8 output rows
+     // j; a lane holds 24 of a row's 384 inputs (three 16-byte chunks), so a
+     // wave reads 4 whole rows per load; the group reduces across its lanes.
+    const int lane16 = t & 15, grp = t >> 4;
+    const uint16_t *w = p.w_k + ((int64_t)kvh * kGateDim + 8 * grp) * 3 * kHeadDim + 8 * lane16;
+    u32x4 wv[8][3];
 #pragma unroll
-    for (int c = 0; c < kHalf / 8; ++c) wv[c] = ld16(w + 8 * c);
-    float acc = 0.f;
+    for (int r = 0; r < 8; ++r)
 #pragma unroll
-    for (int c = 0; c < kHalf / 8; ++c) {
-      const float *pp = pooled + half * kHalf + 8 * c;
-      acc = fmaf(pp[0], bf16_lo(wv[c].x), acc);
-      acc = fmaf(pp[1], bf16_hi(wv[c].x), acc);
-      acc = fmaf(pp[2], bf16_lo(wv[c].y), acc);
-      acc = fmaf(pp[3], bf16_hi(wv[c].y), acc);
-      acc = fmaf(pp[4], bf16_lo(wv[c].z), acc);
-      acc = fmaf(pp[5], bf16_hi(wv[c].z), acc);
-      acc = fmaf(pp[6], bf16_lo(wv[c].w), acc);
-      acc = fmaf(pp[7], bf16_hi(wv[c].w), acc);
+      for (int k = 0; k < 3; ++k) wv[r][k] = ld16(w + r * 3 * kHeadDim + 128 * k);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const float *pp = pooled + 128 * k + 8 * lane16;
+        acc = fmaf(pp[0], bf16_lo(wv[r][k].x), acc);
+        acc = fmaf(pp[1], bf16_hi(wv[r][k].x), acc);
+        acc = fmaf(pp[2], bf16_lo(wv[r][k].y), acc);
+        acc = fmaf(pp[3], bf16_hi(wv[r][k].y), acc);
+        acc = fmaf(pp[4], bf16_lo(wv[r][k].z), acc);
+        acc = fmaf(pp[5], bf16_hi(wv[r][k].z), acc);
+        acc = fmaf(pp[6], bf16_lo(wv[r][k].w), acc);
+        acc = fmaf(pp[7], bf16_hi(wv[r][k].w), acc);
+      }
+      acc = row16_sum(acc);
+      if (lane16 == 0) upart[0][8 * grp + r] = acc;
     }
-    upart[half][j] = acc;
   }
   __syncthreads();
   if (t < 64) {  // 3. norm + RoPE on pairs (t, t+64)
-    float a = upart[0][t] + upart[1][t];
-    float b = upart[0][t + 64] + upart[1][t + 64];
+    float a = upart[0][t];
+    float b = upart[0][t + 64];
     float ss = wave_sum(a * a + b * b);
     float inv = 1.0f / sqrtf(ss * (1.0f / kGateDim) + 1e-6f);
     a = a * inv * p.w_knorm[t];

@@ -52,6 +52,13 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, then s_barrier.  Unlike __syncthreads() it does not wait for
+// outstanding global loads, so gathers issued earlier stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Order-preserving map fp32 -> uint32 for a descending Top-K: NaN ranks as
 // -inf and -0 as +0, so equal keys mean equal scores.
 __device__ __forceinline__ uint32_t score_key(float s) {
