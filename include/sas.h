@@ -12,8 +12,11 @@
  * tokens also, without retraining); attention then reads only those blocks,
  * optionally scaled by continuous gates on the selected blocks.
  *
- * Three calls, in serving order:
+ * Calls, in serving order:
  *   sas_pool_blocks    once per newly completed 64-token block   (pooling)
+ *   sas_append_kv      once per decode step: the new token's K/V rows into
+ *                      the cache, pooling each block this completes
+ *                      (cache write fused with incremental pooling)
  *   sas_gate_topk      once per decode step                      (selection)
  *   sas_sparse_decode  once per decode step                      (attention)
  *
@@ -97,6 +100,28 @@ sas_status sas_pool_blocks(const sas_shape *shape, const void *k_pool, const int
                            const int32_t *pool_seq, const int32_t *pool_blk, int32_t n,
                            const void *w_k, const float *w_knorm, double rope_theta,
                            void *gate_keys, void *stream);
+
+/*
+ * sas_append_kv -- one decode step's cache write fused with incremental
+ * pooling (the 64-token KV blocks and their max + min + average pooling of the
+ * release note and settings table; when a block is pooled is not stated: here
+ * it is pooled by the step that writes its last row).
+ *
+ * For every sequence s, with L = seq_lens[s] >= 1 its length counting the new
+ * token (the token's position is L-1), and every KV head h:
+ *   k_pool[row of token L-1, head h][:] = k_new[s][h][:]
+ *   v_pool[row of token L-1, head h][:] = v_new[s][h][:]
+ * and, when L % 64 == 0, the gate key of block L/64 - 1 (head h) is computed
+ * and stored exactly as sas_pool_blocks computes it (bit-identical), with
+ * the same w_k, w_knorm and rope_theta conventions.
+ * k_new, v_new: bf16 [B][Hkv][128], 16-byte aligned.  Rows are written at
+ * block_table[s][(L-1)/64]; distinct sequences must not share that page.
+ * Everything else in the pools and in gate_keys is left as it is.
+ */
+sas_status sas_append_kv(const sas_shape *shape, const void *k_new, const void *v_new, void *k_pool,
+                         void *v_pool, const int32_t *block_table, const int32_t *seq_lens,
+                         const void *w_k, const float *w_knorm, double rope_theta, void *gate_keys,
+                         void *stream);
 
 /*
  * sas_gate_topk -- gate scores and per-KV-head Top-K block selection: the

@@ -106,6 +106,35 @@ sas_status sas_pool_blocks(const sas_shape *shape, const void *k_pool, const int
   return hip_status(sas::launch_pool(p, (hipStream_t)stream), "sas_pool_blocks launch");
 }
 
+sas_status sas_append_kv(const sas_shape *shape, const void *k_new, const void *v_new, void *k_pool, void *v_pool,
+                         const int32_t *block_table, const int32_t *seq_lens, const void *w_k, const float *w_knorm,
+                         double rope_theta, void *gate_keys, void *stream) {
+  sas_status st = check_shape(shape, true);
+  if (st) return st;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_table || !seq_lens || !w_k || !w_knorm || !gate_keys)
+    return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!(rope_theta > 1.0)) return fail(SAS_ERR_INVALID_ARG, "rope_theta must be > 1");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(gate_keys))
+    return fail(SAS_ERR_UNSUPPORTED, "k_new, v_new, k_pool, v_pool and gate_keys must be 16-byte aligned");
+  sas::AppendParams p;
+  p.k_new = (const uint16_t *)k_new;
+  p.v_new = (const uint16_t *)v_new;
+  p.k_pool = (uint16_t *)k_pool;
+  p.v_pool = (uint16_t *)v_pool;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.w_k = (const uint16_t *)w_k;
+  p.w_knorm = w_knorm;
+  p.gate_keys = (uint16_t *)gate_keys;
+  p.page_stride = shape->page_stride;
+  p.tok_stride = shape->tok_stride;
+  p.head_stride = shape->head_stride;
+  p.n_kv_heads = shape->n_kv_heads;
+  p.max_blocks = shape->max_blocks;
+  p.theta = rope_theta;
+  return hip_status(sas::launch_append(p, shape->batch, (hipStream_t)stream), "sas_append_kv launch");
+}
+
 sas_status sas_gate_topk(const sas_shape *shape, const void *q, const void *w_q, const float *w_qnorm,
                          const void *gate_keys, const int32_t *block_table, const int32_t *seq_lens,
                          double rope_theta, int32_t budget_tokens, int32_t *sel, float *gates, int32_t *cnt,

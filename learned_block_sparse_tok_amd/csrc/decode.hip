@@ -42,7 +42,7 @@ constexpr int kWaves = 8;  // waves per workgroup, one workgroup per CU
 #define SAS_V_NT 1
 #endif
 #ifndef SAS_K_NT
-#define SAS_K_NT 0
+#define SAS_K_NT 1
 #endif
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

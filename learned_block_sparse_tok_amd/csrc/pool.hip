@@ -17,23 +17,26 @@
 //      64*c (angles formed and reduced in fp64), round to bf16, store.
 // Bytes per (block, KV head): 16 KiB of keys read, 256 B of gate key written
 // (w_k is 96 KiB per KV head and stays in L2).
+//
+// The same pooling also runs inside the decode step's cache write
+// (append_kernel): the step that writes a block's last row pools the block
+// there, instead of a second launch re-reading that row.
 #include "sas_device.h"
 #include "sas_kernels.h"
 
 namespace sas {
 
-__global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
-  const int unit = blockIdx.x;
-  const int i = unit / p.n_kv_heads;
-  const int kvh = unit - i * p.n_kv_heads;
-  const int t = threadIdx.x;
-  const int s = p.pool_seq[i], c = p.pool_blk[i];
-  const int32_t page = p.block_table[(int64_t)s * p.max_blocks + c];
-  const uint16_t *kb = p.k_pool + (int64_t)page * p.page_stride + (int64_t)kvh * p.head_stride;
-
+// Gate key of one 64-token key block of one KV head.  Every thread of a
+// 256-thread workgroup calls it (it holds barriers).  kb: the block's row 0 of
+// this head; last_row: when non-null, row 63 is read from there instead of
+// from the pool (the append kernel passes the row it is writing).
+__device__ __forceinline__ void pool_unit(const uint16_t *kb, int64_t tok_stride, const uint16_t *last_row,
+                                          const uint16_t *w_kh, const float *w_knorm, double theta, int c,
+                                          uint16_t *dst) {
   __shared__ float part[2][3][kHeadDim];
   __shared__ float pooled[3 * kHeadDim];
-  __shared__ float upart[1][kGateDim];
+  __shared__ float upart[kGateDim];
+  const int t = threadIdx.x;
 
   {  // 1. pooled statistics
     const int d = t & (kHeadDim - 1);
@@ -41,7 +44,9 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
     float mx = -__builtin_inff(), mn = __builtin_inff(), sum = 0.f;
 #pragma unroll 8
     for (int r = 0; r < kBlock / 2; ++r) {
-      float x = bf16_to_f32(kb[(int64_t)(half * (kBlock / 2) + r) * p.tok_stride + d]);
+      const int row = half * (kBlock / 2) + r;
+      const uint16_t *src = (last_row && row == kBlock - 1) ? last_row : kb + (int64_t)row * tok_stride;
+      float x = bf16_to_f32(src[d]);
       mx = fmaxf(mx, x);
       mn = fminf(mn, x);
       sum += x;
@@ -61,7 +66,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
      // j; a lane holds 24 of a row's 384 inputs (three 16-byte chunks), so a
      // wave reads 4 whole rows per load; the group reduces across its lanes.
     const int lane16 = t & 15, grp = t >> 4;
-    const uint16_t *w = p.w_k + ((int64_t)kvh * kGateDim + 8 * grp) * 3 * kHeadDim + 8 * lane16;
+    const uint16_t *w = w_kh + (int64_t)(8 * grp) * 3 * kHeadDim + 8 * lane16;
     u32x4 wv[8][3];
 #pragma unroll
     for (int r = 0; r < 8; ++r)
@@ -83,30 +88,72 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
         acc = fmaf(pp[7], bf16_hi(wv[r][k].w), acc);
       }
       acc = row16_sum(acc);
-      if (lane16 == 0) upart[0][8 * grp + r] = acc;
+      if (lane16 == 0) upart[8 * grp + r] = acc;
     }
   }
   __syncthreads();
   if (t < 64) {  // 3. norm + RoPE on pairs (t, t+64)
-    float a = upart[0][t];
-    float b = upart[0][t + 64];
+    float a = upart[t];
+    float b = upart[t + 64];
     float ss = wave_sum(a * a + b * b);
     float inv = 1.0f / sqrtf(ss * (1.0f / kGateDim) + 1e-6f);
-    a = a * inv * p.w_knorm[t];
-    b = b * inv * p.w_knorm[t + 64];
+    a = a * inv * w_knorm[t];
+    b = b * inv * w_knorm[t + 64];
     float cf, sf;
-    rope_cos_sin((double)c * kBlock, pow(p.theta, -(double)t / 64.0), cf, sf);
+    rope_cos_sin((double)c * kBlock, pow(theta, -(double)t / 64.0), cf, sf);
     float ra = a * cf - b * sf;
     float rb = b * cf + a * sf;
-    uint16_t *dst = p.gate_keys + ((int64_t)page * p.n_kv_heads + kvh) * kGateDim;
     dst[t] = (uint16_t)f32_to_bf16(ra);
     dst[t + 64] = (uint16_t)f32_to_bf16(rb);
   }
 }
 
+__global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
+  const int unit = blockIdx.x;
+  const int i = unit / p.n_kv_heads;
+  const int kvh = unit - i * p.n_kv_heads;
+  const int s = p.pool_seq[i], c = p.pool_blk[i];
+  const int32_t page = p.block_table[(int64_t)s * p.max_blocks + c];
+  pool_unit(p.k_pool + (int64_t)page * p.page_stride + (int64_t)kvh * p.head_stride, p.tok_stride, nullptr,
+            p.w_k + (int64_t)kvh * kGateDim * 3 * kHeadDim, p.w_knorm, p.theta, c,
+            p.gate_keys + ((int64_t)page * p.n_kv_heads + kvh) * kGateDim);
+}
+
+// One workgroup per (sequence, KV head): threads 0-15 write the new key row,
+// 16-31 the value row (16 bytes each); when the row completes its block
+// (L % 64 == 0) the whole workgroup pools that block, taking row 63 from
+// k_new.  Bytes per (sequence, KV head): 512 B read + 512 B written, plus
+// 16 KiB - 256 B of keys read and 256 B written per completed block.
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+  const int unit = blockIdx.x;
+  const int s = unit / p.n_kv_heads;
+  const int kvh = unit - s * p.n_kv_heads;
+  const int t = threadIdx.x;
+  const int L = p.seq_lens[s];
+  const int pos = L - 1;
+  const int c = pos / kBlock, r = pos - c * kBlock;
+  const int32_t page = p.block_table[(int64_t)s * p.max_blocks + c];
+  const int64_t base = (int64_t)page * p.page_stride + (int64_t)kvh * p.head_stride;
+  const int64_t src = ((int64_t)s * p.n_kv_heads + kvh) * kHeadDim;
+  if (t < 32) {
+    const int lane = t & 15;
+    const uint16_t *from = (t < 16 ? p.k_new : p.v_new) + src + 8 * lane;
+    uint16_t *to = (t < 16 ? p.k_pool : p.v_pool) + base + (int64_t)r * p.tok_stride + 8 * lane;
+    *(u32x4 *)to = ld16(from);
+  }
+  if (L % kBlock == 0)
+    pool_unit(p.k_pool + base, p.tok_stride, p.k_new + src, p.w_k + (int64_t)kvh * kGateDim * 3 * kHeadDim,
+              p.w_knorm, p.theta, c, p.gate_keys + ((int64_t)page * p.n_kv_heads + kvh) * kGateDim);
+}
+
 hipError_t launch_pool(const PoolParams &p, hipStream_t st) {
   if (p.n == 0) return hipSuccess;
   hipLaunchKernelGGL(pool_kernel, dim3((unsigned)(p.n * p.n_kv_heads)), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendParams &p, int batch, hipStream_t st) {
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)(batch * p.n_kv_heads)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

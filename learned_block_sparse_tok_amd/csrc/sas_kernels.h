@@ -20,6 +20,18 @@ struct PoolParams {
   double theta;
 };
 
+struct AppendParams {
+  const uint16_t *k_new, *v_new;  // [B][Hkv][128]
+  uint16_t *k_pool, *v_pool;
+  const int32_t *block_table, *seq_lens;
+  const uint16_t *w_k;            // [Hkv][128][384]
+  const float *w_knorm;           // [128]
+  uint16_t *gate_keys;            // [P][Hkv][128]
+  int64_t page_stride, tok_stride, head_stride;
+  int32_t n_kv_heads, max_blocks;
+  double theta;
+};
+
 struct GateParams {
   const uint16_t *q;        // [B][Hq][128]
   const uint16_t *w_q;      // [Hq][128 out][128 in]
@@ -56,6 +68,7 @@ struct DecodeSplit {
 DecodeSplit decode_split(int batch, int n_kv_heads, int max_sel);
 
 hipError_t launch_pool(const PoolParams &p, hipStream_t st);
+hipError_t launch_append(const AppendParams &p, int batch, hipStream_t st);
 hipError_t launch_gate_topk(const GateParams &p, int batch, hipStream_t st);
 hipError_t launch_decode(const DecodeParams &p, int batch, hipStream_t st);
 

@@ -39,6 +39,7 @@ _lib = None
 _VP, _I32, _F32, _F64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
 _SIGS = {
     "sas_pool_blocks": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _F64, _VP, _VP]),
+    "sas_append_kv": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F64, _VP, _VP]),
     "sas_gate_topk": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _F64, _I32, _VP, _VP, _VP, _VP, _VP]),
     "sas_sparse_decode_workspace_bytes": (_SZ, [_VP, _I32]),
     "sas_sparse_decode": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP, _VP, _SZ, _VP]),
@@ -107,6 +108,19 @@ def pool_blocks(shape: SasShape, k_pool, block_table, pool_seq, pool_blk, w_k, w
                                n, _ptr(w_k, torch.bfloat16, "w_k"), _ptr(w_knorm, torch.float32, "w_knorm"),
                                float(theta), _ptr(gate_keys, torch.bfloat16, "gate_keys"), _stream(stream))
     _check(st, "sas_pool_blocks")
+
+
+def append_kv(shape: SasShape, k_new, v_new, k_pool, v_pool, block_table, seq_lens, w_k, w_knorm, theta,
+              gate_keys, stream=None):
+    """The new token's K/V rows ([B][Hkv][128]) into the pools at position
+    seq_lens[s]-1; blocks this completes are pooled into gate_keys."""
+    st = lib().sas_append_kv(ctypes.byref(shape), _ptr(k_new, torch.bfloat16, "k_new"),
+                             _ptr(v_new, torch.bfloat16, "v_new"), _ptr(k_pool, torch.bfloat16, "k_pool"),
+                             _ptr(v_pool, torch.bfloat16, "v_pool"), _ptr(block_table, torch.int32, "block_table"),
+                             _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(w_k, torch.bfloat16, "w_k"),
+                             _ptr(w_knorm, torch.float32, "w_knorm"), float(theta),
+                             _ptr(gate_keys, torch.bfloat16, "gate_keys"), _stream(stream))
+    _check(st, "sas_append_kv")
 
 
 def gate_topk(shape: SasShape, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, theta, budget_tokens,

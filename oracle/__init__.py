@@ -120,6 +120,24 @@ def pool_blocks(k_pool, block_table, strides, n_kv_heads, pool_seq, pool_blk, w_
     return f64
 
 
+def append_kv(k_pool, v_pool, block_table, strides, n_kv_heads, seq_lens, k_new, v_new, w_k, w_knorm,
+              theta, gate_keys):
+    """One decode step's cache write + incremental pooling, in place: rows
+    k_new / v_new ([B][Hkv][128]) go to position seq_lens[s]-1 of each
+    sequence; blocks that this completes are pooled into gate_keys.  Returns
+    the (sequence, block) pairs pooled, as two int32 arrays."""
+    B, max_blocks = block_table.shape
+    sh = _shape(B, n_kv_heads, n_kv_heads, max_blocks, strides)
+    seq_lens = np.ascontiguousarray(seq_lens, np.int32)
+    done_seq = np.zeros(B, np.int32)
+    done_blk = np.zeros(B, np.int32)
+    n = _load().sas_oracle_append_kv(ctypes.byref(sh), _p(k_pool), _p(v_pool), _p(block_table), _p(seq_lens),
+                                     _p(np.ascontiguousarray(k_new)), _p(np.ascontiguousarray(v_new)), _p(w_k),
+                                     _p(w_knorm), ctypes.c_double(theta), _p(gate_keys), _p(done_seq),
+                                     _p(done_blk))
+    return done_seq[:n].copy(), done_blk[:n].copy()
+
+
 def gate_query(q, w_q, w_qnorm, theta, seq_len, s, h) -> np.ndarray:
     out = np.zeros(GATE_DIM, np.float64)
     _load().sas_oracle_gate_query(_p(q), ctypes.c_int(q.shape[1]), ctypes.c_int(s), ctypes.c_int(h),

@@ -175,6 +175,43 @@ void sas_oracle_pool_blocks(const oracle_shape *sh, const uint16_t *k_pool,
   }
 }
 
+/* One decode step's cache write followed by incremental pooling.  Each
+ * sequence's current token sits at position L-1, L = seq_lens[s] >= 1 the
+ * length with that token counted; its key and value rows (k_new / v_new,
+ * [B][Hkv][128]) are written there for every KV head.  A sequence whose length
+ * reaches a multiple of 64 has just completed block L/64 - 1, and that block
+ * is pooled into its gate key exactly as sas_oracle_pool_blocks does.
+ * READING: the pages pool each full 64-token key block (release note and
+ * settings table); they say nothing of when, so a block is pooled once, at the
+ * step that writes its last row.  Returns the number of blocks pooled; their
+ * (sequence, block) pairs go to done_seq / done_blk ([B] each). */
+int32_t sas_oracle_append_kv(const oracle_shape *sh, uint16_t *k_pool, uint16_t *v_pool,
+                             const int32_t *block_table, const int32_t *seq_lens,
+                             const uint16_t *k_new, const uint16_t *v_new,
+                             const uint16_t *w_k, const float *w_knorm, double theta,
+                             uint16_t *gate_keys, int32_t *done_seq, int32_t *done_blk) {
+  int32_t n_done = 0;
+  for (int s = 0; s < sh->batch; ++s) {
+    const int pos = seq_lens[s] - 1;
+    for (int kvh = 0; kvh < sh->n_kv_heads; ++kvh) {
+      const int64_t off = kv_row(sh, k_pool, block_table, s, kvh, pos) - k_pool;
+      const int64_t src = ((int64_t)s * sh->n_kv_heads + kvh) * HEAD_DIM;
+      for (int d = 0; d < HEAD_DIM; ++d) {
+        k_pool[off + d] = k_new[src + d];
+        v_pool[off + d] = v_new[src + d];
+      }
+    }
+    if (seq_lens[s] % BLOCK == 0) {
+      done_seq[n_done] = s;
+      done_blk[n_done] = seq_lens[s] / BLOCK - 1;
+      ++n_done;
+    }
+  }
+  sas_oracle_pool_blocks(sh, k_pool, block_table, done_seq, done_blk, n_done, w_k, w_knorm,
+                         theta, gate_keys, NULL);
+  return n_done;
+}
+
 /* ------------------------------------------------------------------ */
 /* Stage 2: gate query, block scores, Top-K, gates                     */
 /* ------------------------------------------------------------------ */

@@ -93,6 +93,20 @@ def test_pool_rejects_bad_arguments_and_accepts_empty_list(lib):
     assert lib.sas_pool_blocks(ctypes.byref(sh), None, None, None, None, 0, None, None, 1e6, None, None) == ops.SAS_OK
 
 
+def test_append_rejects_bad_arguments(lib):
+    sh = _shape()
+
+    def call(sh=sh, k_new=FAKE, theta=1e6, pool=FAKE):
+        return lib.sas_append_kv(ctypes.byref(sh), k_new, FAKE, pool, FAKE, FAKE, FAKE, FAKE, FAKE, theta, FAKE,
+                                 None)
+
+    assert call(k_new=None) == ops.SAS_ERR_INVALID_ARG
+    assert call(theta=1.0) == ops.SAS_ERR_INVALID_ARG
+    assert call(pool=ctypes.c_void_p(4096 + 2)) == ops.SAS_ERR_UNSUPPORTED  # not 16-byte aligned
+    assert call(sh=_shape(strides=(2 * 64 * 128, 0, 64 * 128))) == ops.SAS_ERR_INVALID_ARG
+    assert call(sh=_shape(n_kv_heads=3)) == ops.SAS_ERR_INVALID_ARG  # 8 query heads not a multiple of 3
+
+
 def test_workspace_sizes(lib):
     # 256 (sequence, KV head) units fill the CUs: one workgroup each, no partials
     sh = _shape(batch=32, n_q_heads=32, n_kv_heads=8, max_blocks=512)

@@ -123,12 +123,15 @@ def test_full_size_qwen3_14b_planted_recall():
     say(f"  boundary ties {ties}, unenumerated {skipped}")
 
 
-def test_ragged_incremental_serving():
+@pytest.mark.parametrize("fused", [False, True], ids=["scatter_then_pool", "append_kv"])
+def test_ragged_incremental_serving(fused):
     """64 ragged sequences, 128 decode steps: append one token per sequence,
-    pool every block the new token completes, select, attend.  Sampled
-    sequences are checked against the oracle at the first, a middle and the
-    last step; the incrementally pooled gate keys against the oracle's pooling
-    of the same blocks."""
+    pool every block the new token completes, select, attend -- the append
+    either as a tensor scatter followed by sas_pool_blocks over the completed
+    blocks, or as the fused sas_append_kv.  Sampled sequences are checked
+    against the oracle at the first, a middle and the last step; the
+    incrementally pooled gate keys against the oracle's pooling of the same
+    blocks."""
     steps = 128
     w = wl.named("ragged", device=DEV, steps=steps)
     shape = ops.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides)
@@ -145,23 +148,27 @@ def test_ragged_incremental_serving():
     pooled_seq, pooled_blk = [], []
     check_at = {0, steps // 2, steps - 1}
     for step in range(steps):
-        # append the new token at position L (its K/V rows), then L += 1
+        # the new token goes to position L (its K/V rows), then L += 1
         pos = lens.copy()
-        page = bt[np.arange(w.batch), pos // 64].astype(np.int64)
-        base = torch.as_tensor(page * ps + (pos % 64) * ts, device=DEV)
-        idx = base[:, None, None] + heads[None, :, None] * hs + dims[None, None, :]
-        kflat[idx] = k_new[step]
-        vflat[idx] = v_new[step]
         lens += 1
         w.seq_lens.copy_(torch.as_tensor(lens.astype(np.int32)))
         w.q.copy_(q_new[step])
         done = np.nonzero(lens % 64 == 0)[0].astype(np.int32)
-        if len(done):
-            blk = (lens[done] // 64 - 1).astype(np.int32)
-            ops.pool_blocks(shape, w.k_pool, w.block_table, torch.as_tensor(done, device=DEV),
-                            torch.as_tensor(blk, device=DEV), w.w_k, w.w_knorm, w.theta, gk)
-            pooled_seq += done.tolist()
-            pooled_blk += blk.tolist()
+        blk = (lens[done] // 64 - 1).astype(np.int32)
+        if fused:
+            ops.append_kv(shape, k_new[step], v_new[step], w.k_pool, w.v_pool, w.block_table, w.seq_lens, w.w_k,
+                          w.w_knorm, w.theta, gk)
+        else:
+            page = bt[np.arange(w.batch), pos // 64].astype(np.int64)
+            base = torch.as_tensor(page * ps + (pos % 64) * ts, device=DEV)
+            idx = base[:, None, None] + heads[None, :, None] * hs + dims[None, None, :]
+            kflat[idx] = k_new[step]
+            vflat[idx] = v_new[step]
+            if len(done):
+                ops.pool_blocks(shape, w.k_pool, w.block_table, torch.as_tensor(done, device=DEV),
+                                torch.as_tensor(blk, device=DEV), w.w_k, w.w_knorm, w.theta, gk)
+        pooled_seq += done.tolist()
+        pooled_blk += blk.tolist()
         dec.step(w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, w.block_table, w.seq_lens)
         if step in check_at:
             torch.cuda.synchronize()

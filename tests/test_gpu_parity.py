@@ -79,6 +79,62 @@ def test_pool_blocks_empty_list_is_noop():
     assert torch.all(gk == 7)
 
 
+# ------------------------------------------------------------------ cache write + incremental pooling
+APPEND_CASES = [
+    dict(name="paged", lens=[60, 1, 127, 4095, 200], Hq=8, Hkv=2, layout="paged", mb=70),
+    dict(name="contig", lens=[63, 4000], Hq=4, Hkv=1, layout="contiguous", mb=66),
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=lambda c: c["name"])
+def test_append_kv_parity(case):
+    """70 decode steps of sas_append_kv against the oracle's append: pools
+    bit-exact, gate keys of the completed blocks within the pooling bar, and
+    bit-identical to sas_pool_blocks over the same blocks."""
+    steps = 70
+    say("append", case["name"])
+    w = wl.make(len(case["lens"]), case["Hq"], case["Hkv"], case["lens"], 1024, case["layout"], 33, DEV,
+                max_blocks=case["mb"], random_norms=True, extra_pages=3)
+    h = Host(w)
+    Hkv = w.n_kv_heads
+    _, k_new, v_new = wl.append_rows(w, steps, seed=34)
+    kn_h, vn_h = wl.host(k_new), wl.host(v_new)
+    shape = shape_of(w)
+    gk = torch.zeros((w.n_pages, Hkv, wl.GATE_DIM), dtype=torch.bfloat16, device=DEV)
+    gk_o = np.zeros((w.n_pages, Hkv, wl.GATE_DIM), np.uint16)
+    k_o, v_o = h.k.copy(), h.v.copy()
+    lens = h.lens.copy()
+    seq_all, blk_all = [], []
+    for step in range(steps):
+        lens += 1
+        w.seq_lens.copy_(torch.as_tensor(lens, device=DEV))
+        ops.append_kv(shape, k_new[step], v_new[step], w.k_pool, w.v_pool, w.block_table, w.seq_lens, w.w_k,
+                      w.w_knorm, w.theta, gk)
+        seq, blk = oracle.append_kv(k_o, v_o, h.bt, w.strides, Hkv, lens, kn_h[step], vn_h[step], h.w_k, h.wkn,
+                                    w.theta, gk_o)
+        seq_all += seq.tolist()
+        blk_all += blk.tolist()
+    torch.cuda.synchronize()
+    say(f"  blocks completed and pooled: {list(zip(seq_all, blk_all))}")
+    assert len(seq_all) >= 3
+    np.testing.assert_array_equal(wl.host(w.k_pool), k_o)
+    np.testing.assert_array_equal(wl.host(w.v_pool), v_o)
+    gk_g = wl.host(gk)
+    pages = h.bt[seq_all, blk_all]
+    untouched = np.ones(w.n_pages, bool)
+    untouched[pages] = False
+    assert np.all(gk_g[untouched] == 0)
+    f64 = oracle.pool_blocks(k_o, h.bt, w.strides, Hkv, np.array(seq_all, np.int32), np.array(blk_all, np.int32),
+                             h.w_k, h.wkn, w.theta, np.zeros_like(gk_o), want_f64=True)
+    got = oracle.bf16_to_f64(gk_g[pages])
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(f64) + 1e-30)) - 7)
+    excess = np.abs(got - f64) - ulp
+    assert np.all(excess <= 2e-5), float(excess.max())
+    # the fused pooling is the same arithmetic as sas_pool_blocks
+    gk2 = wl.host(gpu_pool(w, np.array(seq_all, np.int32), np.array(blk_all, np.int32)))
+    np.testing.assert_array_equal(gk2[pages], gk_g[pages])
+
+
 # ------------------------------------------------------------------ gate / Top-K
 GATE_CASES = [
     dict(name="tiny_1024", lens=[4096], Hq=4, Hkv=1, budget=1024, mb=64),

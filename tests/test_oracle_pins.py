@@ -140,6 +140,59 @@ def test_gate_key_pipeline_matches_torch(maker):
 
 
 # ---------------------------------------------------------------- gate query / scores
+@pytest.mark.parametrize("layout", ["paged", "contiguous"])
+def test_append_writes_the_row_and_pools_each_completed_block(layout):
+    """The cache-write step: after each append exactly the new token's K/V rows
+    changed, at the place the layout puts token L-1 (read through a numpy
+    reshape of the pool, not the oracle's stride arithmetic), and a block is
+    pooled exactly when its last row is written, to the key the torch pipeline
+    computes from the block's rows."""
+    lens0, steps = [60, 1, 127], 70
+    w = wl.make(3, 4, 2, lens0, 256, layout, 13, "cpu", max_blocks=4, random_norms=True, extra_pages=3)
+    h = Host(w)
+    B, Hkv = w.batch, w.n_kv_heads
+    _, k_new, v_new = wl.append_rows(w, steps, seed=14)
+    k_new, v_new = wl.host(k_new), wl.host(v_new)
+    k, v = h.k.copy(), h.v.copy()
+    gk = np.zeros((w.n_pages, Hkv, wl.GATE_DIM), np.uint16)
+    w_k = torch.from_numpy(oracle.bf16_to_f64(h.w_k))
+    wkn = torch.from_numpy(h.wkn.astype(np.float64))
+
+    def row(a, s, kvh, t):  # a view of token t's row in the layout's own shape
+        if layout == "contiguous":
+            return a[s, t, kvh]
+        return a[h.bt[s, t // 64], kvh, t % 64]
+
+    lens = h.lens.copy()
+    n_pooled = 0
+    for step in range(steps):
+        lens += 1
+        k0, v0, gk0 = k.copy(), v.copy(), gk.copy()
+        seq, blk = oracle.append_kv(k, v, h.bt, w.strides, Hkv, lens, k_new[step], v_new[step], h.w_k, h.wkn,
+                                    w.theta, gk)
+        done = [s for s in range(B) if lens[s] % 64 == 0]
+        assert seq.tolist() == done and blk.tolist() == [int(lens[s]) // 64 - 1 for s in done]
+        for s in range(B):
+            for kvh in range(Hkv):
+                row(k0, s, kvh, lens[s] - 1)[:] = k_new[step, s, kvh]
+                row(v0, s, kvh, lens[s] - 1)[:] = v_new[step, s, kvh]
+        np.testing.assert_array_equal(k, k0)
+        np.testing.assert_array_equal(v, v0)
+        for s, c in zip(seq, blk):
+            page = h.bt[s, c]
+            for kvh in range(Hkv):
+                rows = np.stack([row(k, s, kvh, 64 * c + t) for t in range(64)])
+                want = _torch_gate_key(torch.from_numpy(oracle.bf16_to_f64(rows)), w_k[kvh], wkn, int(c),
+                                       w.theta).numpy()
+                val = oracle.bf16_to_f64(gk[page, kvh])
+                ulp = 2.0 ** (np.floor(np.log2(np.abs(want) + 1e-300)) - 7)
+                assert np.all(np.abs(val - want) <= 0.5 * ulp + 1e-300)
+                gk0[page, kvh] = gk[page, kvh]
+            n_pooled += 1
+        np.testing.assert_array_equal(gk, gk0)  # no other gate key touched
+    assert n_pooled == 5  # 60 -> 64, 128; 1 -> 64; 127 -> 128, 192
+
+
 def test_gate_query_matches_torch():
     w = small_contig()
     h = Host(w)
