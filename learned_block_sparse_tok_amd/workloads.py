@@ -17,6 +17,7 @@ qwen3_4b   8      32/8    32,768    contiguous  2,048
 qwen3_8b   32     32/8    32,768    paged       2,048   (1,024 / 4,096 too)
 qwen3_14b  4      40/8    131,072   paged       2,048   1% planted, +3.0
 ragged     64     32/8    4K..64K   paged       4,096   128 append steps
+prefill_8b 1      32/8    32,768    paged       2,048   every position a query
 =========  =====  ======  ========  ==========  ======  =======================
 
 Values: q, K, V ~ N(0, 1) drawn in fp32 and rounded to bf16 (RNE, by torch);
@@ -46,7 +47,7 @@ GATE_DIM = 128
 ROPE_THETA = 1.0e6  # Qwen3 rotary base
 
 # fixed stream indices, one per drawn array
-_S_Q, _S_K, _S_V, _S_WQ, _S_WK, _S_PERM, _S_PLANT, _S_LENS, _S_APPEND, _S_NORM, _S_SEL, _S_GK = range(12)
+_S_Q, _S_K, _S_V, _S_WQ, _S_WK, _S_PERM, _S_PLANT, _S_LENS, _S_APPEND, _S_NORM, _S_SEL, _S_GK, _S_QALL = range(13)
 
 
 @dataclasses.dataclass
@@ -71,6 +72,10 @@ class Workload:
     strides: tuple  # (page, token, head) strides of the pools, in elements
     planted: np.ndarray | None = None  # int32 [B][Hkv][n_planted] block indices
     plant_delta: float = 0.0
+    # training-time forward of one sequence: "sequence" t of the batch is
+    # position t (length t+1, query q[t]); all positions share one cache and
+    # one block-table row (block_table is that row expanded with stride 0)
+    prefill: bool = False
 
     @property
     def n_pages(self) -> int:
@@ -163,6 +168,21 @@ def make(batch: int, n_q_heads: int, n_kv_heads: int, seq_lens, budget: int, lay
                     planted=planted, plant_delta=plant_delta)
 
 
+def make_prefill(seq_len: int, n_q_heads: int, n_kv_heads: int, budget: int, layout: str, seed: int,
+                 device="cpu", max_blocks: int | None = None, random_norms: bool = False,
+                 theta: float = ROPE_THETA, name: str = "prefill", extra_pages: int = 0) -> Workload:
+    """One sequence of seq_len tokens for the training-time forward, as the
+    batch of its positions (see Workload.prefill): K/V cache, gate weights and
+    block table as make() draws them for one sequence, plus one query row per
+    position, q [seq_len][Hq][128]."""
+    base = make(1, n_q_heads, n_kv_heads, seq_len, budget, layout, seed, device, max_blocks=max_blocks,
+                random_norms=random_norms, theta=theta, name=name, extra_pages=extra_pages)
+    q = _normal_bf16((seq_len, n_q_heads, HEAD_DIM), device, seed, _S_QALL)
+    lens = torch.arange(1, seq_len + 1, dtype=torch.int32, device=device)
+    bt = base.block_table.expand(seq_len, base.max_blocks)
+    return dataclasses.replace(base, batch=seq_len, q=q, seq_lens=lens, block_table=bt, prefill=True)
+
+
 def ragged_lengths(batch: int, seed: int, lo: int = 4096, hi: int = 65536) -> np.ndarray:
     """Whole-token lengths uniform in [lo, hi] inclusive."""
     rng = np.random.Generator(np.random.PCG64(seed * 1000 + _S_LENS))
@@ -184,6 +204,10 @@ def named(name: str, seed: int | None = None, device="cpu", budget: int | None =
     if name == "qwen3_14b":
         return make(4, 40, 8, 131072, budget or 2048, "paged", 4 if seed is None else seed, device,
                     n_planted=20, plant_delta=3.0, name=name, **kw)
+    if name == "prefill_8b":
+        # training-time forward at the training sequence length, Qwen3-8B heads
+        return make_prefill(kw.pop("seq_len", 32768), 32, 8, budget or 2048, "paged", 6 if seed is None else seed,
+                            device, name=name, **kw)
     if name == "ragged":
         sd = 5 if seed is None else seed
         lens = ragged_lengths(64, sd)

@@ -210,3 +210,31 @@ def attend(q, k_pool, v_pool, block_table, strides, n_kv_heads, seq_lens, sel, g
                               _p(np.ascontiguousarray(cnt, np.int32)), ctypes.c_int32(n_sel),
                               ctypes.c_double(sm_scale), _p(pairs), ctypes.c_int64(n), _p(out))
     return out if pairs is not None else out.reshape(B, Hq, HEAD_DIM)
+
+
+def prefill(q, k_pool, v_pool, block_table_row, strides, n_kv_heads, gate_keys, w_q, w_qnorm, theta,
+            budget_tokens, gated, sm_scale, positions=None):
+    """Training-time forward of one sequence with per-query block selection.
+
+    The pages say SAS selects KV blocks for each query and trains with a
+    Top-K of 31 historical blocks on 32,768-token sequences (aigc.news release
+    note; "Tencent Hunyuan open-sources SAS ...": per-query block selection).
+    READING: query position t (0-based, q[t], T = len(q) positions) selects and
+    attends exactly as a decode step whose cache holds the first t+1 tokens:
+    gate query at position t, candidates the complete blocks c < t/64, the
+    Top-K plus its own block t/64, then causal attention over the selected
+    blocks' tokens j <= t.  So the forward is gate_topk + attend over the batch
+    of positions, all sharing the one block-table row.
+
+    positions: optional int array of the positions to compute (default all).
+    Returns (sel, gates, cnt, scores, out) for those positions, shaped as
+    gate_topk / attend return them with the positions as the batch."""
+    T = q.shape[0]
+    pos = np.arange(T, dtype=np.int32) if positions is None else np.asarray(positions, np.int32)
+    qp = np.ascontiguousarray(q[pos])
+    lens = (pos + 1).astype(np.int32)
+    bt = np.ascontiguousarray(np.broadcast_to(np.asarray(block_table_row, np.int32),
+                                              (len(pos), len(block_table_row))))
+    sel, gates, cnt, scores = gate_topk(qp, w_q, w_qnorm, gate_keys, bt, lens, theta, budget_tokens, n_kv_heads)
+    out = attend(qp, k_pool, v_pool, bt, strides, n_kv_heads, lens, sel, gates if gated else None, cnt, sm_scale)
+    return sel, gates, cnt, scores, out

@@ -466,3 +466,68 @@ def test_gate_parameter_count_and_checkpoint_size():
         assert math.ceil(n * 4 / 2 ** 20) != int(ckpt_mib)
         assert round(layers * (per_layer + hq * 128 + hkv * 128) / 1e6, 1) != float(params_m)
         assert round(layers * (hkv * 128 * 128 + hkv * 384 * 128 + 256) / 1e6, 1) != float(params_m)
+
+
+# ---------------------------------------------------------------- training-time forward (every position a query)
+def _prefill_host(T=300, Hq=4, Hkv=2, budget=128, layout="paged", seed=21):
+    w = wl.make_prefill(T, Hq, Hkv, budget, layout, seed, "cpu", random_norms=True, extra_pages=2)
+    h = Host(w)
+    nb = T // 64
+    gk = np.zeros((w.n_pages, Hkv, wl.GATE_DIM), np.uint16)
+    oracle.pool_blocks(h.k, h.bt[:1], w.strides, Hkv, np.zeros(nb, np.int32), np.arange(nb, dtype=np.int32),
+                       h.w_k, h.wkn, w.theta, gk)
+    return w, h, gk
+
+
+@pytest.mark.parametrize("layout", ["paged", "contiguous"])
+def test_prefill_with_full_budget_is_causal_gqa_attention(layout):
+    """Budget covering the whole sequence: every position attends all of its
+    past, so the forward is causal attention (torch SDPA, fp64, GQA heads)."""
+    T, Hq, Hkv = 300, 4, 2
+    w, h, gk = _prefill_host(T, Hq, Hkv, budget=64 * 5, layout=layout)
+    sel, gates, cnt, _, out = oracle.prefill(h.q, h.k, h.v, h.bt[0], w.strides, Hkv, gk, h.w_q, h.wqn, w.theta,
+                                             64 * 5, False, SM_SCALE)
+    assert np.all(cnt == (np.arange(T) // 64 + 1)[:, None])
+    q = torch.from_numpy(oracle.bf16_to_f64(h.q)).permute(1, 0, 2)  # [Hq][T][128]
+    k = torch.stack([torch.from_numpy(dense_kv(h, h.k, T - 1, kv)) for kv in range(Hkv)])  # [Hkv][T][128]
+    v = torch.stack([torch.from_numpy(dense_kv(h, h.v, T - 1, kv)) for kv in range(Hkv)])
+    G = Hq // Hkv
+    ref = F.scaled_dot_product_attention(q, k.repeat_interleave(G, 0), v.repeat_interleave(G, 0), is_causal=True,
+                                         scale=SM_SCALE)
+    np.testing.assert_allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_prefill_is_causal():
+    """Changing the rows of positions >= t0 (queries, keys, values, and the
+    gate keys of the blocks they touch) leaves every position < t0 unchanged."""
+    T, Hkv, t0, budget = 300, 2, 130, 128
+    w, h, gk = _prefill_host(T, 4, Hkv, budget=budget)
+    args = (w.strides, Hkv)
+    r1 = oracle.prefill(h.q, h.k, h.v, h.bt[0], *args, gk, h.w_q, h.wqn, w.theta, budget, True, SM_SCALE)
+    rng = np.random.default_rng(5)
+    q2, k2, v2 = h.q.copy(), h.k.copy(), h.v.copy()
+    q2[t0:] = wl.bf16_bits(torch.randn(q2[t0:].shape).to(torch.bfloat16))
+    for t in range(t0, T):
+        for kv in range(Hkv):
+            for pool in (k2, v2):
+                off = h.bt[0, t // 64] * w.strides[0] + kv * w.strides[2] + (t % 64) * w.strides[1]
+                pool.reshape(-1)[off:off + 128] = wl.bf16_bits(torch.from_numpy(rng.standard_normal(128)).to(torch.bfloat16))
+    nb = T // 64
+    gk2 = np.zeros_like(gk)
+    oracle.pool_blocks(k2, h.bt[:1], w.strides, Hkv, np.zeros(nb, np.int32), np.arange(nb, dtype=np.int32), h.w_k,
+                       h.wkn, w.theta, gk2)
+    r2 = oracle.prefill(q2, k2, v2, h.bt[0], *args, gk2, h.w_q, h.wqn, w.theta, budget, True, SM_SCALE)
+    for a, b in zip(r1, r2):
+        np.testing.assert_array_equal(a[:t0], b[:t0])
+    assert not np.array_equal(r1[4][t0:], r2[4][t0:])
+
+
+def test_prefill_positions_subset_matches_full():
+    T, Hkv, budget = 300, 2, 192
+    w, h, gk = _prefill_host(T, 4, Hkv, budget=budget, layout="contiguous")
+    full = oracle.prefill(h.q, h.k, h.v, h.bt[0], w.strides, Hkv, gk, h.w_q, h.wqn, w.theta, budget, True, SM_SCALE)
+    pos = np.array([0, 63, 64, 200, 299])
+    part = oracle.prefill(h.q, h.k, h.v, h.bt[0], w.strides, Hkv, gk, h.w_q, h.wqn, w.theta, budget, True, SM_SCALE,
+                          positions=pos)
+    for a, b in zip(full, part):
+        np.testing.assert_array_equal(a[pos], b)
