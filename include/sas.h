@@ -19,6 +19,8 @@
  *                      (cache write fused with incremental pooling)
  *   sas_gate_topk      once per decode step                      (selection)
  *   sas_sparse_decode  once per decode step                      (attention)
+ * and, for the training-time forward of a whole sequence (every position a
+ * query): sas_prefill_select, then sas_prefill_attend.
  *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer owned by the caller (for
@@ -145,7 +147,8 @@ sas_status sas_append_kv(const sas_shape *shape, const void *k_new, const void *
  *   gates  fp32   sigmoid(score) per selected historical block, 1 for the
  *                 local block (nullable: not written)
  *   cnt    int32  [B][Hkv] number of selected blocks (>= 1)
- *   scores fp32   [B][Hkv][max_blocks] block scores (entries c >= l are -inf)
+ *   scores fp32   [B][Hkv][max_blocks] block scores (entries c >= l are -inf;
+ *                 nullable: not written)
  * budget_tokens: a positive multiple of 64, at most 64 * 256.
  */
 sas_status sas_gate_topk(const sas_shape *shape, const void *q, const void *w_q,
@@ -177,6 +180,38 @@ sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *
                              const int32_t *seq_lens, const int32_t *sel, const float *gates,
                              const int32_t *cnt, int32_t max_sel, float sm_scale, void *out,
                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Training-time forward of one sequence (every position is a query).  SAS
+ * selects KV blocks for each query and trains with a Top-K of 31 historical
+ * blocks on 32,768-token sequences (aigc.news release note; "Tencent Hunyuan
+ * open-sources SAS ...": per-query block selection).  Position t (0-based,
+ * T = seq_len positions) selects and attends exactly as a decode step whose
+ * cache holds the first t+1 tokens: gate query at position t, candidates the
+ * complete blocks c < t/64, its own block t/64 last, causal attention (keys
+ * j <= t) over the selected blocks.
+ *
+ * shape->batch must be 1 (one sequence per call); T must fit in max_blocks
+ * blocks.  q: bf16 [T][Hq][128]; block_table_row: int32 [max_blocks], the
+ * sequence's pages (the K/V strides of shape address them as for decode).
+ *
+ * sas_prefill_select -- sas_gate_topk for every position: writes sel / gates /
+ *   cnt ([T][Hkv][budget/64], [T][Hkv]) and, when scores is non-NULL, scores
+ *   [T][Hkv][max_blocks], with the same definitions and conventions.
+ * sas_prefill_attend -- the attention of every position over its selection:
+ *   plain (gates NULL) or gated as in sas_sparse_decode, output bf16
+ *   [T][Hq][128].  sel / gates / cnt as sas_prefill_select wrote them
+ *   (max_sel = budget/64).  Needs no workspace.
+ */
+sas_status sas_prefill_select(const sas_shape *shape, const void *q, const void *w_q,
+                              const float *w_qnorm, const void *gate_keys,
+                              const int32_t *block_table_row, int32_t seq_len, double rope_theta,
+                              int32_t budget_tokens, int32_t *sel, float *gates, int32_t *cnt,
+                              float *scores, void *stream);
+sas_status sas_prefill_attend(const sas_shape *shape, const void *q, const void *k_pool,
+                              const void *v_pool, const int32_t *block_table_row, int32_t seq_len,
+                              const int32_t *sel, const float *gates, const int32_t *cnt,
+                              int32_t max_sel, float sm_scale, void *out, void *stream);
 
 /* Text of a status code (static storage). */
 const char *sas_status_str(sas_status status);

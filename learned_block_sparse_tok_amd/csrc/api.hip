@@ -141,7 +141,7 @@ sas_status sas_gate_topk(const sas_shape *shape, const void *q, const void *w_q,
                          float *scores, void *stream) {
   sas_status st = check_shape(shape, false);
   if (st) return st;
-  if (!q || !w_q || !w_qnorm || !gate_keys || !block_table || !seq_lens || !sel || !cnt || !scores)
+  if (!q || !w_q || !w_qnorm || !gate_keys || !block_table || !seq_lens || !sel || !cnt)
     return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
   if (budget_tokens < SAS_BLOCK || budget_tokens % SAS_BLOCK)
     return fail(SAS_ERR_INVALID_ARG, "budget_tokens (%d) must be a positive multiple of %d", budget_tokens,
@@ -167,8 +167,93 @@ sas_status sas_gate_topk(const sas_shape *shape, const void *q, const void *w_q,
   p.group = shape->n_q_heads / shape->n_kv_heads;
   p.max_blocks = shape->max_blocks;
   p.n_sel = budget_tokens / SAS_BLOCK;
+  p.bt_row_stride = shape->max_blocks;
   for (int i = 0; i < SAS_GATE_DIM / 2; ++i) p.inv_freq[i] = pow(rope_theta, -(double)i / (SAS_GATE_DIM / 2));
   return hip_status(sas::launch_gate_topk(p, shape->batch, (hipStream_t)stream), "sas_gate_topk launch");
+}
+
+namespace {
+sas_status check_prefill(const sas_shape *shape, bool need_kv_strides, int32_t seq_len) {
+  sas_status st = check_shape(shape, need_kv_strides);
+  if (st) return st;
+  if (shape->batch != 1) return fail(SAS_ERR_INVALID_ARG, "prefill calls take one sequence (batch %d)", shape->batch);
+  if (seq_len < 1) return fail(SAS_ERR_INVALID_ARG, "seq_len must be positive");
+  if ((seq_len + SAS_BLOCK - 1) / SAS_BLOCK > shape->max_blocks)
+    return fail(SAS_ERR_INVALID_ARG, "seq_len %d needs more than max_blocks (%d) blocks", seq_len, shape->max_blocks);
+  return SAS_OK;
+}
+}  // namespace
+
+sas_status sas_prefill_select(const sas_shape *shape, const void *q, const void *w_q, const float *w_qnorm,
+                              const void *gate_keys, const int32_t *block_table_row, int32_t seq_len,
+                              double rope_theta, int32_t budget_tokens, int32_t *sel, float *gates, int32_t *cnt,
+                              float *scores, void *stream) {
+  sas_status st = check_prefill(shape, false, seq_len);
+  if (st) return st;
+  if (!q || !w_q || !w_qnorm || !gate_keys || !block_table_row || !sel || !cnt)
+    return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (budget_tokens < SAS_BLOCK || budget_tokens % SAS_BLOCK)
+    return fail(SAS_ERR_INVALID_ARG, "budget_tokens (%d) must be a positive multiple of %d", budget_tokens,
+                SAS_BLOCK);
+  if (budget_tokens / SAS_BLOCK > 256)
+    return fail(SAS_ERR_UNSUPPORTED, "budget_tokens (%d) exceeds %d", budget_tokens, 256 * SAS_BLOCK);
+  if (!(rope_theta > 1.0)) return fail(SAS_ERR_INVALID_ARG, "rope_theta must be > 1");
+  if (!aligned16(gate_keys) || !aligned16(w_q))
+    return fail(SAS_ERR_UNSUPPORTED, "gate_keys and w_q must be 16-byte aligned");
+  sas::GateParams p;
+  p.q = (const uint16_t *)q;
+  p.w_q = (const uint16_t *)w_q;
+  p.w_qnorm = w_qnorm;
+  p.gate_keys = (const uint16_t *)gate_keys;
+  p.block_table = block_table_row;
+  p.seq_lens = nullptr;  // entry t is position t: L = t + 1
+  p.sel = sel;
+  p.gates = gates;
+  p.cnt = cnt;
+  p.scores = scores;
+  p.n_q_heads = shape->n_q_heads;
+  p.n_kv_heads = shape->n_kv_heads;
+  p.group = shape->n_q_heads / shape->n_kv_heads;
+  p.max_blocks = shape->max_blocks;
+  p.n_sel = budget_tokens / SAS_BLOCK;
+  p.bt_row_stride = 0;
+  for (int i = 0; i < SAS_GATE_DIM / 2; ++i) p.inv_freq[i] = pow(rope_theta, -(double)i / (SAS_GATE_DIM / 2));
+  return hip_status(sas::launch_gate_topk(p, seq_len, (hipStream_t)stream), "sas_prefill_select launch");
+}
+
+sas_status sas_prefill_attend(const sas_shape *shape, const void *q, const void *k_pool, const void *v_pool,
+                              const int32_t *block_table_row, int32_t seq_len, const int32_t *sel,
+                              const float *gates, const int32_t *cnt, int32_t max_sel, float sm_scale, void *out,
+                              void *stream) {
+  sas_status st = check_prefill(shape, true, seq_len);
+  if (st) return st;
+  if (!q || !k_pool || !v_pool || !block_table_row || !sel || !cnt || !out)
+    return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (max_sel <= 0) return fail(SAS_ERR_INVALID_ARG, "max_sel must be positive");
+  if (!(sm_scale > 0.f)) return fail(SAS_ERR_INVALID_ARG, "sm_scale must be positive");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return fail(SAS_ERR_UNSUPPORTED, "q, k_pool, v_pool and out must be 16-byte aligned");
+  sas::PrefillParams p;
+  p.q = (const uint16_t *)q;
+  p.k_pool = (const uint16_t *)k_pool;
+  p.v_pool = (const uint16_t *)v_pool;
+  p.block_table = block_table_row;
+  p.sel = sel;
+  p.gates = gates;
+  p.cnt = cnt;
+  p.out = (uint16_t *)out;
+  p.page_stride = shape->page_stride;
+  p.tok_stride = shape->tok_stride;
+  p.head_stride = shape->head_stride;
+  p.n_q_heads = shape->n_q_heads;
+  p.n_kv_heads = shape->n_kv_heads;
+  p.group = shape->n_q_heads / shape->n_kv_heads;
+  p.head_groups = (p.group + 3) / 4;
+  p.max_sel = max_sel;
+  p.seq_len = seq_len;
+  p.n_qblocks = (seq_len + SAS_BLOCK - 1) / SAS_BLOCK;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  return hip_status(sas::launch_prefill_attend(p, (hipStream_t)stream), "sas_prefill_attend launch");
 }
 
 namespace {

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane16 = t & 15, grp = t >> 4;
   const int G = p.group;
-  const int32_t L = p.seq_lens[s];
+  const int32_t L = p.seq_lens ? p.seq_lens[s] : s + 1;
   const int n = (L - 1) / kBlock;  // candidates: the blocks before the local block
   const int k_eff = min(p.n_sel - 1, n);
 
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
   const u32x4 qpiece = ld16(qg + (has_q ? 8 * t : 0));
   const double inv_freq = p.inv_freq[lane];
   const float wqn_a = p.w_qnorm[lane], wqn_b = p.w_qnorm[lane + 64];
-  const int32_t *bt = p.block_table + (int64_t)s * p.max_blocks;
+  const int32_t *bt = p.block_table + (int64_t)s * p.bt_row_stride;
   constexpr int kBtUnroll = 4;  // rows of up to 1,024 blocks staged without a loop
   int32_t btv[kBtUnroll];
 #pragma unroll
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
 
   // ---- 3. scores of every candidate (first 512 already in flight)
   const float inv_sqrt_dg = 0.08838834764831845f;  // 1/sqrt(128)
-  float *scores = p.scores + (int64_t)sk * p.max_blocks;
+  float *scores = p.scores ? p.scores + (int64_t)sk * p.max_blocks : nullptr;
   for (int base = 0; base < n; base += 16 * kKeysInFlight) {
     if (base > 0) {
 #pragma unroll
@@ -189,11 +189,12 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
       if (lane16 == 0 && c < n) {
         const float sc = d * inv_sqrt_dg;
         slot[c] = score_key(sc);
-        scores[c] = sc;
+        if (scores) scores[c] = sc;
       }
     }
   }
-  for (int c = n + t; c < p.max_blocks; c += 256) scores[c] = -__builtin_inff();
+  if (scores)
+    for (int c = n + t; c < p.max_blocks; c += 256) scores[c] = -__builtin_inff();
   lds_barrier();
   if (wave != 0) return;
 

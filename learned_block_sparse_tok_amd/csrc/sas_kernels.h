@@ -37,12 +37,13 @@ struct GateParams {
   const uint16_t *w_q;      // [Hq][128 out][128 in]
   const float *w_qnorm;     // [128]
   const uint16_t *gate_keys;
-  const int32_t *block_table, *seq_lens;
+  const int32_t *block_table, *seq_lens;  // seq_lens NULL: entry s is position s of one sequence (L = s + 1)
   int32_t *sel;
   float *gates;             // nullable
   int32_t *cnt;
-  float *scores;            // [B][Hkv][max_blocks]
+  float *scores;            // [B][Hkv][max_blocks], nullable
   int32_t n_q_heads, n_kv_heads, group, max_blocks, n_sel;
+  int32_t bt_row_stride;    // max_blocks, or 0 when every entry shares one block-table row
   double inv_freq[kGateDim / 2];  // rope_theta^(-i/64)
 };
 
@@ -67,7 +68,21 @@ struct DecodeSplit {
 };
 DecodeSplit decode_split(int batch, int n_kv_heads, int max_sel);
 
+struct PrefillParams {
+  const uint16_t *q;            // [T][Hq][128]
+  const uint16_t *k_pool, *v_pool;
+  const int32_t *block_table;   // the sequence's row [max_blocks]
+  const int32_t *sel;           // [T][Hkv][max_sel]
+  const float *gates;           // nullable
+  const int32_t *cnt;           // [T][Hkv]
+  uint16_t *out;                // [T][Hq][128]
+  int64_t page_stride, tok_stride, head_stride;
+  int32_t n_q_heads, n_kv_heads, group, head_groups, max_sel, seq_len, n_qblocks;
+  float scale_log2;
+};
+
 hipError_t launch_pool(const PoolParams &p, hipStream_t st);
+hipError_t launch_prefill_attend(const PrefillParams &p, hipStream_t st);
 hipError_t launch_append(const AppendParams &p, int batch, hipStream_t st);
 hipError_t launch_gate_topk(const GateParams &p, int batch, hipStream_t st);
 hipError_t launch_decode(const DecodeParams &p, int batch, hipStream_t st);

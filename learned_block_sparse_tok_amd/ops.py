@@ -43,6 +43,8 @@ _SIGS = {
     "sas_gate_topk": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _F64, _I32, _VP, _VP, _VP, _VP, _VP]),
     "sas_sparse_decode_workspace_bytes": (_SZ, [_VP, _I32]),
     "sas_sparse_decode": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP, _VP, _SZ, _VP]),
+    "sas_prefill_select": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _F64, _I32, _VP, _VP, _VP, _VP, _VP]),
+    "sas_prefill_attend": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _F32, _VP, _VP]),
     "sas_status_str": (ctypes.c_char_p, [_I32]),
     "sas_last_error": (ctypes.c_char_p, []),
     "sas_version": (_I32, []),
@@ -178,3 +180,60 @@ class SparseDecoder:
         self.select(q, w_q, w_qnorm, gate_keys, block_table, seq_lens, stream)
         self.attend(q, k_pool, v_pool, block_table, seq_lens, stream)
         return self.out
+
+
+def prefill_select(shape: SasShape, q, w_q, w_qnorm, gate_keys, block_table_row, seq_len, theta, budget_tokens,
+                   sel, gates, cnt, scores=None, stream=None):
+    """Gate query, block scores and Top-K for every position of one sequence
+    (q [T][Hq][128]); sel / gates [T][Hkv][budget/64], cnt [T][Hkv]."""
+    st = lib().sas_prefill_select(ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"), _ptr(w_q, torch.bfloat16, "w_q"),
+                                  _ptr(w_qnorm, torch.float32, "w_qnorm"),
+                                  _ptr(gate_keys, torch.bfloat16, "gate_keys"),
+                                  _ptr(block_table_row, torch.int32, "block_table_row"), int(seq_len), float(theta),
+                                  int(budget_tokens), _ptr(sel, torch.int32, "sel"),
+                                  _ptr(gates, torch.float32, "gates"), _ptr(cnt, torch.int32, "cnt"),
+                                  _ptr(scores, torch.float32, "scores"), _stream(stream))
+    _check(st, "sas_prefill_select")
+
+
+def prefill_attend(shape: SasShape, q, k_pool, v_pool, block_table_row, seq_len, sel, gates, cnt, max_sel, sm_scale,
+                   out, stream=None):
+    """Attention of every position of one sequence over its own selection
+    (gates None: plain mode); out bf16 [T][Hq][128]."""
+    st = lib().sas_prefill_attend(ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"),
+                                  _ptr(k_pool, torch.bfloat16, "k_pool"), _ptr(v_pool, torch.bfloat16, "v_pool"),
+                                  _ptr(block_table_row, torch.int32, "block_table_row"), int(seq_len),
+                                  _ptr(sel, torch.int32, "sel"), _ptr(gates, torch.float32, "gates"),
+                                  _ptr(cnt, torch.int32, "cnt"), int(max_sel), float(sm_scale),
+                                  _ptr(out, torch.bfloat16, "out"), _stream(stream))
+    _check(st, "sas_prefill_attend")
+
+
+class Prefill:
+    """Outputs of the training-time forward of one sequence of seq_len tokens
+    (selection + attention), allocated once; forward() runs both calls."""
+
+    def __init__(self, n_q_heads, n_kv_heads, max_blocks, strides, seq_len, budget_tokens, theta, gated,
+                 device="cuda", sm_scale=None, keep_scores=False):
+        self.shape = make_shape(1, n_q_heads, n_kv_heads, max_blocks, strides)
+        self.seq_len, self.budget, self.theta, self.gated = seq_len, budget_tokens, theta, gated
+        self.max_sel = budget_tokens // 64
+        self.sm_scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(128.0)
+        self.sel = torch.empty((seq_len, n_kv_heads, self.max_sel), dtype=torch.int32, device=device)
+        self.gates = torch.empty((seq_len, n_kv_heads, self.max_sel), dtype=torch.float32, device=device)
+        self.cnt = torch.empty((seq_len, n_kv_heads), dtype=torch.int32, device=device)
+        self.scores = (torch.empty((seq_len, n_kv_heads, max_blocks), dtype=torch.float32, device=device)
+                       if keep_scores else None)
+        self.out = torch.empty((seq_len, n_q_heads, 128), dtype=torch.bfloat16, device=device)
+
+    def select(self, q, w_q, w_qnorm, gate_keys, block_table_row, stream=None):
+        prefill_select(self.shape, q, w_q, w_qnorm, gate_keys, block_table_row, self.seq_len, self.theta, self.budget,
+                       self.sel, self.gates, self.cnt, self.scores, stream)
+
+    def attend(self, q, k_pool, v_pool, block_table_row, stream=None):
+        prefill_attend(self.shape, q, k_pool, v_pool, block_table_row, self.seq_len, self.sel,
+                       self.gates if self.gated else None, self.cnt, self.max_sel, self.sm_scale, self.out, stream)
+
+    def forward(self, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table_row, stream=None):
+        self.select(q, w_q, w_qnorm, gate_keys, block_table_row, stream)
+        self.attend(q, k_pool, v_pool, block_table_row, stream)

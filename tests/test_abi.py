@@ -107,6 +107,29 @@ def test_append_rejects_bad_arguments(lib):
     assert call(sh=_shape(n_kv_heads=3)) == ops.SAS_ERR_INVALID_ARG  # 8 query heads not a multiple of 3
 
 
+def test_prefill_rejects_bad_arguments(lib):
+    sh1 = _shape(batch=1)
+
+    def sel_call(sh=sh1, T=100, budget=128, q=FAKE):
+        return lib.sas_prefill_select(ctypes.byref(sh), q, FAKE, FAKE, FAKE, FAKE, T, 1e6, budget, FAKE, FAKE, FAKE,
+                                      None, None)
+
+    def att_call(sh=sh1, T=100, max_sel=2, out=FAKE):
+        return lib.sas_prefill_attend(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, T, FAKE, None, FAKE, max_sel, 0.088,
+                                      out, None)
+
+    assert sel_call(sh=_shape(batch=2)) == ops.SAS_ERR_INVALID_ARG  # one sequence per call
+    assert sel_call(T=0) == ops.SAS_ERR_INVALID_ARG
+    assert sel_call(T=16 * 64 + 1) == ops.SAS_ERR_INVALID_ARG  # needs 17 blocks, max_blocks 16
+    assert sel_call(budget=100) == ops.SAS_ERR_INVALID_ARG
+    assert sel_call(q=None) == ops.SAS_ERR_INVALID_ARG
+    assert att_call(sh=_shape(batch=3)) == ops.SAS_ERR_INVALID_ARG
+    assert att_call(T=-5) == ops.SAS_ERR_INVALID_ARG
+    assert att_call(max_sel=0) == ops.SAS_ERR_INVALID_ARG
+    assert att_call(out=None) == ops.SAS_ERR_INVALID_ARG
+    assert att_call(out=ctypes.c_void_p(4096 + 8)) == ops.SAS_ERR_UNSUPPORTED  # not 16-byte aligned
+
+
 def test_workspace_sizes(lib):
     # 256 (sequence, KV head) units fill the CUs: one workgroup each, no partials
     sh = _shape(batch=32, n_q_heads=32, n_kv_heads=8, max_blocks=512)

@@ -135,6 +135,59 @@ def test_append_kv_parity(case):
     np.testing.assert_array_equal(gk2[pages], gk_g[pages])
 
 
+# ------------------------------------------------------------------ training-time forward (every position a query)
+PREFILL_CASES = [
+    dict(name="paged_g4_ragged", T=1000, Hq=8, Hkv=2, budget=256, layout="paged"),
+    dict(name="contig_g1", T=700, Hq=2, Hkv=2, budget=192, layout="contiguous"),
+    dict(name="paged_g5", T=640, Hq=10, Hkv=2, budget=128, layout="paged"),
+    dict(name="paged_g16_tail1", T=577, Hq=16, Hkv=1, budget=320, layout="paged"),
+    dict(name="full_budget", T=300, Hq=4, Hkv=1, budget=320, layout="paged"),
+]
+
+
+def prefill_gate_keys(w):
+    """Gate keys of the sequence's complete blocks, pooled on the GPU."""
+    nb = w.batch // 64
+    gk = torch.zeros((w.n_pages, w.n_kv_heads, wl.GATE_DIM), dtype=torch.bfloat16, device=DEV)
+    shape1 = ops.make_shape(1, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides)
+    if nb:
+        ops.pool_blocks(shape1, w.k_pool, w.block_table[:1].contiguous(),
+                        torch.zeros(nb, dtype=torch.int32, device=DEV), torch.arange(nb, dtype=torch.int32, device=DEV),
+                        w.w_k, w.w_knorm, w.theta, gk)
+    return gk
+
+
+def gpu_prefill(w, gk, gated, budget):
+    pf = ops.Prefill(w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, w.batch, budget, w.theta, gated,
+                     device=DEV, keep_scores=True)
+    pf.forward(w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, w.block_table[0])
+    torch.cuda.synchronize()
+    return dict(sel=wl.host(pf.sel), gates=wl.host(pf.gates), cnt=wl.host(pf.cnt), scores=wl.host(pf.scores),
+                out=bf16_out(pf.out))
+
+
+@pytest.mark.parametrize("gated", [False, True], ids=["plain", "gated"])
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: c["name"])
+def test_prefill_parity(case, gated):
+    """sas_prefill_select + sas_prefill_attend against the oracle's forward at
+    every position (several query blocks, a ragged last block, group sizes 1,
+    4, 5 and 16), with the decode path's tie accounting."""
+    say("prefill", case["name"], "gated" if gated else "plain")
+    w = wl.make_prefill(case["T"], case["Hq"], case["Hkv"], case["budget"], case["layout"], 41, DEV,
+                        random_norms=True, extra_pages=2)
+    h = Host(w)
+    nb = w.batch // 64
+    gk_o = np.zeros((w.n_pages, w.n_kv_heads, wl.GATE_DIM), np.uint16)
+    oracle.pool_blocks(h.k, h.bt[:1], w.strides, w.n_kv_heads, np.zeros(nb, np.int32), np.arange(nb, dtype=np.int32),
+                       h.w_k, h.wkn, w.theta, gk_o)
+    sel, gates, cnt, scores, out = oracle.prefill(h.q, h.k, h.v, h.bt[0], w.strides, w.n_kv_heads, gk_o, h.w_q,
+                                                  h.wqn, w.theta, case["budget"], gated, SM_SCALE)
+    o = dict(gate_keys=gk_o, sel=sel, gates=gates, cnt=cnt, scores=scores, out=out)
+    g = gpu_prefill(w, prefill_gate_keys(w), gated, case["budget"])
+    ties, skipped = compare_step(h, g, o, gated, case["budget"])
+    say(f"  boundary ties {ties}, unenumerated {skipped}")
+
+
 # ------------------------------------------------------------------ gate / Top-K
 GATE_CASES = [
     dict(name="tiny_1024", lens=[4096], Hq=4, Hkv=1, budget=1024, mb=64),
