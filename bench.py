@@ -31,6 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix throughput, published
 
 
 def log(*a):
@@ -102,6 +103,151 @@ def cpu_baseline(layer, budget, gated, seconds):
                        f"{t_total:.1f} s; gate keys pooled beforehand (untimed, as on the GPU)")
 
 
+def prefill_flops(cnt, group):
+    """Algorithmic attention flops of a training-time forward: every query
+    head of position t does 4 x 128 flops (QK and PV) per attended key, the
+    keys being the full historical blocks plus its own block up to t."""
+    import numpy as np
+    T = cnt.shape[0]
+    own = (np.arange(T) % 64 + 1)[:, None]
+    keys = (cnt.astype(np.int64) - 1) * 64 + own
+    return float(keys.sum()) * group * 4 * 128
+
+
+def prefill_executed_flops(sel, cnt, group):
+    """Matrix work the kernel issues: per 16-query wave and head group, 128
+    MFMAs of 16x16x32 (4 heads x (QK + PV)) for every block in the union of
+    those 16 queries' selections."""
+    import numpy as np
+    T, Hkv, _ = sel.shape
+    visits = 0
+    for t0 in range(0, T, 16):
+        for k in range(Hkv):
+            rows = [sel[t, k, :cnt[t, k]] for t in range(t0, min(T, t0 + 16))]
+            visits += len(np.unique(np.concatenate(rows)))
+    return float(visits) * ((group + 3) // 4) * 128 * 16 * 16 * 32 * 2
+
+
+def cpu_baseline_prefill(w, gk_o_fn, budget, gated, seconds):
+    """The oracle's forward at a bounded sample of positions (the last ones,
+    which attend the most), repeated until `seconds` of host time passed."""
+    import numpy as np
+    import oracle
+    from learned_block_sparse_tok_amd import workloads as wl
+    T = w.batch
+    h_q, h_k, h_v = wl.host(w.q), wl.host(w.k_pool), wl.host(w.v_pool)
+    bt = wl.host(w.block_table[0])
+    gk = gk_o_fn(h_k, bt)
+    pos = np.arange(T - 32, T)
+    n, t_total, reps = 0, 0.0, 0
+    while t_total < seconds or reps == 0:
+        t0 = time.perf_counter()
+        oracle.prefill(h_q, h_k, h_v, bt, w.strides, w.n_kv_heads, gk, wl.host(w.w_q), wl.host(w.w_qnorm), w.theta,
+                       budget, gated, 1.0 / math.sqrt(128), positions=pos)
+        t_total += time.perf_counter() - t0
+        n += len(pos)
+        reps += 1
+    return dict(value=n / t_total, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"positions {T - 32}..{T - 1} of the {T}-token sequence ({'gated' if gated else 'plain'} "
+                       f"mode): gate stage + dense masked attention over each position's past, {reps} repetitions, "
+                       f"{t_total:.1f} s; gate keys pooled beforehand (untimed, as on the GPU)")
+
+
+def run_prefill(args):
+    import numpy as np
+    import torch
+    from learned_block_sparse_tok_amd import ops
+    from learned_block_sparse_tok_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ops.lib()
+    w = wl.named(args.workload, device=dev, budget=args.budget)
+    T, G = w.batch, w.group
+    bt_row = w.block_table[0]
+    nb = T // 64
+    gk = torch.zeros((w.n_pages, w.n_kv_heads, 128), dtype=torch.bfloat16, device=dev)
+    shape1 = ops.make_shape(1, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides)
+    ops.pool_blocks(shape1, w.k_pool, w.block_table[:1].contiguous(), torch.zeros(nb, dtype=torch.int32, device=dev),
+                    torch.arange(nb, dtype=torch.int32, device=dev), w.w_k, w.w_knorm, w.theta, gk)
+    torch.cuda.synchronize()
+    log(f"{args.workload}: T={T}, gate keys pooled")
+    steps = max(1, min(args.steps, 20))
+    warm = max(1, min(args.warmup, 3))
+    results = {}
+    for mode in args.modes.split(","):
+        gated = mode == "gated"
+        pf = ops.Prefill(w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, T, args.budget, w.theta, gated, device=dev)
+        for _ in range(warm):
+            pf.forward(w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, bt_row)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            pf.forward(w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, bt_row)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        stream = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        for _ in range(steps):
+            pf.select(w.q, w.w_q, w.w_qnorm, gk, bt_row)
+        ev[1].record(stream)
+        for _ in range(steps):
+            pf.attend(w.q, w.k_pool, w.v_pool, bt_row)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        sel_ms, att_ms = ev[0].elapsed_time(ev[1]) / steps, ev[1].elapsed_time(ev[2]) / steps
+        cnt, sel = wl.host(pf.cnt), wl.host(pf.sel)
+        flops = prefill_flops(cnt, G)
+        executed = prefill_executed_flops(sel, cnt, G)
+        ms = elapsed * 1e3 / steps
+        results[mode] = dict(tokens_per_s=T * steps / elapsed, ms_per_step=ms, select_ms=sel_ms, attend_ms=att_ms,
+                             attend_tflops=flops / (att_ms * 1e-3) / 1e12, algorithmic_flops=flops,
+                             executed_flops=executed, executed_tflops=executed / (att_ms * 1e-3) / 1e12)
+        log(f"{mode}: {T * steps / elapsed:.0f} tokens/s, {ms:.2f} ms/step (select {sel_ms:.2f} ms, attend "
+            f"{att_ms:.2f} ms = {results[mode]['attend_tflops']:.1f} TFLOP/s algorithmic, "
+            f"{results[mode]['executed_tflops']:.1f} TFLOP/s issued)")
+    worst = min(results, key=lambda m: results[m]["tokens_per_s"])
+    r = results[worst]
+    line = {
+        "metric": "training-time forward tokens/s (one layer, every position selects its own blocks)",
+        "value": round(r["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "seq_len": T, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": 128, "budget_tokens": args.budget, "kv_layout": w.layout,
+                   "mode": f"{worst} (slower of {','.join(results)})", "launch": "eager"},
+        "roofline": {"bound": "mfma", "kernel": "sas_prefill_attend (prefill_attend_kernel)",
+                     "achieved": round(r["attend_tflops"], 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(r["attend_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": r["algorithmic_flops"], "avg_launch_us": round(r["attend_ms"] * 1e3, 1),
+                     "issued_flops_per_launch": r["executed_flops"],
+                     "issued_frac": round(r["executed_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "modes": {m: {k: round(v, 4) for k, v in d.items()} for m, d in results.items()},
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+
+        def pooled(h_k, bt):
+            gk_o = np.zeros((w.n_pages, w.n_kv_heads, 128), np.uint16)
+            oracle.pool_blocks(h_k, bt[None, :].copy(), w.strides, w.n_kv_heads, np.zeros(nb, np.int32),
+                               np.arange(nb, dtype=np.int32), wl.host(w.w_k), wl.host(w.w_knorm), w.theta, gk_o)
+            return gk_o
+
+        line["cpu_baseline"] = cpu_baseline_prefill(w, pooled, args.budget, worst == "gated", args.cpu_seconds)
+        log(f"cpu baseline: {line['cpu_baseline']['value']:.1f} tokens/s on {line['cpu_baseline']['cores']} threads")
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +274,8 @@ def main():
                   f"supported (asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr, flush=True)
         sys.exit(2)
 
+    if args.workload.startswith("prefill"):
+        return run_prefill(args)
     import numpy as np
     import torch
     from learned_block_sparse_tok_amd import ops

@@ -42,6 +42,32 @@ def gpu_step(w: wl.Workload, gate_keys: torch.Tensor, gated: bool, budget: int |
                 scores=wl.host(dec.scores), out=bf16_out(dec.out))
 
 
+def prefill_gate_keys(w: wl.Workload) -> torch.Tensor:
+    """Gate keys of a prefill workload's complete blocks, pooled on the GPU."""
+    dev = w.q.device
+    nb = w.batch // 64
+    gk = torch.zeros((w.n_pages, w.n_kv_heads, wl.GATE_DIM), dtype=torch.bfloat16, device=dev)
+    shape1 = ops.make_shape(1, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides)
+    if nb:
+        ops.pool_blocks(shape1, w.k_pool, w.block_table[:1].contiguous(),
+                        torch.zeros(nb, dtype=torch.int32, device=dev), torch.arange(nb, dtype=torch.int32, device=dev),
+                        w.w_k, w.w_knorm, w.theta, gk)
+    return gk
+
+
+def gpu_prefill(w: wl.Workload, gk: torch.Tensor, gated: bool, budget: int, positions=None):
+    """sas_prefill_select + sas_prefill_attend over the whole sequence; the
+    results of `positions` (default all) copied to the host."""
+    dev = w.q.device
+    pf = ops.Prefill(w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, w.batch, budget, w.theta, gated,
+                     device=dev, keep_scores=True)
+    pf.forward(w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, w.block_table[0])
+    torch.cuda.synchronize()
+    idx = slice(None) if positions is None else torch.as_tensor(np.asarray(positions), device=dev)
+    return dict(sel=wl.host(pf.sel[idx]), gates=wl.host(pf.gates[idx]), cnt=wl.host(pf.cnt[idx]),
+                scores=wl.host(pf.scores[idx]), out=bf16_out(pf.out[idx]))
+
+
 def bf16_out(t: torch.Tensor) -> np.ndarray:
     return oracle.bf16_to_f64(wl.host(t))
 

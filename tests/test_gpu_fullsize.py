@@ -16,7 +16,9 @@ import pytest
 import torch
 
 import oracle
-from gpu_harness import assert_out_close, bf16_out, compare_step, gpu_pool
+import dataclasses
+
+from gpu_harness import assert_out_close, bf16_out, compare_step, gpu_pool, gpu_prefill, prefill_gate_keys
 from harness import SM_SCALE, Host, oracle_step
 from learned_block_sparse_tok_amd import ops
 from learned_block_sparse_tok_amd import workloads as wl
@@ -195,3 +197,32 @@ def test_ragged_incremental_serving(fused):
     ulp = 2.0 ** (np.floor(np.log2(np.abs(want) + 1e-30)) - 7)
     assert np.all(np.abs(got - want) <= ulp + 2e-5)
     say(f"ragged: {n} blocks pooled incrementally")
+
+
+def test_prefill_full_size_sampled_parity():
+    """Training-time forward of one 32,768-token sequence with Qwen3-8B heads
+    (32/8) at the 2,048 budget, in the launch configuration the benchmark
+    times; sampled positions (first and last of blocks, the first complete
+    candidate, the end) checked against the oracle's forward at those
+    positions, both modes."""
+    w = wl.named("prefill_8b", device=DEV)
+    T = w.batch
+    gk = prefill_gate_keys(w)
+    pos = np.array([0, 63, 64, 127, 128, 1000, 4095, 4096, 20000, 32766, 32767])
+    # the oracle sees the sampled positions as a batch sharing the one cache
+    sub = dataclasses.replace(w, batch=len(pos), q=w.q[torch.as_tensor(pos, device=DEV)],
+                              seq_lens=torch.as_tensor(pos + 1, dtype=torch.int32, device=DEV),
+                              block_table=w.block_table[:len(pos)])
+    h = Host(sub)
+    nb = T // 64
+    gk_o = np.zeros((w.n_pages, w.n_kv_heads, wl.GATE_DIM), np.uint16)
+    oracle.pool_blocks(h.k, h.bt[:1], w.strides, w.n_kv_heads, np.zeros(nb, np.int32), np.arange(nb, dtype=np.int32),
+                       h.w_k, h.wkn, w.theta, gk_o)
+    for gated in (False, True):
+        say(f"prefill_8b T={T} {'gated' if gated else 'plain'}: positions {pos.tolist()}")
+        g = gpu_prefill(w, gk, gated, w.budget, positions=pos)
+        sel, gates, cnt, scores, out = oracle.prefill(wl.host(w.q), h.k, h.v, h.bt[0], w.strides, w.n_kv_heads, gk_o,
+                                                      h.w_q, h.wqn, w.theta, w.budget, gated, SM_SCALE, positions=pos)
+        o = dict(gate_keys=gk_o, sel=sel, gates=gates, cnt=cnt, scores=scores, out=out)
+        ties, skipped = compare_step(h, g, o, gated, w.budget)
+        say(f"  boundary ties {ties}, unenumerated {skipped}")

@@ -15,8 +15,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_harness import (assert_out_close, bf16_out, compare_selection, compare_step, gpu_pool, gpu_step,
-                         shape_of)
+from gpu_harness import (assert_out_close, bf16_out, compare_selection, compare_step, gpu_pool, gpu_prefill,
+                         gpu_step, prefill_gate_keys, shape_of)
 from harness import SM_SCALE, Host, complete_blocks, oracle_gate_keys, oracle_step
 from learned_block_sparse_tok_amd import ops
 from learned_block_sparse_tok_amd import workloads as wl
@@ -143,27 +143,6 @@ PREFILL_CASES = [
     dict(name="paged_g16_tail1", T=577, Hq=16, Hkv=1, budget=320, layout="paged"),
     dict(name="full_budget", T=300, Hq=4, Hkv=1, budget=320, layout="paged"),
 ]
-
-
-def prefill_gate_keys(w):
-    """Gate keys of the sequence's complete blocks, pooled on the GPU."""
-    nb = w.batch // 64
-    gk = torch.zeros((w.n_pages, w.n_kv_heads, wl.GATE_DIM), dtype=torch.bfloat16, device=DEV)
-    shape1 = ops.make_shape(1, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides)
-    if nb:
-        ops.pool_blocks(shape1, w.k_pool, w.block_table[:1].contiguous(),
-                        torch.zeros(nb, dtype=torch.int32, device=DEV), torch.arange(nb, dtype=torch.int32, device=DEV),
-                        w.w_k, w.w_knorm, w.theta, gk)
-    return gk
-
-
-def gpu_prefill(w, gk, gated, budget):
-    pf = ops.Prefill(w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, w.batch, budget, w.theta, gated,
-                     device=DEV, keep_scores=True)
-    pf.forward(w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, w.block_table[0])
-    torch.cuda.synchronize()
-    return dict(sel=wl.host(pf.sel), gates=wl.host(pf.gates), cnt=wl.host(pf.cnt), scores=wl.host(pf.scores),
-                out=bf16_out(pf.out))
 
 
 @pytest.mark.parametrize("gated", [False, True], ids=["plain", "gated"])
