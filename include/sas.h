@@ -201,7 +201,8 @@ sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *
  * sas_prefill_attend -- the attention of every position over its selection:
  *   plain (gates NULL) or gated as in sas_sparse_decode, output bf16
  *   [T][Hq][128].  sel / gates / cnt as sas_prefill_select wrote them
- *   (max_sel = budget/64).  Needs no workspace.
+ *   (max_sel = budget/64 <= 64, i.e. budgets up to 4,096 tokens).  Needs no
+ *   workspace.
  */
 sas_status sas_prefill_select(const sas_shape *shape, const void *q, const void *w_q,
                               const float *w_qnorm, const void *gate_keys,

@@ -230,6 +230,7 @@ sas_status sas_prefill_attend(const sas_shape *shape, const void *q, const void 
   if (!q || !k_pool || !v_pool || !block_table_row || !sel || !cnt || !out)
     return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
   if (max_sel <= 0) return fail(SAS_ERR_INVALID_ARG, "max_sel must be positive");
+  if (max_sel > 64) return fail(SAS_ERR_UNSUPPORTED, "max_sel %d exceeds 64 (budgets above 4,096 tokens)", max_sel);
   if (!(sm_scale > 0.f)) return fail(SAS_ERR_INVALID_ARG, "sm_scale must be positive");
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
     return fail(SAS_ERR_UNSUPPORTED, "q, k_pool, v_pool and out must be 16-byte aligned");

@@ -11,17 +11,24 @@
 // One 256-thread workgroup per (64-query block, KV head, group of up to 4
 // query heads).  The workgroup marks the union of its queries' selections in
 // an LDS bitmap and walks it in ascending block order.  Each visited block's
-// K and V rows (32 KiB) are staged once in LDS and shared by the 4 waves; the
-// next block's loads are in flight while the current one is consumed (two
-// stages).  Wave w owns queries 16w .. 16w+15 of the block and the group's
-// heads:
+// K and V rows (32 KiB) are copied once into LDS by the gfx950 global-to-LDS
+// loads (global_load_lds_dwordx4) and shared by the 4 waves; a ring of four
+// 32 KiB stages keeps the next three blocks in flight while one is consumed.
+// The copies are the only vector-memory operations of the walk (the
+// selections of the 64 queries are staged in LDS first), so each iteration
+// waits for exactly the copies of the block it consumes.
+// Rows are stored unpadded (the copy writes 1 KiB per instruction) with a
+// row-dependent XOR swizzle instead: K's 16-byte slots by row % 16 (the
+// A-operand reads of 16 rows at one column hit 16 different slots), V's
+// 32-byte pairs by row % 4 (the transposing reads of 4 rows x 32 bytes hit 4
+// different pairs).  Wave w owns queries 16w .. 16w+15 of the block and the
+// group's heads:
 //   S^T (64 keys x 16 queries) = K . Q^T per head with
-//     v_mfma_f32_16x16x32_bf16, K read from LDS as the A operand (272-byte
-//     row pitch: conflict-free 16-byte reads);
+//     v_mfma_f32_16x16x32_bf16, K read from LDS as the A operand;
 //   the lane of a query that did not select the block masks its column to
 //     -inf; the query's own block is masked causally (key <= query);
 //   online softmax in the log2 domain; O^T += V^T . P^T, V^T read with
-//     ds_read_b64_tr_b16 from a 288-byte-pitch tile.
+//     ds_read_b64_tr_b16.
 // A wave none of whose 16 queries selected the block skips its arithmetic.
 // The work is a dense contraction per visited block: 4 heads x (64 QK + 64
 // PV) MFMAs per wave.
@@ -34,13 +41,51 @@ namespace sas {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunks = 64 * (kHeadDim * 2 / 16) / kThreads;  // 16-byte pieces of K (and V) per thread: 4
-constexpr int kKPitch = 272;
-constexpr int kVPitchP = 288;
-constexpr int kKTile = kBlock * kKPitch;
-constexpr int kStage = kKTile + kBlock * kVPitchP;  // 35 KiB
+constexpr int kRow = kHeadDim * 2;        // 256-byte K / V rows, unpadded
+constexpr int kTile = kBlock * kRow;      // 16 KiB
+constexpr int kStage = 2 * kTile;         // K tile, then V tile
+constexpr int kStages = 4;                // ring: 3 blocks in flight + 1 consumed
+constexpr int kCopies = kStage / 1024 / 4;  // 1 KiB copy instructions per wave per stage: 8
+constexpr int kMaxSel = 64;               // selections per query staged in LDS (budgets up to 4,096)
+
+// One global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
+// i's bytes land at LDS byte lds + 16 i.  Written out (rather than through the
+// builtin) so that the compiler, which does not track these LDS writes,
+// inserts no vmcnt(0) before every later LDS read; the instruction sequence is
+// the one the compiler emits for the builtin (M0 write, one wait state).
+// Completion is awaited explicitly with wait_vm.
+__device__ __forceinline__ void copy16(const void *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+}
+
+// s_waitcnt with only the vector-memory counter: at most n loads outstanding
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
 
 __device__ __forceinline__ bf16x8 as_bf16(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 2^x by the hardware instruction (results below the normal range flush to
+// zero, which a softmax weight can afford)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max / sum over the four 16-lane rows of a wave for each lane position l%16
+// (the lanes that hold one query's column), by the gfx950 row-swap moves:
+// permlane16_swap pairs rows (0,1) and (2,3), permlane32_swap pairs the halves
+__device__ __forceinline__ float rows_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 __device__ __forceinline__ uint32_t pack_rne(float lo, float hi) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -52,8 +97,11 @@ __device__ __forceinline__ uint32_t pack_rne(float lo, float hi) {
 
 template <bool kGated>
 __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage[2][kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kStage];
   __shared__ uint32_t bm[SAS_MAX_BLOCKS_DEV / 32];
+  __shared__ int16_t sel_l[kBlock][kMaxSel];
+  __shared__ float gate_l[kGated ? kBlock : 1][kMaxSel];
+  __shared__ int cnt_l[kBlock];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -74,38 +122,42 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
   const bool qvalid = qi < nq;
   const int tq = t0 + qi;
 
-  // ---- union of the block's selections (blocks 0 .. qb)
+  // ---- the queries' selections into LDS and their union (blocks 0 .. qb)
   const int nwords = (qb + 32) >> 5;
   for (int i = tid; i < nwords; i += kThreads) bm[i] = 0;
+  if (tid < kBlock) cnt_l[tid] = tid < nq ? p.cnt[(int64_t)(t0 + tid) * p.n_kv_heads + kvh] : 0;
   __syncthreads();
   for (int e = tid; e < nq * p.max_sel; e += kThreads) {
     const int q = e / p.max_sel, slot = e - q * p.max_sel;
-    const int64_t u = (int64_t)(t0 + q) * p.n_kv_heads + kvh;
-    if (slot < p.cnt[u]) {
-      const int c = p.sel[u * p.max_sel + slot];
-      if ((unsigned)c <= (unsigned)qb) atomicOr(&bm[c >> 5], 1u << (c & 31));
+    if (slot < cnt_l[q]) {
+      const int64_t u = ((int64_t)(t0 + q) * p.n_kv_heads + kvh) * p.max_sel + slot;
+      int c = p.sel[u];
+      c = (unsigned)c <= (unsigned)qb ? c : qb;  // out-of-range entries are not trusted
+      sel_l[q][slot] = (int16_t)c;
+      if (kGated) gate_l[kGated ? q : 0][slot] = p.gates[u];
+      atomicOr(&bm[c >> 5], 1u << (c & 31));
     }
   }
-  __syncthreads();
-
-  // ---- this lane's walk through its query's ascending selection
-  const int64_t uq = (int64_t)(qvalid ? tq : t0) * p.n_kv_heads + kvh;
-  const int32_t *selq = p.sel + uq * p.max_sel;
-  const float *gq = kGated ? p.gates + uq * p.max_sel : nullptr;
-  const int cq = qvalid ? p.cnt[uq] : 0;
-  int ptr = 0;
-  int nxt_c = cq > 0 ? selq[0] : INT_MAX;
-  float nxt_g = (kGated && cq > 0) ? gq[0] : 1.f;
 
   // B operand of S^T = K Q^T: lane l holds q[query qi][head][32ks + 8(l/16) .. +7]
   bf16x8 qB[4][4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     const bool ok = qvalid && ct < nh;
-    const uint16_t *qrow = p.q + ((int64_t)(ok ? tq : 0) * p.n_q_heads + kvh * G + 4 * hg + (ok ? ct : 0)) * kHeadDim + 8 * g;
+    const uint16_t *qrow =
+        p.q + ((int64_t)(ok ? tq : 0) * p.n_q_heads + kvh * G + 4 * hg + (ok ? ct : 0)) * kHeadDim + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qB[ct][ks] = as_bf16(ok ? ld16(qrow + 32 * ks) : u32x4{0, 0, 0, 0});
   }
+  wait_vm<0>();  // every compiler-visible load done before the copies start
+  __syncthreads();
+
+  // ---- this lane's walk through its query's ascending selection (LDS)
+  const int cq = cnt_l[qi];
+  int ptr = 0;
+  int nxt_c = cq > 0 ? sel_l[qi][0] : INT_MAX;
+  float nxt_g = kGated ? gate_l[kGated ? qi : 0][0] : 1.f;
+
   f32x4 o[4][8];
   float m[4], ls[4];
 #pragma unroll
@@ -116,30 +168,32 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
     ls[ct] = 0.f;
   }
 
+  // ---- block copies into the ring: wave w writes 1 KiB pieces 4w .. 4w+3 of
+  // the K tile and of the V tile (4 rows each); lane i of a piece lands at
+  // byte 16i of it, so it fetches the global 16 bytes that the swizzle puts
+  // there
   const char *kbase = reinterpret_cast<const char *>(p.k_pool) + (int64_t)kvh * p.head_stride * 2;
   const char *vbase = reinterpret_cast<const char *>(p.v_pool) + (int64_t)kvh * p.head_stride * 2;
   const int64_t tok_bytes = p.tok_stride * 2, page_bytes = p.page_stride * 2;
-  u32x4 kr[kChunks], vr[kChunks];
-  auto issue = [&](int c) {  // the block's K and V rows into registers (chunk i: row i/16, bytes 16(i%16))
-    const int64_t off = (int64_t)p.block_table[c] * page_bytes;
+  int64_t k_src[4], v_src[4];  // per-lane byte offsets inside a block
 #pragma unroll
-    for (int k = 0; k < kChunks; ++k) {
-      const int i = tid + kThreads * k;
-      const int64_t a = off + (i >> 4) * tok_bytes + 16 * (i & 15);
-      kr[k] = ld16(kbase + a);
-      vr[k] = ld16(vbase + a);
-    }
-  };
-  auto park = [&](int c, uint8_t *st) {  // registers -> LDS stage; V rows past the sequence end are zeroed
-    const int nvalid = min(kBlock, T - c * kBlock);
+  for (int k = 0; k < 4; ++k) {
+    const int row = 4 * (4 * wave + k) + (lane >> 4), sl = lane & 15;
+    k_src[k] = row * tok_bytes + 16 * (sl ^ (row & 15));
+    v_src[k] = row * tok_bytes + 32 * ((sl >> 1) ^ (row & 3)) + 16 * (sl & 1);
+  }
+  // the block table is read-only here: read it through the constant address
+  // space so that a uniform index gives a scalar load
+  const __attribute__((address_space(4))) int32_t *btc =
+      (const __attribute__((address_space(4))) int32_t *)p.block_table;
+  const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)&ring[0][0];
+  auto copy_block = [&](int c, int st) {
+    const int64_t off = (int64_t)btc[c] * page_bytes;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring0 + st * kStage + 4096 * wave);
 #pragma unroll
-    for (int k = 0; k < kChunks; ++k) {
-      const int i = tid + kThreads * k;
-      const int row = i >> 4, col = i & 15;
-      *reinterpret_cast<u32x4 *>(st + row * kKPitch + 16 * col) = kr[k];
-      *reinterpret_cast<u32x4 *>(st + kKTile + row * kVPitchP + 16 * col) =
-          row < nvalid ? vr[k] : u32x4{0, 0, 0, 0};
-    }
+    for (int k = 0; k < 4; ++k) copy16(kbase + off + k_src[k], dst + 1024 * k);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) copy16(vbase + off + v_src[k], dst + kTile + 1024 * k);
   };
   // uniform cursor over the bitmap
   int wi = 0;
@@ -154,33 +208,49 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
     return c;
   };
 
+  // prologue: the first three blocks of the walk (a missing one is replaced
+  // by a copy of the first into its unused stage, to keep the copy count fixed)
+  int c0 = next_block();  // never -1: every query selects its own block
+  int c1 = next_block();
+  int c2 = next_block();
+  copy_block(c0, 0);
+  copy_block(c1 >= 0 ? c1 : c0, 1);
+  copy_block(c2 >= 0 ? c2 : c0, 2);
+
   const int tr_e = (lane & 15) >> 2, tr_q = lane & 3;
-  int c = next_block();  // never -1: every query selects its own block
-  int buf = 0;
-  issue(c);
-  park(c, stage[0]);
-  __syncthreads();
-  while (c >= 0) {
-    const int cn = next_block();
-    if (cn >= 0) issue(cn);
-    // ---- attend block c from stage[buf]
+  for (int i = 0;; ++i) {
+    const int st = i & (kStages - 1);
+    const int c = c0;
+    wait_vm<2 * kCopies>();  // this wave's copies of block i landed (blocks i+1, i+2 may be in flight)
+    lds_barrier();           // ... and every other wave's; block i-1's stage is free
+    if (c * kBlock + kBlock > T) {  // the sequence's last, partial block: zero V rows past the end
+      uint8_t *vt = ring[st] + kTile;
+      for (int b = tid * 16 + (T - c * kBlock) * kRow; b < kTile; b += kThreads * 16)
+        *reinterpret_cast<u32x4 *>(vt + b) = u32x4{0, 0, 0, 0};
+      lds_barrier();
+    }
+    // block i+3 into the stage block i-1 used
+    const int c3 = next_block();
+    copy_block(c3 >= 0 ? c3 : c, (i + 3) & (kStages - 1));
+
+    // ---- attend block c
     const bool s_l = nxt_c == c;
     const float g_l = s_l ? nxt_g : 0.f;
     if (s_l) {
       ++ptr;
-      nxt_c = ptr < cq ? selq[ptr] : INT_MAX;
-      if (kGated) nxt_g = ptr < cq ? gq[ptr] : 1.f;
+      nxt_c = ptr < cq ? sel_l[qi][ptr] : INT_MAX;
+      if (kGated) nxt_g = gate_l[kGated ? qi : 0][min(ptr, kMaxSel - 1)];
     }
     if (__builtin_amdgcn_ballot_w64(s_l) != 0) {
-      const uint8_t *kt = stage[buf];
-      const uint8_t *vt = stage[buf] + kKTile;
+      const uint8_t *kt = ring[st];
+      const uint8_t *vt = ring[st] + kTile;
       f32x4 sacc[4][4];  // [head][key tile]
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         u32x4 ka[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          ka[ks] = *reinterpret_cast<const u32x4 *>(kt + (16 * t + j) * kKPitch + 64 * ks + 16 * g);
+          ka[ks] = *reinterpret_cast<const u32x4 *>(kt + (16 * t + j) * kRow + 16 * ((4 * ks + g) ^ j));
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           sacc[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -204,11 +274,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
             z[t][r] = keep ? sacc[ct][t][r] * p.scale_log2 : -__builtin_inff();
             mx = fmaxf(mx, z[t][r]);
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = rows_max(mx);
         const float m_new = fmaxf(m[ct], mx);
         const bool live = m_new != -__builtin_inff();
-        const float alpha = live ? exp2f(m[ct] - m_new) : 1.0f;
+        const float alpha = live ? fast_exp2(m[ct] - m_new) : 1.0f;
         float psum = 0.f;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -216,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int t = 2 * s2 + (e >> 2), r = e & 3;
-            const float pe = live ? exp2f(z[t][r] - m_new) : 0.f;
+            const float pe = live ? fast_exp2(z[t][r] - m_new) : 0.f;
             psum += pe;
             pv[e] = kGated ? pe * g_l : pe;
           }
@@ -225,21 +294,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
         }
         ls[ct] = ls[ct] * alpha + psum;
         m[ct] = m_new;
+        // the running max rarely moves once a query has seen a few blocks (and
+        // never for a query that did not select this one): rescale only then
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[ct][dt] *= alpha;
+          for (int dt = 0; dt < 8; ++dt) o[ct][dt] *= alpha;
+        }
       }
       // tr-read lane roles: within the 16-lane group g, lane 4e+q4 addresses
-      // row 4g+e (+16 for the upper half of the k-step, +32 per k-step),
-      // columns 16dt + 4q4 .. +3
-      const uint8_t *vrd = vt + (4 * g + tr_e) * kVPitchP + 8 * tr_q;
+      // row 4g+e (+16 for the upper half of the k-step, +32 per k-step), bytes
+      // 8q4 of the 32-byte pair dt, stored at pair dt ^ e (row % 4 == e)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4 *)(vrd + 32 * s2 * kVPitchP + 32 * dt));
-          i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4 *)(vrd + (32 * s2 + 16) * kVPitchP + 32 * dt));
+          const uint8_t *vrd = vt + (32 * s2 + 4 * g + tr_e) * kRow + 32 * (dt ^ tr_e) + 8 * tr_q;
+          i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)vrd);
+          i16x4 a1 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(vrd + 16 * kRow));
           u32x2 lo2 = __builtin_bit_cast(u32x2, a0), hi2 = __builtin_bit_cast(u32x2, a1);
           const bf16x8 a = as_bf16(u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
 #pragma unroll
@@ -248,18 +320,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
         }
       }
     }
-    if (cn >= 0) park(cn, stage[buf ^ 1]);
-    lds_barrier();
-    buf ^= 1;
-    c = cn;
+    if (c1 < 0) break;  // block i was the walk's last
+    c0 = c1;
+    c1 = c2;
+    c2 = c3;
   }
+  wait_vm<0>();  // the trailing filler copies land before the workgroup ends
 
   // ---- normalise and store: lane holds dims 16dt + 4(l/16) .. +3 of its query
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    float l = ls[ct];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = rows_sum(ls[ct]);
     if (qvalid && ct < nh) {
       const float inv = 1.0f / l;
       uint16_t *dst = p.out + ((int64_t)tq * p.n_q_heads + kvh * G + 4 * hg + ct) * kHeadDim + 4 * g;

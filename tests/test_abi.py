@@ -126,6 +126,7 @@ def test_prefill_rejects_bad_arguments(lib):
     assert att_call(sh=_shape(batch=3)) == ops.SAS_ERR_INVALID_ARG
     assert att_call(T=-5) == ops.SAS_ERR_INVALID_ARG
     assert att_call(max_sel=0) == ops.SAS_ERR_INVALID_ARG
+    assert att_call(max_sel=65) == ops.SAS_ERR_UNSUPPORTED
     assert att_call(out=None) == ops.SAS_ERR_INVALID_ARG
     assert att_call(out=ctypes.c_void_p(4096 + 8)) == ops.SAS_ERR_UNSUPPORTED  # not 16-byte aligned
 
