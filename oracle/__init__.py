@@ -26,6 +26,10 @@ _LIB = os.path.join(_HERE, "_sas_oracle.so")
 BLOCK = 64
 HEAD_DIM = 128
 GATE_DIM = 128
+# alternative readings: how a group's per-head scores make one score, and how
+# a gate enters attention ("scale" its block's share / "logit" a log bias)
+AGGREGATE = {"mean": 0, "max": 1}
+GATE_MODE = {"scale": 0, "logit": 1}
 _lib = None
 
 
@@ -147,7 +151,7 @@ def gate_query(q, w_q, w_qnorm, theta, seq_len, s, h) -> np.ndarray:
 
 
 def gate_topk(q, w_q, w_qnorm, gate_keys, block_table, seq_lens, theta, budget_tokens,
-              n_kv_heads):
+              n_kv_heads, aggregate="mean"):
     """Gate stage for the batch.  Returns (sel, gates, cnt, scores):
     sel int32 [B][Hkv][budget/64] (ascending, local block last, -1 padded),
     gates f32 (same shape; sigmoid(score), 1 for the local block, 0 padding),
@@ -160,10 +164,10 @@ def gate_topk(q, w_q, w_qnorm, gate_keys, block_table, seq_lens, theta, budget_t
     gates = np.zeros((B, n_kv_heads, n_sel), np.float32)
     cnt = np.zeros((B, n_kv_heads), np.int32)
     scores = np.zeros((B, n_kv_heads, max_blocks), np.float32)
-    _load().sas_oracle_gate_topk(ctypes.byref(sh), _p(q), _p(w_q), _p(w_qnorm), _p(gate_keys),
-                                 _p(block_table), _p(np.ascontiguousarray(seq_lens, np.int32)),
-                                 ctypes.c_double(theta), ctypes.c_int32(budget_tokens), _p(sel),
-                                 _p(gates), _p(cnt), _p(scores))
+    _load().sas_oracle_gate_topk_ex(ctypes.byref(sh), _p(q), _p(w_q), _p(w_qnorm), _p(gate_keys),
+                                    _p(block_table), _p(np.ascontiguousarray(seq_lens, np.int32)),
+                                    ctypes.c_double(theta), ctypes.c_int32(budget_tokens),
+                                    ctypes.c_int(AGGREGATE[aggregate]), _p(sel), _p(gates), _p(cnt), _p(scores))
     return sel, gates, cnt, scores
 
 
@@ -189,7 +193,7 @@ def block_gates(scores: np.ndarray, sel: np.ndarray, cnt: int) -> np.ndarray:
 
 
 def attend(q, k_pool, v_pool, block_table, strides, n_kv_heads, seq_lens, sel, gates, cnt,
-           sm_scale, pairs=None):
+           sm_scale, pairs=None, gate_mode="scale"):
     """Dense masked softmax attention.  gates=None is plain Top-K mode.
     pairs: optional int32 [n][2] list of (sequence, query head); default all.
     Returns fp64 [n][128] (or [B][Hq][128] when pairs is None)."""
@@ -208,7 +212,8 @@ def attend(q, k_pool, v_pool, block_table, strides, n_kv_heads, seq_lens, sel, g
                               _p(np.ascontiguousarray(seq_lens, np.int32)),
                               _p(np.ascontiguousarray(sel, np.int32)), _p(g),
                               _p(np.ascontiguousarray(cnt, np.int32)), ctypes.c_int32(n_sel),
-                              ctypes.c_double(sm_scale), _p(pairs), ctypes.c_int64(n), _p(out))
+                              ctypes.c_double(sm_scale), ctypes.c_int(GATE_MODE[gate_mode]), _p(pairs),
+                              ctypes.c_int64(n), _p(out))
     return out if pairs is not None else out.reshape(B, Hq, HEAD_DIM)
 
 

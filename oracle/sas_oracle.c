@@ -238,10 +238,14 @@ void sas_oracle_gate_query(const uint16_t *q /* [B][Hq][128] */, int n_q_heads, 
  * READING: one selection per KV head, scored by the mean of its G query
  * heads' scores.  The result is rounded to fp32 (the precision in which the
  * GPU takes the same ranking decision).  scores[c] for c >= l is left as is. */
-void sas_oracle_block_scores(const oracle_shape *sh, const uint16_t *q, const uint16_t *w_q,
-                             const float *w_qnorm, const uint16_t *gate_keys,
-                             const int32_t *block_table, const int32_t *seq_lens,
-                             double theta, int s, int kvh, float *scores) {
+/* Block scores of one (sequence, KV head).  aggregate 0: the mean of the
+ * group's per-head scores (the default reading); 1: their maximum (the
+ * alternative reading of how one selection per KV head comes from a group of
+ * query heads). */
+void sas_oracle_block_scores_ex(const oracle_shape *sh, const uint16_t *q, const uint16_t *w_q,
+                                const float *w_qnorm, const uint16_t *gate_keys,
+                                const int32_t *block_table, const int32_t *seq_lens,
+                                double theta, int s, int kvh, int aggregate, float *scores) {
   int G = sh->n_q_heads / sh->n_kv_heads;
   int32_t L = seq_lens[s];
   int local = (L - 1) / BLOCK;
@@ -251,15 +255,24 @@ void sas_oracle_block_scores(const oracle_shape *sh, const uint16_t *q, const ui
   for (int c = 0; c < local; ++c) {
     int32_t page = block_table[(int64_t)s * sh->max_blocks + c];
     const uint16_t *gk = gate_keys + ((int64_t)page * sh->n_kv_heads + kvh) * GATE_DIM;
-    double mean = 0.0;
+    double mean = 0.0, mx = -INFINITY;
     for (int g = 0; g < G; ++g) {
       double dot = 0.0;
       for (int j = 0; j < GATE_DIM; ++j) dot += gq[g * GATE_DIM + j] * bf16_value(gk[j]);
       mean += dot / sqrt((double)GATE_DIM);
+      if (dot / sqrt((double)GATE_DIM) > mx) mx = dot / sqrt((double)GATE_DIM);
     }
-    scores[c] = (float)(mean / G);
+    scores[c] = (float)(aggregate == 1 ? mx : mean / G);
   }
   free(gq);
+}
+
+void sas_oracle_block_scores(const oracle_shape *sh, const uint16_t *q, const uint16_t *w_q,
+                             const float *w_qnorm, const uint16_t *gate_keys,
+                             const int32_t *block_table, const int32_t *seq_lens,
+                             double theta, int s, int kvh, float *scores) {
+  sas_oracle_block_scores_ex(sh, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, theta, s, kvh, 0,
+                             scores);
 }
 
 typedef struct {
@@ -329,11 +342,11 @@ int32_t sas_oracle_select(const float *scores, int32_t seq_len, int32_t budget_t
 
 /* Gate stage for the whole batch: scores_out [B][Hkv][max_blocks] (nullable;
  * entries c >= l are set to -inf), sel/gates [B][Hkv][budget/64], cnt [B][Hkv]. */
-void sas_oracle_gate_topk(const oracle_shape *sh, const uint16_t *q, const uint16_t *w_q,
-                          const float *w_qnorm, const uint16_t *gate_keys,
-                          const int32_t *block_table, const int32_t *seq_lens, double theta,
-                          int32_t budget_tokens, int32_t *sel, float *gates, int32_t *cnt,
-                          float *scores_out) {
+void sas_oracle_gate_topk_ex(const oracle_shape *sh, const uint16_t *q, const uint16_t *w_q,
+                             const float *w_qnorm, const uint16_t *gate_keys,
+                             const int32_t *block_table, const int32_t *seq_lens, double theta,
+                             int32_t budget_tokens, int aggregate, int32_t *sel, float *gates,
+                             int32_t *cnt, float *scores_out) {
   int n_sel = budget_tokens / BLOCK;
   int64_t units = (int64_t)sh->batch * sh->n_kv_heads;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -341,12 +354,22 @@ void sas_oracle_gate_topk(const oracle_shape *sh, const uint16_t *q, const uint1
     int s = (int)(u / sh->n_kv_heads), kvh = (int)(u % sh->n_kv_heads);
     float *scores = (float *)malloc(sizeof(float) * (sh->max_blocks > 0 ? sh->max_blocks : 1));
     for (int c = 0; c < sh->max_blocks; ++c) scores[c] = -INFINITY;
-    sas_oracle_block_scores(sh, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, theta, s, kvh, scores);
+    sas_oracle_block_scores_ex(sh, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, theta, s, kvh,
+                               aggregate, scores);
     cnt[u] = sas_oracle_select(scores, seq_lens[s], budget_tokens, sel + u * n_sel,
                                gates ? gates + u * n_sel : NULL);
     if (scores_out) memcpy(scores_out + u * sh->max_blocks, scores, sizeof(float) * sh->max_blocks);
     free(scores);
   }
+}
+
+void sas_oracle_gate_topk(const oracle_shape *sh, const uint16_t *q, const uint16_t *w_q,
+                          const float *w_qnorm, const uint16_t *gate_keys,
+                          const int32_t *block_table, const int32_t *seq_lens, double theta,
+                          int32_t budget_tokens, int32_t *sel, float *gates, int32_t *cnt,
+                          float *scores_out) {
+  sas_oracle_gate_topk_ex(sh, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, theta, budget_tokens, 0,
+                          sel, gates, cnt, scores_out);
 }
 
 /* ------------------------------------------------------------------ */
@@ -362,8 +385,8 @@ void sas_oracle_gate_topk(const oracle_shape *sh, const uint16_t *q, const uint1
 void sas_oracle_attend_head(const oracle_shape *sh, const uint16_t *q, const uint16_t *k_pool,
                             const uint16_t *v_pool, const int32_t *block_table,
                             const int32_t *seq_lens, const int32_t *sel, const float *gates,
-                            const int32_t *cnt, int32_t n_sel, double sm_scale, int s, int h,
-                            double *out /* [128] */) {
+                            const int32_t *cnt, int32_t n_sel, double sm_scale, int gate_mode,
+                            int s, int h, double *out /* [128] */) {
   int G = sh->n_q_heads / sh->n_kv_heads;
   int kvh = h / G;
   int32_t L = seq_lens[s];
@@ -397,15 +420,20 @@ void sas_oracle_attend_head(const oracle_shape *sh, const uint16_t *q, const uin
     z[j] = keep[j] ? dot * sm_scale : -INFINITY;
     if (z[j] > zmax) zmax = z[j];
   }
+  /* gate_mode 0: softmax over the selected tokens, then each token's weight
+   * scaled by its block's gate (the default reading).  gate_mode 1: the gate
+   * as a factor on exp(logit) before normalising (a log-gate bias on the
+   * logits, the alternative reading). */
   double denom = 0.0;
   for (int j = 0; j < L; ++j) {
     z[j] = keep[j] ? exp(z[j] - zmax) : 0.0;
+    if (gate_mode == 1) z[j] *= gate_tok[j];
     denom += z[j];
   }
   for (int d = 0; d < HEAD_DIM; ++d) out[d] = 0.0;
   for (int j = 0; j < L; ++j) {
     double p = denom > 0 ? z[j] / denom : 0.0; /* 0 for masked tokens */
-    double w = p * gate_tok[j];
+    double w = gate_mode == 1 ? p : p * gate_tok[j];
     const uint16_t *vr = kv_row(sh, v_pool, block_table, s, kvh, j);
     for (int d = 0; d < HEAD_DIM; ++d) out[d] += w * bf16_value(vr[d]);
   }
@@ -421,7 +449,7 @@ void sas_oracle_attend_head(const oracle_shape *sh, const uint16_t *q, const uin
 void sas_oracle_attend(const oracle_shape *sh, const uint16_t *q, const uint16_t *k_pool,
                        const uint16_t *v_pool, const int32_t *block_table,
                        const int32_t *seq_lens, const int32_t *sel, const float *gates,
-                       const int32_t *cnt, int32_t n_sel, double sm_scale,
+                       const int32_t *cnt, int32_t n_sel, double sm_scale, int gate_mode,
                        const int32_t *pairs /* [n][2] or NULL */, int64_t n_pairs, double *out) {
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t i = 0; i < n_pairs; ++i) {
@@ -434,7 +462,7 @@ void sas_oracle_attend(const oracle_shape *sh, const uint16_t *q, const uint16_t
       h = (int)(i % sh->n_q_heads);
     }
     sas_oracle_attend_head(sh, q, k_pool, v_pool, block_table, seq_lens, sel, gates, cnt, n_sel,
-                           sm_scale, s, h, out + i * HEAD_DIM);
+                           sm_scale, gate_mode, s, h, out + i * HEAD_DIM);
   }
 }
 

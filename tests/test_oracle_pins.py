@@ -531,3 +531,65 @@ def test_prefill_positions_subset_matches_full():
                           positions=pos)
     for a, b in zip(full, part):
         np.testing.assert_array_equal(a[pos], b)
+
+
+# ---------------------------------------------------------------- alternative readings (flags)
+@pytest.mark.parametrize("maker", [small_paged, small_contig])
+def test_logit_gate_mode_matches_sdpa_with_log_gate_bias(maker):
+    """Gate as a log-bias on the logits: softmax over the selected tokens of
+    z_j + log g_block(j) (torch SDPA with an additive float mask)."""
+    w = maker()
+    h = Host(w)
+    sel, gates, cnt = wl.random_selection(h.lens, w.n_kv_heads, w.budget, seed=17)
+    got = oracle.attend(h.q, h.k, h.v, h.bt, w.strides, w.n_kv_heads, h.lens, sel, gates, cnt, SM_SCALE,
+                        gate_mode="logit")
+    G = w.group
+    for s in range(w.batch):
+        L = int(h.lens[s])
+        for kvh in range(w.n_kv_heads):
+            blocks = sel[s, kvh, :cnt[s, kvh]]
+            gmap = dict(zip(blocks.tolist(), gates[s, kvh, :cnt[s, kvh]].tolist()))
+            bias = torch.tensor([math.log(gmap[j // 64]) if j // 64 in gmap else -math.inf for j in range(L)],
+                                dtype=torch.float64)
+            K = torch.from_numpy(dense_kv(h, h.k, s, kvh))
+            V = torch.from_numpy(dense_kv(h, h.v, s, kvh))
+            qh = torch.from_numpy(oracle.bf16_to_f64(h.q[s, kvh * G:(kvh + 1) * G]))
+            o = F.scaled_dot_product_attention(qh[None, :, None, :], K[None, None].expand(1, G, L, 128),
+                                               V[None, None].expand(1, G, L, 128),
+                                               attn_mask=bias[None, None, None, :], scale=SM_SCALE)
+            np.testing.assert_allclose(got[s, kvh * G:(kvh + 1) * G], o[0, :, 0].numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_logit_gate_mode_ignores_a_common_gate():
+    # a log-bias shared by every selected token cancels in the softmax
+    w = small_paged()
+    h = Host(w)
+    sel, gates, cnt = wl.random_selection(h.lens, w.n_kv_heads, w.budget, seed=18)
+    plain = oracle.attend(h.q, h.k, h.v, h.bt, w.strides, w.n_kv_heads, h.lens, sel, None, cnt, SM_SCALE)
+    same = np.where(sel >= 0, np.float32(0.3), np.float32(0))
+    got = oracle.attend(h.q, h.k, h.v, h.bt, w.strides, w.n_kv_heads, h.lens, sel, same, cnt, SM_SCALE,
+                        gate_mode="logit")
+    np.testing.assert_allclose(got, plain, rtol=1e-12, atol=1e-14)
+
+
+def test_max_aggregation_scores_and_selection():
+    """Max over the group's per-head scores (per-head gate queries pinned
+    against torch above), and the Top-K of those scores."""
+    w = small_paged()
+    h = Host(w)
+    gk = oracle_gate_keys(h)
+    sel, gates, cnt, scores = oracle.gate_topk(h.q, h.w_q, h.wqn, gk, h.bt, h.lens, w.theta, w.budget, w.n_kv_heads,
+                                               aggregate="max")
+    G = w.group
+    for s in range(w.batch):
+        local = (int(h.lens[s]) - 1) // 64
+        for kvh in range(w.n_kv_heads):
+            gq = np.stack([oracle.gate_query(h.q, h.w_q, h.wqn, w.theta, int(h.lens[s]), s, kvh * G + g)
+                           for g in range(G)])
+            keys = oracle.bf16_to_f64(gk[h.bt[s, :local], kvh])
+            want = (keys @ gq.T / math.sqrt(128)).max(axis=1).astype(np.float32)
+            np.testing.assert_allclose(scores[s, kvh, :local], want, rtol=1e-6, atol=1e-7)
+            k = min(w.budget // 64 - 1, local)
+            order = np.lexsort((np.arange(local), -scores[s, kvh, :local].astype(np.float64)))
+            assert sel[s, kvh, :k].tolist() == sorted(order[:k].tolist())
+            assert cnt[s, kvh] == k + 1 and sel[s, kvh, k] == local
