@@ -147,8 +147,7 @@ sas_status sas_append_kv(const sas_shape *shape, const void *k_new, const void *
  *   gates  fp32   sigmoid(score) per selected historical block, 1 for the
  *                 local block (nullable: not written)
  *   cnt    int32  [B][Hkv] number of selected blocks (>= 1)
- *   scores fp32   [B][Hkv][max_blocks] block scores (entries c >= l are -inf;
- *                 nullable: not written)
+ *   scores fp32   [B][Hkv][max_blocks] block scores (entries c >= l are -inf)
  * budget_tokens: a positive multiple of 64, at most 64 * 256.
  */
 sas_status sas_gate_topk(const sas_shape *shape, const void *q, const void *w_q,
@@ -180,6 +179,38 @@ sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *
                              const int32_t *seq_lens, const int32_t *sel, const float *gates,
                              const int32_t *cnt, int32_t max_sel, float sm_scale, void *out,
                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Alternative readings, as options of the decode calls.  The pages say that
+ * one selection serves a KV head (per-KV-head Top-K) and that continuous gates
+ * sit on the selected blocks, but not how a group of query heads makes one
+ * score nor how a gate enters attention.  The calls above use the mean of
+ * the group's per-head scores and scale each selected block's share of the
+ * output by its gate; these variants take the other plain readings:
+ *   aggregate  SAS_AGG_MEAN  mean of the group's per-head scores (default)
+ *              SAS_AGG_MAX   their maximum (group of at most 8 query heads)
+ *   gate_mode  SAS_GATE_SCALE  out = sum_j g(j) P_j V_j, P the softmax over
+ *                              the selection (default)
+ *              SAS_GATE_LOGIT  out = sum_j P'_j V_j, P' the softmax over the
+ *                              selection of z_j + log g(j) (a log-gate bias)
+ * g(j) is the gate of token j's block.  Otherwise identical to sas_gate_topk
+ * and sas_sparse_decode (gate_mode is ignored when gates is NULL).
+ */
+#define SAS_AGG_MEAN 0
+#define SAS_AGG_MAX 1
+#define SAS_GATE_SCALE 0
+#define SAS_GATE_LOGIT 1
+sas_status sas_gate_topk_ex(const sas_shape *shape, const void *q, const void *w_q,
+                            const float *w_qnorm, const void *gate_keys, const int32_t *block_table,
+                            const int32_t *seq_lens, double rope_theta, int32_t budget_tokens,
+                            int32_t aggregate, int32_t *sel, float *gates, int32_t *cnt, float *scores,
+                            void *stream);
+sas_status sas_sparse_decode_ex(const sas_shape *shape, const void *q, const void *k_pool,
+                                const void *v_pool, const int32_t *block_table,
+                                const int32_t *seq_lens, const int32_t *sel, const float *gates,
+                                int32_t gate_mode, const int32_t *cnt, int32_t max_sel,
+                                float sm_scale, void *out, void *workspace, size_t workspace_bytes,
+                                void *stream);
 
 /*
  * Training-time forward of one sequence (every position is a query).  SAS

@@ -135,13 +135,17 @@ sas_status sas_append_kv(const sas_shape *shape, const void *k_new, const void *
   return hip_status(sas::launch_append(p, shape->batch, (hipStream_t)stream), "sas_append_kv launch");
 }
 
-sas_status sas_gate_topk(const sas_shape *shape, const void *q, const void *w_q, const float *w_qnorm,
-                         const void *gate_keys, const int32_t *block_table, const int32_t *seq_lens,
-                         double rope_theta, int32_t budget_tokens, int32_t *sel, float *gates, int32_t *cnt,
-                         float *scores, void *stream) {
+sas_status sas_gate_topk_ex(const sas_shape *shape, const void *q, const void *w_q, const float *w_qnorm,
+                            const void *gate_keys, const int32_t *block_table, const int32_t *seq_lens,
+                            double rope_theta, int32_t budget_tokens, int32_t aggregate, int32_t *sel, float *gates,
+                            int32_t *cnt, float *scores, void *stream) {
   sas_status st = check_shape(shape, false);
   if (st) return st;
-  if (!q || !w_q || !w_qnorm || !gate_keys || !block_table || !seq_lens || !sel || !cnt)
+  if (aggregate != SAS_AGG_MEAN && aggregate != SAS_AGG_MAX)
+    return fail(SAS_ERR_INVALID_ARG, "unknown score aggregation %d", aggregate);
+  if (aggregate == SAS_AGG_MAX && shape->n_q_heads / shape->n_kv_heads > 8)
+    return fail(SAS_ERR_UNSUPPORTED, "max aggregation supports groups of at most 8 query heads");
+  if (!q || !w_q || !w_qnorm || !gate_keys || !block_table || !seq_lens || !sel || !cnt || !scores)
     return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
   if (budget_tokens < SAS_BLOCK || budget_tokens % SAS_BLOCK)
     return fail(SAS_ERR_INVALID_ARG, "budget_tokens (%d) must be a positive multiple of %d", budget_tokens,
@@ -168,8 +172,17 @@ sas_status sas_gate_topk(const sas_shape *shape, const void *q, const void *w_q,
   p.max_blocks = shape->max_blocks;
   p.n_sel = budget_tokens / SAS_BLOCK;
   p.bt_row_stride = shape->max_blocks;
+  p.aggregate = aggregate;
   for (int i = 0; i < SAS_GATE_DIM / 2; ++i) p.inv_freq[i] = pow(rope_theta, -(double)i / (SAS_GATE_DIM / 2));
   return hip_status(sas::launch_gate_topk(p, shape->batch, (hipStream_t)stream), "sas_gate_topk launch");
+}
+
+sas_status sas_gate_topk(const sas_shape *shape, const void *q, const void *w_q, const float *w_qnorm,
+                         const void *gate_keys, const int32_t *block_table, const int32_t *seq_lens,
+                         double rope_theta, int32_t budget_tokens, int32_t *sel, float *gates, int32_t *cnt,
+                         float *scores, void *stream) {
+  return sas_gate_topk_ex(shape, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, rope_theta, budget_tokens,
+                          SAS_AGG_MEAN, sel, gates, cnt, scores, stream);
 }
 
 namespace {
@@ -217,6 +230,7 @@ sas_status sas_prefill_select(const sas_shape *shape, const void *q, const void 
   p.max_blocks = shape->max_blocks;
   p.n_sel = budget_tokens / SAS_BLOCK;
   p.bt_row_stride = 0;
+  p.aggregate = SAS_AGG_MEAN;
   for (int i = 0; i < SAS_GATE_DIM / 2; ++i) p.inv_freq[i] = pow(rope_theta, -(double)i / (SAS_GATE_DIM / 2));
   return hip_status(sas::launch_gate_topk(p, seq_len, (hipStream_t)stream), "sas_prefill_select launch");
 }
@@ -277,12 +291,14 @@ size_t sas_sparse_decode_workspace_bytes(const sas_shape *shape, int32_t max_sel
   return decode_workspace(shape, max_sel).total;
 }
 
-sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *k_pool, const void *v_pool,
-                             const int32_t *block_table, const int32_t *seq_lens, const int32_t *sel,
-                             const float *gates, const int32_t *cnt, int32_t max_sel, float sm_scale, void *out,
-                             void *workspace, size_t workspace_bytes, void *stream) {
+sas_status sas_sparse_decode_ex(const sas_shape *shape, const void *q, const void *k_pool, const void *v_pool,
+                                const int32_t *block_table, const int32_t *seq_lens, const int32_t *sel,
+                                const float *gates, int32_t gate_mode, const int32_t *cnt, int32_t max_sel,
+                                float sm_scale, void *out, void *workspace, size_t workspace_bytes, void *stream) {
   sas_status st = check_shape(shape, true);
   if (st) return st;
+  if (gate_mode != SAS_GATE_SCALE && gate_mode != SAS_GATE_LOGIT)
+    return fail(SAS_ERR_INVALID_ARG, "unknown gate mode %d", gate_mode);
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !sel || !cnt || !out || !workspace)
     return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
   if (max_sel <= 0) return fail(SAS_ERR_INVALID_ARG, "max_sel must be positive");
@@ -316,8 +332,17 @@ sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *
   p.max_sel = max_sel;
   p.wg_per_unit = sp.wg_per_unit;
   p.blocks_per_wave = sp.blocks_per_wave;
+  p.gate_mode = gate_mode;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
   return hip_status(sas::launch_decode(p, shape->batch, (hipStream_t)stream), "sas_sparse_decode launch");
+}
+
+sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *k_pool, const void *v_pool,
+                             const int32_t *block_table, const int32_t *seq_lens, const int32_t *sel,
+                             const float *gates, const int32_t *cnt, int32_t max_sel, float sm_scale, void *out,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  return sas_sparse_decode_ex(shape, q, k_pool, v_pool, block_table, seq_lens, sel, gates, SAS_GATE_SCALE, cnt,
+                              max_sel, sm_scale, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

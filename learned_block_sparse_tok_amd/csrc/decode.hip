@@ -95,7 +95,10 @@ struct BlockSrc {
 // One selected block, with the next block's loads issued as soon as the
 // registers they land in are free: V rows go to the LDS tile, V(next) is
 // issued; S^T = K Q^T, K(next) is issued; online softmax; O^T += V^T P^T.
-template <bool kGated, bool kNext>
+// kMode: 0 plain Top-K attention; 1 each selected block's share of the
+// output scaled by its gate; 2 the gate as a factor on exp(logit) before
+// normalising (a log-gate bias on the block's logits)
+template <int kMode, bool kNext>
 __device__ __forceinline__ void attend_block(WaveState &w, BlockRegs &b, const BlockSrc &cur, const BlockSrc &nxt,
                                              const bf16x8 (&qB)[4], const LaneOffsets &lo, uint8_t *vt,
                                              float scale_log2, int g, int j, int tr_e, int tr_q) {
@@ -146,8 +149,8 @@ __device__ __forceinline__ void attend_block(WaveState &w, BlockRegs &b, const B
     for (int e = 0; e < 8; ++e) {
       const int t = 2 * s2 + (e >> 2), r = e & 3;
       const float pe = live ? exp2f(z[t][r] - m_new) : 0.f;
-      psum += pe;
-      pv[e] = kGated ? pe * cur.gate : pe;
+      pv[e] = kMode ? pe * cur.gate : pe;
+      psum += kMode == 2 ? pv[e] : pe;
     }
     pB[s2] = u32x4{pack2(pv[0], pv[1]), pack2(pv[2], pv[3]), pack2(pv[4], pv[5]), pack2(pv[6], pv[7])};
   }
@@ -181,7 +184,7 @@ __device__ __forceinline__ void attend_block(WaveState &w, BlockRegs &b, const B
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <bool kGated>
+template <int kMode>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t vlds[kWaves][kVTileBytes];
   // the wave index is uniform: keep it (and everything derived) in scalar registers
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
   ws.lsum = 0.f;
   uint8_t *vt = vlds[wave];
   const int32_t *sel = p.sel + (int64_t)unit * p.max_sel;
-  const float *gts = kGated ? p.gates + (int64_t)unit * p.max_sel : nullptr;
+  const float *gts = kMode ? p.gates + (int64_t)unit * p.max_sel : nullptr;
   const int32_t *bt = p.block_table + (int64_t)s * p.max_blocks;
   const char *kpool = reinterpret_cast<const char *>(p.k_pool) + (int64_t)kvh * p.head_stride * 2;
   const char *vpool = reinterpret_cast<const char *>(p.v_pool) + (int64_t)kvh * p.head_stride * 2;
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
   auto source = [&](int i) {
     const int blk = sel[i];
     const int64_t off = (int64_t)bt[blk] * page_bytes;
-    return BlockSrc{kpool + off, vpool + off, min(kBlock, L - blk * kBlock), kGated ? gts[i] : 1.0f};
+    return BlockSrc{kpool + off, vpool + off, min(kBlock, L - blk * kBlock), kMode ? gts[i] : 1.0f};
   };
 
   if (i0 < i1) {
@@ -244,10 +247,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
       for (int ks = 0; ks < 4; ++ks) b.k[t][ks] = ld16_kv<SAS_K_NT>(cur.k + t * lo.k_tile + 64 * ks + lo.k);
     for (int i = i0; i + 1 < i1; ++i) {
       const BlockSrc nxt = source(i + 1);
-      attend_block<kGated, true>(ws, b, cur, nxt, qB, lo, vt, p.scale_log2, g, j, tr_e, tr_q);
+      attend_block<kMode, true>(ws, b, cur, nxt, qB, lo, vt, p.scale_log2, g, j, tr_e, tr_q);
       cur = nxt;
     }
-    attend_block<kGated, false>(ws, b, cur, cur, qB, lo, vt, p.scale_log2, g, j, tr_e, tr_q);
+    attend_block<kMode, false>(ws, b, cur, cur, qB, lo, vt, p.scale_log2, g, j, tr_e, tr_q);
   }
 
   // ---- merge the waves (each parks (o, m, l) in its own V tile)
@@ -338,10 +341,12 @@ DecodeSplit decode_split(int batch, int n_kv_heads, int max_sel) {
 hipError_t launch_decode(const DecodeParams &p, int batch, hipStream_t st) {
   const unsigned units = (unsigned)(batch * p.n_kv_heads);
   const dim3 grid(units * (unsigned)p.wg_per_unit);
-  if (p.gates)
-    hipLaunchKernelGGL((decode_kernel<true>), grid, dim3(kWaves * 64), 0, st, p);
+  if (!p.gates)
+    hipLaunchKernelGGL((decode_kernel<0>), grid, dim3(kWaves * 64), 0, st, p);
+  else if (p.gate_mode == 0)
+    hipLaunchKernelGGL((decode_kernel<1>), grid, dim3(kWaves * 64), 0, st, p);
   else
-    hipLaunchKernelGGL((decode_kernel<false>), grid, dim3(kWaves * 64), 0, st, p);
+    hipLaunchKernelGGL((decode_kernel<2>), grid, dim3(kWaves * 64), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.wg_per_unit == 1) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(units), dim3(256), 0, st, p);

@@ -45,6 +45,12 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
+// kMax: a candidate's score is the maximum over the group's query heads of
+// <gate query, gate key> / sqrt(128) (group <= 8) instead of their mean.
+// kPositions: batch entry s is position s of one sequence (length s + 1, the
+// sequence's one block-table row, scores optional), for the training-time
+// forward; a compile-time switch keeps the decode path's code unchanged.
+template <bool kMax, bool kPositions>
 __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
   // [max(max_blocks, 512)]: block-table row, then score keys
   extern __shared__ __attribute__((aligned(16))) uint32_t slot[];
@@ -60,7 +66,7 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane16 = t & 15, grp = t >> 4;
   const int G = p.group;
-  const int32_t L = p.seq_lens ? p.seq_lens[s] : s + 1;
+  const int32_t L = kPositions ? s + 1 : p.seq_lens[s];
   const int n = (L - 1) / kBlock;  // candidates: the blocks before the local block
   const int k_eff = min(p.n_sel - 1, n);
 
@@ -77,7 +83,7 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
   const u32x4 qpiece = ld16(qg + (has_q ? 8 * t : 0));
   const double inv_freq = p.inv_freq[lane];
   const float wqn_a = p.w_qnorm[lane], wqn_b = p.w_qnorm[lane + 64];
-  const int32_t *bt = p.block_table + (int64_t)s * p.bt_row_stride;
+  const int32_t *bt = kPositions ? p.block_table : p.block_table + (int64_t)s * p.max_blocks;
   constexpr int kBtUnroll = 4;  // rows of up to 1,024 blocks staged without a loop
   int32_t btv[kBtUnroll];
 #pragma unroll
@@ -146,8 +152,13 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
       const float a = vs[g][lane], b = vs[g][lane + 64];
       const float inv = 1.0f / sqrtf(wave_sum(a * a + b * b) * (1.0f / kGateDim) + 1e-6f);
       const float na = a * inv * wa, nb = b * inv * wb;
-      sa += na * cf - nb * sf;
-      sb += nb * cf + na * sf;
+      const float ra = na * cf - nb * sf, rb = nb * cf + na * sf;
+      sa += ra;
+      sb += rb;
+      if (kMax) {  // each head's gate query, for the per-head scores
+        vs[g][lane] = ra;
+        vs[g][lane + 64] = rb;
+      }
     }
     part[wave][lane] = sa;
     part[wave][lane + 64] = sb;
@@ -162,10 +173,17 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
       gm[e] = (part[0][d] + part[1][d] + part[2][d] + part[3][d]) * inv_g;
     }
   }
+  float gh[kMax ? 8 : 1][8];  // kMax: per-head gate queries, dims 8*lane16 .. +7
+  if (kMax) {
+#pragma unroll
+    for (int h = 0; h < (kMax ? 8 : 1); ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gh[h][e] = h < G ? vs[h][8 * lane16 + e] : 0.f;
+  }
 
   // ---- 3. scores of every candidate (first 512 already in flight)
   const float inv_sqrt_dg = 0.08838834764831845f;  // 1/sqrt(128)
-  float *scores = p.scores ? p.scores + (int64_t)sk * p.max_blocks : nullptr;
+  float *scores = (!kPositions || p.scores) ? p.scores + (int64_t)sk * p.max_blocks : nullptr;
   for (int base = 0; base < n; base += 16 * kKeysInFlight) {
     if (base > 0) {
 #pragma unroll
@@ -176,24 +194,43 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
     }
 #pragma unroll
     for (int u = 0; u < kKeysInFlight; ++u) {
-      float d = gm[0] * bf16_lo(v[u].x);
-      d = fmaf(gm[1], bf16_hi(v[u].x), d);
-      d = fmaf(gm[2], bf16_lo(v[u].y), d);
-      d = fmaf(gm[3], bf16_hi(v[u].y), d);
-      d = fmaf(gm[4], bf16_lo(v[u].z), d);
-      d = fmaf(gm[5], bf16_hi(v[u].z), d);
-      d = fmaf(gm[6], bf16_lo(v[u].w), d);
-      d = fmaf(gm[7], bf16_hi(v[u].w), d);
-      d = row16_sum(d);
+      auto dot8 = [&](const float(&w)[8]) {
+        float d = w[0] * bf16_lo(v[u].x);
+        d = fmaf(w[1], bf16_hi(v[u].x), d);
+        d = fmaf(w[2], bf16_lo(v[u].y), d);
+        d = fmaf(w[3], bf16_hi(v[u].y), d);
+        d = fmaf(w[4], bf16_lo(v[u].z), d);
+        d = fmaf(w[5], bf16_hi(v[u].z), d);
+        d = fmaf(w[6], bf16_lo(v[u].w), d);
+        d = fmaf(w[7], bf16_hi(v[u].w), d);
+        return row16_sum(d);
+      };
+      float d;
+      if (kMax) {
+        d = -__builtin_inff();
+#pragma unroll
+        for (int h = 0; h < (kMax ? 8 : 1); ++h)
+          if (h < G) d = fmaxf(d, dot8(gh[h]));
+      } else {
+        d = gm[0] * bf16_lo(v[u].x);
+        d = fmaf(gm[1], bf16_hi(v[u].x), d);
+        d = fmaf(gm[2], bf16_lo(v[u].y), d);
+        d = fmaf(gm[3], bf16_hi(v[u].y), d);
+        d = fmaf(gm[4], bf16_lo(v[u].z), d);
+        d = fmaf(gm[5], bf16_hi(v[u].z), d);
+        d = fmaf(gm[6], bf16_lo(v[u].w), d);
+        d = fmaf(gm[7], bf16_hi(v[u].w), d);
+        d = row16_sum(d);
+      }
       const int c = base + 16 * u + grp;
       if (lane16 == 0 && c < n) {
         const float sc = d * inv_sqrt_dg;
         slot[c] = score_key(sc);
-        if (scores) scores[c] = sc;
+        if (!kPositions || scores) scores[c] = sc;
       }
     }
   }
-  if (scores)
+  if (!kPositions || scores)
     for (int c = n + t; c < p.max_blocks; c += 256) scores[c] = -__builtin_inff();
   lds_barrier();
   if (wave != 0) return;
@@ -314,11 +351,24 @@ hipError_t launch_gate_topk(const GateParams &p, int batch, hipStream_t st) {
   // the selecting wave reads the first 512 slots as whole vectors
   const size_t lds = sizeof(uint32_t) * (size_t)(p.max_blocks > 512 ? (p.max_blocks + 7) / 8 * 8 : 512);
   // allow the largest block-table row (64 KiB of LDS); set once per process
-  static const hipError_t attr = hipFuncSetAttribute((const void *)gate_topk_kernel,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)(sizeof(uint32_t) * SAS_MAX_BLOCKS_DEV));
+  static const hipError_t attr = [] {
+    const int most = (int)(sizeof(uint32_t) * SAS_MAX_BLOCKS_DEV);
+    const void *kernels[] = {(const void *)gate_topk_kernel<false, false>, (const void *)gate_topk_kernel<true, false>,
+                             (const void *)gate_topk_kernel<false, true>};
+    for (const void *k : kernels) {
+      hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, most);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }();
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(gate_topk_kernel, dim3((unsigned)(batch * p.n_kv_heads)), dim3(256), lds, st, p);
+  const dim3 grid((unsigned)(batch * p.n_kv_heads));
+  if (p.bt_row_stride == 0)
+    hipLaunchKernelGGL((gate_topk_kernel<false, true>), grid, dim3(256), lds, st, p);
+  else if (p.aggregate)
+    hipLaunchKernelGGL((gate_topk_kernel<true, false>), grid, dim3(256), lds, st, p);
+  else
+    hipLaunchKernelGGL((gate_topk_kernel<false, false>), grid, dim3(256), lds, st, p);
   return hipGetLastError();
 }
 

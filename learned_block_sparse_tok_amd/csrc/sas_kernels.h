@@ -44,6 +44,7 @@ struct GateParams {
   float *scores;            // [B][Hkv][max_blocks], nullable
   int32_t n_q_heads, n_kv_heads, group, max_blocks, n_sel;
   int32_t bt_row_stride;    // max_blocks, or 0 when every entry shares one block-table row
+  int32_t aggregate;        // 0: mean of the group's per-head scores, 1: their maximum (group <= 8)
   double inv_freq[kGateDim / 2];  // rope_theta^(-i/64)
 };
 
@@ -59,6 +60,7 @@ struct DecodeParams {
   int32_t n_q_heads, n_kv_heads, group, max_blocks, max_sel;
   int32_t wg_per_unit;      // workgroups per (sequence, KV head)
   int32_t blocks_per_wave;  // selected blocks each wave handles
+  int32_t gate_mode;        // with gates: 0 scale each block's share, 1 log-gate bias on the logits
   float scale_log2;         // sm_scale * log2(e)
 };
 

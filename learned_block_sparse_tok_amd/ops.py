@@ -40,6 +40,9 @@ _VP, _I32, _F32, _F64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ct
 _SIGS = {
     "sas_pool_blocks": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _F64, _VP, _VP]),
     "sas_append_kv": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F64, _VP, _VP]),
+    "sas_gate_topk_ex": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _F64, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
+    "sas_sparse_decode_ex": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _I32, _F32, _VP, _VP, _SZ,
+                                    _VP]),
     "sas_gate_topk": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _F64, _I32, _VP, _VP, _VP, _VP, _VP]),
     "sas_sparse_decode_workspace_bytes": (_SZ, [_VP, _I32]),
     "sas_sparse_decode": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP, _VP, _SZ, _VP]),
@@ -125,26 +128,38 @@ def append_kv(shape: SasShape, k_new, v_new, k_pool, v_pool, block_table, seq_le
     _check(st, "sas_append_kv")
 
 
+AGGREGATE = {"mean": 0, "max": 1}  # SAS_AGG_MEAN, SAS_AGG_MAX
+GATE_MODE = {"scale": 0, "logit": 1}  # SAS_GATE_SCALE, SAS_GATE_LOGIT
+
+
 def gate_topk(shape: SasShape, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, theta, budget_tokens,
-              sel, gates, cnt, scores, stream=None):
-    st = lib().sas_gate_topk(ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"), _ptr(w_q, torch.bfloat16, "w_q"),
-                             _ptr(w_qnorm, torch.float32, "w_qnorm"), _ptr(gate_keys, torch.bfloat16, "gate_keys"),
-                             _ptr(block_table, torch.int32, "block_table"), _ptr(seq_lens, torch.int32, "seq_lens"),
-                             float(theta), int(budget_tokens), _ptr(sel, torch.int32, "sel"),
-                             _ptr(gates, torch.float32, "gates"), _ptr(cnt, torch.int32, "cnt"),
-                             _ptr(scores, torch.float32, "scores"), _stream(stream))
+              sel, gates, cnt, scores, stream=None, aggregate="mean"):
+    """sas_gate_topk (aggregate "mean") or sas_gate_topk_ex."""
+    args = (ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"), _ptr(w_q, torch.bfloat16, "w_q"),
+            _ptr(w_qnorm, torch.float32, "w_qnorm"), _ptr(gate_keys, torch.bfloat16, "gate_keys"),
+            _ptr(block_table, torch.int32, "block_table"), _ptr(seq_lens, torch.int32, "seq_lens"),
+            float(theta), int(budget_tokens))
+    outs = (_ptr(sel, torch.int32, "sel"), _ptr(gates, torch.float32, "gates"), _ptr(cnt, torch.int32, "cnt"),
+            _ptr(scores, torch.float32, "scores"), _stream(stream))
+    if aggregate == "mean":
+        st = lib().sas_gate_topk(*args, *outs)
+    else:
+        st = lib().sas_gate_topk_ex(*args, AGGREGATE[aggregate], *outs)
     _check(st, "sas_gate_topk")
 
 
 def sparse_decode(shape: SasShape, q, k_pool, v_pool, block_table, seq_lens, sel, gates, cnt, max_sel,
-                  sm_scale, out, workspace, stream=None):
-    st = lib().sas_sparse_decode(ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"),
-                                 _ptr(k_pool, torch.bfloat16, "k_pool"), _ptr(v_pool, torch.bfloat16, "v_pool"),
-                                 _ptr(block_table, torch.int32, "block_table"),
-                                 _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(sel, torch.int32, "sel"),
-                                 _ptr(gates, torch.float32, "gates"), _ptr(cnt, torch.int32, "cnt"), int(max_sel),
-                                 float(sm_scale), _ptr(out, torch.bfloat16, "out"), _ptr(workspace, None, "workspace"),
-                                 workspace.numel() * workspace.element_size(), _stream(stream))
+                  sm_scale, out, workspace, stream=None, gate_mode="scale"):
+    """sas_sparse_decode (gate_mode "scale") or sas_sparse_decode_ex."""
+    head = (ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"), _ptr(k_pool, torch.bfloat16, "k_pool"),
+            _ptr(v_pool, torch.bfloat16, "v_pool"), _ptr(block_table, torch.int32, "block_table"),
+            _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(sel, torch.int32, "sel"), _ptr(gates, torch.float32, "gates"))
+    tail = (_ptr(cnt, torch.int32, "cnt"), int(max_sel), float(sm_scale), _ptr(out, torch.bfloat16, "out"),
+            _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    if gate_mode == "scale":
+        st = lib().sas_sparse_decode(*head, *tail)
+    else:
+        st = lib().sas_sparse_decode_ex(*head, GATE_MODE[gate_mode], *tail)
     _check(st, "sas_sparse_decode")
 
 
@@ -153,9 +168,10 @@ class SparseDecoder:
     once, by torch) and runs sas_gate_topk + sas_sparse_decode on them."""
 
     def __init__(self, batch, n_q_heads, n_kv_heads, max_blocks, strides, budget, theta, gated,
-                 device="cuda", sm_scale=None):
+                 device="cuda", sm_scale=None, aggregate="mean", gate_mode="scale"):
         self.shape = make_shape(batch, n_q_heads, n_kv_heads, max_blocks, strides)
         self.budget, self.theta, self.gated = budget, theta, gated
+        self.aggregate, self.gate_mode = aggregate, gate_mode
         self.n_sel = budget // BLOCK
         self.sm_scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(HEAD_DIM)
         dev = torch.device(device)
@@ -169,12 +185,12 @@ class SparseDecoder:
 
     def select(self, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, stream=None):
         gate_topk(self.shape, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, self.theta, self.budget,
-                  self.sel, self.gates, self.cnt, self.scores, stream)
+                  self.sel, self.gates, self.cnt, self.scores, stream, aggregate=self.aggregate)
 
     def attend(self, q, k_pool, v_pool, block_table, seq_lens, stream=None):
         sparse_decode(self.shape, q, k_pool, v_pool, block_table, seq_lens, self.sel,
                       self.gates if self.gated else None, self.cnt, self.n_sel, self.sm_scale, self.out,
-                      self.ws_dec, stream)
+                      self.ws_dec, stream, gate_mode=self.gate_mode)
 
     def step(self, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens, stream=None):
         self.select(q, w_q, w_qnorm, gate_keys, block_table, seq_lens, stream)

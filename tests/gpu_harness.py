@@ -108,7 +108,7 @@ def compare_selection(g: dict, o: dict, lens: np.ndarray, budget: int):
 
 
 def alternative_outputs(h: Host, o: dict, s: int, kvh: int, gsel: np.ndarray, gated: bool, budget: int,
-                        limit: int = 64):
+                        limit: int = 64, gate_mode: str = "scale"):
     """Oracle outputs of the G query heads of (s, kvh) under the valid
     resolution of the tie band whose selected set equals gsel's, found by
     enumerating every valid resolution on the oracle side (None when there
@@ -139,7 +139,7 @@ def alternative_outputs(h: Host, o: dict, s: int, kvh: int, gsel: np.ndarray, ga
         gates[s, kvh] = oracle.block_gates(sc, sel[s, kvh], k + 1)
         pairs = np.array([[s, kvh * w.group + g] for g in range(w.group)], np.int32)
         return oracle.attend(h.q, h.k, h.v, h.bt, w.strides, w.n_kv_heads, h.lens, sel,
-                             gates if gated else None, cnt, SM_SCALE, pairs=pairs)
+                             gates if gated else None, cnt, SM_SCALE, pairs=pairs, gate_mode=gate_mode)
     raise AssertionError("GPU selection is not a valid resolution of the tie band")
 
 
@@ -151,7 +151,8 @@ def assert_out_close(got: np.ndarray, want: np.ndarray, what=""):
     return float(err.max()), float(err.mean())
 
 
-def compare_step(h: Host, g: dict, o: dict, gated: bool, budget: int, gate_atol: float = 2e-4):
+def compare_step(h: Host, g: dict, o: dict, gated: bool, budget: int, gate_atol: float = 2e-4,
+                 gate_mode: str = "scale"):
     """Whole-step parity with tie accounting.  Returns (n_ties, n_skipped).
     gate_atol: the two sides' gate keys may differ by one bf16 rounding, which
     moves a score by ~1e-4 and its sigmoid gate by less."""
@@ -163,7 +164,7 @@ def compare_step(h: Host, g: dict, o: dict, gated: bool, budget: int, gate_atol:
     for (s, kvh) in ties:
         heads = slice(kvh * w.group, (kvh + 1) * w.group)
         mask[s, heads] = False
-        alt = alternative_outputs(h, o, s, kvh, g["sel"][s, kvh], gated, budget)
+        alt = alternative_outputs(h, o, s, kvh, g["sel"][s, kvh], gated, budget, gate_mode=gate_mode)
         if alt is None:
             skipped += 1
             continue

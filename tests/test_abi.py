@@ -131,6 +131,18 @@ def test_prefill_rejects_bad_arguments(lib):
     assert att_call(out=ctypes.c_void_p(4096 + 8)) == ops.SAS_ERR_UNSUPPORTED  # not 16-byte aligned
 
 
+def test_variant_entry_points_reject_bad_modes(lib):
+    sh = _shape()
+    gate = lambda agg, shp=sh: lib.sas_gate_topk_ex(ctypes.byref(shp), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1e6, 1024,
+                                                   agg, FAKE, FAKE, FAKE, FAKE, None)
+    assert gate(2) == ops.SAS_ERR_INVALID_ARG
+    assert gate(1, _shape(n_q_heads=32, n_kv_heads=2)) == ops.SAS_ERR_UNSUPPORTED  # group 16 > 8 for max
+    dec = lambda mode: lib.sas_sparse_decode_ex(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mode,
+                                                FAKE, 16, 0.088, FAKE, FAKE, 1 << 24, None)
+    assert dec(5) == ops.SAS_ERR_INVALID_ARG
+    assert dec(-1) == ops.SAS_ERR_INVALID_ARG
+
+
 def test_workspace_sizes(lib):
     # 256 (sequence, KV head) units fill the CUs: one workgroup each, no partials
     sh = _shape(batch=32, n_q_heads=32, n_kv_heads=8, max_blocks=512)

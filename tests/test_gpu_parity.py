@@ -344,6 +344,33 @@ def test_step_parity(case, gated):
 
 
 # ------------------------------------------------------------------ errors
+VARIANTS = [("max", "scale"), ("mean", "logit"), ("max", "logit")]
+
+
+@pytest.mark.parametrize("aggregate,gate_mode", VARIANTS, ids=[f"{a}-{m}" for a, m in VARIANTS])
+@pytest.mark.parametrize("case", [STEP_CASES[0], STEP_CASES[4], STEP_CASES[5]], ids=lambda c: c["name"])
+def test_step_parity_alternative_readings(case, aggregate, gate_mode):
+    """sas_gate_topk_ex / sas_sparse_decode_ex (max-over-heads scores, gate as
+    a log-bias on the logits) against the oracle run with the same options."""
+    say("variant", case["name"], aggregate, gate_mode)
+    w = _step_workload(case)
+    h = Host(w)
+    gk_o = oracle_gate_keys(h)
+    sel, gates, cnt, scores = oracle.gate_topk(h.q, h.w_q, h.wqn, gk_o, h.bt, h.lens, w.theta, case["budget"],
+                                               w.n_kv_heads, aggregate=aggregate)
+    out = oracle.attend(h.q, h.k, h.v, h.bt, w.strides, w.n_kv_heads, h.lens, sel, gates, cnt, SM_SCALE,
+                        gate_mode=gate_mode)
+    o = dict(gate_keys=gk_o, sel=sel, gates=gates, cnt=cnt, scores=scores, out=out)
+    dec = ops.SparseDecoder(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, case["budget"], w.theta,
+                            True, device=DEV, aggregate=aggregate, gate_mode=gate_mode)
+    dec.step(w.q, w.w_q, w.w_qnorm, gpu_pool(w), w.k_pool, w.v_pool, w.block_table, w.seq_lens)
+    torch.cuda.synchronize()
+    g = dict(sel=wl.host(dec.sel), gates=wl.host(dec.gates), cnt=wl.host(dec.cnt), scores=wl.host(dec.scores),
+             out=bf16_out(dec.out))
+    ties, skipped = compare_step(h, g, o, True, case["budget"], gate_mode=gate_mode)
+    say(f"  ties {ties} (outputs of {skipped} not enumerated)")
+
+
 def test_invalid_arguments_raise():
     w = wl.make(1, 4, 1, 300, 1024, "paged", 71, DEV, max_blocks=5)
     shape = shape_of(w)
