@@ -14,6 +14,7 @@ patterns) and it never calls into the GPU library.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -243,3 +244,109 @@ def prefill(q, k_pool, v_pool, block_table_row, strides, n_kv_heads, gate_keys, 
     sel, gates, cnt, scores = gate_topk(qp, w_q, w_qnorm, gate_keys, bt, lens, theta, budget_tokens, n_kv_heads)
     out = attend(qp, k_pool, v_pool, bt, strides, n_kv_heads, lens, sel, gates if gated else None, cnt, sm_scale)
     return sel, gates, cnt, scores, out
+
+
+def _block_rows(pool, block_table, strides, s, c, kvh, nvalid):
+    """The first nvalid rows of block c of sequence s, KV head kvh, fp64 [n][128]."""
+    ps, ts, hs = strides
+    page = int(block_table[s, c])
+    base = page * ps + kvh * hs
+    idx = base + np.arange(nvalid)[:, None] * ts + np.arange(HEAD_DIM)[None, :]
+    return bf16_to_f64(pool.reshape(-1)[idx])
+
+
+def gate_backward(q, k_pool, v_pool, block_table, strides, n_kv_heads, seq_lens, sel, gates, cnt, sm_scale,
+                  w_q, w_qnorm, w_k, w_knorm, gate_keys, theta, d_out, round_keys=True):
+    """Gradients of the gate parameters through the continuous gates of one
+    gated decode step (the default reading: each selected block's share of
+    the output scaled by its gate g = sigmoid(score)).
+
+    SAS puts continuous gates on the selected blocks so that the language-model
+    loss reaches the ranking (aigc.news release note; "Tencent Hunyuan
+    open-sources SAS ...": a differentiable path from the LM loss to the
+    selector).  READING: the Top-K choice itself passes no gradient; the local
+    block's gate is the constant 1; the gate keys' bf16 storage passes the
+    gradient unchanged (straight through); the backbone's q, K, V are inputs.
+
+    d_out: bf16 bits [B][Hq][128], the gradient of the loss w.r.t. the step's
+    output.  With o_h = sum_i g_i sum_{j in block c_i} P_hj v_j:
+      dg_i  = sum_{h in group} sum_{j in c_i} P_hj <d_out_h, v_j>
+      dS_i  = dg_i g_i (1 - g_i)                  (historical blocks only)
+      dghat = sum_i dS_i gk_{c_i} / sqrt(128),   d gk_{c_i} = dS_i ghat / sqrt(128)
+    then through the group mean, RoPE (a rotation: its transpose rotates
+    back), RMSNorm and the bias-free projections.  round_keys: use the stored
+    bf16 gate keys in dghat (as the forward's scores do); False uses the
+    unrounded fp64 keys (the smooth function finite differences can see).
+    Returns dict(d_gates [B][Hkv][n_sel], d_w_q [Hq][128][128],
+    d_w_qnorm [128], d_w_k [Hkv][128][384], d_w_knorm [128]), fp64, summed
+    over the batch; d_gates covers every selected block (local included)."""
+    B, Hq, _ = q.shape
+    Hkv = n_kv_heads
+    G = Hq // Hkv
+    max_blocks = block_table.shape[1]
+    qf, dO = bf16_to_f64(q), bf16_to_f64(d_out)
+    wq, wk = bf16_to_f64(w_q), bf16_to_f64(w_k)
+    wqn, wkn = np.asarray(w_qnorm, np.float64), np.asarray(w_knorm, np.float64)
+    rs = math.sqrt(GATE_DIM)
+    out = dict(d_gates=np.zeros(sel.shape), d_w_q=np.zeros((Hq, GATE_DIM, HEAD_DIM)), d_w_qnorm=np.zeros(GATE_DIM),
+               d_w_k=np.zeros((Hkv, GATE_DIM, 3 * HEAD_DIM)), d_w_knorm=np.zeros(GATE_DIM))
+
+    def rms_parts(u):
+        r = math.sqrt(float(np.mean(u * u)) + 1e-6)
+        return u / r, r
+
+    def rms_back(dn, nrm, r, w):
+        """d(u) from d(n), n = (u / r) * w; also d(w)."""
+        a = dn * w
+        return (a - nrm * float(np.mean(a * nrm))) / r, dn * nrm
+
+    for s in range(B):
+        L = int(seq_lens[s])
+        for kvh in range(Hkv):
+            c_sel = sel[s, kvh, :cnt[s, kvh]]
+            g_sel = np.asarray(gates[s, kvh, :cnt[s, kvh]], np.float64)
+            K = [_block_rows(k_pool, block_table, strides, s, int(c), kvh, min(64, L - 64 * int(c))) for c in c_sel]
+            V = [_block_rows(v_pool, block_table, strides, s, int(c), kvh, min(64, L - 64 * int(c))) for c in c_sel]
+            Kall, Vall = np.concatenate(K), np.concatenate(V)
+            edges = np.cumsum([0] + [len(k) for k in K])
+            dg = np.zeros(len(c_sel))
+            for h in range(kvh * G, (kvh + 1) * G):
+                z = Kall @ qf[s, h] * sm_scale
+                P = np.exp(z - z.max())
+                P /= P.sum()
+                dv = Vall @ dO[s, h]
+                for i in range(len(c_sel)):
+                    dg[i] += float(P[edges[i]:edges[i + 1]] @ dv[edges[i]:edges[i + 1]])
+            out["d_gates"][s, kvh, :len(c_sel)] = dg
+            n_hist = len(c_sel) - 1
+            dS = dg[:n_hist] * g_sel[:n_hist] * (1.0 - g_sel[:n_hist])
+            # gate queries of the group and their mean
+            parts = []
+            for h in range(kvh * G, (kvh + 1) * G):
+                u = wq[h] @ qf[s, h]
+                nrm, r = rms_parts(u)
+                parts.append((h, nrm, r, rope(nrm * wqn, L - 1, theta)))
+            ghat = np.mean([p[3] for p in parts], axis=0)
+            # keys of the historical selection: stored bf16, and the fp64 chain
+            keys = []
+            for i in range(n_hist):
+                c = int(c_sel[i])
+                p_c = pool_stats(k_pool, block_table, strides, max_blocks, Hkv, s, c, kvh)
+                u = wk[kvh] @ p_c
+                nrm, r = rms_parts(u)
+                gk64 = rope(nrm * wkn, 64.0 * c, theta)
+                gk_b = bf16_to_f64(gate_keys[int(block_table[s, c]), kvh]) if round_keys else gk64
+                keys.append((c, p_c, nrm, r, gk_b))
+            dghat = np.zeros(GATE_DIM)
+            for i, (c, p_c, nrm, r, gk_b) in enumerate(keys):
+                dghat += dS[i] * gk_b / rs
+                dm = rope(dS[i] * ghat / rs, -64.0 * c, theta)
+                du, dw = rms_back(dm, nrm, r, wkn)
+                out["d_w_knorm"] += dw
+                out["d_w_k"][kvh] += np.outer(du, p_c)
+            for h, nrm, r, _ in parts:
+                dn = rope(dghat / G, -(L - 1.0), theta)
+                du, dw = rms_back(dn, nrm, r, wqn)
+                out["d_w_qnorm"] += dw
+                out["d_w_q"][h] += np.outer(du, qf[s, h])
+    return out
