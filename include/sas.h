@@ -20,7 +20,8 @@
  *   sas_gate_topk      once per decode step                      (selection)
  *   sas_sparse_decode  once per decode step                      (attention)
  * and, for the training-time forward of a whole sequence (every position a
- * query): sas_prefill_select, then sas_prefill_attend.
+ * query): sas_prefill_select, then sas_prefill_attend; for training the
+ * gates: sas_gate_backward after a gated decode step.
  *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer owned by the caller (for
@@ -244,6 +245,39 @@ sas_status sas_prefill_attend(const sas_shape *shape, const void *q, const void 
                               const void *v_pool, const int32_t *block_table_row, int32_t seq_len,
                               const int32_t *sel, const float *gates, const int32_t *cnt,
                               int32_t max_sel, float sm_scale, void *out, void *stream);
+
+/*
+ * sas_gate_backward -- gradients of the gate parameters through the
+ * continuous gates of one gated decode step (default reading: each selected
+ * block's share of the output scaled by its gate).  SAS's continuous gates on
+ * the selected blocks give the language-model loss a differentiable path to
+ * the block ranking (aigc.news release note; "Tencent Hunyuan open-sources
+ * SAS ...").  The Top-K choice passes no gradient, the local block's gate is
+ * the constant 1, and the bf16 gate keys pass the gradient straight through;
+ * q, K and V (the frozen backbone's) get none.
+ *
+ * Inputs: the step's inputs and its forward outputs sel / gates / cnt (as
+ * sas_gate_topk wrote them, max_sel = budget/64), the gate weights, the gate
+ * keys, and d_out: bf16 [B][Hq][128], the gradient of the loss w.r.t. the
+ * step's output.  Outputs (fp32, overwritten, summed over the batch):
+ *   d_gates    [B][Hkv][max_sel]  dL/dg of every selected block (the local
+ *              block's included, as if free), 0 in the padding
+ *   d_w_q      [Hq][128][128]     d_w_qnorm [128]
+ *   d_w_k      [Hkv][128][384]    d_w_knorm [128]
+ * The sums over the batch run in a fixed order (deterministic).  workspace:
+ * at least sas_gate_backward_workspace_bytes(shape, max_sel) bytes, no
+ * initial contents needed.
+ */
+size_t sas_gate_backward_workspace_bytes(const sas_shape *shape, int32_t max_sel);
+sas_status sas_gate_backward(const sas_shape *shape, const void *q, const void *k_pool,
+                             const void *v_pool, const int32_t *block_table,
+                             const int32_t *seq_lens, const int32_t *sel, const float *gates,
+                             const int32_t *cnt, int32_t max_sel, float sm_scale, const void *w_q,
+                             const float *w_qnorm, const void *w_k, const float *w_knorm,
+                             const void *gate_keys, double rope_theta, const void *d_out,
+                             float *d_gates, float *d_w_q, float *d_w_qnorm, float *d_w_k,
+                             float *d_w_knorm, void *workspace, size_t workspace_bytes,
+                             void *stream);
 
 /* Text of a status code (static storage). */
 const char *sas_status_str(sas_status status);

@@ -345,4 +345,88 @@ sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *
                               max_sel, sm_scale, out, workspace, workspace_bytes, stream);
 }
 
+namespace {
+struct BackwardWorkspace {
+  size_t du_q, dwqn, du_k, dwkn, pool, total;
+};
+BackwardWorkspace backward_workspace(const sas_shape *sh, int32_t max_sel) {
+  const size_t q_rows = (size_t)sh->batch * sh->n_q_heads * SAS_GATE_DIM * sizeof(float);
+  const size_t k_slots = (size_t)sh->batch * sh->n_kv_heads * max_sel;
+  BackwardWorkspace w;
+  w.du_q = 0;
+  w.dwqn = w.du_q + align256(q_rows);
+  w.du_k = w.dwqn + align256(q_rows);
+  w.dwkn = w.du_k + align256(k_slots * SAS_GATE_DIM * sizeof(float));
+  w.pool = w.dwkn + align256(k_slots * SAS_GATE_DIM * sizeof(float));
+  w.total = w.pool + align256(k_slots * 3 * SAS_HEAD_DIM * sizeof(float));
+  return w;
+}
+}  // namespace
+
+size_t sas_gate_backward_workspace_bytes(const sas_shape *shape, int32_t max_sel) {
+  if (!shape || shape->batch <= 0 || shape->n_kv_heads <= 0 || shape->n_q_heads <= 0 || max_sel <= 0) return 0;
+  return backward_workspace(shape, max_sel).total;
+}
+
+sas_status sas_gate_backward(const sas_shape *shape, const void *q, const void *k_pool, const void *v_pool,
+                             const int32_t *block_table, const int32_t *seq_lens, const int32_t *sel,
+                             const float *gates, const int32_t *cnt, int32_t max_sel, float sm_scale,
+                             const void *w_q, const float *w_qnorm, const void *w_k, const float *w_knorm,
+                             const void *gate_keys, double rope_theta, const void *d_out, float *d_gates,
+                             float *d_w_q, float *d_w_qnorm, float *d_w_k, float *d_w_knorm, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  sas_status st = check_shape(shape, true);
+  if (st) return st;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !sel || !gates || !cnt || !w_q || !w_qnorm || !w_k ||
+      !w_knorm || !gate_keys || !d_out || !d_gates || !d_w_q || !d_w_qnorm || !d_w_k || !d_w_knorm || !workspace)
+    return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (max_sel <= 0 || max_sel > 256) return fail(SAS_ERR_INVALID_ARG, "max_sel must be in 1..256");
+  if (!(sm_scale > 0.f)) return fail(SAS_ERR_INVALID_ARG, "sm_scale must be positive");
+  if (!(rope_theta > 1.0)) return fail(SAS_ERR_INVALID_ARG, "rope_theta must be > 1");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(d_out) || !aligned16(w_q) ||
+      !aligned16(w_k) || !aligned16(workspace))
+    return fail(SAS_ERR_UNSUPPORTED, "q, k_pool, v_pool, d_out, w_q, w_k and workspace must be 16-byte aligned");
+  const BackwardWorkspace wl = backward_workspace(shape, max_sel);
+  if (workspace_bytes < wl.total)
+    return fail(SAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, wl.total);
+  sas::BackwardParams p;
+  p.q = (const uint16_t *)q;
+  p.k_pool = (const uint16_t *)k_pool;
+  p.v_pool = (const uint16_t *)v_pool;
+  p.d_out = (const uint16_t *)d_out;
+  p.gate_keys = (const uint16_t *)gate_keys;
+  p.w_q = (const uint16_t *)w_q;
+  p.w_k = (const uint16_t *)w_k;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.sel = sel;
+  p.cnt = cnt;
+  p.gates = gates;
+  p.w_qnorm = w_qnorm;
+  p.w_knorm = w_knorm;
+  p.d_gates = d_gates;
+  p.d_w_q = d_w_q;
+  p.d_w_qnorm = d_w_qnorm;
+  p.d_w_k = d_w_k;
+  p.d_w_knorm = d_w_knorm;
+  char *ws = (char *)workspace;
+  p.ws_du_q = (float *)(ws + wl.du_q);
+  p.ws_dwqn = (float *)(ws + wl.dwqn);
+  p.ws_du_k = (float *)(ws + wl.du_k);
+  p.ws_dwkn = (float *)(ws + wl.dwkn);
+  p.ws_pool = (float *)(ws + wl.pool);
+  p.page_stride = shape->page_stride;
+  p.tok_stride = shape->tok_stride;
+  p.head_stride = shape->head_stride;
+  p.batch = shape->batch;
+  p.n_q_heads = shape->n_q_heads;
+  p.n_kv_heads = shape->n_kv_heads;
+  p.group = shape->n_q_heads / shape->n_kv_heads;
+  p.max_blocks = shape->max_blocks;
+  p.max_sel = max_sel;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  for (int i = 0; i < SAS_GATE_DIM / 2; ++i) p.inv_freq[i] = pow(rope_theta, -(double)i / (SAS_GATE_DIM / 2));
+  return hip_status(sas::launch_gate_backward(p, (hipStream_t)stream), "sas_gate_backward launch");
+}
+
 }  // extern "C"

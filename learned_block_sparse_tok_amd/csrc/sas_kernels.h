@@ -83,7 +83,26 @@ struct PrefillParams {
   float scale_log2;
 };
 
+constexpr int kChainBlocks = 16;  // selected blocks the backward chain handles at a time
+
+struct BackwardParams {
+  const uint16_t *q, *k_pool, *v_pool, *d_out, *gate_keys, *w_q, *w_k;
+  const int32_t *block_table, *seq_lens, *sel, *cnt;
+  const float *gates, *w_qnorm, *w_knorm;
+  float *d_gates;                 // [B][Hkv][max_sel]
+  float *d_w_q, *d_w_qnorm, *d_w_k, *d_w_knorm;
+  // workspace: per-sequence factors of the weight gradients
+  float *ws_du_q, *ws_dwqn;       // [B][Hq][128]
+  float *ws_du_k, *ws_dwkn;       // [B][Hkv][max_sel][128]
+  float *ws_pool;                 // [B][Hkv][max_sel][384]
+  int64_t page_stride, tok_stride, head_stride;
+  int32_t batch, n_q_heads, n_kv_heads, group, max_blocks, max_sel;
+  float scale_log2;
+  double inv_freq[kGateDim / 2];
+};
+
 hipError_t launch_pool(const PoolParams &p, hipStream_t st);
+hipError_t launch_gate_backward(const BackwardParams &p, hipStream_t st);
 hipError_t launch_prefill_attend(const PrefillParams &p, hipStream_t st);
 hipError_t launch_append(const AppendParams &p, int batch, hipStream_t st);
 hipError_t launch_gate_topk(const GateParams &p, int batch, hipStream_t st);

@@ -48,6 +48,9 @@ _SIGS = {
     "sas_sparse_decode": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP, _VP, _SZ, _VP]),
     "sas_prefill_select": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _F64, _I32, _VP, _VP, _VP, _VP, _VP]),
     "sas_prefill_attend": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _F32, _VP, _VP]),
+    "sas_gate_backward_workspace_bytes": (_SZ, [_VP, _I32]),
+    "sas_gate_backward": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP, _VP, _VP, _VP, _VP,
+                                 _F64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "sas_status_str": (ctypes.c_char_p, [_I32]),
     "sas_last_error": (ctypes.c_char_p, []),
     "sas_version": (_I32, []),
@@ -253,3 +256,38 @@ class Prefill:
     def forward(self, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table_row, stream=None):
         self.select(q, w_q, w_qnorm, gate_keys, block_table_row, stream)
         self.attend(q, k_pool, v_pool, block_table_row, stream)
+
+
+def gate_backward_workspace_bytes(shape: SasShape, max_sel: int) -> int:
+    return int(lib().sas_gate_backward_workspace_bytes(ctypes.byref(shape), max_sel))
+
+
+def gate_backward(shape: SasShape, q, k_pool, v_pool, block_table, seq_lens, sel, gates, cnt, max_sel, sm_scale,
+                  w_q, w_qnorm, w_k, w_knorm, gate_keys, theta, d_out, workspace=None, stream=None):
+    """Gradients of the gate parameters through the continuous gates of a gated
+    decode step.  Returns dict(d_gates, d_w_q, d_w_qnorm, d_w_k, d_w_knorm)
+    (fp32 device tensors)."""
+    dev = q.device
+    B, Hq, _ = q.shape
+    Hkv = shape.n_kv_heads
+    out = dict(d_gates=torch.empty((B, Hkv, max_sel), dtype=torch.float32, device=dev),
+               d_w_q=torch.empty((Hq, 128, 128), dtype=torch.float32, device=dev),
+               d_w_qnorm=torch.empty(128, dtype=torch.float32, device=dev),
+               d_w_k=torch.empty((Hkv, 128, 384), dtype=torch.float32, device=dev),
+               d_w_knorm=torch.empty(128, dtype=torch.float32, device=dev))
+    if workspace is None:
+        workspace = torch.empty(gate_backward_workspace_bytes(shape, max_sel), dtype=torch.uint8, device=dev)
+    st = lib().sas_gate_backward(ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"),
+                                 _ptr(k_pool, torch.bfloat16, "k_pool"), _ptr(v_pool, torch.bfloat16, "v_pool"),
+                                 _ptr(block_table, torch.int32, "block_table"), _ptr(seq_lens, torch.int32, "seq_lens"),
+                                 _ptr(sel, torch.int32, "sel"), _ptr(gates, torch.float32, "gates"),
+                                 _ptr(cnt, torch.int32, "cnt"), int(max_sel), float(sm_scale),
+                                 _ptr(w_q, torch.bfloat16, "w_q"), _ptr(w_qnorm, torch.float32, "w_qnorm"),
+                                 _ptr(w_k, torch.bfloat16, "w_k"), _ptr(w_knorm, torch.float32, "w_knorm"),
+                                 _ptr(gate_keys, torch.bfloat16, "gate_keys"), float(theta),
+                                 _ptr(d_out, torch.bfloat16, "d_out"), _ptr(out["d_gates"]), _ptr(out["d_w_q"]),
+                                 _ptr(out["d_w_qnorm"]), _ptr(out["d_w_k"]), _ptr(out["d_w_knorm"]),
+                                 _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+                                 _stream(stream))
+    _check(st, "sas_gate_backward")
+    return out

@@ -143,6 +143,22 @@ def test_variant_entry_points_reject_bad_modes(lib):
     assert dec(-1) == ops.SAS_ERR_INVALID_ARG
 
 
+def test_gate_backward_rejects_bad_arguments(lib):
+    sh = _shape()
+    need = lib.sas_gate_backward_workspace_bytes(ctypes.byref(sh), 16)
+    assert need > 0
+
+    def call(gates=FAKE, max_sel=16, ws_bytes=need, theta=1e6):
+        return lib.sas_gate_backward(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, gates, FAKE, max_sel, 0.088,
+                                     FAKE, FAKE, FAKE, FAKE, FAKE, theta, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     ws_bytes, None)
+
+    assert call(gates=None) == ops.SAS_ERR_INVALID_ARG  # gated steps only
+    assert call(max_sel=0) == ops.SAS_ERR_INVALID_ARG
+    assert call(theta=0.5) == ops.SAS_ERR_INVALID_ARG
+    assert call(ws_bytes=need - 1) == ops.SAS_ERR_WORKSPACE
+
+
 def test_workspace_sizes(lib):
     # 256 (sequence, KV head) units fill the CUs: one workgroup each, no partials
     sh = _shape(batch=32, n_q_heads=32, n_kv_heads=8, max_blocks=512)
