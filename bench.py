@@ -248,6 +248,61 @@ def run_prefill(args):
     print(json.dumps(line), flush=True)
 
 
+def time_backward(args, layers, w0):
+    """sas_gate_backward after a gated step of each layer, launched back to
+    back over the rotated layers and bracketed by HIP events."""
+    import numpy as np
+    import torch
+    from learned_block_sparse_tok_amd import ops
+    from learned_block_sparse_tok_amd import workloads as wl
+    dev = w0.q.device
+    n_sel = args.budget // 64
+    shape = ops.make_shape(w0.batch, w0.n_q_heads, w0.n_kv_heads, w0.max_blocks, w0.strides)
+    ws = torch.empty(ops.gate_backward_workspace_bytes(shape, n_sel), dtype=torch.uint8, device=dev)
+    jobs = []
+    for l, L in enumerate(layers):
+        w = L["w"]
+        dec = ops.SparseDecoder(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, args.budget, w.theta,
+                                True, device=dev)
+        dec.step(w.q, w.w_q, w.w_qnorm, L["gk"], w.k_pool, w.v_pool, w.block_table, w.seq_lens)
+        gen = torch.Generator(device=dev).manual_seed(900 + l)
+        d_out = torch.randn((w.batch, w.n_q_heads, 128), generator=gen, device=dev).to(torch.bfloat16)
+        out = ops.gate_backward(shape, w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens, dec.sel, dec.gates,
+                                dec.cnt, n_sel, dec.sm_scale, w.w_q, w.w_qnorm, w.w_k, w.w_knorm, L["gk"], w.theta,
+                                d_out, workspace=ws)
+        jobs.append((w, L["gk"], dec, d_out, out))
+    torch.cuda.synchronize()
+
+    def one(i):
+        w, gk, dec, d_out, out = jobs[i % len(jobs)]
+        ops.gate_backward(shape, w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens, dec.sel, dec.gates, dec.cnt,
+                          n_sel, dec.sm_scale, w.w_q, w.w_qnorm, w.w_k, w.w_knorm, gk, w.theta, d_out, workspace=ws,
+                          out=out)
+
+    for i in range(args.warmup):
+        one(i)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        one(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    kv_b = float(np.mean([kv_bytes_per_step(wl.host(j[2].cnt), 64 * 128 * 2) for j in jobs]))
+    log(f"gate backward: {ms * 1e3:.1f} us per step, {kv_b / (ms * 1e-3) / 1e9:.0f} GB/s of selected K+V")
+    return {"metric": "continuous-gate backward us/step (gate, gate-query and gate-key parameter gradients)",
+            "value": round(ms * 1e3, 2), "unit": "us", "higher_is_better": False, "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "dtype": "bf16 inputs, fp32 gradients", "data": "synthetic",
+            "config": {"workload": args.workload, "batch": w0.batch, "budget_tokens": args.budget,
+                       "layers_rotated": len(layers)},
+            "roofline": {"bound": "hbm", "kernel": "sas_gate_backward (3 kernels)",
+                         "achieved": round(kv_b / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(kv_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                         "bytes_per_launch": kv_b}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,6 +317,8 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB --steps times (a kernel of "
                          "known traffic, for calibrating the HBM byte counters), then exit")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time sas_gate_backward after the gated step (prints a second JSON line)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each layer's step from a HIP graph instead of launching it eagerly "
                          "(eager is faster here: the host stays ahead of the GPU)")
@@ -411,6 +468,8 @@ def main():
         line["cpu_baseline"] = cpu_baseline(layers[0], args.budget, worst == "gated", args.cpu_seconds)
         log(f"cpu baseline: {line['cpu_baseline']['value']:.1f} queries/s on {line['cpu_baseline']['cores']} threads")
     print(json.dumps(line), flush=True)
+    if args.backward:
+        print(json.dumps(time_backward(args, layers, w0)), flush=True)
 
 
 if __name__ == "__main__":

@@ -347,18 +347,20 @@ sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *
 
 namespace {
 struct BackwardWorkspace {
-  size_t du_q, dwqn, du_k, dwkn, pool, total;
+  size_t du_q, dwqn, du_k, dwkn, pool, part, total;
 };
 BackwardWorkspace backward_workspace(const sas_shape *sh, int32_t max_sel) {
   const size_t q_rows = (size_t)sh->batch * sh->n_q_heads * SAS_GATE_DIM * sizeof(float);
+  const size_t unit_rows = (size_t)sh->batch * sh->n_kv_heads * SAS_GATE_DIM * sizeof(float);
   const size_t k_slots = (size_t)sh->batch * sh->n_kv_heads * max_sel;
   BackwardWorkspace w;
   w.du_q = 0;
   w.dwqn = w.du_q + align256(q_rows);
-  w.du_k = w.dwqn + align256(q_rows);
+  w.du_k = w.dwqn + align256(unit_rows);
   w.dwkn = w.du_k + align256(k_slots * SAS_GATE_DIM * sizeof(float));
-  w.pool = w.dwkn + align256(k_slots * SAS_GATE_DIM * sizeof(float));
-  w.total = w.pool + align256(k_slots * 3 * SAS_HEAD_DIM * sizeof(float));
+  w.pool = w.dwkn + align256(unit_rows);
+  w.part = w.pool + align256(k_slots * 3 * SAS_HEAD_DIM * sizeof(float));
+  w.total = w.part + align256((size_t)sh->n_kv_heads * 12 * sas::kSplitK * 64 * 64 * sizeof(float));
   return w;
 }
 }  // namespace
@@ -415,6 +417,7 @@ sas_status sas_gate_backward(const sas_shape *shape, const void *q, const void *
   p.ws_du_k = (float *)(ws + wl.du_k);
   p.ws_dwkn = (float *)(ws + wl.dwkn);
   p.ws_pool = (float *)(ws + wl.pool);
+  p.ws_part = (float *)(ws + wl.part);
   p.page_stride = shape->page_stride;
   p.tok_stride = shape->tok_stride;
   p.head_stride = shape->head_stride;

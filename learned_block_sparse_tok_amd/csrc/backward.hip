@@ -27,8 +27,11 @@
 //     its RMSNorm weight term; du, pooled statistics and RMSNorm weight term
 //     of every selected historical block), recomputing the gate queries and
 //     the selected blocks' pooled keys in fp32.
-//   gate_param_reduce_kernel  the weight gradients as sums over the batch of
-//     outer products of those factors (a fixed order: deterministic).
+//   gate_param_reduce_kernel + gate_dwk_sum_kernel  the weight gradients as
+//     sums over the batch of outer products of those factors, as 64 x 64
+//     output tiles with the factor rows staged in LDS; dW_k's rows are split
+//     into ranges whose partial tiles are then added in order (a fixed order
+//     throughout: deterministic).
 #include "sas_device.h"
 #include "sas_kernels.h"
 
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
   __shared__ float pooled[kChainBlocks][3 * kHeadDim];
   __shared__ float uk[kChainBlocks][kGateDim];
   __shared__ float rk[kChainBlocks];
-  __shared__ float red[256];
+  __shared__ float dwk_acc[4][kGateDim];  // per wave: the key-side norm-weight term summed over its blocks
 
   const int t = threadIdx.x;
   const int unit = blockIdx.x;
@@ -240,28 +243,32 @@ __global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
   }
   __syncthreads();
 
-  // ---- query side: per head d(u/r * w) = RoPE^T(dghat / G), RMSNorm backward
+  // ---- query side: per head d(u/r * w) = RoPE^T(dghat / G), RMSNorm
+  // backward; the norm-weight term summed over the group's heads
   if (t < 64) {
     float cq, sq;
     rope_cos_sin((double)(L - 1), p.inv_freq[t], cq, sq);
     float dna, dnb;
     rope_back(dghat[t] / (float)G, dghat[t + 64] / (float)G, cq, sq, dna, dnb);
+    float wsa = 0.f, wsb = 0.f;
     for (int h = 0; h < G; ++h) {
       const float na = un[h][t], nb = un[h][t + 64];
       const float aa = dna * p.w_qnorm[t], ab = dnb * p.w_qnorm[t + 64];
       const float mean = wave_sum(aa * na + ab * nb) * (1.0f / kGateDim);
       const float r = rr[h];
       float *du = p.ws_du_q + ((int64_t)s * p.n_q_heads + kvh * G + h) * kGateDim;
-      float *dw = p.ws_dwqn + ((int64_t)s * p.n_q_heads + kvh * G + h) * kGateDim;
       du[t] = (aa - na * mean) / r;
       du[t + 64] = (ab - nb * mean) / r;
-      dw[t] = dna * na;
-      dw[t + 64] = dnb * nb;
+      wsa += dna * na;
+      wsb += dnb * nb;
     }
+    p.ws_dwqn[(int64_t)unit * kGateDim + t] = wsa;
+    p.ws_dwqn[(int64_t)unit * kGateDim + t + 64] = wsb;
   }
 
   // ---- key side, kChainBlocks selected historical blocks at a time
   const int64_t slot0 = (int64_t)unit * p.max_sel;
+  float dwk_a = 0.f, dwk_b = 0.f;  // this lane's pair, summed over the wave's blocks
   for (int i0 = 0; i0 < p.max_sel; i0 += kChainBlocks) {
     const int nb_ = max(0, min(kChainBlocks, n_hist - i0));
     __syncthreads();
@@ -271,6 +278,7 @@ __global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
       const int64_t page = bt[sel[i0 + b]];
       const uint16_t *kb = p.k_pool + page * p.page_stride + (int64_t)kvh * p.head_stride + d;
       float mx = -__builtin_inff(), mn = __builtin_inff(), sum = 0.f;
+#pragma unroll 16
       for (int r = 0; r < kBlock; ++r) {
         const float x = bf16_to_f32(kb[(int64_t)r * p.tok_stride]);
         mx = fmaxf(mx, x);
@@ -310,12 +318,10 @@ __global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
       for (int b = wave; b < kChainBlocks; b += 4) {
         const int i = i0 + b;
         float *du = p.ws_du_k + (slot0 + min(i, p.max_sel - 1)) * kGateDim;
-        float *dw = p.ws_dwkn + (slot0 + min(i, p.max_sel - 1)) * kGateDim;
         float *pk = p.ws_pool + (slot0 + min(i, p.max_sel - 1)) * 3 * kHeadDim;
         if (i >= p.max_sel) break;
         if (b >= nb_) {  // local block or padding: no gradient
           du[lane] = du[lane + 64] = 0.f;
-          dw[lane] = dw[lane + 64] = 0.f;
           for (int e = lane; e < 3 * kHeadDim; e += 64) pk[e] = 0.f;
           continue;
         }
@@ -333,48 +339,142 @@ __global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
         const float mean = wave_sum(aa * na + ab * nb) * (1.0f / kGateDim);
         du[lane] = (aa - na * mean) / r;
         du[lane + 64] = (ab - nb * mean) / r;
-        dw[lane] = dma * na;
-        dw[lane + 64] = dmb * nb;
+        dwk_a += dma * na;
+        dwk_b += dmb * nb;
         for (int e = lane; e < 3 * kHeadDim; e += 64) pk[e] = pooled[b][e];
       }
     }
   }
+  {
+    const int wave = t >> 6, lane = t & 63;
+    dwk_acc[wave][lane] = dwk_a;
+    dwk_acc[wave][lane + 64] = dwk_b;
+  }
+  __syncthreads();
+  if (t < kGateDim)
+    p.ws_dwkn[(int64_t)unit * kGateDim + t] = dwk_acc[0][t] + dwk_acc[1][t] + dwk_acc[2][t] + dwk_acc[3][t];
 }
 
 // ---------------------------------------------------------------- sums over the batch
-// blockIdx.x < Hq*128: one row (h, j) of dW_q; then Hkv*128 rows (kvh, j) of
-// dW_k; then one workgroup for the two norm-weight gradients.
-__global__ __launch_bounds__(256) void gate_param_reduce_kernel(BackwardParams p) {
-  const int t = threadIdx.x;
-  const int rows_q = p.n_q_heads * kGateDim, rows_k = p.n_kv_heads * kGateDim;
-  const int B = p.batch;
-  if ((int)blockIdx.x < rows_q) {
-    const int h = blockIdx.x >> 7, jj = blockIdx.x & 127;
-    if (t < kHeadDim) {
-      float acc = 0.f;
-      for (int s = 0; s < B; ++s)
-        acc = fmaf(p.ws_du_q[((int64_t)s * p.n_q_heads + h) * kGateDim + jj],
-                   bf16_to_f32(p.q[((int64_t)s * p.n_q_heads + h) * kHeadDim + t]), acc);
-      p.d_w_q[((int64_t)h * kGateDim + jj) * kHeadDim + t] = acc;
+// out[j][i] = sum_n a[n][j] * b[n][i] for one 64 x 64 tile: the a and b rows
+// are staged in LDS 32 at a time; thread (ty, tx) owns a 4 x 4 block of the
+// tile and sums the rows in order (deterministic).  b is fp32 or bf16.
+template <typename TB>
+__device__ __forceinline__ float load_b(const TB *b, int64_t i);
+template <>
+__device__ __forceinline__ float load_b<float>(const float *b, int64_t i) { return b[i]; }
+template <>
+__device__ __forceinline__ float load_b<uint16_t>(const uint16_t *b, int64_t i) { return bf16_to_f32(b[i]); }
+
+template <typename TB>
+__device__ void outer_sum_tile(const float *a, int64_t a_row, const TB *b, int64_t b_row, int n, int j0, int i0,
+                               int i_lim, float *out, int64_t out_row, float (&as)[32][64], float (&bs)[32][64]) {
+  const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
+  float acc[4][4] = {};
+  for (int n0 = 0; n0 < n; n0 += 32) {
+    __syncthreads();
+    for (int e = t; e < 32 * 64; e += 256) {
+      const int r = e >> 6, c = e & 63;
+      const bool live = n0 + r < n;
+      as[r][c] = live ? a[(int64_t)(n0 + r) * a_row + j0 + c] : 0.f;
+      bs[r][c] = live && i0 + c < i_lim ? load_b(b, (int64_t)(n0 + r) * b_row + i0 + c) : 0.f;
     }
-  } else if ((int)blockIdx.x < rows_q + rows_k) {
-    const int row = blockIdx.x - rows_q;
-    const int kvh = row >> 7, jj = row & 127;
-    for (int in = t; in < 3 * kHeadDim; in += 256) {
-      float acc = 0.f;
-      for (int s = 0; s < B; ++s) {
-        const int64_t base = ((int64_t)s * p.n_kv_heads + kvh) * p.max_sel;
-        for (int i = 0; i < p.max_sel; ++i)
-          acc = fmaf(p.ws_du_k[(base + i) * kGateDim + jj], p.ws_pool[(base + i) * 3 * kHeadDim + in], acc);
+    __syncthreads();
+#pragma unroll 8
+    for (int r = 0; r < 32; ++r) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        av[u] = as[r][4 * ty + u];
+        bv[u] = bs[r][4 * tx + u];
       }
-      p.d_w_k[((int64_t)kvh * kGateDim + jj) * 3 * kHeadDim + in] = acc;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
     }
-  } else if (t < kGateDim) {
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (i0 + 4 * tx + v < i_lim) out[(int64_t)(j0 + 4 * ty + u) * out_row + i0 + 4 * tx + v] = acc[u][v];
+}
+
+// blocks [0, Hq*4): dW_q[h] tiles (2 x 2 per head), sum over the batch of
+// du_q (x) q; then Hkv*12*kSplitK blocks: partial dW_k[kvh] tiles (2 x 6 per
+// head, the (sequence, slot) rows split into kSplitK ranges), sums of
+// du_k (x) pooled; the last block: the norm-weight gradients as sums over the
+// (sequence, KV head) rows.
+__global__ __launch_bounds__(256) void gate_param_reduce_kernel(BackwardParams p) {
+  __shared__ float as[32][64], bs[32][64];
+  const int tiles_q = p.n_q_heads * 4, tiles_k = p.n_kv_heads * 12;  // dW_k: 12 tiles of 64 x 64 per KV head
+  const int bid = blockIdx.x;
+  if (bid < tiles_q) {
+    const int h = bid >> 2, jt = (bid >> 1) & 1, it = bid & 1;
+    outer_sum_tile<uint16_t>(p.ws_du_q + (int64_t)h * kGateDim, (int64_t)p.n_q_heads * kGateDim,
+                             p.q + (int64_t)h * kHeadDim, (int64_t)p.n_q_heads * kHeadDim, p.batch, 64 * jt, 64 * it,
+                             kHeadDim, p.d_w_q + (int64_t)h * kGateDim * kHeadDim, kHeadDim, as, bs);
+  } else if (bid < tiles_q + tiles_k * kSplitK) {
+    // one of kSplitK consecutive row ranges of one dW_k tile -> a partial tile
+    const int k = (bid - tiles_q) / kSplitK, part = (bid - tiles_q) % kSplitK;
+    const int kvh = k / 12, jt = (k % 12) / 6, it = k % 6;
+    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+    float acc[4][4] = {};
+    const int n = p.batch * p.max_sel;
+    const int per = (n + kSplitK - 1) / kSplitK;
+    const int n_lo = part * per, n_hi = min(n, n_lo + per);
+    for (int n0 = n_lo; n0 < n_hi; n0 += 32) {
+      __syncthreads();
+      for (int e = tid; e < 32 * 64; e += 256) {
+        const int r = e >> 6, c = e & 63;
+        const int nn = n0 + r;
+        const bool live = nn < n_hi;
+        const int64_t slot = live ? ((int64_t)(nn / p.max_sel) * p.n_kv_heads + kvh) * p.max_sel + nn % p.max_sel : 0;
+        as[r][c] = live ? p.ws_du_k[slot * kGateDim + 64 * jt + c] : 0.f;
+        bs[r][c] = live ? p.ws_pool[slot * 3 * kHeadDim + 64 * it + c] : 0.f;
+      }
+      __syncthreads();
+#pragma unroll 8
+      for (int r = 0; r < 32; ++r) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          av[u] = as[r][4 * ty + u];
+          bv[u] = bs[r][4 * tx + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
+      }
+    }
+    float *dst = p.ws_part + ((int64_t)k * kSplitK + part) * 64 * 64;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dst[(4 * ty + u) * 64 + 4 * tx + v] = acc[u][v];
+  } else if (threadIdx.x < kGateDim) {
+    const int t = threadIdx.x;
+    const int units = p.batch * p.n_kv_heads;
     float aq = 0.f, ak = 0.f;
-    for (int s = 0; s < B * p.n_q_heads; ++s) aq += p.ws_dwqn[(int64_t)s * kGateDim + t];
-    for (int s = 0; s < B * p.n_kv_heads * p.max_sel; ++s) ak += p.ws_dwkn[(int64_t)s * kGateDim + t];
+    for (int u = 0; u < units; ++u) {
+      aq += p.ws_dwqn[(int64_t)u * kGateDim + t];
+      ak += p.ws_dwkn[(int64_t)u * kGateDim + t];
+    }
     p.d_w_qnorm[t] = aq;
     p.d_w_knorm[t] = ak;
+  }
+}
+
+// dW_k from its partial tiles, summed in order of the row ranges
+__global__ __launch_bounds__(256) void gate_dwk_sum_kernel(BackwardParams p) {
+  const int k = blockIdx.x;  // tile
+  const int kvh = k / 12, jt = (k % 12) / 6, it = k % 6;
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    float acc = 0.f;
+    for (int part = 0; part < kSplitK; ++part) acc += p.ws_part[((int64_t)k * kSplitK + part) * 64 * 64 + e];
+    p.d_w_k[((int64_t)kvh * kGateDim + 64 * jt + (e >> 6)) * 3 * kHeadDim + 64 * it + (e & 63)] = acc;
   }
 }
 
@@ -386,8 +486,11 @@ hipError_t launch_gate_backward(const BackwardParams &p, hipStream_t st) {
   hipLaunchKernelGGL(gate_chain_kernel, dim3(units), dim3(256), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned rows = (unsigned)((p.n_q_heads + p.n_kv_heads) * kGateDim + 1);
-  hipLaunchKernelGGL(gate_param_reduce_kernel, dim3(rows), dim3(256), 0, st, p);
+  const unsigned tiles = (unsigned)(p.n_q_heads * 4 + p.n_kv_heads * 12 * kSplitK + 1);
+  hipLaunchKernelGGL(gate_param_reduce_kernel, dim3(tiles), dim3(256), 0, st, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gate_dwk_sum_kernel, dim3((unsigned)(p.n_kv_heads * 12)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

@@ -84,6 +84,7 @@ struct PrefillParams {
 };
 
 constexpr int kChainBlocks = 16;  // selected blocks the backward chain handles at a time
+constexpr int kSplitK = 8;        // row ranges of each dW_k tile summed separately, then in order
 
 struct BackwardParams {
   const uint16_t *q, *k_pool, *v_pool, *d_out, *gate_keys, *w_q, *w_k;
@@ -92,9 +93,11 @@ struct BackwardParams {
   float *d_gates;                 // [B][Hkv][max_sel]
   float *d_w_q, *d_w_qnorm, *d_w_k, *d_w_knorm;
   // workspace: per-sequence factors of the weight gradients
-  float *ws_du_q, *ws_dwqn;       // [B][Hq][128]
-  float *ws_du_k, *ws_dwkn;       // [B][Hkv][max_sel][128]
+  float *ws_du_q;                 // [B][Hq][128]
+  float *ws_du_k;                 // [B][Hkv][max_sel][128]
   float *ws_pool;                 // [B][Hkv][max_sel][384]
+  float *ws_dwqn, *ws_dwkn;       // [B][Hkv][128]: norm-weight terms summed per (sequence, KV head)
+  float *ws_part;                 // [Hkv*12][kSplitK][64][64]: partial dW_k tiles
   int64_t page_stride, tok_stride, head_stride;
   int32_t batch, n_q_heads, n_kv_heads, group, max_blocks, max_sel;
   float scale_log2;

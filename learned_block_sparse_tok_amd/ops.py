@@ -263,18 +263,19 @@ def gate_backward_workspace_bytes(shape: SasShape, max_sel: int) -> int:
 
 
 def gate_backward(shape: SasShape, q, k_pool, v_pool, block_table, seq_lens, sel, gates, cnt, max_sel, sm_scale,
-                  w_q, w_qnorm, w_k, w_knorm, gate_keys, theta, d_out, workspace=None, stream=None):
+                  w_q, w_qnorm, w_k, w_knorm, gate_keys, theta, d_out, workspace=None, stream=None, out=None):
     """Gradients of the gate parameters through the continuous gates of a gated
     decode step.  Returns dict(d_gates, d_w_q, d_w_qnorm, d_w_k, d_w_knorm)
-    (fp32 device tensors)."""
+    (fp32 device tensors; `out` may supply them preallocated)."""
     dev = q.device
     B, Hq, _ = q.shape
     Hkv = shape.n_kv_heads
-    out = dict(d_gates=torch.empty((B, Hkv, max_sel), dtype=torch.float32, device=dev),
-               d_w_q=torch.empty((Hq, 128, 128), dtype=torch.float32, device=dev),
-               d_w_qnorm=torch.empty(128, dtype=torch.float32, device=dev),
-               d_w_k=torch.empty((Hkv, 128, 384), dtype=torch.float32, device=dev),
-               d_w_knorm=torch.empty(128, dtype=torch.float32, device=dev))
+    if out is None:
+        out = dict(d_gates=torch.empty((B, Hkv, max_sel), dtype=torch.float32, device=dev),
+                   d_w_q=torch.empty((Hq, 128, 128), dtype=torch.float32, device=dev),
+                   d_w_qnorm=torch.empty(128, dtype=torch.float32, device=dev),
+                   d_w_k=torch.empty((Hkv, 128, 384), dtype=torch.float32, device=dev),
+                   d_w_knorm=torch.empty(128, dtype=torch.float32, device=dev))
     if workspace is None:
         workspace = torch.empty(gate_backward_workspace_bytes(shape, max_sel), dtype=torch.uint8, device=dev)
     st = lib().sas_gate_backward(ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"),

@@ -226,3 +226,64 @@ def test_prefill_full_size_sampled_parity():
         o = dict(gate_keys=gk_o, sel=sel, gates=gates, cnt=cnt, scores=scores, out=out)
         ties, skipped = compare_step(h, g, o, gated, w.budget)
         say(f"  boundary ties {ties}, unenumerated {skipped}")
+
+
+def test_gate_backward_full_size():
+    """sas_gate_backward on the qwen3_8b decode workload (32 sequences, 32K
+    context, budget 2048): d_gates of sampled sequences and every output of a
+    two-sequence sub-batch against the oracle, and the batch sums checked by
+    linearity (the full batch equals the sum over its two halves)."""
+    from test_gpu_backward import close
+    w = wl.named("qwen3_8b", device=DEV)
+    n_sel = w.budget // 64
+    gk = gpu_pool(w)
+    gen = torch.Generator(device=DEV).manual_seed(77)
+    d_out = torch.randn((w.batch, w.n_q_heads, 128), generator=gen, device=DEV).to(torch.bfloat16)
+
+    def run(sub):
+        dec = ops.SparseDecoder(sub.batch, sub.n_q_heads, sub.n_kv_heads, sub.max_blocks, sub.strides, w.budget,
+                                w.theta, True, device=DEV)
+        gks = gpu_pool(sub)
+        dec.select(sub.q, sub.w_q, sub.w_qnorm, gks, sub.block_table, sub.seq_lens)
+        shape = ops.make_shape(sub.batch, sub.n_q_heads, sub.n_kv_heads, sub.max_blocks, sub.strides)
+        return dec, ops.gate_backward(shape, sub.q, sub.k_pool, sub.v_pool, sub.block_table, sub.seq_lens, dec.sel,
+                                      dec.gates, dec.cnt, n_sel, SM_SCALE, sub.w_q, sub.w_qnorm, sub.w_k,
+                                      sub.w_knorm, gks, w.theta, d_out[torch.as_tensor(sub_idx[id(sub)], device=DEV)])
+
+    sub_idx = {}
+
+    def subset(seqs):
+        sub = sub_workload(w, seqs)
+        sub_idx[id(sub)] = list(seqs)
+        return sub
+
+    full = dataclasses.replace(w)
+    sub_idx[id(full)] = list(range(w.batch))
+    dec_f, bf = run(full)
+    lo, hi = subset(range(0, 16)), subset(range(16, 32))
+    _, b_lo = run(lo)
+    _, b_hi = run(hi)
+    torch.cuda.synchronize()
+    for name in ("d_w_q", "d_w_qnorm", "d_w_k", "d_w_knorm"):
+        close(wl.host(bf[name]), wl.host(b_lo[name]).astype(np.float64) + wl.host(b_hi[name]), 1e-5, name + " (halves)")
+    # two sampled sequences against the oracle
+    seqs = [3, 30]
+    two = subset(seqs)
+    dec2, b2 = run(two)
+    torch.cuda.synchronize()
+    h = Host(two)
+    gk_o = np.zeros((two.n_pages, two.n_kv_heads, 128), np.uint16)
+    from harness import complete_blocks
+    cs, cb = complete_blocks(h.lens)
+    oracle.pool_blocks(h.k, h.bt, two.strides, two.n_kv_heads, cs, cb, h.w_k, h.wkn, w.theta, gk_o)
+    sel, gates, cnt, scores = oracle.gate_topk(h.q, h.w_q, h.wqn, gk_o, h.bt, h.lens, w.theta, w.budget,
+                                               w.n_kv_heads)
+    from gpu_harness import compare_selection
+    g = dict(sel=wl.host(dec2.sel), gates=wl.host(dec2.gates), cnt=wl.host(dec2.cnt))
+    assert compare_selection(g, dict(sel=sel, gates=gates, cnt=cnt, scores=scores), h.lens, w.budget) == []
+    bo = oracle.gate_backward(h.q, h.k, h.v, h.bt, two.strides, two.n_kv_heads, h.lens, sel, gates, cnt, SM_SCALE,
+                              h.w_q, h.wqn, h.w_k, h.wkn, gk_o, w.theta, wl.host(d_out)[seqs])
+    for name in ("d_gates", "d_w_q", "d_w_qnorm", "d_w_k", "d_w_knorm"):
+        close(wl.host(b2[name]), bo[name], 1e-3, name)
+    # the full batch's gate gradients of those sequences are the same numbers
+    close(wl.host(bf["d_gates"])[seqs], bo["d_gates"], 1e-3, "d_gates (full batch)")
