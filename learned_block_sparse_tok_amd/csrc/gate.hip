@@ -32,6 +32,7 @@
 namespace sas {
 
 constexpr int kKeysInFlight = 32;  // gate keys per 16-lane group per pass (512 per workgroup)
+constexpr int kKeysEarly = 16;     // of those, issued before the projection
 
 // Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then the
 // row broadcasts of lanes 15 and 31).
@@ -108,6 +109,18 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
   for (int c = t + 256 * kBtUnroll; c < p.max_blocks; c += 256) slot[c] = (uint32_t)bt[c];
   lds_barrier();
 
+  // ---- 1b. issue the first 256 candidates' gate keys now (they arrive
+  // during the projection); the other 256 follow it (keeping all 512 in
+  // registers across the projection would cost occupancy)
+  const uint16_t *gkh = p.gate_keys + (int64_t)kvh * kGateDim + 8 * lane16;
+  const int64_t page_stride = (int64_t)p.n_kv_heads * kGateDim;
+  u32x4 v[kKeysInFlight];
+#pragma unroll
+  for (int u = 0; u < kKeysEarly; ++u) {
+    const int c = 16 * u + grp;
+    v[u] = c < n ? ld16(gkh + (int64_t)slot[c] * page_stride) : u32x4{0, 0, 0, 0};
+  }
+
   // ---- 2. gate queries: v[g][j] = sum_d w_q[h][j][d] q[h][d]
   auto project_row = [&](const u32x4 &w, int r) {
     const int o = grp * rows_per_grp + r;
@@ -132,13 +145,10 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) project_row(wv[u], b0 + u);
   }
-  // ---- 2b. issue the first 512 candidates' gate keys; they arrive while
-  // the gate queries are normalised and rotated
-  const uint16_t *gkh = p.gate_keys + (int64_t)kvh * kGateDim + 8 * lane16;
-  const int64_t page_stride = (int64_t)p.n_kv_heads * kGateDim;
-  u32x4 v[kKeysInFlight];
+  // ---- 2b. issue candidates 256 .. 511; they arrive while the gate queries
+  // are normalised and rotated
 #pragma unroll
-  for (int u = 0; u < kKeysInFlight; ++u) {
+  for (int u = kKeysEarly; u < kKeysInFlight; ++u) {
     const int c = 16 * u + grp;
     v[u] = c < n ? ld16(gkh + (int64_t)slot[c] * page_stride) : u32x4{0, 0, 0, 0};
   }
