@@ -213,6 +213,29 @@ sas_status sas_prefill_select(const sas_shape *shape, const void *q, const void 
   if (!(rope_theta > 1.0)) return fail(SAS_ERR_INVALID_ARG, "rope_theta must be > 1");
   if (!aligned16(gate_keys) || !aligned16(w_q))
     return fail(SAS_ERR_UNSUPPORTED, "gate_keys and w_q must be 16-byte aligned");
+  const int n_qblocks = (seq_len + SAS_BLOCK - 1) / SAS_BLOCK;
+  if (n_qblocks - 1 <= sas::kMaxCandBatched) {  // one workgroup per 64 positions and KV head
+    sas::PrefillSelectParams b;
+    b.q = (const uint16_t *)q;
+    b.w_q = (const uint16_t *)w_q;
+    b.w_qnorm = w_qnorm;
+    b.gate_keys = (const uint16_t *)gate_keys;
+    b.block_table = block_table_row;
+    b.sel = sel;
+    b.gates = gates;
+    b.cnt = cnt;
+    b.scores = scores;
+    b.n_q_heads = shape->n_q_heads;
+    b.n_kv_heads = shape->n_kv_heads;
+    b.group = shape->n_q_heads / shape->n_kv_heads;
+    b.max_blocks = shape->max_blocks;
+    b.n_sel = budget_tokens / SAS_BLOCK;
+    b.seq_len = seq_len;
+    b.n_qblocks = n_qblocks;
+    for (int i = 0; i < SAS_GATE_DIM / 2; ++i) b.inv_freq[i] = pow(rope_theta, -(double)i / (SAS_GATE_DIM / 2));
+    return hip_status(sas::launch_prefill_select(b, (hipStream_t)stream), "sas_prefill_select launch");
+  }
+  // longer sequences: the decode selection kernel once per (position, KV head)
   sas::GateParams p;
   p.q = (const uint16_t *)q;
   p.w_q = (const uint16_t *)w_q;

@@ -104,7 +104,24 @@ struct BackwardParams {
   double inv_freq[kGateDim / 2];
 };
 
+constexpr int kMaxCandBatched = 512;  // candidates per position the batched prefill selection holds
+
+struct PrefillSelectParams {
+  const uint16_t *q;            // [T][Hq][128]
+  const uint16_t *w_q;          // [Hq][128 out][128 in]
+  const float *w_qnorm;
+  const uint16_t *gate_keys;    // [P][Hkv][128]
+  const int32_t *block_table;   // the sequence's row
+  int32_t *sel;                 // [T][Hkv][n_sel]
+  float *gates;                 // nullable
+  int32_t *cnt;                 // [T][Hkv]
+  float *scores;                // [T][Hkv][max_blocks], nullable
+  int32_t n_q_heads, n_kv_heads, group, max_blocks, n_sel, seq_len, n_qblocks;
+  double inv_freq[kGateDim / 2];
+};
+
 hipError_t launch_pool(const PoolParams &p, hipStream_t st);
+hipError_t launch_prefill_select(const PrefillSelectParams &p, hipStream_t st);
 hipError_t launch_gate_backward(const BackwardParams &p, hipStream_t st);
 hipError_t launch_prefill_attend(const PrefillParams &p, hipStream_t st);
 hipError_t launch_append(const AppendParams &p, int batch, hipStream_t st);

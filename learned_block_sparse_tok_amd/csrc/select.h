@@ -1,0 +1,141 @@
+// Exact Top-K of one row of order-preserving score keys by one wave, shared
+// by the decode selection and the training-time forward's selection.
+#pragma once
+#include "sas_device.h"
+
+namespace sas {
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then the
+// row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
+// Writes the selection of one (sequence or position, KV head): the k_eff
+// best of the n candidate keys keys[0 .. n) under (score descending, index
+// ascending), in ascending block order, then the local block n; padding -1
+// up to n_sel; gates (nullable) = sigmoid(score) for the chosen historical
+// blocks, 1 for the local block, 0 padding; *cnt = k_eff + 1.
+//   keys: LDS, 16-byte aligned, readable up to max(n, 512) entries (keys are
+//   > 0; entries past n are ignored); hist: this wave's 256-entry LDS
+//   histogram.  Radix select over 8-bit digits with a wave-private histogram
+//   and DPP prefix sums; keys > T are taken, and the krem lowest-index keys
+//   equal to T.  Lane l sweeps keys [512k + 8l, 512k + 8l + 8); the first 512
+//   stay in registers across the passes.
+__device__ __forceinline__ void wave_select(const uint32_t *keys, int n, int k_eff, int n_sel, uint32_t *hist,
+                                            int32_t *sel, float *gates, int32_t *cnt_out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t k0[8];  // keys 8l .. 8l+7 (0 past the candidates: keys are > 0)
+  {
+    const u32x4 a = *reinterpret_cast<const u32x4 *>(&keys[8 * lane]);
+    const u32x4 b = *reinterpret_cast<const u32x4 *>(&keys[8 * lane + 4]);
+    const uint32_t r[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) k0[e] = 8 * lane + e < n ? r[e] : 0u;
+  }
+  auto key_at = [&](int c0, int e) -> uint32_t {  // key c0 + e of this lane's sweep
+    return c0 == 8 * lane ? k0[e] : (c0 + e < n ? keys[c0 + e] : 0u);
+  };
+  uint32_t T = 0, krem = 0;  // k_eff >= n: every candidate (all keys are > 0)
+  if (k_eff > 0 && k_eff < n) {
+    uint32_t prefix = 0, mask = 0;
+    krem = (uint32_t)k_eff;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      *reinterpret_cast<u32x4 *>(&hist[4 * lane]) = u32x4{0, 0, 0, 0};
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (k0[e] != 0u && (k0[e] & mask) == prefix) atomicAdd(&hist[(k0[e] >> shift) & 255u], 1u);
+      for (int c0 = 8 * lane + 512; c0 < n; c0 += 512) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t k = key_at(c0, e);
+          if (k != 0u && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      // lane l owns digits 255-4l .. 252-4l (descending)
+      const u32x4 h4 = *reinterpret_cast<const u32x4 *>(&hist[252 - 4 * lane]);
+      const uint32_t cnt[4] = {h4.w, h4.z, h4.y, h4.x};
+      const uint32_t tot = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+      uint32_t run = wave_incl_scan(tot) - tot;  // keys in higher digits
+      int found_e = -1;
+      uint32_t found_krem = 0, found_cnt = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (found_e < 0 && run < krem && run + cnt[e] >= krem) {
+          found_e = e;
+          found_krem = krem - run;
+          found_cnt = cnt[e];
+        }
+        run += cnt[e];
+      }
+      const unsigned long long who = __ballot(found_e >= 0);
+      const int leader = (int)__builtin_ctzll(who);  // exactly one lane finds the digit
+      const uint32_t d = 255u - (uint32_t)(4 * leader + __builtin_amdgcn_readlane(found_e, leader));
+      krem = (uint32_t)__builtin_amdgcn_readlane((int)found_krem, leader);
+      const uint32_t bin_cnt = (uint32_t)__builtin_amdgcn_readlane((int)found_cnt, leader);
+      prefix |= d << shift;
+      mask |= 0xFFu << shift;
+      if (bin_cnt == krem) {  // the whole bin is taken: every key >= prefix
+        T = prefix - 1u;      // prefix > 0 here: some keys lie below the bin
+        krem = 0;
+        break;
+      }
+      T = prefix;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  if (k_eff > 0) {
+    uint32_t pos_base = 0, eq_base = 0;
+    for (int c0 = 0; c0 < n; c0 += 512) {
+      const int cl = c0 + 8 * lane;
+      uint32_t kk[8];
+      uint32_t n_eq = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kk[e] = key_at(cl, e);
+        n_eq += (krem > 0 && kk[e] == T);
+      }
+      const uint32_t eq_incl = wave_incl_scan(n_eq);
+      uint32_t eq_rank = eq_base + eq_incl - n_eq;  // equal keys before this lane's
+      uint32_t take_mask = 0, n_take = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bool take = kk[e] > T;
+        if (krem > 0 && kk[e] == T) take = eq_rank++ < krem;
+        take_mask |= (uint32_t)take << e;
+        n_take += take;
+      }
+      const uint32_t take_incl = wave_incl_scan(n_take);
+      uint32_t pos = pos_base + take_incl - n_take;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (take_mask >> e & 1u) {
+          sel[pos] = cl + e;
+          if (gates) gates[pos] = 1.0f / (1.0f + __expf(-key_score(kk[e])));
+          ++pos;
+        }
+      }
+      pos_base += (uint32_t)__builtin_amdgcn_readlane((int)take_incl, 63);
+      eq_base += (uint32_t)__builtin_amdgcn_readlane((int)eq_incl, 63);
+    }
+  }
+  for (int i = k_eff + lane; i < n_sel; i += 64) {
+    sel[i] = i == k_eff ? n : -1;
+    if (gates) gates[i] = i == k_eff ? 1.0f : 0.0f;
+  }
+  if (lane == 0) *cnt_out = k_eff + 1;
+}
+
+}  // namespace sas
+

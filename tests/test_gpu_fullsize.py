@@ -287,3 +287,27 @@ def test_gate_backward_full_size():
         close(wl.host(b2[name]), bo[name], 1e-3, name)
     # the full batch's gate gradients of those sequences are the same numbers
     close(wl.host(bf["d_gates"])[seqs], bo["d_gates"], 1e-3, "d_gates (full batch)")
+
+
+def test_prefill_long_sequence_uses_the_per_position_selection():
+    """A sequence longer than the batched selection holds (33,000 tokens: 516
+    blocks) selects with the per-position gate kernel; sampled positions
+    against the oracle, gated mode."""
+    T = 33000
+    w = wl.make_prefill(T, 8, 2, 2048, "paged", 7, DEV, random_norms=True)
+    gk = prefill_gate_keys(w)
+    pos = np.array([0, 4095, 32831, 32832, 32900, T - 1])
+    sub = dataclasses.replace(w, batch=len(pos), q=w.q[torch.as_tensor(pos, device=DEV)],
+                              seq_lens=torch.as_tensor(pos + 1, dtype=torch.int32, device=DEV),
+                              block_table=w.block_table[:len(pos)])
+    h = Host(sub)
+    nb = T // 64
+    gk_o = np.zeros((w.n_pages, w.n_kv_heads, wl.GATE_DIM), np.uint16)
+    oracle.pool_blocks(h.k, h.bt[:1], w.strides, w.n_kv_heads, np.zeros(nb, np.int32), np.arange(nb, dtype=np.int32),
+                       h.w_k, h.wkn, w.theta, gk_o)
+    g = gpu_prefill(w, gk, True, w.budget, positions=pos)
+    sel, gates, cnt, scores, out = oracle.prefill(wl.host(w.q), h.k, h.v, h.bt[0], w.strides, w.n_kv_heads, gk_o,
+                                                  h.w_q, h.wqn, w.theta, w.budget, True, SM_SCALE, positions=pos)
+    o = dict(gate_keys=gk_o, sel=sel, gates=gates, cnt=cnt, scores=scores, out=out)
+    ties, skipped = compare_step(h, g, o, True, w.budget)
+    say(f"prefill T={T}: boundary ties {ties}, unenumerated {skipped}")
