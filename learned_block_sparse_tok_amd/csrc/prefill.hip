@@ -8,12 +8,14 @@
 // causally, the blocks selected for it (its own block t/64 last), plain or
 // with each historical block scaled by its continuous gate.
 //
-// One 256-thread workgroup per (64-query block, KV head, group of up to 4
+// One 512-thread workgroup per (64-query block, KV head, group of up to 4
 // query heads).  The workgroup marks the union of its queries' selections in
 // an LDS bitmap and walks it in ascending block order.  Each visited block's
 // K and V rows (32 KiB) are copied once into LDS by the gfx950 global-to-LDS
 // loads (global_load_lds_dwordx4) and shared by the 4 waves; a ring of four
 // 32 KiB stages keeps the next three blocks in flight while one is consumed.
+// Eight waves, two per SIMD, so that one wave's softmax runs while the
+// other's matrix products do.
 // The copies are the only vector-memory operations of the walk (the
 // selections of the 64 queries are staged in LDS first), so each iteration
 // waits for exactly the copies of the block it consumes.
@@ -21,8 +23,8 @@
 // row-dependent XOR swizzle instead: K's 16-byte slots by row % 16 (the
 // A-operand reads of 16 rows at one column hit 16 different slots), V's
 // 32-byte pairs by row % 4 (the transposing reads of 4 rows x 32 bytes hit 4
-// different pairs).  Wave w owns queries 16w .. 16w+15 of the block and the
-// group's heads:
+// different pairs).  Wave w owns queries 16(w%4) .. 16(w%4)+15 of the block
+// and two of the group's heads, 2(w/4) and 2(w/4)+1:
 //   S^T (64 keys x 16 queries) = K . Q^T per head with
 //     v_mfma_f32_16x16x32_bf16, K read from LDS as the A operand;
 //   the lane of a query that did not select the block masks its column to
@@ -30,8 +32,8 @@
 //   online softmax in the log2 domain; O^T += V^T . P^T, V^T read with
 //     ds_read_b64_tr_b16.
 // A wave none of whose 16 queries selected the block skips its arithmetic.
-// The work is a dense contraction per visited block: 4 heads x (64 QK + 64
-// PV) MFMAs per wave.
+// The work is a dense contraction per visited block: 2 heads x (16 QK + 16
+// PV) MFMAs x 2 per wave.
 #include <limits.h>
 
 #include "sas_device.h"
@@ -40,12 +42,13 @@
 namespace sas {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // 8 waves: 4 query quarters x 2 head pairs, two waves per SIMD
 constexpr int kRow = kHeadDim * 2;        // 256-byte K / V rows, unpadded
 constexpr int kTile = kBlock * kRow;      // 16 KiB
 constexpr int kStage = 2 * kTile;         // K tile, then V tile
 constexpr int kStages = 4;                // ring: 3 blocks in flight + 1 consumed
-constexpr int kCopies = kStage / 1024 / 4;  // 1 KiB copy instructions per wave per stage: 8
+constexpr int kCopies = kStage / 1024 / 8;  // 1 KiB copy instructions per wave per stage: 4
+constexpr int kCt = 2;                      // query heads per wave
 constexpr int kMaxSel = 64;               // selections per query staged in LDS (budgets up to 4,096)
 
 // One global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
@@ -118,7 +121,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
   const int T = p.seq_len;
   const int t0 = qb * kBlock;
   const int nq = min(kBlock, T - t0);
-  const int qi = 16 * wave + j;  // this lane's query within the block
+  const int qw = wave & 3, hp = wave >> 2;  // query quarter, head pair
+  const int qi = 16 * qw + j;              // this lane's query within the block
+  const int h_lo = 4 * hg + 2 * hp;        // this wave's first query head within the group
   const bool qvalid = qi < nq;
   const int tq = t0 + qi;
 
@@ -140,12 +145,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
   }
 
   // B operand of S^T = K Q^T: lane l holds q[query qi][head][32ks + 8(l/16) .. +7]
-  bf16x8 qB[4][4];
+  bf16x8 qB[kCt][4];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const bool ok = qvalid && ct < nh;
+  for (int ct = 0; ct < kCt; ++ct) {
+    const bool ok = qvalid && 2 * hp + ct < nh;
     const uint16_t *qrow =
-        p.q + ((int64_t)(ok ? tq : 0) * p.n_q_heads + kvh * G + 4 * hg + (ok ? ct : 0)) * kHeadDim + 8 * g;
+        p.q + ((int64_t)(ok ? tq : 0) * p.n_q_heads + kvh * G + (ok ? h_lo + ct : 0)) * kHeadDim + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qB[ct][ks] = as_bf16(ok ? ld16(qrow + 32 * ks) : u32x4{0, 0, 0, 0});
   }
@@ -158,27 +163,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
   int nxt_c = cq > 0 ? sel_l[qi][0] : INT_MAX;
   float nxt_g = kGated ? gate_l[kGated ? qi : 0][0] : 1.f;
 
-  f32x4 o[4][8];
-  float m[4], ls[4];
+  f32x4 o[kCt][8];
+  float m[kCt], ls[kCt];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
+  for (int ct = 0; ct < kCt; ++ct) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[ct] = -__builtin_inff();
     ls[ct] = 0.f;
   }
 
-  // ---- block copies into the ring: wave w writes 1 KiB pieces 4w .. 4w+3 of
+  // ---- block copies into the ring: wave w writes 1 KiB pieces 2w, 2w+1 of
   // the K tile and of the V tile (4 rows each); lane i of a piece lands at
   // byte 16i of it, so it fetches the global 16 bytes that the swizzle puts
   // there
   const char *kbase = reinterpret_cast<const char *>(p.k_pool) + (int64_t)kvh * p.head_stride * 2;
   const char *vbase = reinterpret_cast<const char *>(p.v_pool) + (int64_t)kvh * p.head_stride * 2;
   const int64_t tok_bytes = p.tok_stride * 2, page_bytes = p.page_stride * 2;
-  int64_t k_src[4], v_src[4];  // per-lane byte offsets inside a block
+  int64_t k_src[kCopies / 2], v_src[kCopies / 2];  // per-lane byte offsets inside a block
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int row = 4 * (4 * wave + k) + (lane >> 4), sl = lane & 15;
+  for (int k = 0; k < kCopies / 2; ++k) {
+    const int row = 4 * (2 * wave + k) + (lane >> 4), sl = lane & 15;
     k_src[k] = row * tok_bytes + 16 * (sl ^ (row & 15));
     v_src[k] = row * tok_bytes + 32 * ((sl >> 1) ^ (row & 3)) + 16 * (sl & 1);
   }
@@ -189,11 +194,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
   const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)&ring[0][0];
   auto copy_block = [&](int c, int st) {
     const int64_t off = (int64_t)btc[c] * page_bytes;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring0 + st * kStage + 4096 * wave);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring0 + st * kStage + 2048 * wave);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) copy16(kbase + off + k_src[k], dst + 1024 * k);
+    for (int k = 0; k < kCopies / 2; ++k) copy16(kbase + off + k_src[k], dst + 1024 * k);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) copy16(vbase + off + v_src[k], dst + kTile + 1024 * k);
+    for (int k = 0; k < kCopies / 2; ++k) copy16(vbase + off + v_src[k], dst + kTile + 1024 * k);
   };
   // uniform cursor over the bitmap
   int wi = 0;
@@ -244,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
     if (__builtin_amdgcn_ballot_w64(s_l) != 0) {
       const uint8_t *kt = ring[st];
       const uint8_t *vt = ring[st] + kTile;
-      f32x4 sacc[4][4];  // [head][key tile]
+      f32x4 sacc[kCt][4];  // [head][key tile]
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         u32x4 ka[4];
@@ -252,7 +257,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
         for (int ks = 0; ks < 4; ++ks)
           ka[ks] = *reinterpret_cast<const u32x4 *>(kt + (16 * t + j) * kRow + 16 * ((4 * ks + g) ^ j));
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
+        for (int ct = 0; ct < kCt; ++ct) {
           sacc[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks)
@@ -260,9 +265,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
         }
       }
       const bool causal = c == qb;
-      u32x4 pB[4][2];
+      u32x4 pB[kCt][2];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
+      for (int ct = 0; ct < kCt; ++ct) {
         float z[4][4];
         float mx = -__builtin_inff();
 #pragma unroll
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
           u32x2 lo2 = __builtin_bit_cast(u32x2, a0), hi2 = __builtin_bit_cast(u32x2, a1);
           const bf16x8 a = as_bf16(u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
+          for (int ct = 0; ct < kCt; ++ct)
             o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16(pB[ct][s2]), o[ct][dt], 0, 0, 0);
         }
       }
@@ -329,11 +334,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
 
   // ---- normalise and store: lane holds dims 16dt + 4(l/16) .. +3 of its query
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
+  for (int ct = 0; ct < kCt; ++ct) {
     const float l = rows_sum(ls[ct]);
-    if (qvalid && ct < nh) {
+    if (qvalid && 2 * hp + ct < nh) {
       const float inv = 1.0f / l;
-      uint16_t *dst = p.out + ((int64_t)tq * p.n_q_heads + kvh * G + 4 * hg + ct) * kHeadDim + 4 * g;
+      uint16_t *dst = p.out + ((int64_t)tq * p.n_q_heads + kvh * G + h_lo + ct) * kHeadDim + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const f32x4 v = o[ct][dt] * inv;
