@@ -405,7 +405,7 @@ sas_status sas_gate_backward(const sas_shape *shape, const void *q, const void *
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !sel || !gates || !cnt || !w_q || !w_qnorm || !w_k ||
       !w_knorm || !gate_keys || !d_out || !d_gates || !d_w_q || !d_w_qnorm || !d_w_k || !d_w_knorm || !workspace)
     return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (max_sel <= 0 || max_sel > 256) return fail(SAS_ERR_INVALID_ARG, "max_sel must be in 1..256");
+  if (max_sel <= 0 || max_sel > sas::kMaxSelBackward) return fail(SAS_ERR_INVALID_ARG, "max_sel must be in 1..256");
   if (!(sm_scale > 0.f)) return fail(SAS_ERR_INVALID_ARG, "sm_scale must be positive");
   if (!(rope_theta > 1.0)) return fail(SAS_ERR_INVALID_ARG, "rope_theta must be > 1");
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(d_out) || !aligned16(w_q) ||

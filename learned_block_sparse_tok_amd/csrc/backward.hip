@@ -16,22 +16,24 @@
 // dw_knorm, summed over the batch.
 //
 // Three kernels:
-//   gate_grad_kernel  one 8-wave workgroup per (sequence, KV head): pass 1
-//     recomputes the softmax max / sum of every head over the selection
-//     (S^T = K Q^T on MFMA, as the decode kernel does); pass 2 recomputes S^T
-//     and D^T = V dO^T (V as the A operand, dO as the B operand) per block and
-//     reduces sum P * D.  K is read twice and V once: 48 KiB per selected
-//     block and KV head.
+//   gate_grad_kernel  one 8-wave workgroup per (sequence, KV head), one pass
+//     over the selection: per block S^T = K Q^T (as the decode kernel does)
+//     and D^T = V dO^T (V as the A operand, dO as the B operand) on MFMA,
+//     reduced to per-head sums relative to the block's own score maximum;
+//     the softmax normaliser is applied once the selection's maximum and sum
+//     are known.  K and V are read once: 32 KiB per selected block and KV
+//     head.  The pooled statistics of the historical blocks (the inputs of
+//     the gate-key projection) are taken from the K registers on the way.
 //   gate_chain_kernel one 256-thread workgroup per (sequence, KV head): the
 //     chain from dg to the per-sequence factors (du of every query head with
-//     its RMSNorm weight term; du, pooled statistics and RMSNorm weight term
-//     of every selected historical block), recomputing the gate queries and
-//     the selected blocks' pooled keys in fp32.
+//     its RMSNorm weight term; du and RMSNorm weight term of every selected
+//     historical block), recomputing the gate queries and the selected
+//     blocks' pre-norm gate keys on MFMA.
 //   gate_param_reduce_kernel + gate_dwk_sum_kernel  the weight gradients as
 //     sums over the batch of outer products of those factors, as 64 x 64
-//     output tiles with the factor rows staged in LDS; dW_k's rows are split
-//     into ranges whose partial tiles are then added in order (a fixed order
-//     throughout: deterministic).
+//     output tiles on fp32 MFMA with the factor rows staged in LDS; dW_k's
+//     rows are split into ranges whose partial tiles are then added in order
+//     (a fixed order throughout: deterministic).
 #include "sas_device.h"
 #include "sas_kernels.h"
 
@@ -43,6 +45,30 @@ constexpr float kInvSqrtDg = 0.08838834764831845f;  // 1/sqrt(128)
 
 __device__ __forceinline__ bf16x8 to_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// a lane's value from another lane of its 16-lane row (DPP): kRor4 / kRor8
+// rotate the row by 4 / 8 lanes, kXor2 / kXor1 swap lanes j and j^2 / j^1
+constexpr int kRor4 = 0x124, kRor8 = 0x128, kXor2 = 0x4E, kXor1 = 0xB1;
+template <int kCtrl>
+__device__ __forceinline__ float row_dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
+// One butterfly step over n value pairs (v[c], v[c + n]): a lane keeps the
+// half picked by its bit, takes the same half from its partner lane and
+// combines the two.
+template <int kCtrl, int n>
+__device__ __forceinline__ void keep_half(bool bit, float (&mx)[2 * n], float (&mn)[2 * n], float (&sm)[2 * n]) {
+#pragma unroll
+  for (int c = 0; c < n; ++c) {
+    const float kx = bit ? mx[c + n] : mx[c], sx = bit ? mx[c] : mx[c + n];
+    const float kn = bit ? mn[c + n] : mn[c], sn = bit ? mn[c] : mn[c + n];
+    const float ks = bit ? sm[c + n] : sm[c], ss = bit ? sm[c] : sm[c + n];
+    mx[c] = fmaxf(kx, row_dpp<kCtrl>(sx));
+    mn[c] = fminf(kn, row_dpp<kCtrl>(sn));
+    sm[c] = ks + row_dpp<kCtrl>(ss);
+  }
+}
+
 // the transpose of the rotate-half RoPE rotation at one pair (i, i+64)
 __device__ __forceinline__ void rope_back(float da, float db, float c, float s, float &ga, float &gb) {
   ga = da * c + db * s;
@@ -52,8 +78,17 @@ __device__ __forceinline__ void rope_back(float da, float db, float c, float s, 
 }  // namespace
 
 // ---------------------------------------------------------------- dg per selected block
+// One pass over the selection: per block and head, the block's own score
+// maximum m_ih and a_ih = sum_j 2^(z_hj - m_ih) <dO_h, v_j> (z = score in
+// log2 units) go to LDS, and each wave keeps an online max / sum per head.
+// Once the waves' sums are combined into the selection's M_h and S_h,
+//   dg_i = sum_h a_ih 2^(m_ih - M_h) / S_h.
 __global__ __launch_bounds__(kWavesG * 64, 1) void gate_grad_kernel(BackwardParams p) {
   __shared__ float ml[kWavesG][2][kMaxGroup];
+  __shared__ float fin[2][kMaxGroup];                    // per head: M_h, 1 / S_h
+  __shared__ float bm[kMaxSelBackward][kMaxGroup];       // per block and head: m_ih
+  __shared__ float ba[kMaxSelBackward][kMaxGroup];       // per block and head: a_ih
+  __shared__ int32_t page_l[kMaxSelBackward], nvalid_l[kMaxSelBackward];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, j = lane & 15;
@@ -63,6 +98,13 @@ __global__ __launch_bounds__(kWavesG * 64, 1) void gate_grad_kernel(BackwardPara
   const int G = p.group;
   const int count = p.cnt[unit];
   const int32_t L = p.seq_lens[s];
+  const int32_t *sel = p.sel + (int64_t)unit * p.max_sel;
+  const int32_t *bt = p.block_table + (int64_t)s * p.max_blocks;
+  for (int i = threadIdx.x; i < count; i += kWavesG * 64) {
+    const int blk = sel[i];
+    page_l[i] = bt[blk];
+    nvalid_l[i] = min(kBlock, L - blk * kBlock);
+  }
 
   // B operands: lane l holds q / dO of head l%16, dims 32ks + 8(l/16) .. +7
   bf16x8 qB[4], dB[4];
@@ -74,34 +116,100 @@ __global__ __launch_bounds__(kWavesG * 64, 1) void gate_grad_kernel(BackwardPara
       dB[ks] = to_bf16x8(j < G ? ld16(p.d_out + row + 32 * ks) : u32x4{0, 0, 0, 0});
     }
   }
-  const int32_t *sel = p.sel + (int64_t)unit * p.max_sel;
-  const int32_t *bt = p.block_table + (int64_t)s * p.max_blocks;
   const char *kpool = reinterpret_cast<const char *>(p.k_pool) + (int64_t)kvh * p.head_stride * 2;
   const char *vpool = reinterpret_cast<const char *>(p.v_pool) + (int64_t)kvh * p.head_stride * 2;
   // A-operand lane offset: token 16t + l%16, dims 32ks + 8(l/16)
   const int64_t lane_off = ((int64_t)j * p.tok_stride + 8 * g) * 2;
   const int64_t tile = 16 * p.tok_stride * 2;
+  lds_barrier();
 
-  auto scores = [&](const char *kb, f32x4 (&sacc)[4]) {
+  // each wave keeps the next block's 32 KiB in flight while it works on the
+  // current one: K(next) is issued once S^T has consumed K, V(next) once D^T
+  // has consumed V
+  u32x4 k[4][4], v[4][4];
+  auto load_k = [&](int i) {
+    const char *kb = kpool + (int64_t)page_l[i] * p.page_stride * 2 + lane_off;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      u32x4 k[4];
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) k[ks] = ld16(kb + t * tile + 64 * ks + lane_off);
-      sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < 4; ++ks) k[t][ks] = ld16(kb + t * tile + 64 * ks);
+  };
+  auto load_v = [&](int i) {
+    const char *vb = vpool + (int64_t)page_l[i] * p.page_stride * 2 + lane_off;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(k[ks]), qB[ks], sacc[t], 0, 0, 0);
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) v[t][ks] = ld16(vb + t * tile + 64 * ks);
+  };
+  // The pooled statistics (max, min, mean over the 64 rows of every dim) of
+  // a historical block, taken from the K registers for the key-side chain.
+  // Lane (g, j) holds rows j, 16+j, 32+j, 48+j of dims 32ks + 8g + e; after
+  // the in-lane reduction over its 4 rows, three butterfly steps over the
+  // 16 lanes of its row split e (lane bits 2, 3, 1; the first step may pair
+  // by a rotation since every lane still holds the same dims), and a fourth
+  // splits ks (lane bit 0): lane j ends with ks = 2 b0 + {0, 1},
+  // e = 4 b2 + 2 b3 + b1 reduced over all 64 rows.
+  const bool b0 = j & 1, b1 = j & 2, b2 = j & 4, b3 = j & 8;
+  auto pooled_stats = [&](int i) {
+    float fx[4], fn[4], fs[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float mx[8], mn[8], sm[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] = (e & 1) ? bf16_hi(k[t][ks][e >> 1]) : bf16_lo(k[t][ks][e >> 1]);
+        mx[e] = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mn[e] = fminf(fminf(x[0], x[1]), fminf(x[2], x[3]));
+        sm[e] = (x[0] + x[1]) + (x[2] + x[3]);
+      }
+      keep_half<kRor4, 4>(b2, mx, mn, sm);
+      float mx2[4] = {mx[0], mx[1], mx[2], mx[3]}, mn2[4] = {mn[0], mn[1], mn[2], mn[3]},
+            sm2[4] = {sm[0], sm[1], sm[2], sm[3]};
+      keep_half<kRor8, 2>(b3, mx2, mn2, sm2);
+      float mx3[2] = {mx2[0], mx2[1]}, mn3[2] = {mn2[0], mn2[1]}, sm3[2] = {sm2[0], sm2[1]};
+      keep_half<kXor2, 1>(b1, mx3, mn3, sm3);
+      fx[ks] = mx3[0];
+      fn[ks] = mn3[0];
+      fs[ks] = sm3[0];
+    }
+    keep_half<kXor1, 2>(b0, fx, fn, fs);
+    float *dst = p.ws_pool + ((int64_t)unit * p.max_sel + i) * 3 * kHeadDim;
+    const int e = 4 * b2 + 2 * b3 + b1;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int dim = 32 * (2 * b0 + kk) + 8 * g + e;
+      dst[dim] = fx[kk];
+      dst[kHeadDim + dim] = fn[kk];
+      dst[2 * kHeadDim + dim] = fs[kk] * (1.0f / kBlock);
     }
   };
-
-  // ---- pass 1: max and sum of exp over the whole selection, per head (column)
-  float m = -__builtin_inff(), lsum = 0.f;
+  if (wave < count) {
+    load_k(wave);
+    load_v(wave);
+  }
+  float m = -__builtin_inff(), lsum = 0.f;  // this wave's online max / sum of head (column) j
   for (int i = wave; i < count; i += kWavesG) {
-    const int blk = sel[i];
-    const int64_t off = (int64_t)bt[blk] * p.page_stride * 2;
-    const int nvalid = min(kBlock, L - blk * kBlock);
-    f32x4 sacc[4];
-    scores(kpool + off, sacc);
+    const int nvalid = nvalid_l[i];
+    const bool more = i + kWavesG < count;
+    // S^T = K Q^T and D^T = V dO^T: lane holds rows 16t + 4g + r of column j
+    f32x4 sacc[4], dacc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(k[t][ks]), qB[ks], sacc[t], 0, 0, 0);
+    }
+    if (i < count - 1) pooled_stats(i);
+    if (more) load_k(i + kWavesG);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      dacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) dacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(v[t][ks]), dB[ks], dacc[t], 0, 0, 0);
+    }
+    if (more) load_v(i + kWavesG);
     float z[4][4], mx = -__builtin_inff();
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -111,71 +219,82 @@ __global__ __launch_bounds__(kWavesG * 64, 1) void gate_grad_kernel(BackwardPara
         mx = fmaxf(mx, z[t][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m, mx);
-    float add = 0.f;
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // the block's maximum for head j (row 0 is always valid)
+    float es = 0.f, a = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) add += exp2f(z[t][r] - m_new);
-    lsum = (m == -__builtin_inff() ? 0.f : lsum * exp2f(m - m_new)) + add;
+      for (int r = 0; r < 4; ++r) {
+        const float e = exp2f(z[t][r] - mx);
+        es += e;
+        // rows past the sequence end: e = 0 and their V is not read into the sum
+        a += 16 * t + 4 * g + r < nvalid ? e * dacc[t][r] : 0.f;
+      }
+    es += __shfl_xor(es, 16, 64);
+    es += __shfl_xor(es, 32, 64);
+    a += __shfl_xor(a, 16, 64);
+    a += __shfl_xor(a, 32, 64);
+    if (g == 0) {
+      bm[i][j] = mx;
+      ba[i][j] = a;
+    }
+    const float m_new = fmaxf(m, mx);
+    lsum = (m == -__builtin_inff() ? 0.f : lsum * exp2f(m - m_new)) + es * exp2f(mx - m_new);
     m = m_new;
   }
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
   if (g == 0) {
     ml[wave][0][j] = m;
     ml[wave][1][j] = lsum;
   }
-  __syncthreads();
-  float M = -__builtin_inff(), S = 0.f;
+  lds_barrier();
+  if (threadIdx.x < kMaxGroup) {
+    const int h = threadIdx.x;
+    float M = -__builtin_inff(), S = 0.f;
 #pragma unroll
-  for (int w = 0; w < kWavesG; ++w) M = fmaxf(M, ml[w][0][j]);
+    for (int w = 0; w < kWavesG; ++w) M = fmaxf(M, ml[w][0][h]);
 #pragma unroll
-  for (int w = 0; w < kWavesG; ++w)
-    if (ml[w][0][j] != -__builtin_inff()) S += ml[w][1][j] * exp2f(ml[w][0][j] - M);
-  const float inv_s = j < G && S > 0.f ? 1.0f / S : 0.f;  // columns past the group contribute nothing
-
-  // ---- pass 2: dg_i = sum over the block's tokens and the group's heads of P * <dO, v>
-  for (int i = wave; i < count; i += kWavesG) {
-    const int blk = sel[i];
-    const int64_t off = (int64_t)bt[blk] * p.page_stride * 2;
-    const int nvalid = min(kBlock, L - blk * kBlock);
-    f32x4 sacc[4], dacc[4];
-    scores(kpool + off, sacc);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      u32x4 v[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) v[ks] = ld16(vpool + off + t * tile + 64 * ks + lane_off);
-      dacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) dacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(v[ks]), dB[ks], dacc[t], 0, 0, 0);
-    }
-    float acc = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (16 * t + 4 * g + r < nvalid) acc += exp2f(sacc[t][r] * p.scale_log2 - M) * inv_s * dacc[t][r];
-    acc = wave_sum(acc);
-    if (lane == 0) p.d_gates[(int64_t)unit * p.max_sel + i] = acc;
+    for (int w = 0; w < kWavesG; ++w)
+      if (ml[w][0][h] != -__builtin_inff()) S += ml[w][1][h] * exp2f(ml[w][0][h] - M);
+    fin[0][h] = M;
+    fin[1][h] = h < G && S > 0.f ? 1.0f / S : 0.f;
   }
-  for (int i = count + threadIdx.x; i < p.max_sel; i += kWavesG * 64) p.d_gates[(int64_t)unit * p.max_sel + i] = 0.f;
+  lds_barrier();
+  for (int i = threadIdx.x; i < p.max_sel; i += kWavesG * 64) {
+    float acc = 0.f;
+    if (i < count)
+      for (int h = 0; h < G; ++h) acc += ba[i][h] * exp2f(bm[i][h] - fin[0][h]) * fin[1][h];
+    p.d_gates[(int64_t)unit * p.max_sel + i] = acc;
+  }
 }
 
 // ---------------------------------------------------------------- per-sequence chain
-__global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
-  __shared__ float qv[kMaxGroup][kHeadDim];   // the group's queries (fp32)
-  __shared__ float un[kMaxGroup][kGateDim];   // u / r per head
-  __shared__ float rr[kMaxGroup];             // r per head
-  __shared__ float ghat[kGateDim], dghat[kGateDim];
-  __shared__ float pooled[kChainBlocks][3 * kHeadDim];
-  __shared__ float uk[kChainBlocks][kGateDim];
-  __shared__ float rk[kChainBlocks];
-  __shared__ float dwk_acc[4][kGateDim];  // per wave: the key-side norm-weight term summed over its blocks
+// The element-wise steps work on (row, dim slice) items: thread (row t / 16,
+// o = t % 16) holds dims o + 16k, k = 0..7, i.e. the RoPE pairs
+// (o + 16k, o + 16k + 64) for k = 0..3, and a sum over a row's 128 dims is a
+// DPP sum over its 16 lanes.  Rows are query heads on the query side and
+// selected blocks on the key side.  The two projections run on MFMA:
+// u_h = W_q[h] q_h with q_h as the only non-zero column of the B operand,
+// and U^T = W_k[kvh] P^T for 16 blocks' pooled statistics P at a time.  The
+// max and min rows of P are bf16 values; the mean rows are split into bf16
+// high and low parts (about 16 significant bits).
+constexpr int kPoolPitch = 3 * kHeadDim + 4;  // LDS row of pooled statistics (floats), staggered banks
+constexpr int kUkPitch = kGateDim + 4;
 
-  const int t = threadIdx.x;
+__global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
+  __shared__ float un[kMaxGroup][kGateDim];    // u per head, then u / r
+  __shared__ float part[kMaxGroup][kGateDim];  // per head: rotated weighted query, then the norm-weight term
+  __shared__ float rr[kMaxGroup];              // r per head
+  __shared__ float ghat[kGateDim], dghat[kGateDim];
+  __shared__ float rows16[16][kGateDim];       // dghat partial sums per slot group, then dw_knorm per block row
+  __shared__ __attribute__((aligned(16))) float pooled[kChainBlocks][kPoolPitch];
+  __shared__ float uk[kChainBlocks][kUkPitch];
+  __shared__ int32_t page_l[kMaxSelBackward], blk_l[kMaxSelBackward];  // per slot: page, block index
+  __shared__ float ds_l[kMaxSelBackward];                               // per slot: dL/dscore = dg g (1 - g)
+  __shared__ float wqn_l[kGateDim], wkn_l[kGateDim];
+  __shared__ double invf_l[kGateDim / 2];
+
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int row = t >> 4, o = t & 15;
   const int unit = blockIdx.x;
   const int s = unit / p.n_kv_heads;
   const int kvh = unit - s * p.n_kv_heads;
@@ -188,293 +307,428 @@ __global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
   const float *dg = p.d_gates + (int64_t)unit * p.max_sel;
   const int32_t *bt = p.block_table + (int64_t)s * p.max_blocks;
 
-  // ---- gate queries of the group: u_h = W_q[h] q_h, r_h, u_h / r_h, then the mean rotated query
-  for (int e = t; e < G * kHeadDim; e += 256)
-    qv[e >> 7][e & 127] = bf16_to_f32(p.q[((int64_t)s * p.n_q_heads + kvh * G) * kHeadDim + e]);
-  __syncthreads();
-  for (int e = t; e < G * kGateDim; e += 256) {
-    const int h = e >> 7, jj = e & 127;
-    const uint16_t *wrow = p.w_q + ((int64_t)(kvh * G + h) * kGateDim + jj) * kHeadDim;
-    float acc = 0.f;
-    for (int d = 0; d < kHeadDim; d += 8) {
-      const u32x4 w = ld16(wrow + d);
-      acc = fmaf(qv[h][d + 0], bf16_lo(w.x), acc);
-      acc = fmaf(qv[h][d + 1], bf16_hi(w.x), acc);
-      acc = fmaf(qv[h][d + 2], bf16_lo(w.y), acc);
-      acc = fmaf(qv[h][d + 3], bf16_hi(w.y), acc);
-      acc = fmaf(qv[h][d + 4], bf16_lo(w.z), acc);
-      acc = fmaf(qv[h][d + 5], bf16_hi(w.z), acc);
-      acc = fmaf(qv[h][d + 6], bf16_lo(w.w), acc);
-      acc = fmaf(qv[h][d + 7], bf16_hi(w.w), acc);
-    }
-    un[h][jj] = acc;
-  }
-  __syncthreads();
-  if (t < 64) {  // wave 0: per head RMS, normalise, rotate, mean over the group
-    float cq, sq;
-    rope_cos_sin((double)(L - 1), p.inv_freq[t], cq, sq);
-    float sa = 0.f, sb = 0.f;
-    for (int h = 0; h < G; ++h) {
-      const float a = un[h][t], b = un[h][t + 64];
-      const float r = sqrtf(wave_sum(a * a + b * b) * (1.0f / kGateDim) + 1e-6f);
-      const float na = a / r, nb = b / r;
-      un[h][t] = na;
-      un[h][t + 64] = nb;
-      if (t == 0) rr[h] = r;
-      const float wa = na * p.w_qnorm[t], wb = nb * p.w_qnorm[t + 64];
-      sa += wa * cq - wb * sq;
-      sb += wb * cq + wa * sq;
-    }
-    ghat[t] = sa / (float)G;
-    ghat[t + 64] = sb / (float)G;
-  }
-  __syncthreads();
+  // W_q[h] A operands (row 16mt + l%16, inputs 32ks + 8(l/16) .. +7) and q_h
+  // as column 0 of the B operand
+  auto load_wq = [&](int h, u32x4 (&a)[8][4], bf16x8 (&qb)[4]) {
+    const uint16_t *wq = p.w_q + ((int64_t)(kvh * G + h) * kGateDim + (lane & 15)) * kHeadDim + 8 * (lane >> 4);
+    const uint16_t *qh = p.q + ((int64_t)s * p.n_q_heads + kvh * G + h) * kHeadDim + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[ks] = to_bf16x8((lane & 15) == 0 ? ld16(qh + 32 * ks) : u32x4{0, 0, 0, 0});
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) a[mt][ks] = ld16(wq + (int64_t)16 * mt * kHeadDim + 32 * ks);
+  };
 
-  // ---- dghat = sum_i dS_i gk_i / sqrt(128) over the historical selection
+  // the historical slots' pages, block indices and score gradients (one slot
+  // per thread: at most 255 historical slots), the norm weights and the RoPE
+  // frequencies, gathered into LDS.  Every load is issued unconditionally
+  // (from clamped, valid addresses: slot 0 always holds a block), and the
+  // first head's W_q loads go out between the dependent gathers and their
+  // LDS stores, so that all their latencies overlap.
+  const bool has_slot = t < n_hist;
+  const int ti = has_slot ? t : 0;
+  const int slot_blk = sel[ti];
+  const float slot_g = gts[ti], slot_dg = dg[ti];
+  const float wqn = p.w_qnorm[t & (kGateDim - 1)], wkn = p.w_knorm[t & (kGateDim - 1)];
+  const double invf = p.inv_freq[t & (kGateDim / 2 - 1)];
+  const int slot_page = bt[slot_blk];
+  u32x4 a[8][4];
+  bf16x8 qb[4];
+  load_wq(min(wave, G - 1), a, qb);
+  if (has_slot) {
+    blk_l[t] = slot_blk;
+    page_l[t] = slot_page;
+    ds_l[t] = slot_dg * slot_g * (1.f - slot_g);
+  }
   if (t < kGateDim) {
-    float acc = 0.f;
-    for (int i = 0; i < n_hist; ++i) {
-      const float gi = gts[i];
-      const float dS = dg[i] * gi * (1.f - gi);
-      const int64_t page = bt[sel[i]];
-      acc = fmaf(dS, bf16_to_f32(p.gate_keys[(page * p.n_kv_heads + kvh) * kGateDim + t]), acc);
-    }
-    dghat[t] = acc * kInvSqrtDg;
+    wqn_l[t] = wqn;
+    wkn_l[t] = wkn;
   }
-  __syncthreads();
+  if (t < kGateDim / 2) invf_l[t] = invf;
 
-  // ---- query side: per head d(u/r * w) = RoPE^T(dghat / G), RMSNorm
-  // backward; the norm-weight term summed over the group's heads
-  if (t < 64) {
-    float cq, sq;
-    rope_cos_sin((double)(L - 1), p.inv_freq[t], cq, sq);
-    float dna, dnb;
-    rope_back(dghat[t] / (float)G, dghat[t + 64] / (float)G, cq, sq, dna, dnb);
-    float wsa = 0.f, wsb = 0.f;
-    for (int h = 0; h < G; ++h) {
-      const float na = un[h][t], nb = un[h][t + 64];
-      const float aa = dna * p.w_qnorm[t], ab = dnb * p.w_qnorm[t + 64];
-      const float mean = wave_sum(aa * na + ab * nb) * (1.0f / kGateDim);
-      const float r = rr[h];
-      float *du = p.ws_du_q + ((int64_t)s * p.n_q_heads + kvh * G + h) * kGateDim;
-      du[t] = (aa - na * mean) / r;
-      du[t + 64] = (ab - nb * mean) / r;
-      wsa += dna * na;
-      wsb += dnb * nb;
+  // ---- u_h = W_q[h] q_h, one head per wave at a time
+  for (int h = wave; h < G; h += 4) {
+    if (h != wave) load_wq(h, a, qb);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(a[mt][ks]), qb[ks], acc, 0, 0, 0);
+      if ((lane & 15) == 0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) un[h][16 * mt + 4 * (lane >> 4) + r] = acc[r];
     }
-    p.ws_dwqn[(int64_t)unit * kGateDim + t] = wsa;
-    p.ws_dwqn[(int64_t)unit * kGateDim + t + 64] = wsb;
+  }
+  // W_k A operands of this wave's 32 rows (row 32w + 16mt + l%16, inputs
+  // 32ks + 8(l/16) .. +7), kept in registers for every chunk
+  u32x4 wk[2][12];
+  {
+    const uint16_t *wkb =
+        p.w_k + ((int64_t)kvh * kGateDim + 32 * wave + (lane & 15)) * 3 * kHeadDim + 8 * (lane >> 4);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 12; ++ks) wk[mt][ks] = ld16(wkb + (int64_t)16 * mt * 3 * kHeadDim + 32 * ks);
+  }
+  lds_barrier();
+
+  // ---- per head: RMS, normalise, weight, rotate; the mean over the group in head order
+  float cq[4], sq[4];  // RoPE at the query's position for pairs o + 16k
+#pragma unroll
+  for (int k = 0; k < 4; ++k) rope_cos_sin((double)(L - 1), invf_l[o + 16 * k], cq[k], sq[k]);
+  for (int h = row; h < G; h += 16) {
+    float x[8], ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      x[k] = un[h][o + 16 * k];
+      ss += x[k] * x[k];
+    }
+    const float r = sqrtf(row16_sum(ss) * (1.0f / kGateDim) + 1e-6f);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      x[k] = x[k] / r;
+      un[h][o + 16 * k] = x[k];
+    }
+    if (o == 0) rr[h] = r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int d = o + 16 * k;
+      const float wa = x[k] * wqn_l[d], wb = x[k + 4] * wqn_l[d + 64];
+      part[h][d] = wa * cq[k] - wb * sq[k];
+      part[h][d + 64] = wb * cq[k] + wa * sq[k];
+    }
+  }
+  lds_barrier();
+  if (t < kGateDim) {
+    float a = 0.f;
+    for (int h = 0; h < G; ++h) a += part[h][t];
+    ghat[t] = a / (float)G;
+  }
+
+  // ---- dghat = sum_i dS_i gk_i / sqrt(128) over the historical selection:
+  // thread (slot group row, dims 8o .. 8o+7), then the 16 groups in order
+  {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    const uint16_t *gk = p.gate_keys + (int64_t)kvh * kGateDim + 8 * o;
+    const int64_t gk_page = (int64_t)p.n_kv_heads * kGateDim;
+#pragma unroll 2
+    for (int i = row; i < n_hist; i += 16) {
+      const u32x4 w = ld16(gk + page_l[i] * gk_page);
+      const float d = ds_l[i];
+      acc[0] = fmaf(d, bf16_lo(w.x), acc[0]);
+      acc[1] = fmaf(d, bf16_hi(w.x), acc[1]);
+      acc[2] = fmaf(d, bf16_lo(w.y), acc[2]);
+      acc[3] = fmaf(d, bf16_hi(w.y), acc[3]);
+      acc[4] = fmaf(d, bf16_lo(w.z), acc[4]);
+      acc[5] = fmaf(d, bf16_hi(w.z), acc[5]);
+      acc[6] = fmaf(d, bf16_lo(w.w), acc[6]);
+      acc[7] = fmaf(d, bf16_hi(w.w), acc[7]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rows16[row][8 * o + e] = acc[e];
+  }
+  lds_barrier();
+  if (t < kGateDim) {
+    float a = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) a += rows16[g][t];
+    dghat[t] = a * kInvSqrtDg;
+  }
+  lds_barrier();
+
+  // ---- query side: per head d(n w) = RoPE^T(dghat / G), RMSNorm backward;
+  // the norm-weight term dn * n summed over the heads in order
+  for (int h = row; h < G; h += 16) {
+    float dn[8], n[8], dot = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int d = o + 16 * k;
+      rope_back(dghat[d] / (float)G, dghat[d + 64] / (float)G, cq[k], sq[k], dn[k], dn[k + 4]);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      n[k] = un[h][o + 16 * k];
+      dot += dn[k] * wqn_l[o + 16 * k] * n[k];
+    }
+    const float mean = row16_sum(dot) * (1.0f / kGateDim);
+    const float r = rr[h];
+    float *du = p.ws_du_q + ((int64_t)s * p.n_q_heads + kvh * G + h) * kGateDim;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int d = o + 16 * k;
+      du[d] = (dn[k] * wqn_l[d] - n[k] * mean) / r;
+      part[h][d] = dn[k] * n[k];
+    }
+  }
+  lds_barrier();
+  if (t < kGateDim) {
+    float a = 0.f;
+    for (int h = 0; h < G; ++h) a += part[h][t];
+    p.ws_dwqn[(int64_t)unit * kGateDim + t] = a;
   }
 
   // ---- key side, kChainBlocks selected historical blocks at a time
   const int64_t slot0 = (int64_t)unit * p.max_sel;
-  float dwk_a = 0.f, dwk_b = 0.f;  // this lane's pair, summed over the wave's blocks
+  float dwk[8];  // dm * n of this thread's dims, summed over its block rows
+#pragma unroll
+  for (int k = 0; k < 8; ++k) dwk[k] = 0.f;
   for (int i0 = 0; i0 < p.max_sel; i0 += kChainBlocks) {
     const int nb_ = max(0, min(kChainBlocks, n_hist - i0));
-    __syncthreads();
-    // pooled statistics: thread (block b, dim d) scans the block's 64 rows
-    for (int e = t; e < nb_ * kHeadDim; e += 256) {
-      const int b = e >> 7, d = e & 127;
-      const int64_t page = bt[sel[i0 + b]];
-      const uint16_t *kb = p.k_pool + page * p.page_stride + (int64_t)kvh * p.head_stride + d;
-      float mx = -__builtin_inff(), mn = __builtin_inff(), sum = 0.f;
-#pragma unroll 16
-      for (int r = 0; r < kBlock; ++r) {
-        const float x = bf16_to_f32(kb[(int64_t)r * p.tok_stride]);
-        mx = fmaxf(mx, x);
-        mn = fminf(mn, x);
-        sum += x;
-      }
-      pooled[b][d] = mx;
-      pooled[b][kHeadDim + d] = mn;
-      pooled[b][2 * kHeadDim + d] = sum * (1.0f / kBlock);
-    }
-    __syncthreads();
-    // u = W_k[kvh] . pooled: thread (row jj, half) covers half of the chunk's blocks
+    lds_barrier();
+    // the chunk's pooled statistics, written by gate_grad_kernel: 96 float4
+    // per block, thread t takes float4 t + 256k
     {
-      const int jj = t & 127, half = t >> 7;
-      const uint16_t *wrow = p.w_k + ((int64_t)kvh * kGateDim + jj) * 3 * kHeadDim;
-      float acc[kChainBlocks / 2];
+      constexpr int kQuads = kChainBlocks * 3 * kHeadDim / 4 / 256;
+      const f32x4 *src = reinterpret_cast<const f32x4 *>(p.ws_pool + (slot0 + i0) * 3 * kHeadDim);
+      f32x4 v[kQuads];
 #pragma unroll
-      for (int b = 0; b < kChainBlocks / 2; ++b) acc[b] = 0.f;
-      for (int in = 0; in < 3 * kHeadDim; in += 8) {
-        const u32x4 w = ld16(wrow + in);
-        const float wv[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
-                             bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+      for (int k = 0; k < kQuads; ++k) {
+        const int e4 = t + 256 * k;
+        if (e4 < nb_ * 3 * kHeadDim / 4) v[k] = src[e4];
+      }
 #pragma unroll
-        for (int b = 0; b < kChainBlocks / 2; ++b) {
-          const float *pb = pooled[half * (kChainBlocks / 2) + b] + in;
+      for (int k = 0; k < kQuads; ++k) {
+        const int e4 = t + 256 * k, b = e4 / (3 * kHeadDim / 4), c4 = e4 - b * (3 * kHeadDim / 4);
+        if (e4 < nb_ * 3 * kHeadDim / 4) *reinterpret_cast<f32x4 *>(&pooled[b][4 * c4]) = v[k];
+      }
+    }
+    lds_barrier();
+    // U^T = W_k P^T: lane l holds block l%16, rows 32w + 16mt + 4(l/16) + r
+    // (columns of blocks not in the chunk hold stale values and are not read)
+    {
+      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      const float *pb = &pooled[lane & 15][8 * (lane >> 4)];
+      // inputs 0..255 (max, min) are bf16 values: one MFMA; inputs 256..383
+      // (mean): high part and low part
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[b] = fmaf(wv[e], pb[e], acc[b]);
+      for (int ks = 0; ks < 12; ++ks) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = pb[32 * ks + e];
+        const u32x4 h = {pack_bf16_rne(x[0], x[1]), pack_bf16_rne(x[2], x[3]), pack_bf16_rne(x[4], x[5]),
+                         pack_bf16_rne(x[6], x[7])};
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(wk[mt][ks]), to_bf16x8(h), acc[mt], 0, 0, 0);
+        if (ks >= 8) {
+          float lo[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) lo[e] = x[e] - ((e & 1) ? bf16_hi(h[e >> 1]) : bf16_lo(h[e >> 1]));
+          const u32x4 l = {pack_bf16_rne(lo[0], lo[1]), pack_bf16_rne(lo[2], lo[3]), pack_bf16_rne(lo[4], lo[5]),
+                           pack_bf16_rne(lo[6], lo[7])};
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(wk[mt][ks]), to_bf16x8(l), acc[mt], 0, 0, 0);
         }
       }
 #pragma unroll
-      for (int b = 0; b < kChainBlocks / 2; ++b) uk[half * (kChainBlocks / 2) + b][jj] = acc[b];
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) uk[lane & 15][32 * wave + 16 * mt + 4 * (lane >> 4) + r] = acc[mt][r];
     }
-    __syncthreads();
-    // per block (wave w: blocks w, w+4, ...): RMS, RoPE^T of dS * ghat / sqrt(128), RMSNorm backward
+    lds_barrier();
+    // per block row: RMS, RoPE^T of dS ghat / sqrt(128), RMSNorm backward
     {
-      const int wave = t >> 6, lane = t & 63;
-      for (int b = wave; b < kChainBlocks; b += 4) {
-        const int i = i0 + b;
-        float *du = p.ws_du_k + (slot0 + min(i, p.max_sel - 1)) * kGateDim;
-        float *pk = p.ws_pool + (slot0 + min(i, p.max_sel - 1)) * 3 * kHeadDim;
-        if (i >= p.max_sel) break;
-        if (b >= nb_) {  // local block or padding: no gradient
-          du[lane] = du[lane + 64] = 0.f;
-          for (int e = lane; e < 3 * kHeadDim; e += 64) pk[e] = 0.f;
-          continue;
+      const int b = row, i = i0 + b;
+      if (i < p.max_sel) {
+        float *du = p.ws_du_k + (slot0 + i) * kGateDim;
+        if (b >= nb_) {  // local block or padding: no gradient, and zero pooled rows for the sums
+          float *pk = p.ws_pool + (slot0 + i) * 3 * kHeadDim;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) du[o + 16 * k] = 0.f;
+#pragma unroll
+          for (int k = 0; k < 24; ++k) pk[o + 16 * k] = 0.f;
+        } else {
+          float x[8], ss = 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            x[k] = uk[b][o + 16 * k];
+            ss += x[k] * x[k];
+          }
+          const float r = sqrtf(row16_sum(ss) * (1.0f / kGateDim) + 1e-6f);
+          const float dS = ds_l[i] * kInvSqrtDg;
+          const double pos = (double)blk_l[i] * kBlock;
+          float dm[8], dot = 0.f;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int d = o + 16 * k;
+            float ck, sk;
+            rope_cos_sin(pos, invf_l[d], ck, sk);
+            rope_back(dS * ghat[d], dS * ghat[d + 64], ck, sk, dm[k], dm[k + 4]);
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            x[k] = x[k] / r;
+            dot += dm[k] * wkn_l[o + 16 * k] * x[k];
+          }
+          const float mean = row16_sum(dot) * (1.0f / kGateDim);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int d = o + 16 * k;
+            du[d] = (dm[k] * wkn_l[d] - x[k] * mean) / r;
+            dwk[k] += dm[k] * x[k];
+          }
         }
-        const int c = sel[i];
-        const float a = uk[b][lane], bb = uk[b][lane + 64];
-        const float r = sqrtf(wave_sum(a * a + bb * bb) * (1.0f / kGateDim) + 1e-6f);
-        const float na = a / r, nb = bb / r;
-        const float gi = gts[i];
-        const float dS = dg[i] * gi * (1.f - gi) * kInvSqrtDg;
-        float ck, sk;
-        rope_cos_sin((double)c * kBlock, p.inv_freq[lane], ck, sk);
-        float dma, dmb;
-        rope_back(dS * ghat[lane], dS * ghat[lane + 64], ck, sk, dma, dmb);
-        const float aa = dma * p.w_knorm[lane], ab = dmb * p.w_knorm[lane + 64];
-        const float mean = wave_sum(aa * na + ab * nb) * (1.0f / kGateDim);
-        du[lane] = (aa - na * mean) / r;
-        du[lane + 64] = (ab - nb * mean) / r;
-        dwk_a += dma * na;
-        dwk_b += dmb * nb;
-        for (int e = lane; e < 3 * kHeadDim; e += 64) pk[e] = pooled[b][e];
       }
     }
   }
-  {
-    const int wave = t >> 6, lane = t & 63;
-    dwk_acc[wave][lane] = dwk_a;
-    dwk_acc[wave][lane + 64] = dwk_b;
+  lds_barrier();
+#pragma unroll
+  for (int k = 0; k < 8; ++k) rows16[row][o + 16 * k] = dwk[k];
+  lds_barrier();
+  if (t < kGateDim) {
+    float a = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) a += rows16[g][t];
+    p.ws_dwkn[(int64_t)unit * kGateDim + t] = a;
   }
-  __syncthreads();
-  if (t < kGateDim)
-    p.ws_dwkn[(int64_t)unit * kGateDim + t] = dwk_acc[0][t] + dwk_acc[1][t] + dwk_acc[2][t] + dwk_acc[3][t];
 }
 
 // ---------------------------------------------------------------- sums over the batch
-// out[j][i] = sum_n a[n][j] * b[n][i] for one 64 x 64 tile: the a and b rows
-// are staged in LDS 32 at a time; thread (ty, tx) owns a 4 x 4 block of the
-// tile and sums the rows in order (deterministic).  b is fp32 or bf16.
-template <typename TB>
-__device__ __forceinline__ float load_b(const TB *b, int64_t i);
-template <>
-__device__ __forceinline__ float load_b<float>(const float *b, int64_t i) { return b[i]; }
-template <>
-__device__ __forceinline__ float load_b<uint16_t>(const uint16_t *b, int64_t i) { return bf16_to_f32(b[i]); }
-
-template <typename TB>
-__device__ void outer_sum_tile(const float *a, int64_t a_row, const TB *b, int64_t b_row, int n, int j0, int i0,
-                               int i_lim, float *out, int64_t out_row, float (&as)[32][64], float (&bs)[32][64]) {
-  const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
-  float acc[4][4] = {};
-  for (int n0 = 0; n0 < n; n0 += 32) {
-    __syncthreads();
-    for (int e = t; e < 32 * 64; e += 256) {
-      const int r = e >> 6, c = e & 63;
-      const bool live = n0 + r < n;
-      as[r][c] = live ? a[(int64_t)(n0 + r) * a_row + j0 + c] : 0.f;
-      bs[r][c] = live && i0 + c < i_lim ? load_b(b, (int64_t)(n0 + r) * b_row + i0 + c) : 0.f;
+// acc = sum over rows n in [n_lo, n_hi) of A(n, 64-wide column slice) (x)
+// B(n, 64-wide column slice) for one 64 x 64 tile, on fp32 MFMA (16x16x4):
+// rows are staged in LDS 32 at a time, the next 32 fetched into registers
+// while the current ones are summed.  Wave w owns the 32 x 32 quadrant
+// (rows 32(w/2), columns 32(w%2)) as 2 x 2 MFMA tiles; per 4-row step lane l
+// feeds A(row 4kk + l/16, column l%16) and B(row 4kk + l/16, column l%16).
+// The rows are taken in order (deterministic).
+template <typename FA, typename FB>
+__device__ void outer_sum_tile(FA fa, FB fb, int n_lo, int n_hi, f32x4 (&acc)[2][2], float (&as)[32][64],
+                               float (&bs)[32][64]) {
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int wm = wave >> 1, wn = wave & 1, kr = lane >> 4, c16 = lane & 15;
+  float ra[8], rb[8];
+  auto fetch = [&](int n0) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int e = t + 256 * k, n = n0 + (e >> 6);
+      ra[k] = n < n_hi ? fa(n, e & 63) : 0.f;
+      rb[k] = n < n_hi ? fb(n, e & 63) : 0.f;
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int r = 0; r < 32; ++r) {
-      float av[4], bv[4];
+  };
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        av[u] = as[r][4 * ty + u];
-        bv[u] = bs[r][4 * tx + u];
-      }
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (n_lo < n_hi) fetch(n_lo);
+  for (int n0 = n_lo; n0 < n_hi; n0 += 32) {
+    lds_barrier();
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
+    for (int k = 0; k < 8; ++k) {
+      const int e = t + 256 * k;
+      as[e >> 6][e & 63] = ra[k];
+      bs[e >> 6][e & 63] = rb[k];
+    }
+    lds_barrier();
+    if (n0 + 32 < n_hi) fetch(n0 + 32);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const float a0 = as[4 * kk + kr][32 * wm + c16], a1 = as[4 * kk + kr][32 * wm + 16 + c16];
+      const float b0 = bs[4 * kk + kr][32 * wn + c16], b1 = bs[4 * kk + kr][32 * wn + 16 + c16];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
     }
   }
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-      if (i0 + 4 * tx + v < i_lim) out[(int64_t)(j0 + 4 * ty + u) * out_row + i0 + 4 * tx + v] = acc[u][v];
 }
 
-// blocks [0, Hq*4): dW_q[h] tiles (2 x 2 per head), sum over the batch of
+// writes a tile from outer_sum_tile: lane l of wave w holds rows
+// 32(w/2) + 16i + 4(l/16) + r, column 32(w%2) + 16j + l%16
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[2][2], float *dst, int64_t row_stride) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        dst[(int64_t)(32 * wm + 16 * i + 4 * (lane >> 4) + r) * row_stride + 32 * wn + 16 * j + (lane & 15)] =
+            acc[i][j][r];
+}
+
+// blocks [0, Hq*4): dW_q[h] tiles (2 x 2 per head), sums over the batch of
 // du_q (x) q; then Hkv*12*kSplitK blocks: partial dW_k[kvh] tiles (2 x 6 per
 // head, the (sequence, slot) rows split into kSplitK ranges), sums of
-// du_k (x) pooled; the last block: the norm-weight gradients as sums over the
-// (sequence, KV head) rows.
+// du_k (x) pooled; the last two blocks: the query- and key-side norm-weight
+// gradients as sums over the (sequence, KV head) rows.
 __global__ __launch_bounds__(256) void gate_param_reduce_kernel(BackwardParams p) {
-  __shared__ float as[32][64], bs[32][64];
+  __shared__ __attribute__((aligned(16))) float as[32][64];
+  __shared__ float bs[32][64];
   const int tiles_q = p.n_q_heads * 4, tiles_k = p.n_kv_heads * 12;  // dW_k: 12 tiles of 64 x 64 per KV head
   const int bid = blockIdx.x;
+  const int tid = threadIdx.x;
+  f32x4 acc[2][2];
   if (bid < tiles_q) {
     const int h = bid >> 2, jt = (bid >> 1) & 1, it = bid & 1;
-    outer_sum_tile<uint16_t>(p.ws_du_q + (int64_t)h * kGateDim, (int64_t)p.n_q_heads * kGateDim,
-                             p.q + (int64_t)h * kHeadDim, (int64_t)p.n_q_heads * kHeadDim, p.batch, 64 * jt, 64 * it,
-                             kHeadDim, p.d_w_q + (int64_t)h * kGateDim * kHeadDim, kHeadDim, as, bs);
+    const int64_t rs = (int64_t)p.n_q_heads * kHeadDim;  // row stride of du_q and q over the batch
+    const float *a = p.ws_du_q + (int64_t)h * kGateDim + 64 * jt;
+    const uint16_t *b = p.q + (int64_t)h * kHeadDim + 64 * it;
+    outer_sum_tile([&](int n, int c) { return a[n * rs + c]; }, [&](int n, int c) { return bf16_to_f32(b[n * rs + c]); },
+                   0, p.batch, acc, as, bs);
+    store_tile(acc, p.d_w_q + ((int64_t)h * kGateDim + 64 * jt) * kHeadDim + 64 * it, kHeadDim);
   } else if (bid < tiles_q + tiles_k * kSplitK) {
-    // one of kSplitK consecutive row ranges of one dW_k tile -> a partial tile
-    const int k = (bid - tiles_q) / kSplitK, part = (bid - tiles_q) % kSplitK;
-    const int kvh = k / 12, jt = (k % 12) / 6, it = k % 6;
-    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-    float acc[4][4] = {};
+    // one of kSplitK consecutive row ranges of one dW_k tile -> a partial
+    // tile.  The KV head is the fastest-varying index, so that with
+    // workgroups dealt round-robin to the 8 XCDs all blocks of one KV head
+    // share an L2 (the one that also ran its units' chain, for 8 KV heads).
+    const int kb = bid - tiles_q, kvh = kb % p.n_kv_heads, rest = kb / p.n_kv_heads;
+    const int tile = rest / kSplitK, part = rest % kSplitK;
+    const int k = kvh * 12 + tile, jt = tile / 6, it = tile % 6;
     const int n = p.batch * p.max_sel;
     const int per = (n + kSplitK - 1) / kSplitK;
-    const int n_lo = part * per, n_hi = min(n, n_lo + per);
-    for (int n0 = n_lo; n0 < n_hi; n0 += 32) {
-      __syncthreads();
-      for (int e = tid; e < 32 * 64; e += 256) {
-        const int r = e >> 6, c = e & 63;
-        const int nn = n0 + r;
-        const bool live = nn < n_hi;
-        const int64_t slot = live ? ((int64_t)(nn / p.max_sel) * p.n_kv_heads + kvh) * p.max_sel + nn % p.max_sel : 0;
-        as[r][c] = live ? p.ws_du_k[slot * kGateDim + 64 * jt + c] : 0.f;
-        bs[r][c] = live ? p.ws_pool[slot * 3 * kHeadDim + 64 * it + c] : 0.f;
-      }
-      __syncthreads();
-#pragma unroll 8
-      for (int r = 0; r < 32; ++r) {
-        float av[4], bv[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          av[u] = as[r][4 * ty + u];
-          bv[u] = bs[r][4 * tx + u];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
-      }
-    }
-    float *dst = p.ws_part + ((int64_t)k * kSplitK + part) * 64 * 64;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) dst[(4 * ty + u) * 64 + 4 * tx + v] = acc[u][v];
-  } else if (threadIdx.x < kGateDim) {
-    const int t = threadIdx.x;
+    const int n_lo = min(n, part * per), n_hi = min(n, n_lo + per);
+    auto slot = [&](int nn) { return ((int64_t)(nn / p.max_sel) * p.n_kv_heads + kvh) * p.max_sel + nn % p.max_sel; };
+    outer_sum_tile([&](int nn, int c) { return p.ws_du_k[slot(nn) * kGateDim + 64 * jt + c]; },
+                   [&](int nn, int c) { return p.ws_pool[slot(nn) * 3 * kHeadDim + 64 * it + c]; }, n_lo, n_hi, acc,
+                   as, bs);
+    store_tile(acc, p.ws_part + ((int64_t)k * kSplitK + part) * 64 * 64, 64);
+  } else {
+    // thread (dims 4q .. 4q+3, slice sl) sums rows u = sl, sl + 8, ...; the
+    // eight slices are then added in order
+    const bool key = bid > tiles_q + tiles_k * kSplitK;
+    const float *src = key ? p.ws_dwkn : p.ws_dwqn;
+    const int q = tid & 31, sl = tid >> 5;
     const int units = p.batch * p.n_kv_heads;
-    float aq = 0.f, ak = 0.f;
-    for (int u = 0; u < units; ++u) {
-      aq += p.ws_dwqn[(int64_t)u * kGateDim + t];
-      ak += p.ws_dwkn[(int64_t)u * kGateDim + t];
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 16
+    for (int u = sl; u < units; u += 8) sum += *reinterpret_cast<const f32x4 *>(src + (int64_t)u * kGateDim + 4 * q);
+    float *slices = &as[0][0];  // [8][kGateDim] within the tile buffer
+    *reinterpret_cast<f32x4 *>(slices + sl * kGateDim + 4 * q) = sum;
+    lds_barrier();
+    if (tid < kGateDim) {
+      float a = 0.f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) a += slices[g * kGateDim + tid];
+      (key ? p.d_w_knorm : p.d_w_qnorm)[tid] = a;
     }
-    p.d_w_qnorm[t] = aq;
-    p.d_w_knorm[t] = ak;
   }
 }
 
-// dW_k from its partial tiles, summed in order of the row ranges
+// dW_k from its partial tiles, summed in order of the row ranges: thread t
+// owns elements 4(t + 256q) .. +3 of the tile
 __global__ __launch_bounds__(256) void gate_dwk_sum_kernel(BackwardParams p) {
-  const int k = blockIdx.x;  // tile
-  const int kvh = k / 12, jt = (k % 12) / 6, it = k % 6;
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    float acc = 0.f;
-    for (int part = 0; part < kSplitK; ++part) acc += p.ws_part[((int64_t)k * kSplitK + part) * 64 * 64 + e];
-    p.d_w_k[((int64_t)kvh * kGateDim + 64 * jt + (e >> 6)) * 3 * kHeadDim + 64 * it + (e & 63)] = acc;
+  const int kvh = blockIdx.x % p.n_kv_heads, tile = blockIdx.x / p.n_kv_heads;  // KV head fastest, as above
+  const int k = kvh * 12 + tile, jt = tile / 6, it = tile % 6;
+  const float *src = p.ws_part + (int64_t)k * kSplitK * 64 * 64;
+  f32x4 acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int part = 0; part < kSplitK; ++part)
+      acc[q] += *reinterpret_cast<const f32x4 *>(src + part * 64 * 64 + 4 * (threadIdx.x + 256 * q));
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * (threadIdx.x + 256 * q);
+    float *dst = p.d_w_k + ((int64_t)kvh * kGateDim + 64 * jt + (e >> 6)) * 3 * kHeadDim + 64 * it + (e & 63);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) dst[v] = acc[q][v];
   }
 }
 
@@ -486,7 +740,7 @@ hipError_t launch_gate_backward(const BackwardParams &p, hipStream_t st) {
   hipLaunchKernelGGL(gate_chain_kernel, dim3(units), dim3(256), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned tiles = (unsigned)(p.n_q_heads * 4 + p.n_kv_heads * 12 * kSplitK + 1);
+  const unsigned tiles = (unsigned)(p.n_q_heads * 4 + p.n_kv_heads * 12 * kSplitK + 2);
   hipLaunchKernelGGL(gate_param_reduce_kernel, dim3(tiles), dim3(256), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -33,12 +33,6 @@ constexpr int kGhatPitch = kGateDim + 4;  // LDS row of the mean gate query (flo
 
 __device__ __forceinline__ bf16x8 b8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, b16x2));
-}
-
 }  // namespace
 
 __global__ __launch_bounds__(256, 1) void prefill_select_kernel(PrefillSelectParams p) {

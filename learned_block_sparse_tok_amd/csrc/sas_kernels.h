@@ -85,6 +85,7 @@ struct PrefillParams {
 
 constexpr int kChainBlocks = 16;  // selected blocks the backward chain handles at a time
 constexpr int kSplitK = 8;        // row ranges of each dW_k tile summed separately, then in order
+constexpr int kMaxSelBackward = 256;  // selection slots per (sequence, KV head) the backward accepts
 
 struct BackwardParams {
   const uint16_t *q, *k_pool, *v_pool, *d_out, *gate_keys, *w_q, *w_k;
