@@ -51,23 +51,6 @@ constexpr int kCopies = kStage / 1024 / 8;  // 1 KiB copy instructions per wave 
 constexpr int kCt = 2;                      // query heads per wave
 constexpr int kMaxSel = 64;               // selections per query staged in LDS (budgets up to 4,096)
 
-// One global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
-// i's bytes land at LDS byte lds + 16 i.  Written out (rather than through the
-// builtin) so that the compiler, which does not track these LDS writes,
-// inserts no vmcnt(0) before every later LDS read; the instruction sequence is
-// the one the compiler emits for the builtin (M0 write, one wait state).
-// Completion is awaited explicitly with wait_vm.
-__device__ __forceinline__ void copy16(const void *src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
-}
-
-// s_waitcnt with only the vector-memory counter: at most n loads outstanding
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
-}
-
 __device__ __forceinline__ bf16x8 as_bf16(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // 2^x by the hardware instruction (results below the normal range flush to

@@ -58,6 +58,32 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// One global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
+// i's bytes land at LDS byte lds + 16 i (lds is wave-uniform).  Written out
+// (rather than through the builtin) so that the compiler, which does not
+// track these LDS writes, inserts no vmcnt(0) before every later LDS read;
+// the instruction sequence is the one the compiler emits for the builtin (M0
+// write, one wait state).  The compiler does not count these loads either:
+// completion is awaited explicitly with wait_vm, and every compiler-visible
+// load must be complete before the first copy is issued (a later wait the
+// compiler computes for such a load would not account for the copies).
+__device__ __forceinline__ void copy16(const void *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+}
+
+// s_waitcnt with only the vector-memory counter: at most n loads outstanding
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// LDS byte address of a __shared__ object
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T *p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)p;
+}
+
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
 // operations, then s_barrier.  Unlike __syncthreads() it does not wait for
 // outstanding global loads, so gathers issued earlier stay in flight.
