@@ -403,9 +403,20 @@ def main():
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
 
+        # per-step GPU time: an event after every step of another pass of
+        # --steps steps (the gaps between consecutive events), for p10/p50/p90
+        stream = torch.cuda.current_stream()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        evs[0].record(stream)
+        for i in range(args.steps):
+            run_step(i)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        step_us = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)])
+        p10, p50, p90 = (float(x) for x in np.percentile(step_us, [10, 50, 90]))
+
         # the dominant call alone: sas_sparse_decode launched back to back on the
         # current stream (selections from the steps above), bracketed by HIP events
-        stream = torch.cuda.current_stream()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for i in range(len(layers)):
             L = layers[i]
@@ -429,10 +440,11 @@ def main():
                              decode_ms=dec_ms, decode_gbs=kv_b / (dec_ms * 1e-3) / 1e9,
                              step_gbs=(kv_b + gk_b) / (ms * 1e-3) / 1e9, kv_bytes=kv_b, gk_bytes=gk_b,
                              attended_tokens_per_query=float(np.mean([c.sum() for c in cnts])) * 64 / (
-                                 w0.batch * w0.n_kv_heads))
+                                 w0.batch * w0.n_kv_heads),
+                             step_us_p10=p10, step_us_p50=p50, step_us_p90=p90)
         log(f"{mode}: {results[mode]['queries_per_s']:.0f} queries/s, {ms * 1e3:.1f} us/step, "
             f"decode {dec_ms * 1e3:.1f} us = {results[mode]['decode_gbs']:.0f} GB/s, "
-            f"step {results[mode]['step_gbs']:.0f} GB/s")
+            f"step {results[mode]['step_gbs']:.0f} GB/s; per-step p10/p50/p90 {p10:.1f}/{p50:.1f}/{p90:.1f} us")
 
     worst = min(results, key=lambda m: results[m]["queries_per_s"])
     r = results[worst]

@@ -24,10 +24,11 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 // blocks, 1 for the local block, 0 padding; *cnt = k_eff + 1.
 //   keys: LDS, 16-byte aligned, readable up to max(n, 512) entries (keys are
 //   > 0; entries past n are ignored); hist: this wave's 256-entry LDS
-//   histogram.  Radix select over 8-bit digits with a wave-private histogram
-//   and DPP prefix sums; keys > T are taken, and the krem lowest-index keys
-//   equal to T.  Lane l sweeps keys [512k + 8l, 512k + 8l + 8); the first 512
-//   stay in registers across the passes.
+//   histogram, which afterwards holds the compacted selection (n_sel <= 256).
+//   Radix select over 8-bit digits with a wave-private histogram and DPP
+//   prefix sums; keys > T are taken, and the krem lowest-index keys equal to
+//   T.  Lane l sweeps keys [512k + 8l, 512k + 8l + 8); the first 512 stay in
+//   registers across the passes.
 __device__ __forceinline__ void wave_select(const uint32_t *keys, int n, int k_eff, int n_sel, uint32_t *hist,
                                             int32_t *sel, float *gates, int32_t *cnt_out) {
   const int lane = threadIdx.x & 63;
@@ -95,6 +96,8 @@ __device__ __forceinline__ void wave_select(const uint32_t *keys, int n, int k_e
       __builtin_amdgcn_wave_barrier();
     }
   }
+  // the selected candidates' indices, compacted in ascending order into the
+  // (now free) histogram, then written out with one coalesced store per lane
   if (k_eff > 0) {
     uint32_t pos_base = 0, eq_base = 0;
     for (int c0 = 0; c0 < n; c0 += 512) {
@@ -119,20 +122,26 @@ __device__ __forceinline__ void wave_select(const uint32_t *keys, int n, int k_e
       const uint32_t take_incl = wave_incl_scan(n_take);
       uint32_t pos = pos_base + take_incl - n_take;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (take_mask >> e & 1u) {
-          sel[pos] = cl + e;
-          if (gates) gates[pos] = 1.0f / (1.0f + __expf(-key_score(kk[e])));
-          ++pos;
-        }
-      }
+      for (int e = 0; e < 8; ++e)
+        if (take_mask >> e & 1u) hist[pos++] = (uint32_t)(cl + e);
       pos_base += (uint32_t)__builtin_amdgcn_readlane((int)take_incl, 63);
       eq_base += (uint32_t)__builtin_amdgcn_readlane((int)eq_incl, 63);
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
   }
-  for (int i = k_eff + lane; i < n_sel; i += 64) {
-    sel[i] = i == k_eff ? n : -1;
-    if (gates) gates[i] = i == k_eff ? 1.0f : 0.0f;
+  for (int i = lane; i < n_sel; i += 64) {
+    int32_t c;
+    float g;
+    if (i < k_eff) {
+      c = (int32_t)hist[i];
+      g = 1.0f / (1.0f + __expf(-key_score(keys[c])));
+    } else {
+      c = i == k_eff ? n : -1;
+      g = i == k_eff ? 1.0f : 0.0f;
+    }
+    sel[i] = c;
+    if (gates) gates[i] = g;
   }
   if (lane == 0) *cnt_out = k_eff + 1;
 }
