@@ -367,6 +367,30 @@ def main():
     w0 = layers[0]["w"]
     log(f"setup {time.perf_counter() - t_setup:.1f} s")
 
+    # bulk pooling alone (sas_pool_blocks over every complete block of a layer;
+    # off the step, once per layer): again for each layer, bracketed by HIP events
+    stream = torch.cuda.current_stream()
+    pool_args = []
+    for L in layers:
+        w = L["w"]
+        lens = wl.host(w.seq_lens)
+        seq = np.repeat(np.arange(w.batch, dtype=np.int32), [int(x) // 64 for x in lens])
+        blk = np.concatenate([np.arange(int(x) // 64, dtype=np.int32) for x in lens])
+        pool_args.append((ops.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides), w,
+                          torch.as_tensor(seq, device=dev), torch.as_tensor(blk, device=dev), len(seq)))
+    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    pe0.record(stream)
+    for (shp, w, sq, bk, _), L in zip(pool_args, layers):
+        ops.pool_blocks(shp, w.k_pool, w.block_table, sq, bk, w.w_k, w.w_knorm, w.theta, L["gk"])
+    pe1.record(stream)
+    torch.cuda.synchronize()
+    pool_ms = pe0.elapsed_time(pe1) / len(layers)
+    pool_blocks_n = float(np.mean([a[4] for a in pool_args]))
+    pool_bytes = pool_blocks_n * w0.n_kv_heads * (64 * 128 * 2 + 128 * 2)  # keys read + gate keys written
+    log(f"bulk pooling: {pool_ms:.3f} ms per layer ({int(pool_blocks_n)} blocks x {w0.n_kv_heads} KV heads), "
+        f"{pool_bytes / (pool_ms * 1e-3) / 1e9:.0f} GB/s")
+
     results = {}
     for mode in args.modes.split(","):
         gated = mode == "gated"
@@ -472,6 +496,10 @@ def main():
                      "traffic": recorded_traffic(args.workload, args.budget),
                      "bytes_per_launch": r["kv_bytes"], "avg_launch_us": round(r["decode_ms"] * 1e3, 2)},
         "step_hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
+        "pooling": {"kernel": "sas_pool_blocks (pool_kernel), every complete block of a layer, off the step",
+                    "ms_per_layer": round(pool_ms, 4), "bytes": pool_bytes,
+                    "achieved_gbs": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1),
+                    "frac": round(pool_bytes / (pool_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "tokens_per_s": round(r["queries_per_s"], 1),
         "attended_kv_tokens_per_s": round(r["queries_per_s"] * r["attended_tokens_per_query"], 1),
         "modes": {m: {k: round(v, 3) for k, v in d.items()} for m, d in results.items()},

@@ -7,116 +7,178 @@
 // localmodelwatch model page: KV block size 64, gate hidden size 128, key
 // block pooling max + min + average, Q/K normalization, gate RoPE).
 //
-// One workgroup (256 threads) per (listed block, KV head):
-//   1. a coalesced pass over the 64 x 128 bf16 key rows: per dimension the
-//      running max / min / fp32 sum of 32 rows per thread, halves combined
-//      in LDS -> pooled[384] = [max | min | mean];
-//   2. the 128 x 384 projection w_k[h] . pooled: 16 lanes per w_k row (every
-//      load instruction reads whole rows), reduced across the lanes (DPP);
-//   3. wave 0: RMSNorm (eps 1e-6) * w_knorm, rotate-half RoPE at position
+// One workgroup (256 threads) per (16 listed blocks, KV head):
+//   1. thread (block t/16, dims 8(t%16) .. +7) scans its block's 64 key rows
+//      with 16-byte loads: max, min and an fp32 sum in row order ->
+//      pooled[b][384] = [max | min | mean] in LDS;
+//   2. U^T = w_k[h] . P^T (128 x 384 times 384 x 16 blocks) on MFMA: the max
+//      and min inputs are bf16 values, the means are split into bf16 high and
+//      low parts (about 16 significant bits); w_k is read once per 16 blocks;
+//   3. per block: RMSNorm (eps 1e-6) * w_knorm, rotate-half RoPE at position
 //      64*c (angles formed and reduced in fp64), round to bf16, store.
 // Bytes per (block, KV head): 16 KiB of keys read, 256 B of gate key written
-// (w_k is 96 KiB per KV head and stays in L2).
+// (w_k, 96 KiB per KV head, is read from L2 once per 16 blocks).
 //
 // The same pooling also runs inside the decode step's cache write
 // (append_kernel): the step that writes a block's last row pools the block
-// there, instead of a second launch re-reading that row.
+// there, instead of a second launch re-reading that row.  It runs the same
+// arithmetic on a batch of one block, so its gate keys are bit-identical.
 #include "sas_device.h"
 #include "sas_kernels.h"
 
 namespace sas {
+namespace {
 
-// Gate key of one 64-token key block of one KV head.  Every thread of a
-// 256-thread workgroup calls it (it holds barriers).  kb: the block's row 0 of
-// this head; last_row: when non-null, row 63 is read from there instead of
-// from the pool (the append kernel passes the row it is writing).
-__device__ __forceinline__ void pool_unit(const uint16_t *kb, int64_t tok_stride, const uint16_t *last_row,
-                                          const uint16_t *w_kh, const float *w_knorm, double theta, int c,
-                                          uint16_t *dst) {
-  __shared__ float part[2][3][kHeadDim];
-  __shared__ float pooled[3 * kHeadDim];
-  __shared__ float upart[kGateDim];
-  const int t = threadIdx.x;
+constexpr int kPoolBatch = 16;                // blocks per workgroup
+constexpr int kPooledPitch = 3 * kHeadDim + 4;  // LDS row of pooled statistics (floats), staggered banks
+constexpr int kUPitch = kGateDim + 4;
 
-  {  // 1. pooled statistics
-    const int d = t & (kHeadDim - 1);
-    const int half = t >> 7;
-    float mx = -__builtin_inff(), mn = __builtin_inff(), sum = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < kBlock / 2; ++r) {
-      const int row = half * (kBlock / 2) + r;
-      const uint16_t *src = (last_row && row == kBlock - 1) ? last_row : kb + (int64_t)row * tok_stride;
-      float x = bf16_to_f32(src[d]);
-      mx = fmaxf(mx, x);
-      mn = fminf(mn, x);
-      sum += x;
+__device__ __forceinline__ bf16x8 as_b8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+}  // namespace
+
+// Gate keys of nb <= 16 key blocks of one KV head.  Every thread of a
+// 256-thread workgroup calls it (it holds barriers).  src[b]: block b's row 0
+// of this head; blk[b]: its block index (RoPE position 64 blk[b]); dst[b]: its
+// 128 gate-key values; all three in LDS, written by the caller before a
+// barrier.  last_row: when non-null, block 0's row 63 is read from there
+// instead of from the pool (the append kernel passes the row it is writing).
+__device__ __forceinline__ void pool_batch(int nb, const uint16_t *const *src, const int *blk, uint16_t *const *dst,
+                           int64_t tok_stride, const uint16_t *last_row, const uint16_t *w_kh,
+                           const float *w_knorm, double theta) {
+  __shared__ __attribute__((aligned(16))) float pooled[kPoolBatch][kPooledPitch];
+  __shared__ float uk[kPoolBatch][kUPitch];
+  __shared__ double invf[kGateDim / 2];
+  __shared__ float wkn[kGateDim];
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int b = t >> 4, o = t & 15;
+
+  if (t < kGateDim / 2) invf[t] = pow(theta, -(double)t / 64.0);
+  if (t < kGateDim) wkn[t] = w_knorm[t];
+
+  // ---- 1. pooled statistics
+  if (b < nb) {
+    const uint16_t *kb = src[b] + 8 * o;
+    float mx[8], mn[8], sum[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      mx[e] = -__builtin_inff();
+      mn[e] = __builtin_inff();
+      sum[e] = 0.f;
     }
-    part[half][0][d] = mx;
-    part[half][1][d] = mn;
-    part[half][2][d] = sum;
-  }
-  __syncthreads();
-  if (t < kHeadDim) {
-    pooled[t] = fmaxf(part[0][0][t], part[1][0][t]);
-    pooled[kHeadDim + t] = fminf(part[0][1][t], part[1][1][t]);
-    pooled[2 * kHeadDim + t] = (part[0][2][t] + part[1][2][t]) * (1.0f / kBlock);
-  }
-  __syncthreads();
-  {  // 2. projection to the gate space: each 16-lane group owns 8 output rows
-     // j; a lane holds 24 of a row's 384 inputs (three 16-byte chunks), so a
-     // wave reads 4 whole rows per load; the group reduces across its lanes.
-    const int lane16 = t & 15, grp = t >> 4;
-    const uint16_t *w = w_kh + (int64_t)(8 * grp) * 3 * kHeadDim + 8 * lane16;
-    u32x4 wv[8][3];
+#pragma unroll 16
+    for (int r = 0; r < kBlock; ++r) {
+      const u32x4 w = (last_row && b == 0 && r == kBlock - 1) ? ld16(last_row + 8 * o)
+                                                             : ld16(kb + (int64_t)r * tok_stride);
+      const float x[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                          bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-      for (int k = 0; k < 3; ++k) wv[r][k] = ld16(w + r * 3 * kHeadDim + 128 * k);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      float acc = 0.f;
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const float *pp = pooled + 128 * k + 8 * lane16;
-        acc = fmaf(pp[0], bf16_lo(wv[r][k].x), acc);
-        acc = fmaf(pp[1], bf16_hi(wv[r][k].x), acc);
-        acc = fmaf(pp[2], bf16_lo(wv[r][k].y), acc);
-        acc = fmaf(pp[3], bf16_hi(wv[r][k].y), acc);
-        acc = fmaf(pp[4], bf16_lo(wv[r][k].z), acc);
-        acc = fmaf(pp[5], bf16_hi(wv[r][k].z), acc);
-        acc = fmaf(pp[6], bf16_lo(wv[r][k].w), acc);
-        acc = fmaf(pp[7], bf16_hi(wv[r][k].w), acc);
+      for (int e = 0; e < 8; ++e) {
+        mx[e] = fmaxf(mx[e], x[e]);
+        mn[e] = fminf(mn[e], x[e]);
+        sum[e] += x[e];
       }
-      acc = row16_sum(acc);
-      if (lane16 == 0) upart[8 * grp + r] = acc;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pooled[b][8 * o + e] = mx[e];
+      pooled[b][kHeadDim + 8 * o + e] = mn[e];
+      pooled[b][2 * kHeadDim + 8 * o + e] = sum[e] * (1.0f / kBlock);
     }
   }
-  __syncthreads();
-  if (t < 64) {  // 3. norm + RoPE on pairs (t, t+64)
-    float a = upart[t];
-    float b = upart[t + 64];
-    float ss = wave_sum(a * a + b * b);
-    float inv = 1.0f / sqrtf(ss * (1.0f / kGateDim) + 1e-6f);
-    a = a * inv * w_knorm[t];
-    b = b * inv * w_knorm[t + 64];
-    float cf, sf;
-    rope_cos_sin((double)c * kBlock, pow(theta, -(double)t / 64.0), cf, sf);
-    float ra = a * cf - b * sf;
-    float rb = b * cf + a * sf;
-    dst[t] = (uint16_t)f32_to_bf16(ra);
-    dst[t + 64] = (uint16_t)f32_to_bf16(rb);
+  // w_k A operands of this wave's 32 output rows (row 32w + 16mt + l%16,
+  // inputs 32ks + 8(l/16) .. +7), loaded after the key scan so that the two
+  // never hold registers together (several workgroups then share a CU)
+  u32x4 wk[2][12];
+  {
+    const uint16_t *w = w_kh + (int64_t)(32 * wave + (lane & 15)) * 3 * kHeadDim + 8 * (lane >> 4);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 12; ++ks) wk[mt][ks] = ld16(w + (int64_t)16 * mt * 3 * kHeadDim + 32 * ks);
+  }
+  lds_barrier();
+
+  // ---- 2. U^T = w_k P^T: lane l holds block l%16, rows 32w + 16mt + 4(l/16) + r
+  // (columns of blocks past nb hold stale values and are not read)
+  {
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    const float *pb = &pooled[lane & 15][8 * (lane >> 4)];
+#pragma unroll
+    for (int ks = 0; ks < 12; ++ks) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = pb[32 * ks + e];
+      const u32x4 h = {pack_bf16_rne(x[0], x[1]), pack_bf16_rne(x[2], x[3]), pack_bf16_rne(x[4], x[5]),
+                       pack_bf16_rne(x[6], x[7])};
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_b8(wk[mt][ks]), as_b8(h), acc[mt], 0, 0, 0);
+      if (ks >= 8) {  // the means: add the low parts
+        float lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lo[e] = x[e] - ((e & 1) ? bf16_hi(h[e >> 1]) : bf16_lo(h[e >> 1]));
+        const u32x4 l = {pack_bf16_rne(lo[0], lo[1]), pack_bf16_rne(lo[2], lo[3]), pack_bf16_rne(lo[4], lo[5]),
+                         pack_bf16_rne(lo[6], lo[7])};
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_b8(wk[mt][ks]), as_b8(l), acc[mt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) uk[lane & 15][32 * wave + 16 * mt + 4 * (lane >> 4) + r] = acc[mt][r];
+  }
+  lds_barrier();
+
+  // ---- 3. per block (16 lanes each, dims o + 16k): RMSNorm, w_knorm, RoPE at
+  // position 64 blk; the bf16 results go back to LDS, then out as 16-byte rows
+  if (b < nb) {
+    float x[8], ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      x[k] = uk[b][o + 16 * k];
+      ss += x[k] * x[k];
+    }
+    const float inv = 1.0f / sqrtf(row16_sum(ss) * (1.0f / kGateDim) + 1e-6f);
+    const double pos = (double)blk[b] * kBlock;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int d = o + 16 * k;
+      const float a = x[k] * inv * wkn[d], bb = x[k + 4] * inv * wkn[d + 64];
+      float cf, sf;
+      rope_cos_sin(pos, invf[d], cf, sf);
+      uk[b][d] = a * cf - bb * sf;
+      uk[b][d + 64] = bb * cf + a * sf;
+    }
+  }
+  lds_barrier();
+  if (b < nb) {
+    const float *u = &uk[b][8 * o];
+    *reinterpret_cast<u32x4 *>(dst[b] + 8 * o) =
+        u32x4{pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]), pack_bf16x2(u[4], u[5]), pack_bf16x2(u[6], u[7])};
   }
 }
 
-__global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
-  const int unit = blockIdx.x;
-  const int i = unit / p.n_kv_heads;
-  const int kvh = unit - i * p.n_kv_heads;
-  const int s = p.pool_seq[i], c = p.pool_blk[i];
-  const int32_t page = p.block_table[(int64_t)s * p.max_blocks + c];
-  pool_unit(p.k_pool + (int64_t)page * p.page_stride + (int64_t)kvh * p.head_stride, p.tok_stride, nullptr,
-            p.w_k + (int64_t)kvh * kGateDim * 3 * kHeadDim, p.w_knorm, p.theta, c,
-            p.gate_keys + ((int64_t)page * p.n_kv_heads + kvh) * kGateDim);
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void pool_kernel(PoolParams p) {
+  __shared__ const uint16_t *src_l[kPoolBatch];
+  __shared__ uint16_t *dst_l[kPoolBatch];
+  __shared__ int blk_l[kPoolBatch];
+  const int kvh = blockIdx.x % p.n_kv_heads;  // the KV heads of a batch run in consecutive workgroups
+  const int i0 = (blockIdx.x / p.n_kv_heads) * kPoolBatch;
+  const int nb = min(kPoolBatch, p.n - i0);
+  if ((int)threadIdx.x < nb) {
+    const int i = i0 + threadIdx.x;
+    const int s = p.pool_seq[i], c = p.pool_blk[i];
+    const int32_t page = p.block_table[(int64_t)s * p.max_blocks + c];
+    src_l[threadIdx.x] = p.k_pool + (int64_t)page * p.page_stride + (int64_t)kvh * p.head_stride;
+    dst_l[threadIdx.x] = p.gate_keys + ((int64_t)page * p.n_kv_heads + kvh) * kGateDim;
+    blk_l[threadIdx.x] = c;
+  }
+  lds_barrier();
+  pool_batch(nb, src_l, blk_l, dst_l, p.tok_stride, nullptr, p.w_k + (int64_t)kvh * kGateDim * 3 * kHeadDim,
+             p.w_knorm, p.theta);
 }
 
 // One workgroup per (sequence, KV head): threads 0-15 write the new key row,
@@ -125,6 +187,9 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
 // k_new.  Bytes per (sequence, KV head): 512 B read + 512 B written, plus
 // 16 KiB - 256 B of keys read and 256 B written per completed block.
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+  __shared__ const uint16_t *src_l[1];
+  __shared__ uint16_t *dst_l[1];
+  __shared__ int blk_l[1];
   const int unit = blockIdx.x;
   const int s = unit / p.n_kv_heads;
   const int kvh = unit - s * p.n_kv_heads;
@@ -141,14 +206,22 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     uint16_t *to = (t < 16 ? p.k_pool : p.v_pool) + base + (int64_t)r * p.tok_stride + 8 * lane;
     *(u32x4 *)to = ld16(from);
   }
-  if (L % kBlock == 0)
-    pool_unit(p.k_pool + base, p.tok_stride, p.k_new + src, p.w_k + (int64_t)kvh * kGateDim * 3 * kHeadDim,
-              p.w_knorm, p.theta, c, p.gate_keys + ((int64_t)page * p.n_kv_heads + kvh) * kGateDim);
+  if (L % kBlock == 0) {
+    if (t == 0) {
+      src_l[0] = p.k_pool + base;
+      dst_l[0] = p.gate_keys + ((int64_t)page * p.n_kv_heads + kvh) * kGateDim;
+      blk_l[0] = c;
+    }
+    lds_barrier();
+    pool_batch(1, src_l, blk_l, dst_l, p.tok_stride, p.k_new + src, p.w_k + (int64_t)kvh * kGateDim * 3 * kHeadDim,
+               p.w_knorm, p.theta);
+  }
 }
 
 hipError_t launch_pool(const PoolParams &p, hipStream_t st) {
   if (p.n == 0) return hipSuccess;
-  hipLaunchKernelGGL(pool_kernel, dim3((unsigned)(p.n * p.n_kv_heads)), dim3(256), 0, st, p);
+  const unsigned batches = (unsigned)((p.n + kPoolBatch - 1) / kPoolBatch);
+  hipLaunchKernelGGL(pool_kernel, dim3(batches * (unsigned)p.n_kv_heads), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
