@@ -303,6 +303,114 @@ def time_backward(args, layers, w0):
                          "bytes_per_launch": kv_b}}
 
 
+def run_serve(args):
+    """Incremental serving on the ragged workload: per step every sequence
+    appends one token (sas_append_kv, which pools each block the token
+    completes), then sas_gate_topk + sas_sparse_decode.  The lengths grow by
+    one per step; warm-up steps are the first steps of the same run."""
+    import numpy as np
+    import torch
+    from learned_block_sparse_tok_amd import ops
+    from learned_block_sparse_tok_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ops.lib()
+    warm = max(1, min(args.warmup, 16))
+    steps = max(1, min(args.steps, 120))
+    total = warm + steps
+    budget = args.budget if args.budget != 2048 else 4096  # the ragged workload's budget unless given
+    w = wl.named(args.workload, device=dev, budget=budget, steps=total)
+    shape = ops.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides)
+    gk = torch.zeros((w.n_pages, w.n_kv_heads, 128), dtype=torch.bfloat16, device=dev)
+    lens0 = wl.host(w.seq_lens).astype(np.int64)
+    seq = np.repeat(np.arange(w.batch, dtype=np.int32), [int(L) // 64 for L in lens0])
+    blk = np.concatenate([np.arange(int(L) // 64, dtype=np.int32) for L in lens0])
+    ops.pool_blocks(shape, w.k_pool, w.block_table, torch.as_tensor(seq, device=dev), torch.as_tensor(blk, device=dev),
+                    w.w_k, w.w_knorm, w.theta, gk)
+    q_new, k_new, v_new = wl.append_rows(w, total, seed=55)
+    # per-step lengths: the new token is at position L, then L + 1 tokens are cached
+    lens_all = torch.as_tensor((lens0[None, :] + 1 + np.arange(total)[:, None]).astype(np.int32), device=dev)
+    completed = int(((lens0[None, :] + 1 + np.arange(total)[:, None]) % 64 == 0).sum())
+    torch.cuda.synchronize()
+    log(f"{args.workload}: B={w.batch}, lengths {int(lens0.min())}..{int(lens0.max())}, budget {budget}, "
+        f"{total} steps ({completed} blocks completed on the way)")
+    results = {}
+    for mode in args.modes.split(","):
+        gated = mode == "gated"
+        # each mode replays the same steps from the same starting state: the
+        # appends of a step rewrite the same rows and the same gate keys
+        dec = ops.SparseDecoder(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, budget, w.theta, gated,
+                                device=dev)
+        # The append runs on a second stream (default priority), overlapping
+        # the selection: step i's select reads only gate keys of blocks before
+        # its local block (the block the new token completes is that local
+        # block), and the appends write rows and gate keys no earlier step
+        # reads.  Only step i's attend waits for step i's append.
+        main = torch.cuda.current_stream()
+        side = torch.cuda.Stream(device=dev)
+        done = [torch.cuda.Event() for _ in range(total)]
+
+        def one(i):
+            with torch.cuda.stream(side):
+                ops.append_kv(shape, k_new[i], v_new[i], w.k_pool, w.v_pool, w.block_table, lens_all[i], w.w_k,
+                              w.w_knorm, w.theta, gk)
+                done[i].record(side)
+            dec.select(q_new[i], w.w_q, w.w_qnorm, gk, w.block_table, lens_all[i])
+            main.wait_event(done[i])
+            dec.attend(q_new[i], w.k_pool, w.v_pool, w.block_table, lens_all[i])
+
+        for i in range(warm):
+            one(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(warm, total):
+            one(i)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        # the appends alone, on the main stream (idempotent: the same rows and
+        # gate keys again)
+        stream = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for i in range(warm, total):
+            ops.append_kv(shape, k_new[i], v_new[i], w.k_pool, w.v_pool, w.block_table, lens_all[i], w.w_k,
+                          w.w_knorm, w.theta, gk)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        app_us = ev[0].elapsed_time(ev[1]) / steps * 1e3
+        cnt = wl.host(dec.cnt)
+        kv_b = kv_bytes_per_step(cnt, 64 * 128 * 2)
+        gk_b = gk_bytes_per_step(wl.host(lens_all[total - 1]), w.n_kv_heads)
+        ms = elapsed * 1e3 / steps
+        results[mode] = dict(queries_per_s=w.batch * steps / elapsed, ms_per_step=ms, append_us=app_us,
+                             step_gbs=(kv_b + gk_b) / (ms * 1e-3) / 1e9, kv_bytes=kv_b, gk_bytes=gk_b)
+        log(f"{mode}: {results[mode]['queries_per_s']:.0f} queries/s, {ms * 1e3:.1f} us/step (append {app_us:.1f} us), "
+            f"step {results[mode]['step_gbs']:.0f} GB/s of gate keys + selected K/V")
+    worst = min(results, key=lambda m: results[m]["queries_per_s"])
+    r = results[worst]
+    line = {
+        "metric": "incremental serving queries/s (append + incremental pooling + select + attend per step)",
+        "value": round(r["queries_per_s"], 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": w.batch, "context": f"{int(lens0.min())}..{int(lens0.max())}",
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": 128, "budget_tokens": budget,
+                   "kv_layout": w.layout, "mode": f"{worst} (slower of {','.join(results)})", "launch": "eager"},
+        "step_hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
+        "modes": {m: {k: round(v, 3) for k, v in d.items()} for m, d in results.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -333,6 +441,8 @@ def main():
 
     if args.workload.startswith("prefill"):
         return run_prefill(args)
+    if args.workload == "ragged":
+        return run_serve(args)
     import numpy as np
     import torch
     from learned_block_sparse_tok_amd import ops
