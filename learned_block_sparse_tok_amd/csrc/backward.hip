@@ -45,14 +45,6 @@ constexpr float kInvSqrtDg = 0.08838834764831845f;  // 1/sqrt(128)
 
 __device__ __forceinline__ bf16x8 to_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// a lane's value from another lane of its 16-lane row (DPP): kRor4 / kRor8
-// rotate the row by 4 / 8 lanes, kXor2 / kXor1 swap lanes j and j^2 / j^1
-constexpr int kRor4 = 0x124, kRor8 = 0x128, kXor2 = 0x4E, kXor1 = 0xB1;
-template <int kCtrl>
-__device__ __forceinline__ float row_dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
-}
-
 // One butterfly step over n value pairs (v[c], v[c + n]): a lane keeps the
 // half picked by its bit, takes the same half from its partner lane and
 // combines the two.

@@ -65,9 +65,11 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
   // gather): the group's queries, the RoPE frequency and norm weights of
   // this lane's pair, the block-table row (its whole width, independent of
   // the sequence length), and the query-projection rows.  The G*128
-  // projection outputs are split over the 16 lane-groups, 8G rows each; a
-  // group reads a row as 16 x 16 B (so a wave reads 4 whole rows per load)
-  // and reduces it across the group.
+  // projection outputs form 8G batches of 16 rows of one head (batch b: head
+  // b/8, rows 16(b%8) .. +15, i.e. rows 16b .. 16b+15 of the group's heads);
+  // lane group grp takes batches grp, grp+16, ...  A group reads a row as
+  // 16 x 16 B (so a wave reads 4 whole rows per load), and a transposing row
+  // sum leaves lane o of the group with row o of the batch.
   const uint16_t *qg = p.q + ((int64_t)s * p.n_q_heads + kvh * G) * kHeadDim;
   const bool has_q = 8 * t < G * kHeadDim;  // G <= 16: one 16-byte piece per thread
   const u32x4 qpiece = ld16(qg + (has_q ? 8 * t : 0));
@@ -78,14 +80,18 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
   int32_t btv[kBtUnroll];
 #pragma unroll
   for (int k = 0; k < kBtUnroll; ++k) btv[k] = bt[min(t + 256 * k, p.max_blocks - 1)];
-  constexpr int kRowsInFlight = 32;  // all rows of a group for G <= 4
-  const int rows_per_grp = G * (kGateDim / 16);
-  const int64_t row0 = (int64_t)kvh * G * kGateDim + (int64_t)grp * rows_per_grp;
-  const int64_t row_last = (int64_t)kvh * G * kGateDim + G * kGateDim - 1;
-  const uint16_t *wq_lane = p.w_q + 8 * lane16;
+  constexpr int kRowsInFlight = 32;  // two batches per group: all rows for G <= 4
+  const int n_batches = 8 * G;
+  const uint16_t *wq_lane = p.w_q + ((int64_t)kvh * G * kGateDim) * kHeadDim + 8 * lane16;
   u32x4 wv[kRowsInFlight];
+  auto load_batches = [&](int round) {  // batches grp + 16(2 round), grp + 16(2 round + 1), clamped rows
 #pragma unroll
-  for (int u = 0; u < kRowsInFlight; ++u) wv[u] = ld16(wq_lane + min(row0 + u, row_last) * kHeadDim);
+    for (int u = 0; u < kRowsInFlight; ++u) {
+      const int row = 16 * (grp + 16 * (2 * round + u / 16)) + u % 16;
+      wv[u] = ld16(wq_lane + (int64_t)min(row, G * kGateDim - 1) * kHeadDim);
+    }
+  };
+  load_batches(0);
 
   if (has_q) {
     float *qd = &qs[0][0] + 8 * t;
@@ -110,29 +116,39 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
     v[u] = c < n ? ld16(gkh + (int64_t)slot[c] * page_stride) : u32x4{0, 0, 0, 0};
   }
 
-  // ---- 2. gate queries: v[g][j] = sum_d w_q[h][j][d] q[h][d]
-  auto project_row = [&](const u32x4 &w, int r) {
-    const int o = grp * rows_per_grp + r;
-    const int g = o >> 7, jj = o & 127;
-    const float *qq = qs[g] + 8 * lane16;
-    float acc = qq[0] * bf16_lo(w.x);
-    acc = fmaf(qq[1], bf16_hi(w.x), acc);
-    acc = fmaf(qq[2], bf16_lo(w.y), acc);
-    acc = fmaf(qq[3], bf16_hi(w.y), acc);
-    acc = fmaf(qq[4], bf16_lo(w.z), acc);
-    acc = fmaf(qq[5], bf16_hi(w.z), acc);
-    acc = fmaf(qq[6], bf16_lo(w.w), acc);
-    acc = fmaf(qq[7], bf16_hi(w.w), acc);
-    acc = row16_sum(acc);
-    if (lane16 == 0 && r < rows_per_grp) vs[g][jj] = acc;
+  // ---- 2. gate queries: v[g][j] = sum_d w_q[h][j][d] q[h][d], batch by
+  // batch: lane o of the group ends with row o of the batch
+  auto project_batches = [&](int round) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int b = grp + 16 * (2 * round + i);
+      const int h = min(b >> 3, G - 1);
+      const float *qq = qs[h] + 8 * lane16;
+      float qv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] = qq[e];
+      float pp[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const u32x4 &w = wv[16 * i + r];
+        float acc = qv[0] * bf16_lo(w.x);
+        acc = fmaf(qv[1], bf16_hi(w.x), acc);
+        acc = fmaf(qv[2], bf16_lo(w.y), acc);
+        acc = fmaf(qv[3], bf16_hi(w.y), acc);
+        acc = fmaf(qv[4], bf16_lo(w.z), acc);
+        acc = fmaf(qv[5], bf16_hi(w.z), acc);
+        acc = fmaf(qv[6], bf16_lo(w.w), acc);
+        acc = fmaf(qv[7], bf16_hi(w.w), acc);
+        pp[row16_slot(r)] = acc;
+      }
+      const float tot = row16_transpose_sum(pp);
+      if (b < n_batches) vs[b >> 3][16 * (b & 7) + lane16] = tot;
+    }
   };
-#pragma unroll
-  for (int u = 0; u < kRowsInFlight; ++u) project_row(wv[u], u);  // rows past the group's own are clamped
-  for (int b0 = kRowsInFlight; b0 < rows_per_grp; b0 += kRowsInFlight) {  // G > 4 only
-#pragma unroll
-    for (int u = 0; u < kRowsInFlight; ++u) wv[u] = ld16(wq_lane + min(row0 + b0 + u, row_last) * kHeadDim);
-#pragma unroll
-    for (int u = 0; u < kRowsInFlight; ++u) project_row(wv[u], b0 + u);
+  project_batches(0);
+  for (int round = 1; 32 * round < n_batches; ++round) {  // G > 4 only
+    load_batches(round);
+    project_batches(round);
   }
   // ---- 2b. issue candidates 256 .. 511; they arrive while the gate queries
   // are normalised and rotated
@@ -191,6 +207,9 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
         v[u] = c < n ? ld16(gkh + (int64_t)slot[c] * page_stride) : u32x4{0, 0, 0, 0};
       }
     }
+    // one row sum per candidate, always finished by lane 0 of the group, so
+    // that equal gate keys get bit-equal scores wherever they sit (exact
+    // ties break by block index)
 #pragma unroll
     for (int u = 0; u < kKeysInFlight; ++u) {
       auto dot8 = [&](const float(&w)[8]) {
@@ -211,15 +230,7 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
         for (int h = 0; h < (kMax ? 8 : 1); ++h)
           if (h < G) d = fmaxf(d, dot8(gh[h]));
       } else {
-        d = gm[0] * bf16_lo(v[u].x);
-        d = fmaf(gm[1], bf16_hi(v[u].x), d);
-        d = fmaf(gm[2], bf16_lo(v[u].y), d);
-        d = fmaf(gm[3], bf16_hi(v[u].y), d);
-        d = fmaf(gm[4], bf16_lo(v[u].z), d);
-        d = fmaf(gm[5], bf16_hi(v[u].z), d);
-        d = fmaf(gm[6], bf16_lo(v[u].w), d);
-        d = fmaf(gm[7], bf16_hi(v[u].w), d);
-        d = row16_sum(d);
+        d = dot8(gm);
       }
       const int c = base + 16 * u + grp;
       if (lane16 == 0 && c < n) {

@@ -53,6 +53,40 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// A lane's value from another lane of its 16-lane row (DPP): kRor4 / kRor8
+// rotate the row by 4 / 8 lanes, kXor2 / kXor1 swap lanes j and j^2 / j^1.
+constexpr int kRor4 = 0x124, kRor8 = 0x128, kXor2 = 0x4E, kXor1 = 0xB1;
+template <int kCtrl>
+__device__ __forceinline__ float row_dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
+// One step of a transposing row sum over n value pairs (v[c], v[c + n]): a
+// lane keeps the half its bit picks and adds the same half from its partner.
+template <int kCtrl, int n>
+__device__ __forceinline__ void row16_keep_half(bool bit, float *v) {
+#pragma unroll
+  for (int c = 0; c < n; ++c) {
+    const float keep = bit ? v[c + n] : v[c], send = bit ? v[c] : v[c + n];
+    v[c] = keep + row_dpp<kCtrl>(send);
+  }
+}
+
+// Transposing sum over the 16 lanes of a DPP row: lane o gets the sum over
+// the row's lanes of their value for row index o.  The caller stores row r at
+// v[row16_slot(r)]; the first step may pair lanes by a rotation because every
+// lane still holds all 16 rows, the next three use exact partners (lane bits
+// 3, 1, 0).  15 exchanges instead of 16 separate 4-step row sums.
+__device__ __forceinline__ int row16_slot(int r) { return ((r >> 2) & 1) * 8 + ((r >> 3) & 1) * 4 + (r & 3); }
+__device__ __forceinline__ float row16_transpose_sum(float (&v)[16]) {
+  const int o = threadIdx.x & 15;
+  row16_keep_half<kRor4, 8>(o & 4, v);  // row bit 2
+  row16_keep_half<kRor8, 4>(o & 8, v);  // row bit 3
+  row16_keep_half<kXor2, 2>(o & 2, v);  // row bit 1
+  row16_keep_half<kXor1, 1>(o & 1, v);  // row bit 0
+  return v[0];
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
   return x;
