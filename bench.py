@@ -427,6 +427,8 @@ def main():
                          "known traffic, for calibrating the HBM byte counters), then exit")
     ap.add_argument("--backward", action="store_true",
                     help="also time sas_gate_backward after the gated step (prints a second JSON line)")
+    ap.add_argument("--path", default="auto", choices=["auto", "fused", "two_launches"],
+                    help="sas_decode_step path (auto: one fused launch when the pairs fill the GPU)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each layer's step from a HIP graph instead of launching it eagerly "
                          "(eager is faster here: the host stays ahead of the GPU)")
@@ -506,7 +508,7 @@ def main():
         gated = mode == "gated"
         # one decoder (outputs + workspaces) per layer, as a model keeps per-layer state
         decs = [ops.SparseDecoder(w0.batch, w0.n_q_heads, w0.n_kv_heads, w0.max_blocks, w0.strides, args.budget,
-                                  w0.theta, gated, device=dev) for _ in layers]
+                                  w0.theta, gated, device=dev, path=args.path) for _ in layers]
 
         def step_eager(l):
             L, dec = layers[l], decs[l]

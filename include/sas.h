@@ -19,6 +19,7 @@
  *                      (cache write fused with incremental pooling)
  *   sas_gate_topk      once per decode step                      (selection)
  *   sas_sparse_decode  once per decode step                      (attention)
+ *   sas_decode_step    the two above as one call (one fused launch)
  * and, for the training-time forward of a whole sequence (every position a
  * query): sas_prefill_select, then sas_prefill_attend; for training the
  * gates: sas_gate_backward after a gated decode step.
@@ -212,6 +213,44 @@ sas_status sas_sparse_decode_ex(const sas_shape *shape, const void *q, const voi
                                 int32_t gate_mode, const int32_t *cnt, int32_t max_sel,
                                 float sm_scale, void *out, void *workspace, size_t workspace_bytes,
                                 void *stream);
+
+/*
+ * sas_decode_step -- the whole decode step, selection then attention: the
+ * outputs of sas_gate_topk_ex followed by sas_sparse_decode_ex on the same
+ * arguments (the pages' learned block selection and block-sparse decoding
+ * within the token budget; aigc.news release note, "Tencent Hunyuan
+ * open-sources SAS ...").
+ *
+ * With path SAS_STEP_FUSED it is one kernel launch: each (sequence, KV head)
+ * is scored, selected and attended by one workgroup, which keeps the
+ * selection and the selected blocks' pages on chip.  SAS_STEP_TWO_LAUNCHES
+ * runs the two calls' kernels.  SAS_STEP_AUTO fuses when there are more
+ * (sequence, KV head) pairs than half the GPU's 256 compute units (then both
+ * paths give the same bits), and launches twice otherwise, where the
+ * attention spreads each pair over several workgroups.
+ *
+ * Arguments as for the two calls, with max_sel = budget_tokens / 64:
+ *   aggregate  SAS_AGG_MEAN or SAS_AGG_MAX
+ *   gated      0: plain Top-K attention; 1: gated attention (gate_mode
+ *              SAS_GATE_SCALE or SAS_GATE_LOGIT), which needs `gates`
+ *   gates      written when non-NULL (nullable when gated == 0)
+ *   scores     written when non-NULL (nullable)
+ *   sel, cnt, out  required
+ * workspace: at least sas_decode_step_workspace_bytes(shape, budget_tokens,
+ * path) bytes (0 on the fused path, where workspace may be NULL); no initial
+ * contents needed; calls that overlap in time must not share one.
+ */
+#define SAS_STEP_AUTO 0
+#define SAS_STEP_FUSED 1
+#define SAS_STEP_TWO_LAUNCHES 2
+size_t sas_decode_step_workspace_bytes(const sas_shape *shape, int32_t budget_tokens, int32_t path);
+sas_status sas_decode_step(const sas_shape *shape, const void *q, const void *w_q,
+                           const float *w_qnorm, const void *gate_keys, const void *k_pool,
+                           const void *v_pool, const int32_t *block_table,
+                           const int32_t *seq_lens, double rope_theta, int32_t budget_tokens,
+                           int32_t aggregate, int32_t gated, int32_t gate_mode, float sm_scale,
+                           int32_t path, int32_t *sel, float *gates, int32_t *cnt, float *scores,
+                           void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Training-time forward of one sequence (every position is a query).  SAS

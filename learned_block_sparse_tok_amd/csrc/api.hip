@@ -135,17 +135,21 @@ sas_status sas_append_kv(const sas_shape *shape, const void *k_new, const void *
   return hip_status(sas::launch_append(p, shape->batch, (hipStream_t)stream), "sas_append_kv launch");
 }
 
-sas_status sas_gate_topk_ex(const sas_shape *shape, const void *q, const void *w_q, const float *w_qnorm,
-                            const void *gate_keys, const int32_t *block_table, const int32_t *seq_lens,
-                            double rope_theta, int32_t budget_tokens, int32_t aggregate, int32_t *sel, float *gates,
-                            int32_t *cnt, float *scores, void *stream) {
+namespace {
+// Checks the selection arguments and fills its parameter block (scores
+// nullable only where the caller supplies another buffer or skips them).
+sas_status gate_params(const sas_shape *shape, const void *q, const void *w_q, const float *w_qnorm,
+                       const void *gate_keys, const int32_t *block_table, const int32_t *seq_lens, double rope_theta,
+                       int32_t budget_tokens, int32_t aggregate, int32_t *sel, float *gates, int32_t *cnt,
+                       float *scores, bool scores_nullable, sas::GateParams &p) {
   sas_status st = check_shape(shape, false);
   if (st) return st;
   if (aggregate != SAS_AGG_MEAN && aggregate != SAS_AGG_MAX)
     return fail(SAS_ERR_INVALID_ARG, "unknown score aggregation %d", aggregate);
   if (aggregate == SAS_AGG_MAX && shape->n_q_heads / shape->n_kv_heads > 8)
     return fail(SAS_ERR_UNSUPPORTED, "max aggregation supports groups of at most 8 query heads");
-  if (!q || !w_q || !w_qnorm || !gate_keys || !block_table || !seq_lens || !sel || !cnt || !scores)
+  if (!q || !w_q || !w_qnorm || !gate_keys || !block_table || !seq_lens || !sel || !cnt ||
+      (!scores && !scores_nullable))
     return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
   if (budget_tokens < SAS_BLOCK || budget_tokens % SAS_BLOCK)
     return fail(SAS_ERR_INVALID_ARG, "budget_tokens (%d) must be a positive multiple of %d", budget_tokens,
@@ -155,7 +159,6 @@ sas_status sas_gate_topk_ex(const sas_shape *shape, const void *q, const void *w
   if (!(rope_theta > 1.0)) return fail(SAS_ERR_INVALID_ARG, "rope_theta must be > 1");
   if (!aligned16(gate_keys) || !aligned16(w_q))
     return fail(SAS_ERR_UNSUPPORTED, "gate_keys and w_q must be 16-byte aligned");
-  sas::GateParams p;
   p.q = (const uint16_t *)q;
   p.w_q = (const uint16_t *)w_q;
   p.w_qnorm = w_qnorm;
@@ -174,6 +177,18 @@ sas_status sas_gate_topk_ex(const sas_shape *shape, const void *q, const void *w
   p.bt_row_stride = shape->max_blocks;
   p.aggregate = aggregate;
   for (int i = 0; i < SAS_GATE_DIM / 2; ++i) p.inv_freq[i] = pow(rope_theta, -(double)i / (SAS_GATE_DIM / 2));
+  return SAS_OK;
+}
+}  // namespace
+
+sas_status sas_gate_topk_ex(const sas_shape *shape, const void *q, const void *w_q, const float *w_qnorm,
+                            const void *gate_keys, const int32_t *block_table, const int32_t *seq_lens,
+                            double rope_theta, int32_t budget_tokens, int32_t aggregate, int32_t *sel, float *gates,
+                            int32_t *cnt, float *scores, void *stream) {
+  sas::GateParams p;
+  sas_status st = gate_params(shape, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, rope_theta, budget_tokens,
+                              aggregate, sel, gates, cnt, scores, false, p);
+  if (st) return st;
   return hip_status(sas::launch_gate_topk(p, shape->batch, (hipStream_t)stream), "sas_gate_topk launch");
 }
 
@@ -314,26 +329,24 @@ size_t sas_sparse_decode_workspace_bytes(const sas_shape *shape, int32_t max_sel
   return decode_workspace(shape, max_sel).total;
 }
 
-sas_status sas_sparse_decode_ex(const sas_shape *shape, const void *q, const void *k_pool, const void *v_pool,
-                                const int32_t *block_table, const int32_t *seq_lens, const int32_t *sel,
-                                const float *gates, int32_t gate_mode, const int32_t *cnt, int32_t max_sel,
-                                float sm_scale, void *out, void *workspace, size_t workspace_bytes, void *stream) {
+namespace {
+// Checks the attention arguments (not the workspace) and fills its
+// parameter block for max_sel selection slots per (sequence, KV head).
+sas_status decode_params(const sas_shape *shape, const void *q, const void *k_pool, const void *v_pool,
+                         const int32_t *block_table, const int32_t *seq_lens, const int32_t *sel, const float *gates,
+                         int32_t gate_mode, const int32_t *cnt, int32_t max_sel, float sm_scale, void *out,
+                         sas::DecodeParams &p) {
   sas_status st = check_shape(shape, true);
   if (st) return st;
   if (gate_mode != SAS_GATE_SCALE && gate_mode != SAS_GATE_LOGIT)
     return fail(SAS_ERR_INVALID_ARG, "unknown gate mode %d", gate_mode);
-  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !sel || !cnt || !out || !workspace)
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !sel || !cnt || !out)
     return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
   if (max_sel <= 0) return fail(SAS_ERR_INVALID_ARG, "max_sel must be positive");
   if (!(sm_scale > 0.f)) return fail(SAS_ERR_INVALID_ARG, "sm_scale must be positive");
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(workspace))
-    return fail(SAS_ERR_UNSUPPORTED, "q, k_pool, v_pool and workspace must be 16-byte aligned");
-  const size_t need = sas_sparse_decode_workspace_bytes(shape, max_sel);
-  if (workspace_bytes < need)
-    return fail(SAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
-  sas::DecodeSplit sp = sas::decode_split(shape->batch, shape->n_kv_heads, max_sel);
-  const DecodeWorkspace wl = decode_workspace(shape, max_sel);
-  sas::DecodeParams p;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(SAS_ERR_UNSUPPORTED, "q, k_pool and v_pool must be 16-byte aligned");
+  const sas::DecodeSplit sp = sas::decode_split(shape->batch, shape->n_kv_heads, max_sel);
   p.q = (const uint16_t *)q;
   p.k_pool = (const uint16_t *)k_pool;
   p.v_pool = (const uint16_t *)v_pool;
@@ -342,8 +355,8 @@ sas_status sas_sparse_decode_ex(const sas_shape *shape, const void *q, const voi
   p.sel = sel;
   p.cnt = cnt;
   p.gates = gates;
-  p.part_o = (float *)((char *)workspace + wl.part_o);
-  p.part_ml = (float *)((char *)workspace + wl.part_ml);
+  p.part_o = nullptr;
+  p.part_ml = nullptr;
   p.out = (uint16_t *)out;
   p.page_stride = shape->page_stride;
   p.tok_stride = shape->tok_stride;
@@ -357,6 +370,33 @@ sas_status sas_sparse_decode_ex(const sas_shape *shape, const void *q, const voi
   p.blocks_per_wave = sp.blocks_per_wave;
   p.gate_mode = gate_mode;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
+  return SAS_OK;
+}
+
+// Carves the partial-result buffers of a split decode out of the workspace.
+sas_status decode_workspace_bind(const sas_shape *shape, int32_t max_sel, void *workspace, size_t workspace_bytes,
+                                 sas::DecodeParams &p) {
+  if (!workspace) return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(workspace)) return fail(SAS_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  const DecodeWorkspace wl = decode_workspace(shape, max_sel);
+  if (workspace_bytes < wl.total)
+    return fail(SAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, wl.total);
+  p.part_o = (float *)((char *)workspace + wl.part_o);
+  p.part_ml = (float *)((char *)workspace + wl.part_ml);
+  return SAS_OK;
+}
+}  // namespace
+
+sas_status sas_sparse_decode_ex(const sas_shape *shape, const void *q, const void *k_pool, const void *v_pool,
+                                const int32_t *block_table, const int32_t *seq_lens, const int32_t *sel,
+                                const float *gates, int32_t gate_mode, const int32_t *cnt, int32_t max_sel,
+                                float sm_scale, void *out, void *workspace, size_t workspace_bytes, void *stream) {
+  sas::DecodeParams p;
+  sas_status st = decode_params(shape, q, k_pool, v_pool, block_table, seq_lens, sel, gates, gate_mode, cnt, max_sel,
+                                sm_scale, out, p);
+  if (st) return st;
+  st = decode_workspace_bind(shape, max_sel, workspace, workspace_bytes, p);
+  if (st) return st;
   return hip_status(sas::launch_decode(p, shape->batch, (hipStream_t)stream), "sas_sparse_decode launch");
 }
 
@@ -366,6 +406,71 @@ sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *
                              void *workspace, size_t workspace_bytes, void *stream) {
   return sas_sparse_decode_ex(shape, q, k_pool, v_pool, block_table, seq_lens, sel, gates, SAS_GATE_SCALE, cnt,
                               max_sel, sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+namespace {
+// The path a decode step takes: one fused launch, or the selection and the
+// attention as two launches (fewer (sequence, KV head) units than half the
+// CUs leave the fused kernel's one workgroup per unit short of parallelism;
+// the two-launch attention then splits each unit over several workgroups).
+bool step_fused(const sas_shape *shape, int32_t budget_tokens, int32_t path) {
+  const int n_sel = budget_tokens / SAS_BLOCK;
+  if (path == SAS_STEP_FUSED) return true;
+  if (path == SAS_STEP_TWO_LAUNCHES) return false;
+  return sas::step_fits(shape->n_q_heads / shape->n_kv_heads, shape->max_blocks, n_sel) &&
+         sas::decode_split(shape->batch, shape->n_kv_heads, n_sel).wg_per_unit == 1;
+}
+
+size_t step_scores_bytes(const sas_shape *shape) {
+  return align256((size_t)shape->batch * shape->n_kv_heads * shape->max_blocks * sizeof(float));
+}
+}  // namespace
+
+size_t sas_decode_step_workspace_bytes(const sas_shape *shape, int32_t budget_tokens, int32_t path) {
+  if (!shape || shape->batch <= 0 || shape->n_kv_heads <= 0 || shape->n_q_heads <= 0 || shape->max_blocks <= 0 ||
+      budget_tokens < SAS_BLOCK || shape->n_q_heads % shape->n_kv_heads)
+    return 0;
+  if (step_fused(shape, budget_tokens, path)) return 0;
+  // two launches: the attention's partials, then room for the scores when the caller passes none
+  return decode_workspace(shape, budget_tokens / SAS_BLOCK).total + step_scores_bytes(shape);
+}
+
+sas_status sas_decode_step(const sas_shape *shape, const void *q, const void *w_q, const float *w_qnorm,
+                           const void *gate_keys, const void *k_pool, const void *v_pool,
+                           const int32_t *block_table, const int32_t *seq_lens, double rope_theta,
+                           int32_t budget_tokens, int32_t aggregate, int32_t gated, int32_t gate_mode, float sm_scale,
+                           int32_t path, int32_t *sel, float *gates, int32_t *cnt, float *scores, void *out,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  if (path != SAS_STEP_AUTO && path != SAS_STEP_FUSED && path != SAS_STEP_TWO_LAUNCHES)
+    return fail(SAS_ERR_INVALID_ARG, "unknown step path %d", path);
+  if (gated != 0 && gated != 1) return fail(SAS_ERR_INVALID_ARG, "gated must be 0 or 1");
+  if (gated && !gates) return fail(SAS_ERR_INVALID_ARG, "gated attention needs the gates output");
+  sas::StepParams p;
+  sas_status st = gate_params(shape, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, rope_theta, budget_tokens,
+                              aggregate, sel, gates, cnt, scores, true, p.g);
+  if (st) return st;
+  const int32_t n_sel = budget_tokens / SAS_BLOCK;
+  st = decode_params(shape, q, k_pool, v_pool, block_table, seq_lens, sel, gated ? gates : nullptr, gate_mode, cnt,
+                     n_sel, sm_scale, out, p.d);
+  if (st) return st;
+  const hipStream_t hs = (hipStream_t)stream;
+  if (step_fused(shape, budget_tokens, path)) {
+    if (!sas::step_fits(p.g.group, shape->max_blocks, n_sel))
+      return fail(SAS_ERR_UNSUPPORTED, "shape outside the fused step's limits");
+    p.d.wg_per_unit = 1;  // one workgroup per (sequence, KV head)
+    p.d.blocks_per_wave = (n_sel + 7) / 8;
+    return hip_status(sas::launch_step(p, shape->batch, hs), "sas_decode_step launch");
+  }
+  const size_t need = sas_decode_step_workspace_bytes(shape, budget_tokens, path);
+  if (!workspace) return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (workspace_bytes < need)
+    return fail(SAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  st = decode_workspace_bind(shape, n_sel, workspace, workspace_bytes, p.d);
+  if (st) return st;
+  if (!p.g.scores) p.g.scores = (float *)((char *)workspace + (need - step_scores_bytes(shape)));
+  hipError_t e = sas::launch_gate_topk(p.g, shape->batch, hs);
+  if (e == hipSuccess) e = sas::launch_decode(p.d, shape->batch, hs);
+  return hip_status(e, "sas_decode_step launch");
 }
 
 namespace {

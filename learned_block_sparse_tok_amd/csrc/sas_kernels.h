@@ -70,6 +70,14 @@ struct DecodeSplit {
 };
 DecodeSplit decode_split(int batch, int n_kv_heads, int max_sel);
 
+// The fused decode step: the selection's and the attention's parameter blocks
+// (the attention with one workgroup per (sequence, KV head)).
+struct StepParams {
+  GateParams g;
+  DecodeParams d;
+};
+bool step_fits(int group, int max_blocks, int n_sel);
+
 struct PrefillParams {
   const uint16_t *q;            // [T][Hq][128]
   const uint16_t *k_pool, *v_pool;
@@ -128,5 +136,6 @@ hipError_t launch_prefill_attend(const PrefillParams &p, hipStream_t st);
 hipError_t launch_append(const AppendParams &p, int batch, hipStream_t st);
 hipError_t launch_gate_topk(const GateParams &p, int batch, hipStream_t st);
 hipError_t launch_decode(const DecodeParams &p, int batch, hipStream_t st);
+hipError_t launch_step(const StepParams &p, int batch, hipStream_t st);
 
 }  // namespace sas

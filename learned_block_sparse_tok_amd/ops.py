@@ -46,6 +46,9 @@ _SIGS = {
     "sas_gate_topk": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _F64, _I32, _VP, _VP, _VP, _VP, _VP]),
     "sas_sparse_decode_workspace_bytes": (_SZ, [_VP, _I32]),
     "sas_sparse_decode": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP, _VP, _SZ, _VP]),
+    "sas_decode_step_workspace_bytes": (_SZ, [_VP, _I32, _I32]),
+    "sas_decode_step": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F64, _I32, _I32, _I32, _I32, _F32, _I32,
+                               _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "sas_prefill_select": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _F64, _I32, _VP, _VP, _VP, _VP, _VP]),
     "sas_prefill_attend": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _F32, _VP, _VP]),
     "sas_gate_backward_workspace_bytes": (_SZ, [_VP, _I32]),
@@ -166,15 +169,43 @@ def sparse_decode(shape: SasShape, q, k_pool, v_pool, block_table, seq_lens, sel
     _check(st, "sas_sparse_decode")
 
 
+STEP_PATH = {"auto": 0, "fused": 1, "two_launches": 2}  # SAS_STEP_AUTO, SAS_STEP_FUSED, SAS_STEP_TWO_LAUNCHES
+
+
+def decode_step_workspace_bytes(shape: SasShape, budget_tokens: int, path="auto") -> int:
+    return int(lib().sas_decode_step_workspace_bytes(ctypes.byref(shape), int(budget_tokens), STEP_PATH[path]))
+
+
+def decode_step(shape: SasShape, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens, theta,
+                budget_tokens, sel, gates, cnt, scores, out, workspace, sm_scale, gated, stream=None,
+                aggregate="mean", gate_mode="scale", path="auto"):
+    """sas_decode_step: selection then attention in one call (one fused launch
+    on the "fused" path); gates / scores / workspace may be None where the
+    header allows."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().sas_decode_step(ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"), _ptr(w_q, torch.bfloat16, "w_q"),
+                               _ptr(w_qnorm, torch.float32, "w_qnorm"), _ptr(gate_keys, torch.bfloat16, "gate_keys"),
+                               _ptr(k_pool, torch.bfloat16, "k_pool"), _ptr(v_pool, torch.bfloat16, "v_pool"),
+                               _ptr(block_table, torch.int32, "block_table"), _ptr(seq_lens, torch.int32, "seq_lens"),
+                               float(theta), int(budget_tokens), AGGREGATE[aggregate], int(bool(gated)),
+                               GATE_MODE[gate_mode], float(sm_scale), STEP_PATH[path], _ptr(sel, torch.int32, "sel"),
+                               _ptr(gates, torch.float32, "gates"), _ptr(cnt, torch.int32, "cnt"),
+                               _ptr(scores, torch.float32, "scores"), _ptr(out, torch.bfloat16, "out"),
+                               _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream))
+    _check(st, "sas_decode_step")
+
+
 class SparseDecoder:
     """Holds the outputs and workspaces of one layer's decode step (allocated
-    once, by torch) and runs sas_gate_topk + sas_sparse_decode on them."""
+    once, by torch).  step() runs sas_decode_step on the given path ("auto":
+    one fused launch when there are enough (sequence, KV head) pairs to fill
+    the GPU); select() and attend() run sas_gate_topk and sas_sparse_decode."""
 
     def __init__(self, batch, n_q_heads, n_kv_heads, max_blocks, strides, budget, theta, gated,
-                 device="cuda", sm_scale=None, aggregate="mean", gate_mode="scale"):
+                 device="cuda", sm_scale=None, aggregate="mean", gate_mode="scale", path="auto"):
         self.shape = make_shape(batch, n_q_heads, n_kv_heads, max_blocks, strides)
         self.budget, self.theta, self.gated = budget, theta, gated
-        self.aggregate, self.gate_mode = aggregate, gate_mode
+        self.aggregate, self.gate_mode, self.path = aggregate, gate_mode, path
         self.n_sel = budget // BLOCK
         self.sm_scale = sm_scale if sm_scale is not None else 1.0 / math.sqrt(HEAD_DIM)
         dev = torch.device(device)
@@ -185,6 +216,8 @@ class SparseDecoder:
         self.out = torch.empty((batch, n_q_heads, HEAD_DIM), dtype=torch.bfloat16, device=dev)
         self.ws_dec = torch.empty(sparse_decode_workspace_bytes(self.shape, self.n_sel), dtype=torch.uint8,
                                   device=dev)
+        nws = decode_step_workspace_bytes(self.shape, budget, path)
+        self.ws_step = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
 
     def select(self, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, stream=None):
         gate_topk(self.shape, q, w_q, w_qnorm, gate_keys, block_table, seq_lens, self.theta, self.budget,
@@ -196,8 +229,9 @@ class SparseDecoder:
                       self.ws_dec, stream, gate_mode=self.gate_mode)
 
     def step(self, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens, stream=None):
-        self.select(q, w_q, w_qnorm, gate_keys, block_table, seq_lens, stream)
-        self.attend(q, k_pool, v_pool, block_table, seq_lens, stream)
+        decode_step(self.shape, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens, self.theta,
+                    self.budget, self.sel, self.gates, self.cnt, self.scores, self.out, self.ws_step, self.sm_scale,
+                    self.gated, stream, aggregate=self.aggregate, gate_mode=self.gate_mode, path=self.path)
         return self.out
 
 

@@ -32,10 +32,10 @@ def gpu_pool(w: wl.Workload, seq=None, blk=None) -> torch.Tensor:
     return gk
 
 
-def gpu_step(w: wl.Workload, gate_keys: torch.Tensor, gated: bool, budget: int | None = None):
+def gpu_step(w: wl.Workload, gate_keys: torch.Tensor, gated: bool, budget: int | None = None, path="auto"):
     budget = budget or w.budget
     dec = ops.SparseDecoder(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, budget, w.theta,
-                            gated, device=w.q.device)
+                            gated, device=w.q.device, path=path)
     dec.step(w.q, w.w_q, w.w_qnorm, gate_keys, w.k_pool, w.v_pool, w.block_table, w.seq_lens)
     torch.cuda.synchronize()
     return dict(sel=wl.host(dec.sel), gates=wl.host(dec.gates), cnt=wl.host(dec.cnt),

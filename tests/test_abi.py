@@ -81,6 +81,36 @@ def test_sparse_decode_rejects_bad_arguments(lib):
     assert _decode(lib, _shape(), ws_bytes=100) == ops.SAS_ERR_WORKSPACE
 
 
+def _step(lib, shape, path=0, gated=0, gates=FAKE, ws=FAKE, ws_bytes=1 << 24, budget=1024, aggregate=0):
+    return lib.sas_decode_step(ctypes.byref(shape), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1e6, budget,
+                               aggregate, gated, 0, 0.088, path, FAKE, gates, FAKE, None, FAKE, ws, ws_bytes, None)
+
+
+def test_decode_step_rejects_bad_arguments(lib):
+    sh = _shape()
+    assert _step(lib, sh, path=3) == ops.SAS_ERR_INVALID_ARG
+    assert _step(lib, sh, gated=2) == ops.SAS_ERR_INVALID_ARG
+    assert _step(lib, sh, gated=1, gates=None) == ops.SAS_ERR_INVALID_ARG
+    assert _step(lib, sh, budget=1000) == ops.SAS_ERR_INVALID_ARG
+    assert _step(lib, sh, aggregate=5) == ops.SAS_ERR_INVALID_ARG
+    assert _step(lib, _shape(strides=(0, 128, 8192))) == ops.SAS_ERR_INVALID_ARG
+    # the two-launch path (forced, or chosen for 4 (sequence, KV head) pairs) checks its workspace
+    assert _step(lib, sh, path=ops.STEP_PATH["two_launches"], ws_bytes=100) == ops.SAS_ERR_WORKSPACE
+    assert _step(lib, sh, path=ops.STEP_PATH["auto"], ws=None) == ops.SAS_ERR_INVALID_ARG
+
+
+def test_decode_step_workspace_bytes(lib):
+    small, big = _shape(), _shape(batch=32, n_q_heads=32, n_kv_heads=8)
+    for sh in (small, big):
+        assert ops.decode_step_workspace_bytes(sh, 2048, "fused") == 0
+        two = ops.decode_step_workspace_bytes(sh, 2048, "two_launches")
+        # the attention's partials plus room for the scores
+        assert two >= ops.sparse_decode_workspace_bytes(sh, 32) + sh.batch * sh.n_kv_heads * sh.max_blocks * 4
+    # automatic: 256 (sequence, KV head) pairs are fused, 4 are not
+    assert ops.decode_step_workspace_bytes(big, 2048, "auto") == 0
+    assert ops.decode_step_workspace_bytes(small, 2048, "auto") > 0
+
+
 def test_pool_rejects_bad_arguments_and_accepts_empty_list(lib):
     sh = _shape()
     assert lib.sas_pool_blocks(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, -1, FAKE, FAKE, 1e6, FAKE, None) == \

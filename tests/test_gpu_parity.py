@@ -329,14 +329,17 @@ def _step_workload(case):
     return w
 
 
+# "auto" takes the two launches for these few (sequence, KV head) pairs;
+# "fused" forces the one-launch step on them
+@pytest.mark.parametrize("path", ["auto", "fused"])
 @pytest.mark.parametrize("gated", [False, True], ids=["plain", "gated"])
 @pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: c["name"])
-def test_step_parity(case, gated):
-    say("step", case["name"], gated)
+def test_step_parity(case, gated, path):
+    say("step", case["name"], gated, path)
     w = _step_workload(case)
     h = Host(w)
     o = oracle_step(h, gated, case["budget"])
-    g = gpu_step(w, gpu_pool(w), gated, case["budget"])
+    g = gpu_step(w, gpu_pool(w), gated, case["budget"], path=path)
     ties, skipped = compare_step(h, g, o, gated, case["budget"])
     say(f"  ties {ties} (outputs of {skipped} not enumerated)")
     if w.planted is not None:
@@ -346,16 +349,81 @@ def test_step_parity(case, gated):
                 assert set(w.planted[s, k].tolist()) <= got
 
 
+# ------------------------------------------------------------------ fused step = two launches
+# More (sequence, KV head) pairs than half the CUs: both paths attend with
+# one workgroup per pair, so the fused launch must give the two launches'
+# bits exactly (its selection and attention run the same arithmetic in the
+# same order).  Ragged lengths cover an empty history (L <= 64), a selection
+# shorter than the budget, several 512-candidate score passes and the
+# largest budget.
+FUSED_CASES = [
+    dict(name="b17_ragged", lens=[1, 64, 65, 4097, 2048, 2049, 40000, 777, 12345, 3000, 130, 63, 8191, 8192, 33000,
+                                  5000, 600], Hq=32, Hkv=8, budget=2048, mb=630),
+    dict(name="b17_g5_b4096", lens=[70000, 1, 4096, 9000, 65, 30000, 2500, 128, 129, 60000, 7000, 500, 64, 20000,
+                                    3333, 1234, 16384], Hq=40, Hkv=8, budget=4096, mb=1100),
+    dict(name="b130_g1_b16384", lens=[100 + 811 * i for i in range(130)], Hq=1, Hkv=1, budget=16384, mb=1700),
+    dict(name="b129_g16", lens=[1 + 97 * i for i in range(129)], Hq=16, Hkv=1, budget=1024, mb=200),
+]
+FUSED_OPTS = [("mean", False, "scale"), ("mean", True, "scale"), ("mean", True, "logit"), ("max", True, "scale"),
+              ("max", False, "scale")]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: c["name"])
+def test_fused_step_equals_two_launches(case):
+    w = wl.make(len(case["lens"]), case["Hq"], case["Hkv"], case["lens"], case["budget"], "paged", 91, DEV,
+                max_blocks=case["mb"])
+    assert w.batch * w.n_kv_heads > 128
+    gk = gpu_pool(w)
+    args = (w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, w.block_table, w.seq_lens)
+    for aggregate, gated, gate_mode in FUSED_OPTS:
+        if aggregate == "max" and w.n_q_heads // w.n_kv_heads > 8:
+            continue
+        say("fused", case["name"], aggregate, gated, gate_mode)
+        res = {}
+        for path in ("two_launches", "fused"):
+            dec = ops.SparseDecoder(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, case["budget"],
+                                    w.theta, gated, device=DEV, aggregate=aggregate, gate_mode=gate_mode, path=path)
+            dec.sel.fill_(-7)
+            dec.gates.fill_(3.0)
+            dec.out.zero_()
+            dec.step(*args)
+            torch.cuda.synchronize()
+            res[path] = [t.clone() for t in (dec.sel, dec.gates, dec.cnt, dec.scores, dec.out)]
+        for name, a, b in zip(("sel", "gates", "cnt", "scores", "out"), res["two_launches"], res["fused"]):
+            assert torch.equal(a, b), name
+        cnt = wl.host(res["fused"][2])
+        assert cnt.min() >= 1 and cnt.max() <= case["budget"] // 64
+
+
+def test_fused_step_without_scores_or_gates():
+    # scores and (in plain mode) gates are optional outputs of the step
+    w = wl.make(17, 32, 8, [3000 + 500 * i for i in range(17)], 2048, "paged", 92, DEV, max_blocks=180)
+    gk = gpu_pool(w)
+    dec = ops.SparseDecoder(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, 2048, w.theta, False,
+                            device=DEV, path="fused")
+    dec.step(w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, w.block_table, w.seq_lens)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (dec.sel, dec.cnt, dec.out)]
+    sel, cnt, out = torch.full_like(dec.sel, -7), torch.zeros_like(dec.cnt), torch.zeros_like(dec.out)
+    ops.decode_step(dec.shape, w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, w.block_table, w.seq_lens, w.theta,
+                    2048, sel, None, cnt, None, out, None, dec.sm_scale, False, path="fused")
+    torch.cuda.synchronize()
+    for a, b in zip(ref, (sel, cnt, out)):
+        assert torch.equal(a, b)
+
+
 # ------------------------------------------------------------------ errors
 VARIANTS = [("max", "scale"), ("mean", "logit"), ("max", "logit")]
 
 
+@pytest.mark.parametrize("path", ["auto", "fused"])
 @pytest.mark.parametrize("aggregate,gate_mode", VARIANTS, ids=[f"{a}-{m}" for a, m in VARIANTS])
 @pytest.mark.parametrize("case", [STEP_CASES[0], STEP_CASES[4], STEP_CASES[5]], ids=lambda c: c["name"])
-def test_step_parity_alternative_readings(case, aggregate, gate_mode):
-    """sas_gate_topk_ex / sas_sparse_decode_ex (max-over-heads scores, gate as
-    a log-bias on the logits) against the oracle run with the same options."""
-    say("variant", case["name"], aggregate, gate_mode)
+def test_step_parity_alternative_readings(case, aggregate, gate_mode, path):
+    """The max-over-heads scores and the gate as a log-bias on the logits
+    (sas_decode_step's options, as in sas_gate_topk_ex / sas_sparse_decode_ex)
+    against the oracle run with the same options."""
+    say("variant", case["name"], aggregate, gate_mode, path)
     w = _step_workload(case)
     h = Host(w)
     gk_o = oracle_gate_keys(h)
@@ -365,7 +433,7 @@ def test_step_parity_alternative_readings(case, aggregate, gate_mode):
                         gate_mode=gate_mode)
     o = dict(gate_keys=gk_o, sel=sel, gates=gates, cnt=cnt, scores=scores, out=out)
     dec = ops.SparseDecoder(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, case["budget"], w.theta,
-                            True, device=DEV, aggregate=aggregate, gate_mode=gate_mode)
+                            True, device=DEV, aggregate=aggregate, gate_mode=gate_mode, path=path)
     dec.step(w.q, w.w_q, w.w_qnorm, gpu_pool(w), w.k_pool, w.v_pool, w.block_table, w.seq_lens)
     torch.cuda.synchronize()
     g = dict(sel=wl.host(dec.sel), gates=wl.host(dec.gates), cnt=wl.host(dec.cnt), scores=wl.host(dec.scores),
@@ -394,14 +462,15 @@ def test_invalid_arguments_raise():
 
 
 # ------------------------------------------------------------------ graphs, determinism
-def test_graph_replay_matches_eager():
-    # both calls captured into one HIP graph: every replay, with eager work and
+@pytest.mark.parametrize("path", ["two_launches", "fused"])
+def test_graph_replay_matches_eager(path):
+    # the step captured into one HIP graph: every replay, with eager work and
     # synchronisations in between, reproduces the eager result bit for bit
     w = wl.make(4, 32, 8, [8192, 5000, 3000, 8192], 2048, "paged", 81, DEV, max_blocks=128)
     gk = gpu_pool(w)
     for gated in (False, True):
         dec = ops.SparseDecoder(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, 2048, w.theta, gated,
-                                device=DEV)
+                                device=DEV, path=path)
         args = (w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, w.block_table, w.seq_lens)
         dec.step(*args)
         torch.cuda.synchronize()
