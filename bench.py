@@ -46,15 +46,27 @@ def gk_bytes_per_step(lens, n_kv_heads):
     return int(sum((int(L) - 1) // 64 for L in lens)) * n_kv_heads * 128 * 2
 
 
-def recorded_traffic(workload, budget):
-    """HBM bytes per decode launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE
-    runs recorded in profiles/ (scaled by a plain copy's reading), or None
-    when the workload differs or the decode kernel's sources changed since."""
+def step_extra_bytes(w, n_sel, gated):
+    """Bytes the fused step moves besides K/V and gate keys, each once: the
+    queries, Qproj rows, norm weights and block-table rows it reads; the
+    output, selection, gates, counts and scores it writes."""
+    B, Hq, Hkv = w.batch, w.n_q_heads, w.n_kv_heads
+    reads = B * Hq * 128 * 2 + Hq * 128 * 128 * 2 + 128 * 4 + B * w.max_blocks * 4
+    writes = B * Hq * 128 * 2 + B * Hkv * n_sel * 4 * (2 if gated else 1) + B * Hkv * 4 + B * Hkv * w.max_blocks * 4
+    return reads + writes
+
+
+def recorded_traffic(workload, budget, kernel):
+    """HBM bytes per launch of `kernel` from the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs recorded in profiles/ (scaled by a plain copy's reading),
+    or None when the workload or kernel differs or its sources changed since."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    path = os.path.join(ROOT, "profiles", "step_traffic.json")
     if workload != "qwen3_8b" or budget != 2048 or not os.path.exists(path):
         return None
     rec = json.load(open(path))
+    if rec["kernel"] != kernel:
+        return None
     h = hashlib.sha256()
     for f in rec["kernel_sources"]:
         h.update(open(os.path.join(ROOT, f), "rb").read())
@@ -551,8 +563,9 @@ def main():
         step_us = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)])
         p10, p50, p90 = (float(x) for x in np.percentile(step_us, [10, 50, 90]))
 
-        # the dominant call alone: sas_sparse_decode launched back to back on the
-        # current stream (selections from the steps above), bracketed by HIP events
+        # the attention alone: sas_sparse_decode (decode_kernel, the two-launch
+        # path's dominant kernel) launched back to back on the current stream
+        # (selections from the steps above), bracketed by HIP events
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for i in range(len(layers)):
             L = layers[i]
@@ -566,21 +579,38 @@ def main():
         ev1.record(stream)
         torch.cuda.synchronize()
         dec_ms = ev0.elapsed_time(ev1) / args.steps
+        fused = decs[0].ws_step is None  # the fused path needs no workspace
 
-        # algorithmic bytes: selected K+V blocks (decode) and every candidate's gate key (gate)
+        # algorithmic bytes: selected K+V blocks (attention), every candidate's
+        # gate key (selection), and, for the fused launch, the rest it moves once
         cnts = [wl.host(d.cnt) for d in decs]
         kv_b = float(np.mean([kv_bytes_per_step(c, 64 * 128 * 2) for c in cnts]))
         gk_b = float(np.mean([gk_bytes_per_step(wl.host(L["w"].seq_lens), w0.n_kv_heads) for L in layers]))
+        ex_b = float(step_extra_bytes(w0, args.budget // 64, gated))
         ms = elapsed * 1e3 / args.steps
+        # the dominant kernel: the fused step itself (one launch per step), else
+        # the attention
+        dom_ms = dec_ms
+        if fused:  # the step's one launch, back to back, bracketed by HIP events
+            ev0.record(stream)
+            for i in range(args.steps):
+                run_step(i)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            dom_ms = ev0.elapsed_time(ev1) / args.steps
+        dom_b = kv_b + gk_b + ex_b if fused else kv_b
         results[mode] = dict(queries_per_s=w0.batch * args.steps / elapsed, ms_per_step=ms,
                              decode_ms=dec_ms, decode_gbs=kv_b / (dec_ms * 1e-3) / 1e9,
-                             step_gbs=(kv_b + gk_b) / (ms * 1e-3) / 1e9, kv_bytes=kv_b, gk_bytes=gk_b,
+                             dominant_ms=dom_ms, dominant_bytes=dom_b, dominant_gbs=dom_b / (dom_ms * 1e-3) / 1e9,
+                             step_gbs=(kv_b + gk_b + ex_b) / (ms * 1e-3) / 1e9, kv_bytes=kv_b, gk_bytes=gk_b,
+                             other_bytes=ex_b,
                              attended_tokens_per_query=float(np.mean([c.sum() for c in cnts])) * 64 / (
                                  w0.batch * w0.n_kv_heads),
-                             step_us_p10=p10, step_us_p50=p50, step_us_p90=p90)
-        log(f"{mode}: {results[mode]['queries_per_s']:.0f} queries/s, {ms * 1e3:.1f} us/step, "
-            f"decode {dec_ms * 1e3:.1f} us = {results[mode]['decode_gbs']:.0f} GB/s, "
-            f"step {results[mode]['step_gbs']:.0f} GB/s; per-step p10/p50/p90 {p10:.1f}/{p50:.1f}/{p90:.1f} us")
+                             step_us_p10=p10, step_us_p50=p50, step_us_p90=p90, fused=float(fused))
+        log(f"{mode}: {results[mode]['queries_per_s']:.0f} queries/s, {ms * 1e3:.1f} us/step "
+            f"({'one fused launch' if fused else 'two launches'}), step {results[mode]['step_gbs']:.0f} GB/s; "
+            f"per-step p10/p50/p90 {p10:.1f}/{p50:.1f}/{p90:.1f} us; "
+            f"attention alone (decode_kernel) {dec_ms * 1e3:.1f} us = {results[mode]['decode_gbs']:.0f} GB/s")
 
     worst = min(results, key=lambda m: results[m]["queries_per_s"])
     r = results[worst]
@@ -601,12 +631,19 @@ def main():
                    "n_q_heads": w0.n_q_heads, "n_kv_heads": w0.n_kv_heads, "head_dim": 128,
                    "budget_tokens": args.budget, "kv_layout": w0.layout, "layers_rotated": len(layers),
                    "mode": f"{worst} (slower of {','.join(results)})",
-                   "launch": "hip graph per layer" if args.graph else "eager"},
-        "roofline": {"bound": "hbm", "kernel": "sas_sparse_decode (decode_kernel)",
-                     "achieved": round(r["decode_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(r["decode_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(args.workload, args.budget),
-                     "bytes_per_launch": r["kv_bytes"], "avg_launch_us": round(r["decode_ms"] * 1e3, 2)},
+                   "launch": "hip graph per layer" if args.graph else "eager",
+                   "path": "one fused launch" if r["fused"] else "two launches"},
+        "roofline": {"bound": "hbm",
+                     "kernel": ("sas_decode_step (step_kernel, one fused launch)" if r["fused"]
+                                else "sas_sparse_decode (decode_kernel)"),
+                     "achieved": round(r["dominant_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(r["dominant_gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(args.workload, args.budget,
+                                                 "step_kernel" if r["fused"] else "decode_kernel"),
+                     "bytes_per_launch": r["dominant_bytes"], "avg_launch_us": round(r["dominant_ms"] * 1e3, 2)},
+        "attention_alone": {"kernel": "sas_sparse_decode (decode_kernel)", "avg_launch_us": round(r["decode_ms"] * 1e3, 2),
+                            "bytes_per_launch": r["kv_bytes"], "achieved_gbs": round(r["decode_gbs"], 1),
+                            "frac": round(r["decode_gbs"] / HBM_PEAK_GBS, 4)},
         "step_hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
         "pooling": {"kernel": "sas_pool_blocks (pool_kernel), every complete block of a layer, off the step",
                     "ms_per_layer": round(pool_ms, 4), "bytes": pool_bytes,
