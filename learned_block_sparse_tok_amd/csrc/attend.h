@@ -162,6 +162,35 @@ struct BlockRef {
   float gate;
 };
 
+// This lane's byte offsets inside one (page, KV head) block.
+__device__ __forceinline__ LaneOffsets lane_offsets(const DecodeParams &p) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, j = lane & 15;
+  LaneOffsets lo;
+  lo.k = (uint32_t)((j * p.tok_stride + 8 * g) * 2);
+  lo.v = (uint32_t)((g * p.tok_stride + 8 * j) * 2);
+  lo.k_tile = 16 * p.tok_stride * 2;
+  lo.v_rows = 4 * p.tok_stride * 2;
+  return lo;
+}
+
+// K and V rows of a selected block of KV head kvh.
+__device__ __forceinline__ BlockSrc block_rows(const DecodeParams &p, int kvh, const BlockRef &r, int32_t L) {
+  const int64_t off = (int64_t)r.page * p.page_stride * 2 + (int64_t)kvh * p.head_stride * 2;
+  return BlockSrc{reinterpret_cast<const char *>(p.k_pool) + off, reinterpret_cast<const char *>(p.v_pool) + off,
+                  min(kBlock, L - r.blk * kBlock), r.gate};
+}
+
+// Issues a block's 32 loads into b, V rows first (the order they are consumed).
+__device__ __forceinline__ void issue_block(BlockRegs &b, const BlockSrc &cur, const LaneOffsets &lo) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) b.v[r] = ld16_kv<SAS_V_NT>(cur.v + r * lo.v_rows + lo.v);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) b.k[t][ks] = ld16_kv<SAS_K_NT>(cur.k + t * lo.k_tile + 64 * ks + lo.k);
+}
+
 // One workgroup's share of a (sequence s, KV head kvh) = unit: wave `wave`
 // attends the selected blocks [i0, min(count, i0 + blocks_per_wave)), the
 // waves merge in LDS (vlds: the waves' V tiles), and the workgroup writes the
@@ -171,7 +200,7 @@ struct BlockRef {
 template <int kMode, class Source>
 __device__ __forceinline__ void attend_unit(const DecodeParams &p, uint8_t (*vlds)[kVTileBytes], int s, int kvh,
                                             int unit, int wg, int wave, int i0, int count, int32_t L,
-                                            Source source) {
+                                            Source source, BlockRegs &b, bool first_issued) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, j = lane & 15;
   const int G = p.group;
@@ -182,13 +211,11 @@ __device__ __forceinline__ void attend_unit(const DecodeParams &p, uint8_t (*vld
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qB[ks] = as_bf16x8(j < G ? ld16(qrow + 32 * ks) : u32x4{0, 0, 0, 0});
   }
-  const BlockRef r0 = source(i0);
   const int i1 = min(count, i0 + p.blocks_per_wave);
-  LaneOffsets lo;
-  lo.k = (uint32_t)((j * p.tok_stride + 8 * g) * 2);
-  lo.v = (uint32_t)((g * p.tok_stride + 8 * j) * 2);
-  lo.k_tile = 16 * p.tok_stride * 2;
-  lo.v_rows = 4 * p.tok_stride * 2;
+  const bool local_first = i1 == count;
+  auto at = [&](int i) { return local_first ? (i == i0 ? count - 1 : i - 1) : i; };
+  const BlockRef r0 = source(at(i0));
+  const LaneOffsets lo = lane_offsets(p);
 
   WaveState ws;
 #pragma unroll
@@ -209,16 +236,10 @@ __device__ __forceinline__ void attend_unit(const DecodeParams &p, uint8_t (*vld
     // one register set: block i+1's loads are issued into it while block i is
     // consumed; the steady-state loop issues them unconditionally so that the
     // load counters wait for exactly the block being consumed
-    BlockRegs b;
     BlockSrc cur = rows(r0);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) b.v[r] = ld16_kv<SAS_V_NT>(cur.v + r * lo.v_rows + lo.v);
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) b.k[t][ks] = ld16_kv<SAS_K_NT>(cur.k + t * lo.k_tile + 64 * ks + lo.k);
+    if (!first_issued) issue_block(b, cur, lo);
     for (int i = i0; i + 1 < i1; ++i) {
-      const BlockSrc nxt = rows(source(i + 1));
+      const BlockSrc nxt = rows(source(at(i + 1)));
       attend_block<kMode, true>(ws, b, cur, nxt, qB, lo, vt, p.scale_log2, g, j, tr_e, tr_q);
       cur = nxt;
     }

@@ -53,8 +53,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
     const int blk = max(sel[i], 0);
     return BlockRef{bt[blk], blk, kMode ? gts[i] : 1.0f};
   };
+  BlockRegs b;
   attend_unit<kMode>(p, vlds, s, kvh, unit, wg, wave, (wg * kWaves + wave) * p.blocks_per_wave, p.cnt[unit],
-                     p.seq_lens[s], source);
+                     p.seq_lens[s], source, b, false);
 }
 
 // Merge the wg_per_unit partials of each (sequence, KV head) into the bf16

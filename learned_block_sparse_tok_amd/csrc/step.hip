@@ -217,6 +217,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(StepParams sp) {
     for (int c = n + t; c < p.max_blocks; c += 512) scores[c] = -__builtin_inff();
   lds_barrier();
 
+  // the local block is selected whatever the scores: the wave whose share of
+  // the selection ends with it (and takes it first) issues its K/V loads now,
+  // so that they arrive while wave 0 selects
+  const int bpw = sp.d.blocks_per_wave;
+  const bool prefetch = wave == k_eff / bpw;
+  BlockRegs b;
+  if (prefetch) issue_block(b, block_rows(sp.d, kvh, BlockRef{btl[n], n, 1.0f}, L), lane_offsets(sp.d));
+
   // ---- 4. wave 0 selects; the selection, pages and gates stay in LDS
   if (wave == 0) {
     wave_select(keys, n, k_eff, p.n_sel, hist, p.sel + (int64_t)unit * p.n_sel,
@@ -236,7 +244,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(StepParams sp) {
     return BlockRef{__builtin_amdgcn_readfirstlane(page_l[i]), __builtin_amdgcn_readfirstlane(sel_l[i]),
                     kMode ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gate_l[i]))) : 1.0f};
   };
-  attend_unit<kMode>(sp.d, vlds, s, kvh, unit, 0, wave, wave * sp.d.blocks_per_wave, k_eff + 1, L, source);
+  attend_unit<kMode>(sp.d, vlds, s, kvh, unit, 0, wave, wave * bpw, k_eff + 1, L, source, b, prefetch);
 }
 
 bool step_fits(int group, int max_blocks, int n_sel) {
