@@ -17,20 +17,18 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
-// Writes the selection of one (sequence or position, KV head): the k_eff
-// best of the n candidate keys keys[0 .. n) under (score descending, index
-// ascending), in ascending block order, then the local block n; padding -1
-// up to n_sel; gates (nullable) = sigmoid(score) for the chosen historical
-// blocks, 1 for the local block, 0 padding; *cnt = k_eff + 1.
-//   keys: LDS, 16-byte aligned, readable up to max(n, 512) entries (keys are
-//   > 0; entries past n are ignored); hist: this wave's 256-entry LDS
-//   histogram, which afterwards holds the compacted selection (n_sel <= 256).
-//   Radix select over 8-bit digits with a wave-private histogram and DPP
-//   prefix sums; keys > T are taken, and the krem lowest-index keys equal to
-//   T.  Lane l sweeps keys [512k + 8l, 512k + 8l + 8); the first 512 stay in
-//   registers across the passes.
-__device__ __forceinline__ void wave_select(const uint32_t *keys, int n, int k_eff, int n_sel, uint32_t *hist,
-                                            int32_t *sel, float *gates, int32_t *cnt_out) {
+// Exact Top-K of the n candidate keys keys[0 .. n) of one (sequence or
+// position, KV head) under (score descending, index ascending): calls
+// emit(pos, c, key) for the k_eff chosen candidates c, pos = 0 .. k_eff-1 in
+// ascending c.  keys: LDS, 16-byte aligned, readable up to max(n, 512)
+// entries (keys are > 0; entries past n are ignored); hist: this wave's
+// 256-entry LDS histogram.  Radix select over 8-bit digits with a
+// wave-private histogram and DPP prefix sums; keys > T are taken, and the
+// krem lowest-index keys equal to T.  Lane l sweeps keys
+// [512k + 8l, 512k + 8l + 8); the first 512 stay in registers across the
+// passes.
+template <class Emit>
+__device__ __forceinline__ void wave_select_emit(const uint32_t *keys, int n, int k_eff, uint32_t *hist, Emit emit) {
   const int lane = threadIdx.x & 63;
   uint32_t k0[8];  // keys 8l .. 8l+7 (0 past the candidates: keys are > 0)
   {
@@ -96,8 +94,8 @@ __device__ __forceinline__ void wave_select(const uint32_t *keys, int n, int k_e
       __builtin_amdgcn_wave_barrier();
     }
   }
-  // the selected candidates' indices, compacted in ascending order into the
-  // (now free) histogram, then written out with one coalesced store per lane
+  // the chosen candidates in ascending order, each with its rank among them
+  // (a prefix count over the sweep), handed to emit
   if (k_eff > 0) {
     uint32_t pos_base = 0, eq_base = 0;
     for (int c0 = 0; c0 < n; c0 += 512) {
@@ -123,13 +121,25 @@ __device__ __forceinline__ void wave_select(const uint32_t *keys, int n, int k_e
       uint32_t pos = pos_base + take_incl - n_take;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (take_mask >> e & 1u) hist[pos++] = (uint32_t)(cl + e);
+        if (take_mask >> e & 1u) emit(pos++, cl + e, kk[e]);
       pos_base += (uint32_t)__builtin_amdgcn_readlane((int)take_incl, 63);
       eq_base += (uint32_t)__builtin_amdgcn_readlane((int)eq_incl, 63);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+// Writes the selection of one (sequence or position, KV head): the k_eff
+// best candidates (wave_select_emit) in ascending block order, then the
+// local block n; padding -1 up to n_sel; gates (nullable) = sigmoid(score)
+// for the chosen historical blocks, 1 for the local block, 0 padding;
+// *cnt = k_eff + 1.  hist afterwards holds the compacted selection
+// (n_sel <= 256).
+__device__ __forceinline__ void wave_select(const uint32_t *keys, int n, int k_eff, int n_sel, uint32_t *hist,
+                                            int32_t *sel, float *gates, int32_t *cnt_out) {
+  const int lane = threadIdx.x & 63;
+  wave_select_emit(keys, n, k_eff, hist, [&](uint32_t pos, int c, uint32_t) { hist[pos] = (uint32_t)c; });
   for (int i = lane; i < n_sel; i += 64) {
     int32_t c;
     float g;

@@ -24,7 +24,8 @@
 //   3. scores (one row sum per key, finished by lane 0 of its group, so that
 //      equal keys get equal scores) become order-preserving keys in LDS;
 //   4. wave 0 selects (radix select, ascending order, lowest index at the
-//      threshold) and leaves the selection, pages and gates in LDS;
+//      threshold) straight into LDS arrays of the selection, pages and
+//      gates; the last wave stores the selection outputs from there;
 //   5. the 8 waves attend the selection exactly as the decode kernel does
 //      (its V tiles reuse the LDS the gate phase held).
 #include "attend.h"
@@ -225,18 +226,30 @@ __global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(StepParams sp) {
   BlockRegs b;
   if (prefetch) issue_block(b, block_rows(sp.d, kvh, BlockRef{btl[n], n, 1.0f}, L), lane_offsets(sp.d));
 
-  // ---- 4. wave 0 selects; the selection, pages and gates stay in LDS
+  // ---- 4. wave 0 selects straight into the LDS selection, pages and gates
   if (wave == 0) {
-    wave_select(keys, n, k_eff, p.n_sel, hist, p.sel + (int64_t)unit * p.n_sel,
-                p.gates ? p.gates + (int64_t)unit * p.n_sel : nullptr, p.cnt + unit);
-    for (int i = lane; i <= k_eff; i += 64) {
-      const int c = i < k_eff ? (int)hist[i] : n;
-      sel_l[i] = c;
-      page_l[i] = btl[c];
-      gate_l[i] = i < k_eff ? 1.0f / (1.0f + __expf(-key_score(keys[c]))) : 1.0f;
+    wave_select_emit(keys, n, k_eff, hist, [&](uint32_t pos, int c, uint32_t key) {
+      sel_l[pos] = c;
+      page_l[pos] = btl[c];
+      gate_l[pos] = 1.0f / (1.0f + __expf(-key_score(key)));
+    });
+    if (lane == 0) {  // the local block closes the selection
+      sel_l[k_eff] = n;
+      page_l[k_eff] = btl[n];
+      gate_l[k_eff] = 1.0f;
     }
   }
   lds_barrier();
+  if (wave == kWaves - 1) {  // the selection's outputs, from the LDS arrays (the V tiles overwrite the keys)
+    int32_t *sel = p.sel + (int64_t)unit * p.n_sel;
+    float *gates = p.gates ? p.gates + (int64_t)unit * p.n_sel : nullptr;
+    for (int i = lane; i < p.n_sel; i += 64) {
+      const bool in = i <= k_eff;
+      sel[i] = in ? sel_l[i] : -1;
+      if (gates) gates[i] = in ? gate_l[i] : 0.0f;
+    }
+    if (lane == 0) p.cnt[unit] = k_eff + 1;
+  }
 
   // ---- 5. attention over the selection (the V tiles now overwrite the gate phase's LDS)
   auto source = [&](int i) {
