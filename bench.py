@@ -418,7 +418,8 @@ def run_serve(args):
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": 128, "budget_tokens": budget,
                    "kv_layout": w.layout, "mode": f"{worst} (slower of {','.join(results)})", "launch": "eager"},
         "step_hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
-        "modes": {m: {k: round(v, 3) for k, v in d.items()} for m, d in results.items()},
+        "modes": {m: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in d.items()}
+                  for m, d in results.items()},
     }
     print(json.dumps(line), flush=True)
 
@@ -439,7 +440,7 @@ def main():
                          "known traffic, for calibrating the HBM byte counters), then exit")
     ap.add_argument("--backward", action="store_true",
                     help="also time sas_gate_backward after the gated step (prints a second JSON line)")
-    ap.add_argument("--path", default="auto", choices=["auto", "fused", "two_launches"],
+    ap.add_argument("--path", default="auto", choices=["auto", "fused", "sliced", "two_launches"],
                     help="sas_decode_step path (auto: one fused launch when the pairs fill the GPU)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each layer's step from a HIP graph instead of launching it eagerly "
@@ -580,6 +581,9 @@ def main():
         torch.cuda.synchronize()
         dec_ms = ev0.elapsed_time(ev1) / args.steps
         fused = decs[0].ws_step is None  # the fused path needs no workspace
+        path_name = "one fused launch" if fused else ("sliced selection" if ops.decode_step_workspace_bytes(
+            decs[0].shape, args.budget, args.path) == ops.decode_step_workspace_bytes(decs[0].shape, args.budget,
+                                                                                     "sliced") else "two launches")
 
         # algorithmic bytes: selected K+V blocks (attention), every candidate's
         # gate key (selection), and, for the fused launch, the rest it moves once
@@ -606,9 +610,10 @@ def main():
                              other_bytes=ex_b,
                              attended_tokens_per_query=float(np.mean([c.sum() for c in cnts])) * 64 / (
                                  w0.batch * w0.n_kv_heads),
-                             step_us_p10=p10, step_us_p50=p50, step_us_p90=p90, fused=float(fused))
+                             step_us_p10=p10, step_us_p50=p50, step_us_p90=p90, fused=float(fused),
+                             path=path_name)
         log(f"{mode}: {results[mode]['queries_per_s']:.0f} queries/s, {ms * 1e3:.1f} us/step "
-            f"({'one fused launch' if fused else 'two launches'}), step {results[mode]['step_gbs']:.0f} GB/s; "
+            f"({path_name}), step {results[mode]['step_gbs']:.0f} GB/s; "
             f"per-step p10/p50/p90 {p10:.1f}/{p50:.1f}/{p90:.1f} us; "
             f"attention alone (decode_kernel) {dec_ms * 1e3:.1f} us = {results[mode]['decode_gbs']:.0f} GB/s")
 
@@ -632,7 +637,7 @@ def main():
                    "budget_tokens": args.budget, "kv_layout": w0.layout, "layers_rotated": len(layers),
                    "mode": f"{worst} (slower of {','.join(results)})",
                    "launch": "hip graph per layer" if args.graph else "eager",
-                   "path": "one fused launch" if r["fused"] else "two launches"},
+                   "path": r["path"]},
         "roofline": {"bound": "hbm",
                      "kernel": ("sas_decode_step (step_kernel, one fused launch)" if r["fused"]
                                 else "sas_sparse_decode (decode_kernel)"),
@@ -651,7 +656,8 @@ def main():
                     "frac": round(pool_bytes / (pool_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "tokens_per_s": round(r["queries_per_s"], 1),
         "attended_kv_tokens_per_s": round(r["queries_per_s"] * r["attended_tokens_per_query"], 1),
-        "modes": {m: {k: round(v, 3) for k, v in d.items()} for m, d in results.items()},
+        "modes": {m: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in d.items()}
+                  for m, d in results.items()},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layers[0], args.budget, worst == "gated", args.cpu_seconds)

@@ -221,13 +221,19 @@ sas_status sas_sparse_decode_ex(const sas_shape *shape, const void *q, const voi
  * within the token budget; aigc.news release note, "Tencent Hunyuan
  * open-sources SAS ...").
  *
- * With path SAS_STEP_FUSED it is one kernel launch: each (sequence, KV head)
- * is scored, selected and attended by one workgroup, which keeps the
- * selection and the selected blocks' pages on chip.  SAS_STEP_TWO_LAUNCHES
- * runs the two calls' kernels.  SAS_STEP_AUTO fuses when there are more
- * (sequence, KV head) pairs than half the GPU's 256 compute units (then both
- * paths give the same bits), and launches twice otherwise, where the
- * attention spreads each pair over several workgroups.
+ * Paths (all give the same selection; fused and two-launch outputs are the
+ * same bits whenever the attention runs one workgroup per pair):
+ *   SAS_STEP_FUSED  one kernel launch: each (sequence, KV head) is scored,
+ *                   selected and attended by one workgroup, which keeps the
+ *                   selection and the selected blocks' pages on chip;
+ *   SAS_STEP_SLICED for few pairs: each pair's candidates are scored and
+ *                   reduced to a Top-K list by several workgroups (slices),
+ *                   then one launch merges the lists into the selection and
+ *                   attends with each pair split over several workgroups;
+ *   SAS_STEP_TWO_LAUNCHES  the kernels of the two calls above;
+ *   SAS_STEP_AUTO   fused when there are more (sequence, KV head) pairs than
+ *                   half the GPU's 256 compute units; otherwise sliced for
+ *                   block tables over 1,024 blocks, else two launches.
  *
  * Arguments as for the two calls, with max_sel = budget_tokens / 64:
  *   aggregate  SAS_AGG_MEAN or SAS_AGG_MAX
@@ -237,12 +243,14 @@ sas_status sas_sparse_decode_ex(const sas_shape *shape, const void *q, const voi
  *   scores     written when non-NULL (nullable)
  *   sel, cnt, out  required
  * workspace: at least sas_decode_step_workspace_bytes(shape, budget_tokens,
- * path) bytes (0 on the fused path, where workspace may be NULL); no initial
- * contents needed; calls that overlap in time must not share one.
+ * path) bytes (0 on the fused path, where workspace may be NULL; 0 also for
+ * an unknown path); no initial contents needed; calls that overlap in time
+ * must not share one.
  */
 #define SAS_STEP_AUTO 0
 #define SAS_STEP_FUSED 1
 #define SAS_STEP_TWO_LAUNCHES 2
+#define SAS_STEP_SLICED 3
 size_t sas_decode_step_workspace_bytes(const sas_shape *shape, int32_t budget_tokens, int32_t path);
 sas_status sas_decode_step(const sas_shape *shape, const void *q, const void *w_q,
                            const float *w_qnorm, const void *gate_keys, const void *k_pool,

@@ -409,20 +409,45 @@ sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *
 }
 
 namespace {
-// The path a decode step takes: one fused launch, or the selection and the
-// attention as two launches (fewer (sequence, KV head) units than half the
-// CUs leave the fused kernel's one workgroup per unit short of parallelism;
-// the two-launch attention then splits each unit over several workgroups).
-bool step_fused(const sas_shape *shape, int32_t budget_tokens, int32_t path) {
+// The path a decode step takes.  One fused launch when there are more
+// (sequence, KV head) pairs than half the CUs.  With fewer pairs the
+// attention splits each pair over several workgroups, and the selection
+// either runs one workgroup per pair (sas_gate_topk's kernel) or, for block
+// tables over 1,024 blocks (where one workgroup would score in several
+// passes of 512 candidates), splits each pair's candidates over several
+// workgroups (sliced selection: gate queries, slices, then one launch that
+// merges the slices' lists and attends).
+int step_path(const sas_shape *shape, int32_t budget_tokens, int32_t path) {
+  if (path != SAS_STEP_AUTO) return path;
   const int n_sel = budget_tokens / SAS_BLOCK;
-  if (path == SAS_STEP_FUSED) return true;
-  if (path == SAS_STEP_TWO_LAUNCHES) return false;
-  return sas::step_fits(shape->n_q_heads / shape->n_kv_heads, shape->max_blocks, n_sel) &&
-         sas::decode_split(shape->batch, shape->n_kv_heads, n_sel).wg_per_unit == 1;
+  const bool fits = sas::step_fits(shape->n_q_heads / shape->n_kv_heads, shape->max_blocks, n_sel);
+  if (fits && sas::decode_split(shape->batch, shape->n_kv_heads, n_sel).wg_per_unit == 1) return SAS_STEP_FUSED;
+  return fits && shape->max_blocks > 1024 ? SAS_STEP_SLICED : SAS_STEP_TWO_LAUNCHES;
 }
 
-size_t step_scores_bytes(const sas_shape *shape) {
-  return align256((size_t)shape->batch * shape->n_kv_heads * shape->max_blocks * sizeof(float));
+struct StepWorkspace {
+  size_t part_o, part_ml, scores, gq, cand_key, cand_blk, cand_page, total;  // byte offsets and size
+};
+StepWorkspace step_workspace(const sas_shape *shape, int32_t budget_tokens, int path) {
+  StepWorkspace w{};
+  if (path == SAS_STEP_FUSED) return w;
+  const int n_sel = budget_tokens / SAS_BLOCK;
+  const DecodeWorkspace d = decode_workspace(shape, n_sel);
+  w.part_o = d.part_o;
+  w.part_ml = d.part_ml;
+  w.scores = d.total;  // room for the scores when the caller passes none
+  w.total = w.scores + align256((size_t)shape->batch * shape->n_kv_heads * shape->max_blocks * sizeof(float));
+  if (path == SAS_STEP_SLICED) {
+    int slices, slice_len;
+    sas::gate_slice_layout(shape->batch, shape->n_kv_heads, shape->max_blocks, &slices, &slice_len);
+    const size_t entries = (size_t)shape->batch * shape->n_kv_heads * slices * n_sel;
+    w.gq = w.total;
+    w.cand_key = w.gq + align256((size_t)shape->batch * shape->n_q_heads * SAS_GATE_DIM * sizeof(float));
+    w.cand_blk = w.cand_key + align256(entries * sizeof(uint32_t));
+    w.cand_page = w.cand_blk + align256(entries * sizeof(int32_t));
+    w.total = w.cand_page + align256(entries * sizeof(int32_t));
+  }
+  return w;
 }
 }  // namespace
 
@@ -430,9 +455,8 @@ size_t sas_decode_step_workspace_bytes(const sas_shape *shape, int32_t budget_to
   if (!shape || shape->batch <= 0 || shape->n_kv_heads <= 0 || shape->n_q_heads <= 0 || shape->max_blocks <= 0 ||
       budget_tokens < SAS_BLOCK || shape->n_q_heads % shape->n_kv_heads)
     return 0;
-  if (step_fused(shape, budget_tokens, path)) return 0;
-  // two launches: the attention's partials, then room for the scores when the caller passes none
-  return decode_workspace(shape, budget_tokens / SAS_BLOCK).total + step_scores_bytes(shape);
+  if (path < SAS_STEP_AUTO || path > SAS_STEP_SLICED) return 0;
+  return step_workspace(shape, budget_tokens, step_path(shape, budget_tokens, path)).total;
 }
 
 sas_status sas_decode_step(const sas_shape *shape, const void *q, const void *w_q, const float *w_qnorm,
@@ -441,8 +465,7 @@ sas_status sas_decode_step(const sas_shape *shape, const void *q, const void *w_
                            int32_t budget_tokens, int32_t aggregate, int32_t gated, int32_t gate_mode, float sm_scale,
                            int32_t path, int32_t *sel, float *gates, int32_t *cnt, float *scores, void *out,
                            void *workspace, size_t workspace_bytes, void *stream) {
-  if (path != SAS_STEP_AUTO && path != SAS_STEP_FUSED && path != SAS_STEP_TWO_LAUNCHES)
-    return fail(SAS_ERR_INVALID_ARG, "unknown step path %d", path);
+  if (path < SAS_STEP_AUTO || path > SAS_STEP_SLICED) return fail(SAS_ERR_INVALID_ARG, "unknown step path %d", path);
   if (gated != 0 && gated != 1) return fail(SAS_ERR_INVALID_ARG, "gated must be 0 or 1");
   if (gated && !gates) return fail(SAS_ERR_INVALID_ARG, "gated attention needs the gates output");
   sas::StepParams p;
@@ -454,22 +477,39 @@ sas_status sas_decode_step(const sas_shape *shape, const void *q, const void *w_
                      n_sel, sm_scale, out, p.d);
   if (st) return st;
   const hipStream_t hs = (hipStream_t)stream;
-  if (step_fused(shape, budget_tokens, path)) {
-    if (!sas::step_fits(p.g.group, shape->max_blocks, n_sel))
-      return fail(SAS_ERR_UNSUPPORTED, "shape outside the fused step's limits");
+  const int how = step_path(shape, budget_tokens, path);
+  if (how != SAS_STEP_TWO_LAUNCHES && !sas::step_fits(p.g.group, shape->max_blocks, n_sel))
+    return fail(SAS_ERR_UNSUPPORTED, "shape outside the one-workgroup selection's limits");
+  if (how == SAS_STEP_FUSED) {
     p.d.wg_per_unit = 1;  // one workgroup per (sequence, KV head)
     p.d.blocks_per_wave = (n_sel + 7) / 8;
     return hip_status(sas::launch_step(p, shape->batch, hs), "sas_decode_step launch");
   }
-  const size_t need = sas_decode_step_workspace_bytes(shape, budget_tokens, path);
+  const StepWorkspace wl = step_workspace(shape, budget_tokens, how);
   if (!workspace) return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (workspace_bytes < need)
-    return fail(SAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
-  st = decode_workspace_bind(shape, n_sel, workspace, workspace_bytes, p.d);
-  if (st) return st;
-  if (!p.g.scores) p.g.scores = (float *)((char *)workspace + (need - step_scores_bytes(shape)));
-  hipError_t e = sas::launch_gate_topk(p.g, shape->batch, hs);
-  if (e == hipSuccess) e = sas::launch_decode(p.d, shape->batch, hs);
+  if (!aligned16(workspace)) return fail(SAS_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  if (workspace_bytes < wl.total)
+    return fail(SAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, wl.total);
+  char *ws = (char *)workspace;
+  p.d.part_o = (float *)(ws + wl.part_o);
+  p.d.part_ml = (float *)(ws + wl.part_ml);
+  if (!p.g.scores) p.g.scores = (float *)(ws + wl.scores);
+  hipError_t e;
+  if (how == SAS_STEP_SLICED) {
+    sas::gate_slice_layout(shape->batch, shape->n_kv_heads, shape->max_blocks, &p.g.slices, &p.g.slice_len);
+    p.g.slot_len = ((p.g.slice_len > 512 ? p.g.slice_len : 512) + 7) / 8 * 8;
+    p.g.batch = shape->batch;
+    p.g.gq = (float *)(ws + wl.gq);
+    p.g.cand_key = (uint32_t *)(ws + wl.cand_key);
+    p.g.cand_blk = (int32_t *)(ws + wl.cand_blk);
+    p.g.cand_page = (int32_t *)(ws + wl.cand_page);
+    e = sas::launch_gate_query(p.g, hs);
+    if (e == hipSuccess) e = sas::launch_gate_slices(p.g, shape->batch, hs);
+    if (e == hipSuccess) e = sas::launch_select_decode(p, shape->batch, hs);
+  } else {
+    e = sas::launch_gate_topk(p.g, shape->batch, hs);
+    if (e == hipSuccess) e = sas::launch_decode(p.d, shape->batch, hs);
+  }
   return hip_status(e, "sas_decode_step launch");
 }
 

@@ -61,6 +61,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_kernel(DecodeParams p) 
 // Merge the wg_per_unit partials of each (sequence, KV head) into the bf16
 // output (only launched when a unit spans several workgroups; the kernel
 // boundary orders the partial writes before these reads).
+// kW >= wg_per_unit: every partial's (max, sum, output) is loaded before any
+// is used (unconditional loads, the slots past wg_per_unit clamped to the
+// last one and ignored), so the merge costs one round trip to memory, not
+// one per partial.
+constexpr int kMaxWgPerUnit = 32;
+
+template <int kW>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   const int unit = blockIdx.x;
   const int s = unit / p.n_kv_heads;
@@ -70,16 +77,25 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   const int64_t ubase = (int64_t)unit * nwg * G;
   for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256) {
     const int jj = idx >> 7, d = idx & (kHeadDim - 1);
+    float mw[kW], lw[kW], ow[kW];
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+      const int64_t slot = ubase + (int64_t)min(w, nwg - 1) * G + jj;
+      mw[w] = p.part_ml[slot * 2];
+      lw[w] = p.part_ml[slot * 2 + 1];
+      ow[w] = p.part_o[slot * kHeadDim + d];
+    }
     float M = -__builtin_inff();
-    for (int w = 0; w < nwg; ++w) M = fmaxf(M, p.part_ml[(ubase + (int64_t)w * G + jj) * 2]);
+#pragma unroll
+    for (int w = 0; w < kW; ++w)
+      if (w < nwg) M = fmaxf(M, mw[w]);
     float num = 0.f, den = 0.f;
-    for (int w = 0; w < nwg; ++w) {
-      const int64_t slot = ubase + (int64_t)w * G + jj;
-      const float mw = p.part_ml[slot * 2];
-      if (mw == -__builtin_inff()) continue;
-      const float f = exp2f(mw - M);
-      den = fmaf(f, p.part_ml[slot * 2 + 1], den);
-      num = fmaf(f, p.part_o[slot * kHeadDim + d], num);
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+      if (w >= nwg || mw[w] == -__builtin_inff()) continue;
+      const float f = exp2f(mw[w] - M);
+      den = fmaf(f, lw[w], den);
+      num = fmaf(f, ow[w], num);
     }
     p.out[((int64_t)s * p.n_q_heads + kvh * G + jj) * kHeadDim + d] = (uint16_t)f32_to_bf16(num / den);
   }
@@ -93,9 +109,19 @@ DecodeSplit decode_split(int batch, int n_kv_heads, int max_sel) {
   int wg = cus / units;
   const int max_wg = (max_sel + kWaves - 1) / kWaves;  // >= 1 block per wave
   wg = wg > max_wg ? max_wg : wg;
+  wg = wg > kMaxWgPerUnit ? kMaxWgPerUnit : wg;  // the merge kernel's largest instance
   wg = wg < 1 ? 1 : wg;
   const int waves = wg * kWaves;
   return DecodeSplit{wg, waves, (max_sel + waves - 1) / waves};
+}
+
+hipError_t launch_decode_merge(const DecodeParams &p, int batch, hipStream_t st) {
+  const dim3 grid((unsigned)(batch * p.n_kv_heads));
+  if (p.wg_per_unit <= 4) hipLaunchKernelGGL((decode_merge_kernel<4>), grid, dim3(256), 0, st, p);
+  else if (p.wg_per_unit <= 8) hipLaunchKernelGGL((decode_merge_kernel<8>), grid, dim3(256), 0, st, p);
+  else if (p.wg_per_unit <= 16) hipLaunchKernelGGL((decode_merge_kernel<16>), grid, dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((decode_merge_kernel<32>), grid, dim3(256), 0, st, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeParams &p, int batch, hipStream_t st) {
@@ -109,8 +135,7 @@ hipError_t launch_decode(const DecodeParams &p, int batch, hipStream_t st) {
     hipLaunchKernelGGL((decode_kernel<2>), grid, dim3(kWaves * 64), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.wg_per_unit == 1) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(units), dim3(256), 0, st, p);
-  return hipGetLastError();
+  return launch_decode_merge(p, batch, st);
 }
 
 }  // namespace sas

@@ -45,6 +45,13 @@ struct GateParams {
   int32_t n_q_heads, n_kv_heads, group, max_blocks, n_sel;
   int32_t bt_row_stride;    // max_blocks, or 0 when every entry shares one block-table row
   int32_t aggregate;        // 0: mean of the group's per-head scores, 1: their maximum (group <= 8)
+  // sliced selection (launch_gate_slices): each pair's candidates in `slices`
+  // slices of slice_len; per (pair, slice) n_sel entries of the slice's
+  // Top-K (score key, 0 = padding; block; page); slot_len = LDS rows per slice
+  int32_t slices, slice_len, slot_len, batch;
+  float *gq;                // [B][Hq][128] rotated gate queries (gate_query_kernel)
+  uint32_t *cand_key;
+  int32_t *cand_blk, *cand_page;
   double inv_freq[kGateDim / 2];  // rope_theta^(-i/64)
 };
 
@@ -77,6 +84,11 @@ struct StepParams {
   DecodeParams d;
 };
 bool step_fits(int group, int max_blocks, int n_sel);
+
+constexpr int kMaxSlices = 16;  // slices of one pair's candidates in the sliced selection
+// Slices per pair and their length for the sliced selection; every slice
+// starts inside the block-table row ((slices - 1) * slice_len < max_blocks).
+void gate_slice_layout(int batch, int n_kv_heads, int max_blocks, int *slices, int *slice_len);
 
 struct PrefillParams {
   const uint16_t *q;            // [T][Hq][128]
@@ -135,7 +147,11 @@ hipError_t launch_gate_backward(const BackwardParams &p, hipStream_t st);
 hipError_t launch_prefill_attend(const PrefillParams &p, hipStream_t st);
 hipError_t launch_append(const AppendParams &p, int batch, hipStream_t st);
 hipError_t launch_gate_topk(const GateParams &p, int batch, hipStream_t st);
+hipError_t launch_gate_query(const GateParams &p, hipStream_t st);
+hipError_t launch_gate_slices(const GateParams &p, int batch, hipStream_t st);
 hipError_t launch_decode(const DecodeParams &p, int batch, hipStream_t st);
 hipError_t launch_step(const StepParams &p, int batch, hipStream_t st);
+hipError_t launch_select_decode(const StepParams &p, int batch, hipStream_t st);
+hipError_t launch_decode_merge(const DecodeParams &p, int batch, hipStream_t st);
 
 }  // namespace sas

@@ -41,6 +41,7 @@ constexpr int kStepKeysOff = 0;
 constexpr int kStepBtOff = 4 * SAS_MAX_BLOCKS_DEV;
 constexpr int kStepVsOff = 8 * SAS_MAX_BLOCKS_DEV;
 static_assert(kStepVsOff + 4 * kMaxGroup * kGateDim <= kWaves * kVTileBytes, "gate phase exceeds the V tiles");
+static_assert(3 * 4 * kMaxSlices * kStepMaxSel <= kWaves * kVTileBytes, "slice lists exceed the V tiles");
 
 template <bool kMax, int kMode>
 __global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(StepParams sp) {
@@ -258,6 +259,92 @@ __global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(StepParams sp) {
                     kMode ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gate_l[i]))) : 1.0f};
   };
   attend_unit<kMode>(sp.d, vlds, s, kvh, unit, 0, wave, wave * bpw, k_eff + 1, L, source, b, prefetch);
+}
+
+// The second half of the sliced step (fewer pairs than CUs): the slices'
+// Top-K lists of one pair (launch_gate_slices) are merged into the pair's
+// selection by the same radix select, with the slice lists concatenated in
+// ascending block order so that the lowest-index rule at the threshold is
+// unchanged; then the attention, each pair split over wg_per_unit
+// workgroups as in the decode kernel (partials merged by the decode merge
+// kernel).  Every workgroup of a pair makes the same selection; the first
+// stores it.
+template <int kMode>
+__global__ __launch_bounds__(kWaves * 64, 1) void select_decode_kernel(StepParams sp) {
+  __shared__ __attribute__((aligned(16))) uint8_t vlds[kWaves][kVTileBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[256];
+  __shared__ int32_t sel_l[kStepMaxSel], page_l[kStepMaxSel];
+  __shared__ float gate_l[kStepMaxSel];
+  __shared__ int32_t local_page;
+  const GateParams &p = sp.g;
+  const int nwg = sp.d.wg_per_unit;
+  const int unit = blockIdx.x / nwg;
+  const int wg = blockIdx.x - unit * nwg;
+  const int s = unit / p.n_kv_heads;
+  const int kvh = unit - s * p.n_kv_heads;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int32_t L = p.seq_lens[s];
+  const int n = (L - 1) / kBlock;
+  const int k_eff = min(p.n_sel - 1, n);
+  // the pair's candidate lists (slices x n_sel entries) in the V tiles' space
+  const int m = p.slices * p.n_sel;
+  const int m_pad = max(m, 512);
+  uint32_t *keys = reinterpret_cast<uint32_t *>(&vlds[0][0]);
+  int32_t *cblk = reinterpret_cast<int32_t *>(keys + m_pad);
+  int32_t *cpage = cblk + m_pad;
+  const int64_t base = (int64_t)unit * m;
+  for (int i = t; i < m_pad; i += kWaves * 64) {
+    const bool in = i < m;
+    keys[i] = in ? p.cand_key[base + i] : 0u;
+    cblk[i] = in ? p.cand_blk[base + i] : 0;
+    cpage[i] = in ? p.cand_page[base + i] : 0;
+  }
+  if (t == 0) local_page = p.block_table[(int64_t)s * p.max_blocks + n];
+  __syncthreads();
+  if (wave == 0) {
+    wave_select_emit(keys, m, k_eff, hist, [&](uint32_t pos, int c, uint32_t key) {
+      sel_l[pos] = cblk[c];
+      page_l[pos] = cpage[c];
+      gate_l[pos] = 1.0f / (1.0f + __expf(-key_score(key)));
+    });
+    if (lane == 0) {
+      sel_l[k_eff] = n;
+      page_l[k_eff] = local_page;
+      gate_l[k_eff] = 1.0f;
+    }
+  }
+  lds_barrier();
+  if (wg == 0 && wave == kWaves - 1) {
+    int32_t *sel = p.sel + (int64_t)unit * p.n_sel;
+    float *gates = p.gates ? p.gates + (int64_t)unit * p.n_sel : nullptr;
+    for (int i = lane; i < p.n_sel; i += 64) {
+      const bool in = i <= k_eff;
+      sel[i] = in ? sel_l[i] : -1;
+      if (gates) gates[i] = in ? gate_l[i] : 0.0f;
+    }
+    if (lane == 0) p.cnt[unit] = k_eff + 1;
+  }
+  auto source = [&](int i) {
+    i = min(i, kStepMaxSel - 1);
+    return BlockRef{__builtin_amdgcn_readfirstlane(page_l[i]), __builtin_amdgcn_readfirstlane(sel_l[i]),
+                    kMode ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gate_l[i]))) : 1.0f};
+  };
+  BlockRegs b;
+  attend_unit<kMode>(sp.d, vlds, s, kvh, unit, wg, wave, (wg * kWaves + wave) * sp.d.blocks_per_wave, k_eff + 1, L,
+                     source, b, false);
+}
+
+hipError_t launch_select_decode(const StepParams &p, int batch, hipStream_t st) {
+  const unsigned units = (unsigned)(batch * p.g.n_kv_heads);
+  const dim3 grid(units * (unsigned)p.d.wg_per_unit);
+  const int mode = !p.d.gates ? 0 : (p.d.gate_mode == 0 ? 1 : 2);
+  if (mode == 0) hipLaunchKernelGGL((select_decode_kernel<0>), grid, dim3(kWaves * 64), 0, st, p);
+  else if (mode == 1) hipLaunchKernelGGL((select_decode_kernel<1>), grid, dim3(kWaves * 64), 0, st, p);
+  else hipLaunchKernelGGL((select_decode_kernel<2>), grid, dim3(kWaves * 64), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.d.wg_per_unit == 1) return e;
+  return launch_decode_merge(p.d, batch, st);
 }
 
 bool step_fits(int group, int max_blocks, int n_sel) {

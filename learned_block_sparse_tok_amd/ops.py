@@ -169,7 +169,8 @@ def sparse_decode(shape: SasShape, q, k_pool, v_pool, block_table, seq_lens, sel
     _check(st, "sas_sparse_decode")
 
 
-STEP_PATH = {"auto": 0, "fused": 1, "two_launches": 2}  # SAS_STEP_AUTO, SAS_STEP_FUSED, SAS_STEP_TWO_LAUNCHES
+# SAS_STEP_AUTO, SAS_STEP_FUSED, SAS_STEP_TWO_LAUNCHES, SAS_STEP_SLICED
+STEP_PATH = {"auto": 0, "fused": 1, "two_launches": 2, "sliced": 3}
 
 
 def decode_step_workspace_bytes(shape: SasShape, budget_tokens: int, path="auto") -> int:
@@ -199,7 +200,8 @@ class SparseDecoder:
     """Holds the outputs and workspaces of one layer's decode step (allocated
     once, by torch).  step() runs sas_decode_step on the given path ("auto":
     one fused launch when there are enough (sequence, KV head) pairs to fill
-    the GPU); select() and attend() run sas_gate_topk and sas_sparse_decode."""
+    the GPU; see sas.h for the others); select() and attend() run
+    sas_gate_topk and sas_sparse_decode."""
 
     def __init__(self, batch, n_q_heads, n_kv_heads, max_blocks, strides, budget, theta, gated,
                  device="cuda", sm_scale=None, aggregate="mean", gate_mode="scale", path="auto"):

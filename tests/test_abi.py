@@ -88,7 +88,7 @@ def _step(lib, shape, path=0, gated=0, gates=FAKE, ws=FAKE, ws_bytes=1 << 24, bu
 
 def test_decode_step_rejects_bad_arguments(lib):
     sh = _shape()
-    assert _step(lib, sh, path=3) == ops.SAS_ERR_INVALID_ARG
+    assert _step(lib, sh, path=7) == ops.SAS_ERR_INVALID_ARG
     assert _step(lib, sh, gated=2) == ops.SAS_ERR_INVALID_ARG
     assert _step(lib, sh, gated=1, gates=None) == ops.SAS_ERR_INVALID_ARG
     assert _step(lib, sh, budget=1000) == ops.SAS_ERR_INVALID_ARG
@@ -96,6 +96,7 @@ def test_decode_step_rejects_bad_arguments(lib):
     assert _step(lib, _shape(strides=(0, 128, 8192))) == ops.SAS_ERR_INVALID_ARG
     # the two-launch path (forced, or chosen for 4 (sequence, KV head) pairs) checks its workspace
     assert _step(lib, sh, path=ops.STEP_PATH["two_launches"], ws_bytes=100) == ops.SAS_ERR_WORKSPACE
+    assert _step(lib, sh, path=ops.STEP_PATH["sliced"], ws_bytes=100) == ops.SAS_ERR_WORKSPACE
     assert _step(lib, sh, path=ops.STEP_PATH["auto"], ws=None) == ops.SAS_ERR_INVALID_ARG
 
 
@@ -106,9 +107,17 @@ def test_decode_step_workspace_bytes(lib):
         two = ops.decode_step_workspace_bytes(sh, 2048, "two_launches")
         # the attention's partials plus room for the scores
         assert two >= ops.sparse_decode_workspace_bytes(sh, 32) + sh.batch * sh.n_kv_heads * sh.max_blocks * 4
-    # automatic: 256 (sequence, KV head) pairs are fused, 4 are not
+    # automatic: 256 (sequence, KV head) pairs are fused; 4 take two launches,
+    # or the sliced selection once the block table is over 1,024 blocks
+    long = _shape(max_blocks=2048)
     assert ops.decode_step_workspace_bytes(big, 2048, "auto") == 0
-    assert ops.decode_step_workspace_bytes(small, 2048, "auto") > 0
+    assert ops.decode_step_workspace_bytes(small, 2048, "auto") == ops.decode_step_workspace_bytes(small, 2048,
+                                                                                                  "two_launches")
+    assert ops.decode_step_workspace_bytes(long, 2048, "auto") == ops.decode_step_workspace_bytes(long, 2048,
+                                                                                                 "sliced")
+    # the sliced path adds each pair's slice lists (score key, block, page per entry)
+    assert ops.decode_step_workspace_bytes(small, 2048, "sliced") > ops.decode_step_workspace_bytes(small, 2048,
+                                                                                                   "two_launches")
 
 
 def test_pool_rejects_bad_arguments_and_accepts_empty_list(lib):

@@ -329,9 +329,9 @@ def _step_workload(case):
     return w
 
 
-# "auto" takes the two launches for these few (sequence, KV head) pairs;
-# "fused" forces the one-launch step on them
-@pytest.mark.parametrize("path", ["auto", "fused"])
+# "auto" takes two launches for these few (sequence, KV head) pairs;
+# "fused" forces the one-launch step on them, "sliced" the sliced selection
+@pytest.mark.parametrize("path", ["auto", "fused", "sliced"])
 @pytest.mark.parametrize("gated", [False, True], ids=["plain", "gated"])
 @pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: c["name"])
 def test_step_parity(case, gated, path):
@@ -393,6 +393,45 @@ def test_fused_step_equals_two_launches(case):
             assert torch.equal(a, b), name
         cnt = wl.host(res["fused"][2])
         assert cnt.min() >= 1 and cnt.max() <= case["budget"] // 64
+
+
+# Fewer pairs than half the CUs: the sliced selection (several workgroups
+# per pair, each keeping its slice's Top-K, then one merge) must give the
+# two launches' bits exactly, since both then attend with the same split.
+SLICED_CASES = [
+    dict(name="ragged_g4", lens=[1, 64, 65, 4097, 9000, 33000], Hq=8, Hkv=2, budget=1024, mb=520, layout="paged"),
+    dict(name="b8_g4_32k", lens=[32768] * 8, Hq=32, Hkv=8, budget=2048, mb=512, layout="contiguous"),
+    dict(name="b4_g5_131k", lens=[131072, 100000, 77777, 131000], Hq=40, Hkv=8, budget=2048, mb=2048,
+         layout="paged"),
+    dict(name="g16_b4096", lens=[20000, 700], Hq=16, Hkv=1, budget=4096, mb=320, layout="paged"),
+    dict(name="b2_b16384", lens=[100000, 50000], Hq=4, Hkv=1, budget=16384, mb=1600, layout="paged"),
+]
+
+
+@pytest.mark.parametrize("case", SLICED_CASES, ids=lambda c: c["name"])
+def test_sliced_step_equals_two_launches(case):
+    w = wl.make(len(case["lens"]), case["Hq"], case["Hkv"], case["lens"], case["budget"], case["layout"], 93, DEV,
+                max_blocks=case["mb"])
+    assert w.batch * w.n_kv_heads <= 128
+    gk = gpu_pool(w)
+    args = (w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, w.block_table, w.seq_lens)
+    for aggregate, gated, gate_mode in FUSED_OPTS:
+        if aggregate == "max" and w.n_q_heads // w.n_kv_heads > 8:
+            continue
+        say("sliced", case["name"], aggregate, gated, gate_mode)
+        res = {}
+        for path in ("two_launches", "sliced"):
+            dec = ops.SparseDecoder(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, case["budget"],
+                                    w.theta, gated, device=DEV, aggregate=aggregate, gate_mode=gate_mode, path=path)
+            dec.sel.fill_(-7)
+            dec.gates.fill_(3.0)
+            dec.scores.fill_(5.0)
+            dec.out.zero_()
+            dec.step(*args)
+            torch.cuda.synchronize()
+            res[path] = [t.clone() for t in (dec.sel, dec.gates, dec.cnt, dec.scores, dec.out)]
+        for name, a, b in zip(("sel", "gates", "cnt", "scores", "out"), res["two_launches"], res["sliced"]):
+            assert torch.equal(a, b), name
 
 
 def test_fused_step_without_scores_or_gates():
@@ -462,7 +501,7 @@ def test_invalid_arguments_raise():
 
 
 # ------------------------------------------------------------------ graphs, determinism
-@pytest.mark.parametrize("path", ["two_launches", "fused"])
+@pytest.mark.parametrize("path", ["two_launches", "fused", "sliced"])
 def test_graph_replay_matches_eager(path):
     # the step captured into one HIP graph: every replay, with eager work and
     # synchronisations in between, reproduces the eager result bit for bit
