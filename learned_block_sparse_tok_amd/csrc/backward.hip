@@ -31,7 +31,8 @@
 //     blocks' pre-norm gate keys on MFMA.
 //   gate_param_reduce_kernel + gate_dwk_sum_kernel  the weight gradients as
 //     sums over the batch of outer products of those factors, as 64 x 64
-//     output tiles on fp32 MFMA with the factor rows staged in LDS; dW_k's
+//     output tiles on bf16 MFMA over high/low splits of the fp32 factors,
+//     the factor rows staged in LDS; dW_k's
 //     rows are split into ranges whose partial tiles are then added in order
 //     (a fixed order throughout: deterministic).
 #include "sas_device.h"
@@ -581,25 +582,47 @@ __global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
 
 // ---------------------------------------------------------------- sums over the batch
 // acc = sum over rows n in [n_lo, n_hi) of A(n, 64-wide column slice) (x)
-// B(n, 64-wide column slice) for one 64 x 64 tile, on fp32 MFMA (16x16x4):
-// rows are staged in LDS 32 at a time, the next 32 fetched into registers
-// while the current ones are summed.  Wave w owns the 32 x 32 quadrant
-// (rows 32(w/2), columns 32(w%2)) as 2 x 2 MFMA tiles; per 4-row step lane l
-// feeds A(row 4kk + l/16, column l%16) and B(row 4kk + l/16, column l%16).
-// The rows are taken in order (deterministic).
+// B(n, 64-wide column slice) for one 64 x 64 tile.  The fp32 operands are
+// split into bf16 high and low parts and summed as hi*hi + hi*lo + lo*hi on
+// v_mfma_f32_16x16x32_bf16 (the dropped lo*lo term is ~2^-16 relative; the
+// split itself keeps ~16 significant bits).  Rows go through LDS 32 at a
+// time, already split and transposed (column-major, 8 rows per 16 bytes,
+// a 40-element pitch so that the operand reads are conflict-free), the next
+// 32 fetched into registers while the current ones are summed (fetching
+// further ahead measured slower): thread t fetches rows 8(t/64) .. +7 of
+// column t%64.  Wave w owns the 32 x 32 quadrant (rows 32(w/2), columns
+// 32(w%2)) as 2 x 2 MFMA tiles; lane l feeds column l%16 of its tile and the
+// step's rows 8(l/16) .. +7 to both operands.  The rows are taken in order
+// (deterministic).
+constexpr int kOsPitch = 40;  // bf16 elements per LDS column of 32 rows
+struct OuterLds {
+  uint16_t ah[64][kOsPitch], al[64][kOsPitch], bh[64][kOsPitch], bl[64][kOsPitch];
+};
+
 template <typename FA, typename FB>
-__device__ void outer_sum_tile(FA fa, FB fb, int n_lo, int n_hi, f32x4 (&acc)[2][2], float (&as)[32][64],
-                               float (&bs)[32][64]) {
+__device__ void outer_sum_tile(FA fa, FB fb, int n_lo, int n_hi, f32x4 (&acc)[2][2], OuterLds &ls) {
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  const int wm = wave >> 1, wn = wave & 1, kr = lane >> 4, c16 = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1, g = lane >> 4, c16 = lane & 15;
+  const int col = t & 63, rg = t >> 6;  // fetch: column, group of 8 rows
   float ra[8], rb[8];
   auto fetch = [&](int n0) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int e = t + 256 * k, n = n0 + (e >> 6);
-      ra[k] = n < n_hi ? fa(n, e & 63) : 0.f;
-      rb[k] = n < n_hi ? fb(n, e & 63) : 0.f;
+    for (int e = 0; e < 8; ++e) {
+      const int n = n0 + 8 * rg + e;
+      ra[e] = n < n_hi ? fa(n, col) : 0.f;
+      rb[e] = n < n_hi ? fb(n, col) : 0.f;
     }
+  };
+  auto split = [&](const float (&x)[8], uint16_t *hi, uint16_t *lo) {
+    u32x4 h, l;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t hp = pack_bf16_rne(x[2 * q], x[2 * q + 1]);
+      h[q] = hp;
+      l[q] = pack_bf16_rne(x[2 * q] - bf16_lo(hp), x[2 * q + 1] - bf16_hi(hp));
+    }
+    *reinterpret_cast<u32x4 *>(hi) = h;
+    *reinterpret_cast<u32x4 *>(lo) = l;
   };
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -608,23 +631,26 @@ __device__ void outer_sum_tile(FA fa, FB fb, int n_lo, int n_hi, f32x4 (&acc)[2]
   if (n_lo < n_hi) fetch(n_lo);
   for (int n0 = n_lo; n0 < n_hi; n0 += 32) {
     lds_barrier();
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int e = t + 256 * k;
-      as[e >> 6][e & 63] = ra[k];
-      bs[e >> 6][e & 63] = rb[k];
-    }
+    split(ra, &ls.ah[col][8 * rg], &ls.al[col][8 * rg]);
+    split(rb, &ls.bh[col][8 * rg], &ls.bl[col][8 * rg]);
     lds_barrier();
     if (n0 + 32 < n_hi) fetch(n0 + 32);
+    bf16x8 ah[2], al[2], bh[2], bl[2];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const float a0 = as[4 * kk + kr][32 * wm + c16], a1 = as[4 * kk + kr][32 * wm + 16 + c16];
-      const float b0 = bs[4 * kk + kr][32 * wn + c16], b1 = bs[4 * kk + kr][32 * wn + 16 + c16];
-      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+      ah[i] = to_bf16x8(*reinterpret_cast<const u32x4 *>(&ls.ah[32 * wm + 16 * i + c16][8 * g]));
+      al[i] = to_bf16x8(*reinterpret_cast<const u32x4 *>(&ls.al[32 * wm + 16 * i + c16][8 * g]));
+      bh[i] = to_bf16x8(*reinterpret_cast<const u32x4 *>(&ls.bh[32 * wn + 16 * i + c16][8 * g]));
+      bl[i] = to_bf16x8(*reinterpret_cast<const u32x4 *>(&ls.bl[32 * wn + 16 * i + c16][8 * g]));
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bl[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bh[j], acc[i][j], 0, 0, 0);
+      }
   }
 }
 
@@ -649,8 +675,7 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[2][2], float *dst,
 // du_k (x) pooled; the last two blocks: the query- and key-side norm-weight
 // gradients as sums over the (sequence, KV head) rows.
 __global__ __launch_bounds__(256) void gate_param_reduce_kernel(BackwardParams p) {
-  __shared__ __attribute__((aligned(16))) float as[32][64];
-  __shared__ float bs[32][64];
+  __shared__ __attribute__((aligned(16))) OuterLds ls;
   const int tiles_q = p.n_q_heads * 4, tiles_k = p.n_kv_heads * 12;  // dW_k: 12 tiles of 64 x 64 per KV head
   const int bid = blockIdx.x;
   const int tid = threadIdx.x;
@@ -661,7 +686,7 @@ __global__ __launch_bounds__(256) void gate_param_reduce_kernel(BackwardParams p
     const float *a = p.ws_du_q + (int64_t)h * kGateDim + 64 * jt;
     const uint16_t *b = p.q + (int64_t)h * kHeadDim + 64 * it;
     outer_sum_tile([&](int n, int c) { return a[n * rs + c]; }, [&](int n, int c) { return bf16_to_f32(b[n * rs + c]); },
-                   0, p.batch, acc, as, bs);
+                   0, p.batch, acc, ls);
     store_tile(acc, p.d_w_q + ((int64_t)h * kGateDim + 64 * jt) * kHeadDim + 64 * it, kHeadDim);
   } else if (bid < tiles_q + tiles_k * kSplitK) {
     // one of kSplitK consecutive row ranges of one dW_k tile -> a partial
@@ -677,7 +702,7 @@ __global__ __launch_bounds__(256) void gate_param_reduce_kernel(BackwardParams p
     auto slot = [&](int nn) { return ((int64_t)(nn / p.max_sel) * p.n_kv_heads + kvh) * p.max_sel + nn % p.max_sel; };
     outer_sum_tile([&](int nn, int c) { return p.ws_du_k[slot(nn) * kGateDim + 64 * jt + c]; },
                    [&](int nn, int c) { return p.ws_pool[slot(nn) * 3 * kHeadDim + 64 * it + c]; }, n_lo, n_hi, acc,
-                   as, bs);
+                   ls);
     store_tile(acc, p.ws_part + ((int64_t)k * kSplitK + part) * 64 * 64, 64);
   } else {
     // thread (dims 4q .. 4q+3, slice sl) sums rows u = sl, sl + 8, ...; the
@@ -689,7 +714,7 @@ __global__ __launch_bounds__(256) void gate_param_reduce_kernel(BackwardParams p
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 16
     for (int u = sl; u < units; u += 8) sum += *reinterpret_cast<const f32x4 *>(src + (int64_t)u * kGateDim + 4 * q);
-    float *slices = &as[0][0];  // [8][kGateDim] within the tile buffer
+    float *slices = reinterpret_cast<float *>(&ls);  // [8][kGateDim] within the tile buffers
     *reinterpret_cast<f32x4 *>(slices + sl * kGateDim + 4 * q) = sum;
     lds_barrier();
     if (tid < kGateDim) {
