@@ -364,7 +364,30 @@ __global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
 #pragma unroll
       for (int ks = 0; ks < 12; ++ks) wk[mt][ks] = ld16(wkb + (int64_t)16 * mt * 3 * kHeadDim + 32 * ks);
   }
+  // the pooled statistics of the historical blocks, written by
+  // gate_grad_kernel, kChainBlocks blocks at a time: 96 float4 per block,
+  // thread t takes float4 t + 256k.  The first chunk is fetched here, each
+  // next one while the current one is processed.
+  const int64_t slot0 = (int64_t)unit * p.max_sel;
+  constexpr int kQuads = kChainBlocks * 3 * kHeadDim / 4 / 256;
+  f32x4 pv[kQuads];
+  auto fetch_pooled = [&](int i0) {
+    const int nb_ = max(0, min(kChainBlocks, n_hist - i0));
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(p.ws_pool + (slot0 + i0) * 3 * kHeadDim);
+#pragma unroll
+    for (int k = 0; k < kQuads; ++k)
+      if (t + 256 * k < nb_ * 3 * kHeadDim / 4) pv[k] = src[t + 256 * k];
+  };
+  fetch_pooled(0);
   lds_barrier();
+  // the gate keys of the first two historical slots of this thread's slot
+  // group (dghat below), fetched ahead of the query side
+  const uint16_t *gk = p.gate_keys + (int64_t)kvh * kGateDim + 8 * o;
+  const int64_t gk_page = (int64_t)p.n_kv_heads * kGateDim;
+  u32x4 gk_first[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (row + 16 * k < n_hist) gk_first[k] = ld16(gk + page_l[row + 16 * k] * gk_page);
 
   // ---- per head: RMS, normalise, weight, rotate; the mean over the group in head order
   float cq[4], sq[4];  // RoPE at the query's position for pairs o + 16k
@@ -405,11 +428,9 @@ __global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    const uint16_t *gk = p.gate_keys + (int64_t)kvh * kGateDim + 8 * o;
-    const int64_t gk_page = (int64_t)p.n_kv_heads * kGateDim;
 #pragma unroll 2
     for (int i = row; i < n_hist; i += 16) {
-      const u32x4 w = ld16(gk + page_l[i] * gk_page);
+      const u32x4 w = i < row + 32 ? gk_first[(i - row) >> 4] : ld16(gk + page_l[i] * gk_page);
       const float d = ds_l[i];
       acc[0] = fmaf(d, bf16_lo(w.x), acc[0]);
       acc[1] = fmaf(d, bf16_hi(w.x), acc[1]);
@@ -464,31 +485,19 @@ __global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
   }
 
   // ---- key side, kChainBlocks selected historical blocks at a time
-  const int64_t slot0 = (int64_t)unit * p.max_sel;
   float dwk[8];  // dm * n of this thread's dims, summed over its block rows
 #pragma unroll
   for (int k = 0; k < 8; ++k) dwk[k] = 0.f;
   for (int i0 = 0; i0 < p.max_sel; i0 += kChainBlocks) {
     const int nb_ = max(0, min(kChainBlocks, n_hist - i0));
     lds_barrier();
-    // the chunk's pooled statistics, written by gate_grad_kernel: 96 float4
-    // per block, thread t takes float4 t + 256k
-    {
-      constexpr int kQuads = kChainBlocks * 3 * kHeadDim / 4 / 256;
-      const f32x4 *src = reinterpret_cast<const f32x4 *>(p.ws_pool + (slot0 + i0) * 3 * kHeadDim);
-      f32x4 v[kQuads];
 #pragma unroll
-      for (int k = 0; k < kQuads; ++k) {
-        const int e4 = t + 256 * k;
-        if (e4 < nb_ * 3 * kHeadDim / 4) v[k] = src[e4];
-      }
-#pragma unroll
-      for (int k = 0; k < kQuads; ++k) {
-        const int e4 = t + 256 * k, b = e4 / (3 * kHeadDim / 4), c4 = e4 - b * (3 * kHeadDim / 4);
-        if (e4 < nb_ * 3 * kHeadDim / 4) *reinterpret_cast<f32x4 *>(&pooled[b][4 * c4]) = v[k];
-      }
+    for (int k = 0; k < kQuads; ++k) {
+      const int e4 = t + 256 * k, b = e4 / (3 * kHeadDim / 4), c4 = e4 - b * (3 * kHeadDim / 4);
+      if (e4 < nb_ * 3 * kHeadDim / 4) *reinterpret_cast<f32x4 *>(&pooled[b][4 * c4]) = pv[k];
     }
     lds_barrier();
+    if (i0 + kChainBlocks < p.max_sel) fetch_pooled(i0 + kChainBlocks);
     // U^T = W_k P^T: lane l holds block l%16, rows 32w + 16mt + 4(l/16) + r
     // (columns of blocks not in the chunk hold stale values and are not read)
     {
