@@ -30,6 +30,7 @@ namespace sas {
 namespace {
 
 constexpr int kPoolBatch = 16;                // blocks per workgroup
+constexpr int kPoolAhead = 16;                // key rows each thread keeps in flight
 constexpr int kPooledPitch = 3 * kHeadDim + 4;  // LDS row of pooled statistics (floats), staggered banks
 constexpr int kUPitch = kGateDim + 4;
 
@@ -38,12 +39,17 @@ __device__ __forceinline__ bf16x8 as_b8(u32x4 v) { return __builtin_bit_cast(bf1
 }  // namespace
 
 // Gate keys of nb <= 16 key blocks of one KV head.  Every thread of a
-// 256-thread workgroup calls it (it holds barriers).  src[b]: block b's row 0
-// of this head; blk[b]: its block index (RoPE position 64 blk[b]); dst[b]: its
-// 128 gate-key values; all three in LDS, written by the caller before a
-// barrier.  last_row: when non-null, block 0's row 63 is read from there
+// 256-thread workgroup calls it (it holds barriers).  src[b]: element offset
+// of block b's row 0 of this head in k_pool; blk[b]: its block index (RoPE
+// position 64 blk[b]); dst[b]: element offset of its 128 gate-key values in
+// gate_keys; all three in LDS, written by the caller before a barrier.
+// (Offsets rather than pointers: addresses formed from the kernel's buffer
+// arguments compile to global loads, whose waits count only the loads
+// before them; pointers read back from LDS would compile to flat loads,
+// which the compiler drains completely before any use.)  last_row: when non-null, block 0's row 63 is read from there
 // instead of from the pool (the append kernel passes the row it is writing).
-__device__ __forceinline__ void pool_batch(int nb, const uint16_t *const *src, const int *blk, uint16_t *const *dst,
+__device__ __forceinline__ void pool_batch(int nb, const uint16_t *k_pool, const int64_t *src, const int *blk,
+                                           uint16_t *gate_keys, const int64_t *dst,
                            int64_t tok_stride, const uint16_t *last_row, const uint16_t *w_kh,
                            const float *w_knorm, double theta) {
   __shared__ __attribute__((aligned(16))) float pooled[kPoolBatch][kPooledPitch];
@@ -58,7 +64,7 @@ __device__ __forceinline__ void pool_batch(int nb, const uint16_t *const *src, c
 
   // ---- 1. pooled statistics
   if (b < nb) {
-    const uint16_t *kb = src[b] + 8 * o;
+    const uint16_t *kb = k_pool + src[b] + 8 * o;
     float mx[8], mn[8], sum[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -66,10 +72,18 @@ __device__ __forceinline__ void pool_batch(int nb, const uint16_t *const *src, c
       mn[e] = __builtin_inff();
       sum[e] = 0.f;
     }
-#pragma unroll 16
+    // a rolling window of kPoolAhead rows in flight: row r + kPoolAhead is
+    // issued as soon as row r is consumed (rows summed in order)
+    auto row = [&](int r) {
+      return (last_row && b == 0 && r == kBlock - 1) ? ld16(last_row + 8 * o) : ld16(kb + (int64_t)r * tok_stride);
+    };
+    u32x4 win[kPoolAhead];
+#pragma unroll
+    for (int r = 0; r < kPoolAhead; ++r) win[r] = row(r);
+#pragma unroll
     for (int r = 0; r < kBlock; ++r) {
-      const u32x4 w = (last_row && b == 0 && r == kBlock - 1) ? ld16(last_row + 8 * o)
-                                                             : ld16(kb + (int64_t)r * tok_stride);
+      const u32x4 w = win[r % kPoolAhead];
+      if (r + kPoolAhead < kBlock) win[r % kPoolAhead] = row(r + kPoolAhead);
       const float x[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
                           bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
 #pragma unroll
@@ -156,14 +170,13 @@ __device__ __forceinline__ void pool_batch(int nb, const uint16_t *const *src, c
   lds_barrier();
   if (b < nb) {
     const float *u = &uk[b][8 * o];
-    *reinterpret_cast<u32x4 *>(dst[b] + 8 * o) =
+    *reinterpret_cast<u32x4 *>(gate_keys + dst[b] + 8 * o) =
         u32x4{pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]), pack_bf16x2(u[4], u[5]), pack_bf16x2(u[6], u[7])};
   }
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void pool_kernel(PoolParams p) {
-  __shared__ const uint16_t *src_l[kPoolBatch];
-  __shared__ uint16_t *dst_l[kPoolBatch];
+  __shared__ int64_t src_l[kPoolBatch], dst_l[kPoolBatch];
   __shared__ int blk_l[kPoolBatch];
   const int kvh = blockIdx.x % p.n_kv_heads;  // the KV heads of a batch run in consecutive workgroups
   const int i0 = (blockIdx.x / p.n_kv_heads) * kPoolBatch;
@@ -172,12 +185,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void p
     const int i = i0 + threadIdx.x;
     const int s = p.pool_seq[i], c = p.pool_blk[i];
     const int32_t page = p.block_table[(int64_t)s * p.max_blocks + c];
-    src_l[threadIdx.x] = p.k_pool + (int64_t)page * p.page_stride + (int64_t)kvh * p.head_stride;
-    dst_l[threadIdx.x] = p.gate_keys + ((int64_t)page * p.n_kv_heads + kvh) * kGateDim;
+    src_l[threadIdx.x] = (int64_t)page * p.page_stride + (int64_t)kvh * p.head_stride;
+    dst_l[threadIdx.x] = ((int64_t)page * p.n_kv_heads + kvh) * kGateDim;
     blk_l[threadIdx.x] = c;
   }
   lds_barrier();
-  pool_batch(nb, src_l, blk_l, dst_l, p.tok_stride, nullptr, p.w_k + (int64_t)kvh * kGateDim * 3 * kHeadDim,
+  pool_batch(nb, p.k_pool, src_l, blk_l, p.gate_keys, dst_l, p.tok_stride, nullptr, p.w_k + (int64_t)kvh * kGateDim * 3 * kHeadDim,
              p.w_knorm, p.theta);
 }
 
@@ -187,8 +200,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void p
 // k_new.  Bytes per (sequence, KV head): 512 B read + 512 B written, plus
 // 16 KiB - 256 B of keys read and 256 B written per completed block.
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
-  __shared__ const uint16_t *src_l[1];
-  __shared__ uint16_t *dst_l[1];
+  __shared__ int64_t src_l[1], dst_l[1];
   __shared__ int blk_l[1];
   const int unit = blockIdx.x;
   const int s = unit / p.n_kv_heads;
@@ -208,12 +220,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   }
   if (L % kBlock == 0) {
     if (t == 0) {
-      src_l[0] = p.k_pool + base;
-      dst_l[0] = p.gate_keys + ((int64_t)page * p.n_kv_heads + kvh) * kGateDim;
+      src_l[0] = base;
+      dst_l[0] = ((int64_t)page * p.n_kv_heads + kvh) * kGateDim;
       blk_l[0] = c;
     }
     lds_barrier();
-    pool_batch(1, src_l, blk_l, dst_l, p.tok_stride, p.k_new + src, p.w_k + (int64_t)kvh * kGateDim * 3 * kHeadDim,
+    pool_batch(1, p.k_pool, src_l, blk_l, p.gate_keys, dst_l, p.tok_stride, p.k_new + src, p.w_k + (int64_t)kvh * kGateDim * 3 * kHeadDim,
                p.w_knorm, p.theta);
   }
 }
