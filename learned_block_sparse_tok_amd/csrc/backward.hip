@@ -316,19 +316,20 @@ __global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
   // the historical slots' pages, block indices and score gradients (one slot
   // per thread: at most 255 historical slots), the norm weights and the RoPE
   // frequencies, gathered into LDS.  Every load is issued unconditionally
-  // (from clamped, valid addresses: slot 0 always holds a block), and the
-  // first head's W_q loads go out between the dependent gathers and their
-  // LDS stores, so that all their latencies overlap.
-  const bool has_slot = t < n_hist;
-  const int ti = has_slot ? t : 0;
+  // from clamped, valid addresses (a padding slot's -1 reads block 0's
+  // page), so that none waits for the selection count, and the first head's
+  // W_q loads go out right after the slots, ahead of the dependent
+  // block-table gather: the W_q stream and the slot -> page chain overlap.
+  const int ti = min(t, p.max_sel - 1);
   const int slot_blk = sel[ti];
   const float slot_g = gts[ti], slot_dg = dg[ti];
-  const float wqn = p.w_qnorm[t & (kGateDim - 1)], wkn = p.w_knorm[t & (kGateDim - 1)];
-  const double invf = p.inv_freq[t & (kGateDim / 2 - 1)];
-  const int slot_page = bt[slot_blk];
   u32x4 a[8][4];
   bf16x8 qb[4];
   load_wq(min(wave, G - 1), a, qb);
+  const float wqn = p.w_qnorm[t & (kGateDim - 1)], wkn = p.w_knorm[t & (kGateDim - 1)];
+  const double invf = p.inv_freq[t & (kGateDim / 2 - 1)];
+  const int slot_page = bt[max(slot_blk, 0)];
+  const bool has_slot = t < n_hist;
   if (has_slot) {
     blk_l[t] = slot_blk;
     page_l[t] = slot_page;
