@@ -165,6 +165,59 @@ def cpu_baseline_prefill(w, gk_o_fn, budget, gated, seconds):
                        f"{t_total:.1f} s; gate keys pooled beforehand (untimed, as on the GPU)")
 
 
+def read_ceiling(layers, decs, steps):
+    """The gather ceiling of the attention's own reads: sas_probe_read over
+    exactly the K and V blocks the last steps selected (one 16 KiB chunk per
+    selected (page, KV head) block of K and of V), rotated over the layers
+    like the steps and bracketed by HIP events; the best of 1, 2, 4 and 8
+    chunks per workgroup.  Paged head-major pools only (a block of a
+    contiguous cache is not one 16 KiB chunk): None otherwise."""
+    import numpy as np
+    import torch
+    from learned_block_sparse_tok_amd import ops
+    w0 = layers[0]["w"]
+    ps, ts, hs = w0.strides
+    if ts != 128:
+        return None
+    addrs = []
+    for L, d in zip(layers, decs):
+        w = L["w"]
+        sel = d.sel.long()
+        n_sel = sel.shape[2]
+        valid = torch.arange(n_sel, device=sel.device)[None, None, :] < d.cnt.long()[:, :, None]
+        bt = w.block_table.long()
+        pages = torch.gather(bt, 1, sel.clamp(min=0).reshape(w.batch, -1)).reshape(sel.shape)
+        kvh = torch.arange(w.n_kv_heads, device=sel.device)[None, :, None].expand_as(sel)
+        off = (pages * ps + kvh * hs)[valid] * 2
+        addrs.append(torch.cat([off + w.k_pool.data_ptr(), off + w.v_pool.data_ptr()]).contiguous())
+    chunk_bytes = 64 * 128 * 2
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sinks = [ops.probe_read(a, 4) for a in addrs]
+    best = None
+    for per, reps in [(1, 40), (2, 40), (4, 40), (8, 40), (None, steps)]:
+        if per is None:
+            per = best[1]
+        sinks = [ops.probe_read(a, per) for a in addrs]
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(reps):
+            ops.probe_read(addrs[i % len(addrs)], per, sinks[i % len(addrs)])
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) / reps * 1e3
+        if reps != steps and (best is None or us < best[0]):
+            best = (us, per)
+    nbytes = float(np.mean([a.numel() for a in addrs])) * chunk_bytes
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"read ceiling (sas_probe_read over the selected K/V blocks, {best[1]} chunks per workgroup): "
+        f"{us:.1f} us = {gbs:.0f} GB/s")
+    return {"kernel": "sas_probe_read (read_probe_kernel)",
+            "pattern": "the selected K and V blocks of the timed steps, one 16 KiB chunk each, gathered",
+            "chunks_per_wg": best[1], "bytes_per_launch": nbytes, "avg_launch_us": round(us, 2),
+            "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def run_prefill(args):
     import numpy as np
     import torch
@@ -417,6 +470,7 @@ def run_serve(args):
         "config": {"workload": args.workload, "batch": w.batch, "context": f"{int(lens0.min())}..{int(lens0.max())}",
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": 128, "budget_tokens": budget,
                    "kv_layout": w.layout, "mode": f"{worst} (slower of {','.join(results)})", "launch": "eager"},
+        "read_ceiling": ceiling,
         "step_hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
         "modes": {m: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in d.items()}
                   for m, d in results.items()},
@@ -619,6 +673,7 @@ def main():
 
     worst = min(results, key=lambda m: results[m]["queries_per_s"])
     r = results[worst]
+    ceiling = read_ceiling(layers, decs, args.steps)
     line = {
         "metric": "sparse-decode queries/s + % HBM roofline, Qwen3-8B shape, 32K ctx, 2K budget",
         "value": round(r["queries_per_s"], 1),
@@ -659,6 +714,9 @@ def main():
         "modes": {m: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in d.items()}
                   for m, d in results.items()},
     }
+    if ceiling is not None:
+        line["roofline"]["frac_of_read_ceiling"] = round(r["dominant_gbs"] / ceiling["achieved_gbs"], 4)
+        line["attention_alone"]["frac_of_read_ceiling"] = round(r["decode_gbs"] / ceiling["achieved_gbs"], 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layers[0], args.budget, worst == "gated", args.cpu_seconds)
         log(f"cpu baseline: {line['cpu_baseline']['value']:.1f} queries/s on {line['cpu_baseline']['cores']} threads")

@@ -326,6 +326,27 @@ sas_status sas_gate_backward(const sas_shape *shape, const void *q, const void *
                              float *d_w_knorm, void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/*
+ * sas_probe_read -- measurement utility, not a step of the method: reads
+ * n_chunks 16 KiB chunks with nothing else to do, so that the attention's
+ * gather rate can be compared with a gather ceiling measured on the same
+ * chunks (the attention reads each selected block of K and of V as one
+ * 16 KiB chunk of a paged head-major pool).
+ *   chunk_addr     device array [n_chunks] of device addresses, each
+ *                  16-byte aligned, of 16,384 readable bytes (trusted, like
+ *                  block tables: not checked on the host)
+ *   chunks_per_wg  chunks each 256-thread workgroup reads, 1..64
+ *   sink           device buffer of ceil(n_chunks / chunks_per_wg) 16-byte
+ *                  words, 16-byte aligned: word w = XOR of every 16-byte
+ *                  word of chunks [w * chunks_per_wg, ...) (so the reads
+ *                  cannot be skipped, and a test can check them)
+ * n_chunks = 0 is a no-op.  Errors: SAS_ERR_INVALID_ARG for a NULL pointer,
+ * a negative count, chunks_per_wg outside 1..64, sink_bytes too small or a
+ * misaligned sink.
+ */
+sas_status sas_probe_read(const uint64_t *chunk_addr, int32_t n_chunks, int32_t chunks_per_wg, void *sink,
+                          size_t sink_bytes, void *stream);
+
 /* Text of a status code (static storage). */
 const char *sas_status_str(sas_status status);
 /* Detail of the last failed call on this host thread ("" if none). */

@@ -10,6 +10,11 @@
 
 static_assert(SAS_MAX_BLOCKS == SAS_MAX_BLOCKS_DEV, "block-table limit mismatch");
 
+namespace sas {
+// the read-bandwidth probe (probe.hip), a measurement utility
+hipError_t launch_read_probe(const uint64_t *addr, int32_t n, int32_t per, void *sink, hipStream_t st);
+}  // namespace sas
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -76,6 +81,19 @@ const char *sas_status_str(sas_status st) {
 const char *sas_last_error(void) { return g_last_error; }
 
 int32_t sas_version(void) { return 100; }
+
+sas_status sas_probe_read(const uint64_t *chunk_addr, int32_t n_chunks, int32_t chunks_per_wg, void *sink,
+                          size_t sink_bytes, void *stream) {
+  if (n_chunks < 0) return fail(SAS_ERR_INVALID_ARG, "n_chunks is negative");
+  if (chunks_per_wg < 1 || chunks_per_wg > 64) return fail(SAS_ERR_INVALID_ARG, "chunks_per_wg must be in 1..64");
+  if (n_chunks == 0) return ok();
+  if (!chunk_addr || !sink) return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(sink)) return fail(SAS_ERR_INVALID_ARG, "sink must be 16-byte aligned");
+  const size_t need = (size_t)((n_chunks + chunks_per_wg - 1) / chunks_per_wg) * 16;
+  if (sink_bytes < need) return fail(SAS_ERR_INVALID_ARG, "sink %zu bytes < required %zu", sink_bytes, need);
+  return hip_status(sas::launch_read_probe(chunk_addr, n_chunks, chunks_per_wg, sink, (hipStream_t)stream),
+                    "read probe");
+}
 
 sas_status sas_pool_blocks(const sas_shape *shape, const void *k_pool, const int32_t *block_table,
                            const int32_t *pool_seq, const int32_t *pool_blk, int32_t n, const void *w_k,

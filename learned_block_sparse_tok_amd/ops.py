@@ -47,6 +47,7 @@ _SIGS = {
     "sas_sparse_decode_workspace_bytes": (_SZ, [_VP, _I32]),
     "sas_sparse_decode": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP, _VP, _SZ, _VP]),
     "sas_decode_step_workspace_bytes": (_SZ, [_VP, _I32, _I32]),
+    "sas_probe_read": (_I32, [_VP, _I32, _I32, _VP, _SZ, _VP]),
     "sas_decode_step": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F64, _I32, _I32, _I32, _I32, _F32, _I32,
                                _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "sas_prefill_select": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _F64, _I32, _VP, _VP, _VP, _VP, _VP]),
@@ -171,6 +172,20 @@ def sparse_decode(shape: SasShape, q, k_pool, v_pool, block_table, seq_lens, sel
 
 # SAS_STEP_AUTO, SAS_STEP_FUSED, SAS_STEP_TWO_LAUNCHES, SAS_STEP_SLICED
 STEP_PATH = {"auto": 0, "fused": 1, "two_launches": 2, "sliced": 3}
+
+
+def probe_read(chunk_addr, chunks_per_wg, sink=None, stream=None):
+    """sas_probe_read (measurement utility): reads the 16 KiB chunks whose
+    device addresses chunk_addr (int64 device tensor) lists; returns sink,
+    int32 [ceil(n / chunks_per_wg)][4]: the XOR of each workgroup's words."""
+    n = chunk_addr.numel()
+    words = (n + chunks_per_wg - 1) // chunks_per_wg
+    if sink is None:
+        sink = torch.empty((max(words, 1), 4), dtype=torch.int32, device=chunk_addr.device)
+    st = lib().sas_probe_read(_ptr(chunk_addr, torch.int64, "chunk_addr"), int(n), int(chunks_per_wg),
+                              _ptr(sink, torch.int32, "sink"), sink.numel() * 4, _stream(stream))
+    _check(st, "sas_probe_read")
+    return sink
 
 
 def decode_step_workspace_bytes(shape: SasShape, budget_tokens: int, path="auto") -> int:

@@ -206,3 +206,15 @@ def test_workspace_sizes(lib):
     sh = _shape(batch=4, n_q_heads=40, n_kv_heads=8, max_blocks=2048)
     assert lib.sas_sparse_decode_workspace_bytes(ctypes.byref(sh), 32) >= 2 * 4 * 40 * 130 * 4
     assert lib.sas_sparse_decode_workspace_bytes(ctypes.byref(sh), 0) == 0
+
+
+def test_probe_read_rejects_bad_arguments_and_accepts_empty_list(lib):
+    aligned = ctypes.c_void_p(0x10000)
+    assert lib.sas_probe_read(FAKE, -1, 1, aligned, 64, None) == ops.SAS_ERR_INVALID_ARG
+    assert lib.sas_probe_read(FAKE, 4, 0, aligned, 64, None) == ops.SAS_ERR_INVALID_ARG
+    assert lib.sas_probe_read(FAKE, 4, 65, aligned, 64, None) == ops.SAS_ERR_INVALID_ARG
+    assert lib.sas_probe_read(None, 4, 1, aligned, 64, None) == ops.SAS_ERR_INVALID_ARG
+    assert lib.sas_probe_read(FAKE, 4, 1, None, 64, None) == ops.SAS_ERR_INVALID_ARG
+    assert lib.sas_probe_read(FAKE, 4, 1, ctypes.c_void_p(0x10008), 64, None) == ops.SAS_ERR_INVALID_ARG
+    assert lib.sas_probe_read(FAKE, 5, 2, aligned, 47, None) == ops.SAS_ERR_INVALID_ARG  # needs 3 words
+    assert lib.sas_probe_read(None, 0, 1, None, 0, None) == ops.SAS_OK
