@@ -46,13 +46,16 @@ def gk_bytes_per_step(lens, n_kv_heads):
     return int(sum((int(L) - 1) // 64 for L in lens)) * n_kv_heads * 128 * 2
 
 
-def step_extra_bytes(w, n_sel, gated):
+def step_extra_bytes(w, n_sel, gated, scores=False):
     """Bytes the fused step moves besides K/V and gate keys, each once: the
     queries, Qproj rows, norm weights and block-table rows it reads; the
-    output, selection, gates, counts and scores it writes."""
+    output, selection, gates, counts (and, when requested, the optional
+    per-candidate scores) it writes."""
     B, Hq, Hkv = w.batch, w.n_q_heads, w.n_kv_heads
     reads = B * Hq * 128 * 2 + Hq * 128 * 128 * 2 + 128 * 4 + B * w.max_blocks * 4
-    writes = B * Hq * 128 * 2 + B * Hkv * n_sel * 4 * (2 if gated else 1) + B * Hkv * 4 + B * Hkv * w.max_blocks * 4
+    writes = B * Hq * 128 * 2 + B * Hkv * n_sel * 4 * (2 if gated else 1) + B * Hkv * 4
+    if scores:
+        writes += B * Hkv * w.max_blocks * 4
     return reads + writes
 
 
@@ -574,8 +577,11 @@ def main():
     for mode in args.modes.split(","):
         gated = mode == "gated"
         # one decoder (outputs + workspaces) per layer, as a model keeps per-layer state
+        # the timed step writes what a serving caller uses (selection, gates,
+        # counts, output), not the optional per-candidate score output
         decs = [ops.SparseDecoder(w0.batch, w0.n_q_heads, w0.n_kv_heads, w0.max_blocks, w0.strides, args.budget,
-                                  w0.theta, gated, device=dev, path=args.path) for _ in layers]
+                                  w0.theta, gated, device=dev, path=args.path, keep_scores=False)
+                for _ in layers]
 
         def step_eager(l):
             L, dec = layers[l], decs[l]

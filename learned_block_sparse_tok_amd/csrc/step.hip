@@ -43,8 +43,14 @@ constexpr int kStepVsOff = 8 * SAS_MAX_BLOCKS_DEV;
 static_assert(kStepVsOff + 4 * kMaxGroup * kGateDim <= kWaves * kVTileBytes, "gate phase exceeds the V tiles");
 static_assert(3 * 4 * kMaxSlices * kStepMaxSel <= kWaves * kVTileBytes, "slice lists exceed the V tiles");
 
+// seq_lens, block_table, n_kv_heads and max_blocks also come as leading
+// scalar arguments (copies of sp.g's): the first loads need only these, and
+// they arrive in the first kernel-argument fetch.
 template <bool kMax, int kMode>
-__global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(StepParams sp) {
+__global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(const int32_t *__restrict__ seq_lens_a,
+                                                              const int32_t *__restrict__ block_table_a,
+                                                              int32_t n_kv_heads_a, int32_t max_blocks_a,
+                                                              StepParams sp) {
   __shared__ __attribute__((aligned(16))) uint8_t vlds[kWaves][kVTileBytes];
   __shared__ float qs[kMaxGroup][kHeadDim];
   __shared__ float part[4][kGateDim];
@@ -58,13 +64,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(StepParams sp) {
 
   const GateParams &p = sp.g;
   const int unit = blockIdx.x;  // (sequence, KV head); KV head = unit % Hkv, as in the two kernels
-  const int s = unit / p.n_kv_heads;
-  const int kvh = unit - s * p.n_kv_heads;
+  const int s = unit / n_kv_heads_a;
+  const int kvh = unit - s * n_kv_heads_a;
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane16 = t & 15, grp = t >> 4;  // 32 groups of 16 lanes
   const int G = p.group;
-  const int32_t L = p.seq_lens[s];
+  const int32_t L = seq_lens_a[s];
   const int n = (L - 1) / kBlock;  // candidates: the blocks before the local block
   const int k_eff = min(p.n_sel - 1, n);
 
@@ -74,10 +80,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(StepParams sp) {
   const u32x4 qpiece = ld16(qg + (has_q ? 8 * t : 0));
   const double inv_freq = p.inv_freq[lane];
   const float wqn_a = p.w_qnorm[lane], wqn_b = p.w_qnorm[lane + 64];
-  const int32_t *bt = p.block_table + (int64_t)s * p.max_blocks;
+  const int32_t *bt = block_table_a + (int64_t)s * max_blocks_a;
   int32_t btv[kStepBtUnroll];
 #pragma unroll
-  for (int k = 0; k < kStepBtUnroll; ++k) btv[k] = bt[min(t + 512 * k, p.max_blocks - 1)];
+  for (int k = 0; k < kStepBtUnroll; ++k) btv[k] = bt[min(t + 512 * k, max_blocks_a - 1)];
   // projection batch b: rows 16b .. 16b+15 of the group's heads (head b/8);
   // lane group grp takes batches grp, grp + 32, ...  (one batch for G <= 4)
   const int n_batches = 8 * G;
@@ -110,7 +116,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(StepParams sp) {
   auto gather = [&](int base) {
 #pragma unroll
     for (int u = 0; u < kStepKeys; ++u)
-      v[u] = ld16(gkh + (int64_t)btl[min(base + 32 * u + grp, n)] * page_stride);
+      v[u] = __builtin_nontemporal_load(  // read once: kept out of the caches
+          reinterpret_cast<const u32x4 *>(gkh + (int64_t)btl[min(base + 32 * u + grp, n)] * page_stride));
   };
   gather(0);
   auto project = [&](int b) {  // lane o of the group ends with row o of batch b
@@ -231,9 +238,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(StepParams sp) {
   if (wave == 0) {
     wave_select_emit(keys, n, k_eff, hist, [&](uint32_t pos, int c, uint32_t key) {
       sel_l[pos] = c;
-      page_l[pos] = btl[c];
-      gate_l[pos] = 1.0f / (1.0f + __expf(-key_score(key)));
+      gate_l[pos] = __uint_as_float(key);  // the score key for now
     });
+    // pages and gates one slot per lane, off the emit's serial path
+    for (int i = lane; i < k_eff; i += 64) {
+      page_l[i] = btl[sel_l[i]];
+      gate_l[i] = 1.0f / (1.0f + __expf(-key_score(__float_as_uint(gate_l[i]))));
+    }
     if (lane == 0) {  // the local block closes the selection
       sel_l[k_eff] = n;
       page_l[k_eff] = btl[n];
@@ -355,14 +366,16 @@ hipError_t launch_step(const StepParams &p, int batch, hipStream_t st) {
   const dim3 grid((unsigned)(batch * p.g.n_kv_heads));
   const bool mx = p.g.aggregate != 0;
   const int mode = !p.d.gates ? 0 : (p.d.gate_mode == 0 ? 1 : 2);
+  const int32_t *sl = p.g.seq_lens, *btab = p.g.block_table;  // the leading arguments
+  const int32_t hkv = p.g.n_kv_heads, mb = p.g.max_blocks;
   if (!mx) {
-    if (mode == 0) hipLaunchKernelGGL((step_kernel<false, 0>), grid, dim3(kWaves * 64), 0, st, p);
-    else if (mode == 1) hipLaunchKernelGGL((step_kernel<false, 1>), grid, dim3(kWaves * 64), 0, st, p);
-    else hipLaunchKernelGGL((step_kernel<false, 2>), grid, dim3(kWaves * 64), 0, st, p);
+    if (mode == 0) hipLaunchKernelGGL((step_kernel<false, 0>), grid, dim3(kWaves * 64), 0, st, sl, btab, hkv, mb, p);
+    else if (mode == 1) hipLaunchKernelGGL((step_kernel<false, 1>), grid, dim3(kWaves * 64), 0, st, sl, btab, hkv, mb, p);
+    else hipLaunchKernelGGL((step_kernel<false, 2>), grid, dim3(kWaves * 64), 0, st, sl, btab, hkv, mb, p);
   } else {
-    if (mode == 0) hipLaunchKernelGGL((step_kernel<true, 0>), grid, dim3(kWaves * 64), 0, st, p);
-    else if (mode == 1) hipLaunchKernelGGL((step_kernel<true, 1>), grid, dim3(kWaves * 64), 0, st, p);
-    else hipLaunchKernelGGL((step_kernel<true, 2>), grid, dim3(kWaves * 64), 0, st, p);
+    if (mode == 0) hipLaunchKernelGGL((step_kernel<true, 0>), grid, dim3(kWaves * 64), 0, st, sl, btab, hkv, mb, p);
+    else if (mode == 1) hipLaunchKernelGGL((step_kernel<true, 1>), grid, dim3(kWaves * 64), 0, st, sl, btab, hkv, mb, p);
+    else hipLaunchKernelGGL((step_kernel<true, 2>), grid, dim3(kWaves * 64), 0, st, sl, btab, hkv, mb, p);
   }
   return hipGetLastError();
 }

@@ -216,10 +216,12 @@ class SparseDecoder:
     once, by torch).  step() runs sas_decode_step on the given path ("auto":
     one fused launch when there are enough (sequence, KV head) pairs to fill
     the GPU; see sas.h for the others); select() and attend() run
-    sas_gate_topk and sas_sparse_decode."""
+    sas_gate_topk and sas_sparse_decode.  keep_scores=False leaves the
+    optional per-candidate score output off (scores is None), as a serving
+    caller that needs only the selection and the attention output would."""
 
     def __init__(self, batch, n_q_heads, n_kv_heads, max_blocks, strides, budget, theta, gated,
-                 device="cuda", sm_scale=None, aggregate="mean", gate_mode="scale", path="auto"):
+                 device="cuda", sm_scale=None, aggregate="mean", gate_mode="scale", path="auto", keep_scores=True):
         self.shape = make_shape(batch, n_q_heads, n_kv_heads, max_blocks, strides)
         self.budget, self.theta, self.gated = budget, theta, gated
         self.aggregate, self.gate_mode, self.path = aggregate, gate_mode, path
@@ -229,7 +231,8 @@ class SparseDecoder:
         self.sel = torch.empty((batch, n_kv_heads, self.n_sel), dtype=torch.int32, device=dev)
         self.gates = torch.empty((batch, n_kv_heads, self.n_sel), dtype=torch.float32, device=dev)
         self.cnt = torch.empty((batch, n_kv_heads), dtype=torch.int32, device=dev)
-        self.scores = torch.empty((batch, n_kv_heads, max_blocks), dtype=torch.float32, device=dev)
+        self.scores = (torch.empty((batch, n_kv_heads, max_blocks), dtype=torch.float32, device=dev)
+                       if keep_scores else None)
         self.out = torch.empty((batch, n_q_heads, HEAD_DIM), dtype=torch.bfloat16, device=dev)
         self.ws_dec = torch.empty(sparse_decode_workspace_bytes(self.shape, self.n_sel), dtype=torch.uint8,
                                   device=dev)
