@@ -126,7 +126,9 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateParams p) {
   const int64_t page_stride = (int64_t)p.n_kv_heads * kGateDim;
   u32x4 v[kKeysInFlight];
   auto gather_key = [&](int c) -> u32x4 {
-    return c < n ? ld16(gkh + (int64_t)pg[c] * page_stride) : u32x4{0, 0, 0, 0};
+    // each gate key is read once per launch: non-temporal loads keep them out of the caches
+    return c < n ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(gkh + (int64_t)pg[c] * page_stride))
+                 : u32x4{0, 0, 0, 0};
   };
 #pragma unroll
   for (int u = 0; u < kKeysEarly; ++u) v[u] = gather_key(16 * u + grp);
