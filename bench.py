@@ -2,9 +2,12 @@
 """SAS sparse-decode benchmark on one MI355X.
 
 One step = one decode query per sequence through one attention layer:
-sas_gate_topk (gate query, block scores, per-KV-head Top-K) followed by
-sas_sparse_decode (block-sparse flash-decode over the selection).  Gate keys
-are pooled once by sas_pool_blocks before timing.  Inputs are synthetic and
+sas_decode_step, i.e. the gate query, block scores and per-KV-head Top-K of
+sas_gate_topk followed by the block-sparse flash-decode of sas_sparse_decode
+(one fused launch when the (sequence, KV head) pairs fill the GPU).  The
+step writes the selection, gates, counts and output, not the optional
+per-candidate scores.  Gate keys are pooled once by sas_pool_blocks before
+timing.  Inputs are synthetic and
 already resident in HBM.  Consecutive steps rotate over --layers independent
 layers (own K/V pools, gate keys, gate weights, queries), as consecutive
 attention calls of a model do, so no step re-reads data a previous step left
@@ -12,10 +15,12 @@ in the 256 MB last-level cache.
 
 Steps are launched eagerly (the host stays ahead of the GPU; --graph replays
 a per-layer HIP graph instead).  Prints one JSON line: queries/s (sequences x
-steps / wall time of the timed steps), the roofline entry of the dominant call
-(sas_sparse_decode, launched back to back --steps times on its stream and
-bracketed by HIP events) and the oracle timed on a bounded sample on the
-host.
+steps / wall time of the timed steps), the roofline entry of the dominant
+kernel (the fused step kernel, or sas_sparse_decode on the two-launch path,
+launched back to back --steps times on its stream and bracketed by HIP
+events), the attention alone, a gather ceiling measured by sas_probe_read over
+the same selected K/V blocks (read_ceiling), bulk pooling, and the oracle
+timed on a bounded sample on the host.
 """
 from __future__ import annotations
 
