@@ -478,7 +478,6 @@ def run_serve(args):
         "config": {"workload": args.workload, "batch": w.batch, "context": f"{int(lens0.min())}..{int(lens0.max())}",
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": 128, "budget_tokens": budget,
                    "kv_layout": w.layout, "mode": f"{worst} (slower of {','.join(results)})", "launch": "eager"},
-        "read_ceiling": ceiling,
         "step_hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
         "modes": {m: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in d.items()}
                   for m, d in results.items()},
@@ -715,6 +714,7 @@ def main():
         "attention_alone": {"kernel": "sas_sparse_decode (decode_kernel)", "avg_launch_us": round(r["decode_ms"] * 1e3, 2),
                             "bytes_per_launch": r["kv_bytes"], "achieved_gbs": round(r["decode_gbs"], 1),
                             "frac": round(r["decode_gbs"] / HBM_PEAK_GBS, 4)},
+        "read_ceiling": ceiling,
         "step_hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
         "pooling": {"kernel": "sas_pool_blocks (pool_kernel), every complete block of a layer, off the step",
                     "ms_per_layer": round(pool_ms, 4), "bytes": pool_bytes,
