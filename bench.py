@@ -123,6 +123,62 @@ def cpu_baseline(layer, budget, gated, seconds):
                        f"{t_total:.1f} s; gate keys pooled beforehand (untimed, as on the GPU)")
 
 
+def selection_check(layer, dec, budget):
+    """Oracle leg: every (sequence, KV head)'s selection of the first layer's
+    timed steps against the oracle's gate stage (its own pooling of every
+    complete block from a host copy of K, gate scores, full sort).  Counts
+    the units whose selection is identical, the boundary ties (sets that
+    differ only inside the band of candidates within 1e-3 relative of the
+    oracle's K-th score, the same number taken from it on both sides), and
+    any other mismatch; for planted workloads also the recall of the planted
+    blocks.  The timing of the oracle is cpu_baseline's; this only compares."""
+    import numpy as np
+    import oracle
+    from learned_block_sparse_tok_amd import workloads as wl
+    t0 = time.perf_counter()
+    w = layer["w"]
+    lens = wl.host(w.seq_lens).astype(np.int32)
+    bt = wl.host(w.block_table)
+    gk = np.zeros((w.n_pages, w.n_kv_heads, 128), np.uint16)
+    seq = np.repeat(np.arange(w.batch, dtype=np.int32), [int(L) // 64 for L in lens])
+    blk = np.concatenate([np.arange(int(L) // 64, dtype=np.int32) for L in lens])
+    oracle.pool_blocks(wl.host(w.k_pool), bt, w.strides, w.n_kv_heads, seq, blk, wl.host(w.w_k),
+                       wl.host(w.w_knorm), w.theta, gk)
+    sel, _, cnt, scores = oracle.gate_topk(wl.host(w.q), wl.host(w.w_q), wl.host(w.w_qnorm), gk, bt, lens, w.theta,
+                                           budget, w.n_kv_heads)
+    gsel, gcnt = wl.host(dec.sel), wl.host(dec.cnt)
+    identical = ties = other = 0
+    for s in range(w.batch):
+        n = (int(lens[s]) - 1) // 64
+        k = min(budget // 64 - 1, n)
+        for h in range(w.n_kv_heads):
+            if np.array_equal(gsel[s, h], sel[s, h]) and gcnt[s, h] == cnt[s, h]:
+                identical += 1
+                continue
+            if gcnt[s, h] != cnt[s, h] or gsel[s, h, k] != n or not 0 < k < n:
+                other += 1
+                continue
+            sc = scores[s, h, :n].astype(np.float64)
+            order = np.lexsort((np.arange(n), -np.where(np.isnan(sc), -np.inf, sc)))
+            sk = sc[order[k - 1]]
+            band = set(np.nonzero(np.abs(sc - sk) <= 1e-3 * max(abs(sk), 1.0))[0].tolist())
+            gset, oset = set(gsel[s, h, :k].tolist()), set(sel[s, h, :k].tolist())
+            if gset - band == oset - band and len(gset & band) == len(oset & band):
+                ties += 1
+            else:
+                other += 1
+    out = {"units": w.batch * w.n_kv_heads, "identical": identical, "boundary_ties": ties, "mismatches": other,
+           "band_rel": 1e-3, "layer": 0, "seconds": round(time.perf_counter() - t0, 1)}
+    if w.planted is not None and layer.get("planted"):
+        hit = sum(len(set(gsel[s, h, :gcnt[s, h]].tolist()) & set(w.planted[s, h].tolist()))
+                  for s in range(w.batch) for h in range(w.n_kv_heads))
+        out["planted_recall"] = {"hit": int(hit), "planted": int(w.planted.size),
+                                 "recall": round(hit / w.planted.size, 4), "delta": w.plant_delta}
+    log(f"selection check: {identical} identical, {ties} boundary ties, {other} mismatches of {out['units']} units"
+        + (f"; planted recall {out['planted_recall']['recall']}" if "planted_recall" in out else ""))
+    return out
+
+
 def prefill_flops(cnt, group):
     """Algorithmic attention flops of a training-time forward: every query
     head of position t does 4 x 128 flops (QK and PV) per attended key, the
@@ -452,12 +508,28 @@ def run_serve(args):
         ev[1].record(stream)
         torch.cuda.synchronize()
         app_us = ev[0].elapsed_time(ev[1]) / steps * 1e3
+        # the selection and the attention alone (the last step's inputs),
+        # each launched back to back on the main stream, bracketed by HIP events
+        last = total - 1
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        for _ in range(steps):
+            dec.select(q_new[last], w.w_q, w.w_qnorm, gk, w.block_table, lens_all[last])
+        ev[1].record(stream)
+        for _ in range(steps):
+            dec.attend(q_new[last], w.k_pool, w.v_pool, w.block_table, lens_all[last])
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        sel_us = ev[0].elapsed_time(ev[1]) / steps * 1e3
+        att_us = ev[1].elapsed_time(ev[2]) / steps * 1e3
         cnt = wl.host(dec.cnt)
         kv_b = kv_bytes_per_step(cnt, 64 * 128 * 2)
         gk_b = gk_bytes_per_step(wl.host(lens_all[total - 1]), w.n_kv_heads)
         ms = elapsed * 1e3 / steps
         results[mode] = dict(queries_per_s=w.batch * steps / elapsed, ms_per_step=ms, append_us=app_us,
-                             step_gbs=(kv_b + gk_b) / (ms * 1e-3) / 1e9, kv_bytes=kv_b, gk_bytes=gk_b)
+                             step_gbs=(kv_b + gk_b) / (ms * 1e-3) / 1e9, kv_bytes=kv_b, gk_bytes=gk_b,
+                             select_us=sel_us, select_gbs=gk_b / (sel_us * 1e-6) / 1e9,
+                             attend_us=att_us, attend_gbs=kv_b / (att_us * 1e-6) / 1e9)
         log(f"{mode}: {results[mode]['queries_per_s']:.0f} queries/s, {ms * 1e3:.1f} us/step (append {app_us:.1f} us), "
             f"step {results[mode]['step_gbs']:.0f} GB/s of gate keys + selected K/V")
     worst = min(results, key=lambda m: results[m]["queries_per_s"])
@@ -478,6 +550,14 @@ def run_serve(args):
         "config": {"workload": args.workload, "batch": w.batch, "context": f"{int(lens0.min())}..{int(lens0.max())}",
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": 128, "budget_tokens": budget,
                    "kv_layout": w.layout, "mode": f"{worst} (slower of {','.join(results)})", "launch": "eager"},
+        "roofline": {"bound": "hbm", "kernel": "sas_sparse_decode (decode_kernel)",
+                     "achieved": round(r["attend_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(r["attend_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": r["kv_bytes"], "bytes_note": "selected K/V blocks of the last step",
+                     "avg_launch_us": round(r["attend_us"], 2)},
+        "selection": {"kernel": "sas_gate_topk (gate_topk_kernel)", "avg_launch_us": round(r["select_us"], 2),
+                      "bytes_per_launch": r["gk_bytes"], "achieved_gbs": round(r["select_gbs"], 1),
+                      "frac": round(r["select_gbs"] / HBM_PEAK_GBS, 4)},
         "step_hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
         "modes": {m: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in d.items()}
                   for m, d in results.items()},
@@ -540,6 +620,15 @@ def main():
     layers = []
     for l in range(args.layers):
         w = wl.named(args.workload, seed=100 + l, device=dev, budget=args.budget)
+        planted = False
+        if w.planted is not None and not args.no_cpu_baseline:
+            # the planted relevance spikes: their direction is the test recipe's
+            # (tests/planting.py, which reads the oracle's gate query), so they
+            # ride with the oracle leg
+            sys.path.insert(0, os.path.join(ROOT, "tests"))
+            from planting import plant
+            plant(w)
+            planted = True
         shape = ops.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides)
         gk = torch.zeros((w.n_pages, w.n_kv_heads, 128), dtype=torch.bfloat16, device=dev)
         lens = wl.host(w.seq_lens)
@@ -547,7 +636,7 @@ def main():
         blk = np.concatenate([np.arange(int(L) // 64, dtype=np.int32) for L in lens])
         ops.pool_blocks(shape, w.k_pool, w.block_table, torch.as_tensor(seq, device=dev),
                         torch.as_tensor(blk, device=dev), w.w_k, w.w_knorm, w.theta, gk)
-        layers.append(dict(w=w, gk=gk))
+        layers.append(dict(w=w, gk=gk, planted=planted))
         torch.cuda.synchronize()
         log(f"layer {l}: {args.workload} inputs drawn and gate keys pooled")
     w0 = layers[0]["w"]
@@ -666,12 +755,32 @@ def main():
             ev1.record(stream)
             torch.cuda.synchronize()
             dom_ms = ev0.elapsed_time(ev1) / args.steps
-        dom_b = kv_b + gk_b + ex_b if fused else kv_b
+        # algorithmic bytes: the gate keys of every candidate and the selected
+        # K/V blocks (the queries, weights, indices and outputs the fused
+        # launch also moves are reported apart, not counted)
+        dom_b = kv_b + gk_b if fused else kv_b
+        graph_us = None
+        if not args.graph:  # the same steps replayed from one HIP graph per layer
+            graphs = []
+            for l in range(len(layers)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step_eager(l)
+                graphs.append(g)
+            for i in range(max(args.warmup, len(layers))):
+                graphs[i % len(layers)].replay()
+            torch.cuda.synchronize()
+            tg = time.perf_counter()
+            for i in range(args.steps):
+                graphs[i % len(layers)].replay()
+            torch.cuda.synchronize()
+            graph_us = (time.perf_counter() - tg) * 1e6 / args.steps
+            del graphs
         results[mode] = dict(queries_per_s=w0.batch * args.steps / elapsed, ms_per_step=ms,
                              decode_ms=dec_ms, decode_gbs=kv_b / (dec_ms * 1e-3) / 1e9,
                              dominant_ms=dom_ms, dominant_bytes=dom_b, dominant_gbs=dom_b / (dom_ms * 1e-3) / 1e9,
-                             step_gbs=(kv_b + gk_b + ex_b) / (ms * 1e-3) / 1e9, kv_bytes=kv_b, gk_bytes=gk_b,
-                             other_bytes=ex_b,
+                             step_gbs=(kv_b + gk_b) / (ms * 1e-3) / 1e9, kv_bytes=kv_b, gk_bytes=gk_b,
+                             other_bytes=ex_b, graph_us_per_step=graph_us,
                              attended_tokens_per_query=float(np.mean([c.sum() for c in cnts])) * 64 / (
                                  w0.batch * w0.n_kv_heads),
                              step_us_p10=p10, step_us_p50=p50, step_us_p90=p90, fused=float(fused),
@@ -710,11 +819,18 @@ def main():
                      "frac": round(r["dominant_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(args.workload, args.budget,
                                                  "step_kernel" if r["fused"] else "decode_kernel"),
-                     "bytes_per_launch": r["dominant_bytes"], "avg_launch_us": round(r["dominant_ms"] * 1e3, 2)},
+                     "bytes_per_launch": r["dominant_bytes"], "avg_launch_us": round(r["dominant_ms"] * 1e3, 2),
+                     "bytes_note": ("gate keys of every candidate + selected K/V blocks" if r["fused"] else
+                                    "selected K/V blocks"),
+                     "other_bytes_per_launch": r["other_bytes"] if r["fused"] else None},
         "attention_alone": {"kernel": "sas_sparse_decode (decode_kernel)", "avg_launch_us": round(r["decode_ms"] * 1e3, 2),
                             "bytes_per_launch": r["kv_bytes"], "achieved_gbs": round(r["decode_gbs"], 1),
                             "frac": round(r["decode_gbs"] / HBM_PEAK_GBS, 4)},
         "read_ceiling": ceiling,
+        "hip_graph": (None if r["graph_us_per_step"] is None else
+                      {"us_per_step": round(r["graph_us_per_step"], 2),
+                       "queries_per_s": round(w0.batch * 1e6 / r["graph_us_per_step"], 1),
+                       "note": "the same steps replayed from one HIP graph per layer (eager is the primary figure)"}),
         "step_hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
         "pooling": {"kernel": "sas_pool_blocks (pool_kernel), every complete block of a layer, off the step",
                     "ms_per_layer": round(pool_ms, 4), "bytes": pool_bytes,
@@ -731,6 +847,7 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layers[0], args.budget, worst == "gated", args.cpu_seconds)
         log(f"cpu baseline: {line['cpu_baseline']['value']:.1f} queries/s on {line['cpu_baseline']['cores']} threads")
+        line["selection_check"] = selection_check(layers[0], decs[0], args.budget)
     print(json.dumps(line), flush=True)
     if args.backward:
         print(json.dumps(time_backward(args, layers, w0)), flush=True)

@@ -146,8 +146,9 @@ sas_status sas_append_kv(const sas_shape *shape, const void *k_new, const void *
  * Outputs ([B][Hkv][budget/64] unless noted; the selection ascending, the
  * local block last, padded with -1 / 0):
  *   sel    int32  selected block indices
- *   gates  fp32   sigmoid(score) per selected historical block, 1 for the
- *                 local block (nullable: not written)
+ *   gates  fp32   sigmoid(score) per selected historical block (a NaN
+ *                 score counts as -inf here too: gate 0), 1 for the local
+ *                 block (nullable: not written)
  *   cnt    int32  [B][Hkv] number of selected blocks (>= 1)
  *   scores fp32   [B][Hkv][max_blocks] block scores (entries c >= l are -inf)
  * budget_tokens: a positive multiple of 64, at most 64 * 256.
@@ -173,7 +174,9 @@ sas_status sas_gate_topk(const sas_shape *shape, const void *q, const void *w_q,
  * workspace: device scratch of at least
  * sas_sparse_decode_workspace_bytes(shape, max_sel) bytes (partial results
  * when a (sequence, KV head) is split across workgroups; no initial contents
- * needed).  Calls that overlap in time must not share a workspace.
+ * needed).  Calls that overlap in time must not share a workspace.  The split,
+ * and so the size, follows the compute-unit count of the device current at
+ * the call (read once per device and cached; 256 when no device is visible).
  */
 size_t sas_sparse_decode_workspace_bytes(const sas_shape *shape, int32_t max_sel);
 sas_status sas_sparse_decode(const sas_shape *shape, const void *q, const void *k_pool,
@@ -232,8 +235,9 @@ sas_status sas_sparse_decode_ex(const sas_shape *shape, const void *q, const voi
  *                   attends with each pair split over several workgroups;
  *   SAS_STEP_TWO_LAUNCHES  the kernels of the two calls above;
  *   SAS_STEP_AUTO   fused when there are more (sequence, KV head) pairs than
- *                   half the GPU's 256 compute units; otherwise sliced for
- *                   block tables over 1,024 blocks, else two launches.
+ *                   half the current device's compute units; otherwise
+ *                   sliced for block tables over 1,024 blocks, else two
+ *                   launches.
  *
  * Arguments as for the two calls, with max_sel = budget_tokens / 64:
  *   aggregate  SAS_AGG_MEAN or SAS_AGG_MAX

@@ -1,6 +1,8 @@
 // C ABI of libsas: argument checks, workspace carving, kernel launches.
 #include <math.h>
 #include <stdarg.h>
+
+#include <atomic>
 #include <stdio.h>
 #include <string.h>
 
@@ -38,6 +40,27 @@ sas_status hip_status(hipError_t e, const char *what) {
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Compute units of the current device, read once per device and cached (the
+// decode split and the sliced selection size their grids by it).  256, the
+// MI355X's count, when no device is visible (host-only workspace queries).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int c = g_cus[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  g_cus[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -332,7 +355,7 @@ struct DecodeWorkspace {
   size_t part_o, part_ml, total;  // byte offsets and size
 };
 DecodeWorkspace decode_workspace(const sas_shape *shape, int32_t max_sel) {
-  sas::DecodeSplit sp = sas::decode_split(shape->batch, shape->n_kv_heads, max_sel);
+  sas::DecodeSplit sp = sas::decode_split(shape->batch, shape->n_kv_heads, max_sel, device_cus());
   const size_t slots = (size_t)shape->batch * shape->n_q_heads * sp.wg_per_unit;
   DecodeWorkspace w;
   w.part_o = 0;
@@ -364,7 +387,7 @@ sas_status decode_params(const sas_shape *shape, const void *q, const void *k_po
   if (!(sm_scale > 0.f)) return fail(SAS_ERR_INVALID_ARG, "sm_scale must be positive");
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(SAS_ERR_UNSUPPORTED, "q, k_pool and v_pool must be 16-byte aligned");
-  const sas::DecodeSplit sp = sas::decode_split(shape->batch, shape->n_kv_heads, max_sel);
+  const sas::DecodeSplit sp = sas::decode_split(shape->batch, shape->n_kv_heads, max_sel, device_cus());
   p.q = (const uint16_t *)q;
   p.k_pool = (const uint16_t *)k_pool;
   p.v_pool = (const uint16_t *)v_pool;
@@ -439,7 +462,7 @@ int step_path(const sas_shape *shape, int32_t budget_tokens, int32_t path) {
   if (path != SAS_STEP_AUTO) return path;
   const int n_sel = budget_tokens / SAS_BLOCK;
   const bool fits = sas::step_fits(shape->n_q_heads / shape->n_kv_heads, shape->max_blocks, n_sel);
-  if (fits && sas::decode_split(shape->batch, shape->n_kv_heads, n_sel).wg_per_unit == 1) return SAS_STEP_FUSED;
+  if (fits && sas::decode_split(shape->batch, shape->n_kv_heads, n_sel, device_cus()).wg_per_unit == 1) return SAS_STEP_FUSED;
   return fits && shape->max_blocks > 1024 ? SAS_STEP_SLICED : SAS_STEP_TWO_LAUNCHES;
 }
 
@@ -457,7 +480,7 @@ StepWorkspace step_workspace(const sas_shape *shape, int32_t budget_tokens, int 
   w.total = w.scores + align256((size_t)shape->batch * shape->n_kv_heads * shape->max_blocks * sizeof(float));
   if (path == SAS_STEP_SLICED) {
     int slices, slice_len;
-    sas::gate_slice_layout(shape->batch, shape->n_kv_heads, shape->max_blocks, &slices, &slice_len);
+    sas::gate_slice_layout(shape->batch, shape->n_kv_heads, shape->max_blocks, device_cus(), &slices, &slice_len);
     const size_t entries = (size_t)shape->batch * shape->n_kv_heads * slices * n_sel;
     w.gq = w.total;
     w.cand_key = w.gq + align256((size_t)shape->batch * shape->n_q_heads * SAS_GATE_DIM * sizeof(float));
@@ -514,7 +537,7 @@ sas_status sas_decode_step(const sas_shape *shape, const void *q, const void *w_
   if (!p.g.scores) p.g.scores = (float *)(ws + wl.scores);
   hipError_t e;
   if (how == SAS_STEP_SLICED) {
-    sas::gate_slice_layout(shape->batch, shape->n_kv_heads, shape->max_blocks, &p.g.slices, &p.g.slice_len);
+    sas::gate_slice_layout(shape->batch, shape->n_kv_heads, shape->max_blocks, device_cus(), &p.g.slices, &p.g.slice_len);
     p.g.slot_len = ((p.g.slice_len > 512 ? p.g.slice_len : 512) + 7) / 8 * 8;
     p.g.batch = shape->batch;
     p.g.gq = (float *)(ws + wl.gq);

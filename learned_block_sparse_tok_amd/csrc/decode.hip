@@ -101,11 +101,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   }
 }
 
-DecodeSplit decode_split(int batch, int n_kv_heads, int max_sel) {
+DecodeSplit decode_split(int batch, int n_kv_heads, int max_sel, int cus) {
   // one 8-wave workgroup per CU; a (sequence, KV head) spans several
   // workgroups only when there are fewer units than CUs
   const int units = batch * n_kv_heads;
-  const int cus = 256;
   int wg = cus / units;
   const int max_wg = (max_sel + kWaves - 1) / kWaves;  // >= 1 block per wave
   wg = wg > max_wg ? max_wg : wg;

@@ -415,11 +415,11 @@ hipError_t launch_gate_topk(const GateParams &p, int batch, hipStream_t st) {
   return hipGetLastError();
 }
 
-void gate_slice_layout(int batch, int n_kv_heads, int max_blocks, int *slices, int *slice_len) {
+void gate_slice_layout(int batch, int n_kv_heads, int max_blocks, int cus, int *slices, int *slice_len) {
   // about two workgroups per CU over the pairs, slices of at least 64
   // candidates, and every slice starting inside the block-table row
   const int pairs = batch * n_kv_heads;
-  int sl = (512 + pairs - 1) / pairs;
+  int sl = (2 * cus + pairs - 1) / pairs;
   const int most = (max_blocks + 63) / 64;
   sl = sl > most ? most : sl;
   sl = sl > kMaxSlices ? kMaxSlices : sl;

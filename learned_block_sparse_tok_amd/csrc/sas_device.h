@@ -101,9 +101,17 @@ __device__ __forceinline__ float wave_sum(float x) {
 // completion is awaited explicitly with wait_vm, and every compiler-visible
 // load must be complete before the first copy is issued (a later wait the
 // compiler computes for such a load would not account for the copies).
+// The asm clobbers M0, which the compiler reserves: that is sound only while
+// no compiler-generated code in the kernel keeps a value in M0, and while no
+// other vector-memory instruction falls between the first copy and the
+// drain.  tests/test_prefill_asm.py checks both on the built assembly, so
+// the compiler's warning about the reserved register is silenced here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void copy16(const void *src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // s_waitcnt with only the vector-memory counter: at most n loads outstanding
 template <int n>

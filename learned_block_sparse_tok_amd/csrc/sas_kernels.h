@@ -71,11 +71,12 @@ struct DecodeParams {
   float scale_log2;         // sm_scale * log2(e)
 };
 
-// Decode work split: waves per (sequence, KV head) and blocks per wave.
+// Decode work split: waves per (sequence, KV head) and blocks per wave, for
+// a device of `cus` compute units (one 8-wave workgroup per CU).
 struct DecodeSplit {
   int wg_per_unit, waves_per_unit, blocks_per_wave;
 };
-DecodeSplit decode_split(int batch, int n_kv_heads, int max_sel);
+DecodeSplit decode_split(int batch, int n_kv_heads, int max_sel, int cus);
 
 // The fused decode step: the selection's and the attention's parameter blocks
 // (the attention with one workgroup per (sequence, KV head)).
@@ -86,9 +87,10 @@ struct StepParams {
 bool step_fits(int group, int max_blocks, int n_sel);
 
 constexpr int kMaxSlices = 16;  // slices of one pair's candidates in the sliced selection
-// Slices per pair and their length for the sliced selection; every slice
-// starts inside the block-table row ((slices - 1) * slice_len < max_blocks).
-void gate_slice_layout(int batch, int n_kv_heads, int max_blocks, int *slices, int *slice_len);
+// Slices per pair and their length for the sliced selection (about two
+// workgroups per compute unit of a `cus`-CU device); every slice starts
+// inside the block-table row ((slices - 1) * slice_len < max_blocks).
+void gate_slice_layout(int batch, int n_kv_heads, int max_blocks, int cus, int *slices, int *slice_len);
 
 struct PrefillParams {
   const uint16_t *q;            // [T][Hq][128]

@@ -85,7 +85,10 @@ __device__ __forceinline__ void wave_select_emit(const uint32_t *keys, int n, in
       prefix |= d << shift;
       mask |= 0xFFu << shift;
       if (bin_cnt == krem) {  // the whole bin is taken: every key >= prefix
-        T = prefix - 1u;      // prefix > 0 here: some keys lie below the bin
+        // prefix == 0 (all digits so far 0) only when every non-zero key left
+        // lies in this bin, which holds when padding (key 0) follows fewer
+        // non-zero keys than n: then every non-zero key is taken (keys > 0)
+        T = prefix ? prefix - 1u : 0u;
         krem = 0;
         break;
       }

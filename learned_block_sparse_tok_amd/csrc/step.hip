@@ -30,18 +30,24 @@
 //      (its V tiles reuse the LDS the gate phase held).
 #include "attend.h"
 #include "select.h"
+#include "step_layout.h"
 
 namespace sas {
 
-constexpr int kStepKeys = 16;         // gate keys per 16-lane group per pass (512 per workgroup)
+constexpr int kStepKeys = step_layout::kKeysPerGroup;  // gate keys per 16-lane group per pass (512 per workgroup)
 constexpr int kStepMaxSel = 256;      // selection slots per (sequence, KV head)
 constexpr int kStepBtUnroll = 2;      // block-table entries per thread staged without a loop
-// the gate phase's arrays inside the V tiles: score keys, block-table row, gate queries
-constexpr int kStepKeysOff = 0;
-constexpr int kStepBtOff = 4 * SAS_MAX_BLOCKS_DEV;
-constexpr int kStepVsOff = 8 * SAS_MAX_BLOCKS_DEV;
-static_assert(kStepVsOff + 4 * kMaxGroup * kGateDim <= kWaves * kVTileBytes, "gate phase exceeds the V tiles");
+// the gate phase's arrays inside the V tiles: score keys, block-table row,
+// gate queries (step_layout.h, checked on the host for every width)
+constexpr int kStepKeysOff = step_layout::kKeysOff;
+constexpr int kStepBtOff = step_layout::kBtOff;
+constexpr int kStepVsOff = step_layout::kVsOff;
+static_assert(step_layout::kMaxBlocks == SAS_MAX_BLOCKS_DEV && step_layout::kMaxGroup == kMaxGroup &&
+                  step_layout::kGateDim == kGateDim && step_layout::kVTilesBytes == kWaves * kVTileBytes,
+              "step layout constants disagree with the kernels'");
+static_assert(step_layout::kGroups * 16 == kWaves * 64, "one 16-lane group per 16 threads");
 static_assert(3 * 4 * kMaxSlices * kStepMaxSel <= kWaves * kVTileBytes, "slice lists exceed the V tiles");
+static_assert(3 * 4 * 512 <= kWaves * kVTileBytes, "padded slice lists exceed the V tiles");
 
 // seq_lens, block_table, n_kv_heads and max_blocks also come as leading
 // scalar arguments (copies of sp.g's): the first loads need only these, and
@@ -117,7 +123,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(const int32_t *__r
 #pragma unroll
     for (int u = 0; u < kStepKeys; ++u)
       v[u] = __builtin_nontemporal_load(  // read once: kept out of the caches
-          reinterpret_cast<const u32x4 *>(gkh + (int64_t)btl[min(base + 32 * u + grp, n)] * page_stride));
+          reinterpret_cast<const u32x4 *>(gkh + (int64_t)btl[step_layout::gather_slot(base, u, grp, n)] * page_stride));
   };
   gather(0);
   auto project = [&](int b) {  // lane o of the group ends with row o of batch b

@@ -299,13 +299,15 @@ static int int_cmp(const void *pa, const void *pb) {
 
 /* Continuous gates of a selection of cnt blocks (the last one local):
  * g = sigmoid(score) for the historical blocks, 1 for the local block, 0 for
- * the padding up to n_sel. */
+ * the padding up to n_sel.  A NaN score counts as -inf here as in the
+ * ranking (READING), so its gate is sigmoid(-inf) = 0. */
 void sas_oracle_block_gates(const float *scores, const int32_t *sel, int32_t cnt, int32_t n_sel,
                             float *gates) {
   for (int i = 0; i < n_sel; ++i) {
-    if (i < cnt - 1)
-      gates[i] = (float)(1.0 / (1.0 + exp(-(double)scores[sel[i]])));
-    else
+    if (i < cnt - 1) {
+      double sc = isnan(scores[sel[i]]) ? -INFINITY : (double)scores[sel[i]];
+      gates[i] = (float)(1.0 / (1.0 + exp(-sc)));
+    } else
       gates[i] = i == cnt - 1 ? 1.0f : 0.0f;
   }
 }

@@ -1,21 +1,16 @@
-"""GPU-side test glue: run the libsas path on a workload and compare it with
-the oracle, with tie accounting for the Top-K."""
+"""GPU-side test glue: run the libsas path on a workload (the comparison with
+the oracle and its tie accounting are in compare.py)."""
 from __future__ import annotations
-
-import itertools
-import math
 
 import numpy as np
 import torch
 
 import oracle
-from harness import SM_SCALE, Host, complete_blocks
+from compare import (OUT_MAX_ABS, OUT_MEAN_ABS, TIE_REL, assert_out_close, compare_selection,  # noqa: F401
+                     compare_step, topk_band)
+from harness import complete_blocks
 from learned_block_sparse_tok_amd import ops
 from learned_block_sparse_tok_amd import workloads as wl
-
-TIE_REL = 1e-3       # boundary band: |S_c - S_K| <= 1e-3 * max(|S_K|, 1)
-OUT_MAX_ABS = 2e-2   # attention outputs vs the fp64 oracle, bf16 inputs
-OUT_MEAN_ABS = 2e-3
 
 
 def shape_of(w: wl.Workload) -> ops.SasShape:
@@ -70,112 +65,3 @@ def gpu_prefill(w: wl.Workload, gk: torch.Tensor, gated: bool, budget: int, posi
 
 def bf16_out(t: torch.Tensor) -> np.ndarray:
     return oracle.bf16_to_f64(wl.host(t))
-
-
-def topk_band(scores: np.ndarray, k: int):
-    """K-th best oracle score under (score desc, index asc) and the tie band."""
-    n = len(scores)
-    order = np.lexsort((np.arange(n), -np.where(np.isnan(scores), -np.inf, scores).astype(np.float64)))
-    sk = float(scores[order[k - 1]])
-    tol = TIE_REL * max(abs(sk), 1.0)
-    band = set(np.nonzero(np.abs(scores.astype(np.float64) - sk) <= tol)[0].tolist())
-    return sk, band
-
-
-def compare_selection(g: dict, o: dict, lens: np.ndarray, budget: int):
-    """Selection parity: bit-exact outside the boundary band of each
-    (sequence, KV head); inside it both sides must take the same number of
-    candidates.  Returns the (s, kvh) pairs whose sets differ (ties)."""
-    B, Hkv = o["cnt"].shape
-    ties = []
-    for s in range(B):
-        n = (int(lens[s]) - 1) // 64
-        k = min(budget // 64 - 1, n)
-        for h in range(Hkv):
-            assert g["cnt"][s, h] == o["cnt"][s, h] == k + 1, (s, h)
-            gs, os_ = g["sel"][s, h], o["sel"][s, h]
-            assert gs[k] == os_[k] == n and np.all(gs[k + 1:] == -1)
-            assert np.all(np.diff(gs[:k + 1]) > 0)
-            if np.array_equal(gs, os_):
-                continue
-            assert 0 < k < n, (s, h, gs, os_)
-            _, band = topk_band(o["scores"][s, h, :n], k)
-            gset, oset = set(gs[:k].tolist()), set(os_[:k].tolist())
-            assert gset - band == oset - band, (s, h, sorted(gset ^ oset))
-            assert len(gset & band) == len(oset & band)
-            ties.append((s, h))
-    return ties
-
-
-def alternative_outputs(h: Host, o: dict, s: int, kvh: int, gsel: np.ndarray, gated: bool, budget: int,
-                        limit: int = 64, gate_mode: str = "scale"):
-    """Oracle outputs of the G query heads of (s, kvh) under the valid
-    resolution of the tie band whose selected set equals gsel's, found by
-    enumerating every valid resolution on the oracle side (None when there
-    are more than `limit`)."""
-    w = h.w
-    n = (int(h.lens[s]) - 1) // 64
-    k = min(budget // 64 - 1, n)
-    sc = o["scores"][s, kvh, :n]
-    _, band = topk_band(sc, k)
-    fixed = set(o["sel"][s, kvh, :k].tolist()) - band
-    need = k - len(fixed)
-    band = sorted(band)
-    if math.comb(len(band), need) > limit:
-        return None
-    want = set(gsel[:k].tolist())
-    for comb in itertools.combinations(band, need):
-        chosen = sorted(fixed | set(comb))
-        if set(chosen) != want:
-            continue
-        n_sel = budget // 64
-        sel = np.full((w.batch, w.n_kv_heads, n_sel), -1, np.int32)
-        cnt = np.ones((w.batch, w.n_kv_heads), np.int32)
-        sel[:, :, 0] = 0
-        sel[s, kvh, :k] = chosen
-        sel[s, kvh, k] = n
-        cnt[s, kvh] = k + 1
-        gates = np.zeros_like(sel, dtype=np.float32)
-        gates[s, kvh] = oracle.block_gates(sc, sel[s, kvh], k + 1)
-        pairs = np.array([[s, kvh * w.group + g] for g in range(w.group)], np.int32)
-        return oracle.attend(h.q, h.k, h.v, h.bt, w.strides, w.n_kv_heads, h.lens, sel,
-                             gates if gated else None, cnt, SM_SCALE, pairs=pairs, gate_mode=gate_mode)
-    raise AssertionError("GPU selection is not a valid resolution of the tie band")
-
-
-def assert_out_close(got: np.ndarray, want: np.ndarray, what=""):
-    err = np.abs(got - want)
-    assert np.all(np.isfinite(got)), what
-    assert err.max() <= OUT_MAX_ABS, (what, float(err.max()))
-    assert err.mean() <= OUT_MEAN_ABS, (what, float(err.mean()))
-    return float(err.max()), float(err.mean())
-
-
-def compare_step(h: Host, g: dict, o: dict, gated: bool, budget: int, gate_atol: float = 2e-4,
-                 gate_mode: str = "scale"):
-    """Whole-step parity with tie accounting.  Returns (n_ties, n_skipped).
-    gate_atol: the two sides' gate keys may differ by one bf16 rounding, which
-    moves a score by ~1e-4 and its sigmoid gate by less."""
-    w = h.w
-    ties = compare_selection(g, o, h.lens, budget)
-    tie_set = set(ties)
-    mask = np.ones((w.batch, w.n_q_heads), bool)
-    skipped = 0
-    for (s, kvh) in ties:
-        heads = slice(kvh * w.group, (kvh + 1) * w.group)
-        mask[s, heads] = False
-        alt = alternative_outputs(h, o, s, kvh, g["sel"][s, kvh], gated, budget, gate_mode=gate_mode)
-        if alt is None:
-            skipped += 1
-            continue
-        assert_out_close(g["out"][s, heads], alt, f"tie-resolved output s={s} kvh={kvh}")
-    if mask.any():
-        assert_out_close(g["out"][mask], o["out"][mask], "output")
-    # gates of the blocks both sides selected
-    for s in range(w.batch):
-        for kvh in range(w.n_kv_heads):
-            if (s, kvh) in tie_set:
-                continue
-            c = o["cnt"][s, kvh]
-            np.testing.assert_allclose(g["gates"][s, kvh, :c], o["gates"][s, kvh, :c], rtol=0, atol=gate_atol)
-    return len(ties), skipped

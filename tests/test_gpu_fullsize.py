@@ -18,8 +18,9 @@ import torch
 import oracle
 import dataclasses
 
-from gpu_harness import assert_out_close, bf16_out, compare_step, gpu_pool, gpu_prefill, prefill_gate_keys
-from harness import SM_SCALE, Host, oracle_step
+from gpu_harness import (assert_out_close, bf16_out, compare_selection, compare_step, gpu_pool, gpu_prefill,
+                         prefill_gate_keys)
+from harness import SM_SCALE, Host, complete_blocks, oracle_step
 from learned_block_sparse_tok_amd import ops
 from learned_block_sparse_tok_amd import workloads as wl
 
@@ -84,6 +85,39 @@ def check_sampled(w, dec, seqs, gated, budget):
     return compare_step(h, g, o, gated, budget)
 
 
+def check_every_unit(w, dec, budget):
+    """Selection of every (sequence, KV head) of the full batch against the
+    oracle's gate stage: the oracle pools every complete block from a host
+    copy of K and runs its gate scores and full sort; sel and cnt must match
+    bit for bit outside the boundary band (compare_selection), and the gates
+    of every selected block within the stage tolerance (for a tie unit, the
+    oracle's gates of the band resolution the GPU took).  Returns the ties."""
+    lens = wl.host(w.seq_lens).astype(np.int32)
+    k_host = wl.host(w.k_pool)
+    bt = wl.host(w.block_table)
+    gk_o = np.zeros((w.n_pages, w.n_kv_heads, wl.GATE_DIM), np.uint16)
+    seq, blk = complete_blocks(lens)
+    oracle.pool_blocks(k_host, bt, w.strides, w.n_kv_heads, seq, blk, wl.host(w.w_k), wl.host(w.w_knorm), w.theta,
+                       gk_o)
+    del k_host
+    sel, gates, cnt, scores = oracle.gate_topk(wl.host(w.q), wl.host(w.w_q), wl.host(w.w_qnorm), gk_o, bt, lens,
+                                               w.theta, budget, w.n_kv_heads)
+    o = dict(sel=sel, gates=gates, cnt=cnt, scores=scores)
+    g = dict(sel=wl.host(dec.sel), gates=wl.host(dec.gates), cnt=wl.host(dec.cnt))
+    ties = compare_selection(g, o, lens, budget)
+    tie_set = set(ties)
+    for s in range(w.batch):
+        n = (int(lens[s]) - 1) // 64
+        for kvh in range(w.n_kv_heads):
+            c = int(cnt[s, kvh])
+            want = gates[s, kvh, :c]
+            if (s, kvh) in tie_set:
+                want = oracle.block_gates(scores[s, kvh, :n], g["sel"][s, kvh], c)[:c]
+            np.testing.assert_allclose(g["gates"][s, kvh, :c], want, rtol=0, atol=2e-4)
+    say(f"  every unit's selection: {w.batch * w.n_kv_heads} units, boundary ties {len(ties)}")
+    return ties
+
+
 FULL = [
     ("qwen3_4b", 2048, [0, 5]),
     ("qwen3_8b", 1024, [0, 17, 31]),
@@ -99,11 +133,13 @@ def test_full_size_sampled_parity(name, budget, seqs):
     for gated in (False, True):
         say(f"{name} budget {budget} {'gated' if gated else 'plain'}: sequences {seqs}")
         dec = gpu_full_step(w, gk, gated, budget)
-        ties, skipped = check_sampled(w, dec, seqs, gated, budget)
-        say(f"  boundary ties {ties}, unenumerated {skipped}")
+        ties = check_sampled(w, dec, seqs, gated, budget)
+        say(f"  boundary ties {ties}")
         # every unit of the full batch selected exactly budget/64 blocks
         assert np.all(wl.host(dec.cnt) == budget // 64)
         assert np.all(np.isfinite(bf16_out(dec.out)))
+        if gated:  # the selection is the same in both modes: check every unit once
+            check_every_unit(w, dec, budget)
 
 
 def test_full_size_qwen3_14b_planted_recall():
@@ -121,8 +157,9 @@ def test_full_size_qwen3_14b_planted_recall():
             tot += w.planted.shape[2]
     say(f"qwen3_14b planted recall {hit}/{tot}")
     assert hit == tot
-    ties, skipped = check_sampled(w, dec, [1], True, 2048)
-    say(f"  boundary ties {ties}, unenumerated {skipped}")
+    check_every_unit(w, dec, 2048)
+    ties = check_sampled(w, dec, [1], True, 2048)
+    say(f"  boundary ties {ties}")
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["scatter_then_pool", "append_kv"])
@@ -176,8 +213,9 @@ def test_ragged_incremental_serving(fused):
             torch.cuda.synchronize()
             seqs = [step % 64, (step * 7 + 3) % 64]
             say(f"ragged step {step}: sequences {seqs} lengths {lens[seqs].tolist()}")
-            ties, skipped = check_sampled(w, dec, seqs, True, w.budget)
-            say(f"  boundary ties {ties}, unenumerated {skipped}")
+            ties = check_sampled(w, dec, seqs, True, w.budget)
+            say(f"  boundary ties {ties}")
+            check_every_unit(w, dec, w.budget)
     # incrementally pooled keys vs the oracle's pooling of the same blocks
     # (their pages gathered into a compact pool; block indices kept, since
     # they set the gate-key RoPE position)
@@ -224,8 +262,25 @@ def test_prefill_full_size_sampled_parity():
         sel, gates, cnt, scores, out = oracle.prefill(wl.host(w.q), h.k, h.v, h.bt[0], w.strides, w.n_kv_heads, gk_o,
                                                       h.w_q, h.wqn, w.theta, w.budget, gated, SM_SCALE, positions=pos)
         o = dict(gate_keys=gk_o, sel=sel, gates=gates, cnt=cnt, scores=scores, out=out)
-        ties, skipped = compare_step(h, g, o, gated, w.budget)
-        say(f"  boundary ties {ties}, unenumerated {skipped}")
+        ties = compare_step(h, g, o, gated, w.budget)
+        say(f"  boundary ties {ties}")
+    # the selection of every 8th position (4,096 positions x 8 KV heads)
+    # against the oracle's gate stage
+    every = np.arange(3, T, 8)
+    g = gpu_prefill(w, gk, True, w.budget, positions=every)
+    bt_all = np.ascontiguousarray(np.broadcast_to(h.bt[0], (len(every), h.bt.shape[1])))
+    lens = (every + 1).astype(np.int32)
+    sel, gates, cnt, scores = oracle.gate_topk(wl.host(w.q)[every], h.w_q, h.wqn, gk_o, bt_all, lens, w.theta,
+                                               w.budget, w.n_kv_heads)
+    ties = compare_selection(g, dict(sel=sel, gates=gates, cnt=cnt, scores=scores), lens, w.budget)
+    tie_set = set(ties)
+    for i in range(len(every)):
+        for kvh in range(w.n_kv_heads):
+            c = int(cnt[i, kvh])
+            want = gates[i, kvh, :c] if (i, kvh) not in tie_set else oracle.block_gates(
+                scores[i, kvh, :(int(lens[i]) - 1) // 64], g["sel"][i, kvh], c)[:c]
+            np.testing.assert_allclose(g["gates"][i, kvh, :c], want, rtol=0, atol=2e-4)
+    say(f"  selection of {len(every)} positions x {w.n_kv_heads} KV heads: boundary ties {len(ties)}")
 
 
 def test_gate_backward_full_size():
@@ -309,5 +364,5 @@ def test_prefill_long_sequence_uses_the_per_position_selection():
     sel, gates, cnt, scores, out = oracle.prefill(wl.host(w.q), h.k, h.v, h.bt[0], w.strides, w.n_kv_heads, gk_o,
                                                   h.w_q, h.wqn, w.theta, w.budget, True, SM_SCALE, positions=pos)
     o = dict(gate_keys=gk_o, sel=sel, gates=gates, cnt=cnt, scores=scores, out=out)
-    ties, skipped = compare_step(h, g, o, True, w.budget)
-    say(f"prefill T={T}: boundary ties {ties}, unenumerated {skipped}")
+    ties = compare_step(h, g, o, True, w.budget)
+    say(f"prefill T={T}: boundary ties {ties}")

@@ -285,6 +285,22 @@ def test_select_matches_lexsort():
         assert gates[k] == 1.0 and np.all(gates[k + 1:] == 0) and np.all(sel[k + 1:] == -1)
 
 
+def test_nan_and_minus_inf_scores_rank_last_with_gate_zero():
+    # a NaN score ranks as -inf (below every finite score, ties by index with
+    # real -inf scores) and, selected when the budget covers every candidate,
+    # gets the gate of -inf: scipy's expit(-inf) = 0
+    sc = np.array([0.3, np.nan, -np.inf, 1.5, np.nan, -2.0], np.float32)
+    sel, gates, cnt = oracle.select(sc, 6 * 64 + 1, 64 * 4)  # 3 historical blocks
+    assert list(sel[:cnt]) == [0, 3, 5, 6]
+    sel, gates, cnt = oracle.select(sc, 6 * 64 + 1, 64 * 6)  # 5 of 6: the last -inf/NaN by index drops
+    assert list(sel[:cnt]) == [0, 1, 2, 3, 5, 6]
+    sel, gates, cnt = oracle.select(sc, 6 * 64 + 1, 64 * 8)  # every candidate
+    assert cnt == 7
+    want = scipy.special.expit(np.where(np.isnan(sc), -np.inf, sc).astype(np.float64)).astype(np.float32)
+    np.testing.assert_array_equal(gates[:6], want)
+    assert gates[1] == 0.0 and gates[4] == 0.0 and gates[6] == 1.0
+
+
 @pytest.mark.parametrize("budget", [1024, 2048, 4096])
 def test_budget_block_counts(budget):
     # a budget of B tokens selects exactly B/64 blocks once the context holds them
@@ -602,10 +618,12 @@ def _rope_np(v, pos, theta):
     return np.concatenate([z.real, z.imag])
 
 
-def _smooth_gated_loss(h: Host, sel, cnt, d_out, wq, wqn, wk, wkn):
+def _smooth_gated_loss(h: Host, sel, cnt, d_out, wq, wqn, wk, wkn, key_shift=None):
     """sum_h <d_out_h, o_h> of a gated decode step with the selection held
     fixed and every gate recomputed from the parameters (fp64, gate keys not
-    rounded), written directly from the definitions in numpy."""
+    rounded), written directly from the definitions in numpy.  key_shift:
+    optional {(s, kvh, c): vector} added to block c's fp64 gate key, held
+    constant (a straight-through substitution of another key value)."""
     w = h.w
     G = w.group
     q, dO = oracle.bf16_to_f64(h.q), oracle.bf16_to_f64(d_out)
@@ -628,7 +646,10 @@ def _smooth_gated_loss(h: Host, sel, cnt, d_out, wq, wqn, wk, wkn):
                 p = np.concatenate([kb.max(0), kb.min(0), kb.mean(0)])
                 u = wk[kvh] @ p
                 u = u / math.sqrt(np.mean(u * u) + 1e-6) * wkn
-                g[i] = 1.0 / (1.0 + math.exp(-(ghat @ _rope_np(u, 64.0 * c, w.theta)) / math.sqrt(128)))
+                key = _rope_np(u, 64.0 * c, w.theta)
+                if key_shift is not None:
+                    key = key + key_shift[(s, kvh, int(c))]
+                g[i] = 1.0 / (1.0 + math.exp(-(ghat @ key) / math.sqrt(128)))
             gates_all[s, kvh, :len(blocks)] = g
             tok = np.concatenate([np.arange(64 * c, min(64 * c + 64, L)) for c in blocks])
             gtok = np.concatenate([np.full(min(64, L - 64 * c), g[i]) for i, c in enumerate(blocks)])
@@ -668,6 +689,62 @@ def test_gate_backward_matches_finite_differences():
             assert abs(got - fd) <= 1e-6 * max(1.0, abs(fd)) + 1e-9, (name, idx, got, fd)
             checked += abs(fd) > 1e-6
     assert checked >= 12  # most probes land on entries the loss depends on
+
+
+def test_gate_backward_with_stored_keys_matches_straight_through_differences():
+    """round_keys=True (the stored bf16 gate keys in the gate-query gradient,
+    as the forward's scores use them; the form the GPU is compared with) on a
+    paged workload whose block table is a random permutation over extra
+    pages: against central differences of the independent forward in which
+    each selected block's key is its fp64 key plus the constant difference
+    to the stored bf16 key read at that block's page (straight through)."""
+    w = small_paged(seed=29)
+    h = Host(w)
+    assert not np.array_equal(h.bt, np.arange(h.bt.size).reshape(h.bt.shape))
+    gk = oracle_gate_keys(h)
+    sel, _, cnt, _ = oracle.gate_topk(h.q, h.w_q, h.wqn, gk, h.bt, h.lens, w.theta, w.budget, w.n_kv_heads)
+    d_out = wl.bf16_bits(torch.randn(h.q.shape, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16))
+    wq, wk = oracle.bf16_to_f64(h.w_q), oracle.bf16_to_f64(h.w_k)
+    wqn, wkn = h.wqn.astype(np.float64), h.wkn.astype(np.float64)
+    # the constant shift: stored bf16 key (at the block's page) minus the fp64 key at these parameters
+    shift = {}
+    for s in range(w.batch):
+        L = int(h.lens[s])
+        Kd = [dense_kv(h, h.k, s, k) for k in range(w.n_kv_heads)]
+        for kvh in range(w.n_kv_heads):
+            for c in sel[s, kvh, :cnt[s, kvh] - 1]:
+                kb = Kd[kvh][64 * c:64 * c + 64]
+                p = np.concatenate([kb.max(0), kb.min(0), kb.mean(0)])
+                u = wk[kvh] @ p
+                u = u / math.sqrt(np.mean(u * u) + 1e-6) * wkn
+                stored = oracle.bf16_to_f64(gk[int(h.bt[s, c]), kvh])
+                shift[(s, kvh, int(c))] = stored - _rope_np(u, 64.0 * c, w.theta)
+    shifted = sum(float(np.abs(v).max()) > 0 for v in shift.values())
+    assert shifted > 0
+    _, g0 = _smooth_gated_loss(h, sel, cnt, d_out, wq, wqn, wk, wkn, key_shift=shift)
+    bwd = oracle.gate_backward(h.q, h.k, h.v, h.bt, w.strides, w.n_kv_heads, h.lens, sel, g0, cnt, SM_SCALE,
+                               h.w_q, h.wqn, h.w_k, h.wkn, gk, w.theta, d_out, round_keys=True)
+    rng = np.random.default_rng(10)
+    eps = 1e-5
+    params = dict(d_w_q=wq, d_w_qnorm=wqn, d_w_k=wk, d_w_knorm=wkn)
+    checked = 0
+    for name, arr in params.items():
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, n)) for n in arr.shape)
+            plus, minus = [a.copy() for a in params.values()], [a.copy() for a in params.values()]
+            k = list(params).index(name)
+            plus[k][idx] += eps
+            minus[k][idx] -= eps
+            fd = (_smooth_gated_loss(h, sel, cnt, d_out, *plus, key_shift=shift)[0]
+                  - _smooth_gated_loss(h, sel, cnt, d_out, *minus, key_shift=shift)[0]) / (2 * eps)
+            got = bwd[name][idx]
+            assert abs(got - fd) <= 1e-6 * max(1.0, abs(fd)) + 1e-9, (name, idx, got, fd)
+            checked += abs(fd) > 1e-6
+    assert checked >= 12
+    # and the stored keys matter: the unrounded form differs on d_w_q
+    bwd_raw = oracle.gate_backward(h.q, h.k, h.v, h.bt, w.strides, w.n_kv_heads, h.lens, sel, g0, cnt, SM_SCALE,
+                                   h.w_q, h.wqn, h.w_k, h.wkn, gk, w.theta, d_out, round_keys=False)
+    assert np.abs(bwd_raw["d_w_q"] - bwd["d_w_q"]).max() > 1e-9
 
 
 def test_gate_gradient_is_the_derivative_of_the_gated_output():
