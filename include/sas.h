@@ -265,6 +265,31 @@ sas_status sas_decode_step(const sas_shape *shape, const void *q, const void *w_
                            void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * sas_decode_step_noalloc -- sas_decode_step for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments, outputs and bits
+ * without `workspace`.  The library's own scratch array stands in for it: a
+ * file-scope device array of SAS_NOALLOC_SCRATCH_BYTES per device (held by
+ * each device the library runs on until the process ends; its address is
+ * taken once per device, on the first call with that device current).  The
+ * call itself allocates nothing.  A step that would need a larger workspace
+ * (sas_decode_step_workspace_bytes over the limit; the fused path needs
+ * none) fails with SAS_ERR_WORKSPACE and launches nothing.  Every call on a
+ * device shares that device's one array and leaves the last call's partial
+ * results in it: calls that overlap in time on one device (two streams, two
+ * host threads) race and must not be issued; sequential calls on one stream
+ * are safe.  Nothing in the array needs initial contents.
+ */
+#define SAS_NOALLOC_SCRATCH_BYTES (16u << 20)
+sas_status sas_decode_step_noalloc(const sas_shape *shape, const void *q, const void *w_q,
+                                   const float *w_qnorm, const void *gate_keys, const void *k_pool,
+                                   const void *v_pool, const int32_t *block_table,
+                                   const int32_t *seq_lens, double rope_theta, int32_t budget_tokens,
+                                   int32_t aggregate, int32_t gated, int32_t gate_mode, float sm_scale,
+                                   int32_t path, int32_t *sel, float *gates, int32_t *cnt, float *scores,
+                                   void *out, void *stream);
+
+/*
  * Training-time forward of one sequence (every position is a query).  SAS
  * selects KV blocks for each query and trains with a Top-K of 31 historical
  * blocks on 32,768-token sequences (aigc.news release note; "Tencent Hunyuan

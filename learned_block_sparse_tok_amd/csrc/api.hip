@@ -3,6 +3,7 @@
 #include <stdarg.h>
 
 #include <atomic>
+#include <mutex>
 #include <stdio.h>
 #include <string.h>
 
@@ -500,12 +501,18 @@ size_t sas_decode_step_workspace_bytes(const sas_shape *shape, int32_t budget_to
   return step_workspace(shape, budget_tokens, step_path(shape, budget_tokens, path)).total;
 }
 
-sas_status sas_decode_step(const sas_shape *shape, const void *q, const void *w_q, const float *w_qnorm,
-                           const void *gate_keys, const void *k_pool, const void *v_pool,
-                           const int32_t *block_table, const int32_t *seq_lens, double rope_theta,
-                           int32_t budget_tokens, int32_t aggregate, int32_t gated, int32_t gate_mode, float sm_scale,
-                           int32_t path, int32_t *sel, float *gates, int32_t *cnt, float *scores, void *out,
-                           void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+// The decode step on a given workspace.  ws_fixed: the workspace is the
+// no-allocation entry point's scratch array (size ws_bytes), so a shortfall
+// is reported as that array's limit.
+sas_status decode_step_impl(const sas_shape *shape, const void *q, const void *w_q, const float *w_qnorm,
+                            const void *gate_keys, const void *k_pool, const void *v_pool, const int32_t *block_table,
+                            const int32_t *seq_lens, double rope_theta, int32_t budget_tokens, int32_t aggregate,
+                            int32_t gated, int32_t gate_mode, float sm_scale, int32_t path, int32_t *sel,
+                            float *gates, int32_t *cnt, float *scores, void *out, void *workspace,
+                            size_t workspace_bytes, bool ws_fixed, void *stream) {
   if (path < SAS_STEP_AUTO || path > SAS_STEP_SLICED) return fail(SAS_ERR_INVALID_ARG, "unknown step path %d", path);
   if (gated != 0 && gated != 1) return fail(SAS_ERR_INVALID_ARG, "gated must be 0 or 1");
   if (gated && !gates) return fail(SAS_ERR_INVALID_ARG, "gated attention needs the gates output");
@@ -529,8 +536,14 @@ sas_status sas_decode_step(const sas_shape *shape, const void *q, const void *w_
   const StepWorkspace wl = step_workspace(shape, budget_tokens, how);
   if (!workspace) return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(workspace)) return fail(SAS_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
-  if (workspace_bytes < wl.total)
+  if (workspace_bytes < wl.total) {
+    if (ws_fixed)
+      return fail(SAS_ERR_WORKSPACE,
+                  "this step needs %zu bytes of scratch; sas_decode_step_noalloc holds at most %zu (use "
+                  "sas_decode_step with a caller workspace)",
+                  wl.total, workspace_bytes);
     return fail(SAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, wl.total);
+  }
   char *ws = (char *)workspace;
   p.d.part_o = (float *)(ws + wl.part_o);
   p.d.part_ml = (float *)(ws + wl.part_ml);
@@ -552,6 +565,62 @@ sas_status sas_decode_step(const sas_shape *shape, const void *q, const void *w_
     if (e == hipSuccess) e = sas::launch_decode(p.d, shape->batch, hs);
   }
   return hip_status(e, "sas_decode_step launch");
+}
+
+// Scratch of sas_decode_step_noalloc: one copy per device, held until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in); it uses the device address that
+// hipGetSymbolAddress returns, taken once per device with that device current.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[SAS_NOALLOC_SCRATCH_BYTES];
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+sas_status scratch_of_current_device(void **out) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SAS_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (es != hipSuccess || !p) return hip_status(es != hipSuccess ? es : hipErrorInvalidSymbol,
+                                                    "hipGetSymbolAddress(scratch)");
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SAS_OK;
+}
+}  // namespace
+
+extern "C" {
+
+sas_status sas_decode_step(const sas_shape *shape, const void *q, const void *w_q, const float *w_qnorm,
+                           const void *gate_keys, const void *k_pool, const void *v_pool,
+                           const int32_t *block_table, const int32_t *seq_lens, double rope_theta,
+                           int32_t budget_tokens, int32_t aggregate, int32_t gated, int32_t gate_mode, float sm_scale,
+                           int32_t path, int32_t *sel, float *gates, int32_t *cnt, float *scores, void *out,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_step_impl(shape, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens, rope_theta,
+                          budget_tokens, aggregate, gated, gate_mode, sm_scale, path, sel, gates, cnt, scores, out,
+                          workspace, workspace_bytes, false, stream);
+}
+
+sas_status sas_decode_step_noalloc(const sas_shape *shape, const void *q, const void *w_q, const float *w_qnorm,
+                                   const void *gate_keys, const void *k_pool, const void *v_pool,
+                                   const int32_t *block_table, const int32_t *seq_lens, double rope_theta,
+                                   int32_t budget_tokens, int32_t aggregate, int32_t gated, int32_t gate_mode,
+                                   float sm_scale, int32_t path, int32_t *sel, float *gates, int32_t *cnt,
+                                   float *scores, void *out, void *stream) {
+  void *ws = nullptr;
+  const sas_status st = scratch_of_current_device(&ws);
+  if (st) return st;
+  return decode_step_impl(shape, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens, rope_theta,
+                          budget_tokens, aggregate, gated, gate_mode, sm_scale, path, sel, gates, cnt, scores, out,
+                          ws, SAS_NOALLOC_SCRATCH_BYTES, true, stream);
 }
 
 namespace {

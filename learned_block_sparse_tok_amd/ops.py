@@ -50,6 +50,8 @@ _SIGS = {
     "sas_probe_read": (_I32, [_VP, _I32, _I32, _VP, _SZ, _VP]),
     "sas_decode_step": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F64, _I32, _I32, _I32, _I32, _F32, _I32,
                                _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "sas_decode_step_noalloc": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F64, _I32, _I32, _I32, _I32,
+                                       _F32, _I32, _VP, _VP, _VP, _VP, _VP, _VP]),
     "sas_prefill_select": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _F64, _I32, _VP, _VP, _VP, _VP, _VP]),
     "sas_prefill_attend": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _F32, _VP, _VP]),
     "sas_gate_backward_workspace_bytes": (_SZ, [_VP, _I32]),
@@ -209,6 +211,29 @@ def decode_step(shape: SasShape, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, blo
                                _ptr(scores, torch.float32, "scores"), _ptr(out, torch.bfloat16, "out"),
                                _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream))
     _check(st, "sas_decode_step")
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # SAS_NOALLOC_SCRATCH_BYTES
+
+
+def decode_step_noalloc(shape: SasShape, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens, theta,
+                        budget_tokens, sel, gates, cnt, scores, out, sm_scale, gated, stream=None, aggregate="mean",
+                        gate_mode="scale", path="auto"):
+    """sas_decode_step_noalloc: decode_step with the library's per-device
+    scratch array in place of a workspace (no allocation in the call; calls
+    that overlap on one device race)."""
+    st = lib().sas_decode_step_noalloc(ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"),
+                                       _ptr(w_q, torch.bfloat16, "w_q"), _ptr(w_qnorm, torch.float32, "w_qnorm"),
+                                       _ptr(gate_keys, torch.bfloat16, "gate_keys"),
+                                       _ptr(k_pool, torch.bfloat16, "k_pool"), _ptr(v_pool, torch.bfloat16, "v_pool"),
+                                       _ptr(block_table, torch.int32, "block_table"),
+                                       _ptr(seq_lens, torch.int32, "seq_lens"), float(theta), int(budget_tokens),
+                                       AGGREGATE[aggregate], int(bool(gated)), GATE_MODE[gate_mode], float(sm_scale),
+                                       STEP_PATH[path], _ptr(sel, torch.int32, "sel"),
+                                       _ptr(gates, torch.float32, "gates"), _ptr(cnt, torch.int32, "cnt"),
+                                       _ptr(scores, torch.float32, "scores"), _ptr(out, torch.bfloat16, "out"),
+                                       _stream(stream))
+    _check(st, "sas_decode_step_noalloc")
 
 
 class SparseDecoder:
