@@ -34,7 +34,7 @@ def gpu_step(w: wl.Workload, gate_keys: torch.Tensor, gated: bool, budget: int |
     dec.step(w.q, w.w_q, w.w_qnorm, gate_keys, w.k_pool, w.v_pool, w.block_table, w.seq_lens)
     torch.cuda.synchronize()
     return dict(sel=wl.host(dec.sel), gates=wl.host(dec.gates), cnt=wl.host(dec.cnt),
-                scores=wl.host(dec.scores), out=bf16_out(dec.out))
+                scores=wl.host(dec.scores), out=bf16_out(dec.out), gate_keys=wl.host(gate_keys))
 
 
 def prefill_gate_keys(w: wl.Workload) -> torch.Tensor:
@@ -60,7 +60,7 @@ def gpu_prefill(w: wl.Workload, gk: torch.Tensor, gated: bool, budget: int, posi
     torch.cuda.synchronize()
     idx = slice(None) if positions is None else torch.as_tensor(np.asarray(positions), device=dev)
     return dict(sel=wl.host(pf.sel[idx]), gates=wl.host(pf.gates[idx]), cnt=wl.host(pf.cnt[idx]),
-                scores=wl.host(pf.scores[idx]), out=bf16_out(pf.out[idx]))
+                scores=wl.host(pf.scores[idx]), out=bf16_out(pf.out[idx]), gate_keys=wl.host(gk))
 
 
 def bf16_out(t: torch.Tensor) -> np.ndarray:

@@ -18,6 +18,7 @@ import torch
 import oracle
 import dataclasses
 
+from compare import check_gates
 from gpu_harness import (assert_out_close, bf16_out, compare_selection, compare_step, gpu_pool, gpu_prefill,
                          prefill_gate_keys)
 from harness import SM_SCALE, Host, complete_blocks, oracle_step
@@ -77,15 +78,19 @@ def gpu_sample(dec, seqs):
                 scores=wl.host(dec.scores)[seqs], out=bf16_out(dec.out)[seqs])
 
 
-def check_sampled(w, dec, seqs, gated, budget):
+def check_sampled(w, dec, seqs, gated, budget, gk):
+    """The sampled sequences' whole step against the oracle's (its own
+    pooling of their blocks); the GPU's gate keys of those blocks, in the
+    sub-workload's page order, bound the gate differences."""
     sub = sub_workload(w, seqs)
     h = Host(sub)
     o = oracle_step(h, gated, budget)
     g = gpu_sample(dec, seqs)
+    g["gate_keys"] = wl.host(gk)[wl.host(w.block_table)[list(seqs)].reshape(-1)]
     return compare_step(h, g, o, gated, budget)
 
 
-def check_every_unit(w, dec, budget):
+def check_every_unit(w, dec, budget, gk):
     """Selection of every (sequence, KV head) of the full batch against the
     oracle's gate stage: the oracle pools every complete block from a host
     copy of K and runs its gate scores and full sort; sel and cnt must match
@@ -100,6 +105,8 @@ def check_every_unit(w, dec, budget):
     oracle.pool_blocks(k_host, bt, w.strides, w.n_kv_heads, seq, blk, wl.host(w.w_k), wl.host(w.w_knorm), w.theta,
                        gk_o)
     del k_host
+    gk_g = wl.host(gk)
+    wqn = wl.host(w.w_qnorm)
     sel, gates, cnt, scores = oracle.gate_topk(wl.host(w.q), wl.host(w.w_q), wl.host(w.w_qnorm), gk_o, bt, lens,
                                                w.theta, budget, w.n_kv_heads)
     o = dict(sel=sel, gates=gates, cnt=cnt, scores=scores)
@@ -110,10 +117,11 @@ def check_every_unit(w, dec, budget):
         n = (int(lens[s]) - 1) // 64
         for kvh in range(w.n_kv_heads):
             c = int(cnt[s, kvh])
-            want = gates[s, kvh, :c]
+            want = gates[s, kvh]
             if (s, kvh) in tie_set:
-                want = oracle.block_gates(scores[s, kvh, :n], g["sel"][s, kvh], c)[:c]
-            np.testing.assert_allclose(g["gates"][s, kvh, :c], want, rtol=0, atol=2e-4)
+                want = oracle.block_gates(scores[s, kvh, :n], g["sel"][s, kvh], c)
+            check_gates(g["gates"][s, kvh], want, g["sel"][s, kvh], c, bt[s], kvh, wqn, gk_g, gk_o,
+                        what=f"gates s={s} kvh={kvh}")
     say(f"  every unit's selection: {w.batch * w.n_kv_heads} units, boundary ties {len(ties)}")
     return ties
 
@@ -133,13 +141,13 @@ def test_full_size_sampled_parity(name, budget, seqs):
     for gated in (False, True):
         say(f"{name} budget {budget} {'gated' if gated else 'plain'}: sequences {seqs}")
         dec = gpu_full_step(w, gk, gated, budget)
-        ties = check_sampled(w, dec, seqs, gated, budget)
+        ties = check_sampled(w, dec, seqs, gated, budget, gk)
         say(f"  boundary ties {ties}")
         # every unit of the full batch selected exactly budget/64 blocks
         assert np.all(wl.host(dec.cnt) == budget // 64)
         assert np.all(np.isfinite(bf16_out(dec.out)))
         if gated:  # the selection is the same in both modes: check every unit once
-            check_every_unit(w, dec, budget)
+            check_every_unit(w, dec, budget, gk)
 
 
 def test_full_size_qwen3_14b_planted_recall():
@@ -157,8 +165,8 @@ def test_full_size_qwen3_14b_planted_recall():
             tot += w.planted.shape[2]
     say(f"qwen3_14b planted recall {hit}/{tot}")
     assert hit == tot
-    check_every_unit(w, dec, 2048)
-    ties = check_sampled(w, dec, [1], True, 2048)
+    check_every_unit(w, dec, 2048, gk)
+    ties = check_sampled(w, dec, [1], True, 2048, gk)
     say(f"  boundary ties {ties}")
 
 
@@ -213,9 +221,9 @@ def test_ragged_incremental_serving(fused):
             torch.cuda.synchronize()
             seqs = [step % 64, (step * 7 + 3) % 64]
             say(f"ragged step {step}: sequences {seqs} lengths {lens[seqs].tolist()}")
-            ties = check_sampled(w, dec, seqs, True, w.budget)
+            ties = check_sampled(w, dec, seqs, True, w.budget, gk)
             say(f"  boundary ties {ties}")
-            check_every_unit(w, dec, w.budget)
+            check_every_unit(w, dec, w.budget, gk)
     # incrementally pooled keys vs the oracle's pooling of the same blocks
     # (their pages gathered into a compact pool; block indices kept, since
     # they set the gate-key RoPE position)
@@ -277,9 +285,10 @@ def test_prefill_full_size_sampled_parity():
     for i in range(len(every)):
         for kvh in range(w.n_kv_heads):
             c = int(cnt[i, kvh])
-            want = gates[i, kvh, :c] if (i, kvh) not in tie_set else oracle.block_gates(
-                scores[i, kvh, :(int(lens[i]) - 1) // 64], g["sel"][i, kvh], c)[:c]
-            np.testing.assert_allclose(g["gates"][i, kvh, :c], want, rtol=0, atol=2e-4)
+            want = gates[i, kvh] if (i, kvh) not in tie_set else oracle.block_gates(
+                scores[i, kvh, :(int(lens[i]) - 1) // 64], g["sel"][i, kvh], c)
+            check_gates(g["gates"][i, kvh], want, g["sel"][i, kvh], c, h.bt[0], kvh, h.wqn, g["gate_keys"], gk_o,
+                        what=f"gates position {every[i]} kvh={kvh}")
     say(f"  selection of {len(every)} positions x {w.n_kv_heads} KV heads: boundary ties {len(ties)}")
 
 

@@ -499,10 +499,11 @@ def test_step_parity_alternative_readings(case, aggregate, gate_mode, path):
     o = dict(gate_keys=gk_o, sel=sel, gates=gates, cnt=cnt, scores=scores, out=out)
     dec = ops.SparseDecoder(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, case["budget"], w.theta,
                             True, device=DEV, aggregate=aggregate, gate_mode=gate_mode, path=path)
-    dec.step(w.q, w.w_q, w.w_qnorm, gpu_pool(w), w.k_pool, w.v_pool, w.block_table, w.seq_lens)
+    gk = gpu_pool(w)
+    dec.step(w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, w.block_table, w.seq_lens)
     torch.cuda.synchronize()
     g = dict(sel=wl.host(dec.sel), gates=wl.host(dec.gates), cnt=wl.host(dec.cnt), scores=wl.host(dec.scores),
-             out=bf16_out(dec.out))
+             out=bf16_out(dec.out), gate_keys=wl.host(gk))
     ties = compare_step(h, g, o, True, case["budget"], gate_mode=gate_mode)
     say(f"  boundary ties {ties}")
 
