@@ -191,38 +191,36 @@ __device__ __forceinline__ void issue_block(BlockRegs &b, const BlockSrc &cur, c
     for (int ks = 0; ks < 4; ++ks) b.k[t][ks] = ld16_kv<SAS_K_NT>(cur.k + t * lo.k_tile + 64 * ks + lo.k);
 }
 
-// One workgroup's share of a (sequence s, KV head kvh) = unit: wave `wave`
-// attends the selected blocks [i0, min(count, i0 + blocks_per_wave)), the
-// waves merge in LDS (vlds: the waves' V tiles), and the workgroup writes the
-// bf16 output (one workgroup per unit) or its partial (max, sum,
-// unnormalised output).  source(i) gives selected block i; it is called for
-// i0 before count is tested, so it must stay in bounds for any i0.
-template <int kMode, class Source>
-__device__ __forceinline__ void attend_unit(const DecodeParams &p, uint8_t (*vlds)[kVTileBytes], int s, int kvh,
-                                            int unit, int wg, int wave, int i0, int count, int32_t L,
-                                            Source source, BlockRegs &b, bool first_issued) {
+// B operand of S^T = K Q^T for (sequence s, KV head kvh): lane l holds
+// q[head l%16][32ks + 8(l/16) .. +7] (heads >= G zero).
+__device__ __forceinline__ void load_query_operand(const DecodeParams &p, int s, int kvh, bf16x8 (&qB)[4]) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, j = lane & 15;
-  const int G = p.group;
-  // B operand of S^T = K Q^T: lane l holds q[head l%16][32ks + 8(l/16) .. +7]
-  bf16x8 qB[4];
-  {
-    const uint16_t *qrow = p.q + ((int64_t)s * p.n_q_heads + kvh * G + j) * kHeadDim + 8 * g;
+  const uint16_t *qrow = p.q + ((int64_t)s * p.n_q_heads + kvh * p.group + j) * kHeadDim + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qB[ks] = as_bf16x8(j < G ? ld16(qrow + 32 * ks) : u32x4{0, 0, 0, 0});
-  }
-  const int i1 = min(count, i0 + p.blocks_per_wave);
-  const bool local_first = i1 == count;
-  auto at = [&](int i) { return local_first ? (i == i0 ? count - 1 : i - 1) : i; };
-  const BlockRef r0 = source(at(i0));
-  const LaneOffsets lo = lane_offsets(p);
+  for (int ks = 0; ks < 4; ++ks) qB[ks] = as_bf16x8(j < p.group ? ld16(qrow + 32 * ks) : u32x4{0, 0, 0, 0});
+}
 
-  WaveState ws;
+__device__ __forceinline__ void wave_state_init(WaveState &ws) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) ws.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   ws.m = -__builtin_inff();
   ws.lsum = 0.f;
-  uint8_t *vt = vlds[wave];
+}
+
+// One wave attends the selected blocks item(i0), item(i0 + 1), ...,
+// item(i1 - 1) in that order (item(i) gives a BlockRef; it is called for i0
+// even when i0 >= i1, so it must stay in bounds), accumulating into ws; vt
+// is the wave's V tile.  When first_issued, item(i0)'s loads are already in
+// b (issue_block).
+template <int kMode, class Item>
+__device__ __forceinline__ void attend_blocks(const DecodeParams &p, uint8_t *vt, int kvh, int32_t L, int i0, int i1,
+                                              Item item, BlockRegs &b, bool first_issued, const bf16x8 (&qB)[4],
+                                              WaveState &ws) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, j = lane & 15;
+  const BlockRef r0 = item(i0);
+  const LaneOffsets lo = lane_offsets(p);
   const char *kpool = reinterpret_cast<const char *>(p.k_pool) + (int64_t)kvh * p.head_stride * 2;
   const char *vpool = reinterpret_cast<const char *>(p.v_pool) + (int64_t)kvh * p.head_stride * 2;
   const int64_t page_bytes = p.page_stride * 2;
@@ -231,7 +229,6 @@ __device__ __forceinline__ void attend_unit(const DecodeParams &p, uint8_t (*vld
     const int64_t off = (int64_t)r.page * page_bytes;
     return BlockSrc{kpool + off, vpool + off, min(kBlock, L - r.blk * kBlock), r.gate};
   };
-
   if (i0 < i1) {
     // one register set: block i+1's loads are issued into it while block i is
     // consumed; the steady-state loop issues them unconditionally so that the
@@ -239,19 +236,28 @@ __device__ __forceinline__ void attend_unit(const DecodeParams &p, uint8_t (*vld
     BlockSrc cur = rows(r0);
     if (!first_issued) issue_block(b, cur, lo);
     for (int i = i0; i + 1 < i1; ++i) {
-      const BlockSrc nxt = rows(source(at(i + 1)));
+      const BlockSrc nxt = rows(item(i + 1));
       attend_block<kMode, true>(ws, b, cur, nxt, qB, lo, vt, p.scale_log2, g, j, tr_e, tr_q);
       cur = nxt;
     }
     attend_block<kMode, false>(ws, b, cur, cur, qB, lo, vt, p.scale_log2, g, j, tr_e, tr_q);
   }
+}
 
-  // ---- merge the waves (each parks (o, m, l) in its own V tile)
+// The waves of one workgroup merge their (max, sum, output) in LDS (vlds:
+// the waves' V tiles), in wave order, and the workgroup writes the bf16
+// output of (sequence s, KV head kvh) = unit (one workgroup per unit) or its
+// partial (max, sum, unnormalised output).
+__device__ __forceinline__ void merge_waves(const DecodeParams &p, uint8_t (*vlds)[kVTileBytes], int s, int kvh,
+                                            int unit, int wg, int wave, const WaveState &ws) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, j = lane & 15;
+  const int G = p.group;
   float lsum = ws.lsum;
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
   {
-    float *wo = reinterpret_cast<float *>(vt);  // [16][128] o, then m[16], l[16]
+    float *wo = reinterpret_cast<float *>(vlds[wave]);  // [16][128] o, then m[16], l[16]
     if (j < G) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4 *>(wo + j * kHeadDim + 16 * dt + 4 * g) = ws.o[dt];
@@ -289,6 +295,26 @@ __device__ __forceinline__ void attend_unit(const DecodeParams &p, uint8_t (*vld
       }
     }
   }
+}
+
+// One workgroup's share of a (sequence s, KV head kvh) = unit: wave `wave`
+// attends the selected blocks [i0, min(count, i0 + blocks_per_wave)), the
+// local block (the last, count - 1) first when the share ends with it; then
+// the waves merge (merge_waves).  source(i) gives selected block i; it is
+// called for i0 before count is tested, so it must stay in bounds for any i0.
+template <int kMode, class Source>
+__device__ __forceinline__ void attend_unit(const DecodeParams &p, uint8_t (*vlds)[kVTileBytes], int s, int kvh,
+                                            int unit, int wg, int wave, int i0, int count, int32_t L,
+                                            Source source, BlockRegs &b, bool first_issued) {
+  bf16x8 qB[4];
+  load_query_operand(p, s, kvh, qB);
+  const int i1 = min(count, i0 + p.blocks_per_wave);
+  const bool local_first = i1 == count;
+  auto item = [&](int i) { return source(local_first ? (i == i0 ? count - 1 : i - 1) : i); };
+  WaveState ws;
+  wave_state_init(ws);
+  attend_blocks<kMode>(p, vlds[wave], kvh, L, i0, i1, item, b, first_issued, qB, ws);
+  merge_waves(p, vlds, s, kvh, unit, wg, wave, ws);
 }
 
 }  // namespace sas
