@@ -733,10 +733,14 @@ def main():
         ev1.record(stream)
         torch.cuda.synchronize()
         dec_ms = ev0.elapsed_time(ev1) / args.steps
-        fused = decs[0].ws_step is None  # the fused path needs no workspace
-        path_name = "one fused launch" if fused else ("sliced selection" if ops.decode_step_workspace_bytes(
-            decs[0].shape, args.budget, args.path) == ops.decode_step_workspace_bytes(decs[0].shape, args.budget,
-                                                                                     "sliced") else "two launches")
+        # the path sas_decode_step took, told apart by its workspace size
+        ws_of = lambda pth: ops.decode_step_workspace_bytes(decs[0].shape, args.budget, pth)
+        ws_now = ws_of(args.path)
+        fused = ws_now == 0  # one fused launch, one workgroup per pair, no workspace
+        split_fused = not fused and ws_now == ws_of("fused")
+        path_name = ("one fused launch" if fused else
+                     "fused launch split over workgroups + partial merge" if split_fused else
+                     "sliced selection" if ws_now == ws_of("sliced") else "two launches")
 
         # algorithmic bytes: selected K+V blocks (attention), every candidate's
         # gate key (selection), and, for the fused launch, the rest it moves once
@@ -748,7 +752,7 @@ def main():
         # the dominant kernel: the fused step itself (one launch per step), else
         # the attention
         dom_ms = dec_ms
-        if fused:  # the step's one launch, back to back, bracketed by HIP events
+        if fused or split_fused:  # the step's launches, back to back, bracketed by HIP events
             ev0.record(stream)
             for i in range(args.steps):
                 run_step(i)
@@ -758,7 +762,7 @@ def main():
         # algorithmic bytes: the gate keys of every candidate and the selected
         # K/V blocks (the queries, weights, indices and outputs the fused
         # launch also moves are reported apart, not counted)
-        dom_b = kv_b + gk_b if fused else kv_b
+        dom_b = kv_b + gk_b if fused or split_fused else kv_b
         mode_steps[mode] = step_eager
         results[mode] = dict(queries_per_s=w0.batch * args.steps / elapsed, ms_per_step=ms,
                              decode_ms=dec_ms, decode_gbs=kv_b / (dec_ms * 1e-3) / 1e9,
@@ -768,6 +772,7 @@ def main():
                              attended_tokens_per_query=float(np.mean([c.sum() for c in cnts])) * 64 / (
                                  w0.batch * w0.n_kv_heads),
                              step_us_p10=p10, step_us_p50=p50, step_us_p90=p90, fused=float(fused),
+                             split_fused=float(split_fused),
                              path=path_name)
         log(f"{mode}: {results[mode]['queries_per_s']:.0f} queries/s, {ms * 1e3:.1f} us/step "
             f"({path_name}), step {results[mode]['step_gbs']:.0f} GB/s; "
@@ -819,14 +824,17 @@ def main():
                    "launch": "hip graph per layer" if args.graph else "eager",
                    "path": r["path"]},
         "roofline": {"bound": "hbm",
-                     "kernel": ("sas_decode_step (step_kernel, one fused launch)" if r["fused"]
+                     "kernel": ("sas_decode_step (step_kernel, one fused launch)" if r["fused"] else
+                                "sas_decode_step (step_kernel split over workgroups + decode_merge_kernel)"
+                                if r["split_fused"]
                                 else "sas_sparse_decode (decode_kernel)"),
                      "achieved": round(r["dominant_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(r["dominant_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(args.workload, args.budget,
                                                  "step_kernel" if r["fused"] else "decode_kernel"),
                      "bytes_per_launch": r["dominant_bytes"], "avg_launch_us": round(r["dominant_ms"] * 1e3, 2),
-                     "bytes_note": ("gate keys of every candidate + selected K/V blocks" if r["fused"] else
+                     "bytes_note": ("gate keys of every candidate + selected K/V blocks"
+                                    if r["fused"] or r["split_fused"] else
                                     "selected K/V blocks"),
                      "other_bytes_per_launch": r["other_bytes"] if r["fused"] else None},
         "attention_alone": {"kernel": "sas_sparse_decode (decode_kernel)", "avg_launch_us": round(r["decode_ms"] * 1e3, 2),

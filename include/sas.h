@@ -228,16 +228,20 @@ sas_status sas_sparse_decode_ex(const sas_shape *shape, const void *q, const voi
  * same bits whenever the attention runs one workgroup per pair):
  *   SAS_STEP_FUSED  one kernel launch: each (sequence, KV head) is scored,
  *                   selected and attended by one workgroup, which keeps the
- *                   selection and the selected blocks' pages on chip;
+ *                   selection and the selected blocks' pages on chip; with
+ *                   fewer pairs than the device's compute units, by several
+ *                   workgroups that each make the pair's selection and attend
+ *                   a share of its blocks, plus a launch that merges their
+ *                   partial results;
  *   SAS_STEP_SLICED for few pairs: each pair's candidates are scored and
  *                   reduced to a Top-K list by several workgroups (slices),
  *                   then one launch merges the lists into the selection and
  *                   attends with each pair split over several workgroups;
  *   SAS_STEP_TWO_LAUNCHES  the kernels of the two calls above;
- *   SAS_STEP_AUTO   fused when there are more (sequence, KV head) pairs than
- *                   half the current device's compute units; otherwise
- *                   sliced for block tables over 1,024 blocks, else two
- *                   launches.
+ *   SAS_STEP_AUTO   sliced for fewer pairs than the current device's
+ *                   compute units and block tables over 1,024 blocks, else
+ *                   fused (two launches where the fused kernel's limits
+ *                   are exceeded).
  *
  * Arguments as for the two calls, with max_sel = budget_tokens / 64:
  *   aggregate  SAS_AGG_MEAN or SAS_AGG_MAX
@@ -247,9 +251,9 @@ sas_status sas_sparse_decode_ex(const sas_shape *shape, const void *q, const voi
  *   scores     written when non-NULL (nullable)
  *   sel, cnt, out  required
  * workspace: at least sas_decode_step_workspace_bytes(shape, budget_tokens,
- * path) bytes (0 on the fused path, where workspace may be NULL; 0 also for
- * an unknown path); no initial contents needed; calls that overlap in time
- * must not share one.
+ * path) bytes (0 on the fused path when every pair has one workgroup, where
+ * workspace may be NULL; 0 also for an unknown path); no initial contents
+ * needed; calls that overlap in time must not share one.
  */
 #define SAS_STEP_AUTO 0
 #define SAS_STEP_FUSED 1

@@ -463,8 +463,11 @@ int step_path(const sas_shape *shape, int32_t budget_tokens, int32_t path) {
   if (path != SAS_STEP_AUTO) return path;
   const int n_sel = budget_tokens / SAS_BLOCK;
   const bool fits = sas::step_fits(shape->n_q_heads / shape->n_kv_heads, shape->max_blocks, n_sel);
-  if (fits && sas::decode_split(shape->batch, shape->n_kv_heads, n_sel, device_cus()).wg_per_unit == 1) return SAS_STEP_FUSED;
-  return fits && shape->max_blocks > 1024 ? SAS_STEP_SLICED : SAS_STEP_TWO_LAUNCHES;
+  if (!fits) return SAS_STEP_TWO_LAUNCHES;
+  if (sas::decode_split(shape->batch, shape->n_kv_heads, n_sel, device_cus()).wg_per_unit == 1) return SAS_STEP_FUSED;
+  // few pairs: every workgroup of a split pair repeats the pair's selection,
+  // which is cheap up to two score passes of 512 candidates
+  return shape->max_blocks > 1024 ? SAS_STEP_SLICED : SAS_STEP_FUSED;
 }
 
 struct StepWorkspace {
@@ -472,9 +475,16 @@ struct StepWorkspace {
 };
 StepWorkspace step_workspace(const sas_shape *shape, int32_t budget_tokens, int path) {
   StepWorkspace w{};
-  if (path == SAS_STEP_FUSED) return w;
   const int n_sel = budget_tokens / SAS_BLOCK;
   const DecodeWorkspace d = decode_workspace(shape, n_sel);
+  if (path == SAS_STEP_FUSED) {  // the partials of pairs split over several workgroups
+    if (sas::decode_split(shape->batch, shape->n_kv_heads, n_sel, device_cus()).wg_per_unit > 1) {
+      w.part_o = d.part_o;
+      w.part_ml = d.part_ml;
+      w.total = d.total;
+    }
+    return w;
+  }
   w.part_o = d.part_o;
   w.part_ml = d.part_ml;
   w.scores = d.total;  // room for the scores when the caller passes none
@@ -528,12 +538,9 @@ sas_status decode_step_impl(const sas_shape *shape, const void *q, const void *w
   const int how = step_path(shape, budget_tokens, path);
   if (how != SAS_STEP_TWO_LAUNCHES && !sas::step_fits(p.g.group, shape->max_blocks, n_sel))
     return fail(SAS_ERR_UNSUPPORTED, "shape outside the one-workgroup selection's limits");
-  if (how == SAS_STEP_FUSED) {
-    p.d.wg_per_unit = 1;  // one workgroup per (sequence, KV head)
-    p.d.blocks_per_wave = (n_sel + 7) / 8;
-    return hip_status(sas::launch_step(p, shape->batch, hs), "sas_decode_step launch");
-  }
   const StepWorkspace wl = step_workspace(shape, budget_tokens, how);
+  if (how == SAS_STEP_FUSED && p.d.wg_per_unit == 1)  // one workgroup per (sequence, KV head), no workspace
+    return hip_status(sas::launch_step(p, shape->batch, hs), "sas_decode_step launch");
   if (!workspace) return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned16(workspace)) return fail(SAS_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
   if (workspace_bytes < wl.total) {
@@ -547,9 +554,11 @@ sas_status decode_step_impl(const sas_shape *shape, const void *q, const void *w
   char *ws = (char *)workspace;
   p.d.part_o = (float *)(ws + wl.part_o);
   p.d.part_ml = (float *)(ws + wl.part_ml);
-  if (!p.g.scores) p.g.scores = (float *)(ws + wl.scores);
+  if (!p.g.scores && how != SAS_STEP_FUSED) p.g.scores = (float *)(ws + wl.scores);  // the fused kernel can skip them
   hipError_t e;
-  if (how == SAS_STEP_SLICED) {
+  if (how == SAS_STEP_FUSED) {
+    e = sas::launch_step(p, shape->batch, hs);
+  } else if (how == SAS_STEP_SLICED) {
     sas::gate_slice_layout(shape->batch, shape->n_kv_heads, shape->max_blocks, device_cus(), &p.g.slices, &p.g.slice_len);
     p.g.slot_len = ((p.g.slice_len > 512 ? p.g.slice_len : 512) + 7) / 8 * 8;
     p.g.batch = shape->batch;

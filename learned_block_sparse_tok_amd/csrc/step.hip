@@ -14,7 +14,10 @@
 // same order, and the attention is the decode kernel's own device code.
 //
 // One 512-thread workgroup (8 waves, one per CU at the decode kernel's
-// register budget) per (sequence, KV head):
+// register budget) per (sequence, KV head), or, with fewer pairs than CUs,
+// several per pair (each makes the pair's selection, then attends its share
+// of the blocks and stores a partial result that the decode merge kernel
+// combines):
 //   1. loads: the group's queries, RoPE frequencies and norm weights, the
 //      block-table row (to LDS), and one batch of 16 query-projection rows
 //      per 16-lane group (32 groups; w_q stays in L2);
@@ -69,7 +72,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(const int32_t *__r
   float(*vs)[kGateDim] = reinterpret_cast<float(*)[kGateDim]>(gate_lds + kStepVsOff);
 
   const GateParams &p = sp.g;
-  const int unit = blockIdx.x;  // (sequence, KV head); KV head = unit % Hkv, as in the two kernels
+  // (sequence, KV head) and its share: with fewer pairs than CUs each pair
+  // spans wg_per_unit workgroups, each making the pair's selection and
+  // attending its share of the blocks as the decode kernel splits them
+  const int nwg = sp.d.wg_per_unit;
+  const int unit = nwg == 1 ? (int)blockIdx.x : (int)blockIdx.x / nwg;  // KV head = unit % Hkv
+  const int wg = (int)blockIdx.x - unit * nwg;
   const int s = unit / n_kv_heads_a;
   const int kvh = unit - s * n_kv_heads_a;
   const int t = threadIdx.x, lane = t & 63;
@@ -195,7 +203,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(const int32_t *__r
 
   // ---- 3. scores
   const float inv_sqrt_dg = 0.08838834764831845f;  // 1/sqrt(128)
-  float *scores = p.scores ? p.scores + (int64_t)unit * p.max_blocks : nullptr;
+  float *scores = p.scores && wg == 0 ? p.scores + (int64_t)unit * p.max_blocks : nullptr;
   for (int base = 0; base < n; base += 32 * kStepKeys) {
     if (base > 0) gather(base);
 #pragma unroll
@@ -236,7 +244,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(const int32_t *__r
   // the selection ends with it (and takes it first) issues its K/V loads now,
   // so that they arrive while wave 0 selects
   const int bpw = sp.d.blocks_per_wave;
-  const bool prefetch = wave == k_eff / bpw;
+  const int gwave = wg * kWaves + wave;  // this wave's share among the pair's waves
+  const bool prefetch = gwave == k_eff / bpw;
   BlockRegs b;
   if (prefetch) issue_block(b, block_rows(sp.d, kvh, BlockRef{btl[n], n, 1.0f}, L), lane_offsets(sp.d));
 
@@ -258,7 +267,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(const int32_t *__r
     }
   }
   lds_barrier();
-  if (wave == kWaves - 1) {  // the selection's outputs, from the LDS arrays (the V tiles overwrite the keys)
+  if (wg == 0 && wave == kWaves - 1) {  // the selection's outputs, from the LDS arrays (the V tiles overwrite the keys)
     int32_t *sel = p.sel + (int64_t)unit * p.n_sel;
     float *gates = p.gates ? p.gates + (int64_t)unit * p.n_sel : nullptr;
     for (int i = lane; i < p.n_sel; i += 64) {
@@ -275,7 +284,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(const int32_t *__r
     return BlockRef{__builtin_amdgcn_readfirstlane(page_l[i]), __builtin_amdgcn_readfirstlane(sel_l[i]),
                     kMode ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gate_l[i]))) : 1.0f};
   };
-  attend_unit<kMode>(sp.d, vlds, s, kvh, unit, 0, wave, wave * bpw, k_eff + 1, L, source, b, prefetch);
+  attend_unit<kMode>(sp.d, vlds, s, kvh, unit, wg, wave, gwave * bpw, k_eff + 1, L, source, b, prefetch);
 }
 
 // The second half of the sliced step (fewer pairs than CUs): the slices'
@@ -369,7 +378,7 @@ bool step_fits(int group, int max_blocks, int n_sel) {
 }
 
 hipError_t launch_step(const StepParams &p, int batch, hipStream_t st) {
-  const dim3 grid((unsigned)(batch * p.g.n_kv_heads));
+  const dim3 grid((unsigned)(batch * p.g.n_kv_heads * p.d.wg_per_unit));
   const bool mx = p.g.aggregate != 0;
   const int mode = !p.d.gates ? 0 : (p.d.gate_mode == 0 ? 1 : 2);
   const int32_t *sl = p.g.seq_lens, *btab = p.g.block_table;  // the leading arguments
@@ -383,7 +392,9 @@ hipError_t launch_step(const StepParams &p, int batch, hipStream_t st) {
     else if (mode == 1) hipLaunchKernelGGL((step_kernel<true, 1>), grid, dim3(kWaves * 64), 0, st, sl, btab, hkv, mb, p);
     else hipLaunchKernelGGL((step_kernel<true, 2>), grid, dim3(kWaves * 64), 0, st, sl, btab, hkv, mb, p);
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.d.wg_per_unit == 1) return e;
+  return launch_decode_merge(p.d, batch, st);
 }
 
 }  // namespace sas

@@ -102,17 +102,20 @@ def test_decode_step_rejects_bad_arguments(lib):
 
 def test_decode_step_workspace_bytes(lib):
     small, big = _shape(), _shape(batch=32, n_q_heads=32, n_kv_heads=8)
+    # fused: no workspace when every pair has its own workgroup (256 pairs on
+    # 256 CUs); with few pairs, the partials of the workgroups a pair spans
+    assert ops.decode_step_workspace_bytes(big, 2048, "fused") == 0
+    assert ops.decode_step_workspace_bytes(small, 2048, "fused") == ops.sparse_decode_workspace_bytes(small, 32)
     for sh in (small, big):
-        assert ops.decode_step_workspace_bytes(sh, 2048, "fused") == 0
         two = ops.decode_step_workspace_bytes(sh, 2048, "two_launches")
         # the attention's partials plus room for the scores
         assert two >= ops.sparse_decode_workspace_bytes(sh, 32) + sh.batch * sh.n_kv_heads * sh.max_blocks * 4
-    # automatic: 256 (sequence, KV head) pairs are fused; 4 take two launches,
-    # or the sliced selection once the block table is over 1,024 blocks
+    # automatic: fused, or the sliced selection for few pairs once the block
+    # table is over 1,024 blocks
     long = _shape(max_blocks=2048)
     assert ops.decode_step_workspace_bytes(big, 2048, "auto") == 0
     assert ops.decode_step_workspace_bytes(small, 2048, "auto") == ops.decode_step_workspace_bytes(small, 2048,
-                                                                                                  "two_launches")
+                                                                                                  "fused")
     assert ops.decode_step_workspace_bytes(long, 2048, "auto") == ops.decode_step_workspace_bytes(long, 2048,
                                                                                                  "sliced")
     # the sliced path adds each pair's slice lists (score key, block, page per entry)

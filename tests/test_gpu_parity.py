@@ -326,9 +326,11 @@ def _step_workload(case):
     return w
 
 
-# "auto" takes two launches for these few (sequence, KV head) pairs;
-# "fused" forces the one-launch step on them, "sliced" the sliced selection
-@pytest.mark.parametrize("path", ["auto", "fused", "sliced"])
+# These few (sequence, KV head) pairs split over several workgroups each:
+# "fused" (also what "auto" takes here) repeats the selection in every
+# workgroup of a pair, "sliced" divides it among them, "two_launches"
+# selects with one workgroup per pair.
+@pytest.mark.parametrize("path", ["two_launches", "fused", "sliced"])
 @pytest.mark.parametrize("gated", [False, True], ids=["plain", "gated"])
 @pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: c["name"])
 def test_step_parity(case, gated, path):
@@ -392,9 +394,10 @@ def test_fused_step_equals_two_launches(case):
         assert cnt.min() >= 1 and cnt.max() <= case["budget"] // 64
 
 
-# Fewer pairs than half the CUs: the sliced selection (several workgroups
-# per pair, each keeping its slice's Top-K, then one merge) must give the
-# two launches' bits exactly, since both then attend with the same split.
+# Fewer pairs than CUs: the sliced selection (several workgroups per pair,
+# each keeping its slice's Top-K, then one merge) and the split fused step
+# (each of a pair's workgroups repeating its selection) must give the two
+# launches' bits exactly, since all three then attend with the same split.
 SLICED_CASES = [
     dict(name="ragged_g4", lens=[1, 64, 65, 4097, 9000, 33000], Hq=8, Hkv=2, budget=1024, mb=520, layout="paged"),
     dict(name="b8_g4_32k", lens=[32768] * 8, Hq=32, Hkv=8, budget=2048, mb=512, layout="contiguous"),
@@ -417,7 +420,7 @@ def test_sliced_step_equals_two_launches(case):
             continue
         say("sliced", case["name"], aggregate, gated, gate_mode)
         res = {}
-        for path in ("two_launches", "sliced"):
+        for path in ("two_launches", "sliced", "fused"):
             dec = ops.SparseDecoder(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, case["budget"],
                                     w.theta, gated, device=DEV, aggregate=aggregate, gate_mode=gate_mode, path=path)
             dec.sel.fill_(-7)
@@ -427,8 +430,9 @@ def test_sliced_step_equals_two_launches(case):
             dec.step(*args)
             torch.cuda.synchronize()
             res[path] = [t.clone() for t in (dec.sel, dec.gates, dec.cnt, dec.scores, dec.out)]
-        for name, a, b in zip(("sel", "gates", "cnt", "scores", "out"), res["two_launches"], res["sliced"]):
-            assert torch.equal(a, b), name
+        for path in ("sliced", "fused"):
+            for name, a, b in zip(("sel", "gates", "cnt", "scores", "out"), res["two_launches"], res[path]):
+                assert torch.equal(a, b), (path, name)
 
 
 @pytest.mark.parametrize("path", ["two_launches", "fused", "sliced"])
