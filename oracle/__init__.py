@@ -350,3 +350,36 @@ def gate_backward(q, k_pool, v_pool, block_table, strides, n_kv_heads, seq_lens,
                 out["d_w_qnorm"] += dw
                 out["d_w_q"][h] += np.outer(du, qf[s, h])
     return out
+
+
+def prefill_gate_backward(q, k_pool, v_pool, block_table_row, strides, n_kv_heads, sel, gates, cnt, sm_scale,
+                          w_q, w_qnorm, w_k, w_knorm, gate_keys, theta, d_out, round_keys=True, positions=None):
+    """Gradients of the gate parameters through the continuous gates of the
+    training-time forward of one sequence (prefill above: every position a
+    query), for the loss sum_t sum_h <d_out[t][h], out[t][h]>.
+
+    SAS trains its gates with the language-model loss on 32,768-token
+    sequences, each query selecting its own blocks (aigc.news release note:
+    training Top-K of 31 historical blocks, the LM loss ranking the context
+    end to end; "Tencent Hunyuan open-sources SAS ...": per-query selection,
+    a differentiable path to the selector).  READING: with the forward's
+    reading (position t is the decode step whose cache holds its first t+1
+    tokens) the loss is a sum over positions, so its gradient is the sum of
+    gate_backward's per-step gradients over the batch of positions sharing
+    the one block-table row; each block's key receives the gradient of every
+    position that selected it.
+
+    sel / gates / cnt: [T][Hkv][n_sel], [T][Hkv] as prefill returns them;
+    d_out: bf16 bits [T][Hq][128].  positions: optional subset of positions
+    whose terms are summed (the gradient of the loss with d_out zero at every
+    other position); d_gates then covers those positions only.
+    Returns gate_backward's dict."""
+    T = q.shape[0]
+    pos = np.arange(T, dtype=np.int32) if positions is None else np.asarray(positions, np.int32)
+    lens = (pos + 1).astype(np.int32)
+    bt = np.ascontiguousarray(np.broadcast_to(np.asarray(block_table_row, np.int32),
+                                              (len(pos), len(block_table_row))))
+    return gate_backward(np.ascontiguousarray(q[pos]), k_pool, v_pool, bt, strides, n_kv_heads, lens,
+                         np.ascontiguousarray(sel[pos]), np.ascontiguousarray(gates[pos]),
+                         np.ascontiguousarray(cnt[pos]), sm_scale, w_q, w_qnorm, w_k, w_knorm, gate_keys, theta,
+                         np.ascontiguousarray(d_out[pos]), round_keys=round_keys)

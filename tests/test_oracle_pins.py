@@ -771,3 +771,102 @@ def test_gate_gradient_is_the_derivative_of_the_gated_output():
                 gm[s, kvh, i] -= np.float32(0.25)
                 fd = (loss(gp) - loss(gm)) / (float(gp[s, kvh, i]) - float(gm[s, kvh, i]))
                 np.testing.assert_allclose(bwd["d_gates"][s, kvh, i], fd, rtol=1e-8, atol=1e-10)
+
+
+# ---------------------------------------------------------------- backward of the training-time forward
+def _fd_probe(h, sel, cnt, d_out, bwd, seed, key_shift=None, probes=4):
+    """Central differences of the independent forward (_smooth_gated_loss) at
+    random entries of every gate parameter, against bwd."""
+    wq, wk = oracle.bf16_to_f64(h.w_q), oracle.bf16_to_f64(h.w_k)
+    wqn, wkn = h.wqn.astype(np.float64), h.wkn.astype(np.float64)
+    rng = np.random.default_rng(seed)
+    eps = 1e-5
+    params = dict(d_w_q=wq, d_w_qnorm=wqn, d_w_k=wk, d_w_knorm=wkn)
+    checked = 0
+    for name, arr in params.items():
+        for _ in range(probes):
+            idx = tuple(int(rng.integers(0, n)) for n in arr.shape)
+            plus, minus = [a.copy() for a in params.values()], [a.copy() for a in params.values()]
+            k = list(params).index(name)
+            plus[k][idx] += eps
+            minus[k][idx] -= eps
+            fd = (_smooth_gated_loss(h, sel, cnt, d_out, *plus, key_shift=key_shift)[0]
+                  - _smooth_gated_loss(h, sel, cnt, d_out, *minus, key_shift=key_shift)[0]) / (2 * eps)
+            got = bwd[name][idx]
+            assert abs(got - fd) <= 1e-6 * max(1.0, abs(fd)) + 1e-9, (name, idx, got, fd)
+            checked += abs(fd) > 1e-6
+    return checked
+
+
+def _prefill_backward_case(seed, budget=192, T=200):
+    w = wl.make_prefill(T, 4, 2, budget, "paged", seed, "cpu", random_norms=True, extra_pages=2)
+    h = Host(w)
+    assert not np.array_equal(h.bt[0], np.arange(h.bt.shape[1]))  # a permuted table over extra pages
+    nb = T // 64
+    gk = np.zeros((w.n_pages, 2, wl.GATE_DIM), np.uint16)
+    oracle.pool_blocks(h.k, h.bt[:1], w.strides, 2, np.zeros(nb, np.int32), np.arange(nb, dtype=np.int32), h.w_k,
+                       h.wkn, w.theta, gk)
+    sel, _, cnt, _, _ = oracle.prefill(h.q, h.k, h.v, h.bt[0], w.strides, 2, gk, h.w_q, h.wqn, w.theta, budget,
+                                       True, SM_SCALE)
+    d_out = wl.bf16_bits(torch.randn(h.q.shape, generator=torch.Generator().manual_seed(seed)).to(torch.bfloat16))
+    return w, h, gk, sel, cnt, d_out
+
+
+def test_prefill_gate_backward_matches_finite_differences():
+    """The training-time backward (every position a query, one block table
+    row, each position's cache its first t+1 tokens) against central
+    differences of the independent numpy forward over all positions, with
+    the selections held fixed and unrounded gate keys."""
+    w, h, gk, sel, cnt, d_out = _prefill_backward_case(33)
+    assert (cnt[:, 0] >= 2).sum() > 100  # most positions have historical blocks
+    wq, wk = oracle.bf16_to_f64(h.w_q), oracle.bf16_to_f64(h.w_k)
+    _, g0 = _smooth_gated_loss(h, sel, cnt, d_out, wq, h.wqn.astype(np.float64), wk, h.wkn.astype(np.float64))
+    bwd = oracle.prefill_gate_backward(h.q, h.k, h.v, h.bt[0], w.strides, 2, sel, g0, cnt, SM_SCALE, h.w_q, h.wqn,
+                                       h.w_k, h.wkn, gk, w.theta, d_out, round_keys=False)
+    assert _fd_probe(h, sel, cnt, d_out, bwd, seed=11) >= 10
+
+
+def test_prefill_gate_backward_with_stored_keys_matches_straight_through_differences():
+    """round_keys=True, the form the GPU is compared with: each block's key in
+    the forward is its fp64 key plus the constant difference to the stored
+    bf16 key at the block's page (the same for every position)."""
+    w, h, gk, sel, cnt, d_out = _prefill_backward_case(35)
+    wq, wk = oracle.bf16_to_f64(h.w_q), oracle.bf16_to_f64(h.w_k)
+    wqn, wkn = h.wqn.astype(np.float64), h.wkn.astype(np.float64)
+    Kd = [dense_kv(h, h.k, w.batch - 1, k) for k in range(2)]
+    per_block = {}
+    for kvh in range(2):
+        for c in range(w.batch // 64):
+            kb = Kd[kvh][64 * c:64 * c + 64]
+            p = np.concatenate([kb.max(0), kb.min(0), kb.mean(0)])
+            u = wk[kvh] @ p
+            u = u / math.sqrt(np.mean(u * u) + 1e-6) * wkn
+            per_block[(kvh, c)] = oracle.bf16_to_f64(gk[int(h.bt[0, c]), kvh]) - _rope_np(u, 64.0 * c, w.theta)
+    shift = {(s, kvh, int(c)): per_block[(kvh, int(c))]
+             for s in range(w.batch) for kvh in range(2) for c in sel[s, kvh, :cnt[s, kvh] - 1]}
+    _, g0 = _smooth_gated_loss(h, sel, cnt, d_out, wq, wqn, wk, wkn, key_shift=shift)
+    bwd = oracle.prefill_gate_backward(h.q, h.k, h.v, h.bt[0], w.strides, 2, sel, g0, cnt, SM_SCALE, h.w_q, h.wqn,
+                                       h.w_k, h.wkn, gk, w.theta, d_out, round_keys=True)
+    assert _fd_probe(h, sel, cnt, d_out, bwd, seed=12, key_shift=shift) >= 10
+
+
+def test_prefill_gate_backward_positions_subset_is_zeroed_d_out():
+    """The gradient is linear in d_out: summing the terms of a subset of
+    positions equals the full backward with d_out zero at every other
+    position (the form the full-size GPU check uses); d_gates vanish there."""
+    w, h, gk, sel, cnt, d_out = _prefill_backward_case(37, T=150)
+    _, gates, _, _, _ = oracle.prefill(h.q, h.k, h.v, h.bt[0], w.strides, 2, gk, h.w_q, h.wqn, w.theta, 192, True,
+                                       SM_SCALE)
+    pos = np.array([3, 64, 100, 149])
+    masked = np.zeros_like(d_out)
+    masked[pos] = d_out[pos]
+    args = (h.q, h.k, h.v, h.bt[0], w.strides, 2, sel, gates, cnt, SM_SCALE, h.w_q, h.wqn, h.w_k, h.wkn, gk,
+            w.theta)
+    full = oracle.prefill_gate_backward(*args, masked)
+    part = oracle.prefill_gate_backward(*args, d_out, positions=pos)
+    for name in ("d_w_q", "d_w_qnorm", "d_w_k", "d_w_knorm"):
+        np.testing.assert_allclose(full[name], part[name], rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(full["d_gates"][pos], part["d_gates"])
+    others = np.setdiff1d(np.arange(w.batch), pos)
+    assert np.all(full["d_gates"][others] == 0)
+    assert np.abs(part["d_w_k"]).max() > 0
