@@ -22,7 +22,8 @@
  *   sas_decode_step    the two above as one call (one fused launch)
  * and, for the training-time forward of a whole sequence (every position a
  * query): sas_prefill_select, then sas_prefill_attend; for training the
- * gates: sas_gate_backward after a gated decode step.
+ * gates: sas_gate_backward after a gated decode step, or
+ * sas_prefill_gate_backward after the training-time forward.
  *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer owned by the caller (for
@@ -313,8 +314,11 @@ sas_status sas_decode_step_noalloc(const sas_shape *shape, const void *q, const 
  * sas_prefill_attend -- the attention of every position over its selection:
  *   plain (gates NULL) or gated as in sas_sparse_decode, output bf16
  *   [T][Hq][128].  sel / gates / cnt as sas_prefill_select wrote them
- *   (max_sel = budget/64 <= 64, i.e. budgets up to 4,096 tokens).  Needs no
- *   workspace.
+ *   (max_sel = budget/64 <= 64, i.e. budgets up to 4,096 tokens).  lse
+ *   (nullable): fp32 [T][Hq], the natural-log log-sum-exp of each query
+ *   head's logits sm_scale * <q, k_j> over the tokens it attends (the plain
+ *   softmax normaliser, gated or not), which sas_prefill_gate_backward
+ *   takes.  Needs no workspace.
  */
 sas_status sas_prefill_select(const sas_shape *shape, const void *q, const void *w_q,
                               const float *w_qnorm, const void *gate_keys,
@@ -324,7 +328,7 @@ sas_status sas_prefill_select(const sas_shape *shape, const void *q, const void 
 sas_status sas_prefill_attend(const sas_shape *shape, const void *q, const void *k_pool,
                               const void *v_pool, const int32_t *block_table_row, int32_t seq_len,
                               const int32_t *sel, const float *gates, const int32_t *cnt,
-                              int32_t max_sel, float sm_scale, void *out, void *stream);
+                              int32_t max_sel, float sm_scale, void *out, float *lse, void *stream);
 
 /*
  * sas_gate_backward -- gradients of the gate parameters through the
@@ -358,6 +362,49 @@ sas_status sas_gate_backward(const sas_shape *shape, const void *q, const void *
                              float *d_gates, float *d_w_q, float *d_w_qnorm, float *d_w_k,
                              float *d_w_knorm, void *workspace, size_t workspace_bytes,
                              void *stream);
+
+/*
+ * sas_prefill_gate_backward -- gradients of the gate parameters through the
+ * continuous gates of the training-time forward of one sequence (the
+ * backward of sas_prefill_select + gated sas_prefill_attend).  SAS trains its
+ * gates with the language-model loss on 32,768-token sequences, each query
+ * selecting its own blocks (aigc.news release note: training Top-K of 31
+ * historical blocks; "Tencent Hunyuan open-sources SAS ...": per-query
+ * selection, a differentiable path from the loss to the selector).  Position
+ * t is the decode step whose cache holds its first t+1 tokens, so the loss
+ * sum_t sum_h <d_out[t][h], out[t][h]> has the sum over positions of
+ * sas_gate_backward's per-step gradients, under the same conventions: the
+ * Top-K choice passes no gradient, each position's own block has the
+ * constant gate 1, the bf16 gate keys pass the gradient straight through,
+ * and q, K and V get none.  A block's key collects the gradient of every
+ * position that selected it.
+ *
+ * shape->batch must be 1.  Inputs: q, d_out bf16 [T][Hq][128]; the pools,
+ * block_table_row and seq_len as for sas_prefill_attend; sel / gates / cnt
+ * as sas_prefill_select wrote them (max_sel = budget/64 <= 64); lse
+ * [T][Hq] as sas_prefill_attend wrote it for these inputs; the gate weights
+ * and keys as for sas_prefill_select.  Outputs (fp32, overwritten):
+ *   d_gates   [T][Hkv][max_sel]  dL/dg of every selected block (the own
+ *             block's included, as if free), 0 in the padding
+ *   d_w_q     [Hq][128][128]     d_w_qnorm [128]
+ *   d_w_k     [Hkv][128][384]    d_w_knorm [128]
+ * Sums run in a fixed order (deterministic).  workspace: at least
+ * sas_prefill_gate_backward_workspace_bytes(shape, seq_len, max_sel) bytes,
+ * no initial contents needed; it grows as Hkv * T * T / 16 bytes (a dense
+ * position x block matrix: 512 MiB at T = 32,768 with 8 KV heads) besides
+ * terms linear in T.  Errors as for sas_prefill_attend, plus
+ * SAS_ERR_WORKSPACE.
+ */
+size_t sas_prefill_gate_backward_workspace_bytes(const sas_shape *shape, int32_t seq_len, int32_t max_sel);
+sas_status sas_prefill_gate_backward(const sas_shape *shape, const void *q, const void *k_pool,
+                                     const void *v_pool, const int32_t *block_table_row, int32_t seq_len,
+                                     const int32_t *sel, const float *gates, const int32_t *cnt,
+                                     int32_t max_sel, float sm_scale, const float *lse, const void *w_q,
+                                     const float *w_qnorm, const void *w_k, const float *w_knorm,
+                                     const void *gate_keys, double rope_theta, const void *d_out,
+                                     float *d_gates, float *d_w_q, float *d_w_qnorm, float *d_w_k,
+                                     float *d_w_knorm, void *workspace, size_t workspace_bytes,
+                                     void *stream);
 
 /*
  * sas_probe_read -- measurement utility, not a step of the method: reads

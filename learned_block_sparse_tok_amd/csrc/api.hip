@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include "../../include/sas.h"
+#include "prefill_backward.h"
 #include "sas_device.h"
 #include "sas_kernels.h"
 
@@ -318,7 +319,7 @@ sas_status sas_prefill_select(const sas_shape *shape, const void *q, const void 
 sas_status sas_prefill_attend(const sas_shape *shape, const void *q, const void *k_pool, const void *v_pool,
                               const int32_t *block_table_row, int32_t seq_len, const int32_t *sel,
                               const float *gates, const int32_t *cnt, int32_t max_sel, float sm_scale, void *out,
-                              void *stream) {
+                              float *lse, void *stream) {
   sas_status st = check_prefill(shape, true, seq_len);
   if (st) return st;
   if (!q || !k_pool || !v_pool || !block_table_row || !sel || !cnt || !out)
@@ -337,6 +338,7 @@ sas_status sas_prefill_attend(const sas_shape *shape, const void *q, const void 
   p.gates = gates;
   p.cnt = cnt;
   p.out = (uint16_t *)out;
+  p.lse = lse;
   p.page_stride = shape->page_stride;
   p.tok_stride = shape->tok_stride;
   p.head_stride = shape->head_stride;
@@ -717,6 +719,115 @@ sas_status sas_gate_backward(const sas_shape *shape, const void *q, const void *
   p.scale_log2 = sm_scale * 1.4426950408889634f;
   for (int i = 0; i < SAS_GATE_DIM / 2; ++i) p.inv_freq[i] = pow(rope_theta, -(double)i / (SAS_GATE_DIM / 2));
   return hip_status(sas::launch_gate_backward(p, (hipStream_t)stream), "sas_gate_backward launch");
+}
+
+
+namespace {
+struct PrefillBackwardWorkspace {
+  size_t dgp, ghat, a, du_q, dwqn, pool, dgk, du_k, dwkn, part, total;
+  int n_hist, a_cols, key_chunks, head_groups, n_qblocks;
+};
+PrefillBackwardWorkspace prefill_backward_workspace(const sas_shape *sh, int32_t seq_len, int32_t max_sel) {
+  PrefillBackwardWorkspace w;
+  const size_t T = (size_t)seq_len, Hq = (size_t)sh->n_q_heads, Hkv = (size_t)sh->n_kv_heads, f = sizeof(float);
+  w.n_qblocks = (seq_len + SAS_BLOCK - 1) / SAS_BLOCK;
+  w.n_hist = (seq_len - 1) / SAS_BLOCK;
+  w.a_cols = (w.n_hist + 63) / 64 * 64;
+  w.key_chunks = (w.n_hist + sas::kChainBlocks - 1) / sas::kChainBlocks;
+  w.head_groups = (sh->n_q_heads / sh->n_kv_heads + 3) / 4;
+  const size_t tiles = Hq * 4 + Hkv * (size_t)(w.a_cols / 64) * 2;
+  w.dgp = 0;
+  w.ghat = w.dgp + align256((size_t)w.head_groups * T * Hkv * max_sel * f);
+  w.a = w.ghat + align256(Hkv * T * SAS_GATE_DIM * f);
+  w.du_q = w.a + align256(Hkv * T * (size_t)w.a_cols * f);
+  w.dwqn = w.du_q + align256(T * Hq * SAS_GATE_DIM * f);
+  w.pool = w.dwqn + align256((size_t)w.n_qblocks * Hkv * SAS_GATE_DIM * f);
+  w.dgk = w.pool + align256(Hkv * (size_t)w.n_hist * 3 * SAS_HEAD_DIM * f);
+  w.du_k = w.dgk + align256(Hkv * (size_t)w.a_cols * SAS_GATE_DIM * f);
+  w.dwkn = w.du_k + align256(Hkv * (size_t)w.n_hist * SAS_GATE_DIM * f);
+  w.part = w.dwkn + align256(Hkv * (size_t)w.key_chunks * SAS_GATE_DIM * f);
+  w.total = w.part + align256(tiles * sas::kPrefillSplit * 64 * 64 * f);
+  return w;
+}
+}  // namespace
+
+size_t sas_prefill_gate_backward_workspace_bytes(const sas_shape *shape, int32_t seq_len, int32_t max_sel) {
+  if (!shape || shape->n_kv_heads <= 0 || shape->n_q_heads <= 0 || shape->n_q_heads % shape->n_kv_heads ||
+      seq_len < 1 || max_sel <= 0)
+    return 0;
+  return prefill_backward_workspace(shape, seq_len, max_sel).total;
+}
+
+sas_status sas_prefill_gate_backward(const sas_shape *shape, const void *q, const void *k_pool, const void *v_pool,
+                                     const int32_t *block_table_row, int32_t seq_len, const int32_t *sel,
+                                     const float *gates, const int32_t *cnt, int32_t max_sel, float sm_scale,
+                                     const float *lse, const void *w_q, const float *w_qnorm, const void *w_k,
+                                     const float *w_knorm, const void *gate_keys, double rope_theta,
+                                     const void *d_out, float *d_gates, float *d_w_q, float *d_w_qnorm, float *d_w_k,
+                                     float *d_w_knorm, void *workspace, size_t workspace_bytes, void *stream) {
+  sas_status st = check_prefill(shape, true, seq_len);
+  if (st) return st;
+  if (!q || !k_pool || !v_pool || !block_table_row || !sel || !gates || !cnt || !lse || !w_q || !w_qnorm || !w_k ||
+      !w_knorm || !gate_keys || !d_out || !d_gates || !d_w_q || !d_w_qnorm || !d_w_k || !d_w_knorm || !workspace)
+    return fail(SAS_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (max_sel <= 0) return fail(SAS_ERR_INVALID_ARG, "max_sel must be positive");
+  if (max_sel > 64) return fail(SAS_ERR_UNSUPPORTED, "max_sel %d exceeds 64 (budgets above 4,096 tokens)", max_sel);
+  if (!(sm_scale > 0.f)) return fail(SAS_ERR_INVALID_ARG, "sm_scale must be positive");
+  if (!(rope_theta > 1.0)) return fail(SAS_ERR_INVALID_ARG, "rope_theta must be > 1");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(d_out) || !aligned16(w_q) ||
+      !aligned16(w_k) || !aligned16(gate_keys) || !aligned16(workspace))
+    return fail(SAS_ERR_UNSUPPORTED,
+                "q, k_pool, v_pool, d_out, w_q, w_k, gate_keys and workspace must be 16-byte aligned");
+  const PrefillBackwardWorkspace wl = prefill_backward_workspace(shape, seq_len, max_sel);
+  if (workspace_bytes < wl.total)
+    return fail(SAS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, wl.total);
+  sas::PrefillBackwardParams p;
+  p.q = (const uint16_t *)q;
+  p.k_pool = (const uint16_t *)k_pool;
+  p.v_pool = (const uint16_t *)v_pool;
+  p.d_out = (const uint16_t *)d_out;
+  p.gate_keys = (const uint16_t *)gate_keys;
+  p.w_q = (const uint16_t *)w_q;
+  p.w_k = (const uint16_t *)w_k;
+  p.block_table = block_table_row;
+  p.sel = sel;
+  p.cnt = cnt;
+  p.gates = gates;
+  p.lse = lse;
+  p.w_qnorm = w_qnorm;
+  p.w_knorm = w_knorm;
+  p.d_gates = d_gates;
+  p.d_w_q = d_w_q;
+  p.d_w_qnorm = d_w_qnorm;
+  p.d_w_k = d_w_k;
+  p.d_w_knorm = d_w_knorm;
+  char *ws = (char *)workspace;
+  p.ws_dgp = (float *)(ws + wl.dgp);
+  p.ws_ghat = (float *)(ws + wl.ghat);
+  p.ws_a = (float *)(ws + wl.a);
+  p.ws_du_q = (float *)(ws + wl.du_q);
+  p.ws_dwqn = (float *)(ws + wl.dwqn);
+  p.ws_pool = (float *)(ws + wl.pool);
+  p.ws_dgk = (float *)(ws + wl.dgk);
+  p.ws_du_k = (float *)(ws + wl.du_k);
+  p.ws_dwkn = (float *)(ws + wl.dwkn);
+  p.ws_part = (float *)(ws + wl.part);
+  p.page_stride = shape->page_stride;
+  p.tok_stride = shape->tok_stride;
+  p.head_stride = shape->head_stride;
+  p.n_q_heads = shape->n_q_heads;
+  p.n_kv_heads = shape->n_kv_heads;
+  p.group = shape->n_q_heads / shape->n_kv_heads;
+  p.head_groups = wl.head_groups;
+  p.max_sel = max_sel;
+  p.seq_len = seq_len;
+  p.n_qblocks = wl.n_qblocks;
+  p.n_hist = wl.n_hist;
+  p.a_cols = wl.a_cols;
+  p.key_chunks = wl.key_chunks;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  for (int i = 0; i < SAS_GATE_DIM / 2; ++i) p.inv_freq[i] = pow(rope_theta, -(double)i / (SAS_GATE_DIM / 2));
+  return hip_status(sas::launch_prefill_gate_backward(p, (hipStream_t)stream), "sas_prefill_gate_backward launch");
 }
 
 }  // extern "C"

@@ -35,17 +35,13 @@
 //     the factor rows staged in LDS; dW_k's
 //     rows are split into ranges whose partial tiles are then added in order
 //     (a fixed order throughout: deterministic).
-#include "sas_device.h"
+#include "backward_common.h"
 #include "sas_kernels.h"
 
 namespace sas {
 namespace {
 
 constexpr int kWavesG = 8;
-constexpr float kInvSqrtDg = 0.08838834764831845f;  // 1/sqrt(128)
-
-__device__ __forceinline__ bf16x8 to_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
 // K and V bytes, each read once per launch: non-temporal loads keep them out
 // of the caches (≈3 µs of the grad kernel's 61 at the Qwen3-8B shape)
 __device__ __forceinline__ u32x4 ld16_once(const char *p) {
@@ -66,12 +62,6 @@ __device__ __forceinline__ void keep_half(bool bit, float (&mx)[2 * n], float (&
     mn[c] = fminf(kn, row_dpp<kCtrl>(sn));
     sm[c] = ks + row_dpp<kCtrl>(ss);
   }
-}
-
-// the transpose of the rotate-half RoPE rotation at one pair (i, i+64)
-__device__ __forceinline__ void rope_back(float da, float db, float c, float s, float &ga, float &gb) {
-  ga = da * c + db * s;
-  gb = db * c - da * s;
 }
 
 }  // namespace
@@ -276,8 +266,6 @@ __global__ __launch_bounds__(kWavesG * 64, 1) void gate_grad_kernel(BackwardPara
 // and U^T = W_k[kvh] P^T for 16 blocks' pooled statistics P at a time.  The
 // max and min rows of P are bf16 values; the mean rows are split into bf16
 // high and low parts (about 16 significant bits).
-constexpr int kPoolPitch = 3 * kHeadDim + 4;  // LDS row of pooled statistics (floats), staggered banks
-constexpr int kUkPitch = kGateDim + 4;
 
 __global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
   __shared__ float un[kMaxGroup][kGateDim];    // u per head, then u / r
@@ -363,14 +351,7 @@ __global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
   // W_k A operands of this wave's 32 rows (row 32w + 16mt + l%16, inputs
   // 32ks + 8(l/16) .. +7), kept in registers for every chunk
   u32x4 wk[2][12];
-  {
-    const uint16_t *wkb =
-        p.w_k + ((int64_t)kvh * kGateDim + 32 * wave + (lane & 15)) * 3 * kHeadDim + 8 * (lane >> 4);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < 12; ++ks) wk[mt][ks] = ld16(wkb + (int64_t)16 * mt * 3 * kHeadDim + 32 * ks);
-  }
+  load_wk_rows(p.w_k, kvh, wk);
   // the pooled statistics of the historical blocks, written by
   // gate_grad_kernel, kChainBlocks blocks at a time: 96 float4 per block,
   // thread t takes float4 t + 256k.  The first chunk is fetched here, each
@@ -505,39 +486,8 @@ __global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
     }
     lds_barrier();
     if (i0 + kChainBlocks < p.max_sel) fetch_pooled(i0 + kChainBlocks);
-    // U^T = W_k P^T: lane l holds block l%16, rows 32w + 16mt + 4(l/16) + r
-    // (columns of blocks not in the chunk hold stale values and are not read)
-    {
-      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      const float *pb = &pooled[lane & 15][8 * (lane >> 4)];
-      // inputs 0..255 (max, min) are bf16 values: one MFMA; inputs 256..383
-      // (mean): high part and low part
-#pragma unroll
-      for (int ks = 0; ks < 12; ++ks) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = pb[32 * ks + e];
-        const u32x4 h = {pack_bf16_rne(x[0], x[1]), pack_bf16_rne(x[2], x[3]), pack_bf16_rne(x[4], x[5]),
-                         pack_bf16_rne(x[6], x[7])};
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(wk[mt][ks]), to_bf16x8(h), acc[mt], 0, 0, 0);
-        if (ks >= 8) {
-          float lo[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) lo[e] = x[e] - ((e & 1) ? bf16_hi(h[e >> 1]) : bf16_lo(h[e >> 1]));
-          const u32x4 l = {pack_bf16_rne(lo[0], lo[1]), pack_bf16_rne(lo[2], lo[3]), pack_bf16_rne(lo[4], lo[5]),
-                           pack_bf16_rne(lo[6], lo[7])};
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(wk[mt][ks]), to_bf16x8(l), acc[mt], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) uk[lane & 15][32 * wave + 16 * mt + 4 * (lane >> 4) + r] = acc[mt][r];
-    }
+    // U^T = W_k P^T (columns of blocks not in the chunk hold stale values and are not read)
+    project_pooled<kChainBlocks>(wk, pooled, uk);
     lds_barrier();
     // per block row: RMS, RoPE^T of dS ghat / sqrt(128), RMSNorm backward
     {
@@ -597,94 +547,6 @@ __global__ __launch_bounds__(256) void gate_chain_kernel(BackwardParams p) {
 }
 
 // ---------------------------------------------------------------- sums over the batch
-// acc = sum over rows n in [n_lo, n_hi) of A(n, 64-wide column slice) (x)
-// B(n, 64-wide column slice) for one 64 x 64 tile.  The fp32 operands are
-// split into bf16 high and low parts and summed as hi*hi + hi*lo + lo*hi on
-// v_mfma_f32_16x16x32_bf16 (the dropped lo*lo term is ~2^-16 relative; the
-// split itself keeps ~16 significant bits).  Rows go through LDS 32 at a
-// time, already split and transposed (column-major, 8 rows per 16 bytes,
-// a 40-element pitch so that the operand reads are conflict-free), the next
-// 32 fetched into registers while the current ones are summed (fetching
-// further ahead measured slower): thread t fetches rows 8(t/64) .. +7 of
-// column t%64.  Wave w owns the 32 x 32 quadrant (rows 32(w/2), columns
-// 32(w%2)) as 2 x 2 MFMA tiles; lane l feeds column l%16 of its tile and the
-// step's rows 8(l/16) .. +7 to both operands.  The rows are taken in order
-// (deterministic).
-constexpr int kOsPitch = 40;  // bf16 elements per LDS column of 32 rows
-struct OuterLds {
-  uint16_t ah[64][kOsPitch], al[64][kOsPitch], bh[64][kOsPitch], bl[64][kOsPitch];
-};
-
-template <typename FA, typename FB>
-__device__ void outer_sum_tile(FA fa, FB fb, int n_lo, int n_hi, f32x4 (&acc)[2][2], OuterLds &ls) {
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  const int wm = wave >> 1, wn = wave & 1, g = lane >> 4, c16 = lane & 15;
-  const int col = t & 63, rg = t >> 6;  // fetch: column, group of 8 rows
-  float ra[8], rb[8];
-  auto fetch = [&](int n0) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int n = n0 + 8 * rg + e;
-      ra[e] = n < n_hi ? fa(n, col) : 0.f;
-      rb[e] = n < n_hi ? fb(n, col) : 0.f;
-    }
-  };
-  auto split = [&](const float (&x)[8], uint16_t *hi, uint16_t *lo) {
-    u32x4 h, l;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t hp = pack_bf16_rne(x[2 * q], x[2 * q + 1]);
-      h[q] = hp;
-      l[q] = pack_bf16_rne(x[2 * q] - bf16_lo(hp), x[2 * q + 1] - bf16_hi(hp));
-    }
-    *reinterpret_cast<u32x4 *>(hi) = h;
-    *reinterpret_cast<u32x4 *>(lo) = l;
-  };
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (n_lo < n_hi) fetch(n_lo);
-  for (int n0 = n_lo; n0 < n_hi; n0 += 32) {
-    lds_barrier();
-    split(ra, &ls.ah[col][8 * rg], &ls.al[col][8 * rg]);
-    split(rb, &ls.bh[col][8 * rg], &ls.bl[col][8 * rg]);
-    lds_barrier();
-    if (n0 + 32 < n_hi) fetch(n0 + 32);
-    bf16x8 ah[2], al[2], bh[2], bl[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ah[i] = to_bf16x8(*reinterpret_cast<const u32x4 *>(&ls.ah[32 * wm + 16 * i + c16][8 * g]));
-      al[i] = to_bf16x8(*reinterpret_cast<const u32x4 *>(&ls.al[32 * wm + 16 * i + c16][8 * g]));
-      bh[i] = to_bf16x8(*reinterpret_cast<const u32x4 *>(&ls.bh[32 * wn + 16 * i + c16][8 * g]));
-      bl[i] = to_bf16x8(*reinterpret_cast<const u32x4 *>(&ls.bl[32 * wn + 16 * i + c16][8 * g]));
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bl[j], acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bh[j], acc[i][j], 0, 0, 0);
-      }
-  }
-}
-
-// writes a tile from outer_sum_tile: lane l of wave w holds rows
-// 32(w/2) + 16i + 4(l/16) + r, column 32(w%2) + 16j + l%16
-__device__ __forceinline__ void store_tile(const f32x4 (&acc)[2][2], float *dst, int64_t row_stride) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        dst[(int64_t)(32 * wm + 16 * i + 4 * (lane >> 4) + r) * row_stride + 32 * wn + 16 * j + (lane & 15)] =
-            acc[i][j][r];
-}
-
 // blocks [0, Hq*4): dW_q[h] tiles (2 x 2 per head), sums over the batch of
 // du_q (x) q; then Hkv*12*kSplitK blocks: partial dW_k[kvh] tiles (2 x 6 per
 // head, the (sequence, slot) rows split into kSplitK ranges), sums of
@@ -747,22 +609,8 @@ __global__ __launch_bounds__(256) void gate_param_reduce_kernel(BackwardParams p
 __global__ __launch_bounds__(256) void gate_dwk_sum_kernel(BackwardParams p) {
   const int kvh = blockIdx.x % p.n_kv_heads, tile = blockIdx.x / p.n_kv_heads;  // KV head fastest, as above
   const int k = kvh * 12 + tile, jt = tile / 6, it = tile % 6;
-  const float *src = p.ws_part + (int64_t)k * kSplitK * 64 * 64;
-  f32x4 acc[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int part = 0; part < kSplitK; ++part)
-      acc[q] += *reinterpret_cast<const f32x4 *>(src + part * 64 * 64 + 4 * (threadIdx.x + 256 * q));
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = 4 * (threadIdx.x + 256 * q);
-    float *dst = p.d_w_k + ((int64_t)kvh * kGateDim + 64 * jt + (e >> 6)) * 3 * kHeadDim + 64 * it + (e & 63);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) dst[v] = acc[q][v];
-  }
+  sum_tile_parts(p.ws_part + (int64_t)k * kSplitK * 64 * 64, kSplitK, 64 * 64,
+                 p.d_w_k + ((int64_t)kvh * kGateDim + 64 * jt) * 3 * kHeadDim + 64 * it, 3 * kHeadDim);
 }
 
 hipError_t launch_gate_backward(const BackwardParams &p, hipStream_t st) {

@@ -36,6 +36,7 @@
 // PV) MFMAs x 2 per wave.
 #include <limits.h>
 
+#include "prefill_backward.h"
 #include "sas_device.h"
 #include "sas_kernels.h"
 
@@ -321,13 +322,208 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
     const float l = rows_sum(ls[ct]);
     if (qvalid && 2 * hp + ct < nh) {
       const float inv = 1.0f / l;
-      uint16_t *dst = p.out + ((int64_t)tq * p.n_q_heads + kvh * G + h_lo + ct) * kHeadDim + 4 * g;
+      const int64_t row = (int64_t)tq * p.n_q_heads + kvh * G + h_lo + ct;
+      uint16_t *dst = p.out + row * kHeadDim + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const f32x4 v = o[ct][dt] * inv;
         *reinterpret_cast<u32x2 *>(dst + 16 * dt) = u32x2{pack_rne(v[0], v[1]), pack_rne(v[2], v[3])};
       }
+      // log-sum-exp of the (ungated) logits, natural log: (m + log2 l) ln 2
+      if (p.lse && g == 0) p.lse[row] = (m[ct] + log2f(l)) * 0.6931471805599453f;
     }
+  }
+}
+
+// ---------------------------------------------------------------- backward: dL/dg of every selected block
+// The gradient of the gated output with respect to each selected block's
+// continuous gate, for the backward of the training-time forward:
+//   dg_i = sum_{h in group} sum_{j in block c_i, j <= t} P_hj <dO_h, v_j>,
+// with P_hj = 2^(z_hj - lse2_h) from the forward's log-sum-exp (the plain
+// softmax over the query's selected tokens; the gates scale the blocks'
+// shares afterwards).  The walk is the forward's: one workgroup per
+// (64-query block, KV head, group of up to 4 query heads), the union of the
+// queries' selections in ascending order, each block's K and V rows copied
+// once into the LDS ring.  Per block, wave w (queries 16(w%4) .., heads
+// 2(w/4), 2(w/4)+1) forms S^T = K Q^T and D^T = V dO^T on MFMA (V is read
+// like K, as the A operand, so it is stored with K's swizzle), then per query
+// the sum over the block's keys and its two heads of P * D, added to the
+// query's slot in LDS.  Exactly two waves (the two head pairs) add to each
+// slot, and a sum of two terms onto zero does not depend on their order, so
+// the result is deterministic.  The groups of 4 heads write separate partial
+// sums, added in order by the chain kernel.
+__global__ __launch_bounds__(kThreads, 1) void prefill_grad_kernel(PrefillBackwardParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kStage];
+  __shared__ uint32_t bm[SAS_MAX_BLOCKS_DEV / 32];
+  __shared__ int16_t sel_l[kBlock][kMaxSel];
+  __shared__ float dg_l[kBlock][kMaxSel];
+  __shared__ int cnt_l[kBlock];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4, j = lane & 15;
+  const int G = p.group;
+  const int hg = blockIdx.x % p.head_groups;
+  const int rest = blockIdx.x / p.head_groups;
+  const int kvh = rest % p.n_kv_heads;
+  const int qb = p.n_qblocks - 1 - rest / p.n_kv_heads;
+  const int nh = min(4, G - 4 * hg);
+  const int T = p.seq_len;
+  const int t0 = qb * kBlock;
+  const int nq = min(kBlock, T - t0);
+  const int qw = wave & 3, hp = wave >> 2;
+  const int qi = 16 * qw + j;
+  const int h_lo = 4 * hg + 2 * hp;
+  const bool qvalid = qi < nq;
+  const int tq = t0 + qi;
+
+  // ---- the queries' selections into LDS and their union; slot sums zeroed
+  const int nwords = (qb + 32) >> 5;
+  for (int i = tid; i < nwords; i += kThreads) bm[i] = 0;
+  for (int e = tid; e < kBlock * kMaxSel; e += kThreads) (&dg_l[0][0])[e] = 0.f;
+  if (tid < kBlock) cnt_l[tid] = tid < nq ? p.cnt[(int64_t)(t0 + tid) * p.n_kv_heads + kvh] : 0;
+  __syncthreads();
+  for (int e = tid; e < nq * p.max_sel; e += kThreads) {
+    const int q = e / p.max_sel, slot = e - q * p.max_sel;
+    if (slot < cnt_l[q]) {
+      int c = p.sel[((int64_t)(t0 + q) * p.n_kv_heads + kvh) * p.max_sel + slot];
+      c = (unsigned)c <= (unsigned)qb ? c : qb;  // out-of-range entries are not trusted
+      sel_l[q][slot] = (int16_t)c;
+      atomicOr(&bm[c >> 5], 1u << (c & 31));
+    }
+  }
+
+  // B operands (q and dO of this lane's query, the wave's two heads) and the
+  // forward's log-sum-exp in log2 units
+  bf16x8 qB[kCt][4], dB[kCt][4];
+  float lse2[kCt];
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct) {
+    const bool ok = qvalid && 2 * hp + ct < nh;
+    const int64_t row = (int64_t)(ok ? tq : 0) * p.n_q_heads + kvh * G + (ok ? h_lo + ct : 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      qB[ct][ks] = as_bf16(ok ? ld16(p.q + row * kHeadDim + 8 * g + 32 * ks) : u32x4{0, 0, 0, 0});
+      dB[ct][ks] = as_bf16(ok ? ld16(p.d_out + row * kHeadDim + 8 * g + 32 * ks) : u32x4{0, 0, 0, 0});
+    }
+    lse2[ct] = ok ? p.lse[row] * kLog2e : 0.f;
+  }
+  wait_vm<0>();  // every compiler-visible load done before the copies start
+  __syncthreads();
+
+  const int cq = cnt_l[qi];
+  int ptr = 0;
+  int nxt_c = cq > 0 ? sel_l[qi][0] : INT_MAX;
+
+  // ---- block copies into the ring, K and V both with K's swizzle (16-byte
+  // slots by row % 16): wave w writes 1 KiB pieces 2w, 2w+1 of each tile
+  const char *kbase = reinterpret_cast<const char *>(p.k_pool) + (int64_t)kvh * p.head_stride * 2;
+  const char *vbase = reinterpret_cast<const char *>(p.v_pool) + (int64_t)kvh * p.head_stride * 2;
+  const int64_t tok_bytes = p.tok_stride * 2, page_bytes = p.page_stride * 2;
+  int64_t src[kCopies / 2];
+#pragma unroll
+  for (int k = 0; k < kCopies / 2; ++k) {
+    const int row = 4 * (2 * wave + k) + (lane >> 4), sl = lane & 15;
+    src[k] = row * tok_bytes + 16 * (sl ^ (row & 15));
+  }
+  const __attribute__((address_space(4))) int32_t *btc =
+      (const __attribute__((address_space(4))) int32_t *)p.block_table;
+  const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)&ring[0][0];
+  auto copy_block = [&](int c, int st) {
+    const int64_t off = (int64_t)btc[c] * page_bytes;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring0 + st * kStage + 2048 * wave);
+#pragma unroll
+    for (int k = 0; k < kCopies / 2; ++k) copy16(kbase + off + src[k], dst + 1024 * k);
+#pragma unroll
+    for (int k = 0; k < kCopies / 2; ++k) copy16(vbase + off + src[k], dst + kTile + 1024 * k);
+  };
+  int wi = 0;
+  uint32_t bits = __builtin_amdgcn_readfirstlane(bm[0]);
+  auto next_block = [&]() -> int {
+    while (bits == 0) {
+      if (++wi >= nwords) return -1;
+      bits = __builtin_amdgcn_readfirstlane(bm[wi]);
+    }
+    const int c = (wi << 5) + __builtin_ctz(bits);
+    bits &= bits - 1;
+    return c;
+  };
+  int c0 = next_block();  // never -1: every query selects its own block
+  int c1 = next_block();
+  int c2 = next_block();
+  copy_block(c0, 0);
+  copy_block(c1 >= 0 ? c1 : c0, 1);
+  copy_block(c2 >= 0 ? c2 : c0, 2);
+
+  for (int i = 0;; ++i) {
+    const int st = i & (kStages - 1);
+    const int c = c0;
+    wait_vm<2 * kCopies>();  // this wave's copies of block i landed
+    lds_barrier();           // ... and every other wave's; block i-1's stage is free
+    const int c3 = next_block();
+    copy_block(c3 >= 0 ? c3 : c, (i + 3) & (kStages - 1));
+
+    const bool s_l = nxt_c == c;
+    const int slot = ptr;
+    if (s_l) {
+      ++ptr;
+      nxt_c = ptr < cq ? sel_l[qi][ptr] : INT_MAX;
+    }
+    if (__builtin_amdgcn_ballot_w64(s_l) != 0) {
+      const uint8_t *kt = ring[st];
+      const uint8_t *vt = ring[st] + kTile;
+      f32x4 sacc[kCt][4], dacc[kCt][4];  // [head][key tile]
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        u32x4 ka[4], va[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int off = (16 * t + j) * kRow + 16 * ((4 * ks + g) ^ j);
+          ka[ks] = *reinterpret_cast<const u32x4 *>(kt + off);
+          va[ks] = *reinterpret_cast<const u32x4 *>(vt + off);
+        }
+#pragma unroll
+        for (int ct = 0; ct < kCt; ++ct) {
+          sacc[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dacc[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            sacc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(ka[ks]), qB[ct][ks], sacc[ct][t], 0, 0, 0);
+            dacc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(va[ks]), dB[ct][ks], dacc[ct][t], 0, 0, 0);
+          }
+        }
+      }
+      // keys the query may not see (another query's block, later keys of its
+      // own block, rows past the sequence end) are dropped by the select, so
+      // that whatever such rows hold never enters the sum
+      const bool causal = c == qb;
+      float acc = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < kCt; ++ct)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tau = 16 * t + 4 * g + r;
+            const bool keep = s_l && (!causal || tau <= qi);
+            const float pe = fast_exp2(sacc[ct][t][r] * p.scale_log2 - lse2[ct]);
+            acc += keep ? pe * dacc[ct][t][r] : 0.f;
+          }
+      acc = rows_sum(acc);
+      if (s_l && g == 0) atomicAdd(&dg_l[qi][slot], acc);
+    }
+    if (c1 < 0) break;  // block i was the walk's last
+    c0 = c1;
+    c1 = c2;
+    c2 = c3;
+  }
+  wait_vm<0>();  // the trailing filler copies land before the workgroup ends
+  __syncthreads();
+  float *dst = p.ws_dgp + (((int64_t)hg * T + t0) * p.n_kv_heads + kvh) * p.max_sel;
+  for (int e = tid; e < nq * p.max_sel; e += kThreads) {
+    const int q = e / p.max_sel, slot = e - q * p.max_sel;
+    dst[(int64_t)q * p.n_kv_heads * p.max_sel + slot] = dg_l[q][slot];
   }
 }
 
@@ -337,6 +533,12 @@ hipError_t launch_prefill_attend(const PrefillParams &p, hipStream_t st) {
     hipLaunchKernelGGL((prefill_attend_kernel<true>), grid, dim3(kThreads), 0, st, p);
   else
     hipLaunchKernelGGL((prefill_attend_kernel<false>), grid, dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_grad(const PrefillBackwardParams &p, hipStream_t st) {
+  const dim3 grid((unsigned)(p.n_qblocks * p.n_kv_heads * p.head_groups));
+  hipLaunchKernelGGL(prefill_grad_kernel, grid, dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 

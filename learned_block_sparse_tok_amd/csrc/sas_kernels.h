@@ -100,6 +100,7 @@ struct PrefillParams {
   const float *gates;           // nullable
   const int32_t *cnt;           // [T][Hkv]
   uint16_t *out;                // [T][Hq][128]
+  float *lse;                   // [T][Hq] log-sum-exp of the logits, nullable
   int64_t page_stride, tok_stride, head_stride;
   int32_t n_q_heads, n_kv_heads, group, head_groups, max_sel, seq_len, n_qblocks;
   float scale_log2;

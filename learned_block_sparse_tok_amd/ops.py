@@ -53,7 +53,10 @@ _SIGS = {
     "sas_decode_step_noalloc": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _F64, _I32, _I32, _I32, _I32,
                                        _F32, _I32, _VP, _VP, _VP, _VP, _VP, _VP]),
     "sas_prefill_select": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _F64, _I32, _VP, _VP, _VP, _VP, _VP]),
-    "sas_prefill_attend": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _F32, _VP, _VP]),
+    "sas_prefill_attend": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _F32, _VP, _VP, _VP]),
+    "sas_prefill_gate_backward_workspace_bytes": (_SZ, [_VP, _I32, _I32]),
+    "sas_prefill_gate_backward": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _F32, _VP, _VP, _VP,
+                                         _VP, _VP, _VP, _F64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "sas_gate_backward_workspace_bytes": (_SZ, [_VP, _I32]),
     "sas_gate_backward": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP, _VP, _VP, _VP, _VP,
                                  _F64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
@@ -295,16 +298,54 @@ def prefill_select(shape: SasShape, q, w_q, w_qnorm, gate_keys, block_table_row,
 
 
 def prefill_attend(shape: SasShape, q, k_pool, v_pool, block_table_row, seq_len, sel, gates, cnt, max_sel, sm_scale,
-                   out, stream=None):
+                   out, lse=None, stream=None):
     """Attention of every position of one sequence over its own selection
-    (gates None: plain mode); out bf16 [T][Hq][128]."""
+    (gates None: plain mode); out bf16 [T][Hq][128]; lse (optional) fp32
+    [T][Hq], the log-sum-exp of each query head's logits."""
     st = lib().sas_prefill_attend(ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"),
                                   _ptr(k_pool, torch.bfloat16, "k_pool"), _ptr(v_pool, torch.bfloat16, "v_pool"),
                                   _ptr(block_table_row, torch.int32, "block_table_row"), int(seq_len),
                                   _ptr(sel, torch.int32, "sel"), _ptr(gates, torch.float32, "gates"),
                                   _ptr(cnt, torch.int32, "cnt"), int(max_sel), float(sm_scale),
-                                  _ptr(out, torch.bfloat16, "out"), _stream(stream))
+                                  _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream))
     _check(st, "sas_prefill_attend")
+
+
+def prefill_gate_backward_workspace_bytes(shape: SasShape, seq_len: int, max_sel: int) -> int:
+    return int(lib().sas_prefill_gate_backward_workspace_bytes(ctypes.byref(shape), int(seq_len), int(max_sel)))
+
+
+def prefill_gate_backward(shape: SasShape, q, k_pool, v_pool, block_table_row, seq_len, sel, gates, cnt, max_sel,
+                          sm_scale, lse, w_q, w_qnorm, w_k, w_knorm, gate_keys, theta, d_out, workspace=None,
+                          stream=None, out=None):
+    """Gradients of the gate parameters through the continuous gates of the
+    training-time forward of one sequence.  Returns dict(d_gates, d_w_q,
+    d_w_qnorm, d_w_k, d_w_knorm) (fp32 device tensors; `out` may supply
+    them preallocated)."""
+    dev = q.device
+    T, Hq, _ = q.shape
+    Hkv = shape.n_kv_heads
+    if out is None:
+        out = dict(d_gates=torch.empty((T, Hkv, max_sel), dtype=torch.float32, device=dev),
+                   d_w_q=torch.empty((Hq, 128, 128), dtype=torch.float32, device=dev),
+                   d_w_qnorm=torch.empty(128, dtype=torch.float32, device=dev),
+                   d_w_k=torch.empty((Hkv, 128, 384), dtype=torch.float32, device=dev),
+                   d_w_knorm=torch.empty(128, dtype=torch.float32, device=dev))
+    if workspace is None:
+        workspace = torch.empty(prefill_gate_backward_workspace_bytes(shape, seq_len, max_sel), dtype=torch.uint8,
+                                device=dev)
+    st = lib().sas_prefill_gate_backward(
+        ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"), _ptr(k_pool, torch.bfloat16, "k_pool"),
+        _ptr(v_pool, torch.bfloat16, "v_pool"), _ptr(block_table_row, torch.int32, "block_table_row"), int(seq_len),
+        _ptr(sel, torch.int32, "sel"), _ptr(gates, torch.float32, "gates"), _ptr(cnt, torch.int32, "cnt"),
+        int(max_sel), float(sm_scale), _ptr(lse, torch.float32, "lse"), _ptr(w_q, torch.bfloat16, "w_q"),
+        _ptr(w_qnorm, torch.float32, "w_qnorm"), _ptr(w_k, torch.bfloat16, "w_k"),
+        _ptr(w_knorm, torch.float32, "w_knorm"), _ptr(gate_keys, torch.bfloat16, "gate_keys"), float(theta),
+        _ptr(d_out, torch.bfloat16, "d_out"), _ptr(out["d_gates"]), _ptr(out["d_w_q"]), _ptr(out["d_w_qnorm"]),
+        _ptr(out["d_w_k"]), _ptr(out["d_w_knorm"]), _ptr(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "sas_prefill_gate_backward")
+    return out
 
 
 class Prefill:
@@ -323,6 +364,7 @@ class Prefill:
         self.scores = (torch.empty((seq_len, n_kv_heads, max_blocks), dtype=torch.float32, device=device)
                        if keep_scores else None)
         self.out = torch.empty((seq_len, n_q_heads, 128), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((seq_len, n_q_heads), dtype=torch.float32, device=device)
 
     def select(self, q, w_q, w_qnorm, gate_keys, block_table_row, stream=None):
         prefill_select(self.shape, q, w_q, w_qnorm, gate_keys, block_table_row, self.seq_len, self.theta, self.budget,
@@ -330,7 +372,8 @@ class Prefill:
 
     def attend(self, q, k_pool, v_pool, block_table_row, stream=None):
         prefill_attend(self.shape, q, k_pool, v_pool, block_table_row, self.seq_len, self.sel,
-                       self.gates if self.gated else None, self.cnt, self.max_sel, self.sm_scale, self.out, stream)
+                       self.gates if self.gated else None, self.cnt, self.max_sel, self.sm_scale, self.out,
+                       self.lse, stream)
 
     def forward(self, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table_row, stream=None):
         self.select(q, w_q, w_qnorm, gate_keys, block_table_row, stream)

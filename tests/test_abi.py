@@ -158,7 +158,7 @@ def test_prefill_rejects_bad_arguments(lib):
 
     def att_call(sh=sh1, T=100, max_sel=2, out=FAKE):
         return lib.sas_prefill_attend(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, T, FAKE, None, FAKE, max_sel, 0.088,
-                                      out, None)
+                                      out, None, None)
 
     assert sel_call(sh=_shape(batch=2)) == ops.SAS_ERR_INVALID_ARG  # one sequence per call
     assert sel_call(T=0) == ops.SAS_ERR_INVALID_ARG
@@ -221,3 +221,27 @@ def test_probe_read_rejects_bad_arguments_and_accepts_empty_list(lib):
     assert lib.sas_probe_read(FAKE, 4, 1, ctypes.c_void_p(0x10008), 64, None) == ops.SAS_ERR_INVALID_ARG
     assert lib.sas_probe_read(FAKE, 5, 2, aligned, 47, None) == ops.SAS_ERR_INVALID_ARG  # needs 3 words
     assert lib.sas_probe_read(None, 0, 1, None, 0, None) == ops.SAS_OK
+
+
+def test_prefill_gate_backward_rejects_bad_arguments(lib):
+    sh1 = _shape(batch=1)
+    T = 1000
+    need = lib.sas_prefill_gate_backward_workspace_bytes(ctypes.byref(sh1), T, 16)
+    # the dense position x block matrix dominates: Hkv * T * (blocks rounded up to 64) floats
+    assert need >= 2 * T * 64 * 4
+    assert lib.sas_prefill_gate_backward_workspace_bytes(ctypes.byref(sh1), 0, 16) == 0
+
+    def call(sh=sh1, T=T, lse=FAKE, max_sel=16, ws_bytes=need, theta=1e6, ws=FAKE):
+        return lib.sas_prefill_gate_backward(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, T, FAKE, FAKE, FAKE, max_sel,
+                                             0.088, lse, FAKE, FAKE, FAKE, FAKE, FAKE, theta, FAKE, FAKE, FAKE, FAKE,
+                                             FAKE, FAKE, ws, ws_bytes, None)
+
+    assert call(sh=_shape(batch=2)) == ops.SAS_ERR_INVALID_ARG  # one sequence per call
+    assert call(T=0) == ops.SAS_ERR_INVALID_ARG
+    assert call(T=16 * 64 + 1) == ops.SAS_ERR_INVALID_ARG  # needs 17 blocks, max_blocks 16
+    assert call(lse=None) == ops.SAS_ERR_INVALID_ARG  # the forward's log-sum-exp is required
+    assert call(max_sel=0) == ops.SAS_ERR_INVALID_ARG
+    assert call(max_sel=65) == ops.SAS_ERR_UNSUPPORTED
+    assert call(theta=1.0) == ops.SAS_ERR_INVALID_ARG
+    assert call(ws_bytes=need - 1) == ops.SAS_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(4096 + 4)) == ops.SAS_ERR_UNSUPPORTED  # not 16-byte aligned

@@ -97,3 +97,90 @@ def test_gate_backward_parity(case):
     torch.cuda.synchronize()
     for name in bg:
         assert torch.equal(bg[name], bg2[name]), name
+
+
+# ------------------------------------------------------------------ backward of the training-time forward
+PREFILL_BWD_CASES = [
+    dict(name="paged_g4_t1000", T=1000, Hq=8, Hkv=2, budget=256, layout="paged", seed=71),
+    dict(name="contig_g5_t700", T=700, Hq=10, Hkv=2, budget=512, layout="contiguous", seed=72),
+    dict(name="paged_g1_t577", T=577, Hq=2, Hkv=2, budget=128, layout="paged", seed=73),
+    dict(name="paged_g8_t900_b1024", T=900, Hq=16, Hkv=2, budget=1024, layout="paged", seed=74),
+    dict(name="paged_g16_t300", T=300, Hq=16, Hkv=1, budget=192, layout="paged", seed=75),
+    dict(name="one_block_t50", T=50, Hq=4, Hkv=1, budget=128, layout="paged", seed=76),
+]
+
+
+def prefill_oracle_gates(o: dict, sel_g: np.ndarray, cnt: np.ndarray) -> np.ndarray:
+    """The oracle's gates (sigmoid of its own scores) of the GPU's selection:
+    the oracle's where the two selections agree, else recomputed per unit."""
+    gates = o["gates"].copy()
+    T, Hkv, _ = sel_g.shape
+    for t in range(T):
+        for k in range(Hkv):
+            if not np.array_equal(sel_g[t, k], o["sel"][t, k]):
+                gates[t, k] = oracle.block_gates(o["scores"][t, k], sel_g[t, k], int(cnt[t, k]))
+    return gates
+
+
+def gpu_prefill_backward(w, gk, budget, d_out, pf=None):
+    """sas_prefill_select + gated sas_prefill_attend (with lse) +
+    sas_prefill_gate_backward; returns (Prefill, dict of device gradients)."""
+    if pf is None:
+        pf = ops.Prefill(w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, w.batch, budget, w.theta, True,
+                         device=DEV, keep_scores=True)
+        pf.forward(w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, w.block_table[0])
+    shape = ops.make_shape(1, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides)
+    bg = ops.prefill_gate_backward(shape, w.q, w.k_pool, w.v_pool, w.block_table[0], w.batch, pf.sel, pf.gates,
+                                   pf.cnt, budget // 64, SM_SCALE, pf.lse, w.w_q, w.w_qnorm, w.w_k, w.w_knorm, gk,
+                                   w.theta, d_out)
+    return pf, bg
+
+
+@pytest.mark.parametrize("case", PREFILL_BWD_CASES, ids=lambda c: c["name"])
+def test_prefill_gate_backward_parity(case):
+    """sas_prefill_gate_backward against oracle.prefill_gate_backward at every
+    position (several 64-position tiles, ragged last tile, groups of 1, 4, 5,
+    8 and 16 query heads, budgets 128 to 1,024, paged and contiguous, a
+    sequence with no historical block).  Each side runs its own forward; the
+    GPU's selection is validated against the oracle's (ties resolved inside
+    the band are allowed) and the oracle's backward runs on it, with the
+    oracle's own gates of those blocks."""
+    from gpu_harness import prefill_gate_keys
+    say("prefill gate backward", case["name"])
+    w = wl.make_prefill(case["T"], case["Hq"], case["Hkv"], case["budget"], case["layout"], case["seed"], DEV,
+                        random_norms=True, extra_pages=2)
+    h = Host(w)
+    budget = case["budget"]
+    nb = w.batch // 64
+    gk_o = np.zeros((w.n_pages, w.n_kv_heads, wl.GATE_DIM), np.uint16)
+    oracle.pool_blocks(h.k, h.bt[:1], w.strides, w.n_kv_heads, np.zeros(nb, np.int32), np.arange(nb, dtype=np.int32),
+                       h.w_k, h.wkn, w.theta, gk_o)
+    sel_o, gates_o, cnt_o, scores_o, _ = oracle.prefill(h.q, h.k, h.v, h.bt[0], w.strides, w.n_kv_heads, gk_o,
+                                                        h.w_q, h.wqn, w.theta, budget, True, SM_SCALE)
+    gk_g = prefill_gate_keys(w)
+    gen = torch.Generator(device=DEV).manual_seed(case["seed"])
+    d_out = torch.randn((w.batch, w.n_q_heads, 128), generator=gen, device=DEV).to(torch.bfloat16)
+    pf, bg = gpu_prefill_backward(w, gk_g, budget, d_out)
+    torch.cuda.synchronize()
+    sel_g, cnt_g = wl.host(pf.sel), wl.host(pf.cnt)
+    o = dict(sel=sel_o, gates=gates_o, cnt=cnt_o, scores=scores_o)
+    ties = compare_selection(dict(sel=sel_g, gates=wl.host(pf.gates), cnt=cnt_g), o, h.lens, budget)
+    say(f"  boundary ties {len(ties)}")
+    gates_for = prefill_oracle_gates(o, sel_g, cnt_g)
+    bo = oracle.prefill_gate_backward(h.q, h.k, h.v, h.bt[0], w.strides, w.n_kv_heads, sel_g, gates_for, cnt_g,
+                                      SM_SCALE, h.w_q, h.wqn, h.w_k, h.wkn, gk_o, w.theta, wl.host(d_out))
+    for name in ("d_gates", "d_w_q", "d_w_qnorm", "d_w_k", "d_w_knorm"):
+        if name in ("d_w_k", "d_w_knorm") and w.batch <= 64:
+            # no position has a historical block: the key side is exactly zero
+            assert not np.any(wl.host(bg[name])), name
+            continue
+        close(wl.host(bg[name]), bo[name], 1e-3, name)
+    dgh = wl.host(bg["d_gates"])
+    for t in range(w.batch):
+        for k in range(w.n_kv_heads):
+            assert np.all(dgh[t, k, cnt_g[t, k]:] == 0)
+    # a fixed summation order: the same inputs give the same bits
+    _, bg2 = gpu_prefill_backward(w, gk_g, budget, d_out, pf=pf)
+    torch.cuda.synchronize()
+    for name in bg:
+        assert torch.equal(bg[name], bg2[name]), name

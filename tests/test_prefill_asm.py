@@ -8,7 +8,8 @@ only sound when (1) nothing else in the kernel uses M0, which the asm clobbers,
 and (2) no other vector-memory instruction is issued between the first copy
 and the final drain, so that each vmcnt wait counts copies only.  This test
 compiles prefill.hip for gfx950 with the library's flags and checks both on
-the generated AMD assembly of every prefill_attend_kernel instance.
+the generated AMD assembly of every prefill_attend_kernel instance and of
+prefill_grad_kernel (the backward's walk, which copies the same way).
 """
 from __future__ import annotations
 
@@ -27,11 +28,12 @@ VMEM = re.compile(r"^\s*(global|buffer|flat|scratch)_\w+")
 
 
 def kernel_bodies(asm: str):
-    """(name, [instruction lines]) of every prefill_attend_kernel instance."""
+    """(name, [instruction lines]) of every prefill_attend_kernel instance and
+    of prefill_grad_kernel."""
     lines = asm.splitlines()
     out, cur, name = [], None, None
     for ln in lines:
-        m = re.match(r"^(_Z\w*prefill_attend_kernel\w*):", ln)
+        m = re.match(r"^(_Z\w*prefill_(?:attend|grad)_kernel\w*):", ln)
         if m:
             cur, name = [], m.group(1)
             continue
@@ -54,7 +56,8 @@ def test_prefill_copies_own_m0_and_the_load_counter(tmp_path):
                            os.path.join(CSRC, "prefill.hip"), "-o", str(out)],
                           stderr=subprocess.DEVNULL)
     bodies = kernel_bodies(out.read_text())
-    assert len(bodies) >= 2  # plain and gated instances
+    assert len(bodies) >= 3  # plain and gated forward, and the backward's walk
+    assert any("prefill_grad_kernel" in name for name, _ in bodies)
     for name, ins in bodies:
         copies = [i for i, s in enumerate(ins) if s.startswith("global_load_lds_dwordx4")]
         assert copies, name
