@@ -375,6 +375,62 @@ def run_prefill(args):
         line["cpu_baseline"] = cpu_baseline_prefill(w, pooled, args.budget, worst == "gated", args.cpu_seconds)
         log(f"cpu baseline: {line['cpu_baseline']['value']:.1f} tokens/s on {line['cpu_baseline']['cores']} threads")
     print(json.dumps(line), flush=True)
+    if args.backward:
+        print(json.dumps(time_prefill_backward(args, w, gk, bt_row, steps, warm)), flush=True)
+
+
+def time_prefill_backward(args, w, gk, bt_row, steps, warm):
+    """sas_prefill_gate_backward after the gated training-time forward (with
+    its log-sum-exp), launched back to back and bracketed by HIP events on the
+    launch stream."""
+    import torch
+    from learned_block_sparse_tok_amd import ops
+    from learned_block_sparse_tok_amd import workloads as wl
+    dev = w.q.device
+    T, G, n_sel = w.batch, w.group, args.budget // 64
+    pf = ops.Prefill(w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, T, args.budget, w.theta, True, device=dev)
+    pf.forward(w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, bt_row)
+    gen = torch.Generator(device=dev).manual_seed(901)
+    d_out = torch.randn((T, w.n_q_heads, 128), generator=gen, device=dev).to(torch.bfloat16)
+    shape1 = ops.make_shape(1, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides)
+    ws_bytes = ops.prefill_gate_backward_workspace_bytes(shape1, T, n_sel)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def one(out=None):
+        return ops.prefill_gate_backward(shape1, w.q, w.k_pool, w.v_pool, bt_row, T, pf.sel, pf.gates, pf.cnt, n_sel,
+                                         pf.sm_scale, pf.lse, w.w_q, w.w_qnorm, w.w_k, w.w_knorm, gk, w.theta, d_out,
+                                         workspace=ws, out=out)
+
+    out = one()
+    for _ in range(warm):
+        one(out)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        one(out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    # the walk's algorithmic work: per query head, position and attended key,
+    # 2 x 128 flops for the score and 2 x 128 for <dO, v> (the forward's count)
+    flops = prefill_flops(wl.host(pf.cnt), G)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"training-time backward: {ms:.2f} ms per sequence = {T / (ms * 1e-3):.0f} tokens/s, walk work "
+        f"{tflops:.1f} TFLOP/s over the whole call, workspace {ws_bytes / 2**20:.0f} MiB")
+    return {"metric": "training-time backward tokens/s (continuous-gate gradients of one layer)",
+            "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "higher_is_better": True, "n_gpus": 1,
+            "steps": steps, "warmup": warm, "ms_per_step": round(ms, 4), "dtype": "bf16 inputs, fp32 gradients",
+            "data": "synthetic",
+            "config": {"workload": args.workload, "seq_len": T, "n_q_heads": w.n_q_heads,
+                       "n_kv_heads": w.n_kv_heads, "budget_tokens": args.budget, "kv_layout": w.layout,
+                       "workspace_bytes": ws_bytes},
+            "roofline": {"bound": "mfma", "kernel": "sas_prefill_gate_backward (whole call, 7 kernels; the "
+                                                     "block walk prefill_grad_kernel dominates)",
+                         "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "flops_per_launch": flops, "avg_launch_us": round(ms * 1e3, 1)}}
 
 
 def time_backward(args, layers, w0):
@@ -580,7 +636,8 @@ def main():
                     help="only run a plain device-to-device copy of this many MiB --steps times (a kernel of "
                          "known traffic, for calibrating the HBM byte counters), then exit")
     ap.add_argument("--backward", action="store_true",
-                    help="also time sas_gate_backward after the gated step (prints a second JSON line)")
+                    help="also time the continuous-gate backward (sas_gate_backward after the gated step, or "
+                         "sas_prefill_gate_backward after the training-time forward): a second JSON line")
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "sliced", "two_launches"],
                     help="sas_decode_step path (auto: one fused launch when the pairs fill the GPU)")
     ap.add_argument("--graph", action="store_true",

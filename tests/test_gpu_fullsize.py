@@ -375,3 +375,62 @@ def test_prefill_long_sequence_uses_the_per_position_selection():
     o = dict(gate_keys=gk_o, sel=sel, gates=gates, cnt=cnt, scores=scores, out=out)
     ties = compare_step(h, g, o, True, w.budget)
     say(f"prefill T={T}: boundary ties {ties}")
+
+
+def test_prefill_gate_backward_full_size():
+    """sas_prefill_gate_backward on the training-time workload of the
+    benchmark (one 32,768-token sequence, Qwen3-8B heads, budget 2,048), in
+    the launch configuration the benchmark times.  The gradient is linear in
+    d_out, so with d_out zero except at sampled positions the GPU's whole
+    backward must equal the oracle's backward summed over those positions
+    alone (on the GPU's validated selection); d_gates vanish elsewhere.  The
+    full-d_out run is then checked by linearity: it equals the sum of the
+    sampled run and the run on the complementary positions."""
+    from test_gpu_backward import close, gpu_prefill_backward, prefill_oracle_gates
+    w = wl.named("prefill_8b", device=DEV)
+    T = w.batch
+    gk = prefill_gate_keys(w)
+    pos = np.array([0, 63, 64, 130, 4095, 4096, 16000, 27000, 32767])
+    gen = torch.Generator(device=DEV).manual_seed(81)
+    d_full = torch.randn((T, w.n_q_heads, 128), generator=gen, device=DEV).to(torch.bfloat16)
+    mask = torch.zeros(T, dtype=torch.bool, device=DEV)
+    mask[torch.as_tensor(pos, device=DEV)] = True
+    d_s = torch.where(mask[:, None, None], d_full, torch.zeros_like(d_full))
+    d_c = torch.where(mask[:, None, None], torch.zeros_like(d_full), d_full)
+    pf, b_s = gpu_prefill_backward(w, gk, w.budget, d_s)
+    b_s = {k: v.clone() for k, v in b_s.items()}
+    _, b_c = gpu_prefill_backward(w, gk, w.budget, d_c, pf=pf)
+    b_c = {k: v.clone() for k, v in b_c.items()}
+    _, b_f = gpu_prefill_backward(w, gk, w.budget, d_full, pf=pf)
+    torch.cuda.synchronize()
+    for name in ("d_w_q", "d_w_qnorm", "d_w_k", "d_w_knorm"):
+        close(wl.host(b_f[name]), wl.host(b_s[name]).astype(np.float64) + wl.host(b_c[name]), 1e-5,
+              name + " (sampled + complement)")
+    np.testing.assert_array_equal(wl.host(b_f["d_gates"])[pos], wl.host(b_s["d_gates"])[pos])
+    others = np.setdiff1d(np.arange(T), pos)
+    assert not np.any(wl.host(b_s["d_gates"])[others])
+    # the oracle at the sampled positions
+    sub = dataclasses.replace(w, batch=len(pos), q=w.q[torch.as_tensor(pos, device=DEV)],
+                              seq_lens=torch.as_tensor(pos + 1, dtype=torch.int32, device=DEV),
+                              block_table=w.block_table[:len(pos)])
+    h = Host(sub)
+    nb = T // 64
+    gk_o = np.zeros((w.n_pages, w.n_kv_heads, wl.GATE_DIM), np.uint16)
+    oracle.pool_blocks(h.k, h.bt[:1], w.strides, w.n_kv_heads, np.zeros(nb, np.int32), np.arange(nb, dtype=np.int32),
+                       h.w_k, h.wkn, w.theta, gk_o)
+    q_all = wl.host(w.q)
+    sel_o, gates_o, cnt_o, scores_o, _ = oracle.prefill(q_all, h.k, h.v, h.bt[0], w.strides, w.n_kv_heads, gk_o,
+                                                        h.w_q, h.wqn, w.theta, w.budget, True, SM_SCALE,
+                                                        positions=pos)
+    sel_g, cnt_g, gates_g = wl.host(pf.sel), wl.host(pf.cnt), wl.host(pf.gates)
+    o = dict(sel=sel_o, gates=gates_o, cnt=cnt_o, scores=scores_o)
+    ties = compare_selection(dict(sel=sel_g[pos], gates=gates_g[pos], cnt=cnt_g[pos]), o, pos + 1, w.budget)
+    say(f"prefill_8b backward: positions {pos.tolist()}, boundary ties {ties}")
+    gates_for = gates_g.copy()
+    gates_for[pos] = prefill_oracle_gates(o, sel_g[pos], cnt_g[pos])
+    bo = oracle.prefill_gate_backward(q_all, h.k, h.v, h.bt[0], w.strides, w.n_kv_heads, sel_g, gates_for, cnt_g,
+                                      SM_SCALE, h.w_q, h.wqn, h.w_k, h.wkn, gk_o, w.theta, wl.host(d_s),
+                                      positions=pos)
+    close(wl.host(b_s["d_gates"])[pos], bo["d_gates"], 1e-3, "d_gates")
+    for name in ("d_w_q", "d_w_qnorm", "d_w_k", "d_w_knorm"):
+        close(wl.host(b_s[name]), bo[name], 1e-3, name)
