@@ -191,17 +191,20 @@ def prefill_flops(cnt, group):
 
 
 def prefill_executed_flops(sel, cnt, group):
-    """Matrix work the kernel issues: per 16-query wave and head group, 128
-    MFMAs of 16x16x32 (4 heads x (QK + PV)) for every block in the union of
-    those 16 queries' selections."""
+    """Matrix work the kernel issues: a wave's 16 MFMA columns are 16/h
+    queries x h heads (h = 4 for groups of 3 or more heads, else the group
+    size), and per block in the union of those queries' selections the wave
+    issues 32 MFMAs of 16x16x32 (QK + PV), once per group of h heads."""
     import numpy as np
     T, Hkv, _ = sel.shape
+    hw = 4 if group >= 3 else group
+    qw = 16 // hw
     visits = 0
-    for t0 in range(0, T, 16):
+    for t0 in range(0, T, qw):
         for k in range(Hkv):
-            rows = [sel[t, k, :cnt[t, k]] for t in range(t0, min(T, t0 + 16))]
+            rows = [sel[t, k, :cnt[t, k]] for t in range(t0, min(T, t0 + qw))]
             visits += len(np.unique(np.concatenate(rows)))
-    return float(visits) * ((group + 3) // 4) * 128 * 16 * 16 * 32 * 2
+    return float(visits) * ((group + hw - 1) // hw) * 32 * 16 * 16 * 32 * 2
 
 
 def cpu_baseline_prefill(w, gk_o_fn, budget, gated, seconds):

@@ -345,7 +345,7 @@ sas_status sas_prefill_attend(const sas_shape *shape, const void *q, const void 
   p.n_q_heads = shape->n_q_heads;
   p.n_kv_heads = shape->n_kv_heads;
   p.group = shape->n_q_heads / shape->n_kv_heads;
-  p.head_groups = (p.group + 3) / 4;
+  p.head_groups = 0;  // set by the launcher for its wave layout
   p.max_sel = max_sel;
   p.seq_len = seq_len;
   p.n_qblocks = (seq_len + SAS_BLOCK - 1) / SAS_BLOCK;
@@ -734,7 +734,8 @@ PrefillBackwardWorkspace prefill_backward_workspace(const sas_shape *sh, int32_t
   w.n_hist = (seq_len - 1) / SAS_BLOCK;
   w.a_cols = (w.n_hist + 63) / 64 * 64;
   w.key_chunks = (w.n_hist + sas::kChainBlocks - 1) / sas::kChainBlocks;
-  w.head_groups = (sh->n_q_heads / sh->n_kv_heads + 3) / 4;
+  const int hw = sas::prefill_heads_per_wave(sh->n_q_heads / sh->n_kv_heads);
+  w.head_groups = (sh->n_q_heads / sh->n_kv_heads + hw - 1) / hw;
   const size_t tiles = Hq * 4 + Hkv * (size_t)(w.a_cols / 64) * 2;
   w.dgp = 0;
   w.ghat = w.dgp + align256((size_t)w.head_groups * T * Hkv * max_sel * f);

@@ -1,5 +1,5 @@
 // Training-time forward: every position of one sequence attends its own
-// block selection.
+// block selection; and the walk of its continuous-gate backward.
 //
 // SAS selects KV blocks for each query and trains with a Top-K of 31
 // historical 64-token blocks on 32,768-token sequences ("Tencent released
@@ -8,32 +8,36 @@
 // causally, the blocks selected for it (its own block t/64 last), plain or
 // with each historical block scaled by its continuous gate.
 //
-// One 512-thread workgroup per (64-query block, KV head, group of up to 4
-// query heads).  The workgroup marks the union of its queries' selections in
-// an LDS bitmap and walks it in ascending block order.  Each visited block's
-// K and V rows (32 KiB) are copied once into LDS by the gfx950 global-to-LDS
-// loads (global_load_lds_dwordx4) and shared by the 4 waves; a ring of four
-// 32 KiB stages keeps the next three blocks in flight while one is consumed.
-// Eight waves, two per SIMD, so that one wave's softmax runs while the
-// other's matrix products do.
-// The copies are the only vector-memory operations of the walk (the
-// selections of the 64 queries are staged in LDS first), so each iteration
-// waits for exactly the copies of the block it consumes.
+// One workgroup per (64-query block, KV head, group of kHW query heads).
+// The workgroup marks the union of its queries' selections in an LDS bitmap
+// and walks it in ascending block order.  Each visited block's K and V rows
+// (32 KiB) are copied once into LDS by the gfx950 global-to-LDS loads
+// (global_load_lds_dwordx4) and shared by all waves; a ring of four 32 KiB
+// stages keeps the next three blocks in flight while one is consumed.  The
+// copies are the only vector-memory operations of the walk (the selections of
+// the 64 queries are staged in LDS first), so each iteration waits for
+// exactly the copies of the block it consumes.
+//
+// The selections are sparse (31 of up to 511 blocks per query), so a wave's
+// 16 MFMA columns hold few queries and all their heads: 16/kHW queries x kHW
+// heads (kHW = 4 for groups of 3 or more heads, else the group size), and
+// the workgroup has 4 kHW waves (64 queries).  A wave whose queries did not
+// select a block skips it; with 4 queries per wave about a fifth of the
+// waves work on each block of a 511-block union, against two thirds with 16
+// queries per wave, for the same useful columns.
+//
 // Rows are stored unpadded (the copy writes 1 KiB per instruction) with a
 // row-dependent XOR swizzle instead: K's 16-byte slots by row % 16 (the
 // A-operand reads of 16 rows at one column hit 16 different slots), V's
 // 32-byte pairs by row % 4 (the transposing reads of 4 rows x 32 bytes hit 4
-// different pairs).  Wave w owns queries 16(w%4) .. 16(w%4)+15 of the block
-// and two of the group's heads, 2(w/4) and 2(w/4)+1:
-//   S^T (64 keys x 16 queries) = K . Q^T per head with
-//     v_mfma_f32_16x16x32_bf16, K read from LDS as the A operand;
-//   the lane of a query that did not select the block masks its column to
-//     -inf; the query's own block is masked causally (key <= query);
+// different pairs).  Per visited block a working wave forms
+//   S^T (64 keys x 16 columns) = K . Q^T with v_mfma_f32_16x16x32_bf16, K
+//     read from LDS as the A operand;
+//   the column of a query that did not select the block is masked to -inf;
+//     the query's own block is masked causally (key <= query);
 //   online softmax in the log2 domain; O^T += V^T . P^T, V^T read with
 //     ds_read_b64_tr_b16.
-// A wave none of whose 16 queries selected the block skips its arithmetic.
-// The work is a dense contraction per visited block: 2 heads x (16 QK + 16
-// PV) MFMAs x 2 per wave.
+// 16 QK + 16 PV MFMAs per working wave and block.
 #include <limits.h>
 
 #include "prefill_backward.h"
@@ -43,14 +47,21 @@
 namespace sas {
 namespace {
 
-constexpr int kThreads = 512;  // 8 waves: 4 query quarters x 2 head pairs, two waves per SIMD
 constexpr int kRow = kHeadDim * 2;        // 256-byte K / V rows, unpadded
 constexpr int kTile = kBlock * kRow;      // 16 KiB
 constexpr int kStage = 2 * kTile;         // K tile, then V tile
 constexpr int kStages = 4;                // ring: 3 blocks in flight + 1 consumed
-constexpr int kCopies = kStage / 1024 / 8;  // 1 KiB copy instructions per wave per stage: 4
-constexpr int kCt = 2;                      // query heads per wave
 constexpr int kMaxSel = 64;               // selections per query staged in LDS (budgets up to 4,096)
+
+// Wave layout for kHW heads per query column group: the wave's 16 MFMA
+// columns are kQW queries x kHW heads (column j: query j / kHW, head j % kHW)
+template <int kHW>
+struct Layout {
+  static constexpr int kWaves = 4 * kHW;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kQW = 16 / kHW;
+  static constexpr int kCopies = kTile / 1024 / kWaves;  // 1 KiB copies per wave per tile (K or V)
+};
 
 __device__ __forceinline__ bf16x8 as_bf16(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -59,7 +70,7 @@ __device__ __forceinline__ bf16x8 as_bf16(u32x4 v) { return __builtin_bit_cast(b
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // max / sum over the four 16-lane rows of a wave for each lane position l%16
-// (the lanes that hold one query's column), by the gfx950 row-swap moves:
+// (the lanes that hold one column), by the gfx950 row-swap moves:
 // permlane16_swap pairs rows (0,1) and (2,3), permlane32_swap pairs the halves
 __device__ __forceinline__ float rows_max(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -80,114 +91,93 @@ __device__ __forceinline__ uint32_t pack_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, b16x2));
 }
 
-}  // namespace
+// LDS of a walk: the ring first (1 KiB aligned), the union bitmap, the
+// queries' selections (block indices) and counts
+struct WalkLds {
+  uint8_t ring[kStages][kStage];
+  uint32_t bm[SAS_MAX_BLOCKS_DEV / 32];
+  int16_t sel[kBlock][kMaxSel];
+  int cnt[kBlock];
+};
 
-template <bool kGated>
-__global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kStage];
-  __shared__ uint32_t bm[SAS_MAX_BLOCKS_DEV / 32];
-  __shared__ int16_t sel_l[kBlock][kMaxSel];
-  __shared__ float gate_l[kGated ? kBlock : 1][kMaxSel];
-  __shared__ int cnt_l[kBlock];
-
+// The 64 queries' selections into LDS (gates too when gate_l is given) and
+// their union as a bitmap over blocks 0 .. qb; returns the bitmap's words.
+template <int kThreads>
+__device__ __forceinline__ int stage_union(WalkLds &L, float (*gate_l)[kMaxSel], const int32_t *sel,
+                                           const float *gates, const int32_t *cnt, int n_kv_heads, int kvh,
+                                           int max_sel, int t0, int nq, int qb) {
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int g = lane >> 4, j = lane & 15;
-  const int G = p.group;
-  // blockIdx -> (query block, KV head, head group): heaviest query blocks
-  // first, consecutive workgroups on different KV heads
-  const int hg = blockIdx.x % p.head_groups;
-  const int rest = blockIdx.x / p.head_groups;
-  const int kvh = rest % p.n_kv_heads;
-  const int qb = p.n_qblocks - 1 - rest / p.n_kv_heads;
-  const int nh = min(4, G - 4 * hg);  // heads of this workgroup (>= 1)
-  const int T = p.seq_len;
-  const int t0 = qb * kBlock;
-  const int nq = min(kBlock, T - t0);
-  const int qw = wave & 3, hp = wave >> 2;  // query quarter, head pair
-  const int qi = 16 * qw + j;              // this lane's query within the block
-  const int h_lo = 4 * hg + 2 * hp;        // this wave's first query head within the group
-  const bool qvalid = qi < nq;
-  const int tq = t0 + qi;
-
-  // ---- the queries' selections into LDS and their union (blocks 0 .. qb)
   const int nwords = (qb + 32) >> 5;
-  for (int i = tid; i < nwords; i += kThreads) bm[i] = 0;
-  if (tid < kBlock) cnt_l[tid] = tid < nq ? p.cnt[(int64_t)(t0 + tid) * p.n_kv_heads + kvh] : 0;
+  for (int i = tid; i < nwords; i += kThreads) L.bm[i] = 0;
+  if (tid < kBlock) L.cnt[tid] = tid < nq ? cnt[(int64_t)(t0 + tid) * n_kv_heads + kvh] : 0;
   __syncthreads();
-  for (int e = tid; e < nq * p.max_sel; e += kThreads) {
-    const int q = e / p.max_sel, slot = e - q * p.max_sel;
-    if (slot < cnt_l[q]) {
-      const int64_t u = ((int64_t)(t0 + q) * p.n_kv_heads + kvh) * p.max_sel + slot;
-      int c = p.sel[u];
+  for (int e = tid; e < nq * max_sel; e += kThreads) {
+    const int q = e / max_sel, slot = e - q * max_sel;
+    if (slot < L.cnt[q]) {
+      const int64_t u = ((int64_t)(t0 + q) * n_kv_heads + kvh) * max_sel + slot;
+      int c = sel[u];
       c = (unsigned)c <= (unsigned)qb ? c : qb;  // out-of-range entries are not trusted
-      sel_l[q][slot] = (int16_t)c;
-      if (kGated) gate_l[kGated ? q : 0][slot] = p.gates[u];
-      atomicOr(&bm[c >> 5], 1u << (c & 31));
+      L.sel[q][slot] = (int16_t)c;
+      if (gate_l) gate_l[q][slot] = gates[u];
+      atomicOr(&L.bm[c >> 5], 1u << (c & 31));
     }
   }
+  return nwords;
+}
 
-  // B operand of S^T = K Q^T: lane l holds q[query qi][head][32ks + 8(l/16) .. +7]
-  bf16x8 qB[kCt][4];
-#pragma unroll
-  for (int ct = 0; ct < kCt; ++ct) {
-    const bool ok = qvalid && 2 * hp + ct < nh;
-    const uint16_t *qrow =
-        p.q + ((int64_t)(ok ? tq : 0) * p.n_q_heads + kvh * G + (ok ? h_lo + ct : 0)) * kHeadDim + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qB[ct][ks] = as_bf16(ok ? ld16(qrow + 32 * ks) : u32x4{0, 0, 0, 0});
+// The ring's block copies: wave w writes 1 KiB pieces w kCopies .. of the K
+// tile and of the V tile (4 rows each); lane i of a piece lands at byte 16i
+// of it, so it fetches the global 16 bytes that the swizzle puts there.
+// kVLikeK: V stored with K's swizzle (read as an A operand, not transposed).
+template <int kHW, bool kVLikeK>
+struct Ring {
+  static constexpr int kC = Layout<kHW>::kCopies;
+  const char *kbase, *vbase;
+  const __attribute__((address_space(4))) int32_t *btc;  // the block table, read by scalar loads
+  int64_t page_bytes, tok_bytes;
+  uint32_t dst0;
+  int wave;
+
+  __device__ __forceinline__ Ring(const uint16_t *k_pool, const uint16_t *v_pool, const int32_t *block_table,
+                                  int64_t page_stride, int64_t tok_stride, int64_t head_stride, int kvh,
+                                  const uint8_t *ring0, int wave_) {
+    kbase = reinterpret_cast<const char *>(k_pool) + (int64_t)kvh * head_stride * 2;
+    vbase = reinterpret_cast<const char *>(v_pool) + (int64_t)kvh * head_stride * 2;
+    btc = (const __attribute__((address_space(4))) int32_t *)block_table;
+    page_bytes = page_stride * 2;
+    tok_bytes = tok_stride * 2;
+    wave = wave_;
+    dst0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)ring0 + 1024 * kC * wave;
   }
-  wait_vm<0>();  // every compiler-visible load done before the copies start
-  __syncthreads();
-
-  // ---- this lane's walk through its query's ascending selection (LDS)
-  const int cq = cnt_l[qi];
-  int ptr = 0;
-  int nxt_c = cq > 0 ? sel_l[qi][0] : INT_MAX;
-  float nxt_g = kGated ? gate_l[kGated ? qi : 0][0] : 1.f;
-
-  f32x4 o[kCt][8];
-  float m[kCt], ls[kCt];
-#pragma unroll
-  for (int ct = 0; ct < kCt; ++ct) {
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[ct] = -__builtin_inff();
-    ls[ct] = 0.f;
-  }
-
-  // ---- block copies into the ring: wave w writes 1 KiB pieces 2w, 2w+1 of
-  // the K tile and of the V tile (4 rows each); lane i of a piece lands at
-  // byte 16i of it, so it fetches the global 16 bytes that the swizzle puts
-  // there
-  const char *kbase = reinterpret_cast<const char *>(p.k_pool) + (int64_t)kvh * p.head_stride * 2;
-  const char *vbase = reinterpret_cast<const char *>(p.v_pool) + (int64_t)kvh * p.head_stride * 2;
-  const int64_t tok_bytes = p.tok_stride * 2, page_bytes = p.page_stride * 2;
-  int64_t k_src[kCopies / 2], v_src[kCopies / 2];  // per-lane byte offsets inside a block
-#pragma unroll
-  for (int k = 0; k < kCopies / 2; ++k) {
-    const int row = 4 * (2 * wave + k) + (lane >> 4), sl = lane & 15;
-    k_src[k] = row * tok_bytes + 16 * (sl ^ (row & 15));
-    v_src[k] = row * tok_bytes + 32 * ((sl >> 1) ^ (row & 3)) + 16 * (sl & 1);
-  }
-  // the block table is read-only here: read it through the constant address
-  // space so that a uniform index gives a scalar load
-  const __attribute__((address_space(4))) int32_t *btc =
-      (const __attribute__((address_space(4))) int32_t *)p.block_table;
-  const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)&ring[0][0];
-  auto copy_block = [&](int c, int st) {
+  // the per-lane source offsets are recomputed at each copy (a few integer
+  // operations) rather than held in registers across the walk
+  __device__ __forceinline__ void copy(int c, int st) const {
     const int64_t off = (int64_t)btc[c] * page_bytes;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring0 + st * kStage + 2048 * wave);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(dst0 + st * kStage);
+    const int lane = threadIdx.x & 63, sl = lane & 15;
 #pragma unroll
-    for (int k = 0; k < kCopies / 2; ++k) copy16(kbase + off + k_src[k], dst + 1024 * k);
+    for (int k = 0; k < kC; ++k) {
+      const int row = 4 * (kC * wave + k) + (lane >> 4);
+      copy16(kbase + off + row * tok_bytes + 16 * (sl ^ (row & 15)), dst + 1024 * k);
+    }
 #pragma unroll
-    for (int k = 0; k < kCopies / 2; ++k) copy16(vbase + off + v_src[k], dst + kTile + 1024 * k);
-  };
-  // uniform cursor over the bitmap
-  int wi = 0;
-  uint32_t bits = __builtin_amdgcn_readfirstlane(bm[0]);
-  auto next_block = [&]() -> int {
+    for (int k = 0; k < kC; ++k) {
+      const int row = 4 * (kC * wave + k) + (lane >> 4);
+      const int64_t col = kVLikeK ? 16 * (sl ^ (row & 15)) : 32 * ((sl >> 1) ^ (row & 3)) + 16 * (sl & 1);
+      copy16(vbase + off + row * tok_bytes + col, dst + kTile + 1024 * k);
+    }
+  }
+};
+
+// uniform cursor over the union bitmap, ascending
+struct Cursor {
+  const uint32_t *bm;
+  int wi, nwords;
+  uint32_t bits;
+  __device__ __forceinline__ Cursor(const uint32_t *bm_, int nwords_) : bm(bm_), wi(0), nwords(nwords_) {
+    bits = __builtin_amdgcn_readfirstlane(bm[0]);
+  }
+  __device__ __forceinline__ int next() {
     while (bits == 0) {
       if (++wi >= nwords) return -1;
       bits = __builtin_amdgcn_readfirstlane(bm[wi]);
@@ -195,143 +185,247 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
     const int c = (wi << 5) + __builtin_ctz(bits);
     bits &= bits - 1;
     return c;
-  };
+  }
+};
 
-  // prologue: the first three blocks of the walk (a missing one is replaced
-  // by a copy of the first into its unused stage, to keep the copy count fixed)
-  int c0 = next_block();  // never -1: every query selects its own block
-  int c1 = next_block();
-  int c2 = next_block();
-  copy_block(c0, 0);
-  copy_block(c1 >= 0 ? c1 : c0, 1);
-  copy_block(c2 >= 0 ? c2 : c0, 2);
-
-  const int tr_e = (lane & 15) >> 2, tr_q = lane & 3;
+// The walk: the first three blocks copied ahead (a missing one replaced by a
+// copy of the first into its unused stage, to keep the copy count fixed),
+// then per block: wait for its copies (at most the two later stages' copies
+// outstanding), the workgroup barrier (block i-1's stage is free), the copy
+// of block i+3 into that stage, visit(c, stage).  before_visit(c, stage)
+// runs after the barrier (it may write the stage and must end with its own
+// barrier).
+template <int kHW, bool kVLikeK, typename Before, typename Visit>
+__device__ __forceinline__ void walk(const Ring<kHW, kVLikeK> &ring, Cursor &cur, Before before_visit, Visit visit) {
+  constexpr int kC = Layout<kHW>::kCopies;
+  int c0 = cur.next();  // never -1: every query selects its own block
+  int c1 = cur.next();
+  int c2 = cur.next();
+  ring.copy(c0, 0);
+  ring.copy(c1 >= 0 ? c1 : c0, 1);
+  ring.copy(c2 >= 0 ? c2 : c0, 2);
   for (int i = 0;; ++i) {
     const int st = i & (kStages - 1);
     const int c = c0;
-    wait_vm<2 * kCopies>();  // this wave's copies of block i landed (blocks i+1, i+2 may be in flight)
-    lds_barrier();           // ... and every other wave's; block i-1's stage is free
-    if (c * kBlock + kBlock > T) {  // the sequence's last, partial block: zero V rows past the end
-      uint8_t *vt = ring[st] + kTile;
-      for (int b = tid * 16 + (T - c * kBlock) * kRow; b < kTile; b += kThreads * 16)
-        *reinterpret_cast<u32x4 *>(vt + b) = u32x4{0, 0, 0, 0};
-      lds_barrier();
-    }
-    // block i+3 into the stage block i-1 used
-    const int c3 = next_block();
-    copy_block(c3 >= 0 ? c3 : c, (i + 3) & (kStages - 1));
-
-    // ---- attend block c
-    const bool s_l = nxt_c == c;
-    const float g_l = s_l ? nxt_g : 0.f;
-    if (s_l) {
-      ++ptr;
-      nxt_c = ptr < cq ? sel_l[qi][ptr] : INT_MAX;
-      if (kGated) nxt_g = gate_l[kGated ? qi : 0][min(ptr, kMaxSel - 1)];
-    }
-    if (__builtin_amdgcn_ballot_w64(s_l) != 0) {
-      const uint8_t *kt = ring[st];
-      const uint8_t *vt = ring[st] + kTile;
-      f32x4 sacc[kCt][4];  // [head][key tile]
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        u32x4 ka[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          ka[ks] = *reinterpret_cast<const u32x4 *>(kt + (16 * t + j) * kRow + 16 * ((4 * ks + g) ^ j));
-#pragma unroll
-        for (int ct = 0; ct < kCt; ++ct) {
-          sacc[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-            sacc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(ka[ks]), qB[ct][ks], sacc[ct][t], 0, 0, 0);
-        }
-      }
-      const bool causal = c == qb;
-      u32x4 pB[kCt][2];
-#pragma unroll
-      for (int ct = 0; ct < kCt; ++ct) {
-        float z[4][4];
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int tau = 16 * t + 4 * g + r;
-            const bool keep = s_l && (!causal || tau <= qi);
-            z[t][r] = keep ? sacc[ct][t][r] * p.scale_log2 : -__builtin_inff();
-            mx = fmaxf(mx, z[t][r]);
-          }
-        mx = rows_max(mx);
-        const float m_new = fmaxf(m[ct], mx);
-        const bool live = m_new != -__builtin_inff();
-        const float alpha = live ? fast_exp2(m[ct] - m_new) : 1.0f;
-        float psum = 0.f;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          float pv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int t = 2 * s2 + (e >> 2), r = e & 3;
-            const float pe = live ? fast_exp2(z[t][r] - m_new) : 0.f;
-            psum += pe;
-            pv[e] = kGated ? pe * g_l : pe;
-          }
-          pB[ct][s2] = u32x4{pack_rne(pv[0], pv[1]), pack_rne(pv[2], pv[3]), pack_rne(pv[4], pv[5]),
-                             pack_rne(pv[6], pv[7])};
-        }
-        ls[ct] = ls[ct] * alpha + psum;
-        m[ct] = m_new;
-        // the running max rarely moves once a query has seen a few blocks (and
-        // never for a query that did not select this one): rescale only then
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) o[ct][dt] *= alpha;
-        }
-      }
-      // tr-read lane roles: within the 16-lane group g, lane 4e+q4 addresses
-      // row 4g+e (+16 for the upper half of the k-step, +32 per k-step), bytes
-      // 8q4 of the 32-byte pair dt, stored at pair dt ^ e (row % 4 == e)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const uint8_t *vrd = vt + (32 * s2 + 4 * g + tr_e) * kRow + 32 * (dt ^ tr_e) + 8 * tr_q;
-          i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)vrd);
-          i16x4 a1 =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(vrd + 16 * kRow));
-          u32x2 lo2 = __builtin_bit_cast(u32x2, a0), hi2 = __builtin_bit_cast(u32x2, a1);
-          const bf16x8 a = as_bf16(u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
-#pragma unroll
-          for (int ct = 0; ct < kCt; ++ct)
-            o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16(pB[ct][s2]), o[ct][dt], 0, 0, 0);
-        }
-      }
-    }
+    wait_vm<2 * 2 * kC>();  // this wave's copies of block i landed (blocks i+1, i+2 may be in flight)
+    lds_barrier();          // ... and every other wave's; block i-1's stage is free
+    before_visit(c, st);
+    const int c3 = cur.next();
+    ring.copy(c3 >= 0 ? c3 : c, (i + 3) & (kStages - 1));
+    visit(c, st);
     if (c1 < 0) break;  // block i was the walk's last
     c0 = c1;
     c1 = c2;
     c2 = c3;
   }
   wait_vm<0>();  // the trailing filler copies land before the workgroup ends
+}
 
-  // ---- normalise and store: lane holds dims 16dt + 4(l/16) .. +3 of its query
+// The same walk taking the blocks two at a time: one barrier per pair, the
+// next pair's copies (into the stages of the previous pair) in flight while
+// the current pair is visited.  A wave works on a pair's blocks back to back,
+// and the waves that work on only one of the two overlap with those on the
+// other, where the one-block walk makes every wave wait at the barrier after
+// each block.
+template <int kHW, bool kVLikeK, typename Before, typename Visit>
+__device__ __forceinline__ void walk_pairs(const Ring<kHW, kVLikeK> &ring, Cursor &cur, Before before_visit,
+                                           Visit visit) {
+  int a0 = cur.next();  // never -1: every query selects its own block
+  int a1 = cur.next();
+  ring.copy(a0, 0);
+  ring.copy(a1 >= 0 ? a1 : a0, 1);
+  for (int k = 0;; ++k) {
+    const int s0 = (2 * k) & (kStages - 1), s1 = (2 * k + 1) & (kStages - 1);
+    wait_vm<0>();   // this wave's copies of the pair landed (nothing else is in flight)
+    lds_barrier();  // ... and every other wave's; the previous pair's stages are free
+    before_visit(a0, s0);
+    if (a1 >= 0) before_visit(a1, s1);
+    const int b0 = a1 >= 0 ? cur.next() : -1;
+    const int b1 = b0 >= 0 ? cur.next() : -1;
+    ring.copy(b0 >= 0 ? b0 : a0, (2 * k + 2) & (kStages - 1));  // a missing block: a filler copy, fixed count
+    ring.copy(b1 >= 0 ? b1 : a0, (2 * k + 3) & (kStages - 1));
+    visit(a0, s0);
+    if (a1 >= 0) visit(a1, s1);
+    if (b0 < 0) break;  // the pair was the walk's last
+    a0 = b0;
+    a1 = b1;
+  }
+  wait_vm<0>();  // the trailing filler copies land before the workgroup ends
+}
+constexpr bool kWalkPairs = true;
+
+// blockIdx -> (query block, KV head, head group): heaviest query blocks
+// first, consecutive workgroups on different KV heads
+struct Tile {
+  int hg, kvh, qb, t0, nq;
+};
+__device__ __forceinline__ Tile tile_of(int head_groups, int n_kv_heads, int n_qblocks, int seq_len) {
+  Tile w;
+  w.hg = blockIdx.x % head_groups;
+  const int rest = blockIdx.x / head_groups;
+  w.kvh = rest % n_kv_heads;
+  w.qb = n_qblocks - 1 - rest / n_kv_heads;
+  w.t0 = w.qb * kBlock;
+  w.nq = min(kBlock, seq_len - w.t0);
+  return w;
+}
+
+}  // namespace
+
+template <bool kGated, int kHW>
+__global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kernel(PrefillParams p) {
+  using Lay = Layout<kHW>;
+  __shared__ __attribute__((aligned(1024))) WalkLds L;
+  __shared__ float gate_l[kGated ? kBlock : 1][kMaxSel];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4, j = lane & 15;
+  const int G = p.group;
+  const Tile w = tile_of(p.head_groups, p.n_kv_heads, p.n_qblocks, p.seq_len);
+  const int nh = min(kHW, G - kHW * w.hg);  // heads of this workgroup (>= 1)
+  const int qi = Lay::kQW * wave + j / kHW;  // this lane's column: query within the block, and head
+  const int hh = j % kHW;
+  const bool qvalid = qi < w.nq;
+  const bool cvalid = qvalid && hh < nh;
+  const int tq = w.t0 + qi;
+  const int64_t qrow = (int64_t)(cvalid ? tq : 0) * p.n_q_heads + w.kvh * G + (cvalid ? kHW * w.hg + hh : 0);
+
+  const int nwords = stage_union<Lay::kThreads>(L, kGated ? gate_l : nullptr, p.sel, p.gates, p.cnt, p.n_kv_heads,
+                                                w.kvh, p.max_sel, w.t0, w.nq, w.qb);
+
+  // B operand of S^T = K Q^T: lane l holds q[its column][32ks + 8(l/16) .. +7]
+  bf16x8 qB[4];
 #pragma unroll
-  for (int ct = 0; ct < kCt; ++ct) {
-    const float l = rows_sum(ls[ct]);
-    if (qvalid && 2 * hp + ct < nh) {
-      const float inv = 1.0f / l;
-      const int64_t row = (int64_t)tq * p.n_q_heads + kvh * G + h_lo + ct;
-      uint16_t *dst = p.out + row * kHeadDim + 4 * g;
+  for (int ks = 0; ks < 4; ++ks)
+    qB[ks] = as_bf16(cvalid ? ld16(p.q + qrow * kHeadDim + 8 * g + 32 * ks) : u32x4{0, 0, 0, 0});
+  wait_vm<0>();  // every compiler-visible load done before the copies start
+  __syncthreads();
+
+  // ---- this lane's walk through its query's ascending selection (LDS)
+  const int cq = L.cnt[qi];
+  int ptr = 0;
+  int nxt_c = cq > 0 ? L.sel[qi][0] : INT_MAX;
+
+  f32x4 o[8];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const f32x4 v = o[ct][dt] * inv;
-        *reinterpret_cast<u32x2 *>(dst + 16 * dt) = u32x2{pack_rne(v[0], v[1]), pack_rne(v[2], v[3])};
-      }
-      // log-sum-exp of the (ungated) logits, natural log: (m + log2 l) ln 2
-      if (p.lse && g == 0) p.lse[row] = (m[ct] + log2f(l)) * 0.6931471805599453f;
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -__builtin_inff(), ls = 0.f;
+
+  const Ring<kHW, false> ring(p.k_pool, p.v_pool, p.block_table, p.page_stride, p.tok_stride, p.head_stride, w.kvh,
+                              &L.ring[0][0], wave);
+  Cursor cur(L.bm, nwords);
+  const int T = p.seq_len;
+  // transposed V reads: within the 16-lane group g, lane 4e+q4 addresses row
+  // 4g+e (+16 for the upper half of a k-step, +32 per k-step), bytes 8q4 of
+  // the 32-byte pair dt, stored at pair dt ^ e (row % 4 == e).  The pair's low
+  // two bits take the XOR; its high bit, the k-step and the half are
+  // constant offsets, so four per-lane offsets serve all 32 reads.
+  uint32_t tr_off[4];
+  {
+    const int tr_e = (lane & 15) >> 2, tr_q = lane & 3;
+#pragma unroll
+    for (int d3 = 0; d3 < 4; ++d3) tr_off[d3] = (4 * g + tr_e) * kRow + 32 * (d3 ^ tr_e) + 8 * tr_q;
+  }
+  auto before = [&](int c, int st) {
+         if (c * kBlock + kBlock > T) {  // the sequence's last, partial block: zero V rows past the end
+           uint8_t *vt = L.ring[st] + kTile;
+           for (int b = tid * 16 + (T - c * kBlock) * kRow; b < kTile; b += Lay::kThreads * 16)
+             *reinterpret_cast<u32x4 *>(vt + b) = u32x4{0, 0, 0, 0};
+           lds_barrier();
+         }
+       };
+  auto visit = [&](int c, int st) {
+         const bool s_l = nxt_c == c;
+         const float g_l = kGated && s_l ? gate_l[kGated ? qi : 0][ptr] : 0.f;
+         if (s_l) {
+           ++ptr;
+           nxt_c = ptr < cq ? L.sel[qi][ptr] : INT_MAX;
+         }
+         if (__builtin_amdgcn_ballot_w64(s_l) == 0) return;
+         const uint8_t *kt = L.ring[st];
+         const uint8_t *vt = L.ring[st] + kTile;
+         f32x4 sacc[4];  // [key tile]
+#pragma unroll
+         for (int t = 0; t < 4; ++t) {
+           u32x4 ka[4];
+#pragma unroll
+           for (int ks = 0; ks < 4; ++ks)
+             ka[ks] = *reinterpret_cast<const u32x4 *>(kt + (16 * t + j) * kRow + 16 * ((4 * ks + g) ^ j));
+           sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+           for (int ks = 0; ks < 4; ++ks)
+             sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(ka[ks]), qB[ks], sacc[t], 0, 0, 0);
+         }
+         const bool causal = c == w.qb;
+         float z[4][4];
+         float mx = -__builtin_inff();
+#pragma unroll
+         for (int t = 0; t < 4; ++t)
+#pragma unroll
+           for (int r = 0; r < 4; ++r) {
+             const int tau = 16 * t + 4 * g + r;
+             const bool keep = s_l && (!causal || tau <= qi);
+             z[t][r] = keep ? sacc[t][r] * p.scale_log2 : -__builtin_inff();
+             mx = fmaxf(mx, z[t][r]);
+           }
+         mx = rows_max(mx);
+         const float m_new = fmaxf(m, mx);
+         const bool live = m_new != -__builtin_inff();
+         const float alpha = live ? fast_exp2(m - m_new) : 1.0f;
+         float psum = 0.f;
+         u32x4 pB[2];
+#pragma unroll
+         for (int s2 = 0; s2 < 2; ++s2) {
+           float pv[8];
+#pragma unroll
+           for (int e = 0; e < 8; ++e) {
+             const int t = 2 * s2 + (e >> 2), r = e & 3;
+             const float pe = live ? fast_exp2(z[t][r] - m_new) : 0.f;
+             psum += pe;
+             pv[e] = kGated ? pe * g_l : pe;
+           }
+           pB[s2] = u32x4{pack_rne(pv[0], pv[1]), pack_rne(pv[2], pv[3]), pack_rne(pv[4], pv[5]),
+                          pack_rne(pv[6], pv[7])};
+         }
+         ls = ls * alpha + psum;
+         m = m_new;
+         // the running max rarely moves once a query has seen a few blocks (and
+         // never for a query that did not select this one): rescale only then
+         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+           for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+         }
+#pragma unroll
+         for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+           for (int dt = 0; dt < 8; ++dt) {
+             const uint8_t *vrd = vt + tr_off[dt & 3] + 128 * (dt >> 2) + 32 * s2 * kRow;
+             i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)vrd);
+             i16x4 a1 =
+                 __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(vrd + 16 * kRow));
+             u32x2 lo2 = __builtin_bit_cast(u32x2, a0), hi2 = __builtin_bit_cast(u32x2, a1);
+             const bf16x8 a = as_bf16(u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
+             o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16(pB[s2]), o[dt], 0, 0, 0);
+           }
+         }
+       };
+  if (kWalkPairs) walk_pairs(ring, cur, before, visit);
+  else walk(ring, cur, before, visit);
+
+  // ---- normalise and store: lane holds dims 16dt + 4(l/16) .. +3 of its column
+  const float l = rows_sum(ls);
+  if (cvalid) {
+    const float inv = 1.0f / l;
+    uint16_t *dst = p.out + qrow * kHeadDim + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const f32x4 v = o[dt] * inv;
+      *reinterpret_cast<u32x2 *>(dst + 16 * dt) = u32x2{pack_rne(v[0], v[1]), pack_rne(v[2], v[3])};
     }
+    // log-sum-exp of the (ungated) logits, natural log: (m + log2 l) ln 2
+    if (p.lse && g == 0) p.lse[qrow] = (m + log2f(l)) * 0.6931471805599453f;
   }
 }
 
@@ -341,204 +435,142 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_attend_kernel(PrefillPara
 //   dg_i = sum_{h in group} sum_{j in block c_i, j <= t} P_hj <dO_h, v_j>,
 // with P_hj = 2^(z_hj - lse2_h) from the forward's log-sum-exp (the plain
 // softmax over the query's selected tokens; the gates scale the blocks'
-// shares afterwards).  The walk is the forward's: one workgroup per
-// (64-query block, KV head, group of up to 4 query heads), the union of the
-// queries' selections in ascending order, each block's K and V rows copied
-// once into the LDS ring.  Per block, wave w (queries 16(w%4) .., heads
-// 2(w/4), 2(w/4)+1) forms S^T = K Q^T and D^T = V dO^T on MFMA (V is read
-// like K, as the A operand, so it is stored with K's swizzle), then per query
-// the sum over the block's keys and its two heads of P * D, added to the
-// query's slot in LDS.  Exactly two waves (the two head pairs) add to each
-// slot, and a sum of two terms onto zero does not depend on their order, so
-// the result is deterministic.  The groups of 4 heads write separate partial
-// sums, added in order by the chain kernel.
-__global__ __launch_bounds__(kThreads, 1) void prefill_grad_kernel(PrefillBackwardParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kStage];
-  __shared__ uint32_t bm[SAS_MAX_BLOCKS_DEV / 32];
-  __shared__ int16_t sel_l[kBlock][kMaxSel];
+// shares afterwards).  The walk and the wave layout are the forward's; per
+// block a working wave forms S^T = K Q^T and D^T = V dO^T on MFMA (V is read
+// like K, as the A operand, so it is stored with K's swizzle), then per
+// column the sum over the block's keys of P * D, and per query the sum over
+// its kHW head columns, written to the query's slot in LDS (each query's
+// heads are all in one wave: one write per slot).  A group of G > 4 heads
+// spans several workgroups, whose partial sums the chain kernel adds in
+// order.
+template <int kHW>
+__global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_grad_kernel(PrefillBackwardParams p) {
+  using Lay = Layout<kHW>;
+  __shared__ __attribute__((aligned(1024))) WalkLds L;
   __shared__ float dg_l[kBlock][kMaxSel];
-  __shared__ int cnt_l[kBlock];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4, j = lane & 15;
   const int G = p.group;
-  const int hg = blockIdx.x % p.head_groups;
-  const int rest = blockIdx.x / p.head_groups;
-  const int kvh = rest % p.n_kv_heads;
-  const int qb = p.n_qblocks - 1 - rest / p.n_kv_heads;
-  const int nh = min(4, G - 4 * hg);
-  const int T = p.seq_len;
-  const int t0 = qb * kBlock;
-  const int nq = min(kBlock, T - t0);
-  const int qw = wave & 3, hp = wave >> 2;
-  const int qi = 16 * qw + j;
-  const int h_lo = 4 * hg + 2 * hp;
-  const bool qvalid = qi < nq;
-  const int tq = t0 + qi;
+  const Tile w = tile_of(p.head_groups, p.n_kv_heads, p.n_qblocks, p.seq_len);
+  const int nh = min(kHW, G - kHW * w.hg);
+  const int qi = Lay::kQW * wave + j / kHW;
+  const int hh = j % kHW;
+  const bool qvalid = qi < w.nq;
+  const bool cvalid = qvalid && hh < nh;
+  const int tq = w.t0 + qi;
+  const int64_t qrow = (int64_t)(cvalid ? tq : 0) * p.n_q_heads + w.kvh * G + (cvalid ? kHW * w.hg + hh : 0);
 
-  // ---- the queries' selections into LDS and their union; slot sums zeroed
-  const int nwords = (qb + 32) >> 5;
-  for (int i = tid; i < nwords; i += kThreads) bm[i] = 0;
-  for (int e = tid; e < kBlock * kMaxSel; e += kThreads) (&dg_l[0][0])[e] = 0.f;
-  if (tid < kBlock) cnt_l[tid] = tid < nq ? p.cnt[(int64_t)(t0 + tid) * p.n_kv_heads + kvh] : 0;
-  __syncthreads();
-  for (int e = tid; e < nq * p.max_sel; e += kThreads) {
-    const int q = e / p.max_sel, slot = e - q * p.max_sel;
-    if (slot < cnt_l[q]) {
-      int c = p.sel[((int64_t)(t0 + q) * p.n_kv_heads + kvh) * p.max_sel + slot];
-      c = (unsigned)c <= (unsigned)qb ? c : qb;  // out-of-range entries are not trusted
-      sel_l[q][slot] = (int16_t)c;
-      atomicOr(&bm[c >> 5], 1u << (c & 31));
-    }
-  }
+  for (int e = tid; e < kBlock * kMaxSel; e += Lay::kThreads) (&dg_l[0][0])[e] = 0.f;
+  const int nwords = stage_union<Lay::kThreads>(L, nullptr, p.sel, nullptr, p.cnt, p.n_kv_heads, w.kvh, p.max_sel,
+                                                w.t0, w.nq, w.qb);
 
-  // B operands (q and dO of this lane's query, the wave's two heads) and the
-  // forward's log-sum-exp in log2 units
-  bf16x8 qB[kCt][4], dB[kCt][4];
-  float lse2[kCt];
+  // B operands (q and dO of this lane's column) and the forward's
+  // log-sum-exp in log2 units
+  bf16x8 qB[4], dB[4];
 #pragma unroll
-  for (int ct = 0; ct < kCt; ++ct) {
-    const bool ok = qvalid && 2 * hp + ct < nh;
-    const int64_t row = (int64_t)(ok ? tq : 0) * p.n_q_heads + kvh * G + (ok ? h_lo + ct : 0);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      qB[ct][ks] = as_bf16(ok ? ld16(p.q + row * kHeadDim + 8 * g + 32 * ks) : u32x4{0, 0, 0, 0});
-      dB[ct][ks] = as_bf16(ok ? ld16(p.d_out + row * kHeadDim + 8 * g + 32 * ks) : u32x4{0, 0, 0, 0});
-    }
-    lse2[ct] = ok ? p.lse[row] * kLog2e : 0.f;
+  for (int ks = 0; ks < 4; ++ks) {
+    qB[ks] = as_bf16(cvalid ? ld16(p.q + qrow * kHeadDim + 8 * g + 32 * ks) : u32x4{0, 0, 0, 0});
+    dB[ks] = as_bf16(cvalid ? ld16(p.d_out + qrow * kHeadDim + 8 * g + 32 * ks) : u32x4{0, 0, 0, 0});
   }
+  const float lse2 = cvalid ? p.lse[qrow] * kLog2e : 0.f;
   wait_vm<0>();  // every compiler-visible load done before the copies start
   __syncthreads();
 
-  const int cq = cnt_l[qi];
+  const int cq = L.cnt[qi];
   int ptr = 0;
-  int nxt_c = cq > 0 ? sel_l[qi][0] : INT_MAX;
+  int nxt_c = cq > 0 ? L.sel[qi][0] : INT_MAX;
 
-  // ---- block copies into the ring, K and V both with K's swizzle (16-byte
-  // slots by row % 16): wave w writes 1 KiB pieces 2w, 2w+1 of each tile
-  const char *kbase = reinterpret_cast<const char *>(p.k_pool) + (int64_t)kvh * p.head_stride * 2;
-  const char *vbase = reinterpret_cast<const char *>(p.v_pool) + (int64_t)kvh * p.head_stride * 2;
-  const int64_t tok_bytes = p.tok_stride * 2, page_bytes = p.page_stride * 2;
-  int64_t src[kCopies / 2];
+  const Ring<kHW, true> ring(p.k_pool, p.v_pool, p.block_table, p.page_stride, p.tok_stride, p.head_stride, w.kvh,
+                             &L.ring[0][0], wave);
+  Cursor cur(L.bm, nwords);
+  auto visit = [&](int c, int st) {
+         const bool s_l = nxt_c == c;
+         const int slot = ptr;
+         if (s_l) {
+           ++ptr;
+           nxt_c = ptr < cq ? L.sel[qi][ptr] : INT_MAX;
+         }
+         if (__builtin_amdgcn_ballot_w64(s_l) == 0) return;
+         const uint8_t *kt = L.ring[st];
+         const uint8_t *vt = L.ring[st] + kTile;
+         // keys the query may not see (another query's block, later keys of its
+         // own block, rows past the sequence end) are dropped by the select, so
+         // that whatever such rows hold never enters the sum; one key tile at a
+         // time (its scores and products die with it)
+         const bool causal = c == w.qb;
+         float acc = 0.f;
 #pragma unroll
-  for (int k = 0; k < kCopies / 2; ++k) {
-    const int row = 4 * (2 * wave + k) + (lane >> 4), sl = lane & 15;
-    src[k] = row * tok_bytes + 16 * (sl ^ (row & 15));
-  }
-  const __attribute__((address_space(4))) int32_t *btc =
-      (const __attribute__((address_space(4))) int32_t *)p.block_table;
-  const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)&ring[0][0];
-  auto copy_block = [&](int c, int st) {
-    const int64_t off = (int64_t)btc[c] * page_bytes;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring0 + st * kStage + 2048 * wave);
+         for (int t = 0; t < 4; ++t) {
+           u32x4 ka[4], va[4];
 #pragma unroll
-    for (int k = 0; k < kCopies / 2; ++k) copy16(kbase + off + src[k], dst + 1024 * k);
+           for (int ks = 0; ks < 4; ++ks) {
+             const int off = (16 * t + j) * kRow + 16 * ((4 * ks + g) ^ j);
+             ka[ks] = *reinterpret_cast<const u32x4 *>(kt + off);
+             va[ks] = *reinterpret_cast<const u32x4 *>(vt + off);
+           }
+           f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, dacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < kCopies / 2; ++k) copy16(vbase + off + src[k], dst + kTile + 1024 * k);
-  };
-  int wi = 0;
-  uint32_t bits = __builtin_amdgcn_readfirstlane(bm[0]);
-  auto next_block = [&]() -> int {
-    while (bits == 0) {
-      if (++wi >= nwords) return -1;
-      bits = __builtin_amdgcn_readfirstlane(bm[wi]);
-    }
-    const int c = (wi << 5) + __builtin_ctz(bits);
-    bits &= bits - 1;
-    return c;
-  };
-  int c0 = next_block();  // never -1: every query selects its own block
-  int c1 = next_block();
-  int c2 = next_block();
-  copy_block(c0, 0);
-  copy_block(c1 >= 0 ? c1 : c0, 1);
-  copy_block(c2 >= 0 ? c2 : c0, 2);
-
-  for (int i = 0;; ++i) {
-    const int st = i & (kStages - 1);
-    const int c = c0;
-    wait_vm<2 * kCopies>();  // this wave's copies of block i landed
-    lds_barrier();           // ... and every other wave's; block i-1's stage is free
-    const int c3 = next_block();
-    copy_block(c3 >= 0 ? c3 : c, (i + 3) & (kStages - 1));
-
-    const bool s_l = nxt_c == c;
-    const int slot = ptr;
-    if (s_l) {
-      ++ptr;
-      nxt_c = ptr < cq ? sel_l[qi][ptr] : INT_MAX;
-    }
-    if (__builtin_amdgcn_ballot_w64(s_l) != 0) {
-      const uint8_t *kt = ring[st];
-      const uint8_t *vt = ring[st] + kTile;
-      f32x4 sacc[kCt][4], dacc[kCt][4];  // [head][key tile]
+           for (int ks = 0; ks < 4; ++ks) {
+             sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(ka[ks]), qB[ks], sacc, 0, 0, 0);
+             dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(va[ks]), dB[ks], dacc, 0, 0, 0);
+           }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        u32x4 ka[4], va[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int off = (16 * t + j) * kRow + 16 * ((4 * ks + g) ^ j);
-          ka[ks] = *reinterpret_cast<const u32x4 *>(kt + off);
-          va[ks] = *reinterpret_cast<const u32x4 *>(vt + off);
-        }
-#pragma unroll
-        for (int ct = 0; ct < kCt; ++ct) {
-          sacc[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dacc[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            sacc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(ka[ks]), qB[ct][ks], sacc[ct][t], 0, 0, 0);
-            dacc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(va[ks]), dB[ct][ks], dacc[ct][t], 0, 0, 0);
-          }
-        }
-      }
-      // keys the query may not see (another query's block, later keys of its
-      // own block, rows past the sequence end) are dropped by the select, so
-      // that whatever such rows hold never enters the sum
-      const bool causal = c == qb;
-      float acc = 0.f;
-#pragma unroll
-      for (int ct = 0; ct < kCt; ++ct)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int tau = 16 * t + 4 * g + r;
-            const bool keep = s_l && (!causal || tau <= qi);
-            const float pe = fast_exp2(sacc[ct][t][r] * p.scale_log2 - lse2[ct]);
-            acc += keep ? pe * dacc[ct][t][r] : 0.f;
-          }
-      acc = rows_sum(acc);
-      if (s_l && g == 0) atomicAdd(&dg_l[qi][slot], acc);
-    }
-    if (c1 < 0) break;  // block i was the walk's last
-    c0 = c1;
-    c1 = c2;
-    c2 = c3;
-  }
-  wait_vm<0>();  // the trailing filler copies land before the workgroup ends
+           for (int r = 0; r < 4; ++r) {
+             const int tau = 16 * t + 4 * g + r;
+             const bool keep = s_l && (!causal || tau <= qi);
+             const float pe = fast_exp2(sacc[r] * p.scale_log2 - lse2);
+             acc += keep ? pe * dacc[r] : 0.f;
+           }
+         }
+         acc = rows_sum(acc);
+         // the query's kHW head columns are adjacent lanes
+         if (kHW >= 2) acc += __shfl_xor(acc, 1, 64);
+         if (kHW >= 4) acc += __shfl_xor(acc, 2, 64);
+         if (s_l && g == 0 && hh == 0) dg_l[qi][slot] = acc;
+       };
+  if (kWalkPairs) walk_pairs(ring, cur, [&](int, int) {}, visit);
+  else walk(ring, cur, [&](int, int) {}, visit);
   __syncthreads();
-  float *dst = p.ws_dgp + (((int64_t)hg * T + t0) * p.n_kv_heads + kvh) * p.max_sel;
-  for (int e = tid; e < nq * p.max_sel; e += kThreads) {
+  float *dst = p.ws_dgp + (((int64_t)w.hg * p.seq_len + w.t0) * p.n_kv_heads + w.kvh) * p.max_sel;
+  for (int e = tid; e < w.nq * p.max_sel; e += Lay::kThreads) {
     const int q = e / p.max_sel, slot = e - q * p.max_sel;
     dst[(int64_t)q * p.n_kv_heads * p.max_sel + slot] = dg_l[q][slot];
   }
 }
 
-hipError_t launch_prefill_attend(const PrefillParams &p, hipStream_t st) {
+namespace {
+template <int kHW>
+hipError_t launch_attend_hw(PrefillParams p, hipStream_t st) {
+  p.head_groups = (p.group + kHW - 1) / kHW;
   const dim3 grid((unsigned)(p.n_qblocks * p.n_kv_heads * p.head_groups));
   if (p.gates)
-    hipLaunchKernelGGL((prefill_attend_kernel<true>), grid, dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((prefill_attend_kernel<true, kHW>), grid, dim3(Layout<kHW>::kThreads), 0, st, p);
   else
-    hipLaunchKernelGGL((prefill_attend_kernel<false>), grid, dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((prefill_attend_kernel<false, kHW>), grid, dim3(Layout<kHW>::kThreads), 0, st, p);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_prefill_attend(const PrefillParams &p, hipStream_t st) {
+  switch (prefill_heads_per_wave(p.group)) {
+    case 1: return launch_attend_hw<1>(p, st);
+    case 2: return launch_attend_hw<2>(p, st);
+    default: return launch_attend_hw<4>(p, st);
+  }
 }
 
 hipError_t launch_prefill_grad(const PrefillBackwardParams &p, hipStream_t st) {
+  const int hw = prefill_heads_per_wave(p.group);
   const dim3 grid((unsigned)(p.n_qblocks * p.n_kv_heads * p.head_groups));
-  hipLaunchKernelGGL(prefill_grad_kernel, grid, dim3(kThreads), 0, st, p);
+  if (hw == 1)
+    hipLaunchKernelGGL((prefill_grad_kernel<1>), grid, dim3(Layout<1>::kThreads), 0, st, p);
+  else if (hw == 2)
+    hipLaunchKernelGGL((prefill_grad_kernel<2>), grid, dim3(Layout<2>::kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((prefill_grad_kernel<4>), grid, dim3(Layout<4>::kThreads), 0, st, p);
   return hipGetLastError();
 }
 

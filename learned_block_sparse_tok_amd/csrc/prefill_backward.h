@@ -7,6 +7,12 @@ namespace sas {
 
 constexpr int kPrefillSplit = 16;  // row ranges of each long sum over positions, added in order afterwards
 
+// Query heads per MFMA column group of the training-time walks (a wave's 16
+// columns are 16/h queries x h heads), for a group of G query heads; a
+// workgroup covers one group of h heads, so a KV head's G heads take
+// ceil(G / h) workgroups per 64 queries.
+__host__ __device__ inline int prefill_heads_per_wave(int group) { return group >= 3 ? 4 : group; }
+
 struct PrefillBackwardParams {
   const uint16_t *q, *k_pool, *v_pool, *d_out;  // q, d_out [T][Hq][128]
   const uint16_t *gate_keys, *w_q, *w_k;
@@ -17,7 +23,7 @@ struct PrefillBackwardParams {
   float *d_gates;                               // [T][Hkv][max_sel]
   float *d_w_q, *d_w_qnorm, *d_w_k, *d_w_knorm;
   // workspace
-  float *ws_dgp;   // [head_groups][T][Hkv][max_sel]  dL/dg, one term per group of 4 query heads
+  float *ws_dgp;   // [head_groups][T][Hkv][max_sel]  dL/dg, one term per workgroup head group
   float *ws_ghat;  // [Hkv][T][128]                   group-mean gate query of every position
   float *ws_a;     // [Hkv][T][a_cols]                dS / sqrt(128) at each historical block's column, else 0
   float *ws_du_q;  // [T][Hq][128]                    d(pre-norm gate query)

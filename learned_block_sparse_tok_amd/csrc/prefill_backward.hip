@@ -19,7 +19,7 @@
 //
 // Kernels, in launch order:
 //   prefill_grad_kernel (prefill.hip)  dg per (position, KV head, slot), per
-//     group of 4 query heads, from the walk of the forward with the forward's
+//     workgroup head group, from the walk of the forward with the forward's
 //     log-sum-exp.
 //   prefill_pool_stats_kernel  max / min / mean of every block that can be
 //     historical, per KV head (the inputs of the gate-key projection).
