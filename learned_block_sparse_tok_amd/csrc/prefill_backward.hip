@@ -233,19 +233,32 @@ __global__ __launch_bounds__(256) void prefill_chain_kernel(PrefillBackwardParam
 
   // ---- rows of A: columns [0, cols) of the tile's positions (every column a
   // dgk tile reads for these positions), dS / sqrt(128) where the position
-  // selected the block, else 0
+  // selected the block, else 0.  512 columns at a time, through a map in LDS
+  // (the projection buffer, free here) of each (position, column)'s slot.
   {
     const int cols = tau >= 1 ? min(p.a_cols, kBlock * ((tau - 1) / kBlock + 1)) : 0;
-    for (int e = tid; e < nq * cols; e += 256) {
-      const int q = e / cols, c = e - q * cols;
-      const int n = nh_l[q];
-      int lo = 0, hi = n;  // first slot whose block is >= c
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (sel_l[q][mid] < c) lo = mid + 1;
-        else hi = mid;
+    constexpr int kMapCols = 512;
+    static_assert(kBlock * kMapCols <= (int)sizeof(un), "slot map exceeds the projection buffer");
+    int8_t *map = reinterpret_cast<int8_t *>(&un[0][0]);
+    for (int c0 = 0; c0 < cols; c0 += kMapCols) {
+      const int nc = min(kMapCols, cols - c0);
+      __syncthreads();  // earlier reads of the buffer are done
+      for (int e = tid; e < kBlock * kMapCols / 16; e += 256)
+        reinterpret_cast<u32x4 *>(map)[e] = u32x4{~0u, ~0u, ~0u, ~0u};  // slot -1
+      __syncthreads();
+      for (int e = tid; e < kBlock * kMaxSelP; e += 256) {
+        const int q = e / kMaxSelP, i = e - q * kMaxSelP;
+        if (i < nh_l[q]) {
+          const int c = sel_l[q][i] - c0;
+          if ((unsigned)c < (unsigned)nc) map[q * kMapCols + c] = (int8_t)i;
+        }
       }
-      p.ws_a[((int64_t)kvh * T + t0 + q) * p.a_cols + c] = lo < n && sel_l[q][lo] == c ? ds_l[q][lo] : 0.f;
+      __syncthreads();
+      for (int e = tid; e < nq * nc; e += 256) {
+        const int q = e / nc, c = e - q * nc;
+        const int i = map[q * kMapCols + c];
+        p.ws_a[((int64_t)kvh * T + t0 + q) * p.a_cols + c0 + c] = i >= 0 ? ds_l[q][i] : 0.f;
+      }
     }
   }
 
@@ -339,35 +352,35 @@ __global__ __launch_bounds__(256) void prefill_tiles_kernel(PrefillBackwardParam
 }
 
 // the partial tiles added in order: dW_q (Hq*4 blocks), dgk (Hkv*(a_cols/64)*2
-// blocks); the last block sums the query-norm weight terms over the
-// (64 positions, KV head) rows
+// blocks); then 32 blocks for the query-norm weight terms, block b summing
+// dims 4b .. 4b+3 over the (64 positions, KV head) rows: thread t takes rows
+// t, t+256, ..., then a fixed tree over the threads
 __global__ __launch_bounds__(256) void prefill_sums_kernel(PrefillBackwardParams p) {
-  __shared__ float slices[8][kGateDim];
+  __shared__ f32x4 red[256];
   const int k = blockIdx.x, Hq = p.n_q_heads;
   const int n_dgk = p.n_kv_heads * (p.a_cols / 64) * 2;
-  const float *src = p.ws_part + (int64_t)k * kPrefillSplit * 64 * 64;
   if (k < Hq * 4) {
     const int h = k >> 2, jt = (k >> 1) & 1, it = k & 1;
-    sum_tile_parts(src, kPrefillSplit, 64 * 64, p.d_w_q + ((int64_t)h * kGateDim + 64 * jt) * kHeadDim + 64 * it,
-                   kHeadDim);
+    sum_tile_parts(p.ws_part + (int64_t)k * kPrefillSplit * 64 * 64, kPrefillSplit, 64 * 64,
+                   p.d_w_q + ((int64_t)h * kGateDim + 64 * jt) * kHeadDim + 64 * it, kHeadDim);
   } else if (k < Hq * 4 + n_dgk) {
     const int k2 = k - Hq * 4, kvh = k2 % p.n_kv_heads, rest = k2 / p.n_kv_heads;
     const int ct = rest >> 1, jd = rest & 1;
-    sum_tile_parts(src, kPrefillSplit, 64 * 64, p.ws_dgk + ((int64_t)kvh * p.a_cols + 64 * ct) * kGateDim + 64 * jd,
-                   kGateDim);
+    sum_tile_parts(p.ws_part + (int64_t)k * kPrefillSplit * 64 * 64, kPrefillSplit, 64 * 64,
+                   p.ws_dgk + ((int64_t)kvh * p.a_cols + 64 * ct) * kGateDim + 64 * jd, kGateDim);
   } else {
-    const int q = threadIdx.x & 31, sl = threadIdx.x >> 5;
+    const int b = k - Hq * 4 - n_dgk;
     const int rows = p.n_qblocks * p.n_kv_heads;
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    for (int u = sl; u < rows; u += 8) sum += *reinterpret_cast<const f32x4 *>(p.ws_dwqn + (int64_t)u * kGateDim + 4 * q);
-    *reinterpret_cast<f32x4 *>(&slices[sl][4 * q]) = sum;
+    for (int u = threadIdx.x; u < rows; u += 256)
+      sum += *reinterpret_cast<const f32x4 *>(p.ws_dwqn + (int64_t)u * kGateDim + 4 * b);
+    red[threadIdx.x] = sum;
     __syncthreads();
-    if (threadIdx.x < kGateDim) {
-      float a = 0.f;
-#pragma unroll
-      for (int g = 0; g < 8; ++g) a += slices[g][threadIdx.x];
-      p.d_w_qnorm[threadIdx.x] = a;
+    for (int half = 128; half > 0; half >>= 1) {
+      if ((int)threadIdx.x < half) red[threadIdx.x] += red[threadIdx.x + half];
+      __syncthreads();
     }
+    if (threadIdx.x == 0) *reinterpret_cast<f32x4 *>(p.d_w_qnorm + 4 * b) = red[0];
   }
 }
 
@@ -480,7 +493,7 @@ hipError_t launch_prefill_gate_backward(const PrefillBackwardParams &p, hipStrea
   const int tiles = p.n_q_heads * 4 + p.n_kv_heads * (p.a_cols / 64) * 2;
   hipLaunchKernelGGL(prefill_tiles_kernel, dim3((unsigned)(tiles * kPrefillSplit)), dim3(256), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(prefill_sums_kernel, dim3((unsigned)(tiles + 1)), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(prefill_sums_kernel, dim3((unsigned)(tiles + kGateDim / 4)), dim3(256), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.n_hist > 0) {
     hipLaunchKernelGGL(prefill_key_chain_kernel, dim3((unsigned)(p.key_chunks * p.n_kv_heads)), dim3(256), 0, st, p);
