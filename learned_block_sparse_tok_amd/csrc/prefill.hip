@@ -358,22 +358,46 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kerne
            for (int ks = 0; ks < 4; ++ks)
              sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(ka[ks]), qB[ks], sacc[t], 0, 0, 0);
          }
+         // a block before the query's own is whole and visible: the column's
+         // mask is one term added to every exponent (-inf for a query that did
+         // not select the block); the own block (uniform branch) masks per key
          const bool causal = c == w.qb;
-         float z[4][4];
-         float mx = -__builtin_inff();
+         float arg[4][4];  // exponents, relative to the new running max
+         float mx;
+         if (!causal) {
+           float mr = -__builtin_inff();
 #pragma unroll
-         for (int t = 0; t < 4; ++t)
+           for (int t = 0; t < 4; ++t)
 #pragma unroll
-           for (int r = 0; r < 4; ++r) {
-             const int tau = 16 * t + 4 * g + r;
-             const bool keep = s_l && (!causal || tau <= qi);
-             z[t][r] = keep ? sacc[t][r] * p.scale_log2 : -__builtin_inff();
-             mx = fmaxf(mx, z[t][r]);
-           }
+             for (int r = 0; r < 4; ++r) mr = fmaxf(mr, sacc[t][r]);
+           mx = s_l ? mr * p.scale_log2 : -__builtin_inff();
+         } else {
+           mx = -__builtin_inff();
+#pragma unroll
+           for (int t = 0; t < 4; ++t)
+#pragma unroll
+             for (int r = 0; r < 4; ++r) {
+               const bool keep = s_l && 16 * t + 4 * g + r <= qi;
+               arg[t][r] = keep ? sacc[t][r] * p.scale_log2 : -__builtin_inff();
+               mx = fmaxf(mx, arg[t][r]);
+             }
+         }
          mx = rows_max(mx);
          const float m_new = fmaxf(m, mx);
          const bool live = m_new != -__builtin_inff();
          const float alpha = live ? fast_exp2(m - m_new) : 1.0f;
+         if (!causal) {
+           const float nb = s_l && live ? -m_new : -__builtin_inff();
+#pragma unroll
+           for (int t = 0; t < 4; ++t)
+#pragma unroll
+             for (int r = 0; r < 4; ++r) arg[t][r] = fmaf(sacc[t][r], p.scale_log2, nb);
+         } else {
+#pragma unroll
+           for (int t = 0; t < 4; ++t)
+#pragma unroll
+             for (int r = 0; r < 4; ++r) arg[t][r] = live ? arg[t][r] - m_new : -__builtin_inff();
+         }
          float psum = 0.f;
          u32x4 pB[2];
 #pragma unroll
@@ -382,7 +406,7 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kerne
 #pragma unroll
            for (int e = 0; e < 8; ++e) {
              const int t = 2 * s2 + (e >> 2), r = e & 3;
-             const float pe = live ? fast_exp2(z[t][r] - m_new) : 0.f;
+             const float pe = fast_exp2(arg[t][r]);
              psum += pe;
              pv[e] = kGated ? pe * g_l : pe;
            }
@@ -496,10 +520,10 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_grad_kernel(
          if (__builtin_amdgcn_ballot_w64(s_l) == 0) return;
          const uint8_t *kt = L.ring[st];
          const uint8_t *vt = L.ring[st] + kTile;
-         // keys the query may not see (another query's block, later keys of its
-         // own block, rows past the sequence end) are dropped by the select, so
-         // that whatever such rows hold never enters the sum; one key tile at a
-         // time (its scores and products die with it)
+         // keys the query may not see (later keys of its own block, rows past
+         // the sequence end) are dropped by a select on the own block, so that
+         // whatever such rows hold never enters the sum; one key tile at a time
+         // (its scores and products die with it)
          const bool causal = c == w.qb;
          float acc = 0.f;
 #pragma unroll
@@ -517,14 +541,21 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_grad_kernel(
              sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(ka[ks]), qB[ks], sacc, 0, 0, 0);
              dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(va[ks]), dB[ks], dacc, 0, 0, 0);
            }
+           if (!causal) {
 #pragma unroll
-           for (int r = 0; r < 4; ++r) {
-             const int tau = 16 * t + 4 * g + r;
-             const bool keep = s_l && (!causal || tau <= qi);
-             const float pe = fast_exp2(sacc[r] * p.scale_log2 - lse2);
-             acc += keep ? pe * dacc[r] : 0.f;
+             for (int r = 0; r < 4; ++r) acc = fmaf(fast_exp2(fmaf(sacc[r], p.scale_log2, -lse2)), dacc[r], acc);
+           } else {
+#pragma unroll
+             for (int r = 0; r < 4; ++r) {
+               const bool keep = 16 * t + 4 * g + r <= qi;
+               const float pe = fast_exp2(sacc[r] * p.scale_log2 - lse2);
+               acc += keep ? pe * dacc[r] : 0.f;
+             }
            }
          }
+         // a query that did not select the block contributes nothing (the
+         // select also drops whatever its column computed)
+         acc = s_l ? acc : 0.f;
          acc = rows_sum(acc);
          // the query's kHW head columns are adjacent lanes
          if (kHW >= 2) acc += __shfl_xor(acc, 1, 64);
