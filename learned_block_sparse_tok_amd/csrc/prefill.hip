@@ -52,6 +52,7 @@ constexpr int kTile = kBlock * kRow;      // 16 KiB
 constexpr int kStage = 2 * kTile;         // K tile, then V tile
 constexpr int kStages = 4;                // ring: 3 blocks in flight + 1 consumed
 constexpr int kMaxSel = 64;               // selections per query staged in LDS (budgets up to 4,096)
+constexpr float kMaxSlack = 8.f;          // lag of the softmax's reference max behind the true max (log2 units)
 
 // Wave layout for kHW heads per query column group: the wave's 16 MFMA
 // columns are kQW queries x kHW heads (column j: query j / kHW, head j % kHW)
@@ -383,7 +384,11 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kerne
              }
          }
          mx = rows_max(mx);
-         const float m_new = fmaxf(m, mx);
+         // the reference max moves only when a block's max exceeds it by more
+         // than kMaxSlack (log2 units), so the output's rescale is rare: the
+         // weights then reach at most 2^kMaxSlack, exact in fp32 and in bf16's
+         // range, and the normalisation uses the same reference
+         const float m_new = mx > m + kMaxSlack ? mx : m;
          const bool live = m_new != -__builtin_inff();
          const float alpha = live ? fast_exp2(m - m_new) : 1.0f;
          if (!causal) {
