@@ -379,7 +379,49 @@ def run_prefill(args):
         log(f"cpu baseline: {line['cpu_baseline']['value']:.1f} tokens/s on {line['cpu_baseline']['cores']} threads")
     print(json.dumps(line), flush=True)
     if args.backward:
-        print(json.dumps(time_prefill_backward(args, w, gk, bt_row, steps, warm)), flush=True)
+        bline = time_prefill_backward(args, w, gk, bt_row, steps, warm)
+        if not args.no_cpu_baseline:
+            bline["cpu_baseline"] = cpu_baseline_prefill_backward(w, pooled, args.budget, args.cpu_seconds)
+            log(f"cpu baseline (backward): {bline['cpu_baseline']['value']:.1f} tokens/s on "
+                f"{bline['cpu_baseline']['cores']} threads")
+        print(json.dumps(bline), flush=True)
+
+
+def cpu_baseline_prefill_backward(w, gk_o_fn, budget, seconds):
+    """The oracle's gate backward of the training-time forward at a bounded
+    sample of positions (the last ones), on its own selection of them,
+    repeated until `seconds` of host time passed."""
+    import numpy as np
+    import oracle
+    from learned_block_sparse_tok_amd import workloads as wl
+    T = w.batch
+    h_q, h_k, h_v = wl.host(w.q), wl.host(w.k_pool), wl.host(w.v_pool)
+    bt = wl.host(w.block_table[0])
+    gk = gk_o_fn(h_k, bt)
+    pos = np.arange(T - 32, T)
+    w_q, w_qn, w_k, w_kn = wl.host(w.w_q), wl.host(w.w_qnorm), wl.host(w.w_k), wl.host(w.w_knorm)
+    bt_all = np.ascontiguousarray(np.broadcast_to(bt, (len(pos), len(bt))))
+    sel_p, gates_p, cnt_p, _ = oracle.gate_topk(np.ascontiguousarray(h_q[pos]), w_q, w_qn, gk, bt_all,
+                                                (pos + 1).astype(np.int32), w.theta, budget, w.n_kv_heads)
+    n_sel = budget // 64
+    sel = np.full((T, w.n_kv_heads, n_sel), -1, np.int32)
+    gates = np.zeros((T, w.n_kv_heads, n_sel), np.float32)
+    cnt = np.zeros((T, w.n_kv_heads), np.int32)
+    sel[pos], gates[pos], cnt[pos] = sel_p, gates_p, cnt_p
+    import torch
+    d_out = wl.bf16_bits(torch.randn(h_q.shape, generator=torch.Generator().manual_seed(7)).to(torch.bfloat16))
+    n, t_total, reps = 0, 0.0, 0
+    while t_total < seconds or reps == 0:
+        t0 = time.perf_counter()
+        oracle.prefill_gate_backward(h_q, h_k, h_v, bt, w.strides, w.n_kv_heads, sel, gates, cnt,
+                                     1.0 / math.sqrt(128), w_q, w_qn, w_k, w_kn, gk, w.theta, d_out, positions=pos)
+        t_total += time.perf_counter() - t0
+        n += len(pos)
+        reps += 1
+    return dict(value=n / t_total, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"positions {T - 32}..{T - 1} of the {T}-token sequence: the gate backward (gradients of "
+                       f"every gate parameter and of the gates) on the oracle's own selection of those positions, "
+                       f"{reps} repetitions, {t_total:.1f} s; selection and gate keys computed beforehand (untimed)")
 
 
 def time_prefill_backward(args, w, gk, bt_row, steps, warm):
