@@ -107,6 +107,7 @@ PREFILL_BWD_CASES = [
     dict(name="paged_g8_t900_b1024", T=900, Hq=16, Hkv=2, budget=1024, layout="paged", seed=74),
     dict(name="paged_g16_t300", T=300, Hq=16, Hkv=1, budget=192, layout="paged", seed=75),
     dict(name="one_block_t50", T=50, Hq=4, Hkv=1, budget=128, layout="paged", seed=76),
+    dict(name="g2_full_budget_t1100_b4096", T=1100, Hq=4, Hkv=2, budget=4096, layout="contiguous", seed=77),
 ]
 
 
@@ -139,9 +140,9 @@ def gpu_prefill_backward(w, gk, budget, d_out, pf=None):
 @pytest.mark.parametrize("case", PREFILL_BWD_CASES, ids=lambda c: c["name"])
 def test_prefill_gate_backward_parity(case):
     """sas_prefill_gate_backward against oracle.prefill_gate_backward at every
-    position (several 64-position tiles, ragged last tile, groups of 1, 4, 5,
-    8 and 16 query heads, budgets 128 to 1,024, paged and contiguous, a
-    sequence with no historical block).  Each side runs its own forward; the
+    position (several 64-position tiles, ragged last tile, groups of 1, 2, 4,
+    5, 8 and 16 query heads, budgets 128 to 4,096 (the largest selecting every
+    candidate), paged and contiguous, a sequence with no historical block).  Each side runs its own forward; the
     GPU's selection is validated against the oracle's (ties resolved inside
     the band are allowed) and the oracle's backward runs on it, with the
     oracle's own gates of those blocks."""

@@ -142,6 +142,7 @@ PREFILL_CASES = [
     dict(name="paged_g5", T=640, Hq=10, Hkv=2, budget=128, layout="paged"),
     dict(name="paged_g16_tail1", T=577, Hq=16, Hkv=1, budget=320, layout="paged"),
     dict(name="full_budget", T=300, Hq=4, Hkv=1, budget=320, layout="paged"),
+    dict(name="b4096_g2", T=1500, Hq=4, Hkv=2, budget=4096, layout="paged"),
 ]
 
 
@@ -150,7 +151,8 @@ PREFILL_CASES = [
 def test_prefill_parity(case, gated):
     """sas_prefill_select + sas_prefill_attend against the oracle's forward at
     every position (several query blocks, a ragged last block, group sizes 1,
-    4, 5 and 16), with the decode path's tie accounting."""
+    2, 4, 5 and 16, budgets up to 4,096), with the decode path's tie
+    accounting."""
     say("prefill", case["name"], "gated" if gated else "plain")
     w = wl.make_prefill(case["T"], case["Hq"], case["Hkv"], case["budget"], case["layout"], 41, DEV,
                         random_norms=True, extra_pages=2)
