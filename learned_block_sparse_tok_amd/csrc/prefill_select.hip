@@ -8,7 +8,7 @@
 // size 128, Qproj, Q/K normalization, gate RoPE; "Tencent Hunyuan
 // open-sources SAS ...": per-query block selection).  The 64 positions of a
 // block share their candidate set (blocks 0 .. b-1 for block b), so one
-// 256-thread workgroup per (64-position block, KV head) does:
+// 512-thread workgroup (8 waves) per (64-position block, KV head) does:
 //   1. the RoPE table of its 64 positions (angles reduced in fp64);
 //   2. per query head, U^T = W_q[h] . Q^T on v_mfma_f32_16x16x32_bf16 (bf16
 //      products are exact, sums fp32), RMSNorm, * w_qnorm and RoPE on the
@@ -17,7 +17,9 @@
 //   3. the scores S^T = GK . ghat^T / sqrt(128) on MFMA with ghat split into
 //      bf16 high and low parts (about 16 significant bits: the scores keep
 //      fp32-level accuracy), gate keys gathered through the block table;
-//   4. one exact Top-K per position (wave_select), four waves in parallel.
+//   4. one exact Top-K per position (wave_select), eight waves in parallel
+//      (the score keys' 132 KiB of LDS leave room for one workgroup per CU,
+//      and the selections are latency-bound: more waves, more in flight).
 // It replaces 64 per-position gate workgroups, each of which re-read W_q and
 // the candidates' gate keys.
 #include "sas_device.h"
@@ -28,6 +30,8 @@ namespace sas {
 namespace {
 
 constexpr int kPos = 64;                 // positions per workgroup
+constexpr int kWavesSel = 8;             // waves per workgroup
+constexpr int kThreadsSel = 64 * kWavesSel;
 constexpr int kRowWords = kMaxCandBatched + 4;  // LDS row of score keys: 16-byte aligned, staggered banks
 constexpr int kGhatPitch = kGateDim + 4;  // LDS row of the mean gate query (floats)
 
@@ -35,9 +39,9 @@ __device__ __forceinline__ bf16x8 b8(u32x4 v) { return __builtin_bit_cast(bf16x8
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 1) void prefill_select_kernel(PrefillSelectParams p) {
+__global__ __launch_bounds__(kThreadsSel, 1) void prefill_select_kernel(PrefillSelectParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t big[kPos * kRowWords];  // phases 1-2 tables, then score keys
-  __shared__ __attribute__((aligned(16))) uint32_t hist[4][256];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kWavesSel][256];
   __shared__ int32_t bt_l[kMaxCandBatched];
   float *cosv = reinterpret_cast<float *>(big);  // [64 positions][64 frequencies]
   float *sinv = cosv + kPos * 64;
@@ -55,14 +59,14 @@ __global__ __launch_bounds__(256, 1) void prefill_select_kernel(PrefillSelectPar
   const int G = p.group;
 
   // ---- 1. RoPE table, block-table row, zeroed mean gate query
-  for (int e = t; e < kPos * 64; e += 256) {
+  for (int e = t; e < kPos * 64; e += kThreadsSel) {
     float c, s;
     rope_cos_sin((double)(t0 + (e >> 6)), p.inv_freq[e & 63], c, s);
     cosv[e] = c;
     sinv[e] = s;
   }
-  for (int e = t; e < kPos * kGhatPitch; e += 256) ghat[e] = 0.f;
-  for (int c = t; c < nc; c += 256) bt_l[c] = p.block_table[c];
+  for (int e = t; e < kPos * kGhatPitch; e += kThreadsSel) ghat[e] = 0.f;
+  for (int c = t; c < nc; c += kThreadsSel) bt_l[c] = p.block_table[c];
   // this lane's w_qnorm entries: rows 16mt + 4g + r
   float wqn[8][4];
 #pragma unroll
@@ -71,9 +75,9 @@ __global__ __launch_bounds__(256, 1) void prefill_select_kernel(PrefillSelectPar
     for (int r = 0; r < 4; ++r) wqn[mt][r] = p.w_qnorm[16 * mt + 4 * g + r];
   __syncthreads();
 
-  // ---- 2. gate queries, rounds of up to 4 heads (wave w: head 4k + w)
+  // ---- 2. gate queries, rounds of up to kWavesSel heads (wave w: head h0 + w)
   const float inv_g = 1.0f / (float)G;
-  for (int h0 = 0; h0 < G; h0 += 4) {
+  for (int h0 = 0; h0 < G; h0 += kWavesSel) {
     const int h = h0 + wave;
     const bool active = h < G;
     const int head = kvh * G + (active ? h : 0);
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(256, 1) void prefill_select_kernel(PrefillSelectPar
         }
     }
     // add into the mean gate query, one wave at a time (fixed head order)
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kWavesSel; ++w) {
       if (wave == w && active) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(256, 1) void prefill_select_kernel(PrefillSelectPar
   const float inv_sqrt_dg = 0.08838834764831845f;  // 1/sqrt(128)
   const uint16_t *gkh = p.gate_keys + (int64_t)kvh * kGateDim + 8 * g;
   const int64_t page_stride = (int64_t)p.n_kv_heads * kGateDim;
-  for (int ct = wave; 16 * ct < nc; ct += 4) {
+  for (int ct = wave; 16 * ct < nc; ct += kWavesSel) {
     const int c_lane = min(16 * ct + j, nc - 1);  // A operand row: candidate 16ct + l%16
     const uint16_t *krow = gkh + (int64_t)bt_l[c_lane] * page_stride;
     u32x4 a[4];
@@ -194,15 +198,15 @@ __global__ __launch_bounds__(256, 1) void prefill_select_kernel(PrefillSelectPar
     }
   }
   if (p.scores && p.max_blocks > nc)
-    for (int e = t; e < nq * (p.max_blocks - nc); e += 256) {
+    for (int e = t; e < nq * (p.max_blocks - nc); e += kThreadsSel) {
       const int pos = e / (p.max_blocks - nc), c = nc + e % (p.max_blocks - nc);
       p.scores[((int64_t)(t0 + pos) * p.n_kv_heads + kvh) * p.max_blocks + c] = -__builtin_inff();
     }
   lds_barrier();
 
-  // ---- 4. exact Top-K per position (wave w: positions w, w+4, ...)
+  // ---- 4. exact Top-K per position (wave w: positions w, w + kWavesSel, ...)
   const int k_eff = min(p.n_sel - 1, nc);
-  for (int pos = wave; pos < nq; pos += 4) {
+  for (int pos = wave; pos < nq; pos += kWavesSel) {
     const int64_t u = (int64_t)(t0 + pos) * p.n_kv_heads + kvh;
     wave_select(keys + pos * kRowWords, nc, k_eff, p.n_sel, hist[wave], p.sel + u * p.n_sel,
                 p.gates ? p.gates + u * p.n_sel : nullptr, p.cnt + u);
@@ -210,7 +214,7 @@ __global__ __launch_bounds__(256, 1) void prefill_select_kernel(PrefillSelectPar
 }
 
 hipError_t launch_prefill_select(const PrefillSelectParams &p, hipStream_t st) {
-  hipLaunchKernelGGL(prefill_select_kernel, dim3((unsigned)(p.n_qblocks * p.n_kv_heads)), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(prefill_select_kernel, dim3((unsigned)(p.n_qblocks * p.n_kv_heads)), dim3(kThreadsSel), 0, st, p);
   return hipGetLastError();
 }
 
