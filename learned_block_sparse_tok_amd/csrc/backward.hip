@@ -35,6 +35,8 @@
 //     the factor rows staged in LDS; dW_k's
 //     rows are split into ranges whose partial tiles are then added in order
 //     (a fixed order throughout: deterministic).
+#include <type_traits>
+
 #include "backward_common.h"
 #include "sas_kernels.h"
 
@@ -174,14 +176,16 @@ __global__ __launch_bounds__(kWavesG * 64, 1) void gate_grad_kernel(BackwardPara
       dst[2 * kHeadDim + dim] = fs[kk] * (1.0f / kBlock);
     }
   };
-  if (wave < count) {
-    load_k(wave);
-    load_v(wave);
-  }
   float m = -__builtin_inff(), lsum = 0.f;  // this wave's online max / sum of head (column) j
-  for (int i = wave; i < count; i += kWavesG) {
+  // One block of the wave's share; kMore: a later block follows, whose loads
+  // go out here.  Every block but the wave's last runs with kMore, so the
+  // steady-state loop issues its loads unconditionally and the load counters
+  // wait for exactly the block being consumed (a load issued on one branch
+  // only makes the counter wait at the join cover the other branch too,
+  // which held D^T until the next block's K had landed).
+  auto block = [&](int i, auto more) {
+    constexpr bool kMore = decltype(more)::value;
     const int nvalid = nvalid_l[i];
-    const bool more = i + kWavesG < count;
     // S^T = K Q^T and D^T = V dO^T: lane holds rows 16t + 4g + r of column j
     f32x4 sacc[4], dacc[4];
 #pragma unroll
@@ -190,15 +194,16 @@ __global__ __launch_bounds__(kWavesG * 64, 1) void gate_grad_kernel(BackwardPara
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(k[t][ks]), qB[ks], sacc[t], 0, 0, 0);
     }
-    if (i < count - 1) pooled_stats(i);
-    if (more) load_k(i + kWavesG);
+    // every block before the local one (the selection's last) is historical
+    if (kMore || i < count - 1) pooled_stats(i);
+    if (kMore) load_k(i + kWavesG);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       dacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) dacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(v[t][ks]), dB[ks], dacc[t], 0, 0, 0);
     }
-    if (more) load_v(i + kWavesG);
+    if (kMore) load_v(i + kWavesG);
     float z[4][4], mx = -__builtin_inff();
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(kWavesG * 64, 1) void gate_grad_kernel(BackwardPara
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float e = exp2f(z[t][r] - mx);
+        const float e = __builtin_amdgcn_exp2f(z[t][r] - mx);  // z - mx <= 0; 2^-inf = 0
         es += e;
         // rows past the sequence end: e = 0 and their V is not read into the sum
         a += 16 * t + 4 * g + r < nvalid ? e * dacc[t][r] : 0.f;
@@ -230,6 +235,13 @@ __global__ __launch_bounds__(kWavesG * 64, 1) void gate_grad_kernel(BackwardPara
     const float m_new = fmaxf(m, mx);
     lsum = (m == -__builtin_inff() ? 0.f : lsum * exp2f(m - m_new)) + es * exp2f(mx - m_new);
     m = m_new;
+  };
+  if (wave < count) {
+    load_k(wave);
+    load_v(wave);
+    int i = wave;
+    for (; i + kWavesG < count; i += kWavesG) block(i, std::true_type{});
+    block(i, std::false_type{});
   }
   if (g == 0) {
     ml[wave][0][j] = m;
