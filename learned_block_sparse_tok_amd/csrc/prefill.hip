@@ -224,13 +224,16 @@ __device__ __forceinline__ void walk(const Ring<kHW, kVLikeK> &ring, Cursor &cur
 
 // The same walk taking the blocks two at a time: one barrier per pair, the
 // next pair's copies (into the stages of the previous pair) in flight while
-// the current pair is visited.  A wave works on a pair's blocks back to back,
-// and the waves that work on only one of the two overlap with those on the
-// other, where the one-block walk makes every wave wait at the barrier after
-// each block.
-template <int kHW, bool kVLikeK, typename Before, typename Visit>
+// the current pair is visited by visit_pair(c0, stage0, c1, stage1) (c1 = -1
+// for a last, unpaired block: no query selects it).  The waves that work on only one of the
+// two overlap with those on the other, where the one-block walk makes every
+// wave wait at the barrier after each block.  A wave whose queries selected
+// both blocks sets the pair's pace, so visit_pair may interleave the two
+// blocks' work for it (the backward's walk does; the forward's online
+// softmax needs more registers for that than its 16-wave layout leaves).
+template <int kHW, bool kVLikeK, typename Before, typename Visit, typename VisitPair>
 __device__ __forceinline__ void walk_pairs(const Ring<kHW, kVLikeK> &ring, Cursor &cur, Before before_visit,
-                                           Visit visit) {
+                                           Visit visit, VisitPair visit_pair) {
   int a0 = cur.next();  // never -1: every query selects its own block
   int a1 = cur.next();
   ring.copy(a0, 0);
@@ -245,8 +248,7 @@ __device__ __forceinline__ void walk_pairs(const Ring<kHW, kVLikeK> &ring, Curso
     const int b1 = b0 >= 0 ? cur.next() : -1;
     ring.copy(b0 >= 0 ? b0 : a0, (2 * k + 2) & (kStages - 1));  // a missing block: a filler copy, fixed count
     ring.copy(b1 >= 0 ? b1 : a0, (2 * k + 3) & (kStages - 1));
-    visit(a0, s0);
-    if (a1 >= 0) visit(a1, s1);
+    visit_pair(a0, s0, a1, s1);  // a1 = -1: no second block (no query selects it)
     if (b0 < 0) break;  // the pair was the walk's last
     a0 = b0;
     a1 = b1;
@@ -337,110 +339,146 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kerne
            lds_barrier();
          }
        };
+  // whether this lane's query selected block c (the query's selection is
+  // walked in ascending order, as the union is), and the block's gate
+  auto advance = [&](int c, float &g_l) {
+    const bool s_l = nxt_c == c;
+    g_l = kGated && s_l ? gate_l[kGated ? qi : 0][ptr] : 0.f;
+    if (s_l) {
+      ++ptr;
+      nxt_c = ptr < cq ? L.sel[qi][ptr] : INT_MAX;
+    }
+    return s_l;
+  };
+  // S^T = K Q^T for the block in stage st: lane holds keys 16t + 4(l/16) + r
+  // of its column
+  auto scores = [&](int st, f32x4 (&sacc)[4]) {
+    const uint8_t *kt = L.ring[st];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      u32x4 ka[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        ka[ks] = *reinterpret_cast<const u32x4 *>(kt + (16 * t + j) * kRow + 16 * ((4 * ks + g) ^ j));
+      sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(ka[ks]), qB[ks], sacc[t], 0, 0, 0);
+    }
+  };
+  // the weights 2^arg (times the gate) as bf16 pairs in the B-operand layout
+  // of O^T += V^T P^T (k index = the key order of S^T); returns their sum
+  auto weights = [&](const float (&arg)[4][4], float g_l, u32x4 (&pB)[2]) {
+    float psum = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = 2 * s2 + (e >> 2), r = e & 3;
+        const float pe = fast_exp2(arg[t][r]);
+        psum += pe;
+        pv[e] = kGated ? pe * g_l : pe;
+      }
+      pB[s2] = u32x4{pack_rne(pv[0], pv[1]), pack_rne(pv[2], pv[3]), pack_rne(pv[4], pv[5]), pack_rne(pv[6], pv[7])};
+    }
+    return psum;
+  };
+  // the reference max moves only when a block's max exceeds it by more than
+  // kMaxSlack (log2 units), so the output's rescale is rare: the weights
+  // then reach at most 2^kMaxSlack, exact in fp32 and in bf16's range, and
+  // the normalisation uses the same reference.  The running max rarely moves
+  // once a query has seen a few blocks (and never for a query that did not
+  // select the block): rescale only then.
+  auto new_max = [&](float mx, float &alpha) {
+    const float m_new = mx > m + kMaxSlack ? mx : m;
+    alpha = m_new != -__builtin_inff() ? fast_exp2(m - m_new) : 1.0f;
+    return m_new;
+  };
+  auto rescale = [&](float alpha) {
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    }
+  };
+  // O^T += V^T P^T for the block in stage st, V^T by the transposing reads
+  auto accumulate = [&](int st, const u32x4 (&pB)[2]) {
+    const uint8_t *vt = L.ring[st] + kTile;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint8_t *vrd = vt + tr_off[dt & 3] + 128 * (dt >> 2) + 32 * s2 * kRow;
+        i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)vrd);
+        i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(vrd + 16 * kRow));
+        u32x2 lo2 = __builtin_bit_cast(u32x2, a0), hi2 = __builtin_bit_cast(u32x2, a1);
+        const bf16x8 a = as_bf16(u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16(pB[s2]), o[dt], 0, 0, 0);
+      }
+    }
+  };
+  // one block, selected by at least one of the wave's queries
+  auto visit_one = [&](int c, int st, bool s_l, float g_l) {
+    f32x4 sacc[4];
+    scores(st, sacc);
+    // a block before the query's own is whole and visible: the column's
+    // mask is one term added to every exponent (-inf for a query that did
+    // not select the block); the own block (uniform branch) masks per key
+    const bool causal = c == w.qb;
+    float arg[4][4];  // exponents, relative to the new running max
+    float mx;
+    if (!causal) {
+      float mr = -__builtin_inff();
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mr = fmaxf(mr, sacc[t][r]);
+      mx = s_l ? mr * p.scale_log2 : -__builtin_inff();
+    } else {
+      mx = -__builtin_inff();
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool keep = s_l && 16 * t + 4 * g + r <= qi;
+          arg[t][r] = keep ? sacc[t][r] * p.scale_log2 : -__builtin_inff();
+          mx = fmaxf(mx, arg[t][r]);
+        }
+    }
+    float alpha;
+    const float m_new = new_max(rows_max(mx), alpha);
+    const bool live = m_new != -__builtin_inff();
+    if (!causal) {
+      const float nb = s_l && live ? -m_new : -__builtin_inff();
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) arg[t][r] = fmaf(sacc[t][r], p.scale_log2, nb);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) arg[t][r] = live ? arg[t][r] - m_new : -__builtin_inff();
+    }
+    u32x4 pB[2];
+    const float psum = weights(arg, g_l, pB);
+    ls = ls * alpha + psum;
+    m = m_new;
+    rescale(alpha);
+    accumulate(st, pB);
+  };
   auto visit = [&](int c, int st) {
-         const bool s_l = nxt_c == c;
-         const float g_l = kGated && s_l ? gate_l[kGated ? qi : 0][ptr] : 0.f;
-         if (s_l) {
-           ++ptr;
-           nxt_c = ptr < cq ? L.sel[qi][ptr] : INT_MAX;
-         }
-         if (__builtin_amdgcn_ballot_w64(s_l) == 0) return;
-         const uint8_t *kt = L.ring[st];
-         const uint8_t *vt = L.ring[st] + kTile;
-         f32x4 sacc[4];  // [key tile]
-#pragma unroll
-         for (int t = 0; t < 4; ++t) {
-           u32x4 ka[4];
-#pragma unroll
-           for (int ks = 0; ks < 4; ++ks)
-             ka[ks] = *reinterpret_cast<const u32x4 *>(kt + (16 * t + j) * kRow + 16 * ((4 * ks + g) ^ j));
-           sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-           for (int ks = 0; ks < 4; ++ks)
-             sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(ka[ks]), qB[ks], sacc[t], 0, 0, 0);
-         }
-         // a block before the query's own is whole and visible: the column's
-         // mask is one term added to every exponent (-inf for a query that did
-         // not select the block); the own block (uniform branch) masks per key
-         const bool causal = c == w.qb;
-         float arg[4][4];  // exponents, relative to the new running max
-         float mx;
-         if (!causal) {
-           float mr = -__builtin_inff();
-#pragma unroll
-           for (int t = 0; t < 4; ++t)
-#pragma unroll
-             for (int r = 0; r < 4; ++r) mr = fmaxf(mr, sacc[t][r]);
-           mx = s_l ? mr * p.scale_log2 : -__builtin_inff();
-         } else {
-           mx = -__builtin_inff();
-#pragma unroll
-           for (int t = 0; t < 4; ++t)
-#pragma unroll
-             for (int r = 0; r < 4; ++r) {
-               const bool keep = s_l && 16 * t + 4 * g + r <= qi;
-               arg[t][r] = keep ? sacc[t][r] * p.scale_log2 : -__builtin_inff();
-               mx = fmaxf(mx, arg[t][r]);
-             }
-         }
-         mx = rows_max(mx);
-         // the reference max moves only when a block's max exceeds it by more
-         // than kMaxSlack (log2 units), so the output's rescale is rare: the
-         // weights then reach at most 2^kMaxSlack, exact in fp32 and in bf16's
-         // range, and the normalisation uses the same reference
-         const float m_new = mx > m + kMaxSlack ? mx : m;
-         const bool live = m_new != -__builtin_inff();
-         const float alpha = live ? fast_exp2(m - m_new) : 1.0f;
-         if (!causal) {
-           const float nb = s_l && live ? -m_new : -__builtin_inff();
-#pragma unroll
-           for (int t = 0; t < 4; ++t)
-#pragma unroll
-             for (int r = 0; r < 4; ++r) arg[t][r] = fmaf(sacc[t][r], p.scale_log2, nb);
-         } else {
-#pragma unroll
-           for (int t = 0; t < 4; ++t)
-#pragma unroll
-             for (int r = 0; r < 4; ++r) arg[t][r] = live ? arg[t][r] - m_new : -__builtin_inff();
-         }
-         float psum = 0.f;
-         u32x4 pB[2];
-#pragma unroll
-         for (int s2 = 0; s2 < 2; ++s2) {
-           float pv[8];
-#pragma unroll
-           for (int e = 0; e < 8; ++e) {
-             const int t = 2 * s2 + (e >> 2), r = e & 3;
-             const float pe = fast_exp2(arg[t][r]);
-             psum += pe;
-             pv[e] = kGated ? pe * g_l : pe;
-           }
-           pB[s2] = u32x4{pack_rne(pv[0], pv[1]), pack_rne(pv[2], pv[3]), pack_rne(pv[4], pv[5]),
-                          pack_rne(pv[6], pv[7])};
-         }
-         ls = ls * alpha + psum;
-         m = m_new;
-         // the running max rarely moves once a query has seen a few blocks (and
-         // never for a query that did not select this one): rescale only then
-         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-           for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-         }
-#pragma unroll
-         for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-           for (int dt = 0; dt < 8; ++dt) {
-             const uint8_t *vrd = vt + tr_off[dt & 3] + 128 * (dt >> 2) + 32 * s2 * kRow;
-             i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)vrd);
-             i16x4 a1 =
-                 __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(vrd + 16 * kRow));
-             u32x2 lo2 = __builtin_bit_cast(u32x2, a0), hi2 = __builtin_bit_cast(u32x2, a1);
-             const bf16x8 a = as_bf16(u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
-             o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16(pB[s2]), o[dt], 0, 0, 0);
-           }
-         }
-       };
-  if (kWalkPairs) walk_pairs(ring, cur, before, visit);
+    float g_l;
+    const bool s_l = advance(c, g_l);
+    if (__builtin_amdgcn_ballot_w64(s_l) != 0) visit_one(c, st, s_l, g_l);
+  };
+  // the two blocks of a pair in turn (c1 = -1: no second block, which no
+  // query selects)
+  auto visit_pair = [&](int c0, int st0, int c1, int st1) {
+    visit(c0, st0);
+    visit(c1, st1);
+  };
+  if (kWalkPairs) walk_pairs(ring, cur, before, visit, visit_pair);
   else walk(ring, cur, before, visit);
 
   // ---- normalise and store: lane holds dims 16dt + 4(l/16) .. +3 of its column
@@ -515,59 +553,93 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_grad_kernel(
   const Ring<kHW, true> ring(p.k_pool, p.v_pool, p.block_table, p.page_stride, p.tok_stride, p.head_stride, w.kvh,
                              &L.ring[0][0], wave);
   Cursor cur(L.bm, nwords);
+  // whether this lane's query selected block c, and the slot it takes
+  auto advance = [&](int c, int &slot) {
+    const bool s_l = nxt_c == c;
+    slot = ptr;
+    if (s_l) {
+      ++ptr;
+      nxt_c = ptr < cq ? L.sel[qi][ptr] : INT_MAX;
+    }
+    return s_l;
+  };
+  // key tile t of the block in stage st: this lane's sum over its 4 keys of
+  // P * D.  Keys the query may not see (later keys of its own block, rows
+  // past the sequence end) are dropped by a select on the own block, so
+  // that whatever such rows hold never enters the sum.
+  auto tile_sum = [&](int st, int t, bool causal, float acc) {
+    const uint8_t *kt = L.ring[st];
+    const uint8_t *vt = L.ring[st] + kTile;
+    u32x4 ka[4], va[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int off = (16 * t + j) * kRow + 16 * ((4 * ks + g) ^ j);
+      ka[ks] = *reinterpret_cast<const u32x4 *>(kt + off);
+      va[ks] = *reinterpret_cast<const u32x4 *>(vt + off);
+    }
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, dacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(ka[ks]), qB[ks], sacc, 0, 0, 0);
+      dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(va[ks]), dB[ks], dacc, 0, 0, 0);
+    }
+    if (!causal) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc = fmaf(fast_exp2(fmaf(sacc[r], p.scale_log2, -lse2)), dacc[r], acc);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool keep = 16 * t + 4 * g + r <= qi;
+        const float pe = fast_exp2(sacc[r] * p.scale_log2 - lse2);
+        acc += keep ? pe * dacc[r] : 0.f;
+      }
+    }
+    return acc;
+  };
+  // the column sums of one block to the query's slot: a query that did not
+  // select the block contributes nothing (the select also drops whatever
+  // its column computed); the query's kHW head columns are adjacent lanes
+  auto finish = [&](float acc, bool s_l, int slot) {
+    acc = s_l ? acc : 0.f;
+    acc = rows_sum(acc);
+    if (kHW >= 2) acc += __shfl_xor(acc, 1, 64);
+    if (kHW >= 4) acc += __shfl_xor(acc, 2, 64);
+    if (s_l && g == 0 && hh == 0) dg_l[qi][slot] = acc;
+  };
+  auto block_sum = [&](int c, int st) {
+    const bool causal = c == w.qb;
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc = tile_sum(st, t, causal, acc);
+    return acc;
+  };
   auto visit = [&](int c, int st) {
-         const bool s_l = nxt_c == c;
-         const int slot = ptr;
-         if (s_l) {
-           ++ptr;
-           nxt_c = ptr < cq ? L.sel[qi][ptr] : INT_MAX;
-         }
-         if (__builtin_amdgcn_ballot_w64(s_l) == 0) return;
-         const uint8_t *kt = L.ring[st];
-         const uint8_t *vt = L.ring[st] + kTile;
-         // keys the query may not see (later keys of its own block, rows past
-         // the sequence end) are dropped by a select on the own block, so that
-         // whatever such rows hold never enters the sum; one key tile at a time
-         // (its scores and products die with it)
-         const bool causal = c == w.qb;
-         float acc = 0.f;
+    int slot;
+    const bool s_l = advance(c, slot);
+    if (__builtin_amdgcn_ballot_w64(s_l) != 0) finish(block_sum(c, st), s_l, slot);
+  };
+  // two blocks (c0 < c1: only c1 can be a query's own block); a wave with
+  // queries in both whole blocks works on the two key tiles side by side
+  auto visit_pair = [&](int c0, int st0, int c1, int st1) {
+    int slot0, slot1;
+    const bool s0 = advance(c0, slot0);
+    const bool s1 = advance(c1, slot1);
+    const bool any0 = __builtin_amdgcn_ballot_w64(s0) != 0, any1 = __builtin_amdgcn_ballot_w64(s1) != 0;
+    if (!any0 || !any1 || c1 == w.qb) {
+      if (any0) finish(block_sum(c0, st0), s0, slot0);
+      if (any1) finish(block_sum(c1, st1), s1, slot1);
+      return;
+    }
+    float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-         for (int t = 0; t < 4; ++t) {
-           u32x4 ka[4], va[4];
-#pragma unroll
-           for (int ks = 0; ks < 4; ++ks) {
-             const int off = (16 * t + j) * kRow + 16 * ((4 * ks + g) ^ j);
-             ka[ks] = *reinterpret_cast<const u32x4 *>(kt + off);
-             va[ks] = *reinterpret_cast<const u32x4 *>(vt + off);
-           }
-           f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, dacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-           for (int ks = 0; ks < 4; ++ks) {
-             sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(ka[ks]), qB[ks], sacc, 0, 0, 0);
-             dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(va[ks]), dB[ks], dacc, 0, 0, 0);
-           }
-           if (!causal) {
-#pragma unroll
-             for (int r = 0; r < 4; ++r) acc = fmaf(fast_exp2(fmaf(sacc[r], p.scale_log2, -lse2)), dacc[r], acc);
-           } else {
-#pragma unroll
-             for (int r = 0; r < 4; ++r) {
-               const bool keep = 16 * t + 4 * g + r <= qi;
-               const float pe = fast_exp2(sacc[r] * p.scale_log2 - lse2);
-               acc += keep ? pe * dacc[r] : 0.f;
-             }
-           }
-         }
-         // a query that did not select the block contributes nothing (the
-         // select also drops whatever its column computed)
-         acc = s_l ? acc : 0.f;
-         acc = rows_sum(acc);
-         // the query's kHW head columns are adjacent lanes
-         if (kHW >= 2) acc += __shfl_xor(acc, 1, 64);
-         if (kHW >= 4) acc += __shfl_xor(acc, 2, 64);
-         if (s_l && g == 0 && hh == 0) dg_l[qi][slot] = acc;
-       };
-  if (kWalkPairs) walk_pairs(ring, cur, [&](int, int) {}, visit);
+    for (int t = 0; t < 4; ++t) {
+      acc0 = tile_sum(st0, t, false, acc0);
+      acc1 = tile_sum(st1, t, false, acc1);
+    }
+    finish(acc0, s0, slot0);
+    finish(acc1, s1, slot1);
+  };
+  if (kWalkPairs) walk_pairs(ring, cur, [&](int, int) {}, visit, visit_pair);
   else walk(ring, cur, [&](int, int) {}, visit);
   __syncthreads();
   float *dst = p.ws_dgp + (((int64_t)w.hg * p.seq_len + w.t0) * p.n_kv_heads + w.kvh) * p.max_sel;
