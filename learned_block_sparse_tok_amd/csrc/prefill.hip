@@ -339,144 +339,113 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kerne
            lds_barrier();
          }
        };
-  // whether this lane's query selected block c (the query's selection is
-  // walked in ascending order, as the union is), and the block's gate
-  auto advance = [&](int c, float &g_l) {
-    const bool s_l = nxt_c == c;
-    g_l = kGated && s_l ? gate_l[kGated ? qi : 0][ptr] : 0.f;
-    if (s_l) {
-      ++ptr;
-      nxt_c = ptr < cq ? L.sel[qi][ptr] : INT_MAX;
-    }
-    return s_l;
-  };
-  // S^T = K Q^T for the block in stage st: lane holds keys 16t + 4(l/16) + r
-  // of its column
-  auto scores = [&](int st, f32x4 (&sacc)[4]) {
-    const uint8_t *kt = L.ring[st];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      u32x4 ka[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        ka[ks] = *reinterpret_cast<const u32x4 *>(kt + (16 * t + j) * kRow + 16 * ((4 * ks + g) ^ j));
-      sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(ka[ks]), qB[ks], sacc[t], 0, 0, 0);
-    }
-  };
-  // the weights 2^arg (times the gate) as bf16 pairs in the B-operand layout
-  // of O^T += V^T P^T (k index = the key order of S^T); returns their sum
-  auto weights = [&](const float (&arg)[4][4], float g_l, u32x4 (&pB)[2]) {
-    float psum = 0.f;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      float pv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = 2 * s2 + (e >> 2), r = e & 3;
-        const float pe = fast_exp2(arg[t][r]);
-        psum += pe;
-        pv[e] = kGated ? pe * g_l : pe;
-      }
-      pB[s2] = u32x4{pack_rne(pv[0], pv[1]), pack_rne(pv[2], pv[3]), pack_rne(pv[4], pv[5]), pack_rne(pv[6], pv[7])};
-    }
-    return psum;
-  };
-  // the reference max moves only when a block's max exceeds it by more than
-  // kMaxSlack (log2 units), so the output's rescale is rare: the weights
-  // then reach at most 2^kMaxSlack, exact in fp32 and in bf16's range, and
-  // the normalisation uses the same reference.  The running max rarely moves
-  // once a query has seen a few blocks (and never for a query that did not
-  // select the block): rescale only then.
-  auto new_max = [&](float mx, float &alpha) {
-    const float m_new = mx > m + kMaxSlack ? mx : m;
-    alpha = m_new != -__builtin_inff() ? fast_exp2(m - m_new) : 1.0f;
-    return m_new;
-  };
-  auto rescale = [&](float alpha) {
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-    }
-  };
-  // O^T += V^T P^T for the block in stage st, V^T by the transposing reads
-  auto accumulate = [&](int st, const u32x4 (&pB)[2]) {
-    const uint8_t *vt = L.ring[st] + kTile;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const uint8_t *vrd = vt + tr_off[dt & 3] + 128 * (dt >> 2) + 32 * s2 * kRow;
-        i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)vrd);
-        i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(vrd + 16 * kRow));
-        u32x2 lo2 = __builtin_bit_cast(u32x2, a0), hi2 = __builtin_bit_cast(u32x2, a1);
-        const bf16x8 a = as_bf16(u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16(pB[s2]), o[dt], 0, 0, 0);
-      }
-    }
-  };
-  // one block, selected by at least one of the wave's queries
-  auto visit_one = [&](int c, int st, bool s_l, float g_l) {
-    f32x4 sacc[4];
-    scores(st, sacc);
-    // a block before the query's own is whole and visible: the column's
-    // mask is one term added to every exponent (-inf for a query that did
-    // not select the block); the own block (uniform branch) masks per key
-    const bool causal = c == w.qb;
-    float arg[4][4];  // exponents, relative to the new running max
-    float mx;
-    if (!causal) {
-      float mr = -__builtin_inff();
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mr = fmaxf(mr, sacc[t][r]);
-      mx = s_l ? mr * p.scale_log2 : -__builtin_inff();
-    } else {
-      mx = -__builtin_inff();
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool keep = s_l && 16 * t + 4 * g + r <= qi;
-          arg[t][r] = keep ? sacc[t][r] * p.scale_log2 : -__builtin_inff();
-          mx = fmaxf(mx, arg[t][r]);
-        }
-    }
-    float alpha;
-    const float m_new = new_max(rows_max(mx), alpha);
-    const bool live = m_new != -__builtin_inff();
-    if (!causal) {
-      const float nb = s_l && live ? -m_new : -__builtin_inff();
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) arg[t][r] = fmaf(sacc[t][r], p.scale_log2, nb);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) arg[t][r] = live ? arg[t][r] - m_new : -__builtin_inff();
-    }
-    u32x4 pB[2];
-    const float psum = weights(arg, g_l, pB);
-    ls = ls * alpha + psum;
-    m = m_new;
-    rescale(alpha);
-    accumulate(st, pB);
-  };
   auto visit = [&](int c, int st) {
-    float g_l;
-    const bool s_l = advance(c, g_l);
-    if (__builtin_amdgcn_ballot_w64(s_l) != 0) visit_one(c, st, s_l, g_l);
-  };
-  // the two blocks of a pair in turn (c1 = -1: no second block, which no
-  // query selects)
+         const bool s_l = nxt_c == c;
+         const float g_l = kGated && s_l ? gate_l[kGated ? qi : 0][ptr] : 0.f;
+         if (s_l) {
+           ++ptr;
+           nxt_c = ptr < cq ? L.sel[qi][ptr] : INT_MAX;
+         }
+         if (__builtin_amdgcn_ballot_w64(s_l) == 0) return;
+         const uint8_t *kt = L.ring[st];
+         const uint8_t *vt = L.ring[st] + kTile;
+         f32x4 sacc[4];  // [key tile]
+#pragma unroll
+         for (int t = 0; t < 4; ++t) {
+           u32x4 ka[4];
+#pragma unroll
+           for (int ks = 0; ks < 4; ++ks)
+             ka[ks] = *reinterpret_cast<const u32x4 *>(kt + (16 * t + j) * kRow + 16 * ((4 * ks + g) ^ j));
+           sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+           for (int ks = 0; ks < 4; ++ks)
+             sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(ka[ks]), qB[ks], sacc[t], 0, 0, 0);
+         }
+         // a block before the query's own is whole and visible: the column's
+         // mask is one term added to every exponent (-inf for a query that did
+         // not select the block); the own block (uniform branch) masks per key
+         const bool causal = c == w.qb;
+         float arg[4][4];  // exponents, relative to the new running max
+         float mx;
+         if (!causal) {
+           float mr = -__builtin_inff();
+#pragma unroll
+           for (int t = 0; t < 4; ++t)
+#pragma unroll
+             for (int r = 0; r < 4; ++r) mr = fmaxf(mr, sacc[t][r]);
+           mx = s_l ? mr * p.scale_log2 : -__builtin_inff();
+         } else {
+           mx = -__builtin_inff();
+#pragma unroll
+           for (int t = 0; t < 4; ++t)
+#pragma unroll
+             for (int r = 0; r < 4; ++r) {
+               const bool keep = s_l && 16 * t + 4 * g + r <= qi;
+               arg[t][r] = keep ? sacc[t][r] * p.scale_log2 : -__builtin_inff();
+               mx = fmaxf(mx, arg[t][r]);
+             }
+         }
+         mx = rows_max(mx);
+         // the reference max moves only when a block's max exceeds it by more
+         // than kMaxSlack (log2 units), so the output's rescale is rare: the
+         // weights then reach at most 2^kMaxSlack, exact in fp32 and in bf16's
+         // range, and the normalisation uses the same reference
+         const float m_new = mx > m + kMaxSlack ? mx : m;
+         const bool live = m_new != -__builtin_inff();
+         const float alpha = live ? fast_exp2(m - m_new) : 1.0f;
+         if (!causal) {
+           const float nb = s_l && live ? -m_new : -__builtin_inff();
+#pragma unroll
+           for (int t = 0; t < 4; ++t)
+#pragma unroll
+             for (int r = 0; r < 4; ++r) arg[t][r] = fmaf(sacc[t][r], p.scale_log2, nb);
+         } else {
+#pragma unroll
+           for (int t = 0; t < 4; ++t)
+#pragma unroll
+             for (int r = 0; r < 4; ++r) arg[t][r] = live ? arg[t][r] - m_new : -__builtin_inff();
+         }
+         float psum = 0.f;
+         u32x4 pB[2];
+#pragma unroll
+         for (int s2 = 0; s2 < 2; ++s2) {
+           float pv[8];
+#pragma unroll
+           for (int e = 0; e < 8; ++e) {
+             const int t = 2 * s2 + (e >> 2), r = e & 3;
+             const float pe = fast_exp2(arg[t][r]);
+             psum += pe;
+             pv[e] = kGated ? pe * g_l : pe;
+           }
+           pB[s2] = u32x4{pack_rne(pv[0], pv[1]), pack_rne(pv[2], pv[3]), pack_rne(pv[4], pv[5]),
+                          pack_rne(pv[6], pv[7])};
+         }
+         ls = ls * alpha + psum;
+         m = m_new;
+         // the running max rarely moves once a query has seen a few blocks (and
+         // never for a query that did not select this one): rescale only then
+         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+           for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+         }
+#pragma unroll
+         for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+           for (int dt = 0; dt < 8; ++dt) {
+             const uint8_t *vrd = vt + tr_off[dt & 3] + 128 * (dt >> 2) + 32 * s2 * kRow;
+             i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)vrd);
+             i16x4 a1 =
+                 __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(vrd + 16 * kRow));
+             u32x2 lo2 = __builtin_bit_cast(u32x2, a0), hi2 = __builtin_bit_cast(u32x2, a1);
+             const bf16x8 a = as_bf16(u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
+             o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16(pB[s2]), o[dt], 0, 0, 0);
+           }
+         }
+       };
+  // the two blocks of a pair in turn (c1 = -1: no second block)
   auto visit_pair = [&](int c0, int st0, int c1, int st1) {
     visit(c0, st0);
-    visit(c1, st1);
+    if (c1 >= 0) visit(c1, st1);
   };
   if (kWalkPairs) walk_pairs(ring, cur, before, visit, visit_pair);
   else walk(ring, cur, before, visit);
