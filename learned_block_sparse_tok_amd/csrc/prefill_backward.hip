@@ -93,10 +93,16 @@ __global__ __launch_bounds__(256) void prefill_pool_stats_kernel(PrefillBackward
 // reach the thread layout through LDS.
 __global__ __launch_bounds__(256) void prefill_chain_kernel(PrefillBackwardParams p) {
   __shared__ __attribute__((aligned(16))) float un[kBlock][kUnPitch];
-  __shared__ int16_t sel_l[kBlock][kMaxSelP];  // historical blocks of each position, ascending
-  __shared__ int32_t page_l[kBlock][kMaxSelP];
-  __shared__ float ds_l[kBlock][kMaxSelP];     // dS / sqrt(128)
+  // the positions' selections, first; then the query-norm weight terms
+  // (dn * n summed over the heads) of the positions' dims
+  __shared__ __attribute__((aligned(16))) uint8_t slots[kBlock * kMaxSelP * (2 + 4 + 4)];
+  static_assert(sizeof(slots) >= sizeof(float) * kBlock * kUnPitch, "weight terms exceed the selection buffer");
+  auto sel_l = reinterpret_cast<int16_t(*)[kMaxSelP]>(slots);  // historical blocks of each position, ascending
+  auto page_l = reinterpret_cast<int32_t(*)[kMaxSelP]>(slots + kBlock * kMaxSelP * 2);
+  auto ds_l = reinterpret_cast<float(*)[kMaxSelP]>(slots + kBlock * kMaxSelP * 6);  // dS / sqrt(128)
+  auto wsum_l = reinterpret_cast<float(*)[kUnPitch]>(slots);
   __shared__ int nh_l[kBlock];                 // historical blocks per position
+  __shared__ float wqn_l[kGateDim];            // w_qnorm
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int pp = tid >> 2, o = tid & 3;
@@ -109,6 +115,7 @@ __global__ __launch_bounds__(256) void prefill_chain_kernel(PrefillBackwardParam
 
   // ---- dg (the head groups' terms in order), dS, the historical slots
   if (tid < kBlock) nh_l[tid] = tid < nq ? p.cnt[(int64_t)(t0 + tid) * Hkv + kvh] - 1 : 0;
+  if (tid < kGateDim) wqn_l[tid] = p.w_qnorm[tid];
   __syncthreads();
   for (int e = tid; e < nq * S; e += 256) {
     const int q = e / S, i = e - q * S;
@@ -126,15 +133,12 @@ __global__ __launch_bounds__(256) void prefill_chain_kernel(PrefillBackwardParam
     }
   }
 
-  // RoPE at the position for this thread's 16 pairs, the norm weights
-  float cs[16], sn[16], wqa[16], wqb[16];
+  // RoPE at the position for this thread's 16 pairs
+  float cs[16], sn[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int d = 16 * o + e;
-    rope_cos_sin((double)t, p.inv_freq[d], cs[e], sn[e]);
-    wqa[e] = p.w_qnorm[d];
-    wqb[e] = p.w_qnorm[d + 64];
-  }
+  for (int e = 0; e < 16; ++e) rope_cos_sin((double)t, p.inv_freq[16 * o + e], cs[e], sn[e]);
+  // w_qnorm of this thread's dim e (e < 16: 16o + e; else 64 + 16o + e - 16)
+  auto wqn = [&](int e) { return wqn_l[e < 16 ? 16 * o + e : 64 + 16 * o + (e - 16)]; };
 
   // u = W_q[hq] q_t for the 64 positions into un[position][dim]
   auto project = [&](int hq) {
@@ -176,37 +180,6 @@ __global__ __launch_bounds__(256) void prefill_chain_kernel(PrefillBackwardParam
       }
     }
   };
-
-  // ---- the group-mean gate query: per head RMS, normalise, weight, rotate
-  float gh[32];
-#pragma unroll
-  for (int e = 0; e < 32; ++e) gh[e] = 0.f;
-  for (int h = 0; h < G; ++h) {
-    __syncthreads();  // the previous head's reads of un are done
-    project(kvh * G + h);
-    __syncthreads();
-    float x[32], ss = 0.f;
-    read_un(x);
-#pragma unroll
-    for (int e = 0; e < 32; ++e) ss += x[e] * x[e];
-    const float r = sqrtf(quad_sum(ss) * (1.0f / kGateDim) + 1e-6f);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float wa = x[e] / r * wqa[e], wb = x[16 + e] / r * wqb[e];
-      gh[e] += wa * cs[e] - wb * sn[e];
-      gh[16 + e] += wb * cs[e] + wa * sn[e];
-    }
-  }
-  if (valid) {
-    float *dst = p.ws_ghat + ((int64_t)kvh * T + t) * kGateDim;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      *reinterpret_cast<f32x4 *>(dst + 16 * o + 4 * k) =
-          f32x4{gh[4 * k], gh[4 * k + 1], gh[4 * k + 2], gh[4 * k + 3]} * (1.0f / G);
-      *reinterpret_cast<f32x4 *>(dst + 64 + 16 * o + 4 * k) =
-          f32x4{gh[16 + 4 * k], gh[17 + 4 * k], gh[18 + 4 * k], gh[19 + 4 * k]} * (1.0f / G);
-    }
-  }
 
   // ---- dghat = sum_i dS_i gk_{c_i} / sqrt(128) over the position's historical selection
   float dgh[32];
@@ -262,16 +235,20 @@ __global__ __launch_bounds__(256) void prefill_chain_kernel(PrefillBackwardParam
     }
   }
 
-  // ---- query side: d(n w) = RoPE^T(dghat / G), the same for every head of
-  // the group; per head RMSNorm backward to du_q, and dn * n summed over heads
+  // ---- one pass over the group's heads: u = W_q[h] q_t, its RMS r and
+  // n = u / r; the gate query's terms (n * w_qnorm, rotated) summed in head
+  // order into the group mean; and the query side of the backward:
+  // d(n w) = RoPE^T(dghat / G), the same for every head of the group (it
+  // depends on the selection's dS only), RMSNorm backward to du_q, and
+  // dn * n summed over the heads in order
   float dn[32];
 #pragma unroll
   for (int e = 0; e < 16; ++e) rope_back(dgh[e] / (float)G, dgh[16 + e] / (float)G, cs[e], sn[e], dn[e], dn[16 + e]);
-  float wsum[32];
+  float gh[32];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) wsum[e] = 0.f;
+  for (int e = 0; e < 32; ++e) gh[e] = 0.f;
   for (int h = 0; h < G; ++h) {
-    __syncthreads();
+    __syncthreads();  // the previous head's reads of un (and, at h = 0, of the selections) are done
     project(kvh * G + h);
     __syncthreads();
     float x[32], ss = 0.f;
@@ -283,14 +260,25 @@ __global__ __launch_bounds__(256) void prefill_chain_kernel(PrefillBackwardParam
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       x[e] = x[e] / r;
-      dot += dn[e] * (e < 16 ? wqa[e] : wqb[e - 16]) * x[e];
+      dot += dn[e] * wqn(e) * x[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float wa = x[e] * wqn(e), wb = x[16 + e] * wqn(16 + e);
+      gh[e] += wa * cs[e] - wb * sn[e];
+      gh[16 + e] += wb * cs[e] + wa * sn[e];
     }
     const float mean = quad_sum(dot) * (1.0f / kGateDim);
     float du[32];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      du[e] = (dn[e] * (e < 16 ? wqa[e] : wqb[e - 16]) - x[e] * mean) / r;
-      wsum[e] += dn[e] * x[e];
+    for (int e = 0; e < 32; ++e) du[e] = (dn[e] * wqn(e) - x[e] * mean) / r;
+    // this thread's own entries: no other thread touches them
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      f32x4 *ws = reinterpret_cast<f32x4 *>(&wsum_l[pp][(k < 4 ? 0 : 64) + 16 * o + 4 * (k & 3)]);
+      const int e0 = (k < 4 ? 0 : 16) + 4 * (k & 3);
+      const f32x4 term = {dn[e0] * x[e0], dn[e0 + 1] * x[e0 + 1], dn[e0 + 2] * x[e0 + 2], dn[e0 + 3] * x[e0 + 3]};
+      *ws = h == 0 ? term : *ws + term;
     }
     if (valid) {
       float *dst = p.ws_du_q + ((int64_t)t * Hq + kvh * G + h) * kGateDim;
@@ -302,17 +290,22 @@ __global__ __launch_bounds__(256) void prefill_chain_kernel(PrefillBackwardParam
       }
     }
   }
-  // ---- the query-norm weight terms summed over the 64 positions in order
-  __syncthreads();
+  if (valid) {
+    float *dst = p.ws_ghat + ((int64_t)kvh * T + t) * kGateDim;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    un[pp][16 * o + e] = valid ? wsum[e] : 0.f;
-    un[pp][64 + 16 * o + e] = valid ? wsum[16 + e] : 0.f;
+    for (int k = 0; k < 4; ++k) {
+      *reinterpret_cast<f32x4 *>(dst + 16 * o + 4 * k) =
+          f32x4{gh[4 * k], gh[4 * k + 1], gh[4 * k + 2], gh[4 * k + 3]} * (1.0f / G);
+      *reinterpret_cast<f32x4 *>(dst + 64 + 16 * o + 4 * k) =
+          f32x4{gh[16 + 4 * k], gh[17 + 4 * k], gh[18 + 4 * k], gh[19 + 4 * k]} * (1.0f / G);
+    }
   }
+  // ---- the query-norm weight terms summed over the 64 positions in order
+  // (those of positions past the sequence end are zero: q = 0 there)
   __syncthreads();
   if (tid < kGateDim) {
     float a = 0.f;
-    for (int q = 0; q < kBlock; ++q) a += un[q][tid];
+    for (int q = 0; q < nq; ++q) a += wsum_l[q][tid];
     p.ws_dwqn[((int64_t)tau * Hkv + kvh) * kGateDim + tid] = a;
   }
 }
