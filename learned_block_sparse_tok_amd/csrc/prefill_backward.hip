@@ -113,23 +113,53 @@ __global__ __launch_bounds__(256) void prefill_chain_kernel(PrefillBackwardParam
   const int t = t0 + pp;
   const bool valid = pp < nq;
 
-  // ---- dg (the head groups' terms in order), dS, the historical slots
+  // ---- dg (the head groups' terms in order), dS, the historical slots.
+  // Thread t takes the (position, slot) items t + 256k: their dg terms,
+  // blocks and gates are all loaded before the first is used (they do not
+  // depend on the counts), then the blocks' pages, then LDS.
+  constexpr int kItems = kBlock * kMaxSelP / 256;
+  const int n_items = nq * S;
+  const int64_t hg_stride = (int64_t)T * Hkv * S;
+  float dgv[kItems], gv[kItems];
+  int cv[kItems];
+#pragma unroll
+  for (int k = 0; k < kItems; ++k) {
+    const int e = tid + 256 * k;
+    if (e < n_items) {
+      const int q = e / S, i = e - q * S;
+      const int64_t u = ((int64_t)(t0 + q) * Hkv + kvh) * S + i;
+      dgv[k] = p.ws_dgp[u];
+      cv[k] = p.sel[u];
+      gv[k] = p.gates[u];
+    }
+  }
   if (tid < kBlock) nh_l[tid] = tid < nq ? p.cnt[(int64_t)(t0 + tid) * Hkv + kvh] - 1 : 0;
   if (tid < kGateDim) wqn_l[tid] = p.w_qnorm[tid];
   __syncthreads();
-  for (int e = tid; e < nq * S; e += 256) {
-    const int q = e / S, i = e - q * S;
-    const int64_t u = ((int64_t)(t0 + q) * Hkv + kvh) * S + i;
-    float dg = 0.f;
-    for (int hg = 0; hg < p.head_groups; ++hg) dg += p.ws_dgp[(int64_t)hg * T * Hkv * S + u];
-    p.d_gates[u] = dg;
-    if (i < nh_l[q]) {
-      int c = p.sel[u];
-      c = (unsigned)c < (unsigned)tau ? c : 0;  // a historical block precedes the position's own (trusted; clamped)
-      const float g = p.gates[u];
-      sel_l[q][i] = (int16_t)c;
-      page_l[q][i] = p.block_table[c];
-      ds_l[q][i] = dg * g * (1.f - g) * kInvSqrtDg;
+  int pg[kItems];
+#pragma unroll
+  for (int k = 0; k < kItems; ++k) {
+    const int e = tid + 256 * k;
+    if (e < n_items) {
+      const int q = e / S, i = e - q * S;
+      const int64_t u = ((int64_t)(t0 + q) * Hkv + kvh) * S + i;
+      for (int hg = 1; hg < p.head_groups; ++hg) dgv[k] += p.ws_dgp[hg * hg_stride + u];
+      p.d_gates[u] = dgv[k];
+      // a historical block precedes the position's own (trusted; clamped)
+      cv[k] = (unsigned)cv[k] < (unsigned)tau ? cv[k] : 0;
+      if (i < nh_l[q]) pg[k] = p.block_table[cv[k]];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kItems; ++k) {
+    const int e = tid + 256 * k;
+    if (e < n_items) {
+      const int q = e / S, i = e - q * S;
+      if (i < nh_l[q]) {
+        sel_l[q][i] = (int16_t)cv[k];
+        page_l[q][i] = pg[k];
+        ds_l[q][i] = dgv[k] * gv[k] * (1.f - gv[k]) * kInvSqrtDg;
+      }
     }
   }
 
@@ -227,10 +257,18 @@ __global__ __launch_bounds__(256) void prefill_chain_kernel(PrefillBackwardParam
         }
       }
       __syncthreads();
-      for (int e = tid; e < nq * nc; e += 256) {
-        const int q = e / nc, c = e - q * nc;
-        const int i = map[q * kMapCols + c];
-        p.ws_a[((int64_t)kvh * T + t0 + q) * p.a_cols + c0 + c] = i >= 0 ? ds_l[q][i] : 0.f;
+      // four columns per item (nc and the column offsets are multiples of 64)
+      const int nc4 = nc >> 2;
+      for (int e = tid; e < nq * nc4; e += 256) {
+        const int q = e / nc4, c = 4 * (e - q * nc4);
+        const uint32_t m4 = *reinterpret_cast<const uint32_t *>(map + q * kMapCols + c);
+        f32x4 v;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int i = (int8_t)(m4 >> (8 * k));
+          v[k] = i >= 0 ? ds_l[q][i] : 0.f;
+        }
+        *reinterpret_cast<f32x4 *>(p.ws_a + ((int64_t)kvh * T + t0 + q) * p.a_cols + c0 + c) = v;
       }
     }
   }
