@@ -736,7 +736,7 @@ PrefillBackwardWorkspace prefill_backward_workspace(const sas_shape *sh, int32_t
   w.key_chunks = (w.n_hist + sas::kChainBlocks - 1) / sas::kChainBlocks;
   const int hw = sas::prefill_heads_per_wave(sh->n_q_heads / sh->n_kv_heads);
   w.head_groups = (sh->n_q_heads / sh->n_kv_heads + hw - 1) / hw;
-  const size_t tiles = Hq * 4 + Hkv * (size_t)(w.a_cols / 64) * 2;
+  const size_t tiles = Hq + Hkv * (size_t)((w.a_cols + 127) / 128);  // 128 x 128 partial tiles
   w.dgp = 0;
   w.ghat = w.dgp + align256((size_t)w.head_groups * T * Hkv * max_sel * f);
   w.a = w.ghat + align256(Hkv * T * SAS_GATE_DIM * f);
@@ -747,7 +747,7 @@ PrefillBackwardWorkspace prefill_backward_workspace(const sas_shape *sh, int32_t
   w.du_k = w.dgk + align256(Hkv * (size_t)w.a_cols * SAS_GATE_DIM * f);
   w.dwkn = w.du_k + align256(Hkv * (size_t)w.n_hist * SAS_GATE_DIM * f);
   w.part = w.dwkn + align256(Hkv * (size_t)w.key_chunks * SAS_GATE_DIM * f);
-  w.total = w.part + align256(tiles * sas::kPrefillSplit * 64 * 64 * f);
+  w.total = w.part + align256(tiles * sas::kPrefillSplit * 128 * 128 * f);
   return w;
 }
 }  // namespace

@@ -147,6 +147,88 @@ __device__ void outer_sum_tile(FA fa, FB fb, int n_lo, int n_hi, f32x4 (&acc)[2]
   }
 }
 
+// The same sum for a 128 x 128 tile: acc(m, c) = sum over rows n of
+// fa(n, m) * fb(n, c).  Wave w owns rows 64(w/2) .. +63 and columns
+// 64(w%2) .. +63 (4 x 4 MFMA tiles: 48 MFMAs per 32 rows, four times the
+// 64 x 64 tile's MFMAs for each LDS round).  kExactB: fb's values are bf16
+// (their low parts are zero), so the high(a) x low(b) products are skipped.
+struct OuterLds128 {
+  uint16_t ah[128][kOsPitch], al[128][kOsPitch], bh[128][kOsPitch], bl[128][kOsPitch];
+};
+
+template <bool kExactB, typename FA, typename FB>
+__device__ void outer_sum_tile128(FA fa, FB fb, int n_lo, int n_hi, f32x4 (&acc)[4][4], OuterLds128 &ls) {
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int wm = wave >> 1, wn = wave & 1, g = lane >> 4, c16 = lane & 15;
+  const int col = t & 127, rg = t >> 7;  // fetch: column, group of 16 rows
+  float ra[16], rb[16];
+  auto fetch = [&](int n0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int n = n0 + 16 * rg + e;
+      ra[e] = n < n_hi ? fa(n, col) : 0.f;
+      rb[e] = n < n_hi ? fb(n, col) : 0.f;
+    }
+  };
+  auto split = [&](const float (&x)[16], uint16_t *hi, uint16_t *lo, bool low_parts) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 hv, lv;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float x0 = x[8 * h + 2 * q], x1 = x[8 * h + 2 * q + 1];
+        const uint32_t hp = pack_bf16_rne(x0, x1);
+        hv[q] = hp;
+        lv[q] = low_parts ? pack_bf16_rne(x0 - bf16_lo(hp), x1 - bf16_hi(hp)) : 0u;
+      }
+      *reinterpret_cast<u32x4 *>(hi + 8 * h) = hv;
+      if (low_parts) *reinterpret_cast<u32x4 *>(lo + 8 * h) = lv;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (n_lo < n_hi) fetch(n_lo);
+  for (int n0 = n_lo; n0 < n_hi; n0 += 32) {
+    lds_barrier();
+    split(ra, &ls.ah[col][16 * rg], &ls.al[col][16 * rg], true);
+    split(rb, &ls.bh[col][16 * rg], &ls.bl[col][16 * rg], !kExactB);
+    lds_barrier();
+    if (n0 + 32 < n_hi) fetch(n0 + 32);
+    bf16x8 ah[4], al[4], bh[4], bl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ah[i] = to_bf16x8(*reinterpret_cast<const u32x4 *>(&ls.ah[64 * wm + 16 * i + c16][8 * g]));
+      al[i] = to_bf16x8(*reinterpret_cast<const u32x4 *>(&ls.al[64 * wm + 16 * i + c16][8 * g]));
+      bh[i] = to_bf16x8(*reinterpret_cast<const u32x4 *>(&ls.bh[64 * wn + 16 * i + c16][8 * g]));
+      if (!kExactB) bl[i] = to_bf16x8(*reinterpret_cast<const u32x4 *>(&ls.bl[64 * wn + 16 * i + c16][8 * g]));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+        if (!kExactB) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bl[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bh[j], acc[i][j], 0, 0, 0);
+      }
+  }
+}
+
+// writes a tile from outer_sum_tile128 to a dense 128 x 128 buffer: lane l
+// of wave w holds rows 64(w/2) + 16i + 4(l/16) + r, column 64(w%2) + 16j + l%16
+__device__ __forceinline__ void store_tile128(const f32x4 (&acc)[4][4], float *dst) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        dst[(64 * wm + 16 * i + 4 * (lane >> 4) + r) * 128 + 64 * wn + 16 * j + (lane & 15)] = acc[i][j][r];
+}
+
 // writes a tile from outer_sum_tile: lane l of wave w holds rows
 // 32(w/2) + 16i + 4(l/16) + r, column 32(w%2) + 16j + l%16
 __device__ __forceinline__ void store_tile(const f32x4 (&acc)[2][2], float *dst, int64_t row_stride) {

@@ -29,7 +29,7 @@
 //     query-norm weight terms, and the rows of the dense matrix A (position x
 //     block, dS / sqrt(128) where the position selected the block) through
 //     which dgk becomes a plain contraction: dgk = A^T ghat.
-//   prefill_tiles_kernel  64 x 64 tiles of dW_q = sum_t du_q (x) q and of
+//   prefill_tiles_kernel  128 x 128 tiles of dW_q = sum_t du_q (x) q and of
 //     dgk = A^T ghat as partial sums over kPrefillSplit ranges of positions
 //     (A is lower-triangular by blocks: a column tile of blocks starts at the
 //     first position that can select it).
@@ -349,58 +349,71 @@ __global__ __launch_bounds__(256) void prefill_chain_kernel(PrefillBackwardParam
 }
 
 // ---------------------------------------------------------------- long sums over positions: partial tiles
-// blocks [0, Hq*4*kPrefillSplit): dW_q[h] tile (jt, it) over one of
-// kPrefillSplit ranges of positions, sum of du_q (x) q; then
-// Hkv*(a_cols/64)*2*kPrefillSplit blocks: dgk tiles (64 blocks x 64 dims) of
-// A^T ghat over one range of the positions that can select the tile's blocks.
+// blocks [0, Hq*kPrefillSplit): dW_q[h] (128 x 128) over one of
+// kPrefillSplit ranges of positions, the sum of du_q (x) q (q is bf16: no
+// low parts on that side); then Hkv*ceil(a_cols/128)*kPrefillSplit blocks:
+// dgk tiles (128 blocks x 128 dims) of A^T ghat over one range of the
+// positions that can select the tile's blocks.  A is taken as zero for a
+// block at or after a position's own, which the position cannot select.
 __global__ __launch_bounds__(256) void prefill_tiles_kernel(PrefillBackwardParams p) {
-  __shared__ __attribute__((aligned(16))) OuterLds ls;
+  __shared__ __attribute__((aligned(16))) OuterLds128 ls;
   const int k = blockIdx.x / kPrefillSplit, part = blockIdx.x % kPrefillSplit;
   const int Hq = p.n_q_heads, T = p.seq_len;
-  f32x4 acc[2][2];
+  f32x4 acc[4][4];
   auto range = [&](int n0, int n) {  // part's share of rows [n0, n)
     const int len = max(0, n - n0), per = (len + kPrefillSplit - 1) / kPrefillSplit;
     return make_int2(n0 + min(len, part * per), n0 + min(len, part * per + per));
   };
-  if (k < Hq * 4) {
-    const int h = k >> 2, jt = (k >> 1) & 1, it = k & 1;
+  if (k < Hq) {
     const int64_t rs = (int64_t)Hq * kHeadDim;
-    const float *a = p.ws_du_q + (int64_t)h * kGateDim + 64 * jt;
-    const uint16_t *b = p.q + (int64_t)h * kHeadDim + 64 * it;
+    const float *a = p.ws_du_q + (int64_t)k * kGateDim;
+    const uint16_t *b = p.q + (int64_t)k * kHeadDim;
     const int2 r = range(0, T);
-    outer_sum_tile([&](int n, int c) { return a[n * rs + c]; }, [&](int n, int c) { return bf16_to_f32(b[n * rs + c]); },
-                   r.x, r.y, acc, ls);
+    outer_sum_tile128<true>([&](int n, int c) { return a[n * rs + c]; },
+                            [&](int n, int c) { return bf16_to_f32(b[n * rs + c]); }, r.x, r.y, acc, ls);
   } else {
-    const int k2 = k - Hq * 4, kvh = k2 % p.n_kv_heads, rest = k2 / p.n_kv_heads;
-    const int ct = rest >> 1, jd = rest & 1;
-    const float *a = p.ws_a + (int64_t)kvh * T * p.a_cols + 64 * ct;
-    const float *b = p.ws_ghat + (int64_t)kvh * T * kGateDim + 64 * jd;
-    const int2 r = range(min(T, kBlock * (kBlock * ct + 1)), T);
-    outer_sum_tile([&](int n, int c) { return a[(int64_t)n * p.a_cols + c]; },
-                   [&](int n, int c) { return b[(int64_t)n * kGateDim + c]; }, r.x, r.y, acc, ls);
+    const int k2 = k - Hq, kvh = k2 % p.n_kv_heads, c0 = 128 * (k2 / p.n_kv_heads);
+    const float *a = p.ws_a + (int64_t)kvh * T * p.a_cols + c0;
+    const float *b = p.ws_ghat + (int64_t)kvh * T * kGateDim;
+    const int2 r = range(min(T, kBlock * (c0 + 1)), T);
+    outer_sum_tile128<false>([&](int n, int c) { return c0 + c < (n >> 6) ? a[(int64_t)n * p.a_cols + c] : 0.f; },
+                             [&](int n, int c) { return b[(int64_t)n * kGateDim + c]; }, r.x, r.y, acc, ls);
   }
-  store_tile(acc, p.ws_part + ((int64_t)k * kPrefillSplit + part) * 64 * 64, 64);
+  store_tile128(acc, p.ws_part + ((int64_t)k * kPrefillSplit + part) * 128 * 128);
 }
 
-// the partial tiles added in order: dW_q (Hq*4 blocks), dgk (Hkv*(a_cols/64)*2
-// blocks); then 32 blocks for the query-norm weight terms, block b summing
+// the partial tiles added in order, a quarter tile (32 rows) per block:
+// dW_q (Hq*4 blocks), dgk (Hkv*ceil(a_cols/128)*4 blocks, rows past a_cols
+// dropped); then 32 blocks for the query-norm weight terms, block b summing
 // dims 4b .. 4b+3 over the (64 positions, KV head) rows: thread t takes rows
 // t, t+256, ..., then a fixed tree over the threads
 __global__ __launch_bounds__(256) void prefill_sums_kernel(PrefillBackwardParams p) {
   __shared__ f32x4 red[256];
-  const int k = blockIdx.x, Hq = p.n_q_heads;
-  const int n_dgk = p.n_kv_heads * (p.a_cols / 64) * 2;
-  if (k < Hq * 4) {
-    const int h = k >> 2, jt = (k >> 1) & 1, it = k & 1;
-    sum_tile_parts(p.ws_part + (int64_t)k * kPrefillSplit * 64 * 64, kPrefillSplit, 64 * 64,
-                   p.d_w_q + ((int64_t)h * kGateDim + 64 * jt) * kHeadDim + 64 * it, kHeadDim);
-  } else if (k < Hq * 4 + n_dgk) {
-    const int k2 = k - Hq * 4, kvh = k2 % p.n_kv_heads, rest = k2 / p.n_kv_heads;
-    const int ct = rest >> 1, jd = rest & 1;
-    sum_tile_parts(p.ws_part + (int64_t)k * kPrefillSplit * 64 * 64, kPrefillSplit, 64 * 64,
-                   p.ws_dgk + ((int64_t)kvh * p.a_cols + 64 * ct) * kGateDim + 64 * jd, kGateDim);
+  const int Hq = p.n_q_heads;
+  const int n_tiles = Hq + p.n_kv_heads * ((p.a_cols + 127) / 128);
+  const int k = blockIdx.x >> 2, quarter = blockIdx.x & 3;
+  if (k < n_tiles) {
+    const float *src = p.ws_part + (int64_t)k * kPrefillSplit * 128 * 128;
+    float *dst;
+    int rows = 128;
+    if (k < Hq) {
+      dst = p.d_w_q + (int64_t)k * kGateDim * kHeadDim;
+    } else {
+      const int k2 = k - Hq, kvh = k2 % p.n_kv_heads, c0 = 128 * (k2 / p.n_kv_heads);
+      dst = p.ws_dgk + ((int64_t)kvh * p.a_cols + c0) * kGateDim;
+      rows = min(128, p.a_cols - c0);
+    }
+    // thread t owns elements 4(t + 256q) .. +3 of the quarter's 32 x 128
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 32 * 128 * quarter + 4 * (threadIdx.x + 256 * q);
+      if ((e >> 7) >= rows) continue;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int part = 0; part < kPrefillSplit; ++part) acc += *reinterpret_cast<const f32x4 *>(src + part * 128 * 128 + e);
+      *reinterpret_cast<f32x4 *>(dst + e) = acc;
+    }
   } else {
-    const int b = k - Hq * 4 - n_dgk;
+    const int b = blockIdx.x - 4 * n_tiles;
     const int rows = p.n_qblocks * p.n_kv_heads;
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
     for (int u = threadIdx.x; u < rows; u += 256)
@@ -521,10 +534,10 @@ hipError_t launch_prefill_gate_backward(const PrefillBackwardParams &p, hipStrea
   }
   hipLaunchKernelGGL(prefill_chain_kernel, dim3((unsigned)(p.n_qblocks * p.n_kv_heads)), dim3(256), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int tiles = p.n_q_heads * 4 + p.n_kv_heads * (p.a_cols / 64) * 2;
+  const int tiles = p.n_q_heads + p.n_kv_heads * ((p.a_cols + 127) / 128);
   hipLaunchKernelGGL(prefill_tiles_kernel, dim3((unsigned)(tiles * kPrefillSplit)), dim3(256), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(prefill_sums_kernel, dim3((unsigned)(tiles + kGateDim / 4)), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(prefill_sums_kernel, dim3((unsigned)(4 * tiles + kGateDim / 4)), dim3(256), 0, st, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.n_hist > 0) {
     hipLaunchKernelGGL(prefill_key_chain_kernel, dim3((unsigned)(p.key_chunks * p.n_kv_heads)), dim3(256), 0, st, p);
