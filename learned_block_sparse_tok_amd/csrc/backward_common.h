@@ -148,41 +148,42 @@ __device__ void outer_sum_tile(FA fa, FB fb, int n_lo, int n_hi, f32x4 (&acc)[2]
 }
 
 // The same sum for a 128 x 128 tile: acc(m, c) = sum over rows n of
-// fa(n, m) * fb(n, c).  Wave w owns rows 64(w/2) .. +63 and columns
-// 64(w%2) .. +63 (4 x 4 MFMA tiles: 48 MFMAs per 32 rows, four times the
-// 64 x 64 tile's MFMAs for each LDS round).  kExactB: fb's values are bf16
-// (their low parts are zero), so the high(a) x low(b) products are skipped.
+// fa4(n, m)[k] * fb4(n, c)[k'] for the columns m + k, c + k' (fa4 / fb4 give
+// four adjacent columns, m and c multiples of 4).  Wave w owns rows
+// 64(w/2) .. +63 and columns 64(w%2) .. +63 (4 x 4 MFMA tiles: 48 MFMAs per
+// 32 rows, four times the 64 x 64 tile's MFMAs for each LDS round); thread
+// t fetches rows 4(t/32) .. +3 of the 32 and columns 4(t%32) .. +3.
+// kExactB: fb's values are bf16 (their low parts are zero), so the
+// high(a) x low(b) products are skipped.
 struct OuterLds128 {
   uint16_t ah[128][kOsPitch], al[128][kOsPitch], bh[128][kOsPitch], bl[128][kOsPitch];
 };
 
-template <bool kExactB, typename FA, typename FB>
-__device__ void outer_sum_tile128(FA fa, FB fb, int n_lo, int n_hi, f32x4 (&acc)[4][4], OuterLds128 &ls) {
+template <bool kExactB, typename FA4, typename FB4>
+__device__ void outer_sum_tile128(FA4 fa4, FB4 fb4, int n_lo, int n_hi, f32x4 (&acc)[4][4], OuterLds128 &ls) {
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 4, c16 = lane & 15;
-  const int col = t & 127, rg = t >> 7;  // fetch: column, group of 16 rows
-  float ra[16], rb[16];
+  const int c4 = 4 * (t & 31), rg = t >> 5;
+  f32x4 ra[4], rb[4];
   auto fetch = [&](int n0) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int n = n0 + 16 * rg + e;
-      ra[e] = n < n_hi ? fa(n, col) : 0.f;
-      rb[e] = n < n_hi ? fb(n, col) : 0.f;
+    for (int r = 0; r < 4; ++r) {
+      const int n = n0 + 4 * rg + r;
+      ra[r] = n < n_hi ? fa4(n, c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      rb[r] = n < n_hi ? fb4(n, c4) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
-  auto split = [&](const float (&x)[16], uint16_t *hi, uint16_t *lo, bool low_parts) {
+  // column c4 + k, rows 4rg .. +3: bf16 high parts and (if wanted) the
+  // bf16 rounding of what they leave
+  auto split = [&](const f32x4 (&x)[4], uint16_t (*hi)[kOsPitch], uint16_t (*lo)[kOsPitch], bool low_parts) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4 hv, lv;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float x0 = x[8 * h + 2 * q], x1 = x[8 * h + 2 * q + 1];
-        const uint32_t hp = pack_bf16_rne(x0, x1);
-        hv[q] = hp;
-        lv[q] = low_parts ? pack_bf16_rne(x0 - bf16_lo(hp), x1 - bf16_hi(hp)) : 0u;
-      }
-      *reinterpret_cast<u32x4 *>(hi + 8 * h) = hv;
-      if (low_parts) *reinterpret_cast<u32x4 *>(lo + 8 * h) = lv;
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t h0 = pack_bf16_rne(x[0][k], x[1][k]), h1 = pack_bf16_rne(x[2][k], x[3][k]);
+      *reinterpret_cast<u32x2 *>(&hi[c4 + k][4 * rg]) = u32x2{h0, h1};
+      if (low_parts)
+        *reinterpret_cast<u32x2 *>(&lo[c4 + k][4 * rg]) =
+            u32x2{pack_bf16_rne(x[0][k] - bf16_lo(h0), x[1][k] - bf16_hi(h0)),
+                  pack_bf16_rne(x[2][k] - bf16_lo(h1), x[3][k] - bf16_hi(h1))};
     }
   };
 #pragma unroll
@@ -192,8 +193,8 @@ __device__ void outer_sum_tile128(FA fa, FB fb, int n_lo, int n_hi, f32x4 (&acc)
   if (n_lo < n_hi) fetch(n_lo);
   for (int n0 = n_lo; n0 < n_hi; n0 += 32) {
     lds_barrier();
-    split(ra, &ls.ah[col][16 * rg], &ls.al[col][16 * rg], true);
-    split(rb, &ls.bh[col][16 * rg], &ls.bl[col][16 * rg], !kExactB);
+    split(ra, ls.ah, ls.al, true);
+    split(rb, ls.bh, ls.bl, !kExactB);
     lds_barrier();
     if (n0 + 32 < n_hi) fetch(n0 + 32);
     bf16x8 ah[4], al[4], bh[4], bl[4];

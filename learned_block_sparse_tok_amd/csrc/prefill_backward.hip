@@ -369,15 +369,32 @@ __global__ __launch_bounds__(256) void prefill_tiles_kernel(PrefillBackwardParam
     const float *a = p.ws_du_q + (int64_t)k * kGateDim;
     const uint16_t *b = p.q + (int64_t)k * kHeadDim;
     const int2 r = range(0, T);
-    outer_sum_tile128<true>([&](int n, int c) { return a[n * rs + c]; },
-                            [&](int n, int c) { return bf16_to_f32(b[n * rs + c]); }, r.x, r.y, acc, ls);
+    outer_sum_tile128<true>([&](int n, int c) { return *reinterpret_cast<const f32x4 *>(a + n * rs + c); },
+                            [&](int n, int c) {
+                              const u32x2 v = *reinterpret_cast<const u32x2 *>(b + n * rs + c);
+                              return f32x4{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+                            },
+                            r.x, r.y, acc, ls);
   } else {
     const int k2 = k - Hq, kvh = k2 % p.n_kv_heads, c0 = 128 * (k2 / p.n_kv_heads);
     const float *a = p.ws_a + (int64_t)kvh * T * p.a_cols + c0;
     const float *b = p.ws_ghat + (int64_t)kvh * T * kGateDim;
     const int2 r = range(min(T, kBlock * (c0 + 1)), T);
-    outer_sum_tile128<false>([&](int n, int c) { return c0 + c < (n >> 6) ? a[(int64_t)n * p.a_cols + c] : 0.f; },
-                             [&](int n, int c) { return b[(int64_t)n * kGateDim + c]; }, r.x, r.y, acc, ls);
+    // columns c0 + c .. +3 lie in A's row whenever the first is a block the
+    // position can select (a_cols is a multiple of 64)
+    outer_sum_tile128<false>(
+        [&](int n, int c) {
+          const int own = n >> 6;
+          f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (c0 + c < own) {
+            v = *reinterpret_cast<const f32x4 *>(a + (int64_t)n * p.a_cols + c);
+#pragma unroll
+            for (int k = 1; k < 4; ++k) v[k] = c0 + c + k < own ? v[k] : 0.f;
+          }
+          return v;
+        },
+        [&](int n, int c) { return *reinterpret_cast<const f32x4 *>(b + (int64_t)n * kGateDim + c); }, r.x, r.y, acc,
+        ls);
   }
   store_tile128(acc, p.ws_part + ((int64_t)k * kPrefillSplit + part) * 128 * 128);
 }
