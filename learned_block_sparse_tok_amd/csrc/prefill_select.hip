@@ -13,7 +13,8 @@
 //   2. per query head, U^T = W_q[h] . Q^T on v_mfma_f32_16x16x32_bf16 (bf16
 //      products are exact, sums fp32), RMSNorm, * w_qnorm and RoPE on the
 //      accumulator lanes, added into the mean gate query in LDS in head order
-//      (deterministic);
+//      (deterministic); with fewer heads than waves, a head's positions are
+//      split over several waves;
 //   3. the scores S^T = GK . ghat^T / sqrt(128) on MFMA with ghat split into
 //      bf16 high and low parts (about 16 significant bits: the scores keep
 //      fp32-level accuracy), gate keys gathered through the block table;
@@ -43,6 +44,7 @@ __global__ __launch_bounds__(kThreadsSel, 1) void prefill_select_kernel(PrefillS
   __shared__ __attribute__((aligned(16))) uint32_t big[kPos * kRowWords];  // phases 1-2 tables, then score keys
   __shared__ __attribute__((aligned(16))) uint32_t hist[kWavesSel][256];
   __shared__ int32_t bt_l[kMaxCandBatched];
+  __shared__ float wqn_l[kGateDim];
   float *cosv = reinterpret_cast<float *>(big);  // [64 positions][64 frequencies]
   float *sinv = cosv + kPos * 64;
   float *ghat = sinv + kPos * 64;                 // [64 positions][kGhatPitch]
@@ -67,18 +69,21 @@ __global__ __launch_bounds__(kThreadsSel, 1) void prefill_select_kernel(PrefillS
   }
   for (int e = t; e < kPos * kGhatPitch; e += kThreadsSel) ghat[e] = 0.f;
   for (int c = t; c < nc; c += kThreadsSel) bt_l[c] = p.block_table[c];
-  // this lane's w_qnorm entries: rows 16mt + 4g + r
-  float wqn[8][4];
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) wqn[mt][r] = p.w_qnorm[16 * mt + 4 * g + r];
+  if (t < kGateDim) wqn_l[t] = p.w_qnorm[t];
   __syncthreads();
 
-  // ---- 2. gate queries, rounds of up to kWavesSel heads (wave w: head h0 + w)
+  // ---- 2. gate queries.  Work items (head, group of position tiles): with
+  // fewer heads than waves, each head's 4 tiles of 16 positions are split
+  // over S = 4, 2 or 1 waves (G <= 2, G <= 4, else), so that more waves share
+  // the projections; rounds of kWavesSel / S heads (wave w: head h0 + w %
+  // (kWavesSel / S), tiles of part w / (kWavesSel / S)).
   const float inv_g = 1.0f / (float)G;
-  for (int h0 = 0; h0 < G; h0 += kWavesSel) {
-    const int h = h0 + wave;
+  const int S = G <= 2 ? 4 : G <= 4 ? 2 : 1;
+  const int ntw = 4 / S;          // position tiles per work item
+  const int hpr = kWavesSel / S;  // heads per round
+  const int hr = wave % hpr, part = wave / hpr;
+  for (int h0 = 0; h0 < G; h0 += hpr) {
+    const int h = h0 + hr;
     const bool active = h < G;
     const int head = kvh * G + (active ? h : 0);
     // B operand: lane l holds q[position 16nt + l%16][head][32ks + 8(l/16) .. +7]
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(kThreadsSel, 1) void prefill_select_kernel(PrefillS
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int pos = 16 * nt + j;
-      const bool ok = active && pos < nq;
+      const bool ok = active && nt / ntw == part && pos < nq;
       const uint16_t *qrow = p.q + ((int64_t)(t0 + (ok ? pos : 0)) * p.n_q_heads + head) * kHeadDim + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) qB[nt][ks] = b8(ok ? ld16(qrow + 32 * ks) : u32x4{0, 0, 0, 0});
@@ -96,52 +101,60 @@ __global__ __launch_bounds__(kThreadsSel, 1) void prefill_select_kernel(PrefillS
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint16_t *wrow = p.w_q + (int64_t)head * kGateDim * kHeadDim + 8 * g;
+    if (active) {
+      const uint16_t *wrow = p.w_q + (int64_t)head * kGateDim * kHeadDim + 8 * g;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      u32x4 a[4];  // A operand: lane l holds W_q[h][row 16mt + l%16][32ks + 8(l/16) .. +7]
+      for (int mt = 0; mt < 8; ++mt) {
+        u32x4 a[4];  // A operand: lane l holds W_q[h][row 16mt + l%16][32ks + 8(l/16) .. +7]
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) a[ks] = ld16(wrow + (16 * mt + j) * kHeadDim + 32 * ks);
+        for (int ks = 0; ks < 4; ++ks) a[ks] = ld16(wrow + (16 * mt + j) * kHeadDim + 32 * ks);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < 4; ++nt) {
+          if (nt / ntw != part) continue;  // uniform: not this item's tile
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b8(a[ks]), qB[nt][ks], acc[nt][mt], 0, 0, 0);
-    }
-    // RMSNorm (the 128 rows of a position sit in the 4 lanes l%16 == const),
-    // * w_qnorm, rotate-half RoPE: row i < 64 pairs with row i + 64 (tile mt + 4)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      float ss = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ss = fmaf(acc[nt][mt][r], acc[nt][mt][r], ss);
-      ss += __shfl_xor(ss, 16, 64);
-      ss += __shfl_xor(ss, 32, 64);
-      const float inv = 1.0f / sqrtf(ss * (1.0f / kGateDim) + 1e-6f);
-      const int pos = 16 * nt + j;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * mt + 4 * g + r;
-          const float na = acc[nt][mt][r] * inv * wqn[mt][r];
-          const float nb = acc[nt][mt + 4][r] * inv * wqn[mt + 4][r];
-          const float c = cosv[pos * 64 + i], s = sinv[pos * 64 + i];
-          acc[nt][mt][r] = na * c - nb * s;
-          acc[nt][mt + 4][r] = nb * c + na * s;
+          for (int ks = 0; ks < 4; ++ks)
+            acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b8(a[ks]), qB[nt][ks], acc[nt][mt], 0, 0, 0);
         }
-    }
-    // add into the mean gate query, one wave at a time (fixed head order)
-    for (int w = 0; w < kWavesSel; ++w) {
-      if (wave == w && active) {
+      }
+      // RMSNorm (the 128 rows of a position sit in the 4 lanes l%16 == const),
+      // * w_qnorm, rotate-half RoPE: row i < 64 pairs with row i + 64 (tile mt + 4)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+      for (int nt = 0; nt < 4; ++nt) {
+        if (nt / ntw != part) continue;
+        float ss = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ss = fmaf(acc[nt][mt][r], acc[nt][mt][r], ss);
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        const float inv = 1.0f / sqrtf(ss * (1.0f / kGateDim) + 1e-6f);
+        const int pos = 16 * nt + j;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * mt + 4 * g + r;
+            const float na = acc[nt][mt][r] * inv * wqn_l[i];
+            const float nb = acc[nt][mt + 4][r] * inv * wqn_l[i + 64];
+            const float c = cosv[pos * 64 + i], s = sinv[pos * 64 + i];
+            acc[nt][mt][r] = na * c - nb * s;
+            acc[nt][mt + 4][r] = nb * c + na * s;
+          }
+      }
+    }
+    // add into the mean gate query in head order (the items of one head
+    // cover disjoint positions and add at the same time)
+    for (int hh = 0; hh < hpr; ++hh) {
+      if (hr == hh && active) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          if (nt / ntw != part) continue;
 #pragma unroll
           for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) ghat[(16 * nt + j) * kGhatPitch + 16 * mt + 4 * g + r] += acc[nt][mt][r] * inv_g;
+        }
       }
       __syncthreads();
     }
