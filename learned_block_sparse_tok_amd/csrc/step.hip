@@ -37,6 +37,26 @@
 
 namespace sas {
 
+// blockIdx -> (pair, workgroup of the pair).  One workgroup per pair: the
+// pair is the block index.  Several: when the pair count is a multiple of 8,
+// the workgroups of one pair are placed on one XCD (workgroups are dealt to
+// the 8 XCDs round-robin), so that their repeated selections read the pair's
+// block-table row and gate keys through one L2; else consecutive.
+namespace {
+__device__ __forceinline__ void split_unit(int nwg, int &unit, int &wg) {
+  const int b = (int)blockIdx.x;
+  const int units = (int)gridDim.x / nwg;
+  if (nwg > 1 && (units & 7) == 0) {
+    const int x = b & 7, k = b >> 3;
+    unit = x + 8 * (k / nwg);
+    wg = k - (k / nwg) * nwg;
+  } else {
+    unit = nwg == 1 ? b : b / nwg;
+    wg = b - unit * nwg;
+  }
+}
+}  // namespace
+
 constexpr int kStepKeys = step_layout::kKeysPerGroup;  // gate keys per 16-lane group per pass (512 per workgroup)
 constexpr int kStepMaxSel = 256;      // selection slots per (sequence, KV head)
 constexpr int kStepBtUnroll = 2;      // block-table entries per thread staged without a loop
@@ -76,8 +96,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void step_kernel(const int32_t *__r
   // spans wg_per_unit workgroups, each making the pair's selection and
   // attending its share of the blocks as the decode kernel splits them
   const int nwg = sp.d.wg_per_unit;
-  const int unit = nwg == 1 ? (int)blockIdx.x : (int)blockIdx.x / nwg;  // KV head = unit % Hkv
-  const int wg = (int)blockIdx.x - unit * nwg;
+  int unit, wg;
+  split_unit(nwg, unit, wg);  // KV head = unit % Hkv
   const int s = unit / n_kv_heads_a;
   const int kvh = unit - s * n_kv_heads_a;
   const int t = threadIdx.x, lane = t & 63;
@@ -304,8 +324,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void select_decode_kernel(StepParam
   __shared__ int32_t local_page;
   const GateParams &p = sp.g;
   const int nwg = sp.d.wg_per_unit;
-  const int unit = blockIdx.x / nwg;
-  const int wg = blockIdx.x - unit * nwg;
+  int unit, wg;
+  split_unit(nwg, unit, wg);
   const int s = unit / p.n_kv_heads;
   const int kvh = unit - s * p.n_kv_heads;
   const int t = threadIdx.x, lane = t & 63;
