@@ -257,6 +257,132 @@ __device__ __forceinline__ void walk_pairs(const Ring<kHW, kVLikeK> &ring, Curso
 }
 constexpr bool kWalkPairs = true;
 
+// ---- the paired visiting order (sequences of up to kOrdBlocks blocks)
+//
+// Between two barriers the walk visits two blocks, and a wave whose queries
+// selected both sets the pace (its two visits run back to back while the
+// other waves wait).  With the blocks in ascending order that is the case
+// for most pairs of a long union; paired greedily instead, each block with
+// a later one that no wave shares, it is rare.  Each query's selection is
+// then looked up per block in a bitmap (qbits) rather than walked in order.
+constexpr int kOrdWords = 16;               // union bitmap words of a paired walk
+constexpr int kOrdBlocks = 32 * kOrdWords;  // 512 blocks: 32,768 tokens
+
+// qbits[q]: bit c set when query q selected block c; qpre[q][w]: the
+// query's selected blocks in words 0 .. w-1, so that block c is its slot
+// qpre[q][c/32] + (its selected blocks below c in word c/32)
+template <int kThreads>
+__device__ __forceinline__ void stage_query_bits(const WalkLds &L, uint32_t (*qbits)[kOrdWords],
+                                                 uint8_t (*qpre)[kOrdWords]) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < kBlock * kOrdWords; e += kThreads) (&qbits[0][0])[e] = 0u;
+  __syncthreads();
+  for (int e = tid; e < kBlock * kMaxSel; e += kThreads) {
+    const int q = e / kMaxSel, slot = e - q * kMaxSel;
+    if (slot < L.cnt[q]) {
+      const int c = L.sel[q][slot];
+      if ((unsigned)c < (unsigned)kOrdBlocks) atomicOr(&qbits[q][c >> 5], 1u << (c & 31));
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < kBlock * kOrdWords; e += kThreads) {
+    const int q = e / kOrdWords, w = e - q * kOrdWords;
+    int a = 0;
+    for (int v = 0; v < w; ++v) a += __builtin_popcount(qbits[q][v]);
+    qpre[q][w] = (uint8_t)a;
+  }
+}
+
+// The union's blocks in ascending order (ulist), each block's mask of the
+// waves with a query that selected it (wmask), then, chunk by chunk of 64
+// blocks (a wave per chunk), pairs taken greedily: each block not yet taken
+// with the first later untaken block of its chunk that shares no wave with
+// it, else the next untaken one.  Pair k is (order[2k], order[2k+1]); only
+// the last pair of an odd union has no second block (-1).  The arrays take
+// the place of the staged selections (L.sel), read into qbits before.
+// Returns the number of pairs; the caller synchronises before the walk.
+template <int kThreads, int kQW>
+__device__ __forceinline__ int stage_order(WalkLds &L, const uint32_t (*qbits)[kOrdWords], int *wpre, int nwords) {
+  static_assert(sizeof(L.sel) >= kOrdBlocks * (2 + 2 + 4), "order arrays exceed the selection buffer");
+  int16_t *ulist = reinterpret_cast<int16_t *>(&L.sel[0][0]);
+  int16_t *order = ulist + kOrdBlocks;
+  uint32_t *wmask = reinterpret_cast<uint32_t *>(ulist + 2 * kOrdBlocks);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __syncthreads();  // L.sel is read no more
+  for (int c = tid; c < kOrdBlocks; c += kThreads) wmask[c] = 0u;
+  if (tid <= kOrdWords) {
+    int a = 0;
+    for (int v = 0; v < tid && v < nwords; ++v) a += __builtin_popcount(L.bm[v]);
+    wpre[tid] = a;
+  }
+  __syncthreads();
+  for (int c = tid; c < 32 * nwords; c += kThreads) {
+    const uint32_t word = L.bm[c >> 5], bit = 1u << (c & 31);
+    if (word & bit) ulist[wpre[c >> 5] + __builtin_popcount(word & (bit - 1u))] = (int16_t)c;
+  }
+  for (int e = tid; e < kBlock * kOrdWords; e += kThreads) {
+    const int q = e / kOrdWords, w = e - q * kOrdWords;
+    for (uint32_t bits = qbits[q][w]; bits; bits &= bits - 1u)
+      atomicOr(&wmask[32 * w + __builtin_ctz(bits)], 1u << (q / kQW));
+  }
+  __syncthreads();
+  const int n = wpre[nwords];
+  constexpr int kWaves = kThreads / 64;
+  for (int k = wave; 64 * k < n; k += kWaves) {
+    const int cnt = min(64, n - 64 * k);
+    const bool valid = lane < cnt;
+    const int b = valid ? ulist[64 * k + lane] : 0;
+    const uint32_t m = valid ? wmask[b] : 0u;
+    uint64_t taken = 0;
+    int pi = 0;
+    for (int i = 0; i < cnt; ++i) {
+      if ((taken >> i) & 1u) continue;
+      taken |= 1ull << i;
+      const uint32_t mi = (uint32_t)__builtin_amdgcn_readlane((int)m, i);
+      const bool open = valid && lane > i && !((taken >> lane) & 1u);
+      uint64_t cand = __builtin_amdgcn_ballot_w64(open && (m & mi) == 0u);
+      if (cand == 0) cand = __builtin_amdgcn_ballot_w64(open);
+      const int j = cand ? (int)__builtin_ctzll(cand) : -1;
+      if (j >= 0) taken |= 1ull << j;
+      const int bi = __builtin_amdgcn_readlane(b, i);
+      const int bj = j >= 0 ? __builtin_amdgcn_readlane(b, j) : -1;
+      if (lane == 0) {
+        order[64 * k + 2 * pi] = (int16_t)bi;
+        order[64 * k + 2 * pi + 1] = (int16_t)bj;
+      }
+      ++pi;
+    }
+  }
+  return (n + 1) >> 1;
+}
+
+// The walk of walk_pairs over a given order of pairs (stage_order).
+template <int kHW, bool kVLikeK, typename Before, typename VisitPair>
+__device__ __forceinline__ void walk_ordered(const Ring<kHW, kVLikeK> &ring, const int16_t *order, int npairs,
+                                             Before before_visit, VisitPair visit_pair) {
+  auto blk = [&](int i) { return __builtin_amdgcn_readfirstlane((int)order[i]); };
+  int a0 = blk(0), a1 = blk(1);  // a0: never -1 (every query selects its own block)
+  ring.copy(a0, 0);
+  ring.copy(a1 >= 0 ? a1 : a0, 1);
+  for (int k = 0; k < npairs; ++k) {
+    const int s0 = (2 * k) & (kStages - 1), s1 = (2 * k + 1) & (kStages - 1);
+    wait_vm<0>();   // this wave's copies of the pair landed (nothing else is in flight)
+    lds_barrier();  // ... and every other wave's; the previous pair's stages are free
+    before_visit(a0, s0);
+    if (a1 >= 0) before_visit(a1, s1);
+    const bool more = k + 1 < npairs;
+    const int b0 = more ? blk(2 * k + 2) : -1;
+    const int b1 = more ? blk(2 * k + 3) : -1;
+    ring.copy(b0 >= 0 ? b0 : a0, (2 * k + 2) & (kStages - 1));  // a missing block: a filler copy, fixed count
+    ring.copy(b1 >= 0 ? b1 : a0, (2 * k + 3) & (kStages - 1));
+    visit_pair(a0, s0, a1, s1);
+    a0 = b0;
+    a1 = b1;
+  }
+  wait_vm<0>();  // the trailing filler copies land before the workgroup ends
+}
+
 // blockIdx -> (query block, KV head, head group): heaviest query blocks
 // first, consecutive workgroups on different KV heads
 struct Tile {
@@ -275,11 +401,14 @@ __device__ __forceinline__ Tile tile_of(int head_groups, int n_kv_heads, int n_q
 
 }  // namespace
 
-template <bool kGated, int kHW>
+template <bool kGated, int kHW, bool kOrdered>
 __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kernel(PrefillParams p) {
   using Lay = Layout<kHW>;
   __shared__ __attribute__((aligned(1024))) WalkLds L;
   __shared__ float gate_l[kGated ? kBlock : 1][kMaxSel];
+  __shared__ uint32_t qbits[kOrdered ? kBlock : 1][kOrdWords];
+  __shared__ uint8_t qpre[kOrdered ? kBlock : 1][kOrdWords];
+  __shared__ int wpre[kOrdWords + 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -297,6 +426,12 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kerne
 
   const int nwords = stage_union<Lay::kThreads>(L, kGated ? gate_l : nullptr, p.sel, p.gates, p.cnt, p.n_kv_heads,
                                                 w.kvh, p.max_sel, w.t0, w.nq, w.qb);
+  int npairs = 0;
+  if constexpr (kOrdered) {
+    __syncthreads();
+    stage_query_bits<Lay::kThreads>(L, qbits, qpre);
+    npairs = stage_order<Lay::kThreads, Lay::kQW>(L, qbits, wpre, nwords);
+  }
 
   // B operand of S^T = K Q^T: lane l holds q[its column][32ks + 8(l/16) .. +7]
   bf16x8 qB[4];
@@ -306,10 +441,11 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kerne
   wait_vm<0>();  // every compiler-visible load done before the copies start
   __syncthreads();
 
-  // ---- this lane's walk through its query's ascending selection (LDS)
-  const int cq = L.cnt[qi];
+  // ---- this lane's walk through its query's ascending selection (LDS;
+  // the paired order looks each block up in the query's bitmap instead)
+  const int cq = kOrdered ? 0 : L.cnt[qi];
   int ptr = 0;
-  int nxt_c = cq > 0 ? L.sel[qi][0] : INT_MAX;
+  int nxt_c = !kOrdered && cq > 0 ? L.sel[qi][0] : INT_MAX;
 
   f32x4 o[8];
 #pragma unroll
@@ -340,11 +476,26 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kerne
          }
        };
   auto visit = [&](int c, int st) {
-         const bool s_l = nxt_c == c;
-         const float g_l = kGated && s_l ? gate_l[kGated ? qi : 0][ptr] : 0.f;
-         if (s_l) {
-           ++ptr;
-           nxt_c = ptr < cq ? L.sel[qi][ptr] : INT_MAX;
+         bool s_l;
+         float g_l = 0.f;
+         if constexpr (kOrdered) {
+           // the query's bitmap word of c and its prefix count, read together,
+           // so that the gate's slot is known one LDS round trip in and its
+           // read goes out with the key tiles'
+           const uint32_t wb = qbits[kOrdered ? qi : 0][c >> 5], bit = 1u << (c & 31);
+           const int pre = qpre[kOrdered ? qi : 0][c >> 5];
+           s_l = (wb & bit) != 0u;
+           if constexpr (kGated) {  // read whether or not the query selected c (no branch)
+             const float gv = gate_l[kGated ? qi : 0][min(pre + __builtin_popcount(wb & (bit - 1u)), kMaxSel - 1)];
+             g_l = s_l ? gv : 0.f;
+           }
+         } else {
+           s_l = nxt_c == c;
+           g_l = kGated && s_l ? gate_l[kGated ? qi : 0][ptr] : 0.f;
+           if (s_l) {
+             ++ptr;
+             nxt_c = ptr < cq ? L.sel[qi][ptr] : INT_MAX;
+           }
          }
          if (__builtin_amdgcn_ballot_w64(s_l) == 0) return;
          const uint8_t *kt = L.ring[st];
@@ -428,18 +579,24 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kerne
 #pragma unroll
            for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
          }
+         // O^T += V^T P^T in 16 steps (k-step s2 = i / 8, output tile dt =
+         // i % 8): step i + 1's V^T operand is read while step i's product
+         // runs, so that the reads do not wait one by one
+         auto vread = [&](int i) {
+           const int s2 = i >> 3, dt = i & 7;
+           const uint8_t *vrd = vt + tr_off[dt & 3] + 128 * (dt >> 2) + 32 * s2 * kRow;
+           const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)vrd);
+           const i16x4 a1 =
+               __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(vrd + 16 * kRow));
+           const u32x2 lo2 = __builtin_bit_cast(u32x2, a0), hi2 = __builtin_bit_cast(u32x2, a1);
+           return u32x4{lo2.x, lo2.y, hi2.x, hi2.y};
+         };
+         u32x4 va = vread(0);
 #pragma unroll
-         for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-           for (int dt = 0; dt < 8; ++dt) {
-             const uint8_t *vrd = vt + tr_off[dt & 3] + 128 * (dt >> 2) + 32 * s2 * kRow;
-             i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)vrd);
-             i16x4 a1 =
-                 __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(vrd + 16 * kRow));
-             u32x2 lo2 = __builtin_bit_cast(u32x2, a0), hi2 = __builtin_bit_cast(u32x2, a1);
-             const bf16x8 a = as_bf16(u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
-             o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16(pB[s2]), o[dt], 0, 0, 0);
-           }
+         for (int i = 0; i < 16; ++i) {
+           const u32x4 vn = i + 1 < 16 ? vread(i + 1) : va;
+           o[i & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(va), as_bf16(pB[i >> 3]), o[i & 7], 0, 0, 0);
+           va = vn;
          }
        };
   // the two blocks of a pair in turn (c1 = -1: no second block)
@@ -447,7 +604,9 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kerne
     visit(c0, st0);
     if (c1 >= 0) visit(c1, st1);
   };
-  if (kWalkPairs) walk_pairs(ring, cur, before, visit, visit_pair);
+  if constexpr (kOrdered) walk_ordered(ring, reinterpret_cast<const int16_t *>(&L.sel[0][0]) + kOrdBlocks, npairs,
+                                       before, visit_pair);
+  else if (kWalkPairs) walk_pairs(ring, cur, before, visit, visit_pair);
   else walk(ring, cur, before, visit);
 
   // ---- normalise and store: lane holds dims 16dt + 4(l/16) .. +3 of its column
@@ -479,11 +638,14 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kerne
 // heads are all in one wave: one write per slot).  A group of G > 4 heads
 // spans several workgroups, whose partial sums the chain kernel adds in
 // order.
-template <int kHW>
+template <int kHW, bool kOrdered>
 __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_grad_kernel(PrefillBackwardParams p) {
   using Lay = Layout<kHW>;
   __shared__ __attribute__((aligned(1024))) WalkLds L;
   __shared__ float dg_l[kBlock][kMaxSel];
+  __shared__ uint32_t qbits[kOrdered ? kBlock : 1][kOrdWords];
+  __shared__ uint8_t qpre[kOrdered ? kBlock : 1][kOrdWords];
+  __shared__ int wpre[kOrdWords + 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -515,22 +677,35 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_grad_kernel(
   wait_vm<0>();  // every compiler-visible load done before the copies start
   __syncthreads();
 
-  const int cq = L.cnt[qi];
+  int npairs = 0;
+  if constexpr (kOrdered) {
+    stage_query_bits<Lay::kThreads>(L, qbits, qpre);
+    npairs = stage_order<Lay::kThreads, Lay::kQW>(L, qbits, wpre, nwords);
+    __syncthreads();
+  }
+  const int cq = kOrdered ? 0 : L.cnt[qi];
   int ptr = 0;
-  int nxt_c = cq > 0 ? L.sel[qi][0] : INT_MAX;
+  int nxt_c = !kOrdered && cq > 0 ? L.sel[qi][0] : INT_MAX;
 
   const Ring<kHW, true> ring(p.k_pool, p.v_pool, p.block_table, p.page_stride, p.tok_stride, p.head_stride, w.kvh,
                              &L.ring[0][0], wave);
   Cursor cur(L.bm, nwords);
   // whether this lane's query selected block c, and the slot it takes
   auto advance = [&](int c, int &slot) {
-    const bool s_l = nxt_c == c;
-    slot = ptr;
-    if (s_l) {
-      ++ptr;
-      nxt_c = ptr < cq ? L.sel[qi][ptr] : INT_MAX;
+    if constexpr (kOrdered) {
+      if (c < 0) return false;  // no second block
+      const uint32_t wb = qbits[kOrdered ? qi : 0][c >> 5], bit = 1u << (c & 31);
+      slot = qpre[kOrdered ? qi : 0][c >> 5] + __builtin_popcount(wb & (bit - 1u));
+      return (wb & bit) != 0u;
+    } else {
+      const bool s_l = nxt_c == c;
+      slot = ptr;
+      if (s_l) {
+        ++ptr;
+        nxt_c = ptr < cq ? L.sel[qi][ptr] : INT_MAX;
+      }
+      return s_l;
     }
-    return s_l;
   };
   // key tile t of the block in stage st: this lane's sum over its 4 keys of
   // P * D.  Keys the query may not see (later keys of its own block, rows
@@ -594,7 +769,7 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_grad_kernel(
     const bool s0 = advance(c0, slot0);
     const bool s1 = advance(c1, slot1);
     const bool any0 = __builtin_amdgcn_ballot_w64(s0) != 0, any1 = __builtin_amdgcn_ballot_w64(s1) != 0;
-    if (!any0 || !any1 || c1 == w.qb) {
+    if (!any0 || !any1 || c0 == w.qb || c1 == w.qb) {
       if (any0) finish(block_sum(c0, st0), s0, slot0);
       if (any1) finish(block_sum(c1, st1), s1, slot1);
       return;
@@ -608,7 +783,10 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_grad_kernel(
     finish(acc0, s0, slot0);
     finish(acc1, s1, slot1);
   };
-  if (kWalkPairs) walk_pairs(ring, cur, [&](int, int) {}, visit, visit_pair);
+  if constexpr (kOrdered)
+    walk_ordered(ring, reinterpret_cast<const int16_t *>(&L.sel[0][0]) + kOrdBlocks, npairs, [&](int, int) {},
+                 visit_pair);
+  else if (kWalkPairs) walk_pairs(ring, cur, [&](int, int) {}, visit, visit_pair);
   else walk(ring, cur, [&](int, int) {}, visit);
   __syncthreads();
   float *dst = p.ws_dgp + (((int64_t)w.hg * p.seq_len + w.t0) * p.n_kv_heads + w.kvh) * p.max_sel;
@@ -623,10 +801,16 @@ template <int kHW>
 hipError_t launch_attend_hw(PrefillParams p, hipStream_t st) {
   p.head_groups = (p.group + kHW - 1) / kHW;
   const dim3 grid((unsigned)(p.n_qblocks * p.n_kv_heads * p.head_groups));
-  if (p.gates)
-    hipLaunchKernelGGL((prefill_attend_kernel<true, kHW>), grid, dim3(Layout<kHW>::kThreads), 0, st, p);
+  // the paired order for sequences of up to kOrdBlocks blocks (its bitmaps' size)
+  const bool ordered = p.n_qblocks <= kOrdBlocks;
+  if (p.gates && ordered)
+    hipLaunchKernelGGL((prefill_attend_kernel<true, kHW, true>), grid, dim3(Layout<kHW>::kThreads), 0, st, p);
+  else if (p.gates)
+    hipLaunchKernelGGL((prefill_attend_kernel<true, kHW, false>), grid, dim3(Layout<kHW>::kThreads), 0, st, p);
+  else if (ordered)
+    hipLaunchKernelGGL((prefill_attend_kernel<false, kHW, true>), grid, dim3(Layout<kHW>::kThreads), 0, st, p);
   else
-    hipLaunchKernelGGL((prefill_attend_kernel<false, kHW>), grid, dim3(Layout<kHW>::kThreads), 0, st, p);
+    hipLaunchKernelGGL((prefill_attend_kernel<false, kHW, false>), grid, dim3(Layout<kHW>::kThreads), 0, st, p);
   return hipGetLastError();
 }
 }  // namespace
@@ -642,12 +826,19 @@ hipError_t launch_prefill_attend(const PrefillParams &p, hipStream_t st) {
 hipError_t launch_prefill_grad(const PrefillBackwardParams &p, hipStream_t st) {
   const int hw = prefill_heads_per_wave(p.group);
   const dim3 grid((unsigned)(p.n_qblocks * p.n_kv_heads * p.head_groups));
-  if (hw == 1)
-    hipLaunchKernelGGL((prefill_grad_kernel<1>), grid, dim3(Layout<1>::kThreads), 0, st, p);
+  const bool ordered = p.n_qblocks <= kOrdBlocks;  // the paired order (its bitmaps' size)
+  if (hw == 1 && ordered)
+    hipLaunchKernelGGL((prefill_grad_kernel<1, true>), grid, dim3(Layout<1>::kThreads), 0, st, p);
+  else if (hw == 1)
+    hipLaunchKernelGGL((prefill_grad_kernel<1, false>), grid, dim3(Layout<1>::kThreads), 0, st, p);
+  else if (hw == 2 && ordered)
+    hipLaunchKernelGGL((prefill_grad_kernel<2, true>), grid, dim3(Layout<2>::kThreads), 0, st, p);
   else if (hw == 2)
-    hipLaunchKernelGGL((prefill_grad_kernel<2>), grid, dim3(Layout<2>::kThreads), 0, st, p);
+    hipLaunchKernelGGL((prefill_grad_kernel<2, false>), grid, dim3(Layout<2>::kThreads), 0, st, p);
+  else if (ordered)
+    hipLaunchKernelGGL((prefill_grad_kernel<4, true>), grid, dim3(Layout<4>::kThreads), 0, st, p);
   else
-    hipLaunchKernelGGL((prefill_grad_kernel<4>), grid, dim3(Layout<4>::kThreads), 0, st, p);
+    hipLaunchKernelGGL((prefill_grad_kernel<4, false>), grid, dim3(Layout<4>::kThreads), 0, st, p);
   return hipGetLastError();
 }
 
