@@ -10,7 +10,10 @@
 //
 // One workgroup per (64-query block, KV head, group of kHW query heads).
 // The workgroup marks the union of its queries' selections in an LDS bitmap
-// and walks it in ascending block order.  Each visited block's K and V rows
+// and walks it two blocks at a time: for sequences of up to 512 blocks in a
+// paired order (each block with a later one that no wave shares, each
+// query's selection looked up in a per-query bitmap), else in ascending
+// block order (each query's selection walked with a pointer).  Each visited block's K and V rows
 // (32 KiB) are copied once into LDS by the gfx950 global-to-LDS loads
 // (global_load_lds_dwordx4) and shared by all waves; a ring of four 32 KiB
 // stages keeps the next three blocks in flight while one is consumed.  The
