@@ -155,8 +155,10 @@ struct Ring {
   }
   // the per-lane source offsets are recomputed at each copy (a few integer
   // operations) rather than held in registers across the walk
-  __device__ __forceinline__ void copy(int c, int st) const {
-    const int64_t off = (int64_t)btc[c] * page_bytes;
+  __device__ __forceinline__ void copy(int c, int st) const { copy_page(btc[c], st); }
+  // the same with the block's page already known (no block-table load)
+  __device__ __forceinline__ void copy_page(int page, int st) const {
+    const int64_t off = (int64_t)page * page_bytes;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(dst0 + st * kStage);
     const int lane = threadIdx.x & 63, sl = lane & 15;
 #pragma unroll
@@ -301,12 +303,23 @@ __device__ __forceinline__ void stage_query_bits(const WalkLds &L, uint32_t (*qb
 // blocks (a wave per chunk), pairs taken greedily: each block not yet taken
 // with the first later untaken block of its chunk that shares no wave with
 // it, else the next untaken one.  Pair k is (order[2k], order[2k+1]); only
-// the last pair of an odd union has no second block (-1).  The arrays take
-// the place of the staged selections (L.sel), read into qbits before.
-// Returns the number of pairs; the caller synchronises before the walk.
+// the last pair of an odd union has no second block (-1).  The walk reads
+// pair k as one 16-byte entry of the pair table (pair_table): each block
+// with its wave mask in the upper 16 bits (0xFFFF: no second block), then
+// the two blocks' pages (the first's again for a missing second block), so
+// that it needs no block-table load and a wave skips a block none of its
+// queries selected without reading their bitmaps.  The arrays take the
+// place of the staged selections (L.sel), read into qbits before.  Returns
+// the number of pairs; the caller synchronises before the walk.
+__device__ __forceinline__ u32x4 *pair_table(WalkLds &L) {
+  return reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(&L.sel[0][0]) + kOrdBlocks * (2 + 2 + 4));
+}
 template <int kThreads, int kQW>
-__device__ __forceinline__ int stage_order(WalkLds &L, const uint32_t (*qbits)[kOrdWords], int *wpre, int nwords) {
-  static_assert(sizeof(L.sel) >= kOrdBlocks * (2 + 2 + 4), "order arrays exceed the selection buffer");
+__device__ __forceinline__ int stage_order(WalkLds &L, const uint32_t (*qbits)[kOrdWords], int *wpre, int nwords,
+                                           const int32_t *block_table) {
+  static_assert(sizeof(L.sel) >= kOrdBlocks * (2 + 2 + 4) + kOrdBlocks / 2 * 16,
+                "order arrays exceed the selection buffer");
+  static_assert(kThreads / 64 <= 16, "wave masks are 16 bits");
   int16_t *ulist = reinterpret_cast<int16_t *>(&L.sel[0][0]);
   int16_t *order = ulist + kOrdBlocks;
   uint32_t *wmask = reinterpret_cast<uint32_t *>(ulist + 2 * kOrdBlocks);
@@ -357,31 +370,45 @@ __device__ __forceinline__ int stage_order(WalkLds &L, const uint32_t (*qbits)[k
       ++pi;
     }
   }
-  return (n + 1) >> 1;
+  __syncthreads();
+  const int np = (n + 1) >> 1;
+  u32x4 *pairs = pair_table(L);
+  for (int i = tid; i < np; i += kThreads) {
+    const int b0 = order[2 * i], b1 = order[2 * i + 1];
+    const int pg0 = block_table[b0];
+    pairs[i] = u32x4{(uint32_t)b0 | wmask[b0] << 16, b1 >= 0 ? (uint32_t)b1 | wmask[b1] << 16 : 0xFFFFu,
+                     (uint32_t)pg0, (uint32_t)(b1 >= 0 ? block_table[b1] : pg0)};
+  }
+  return np;
 }
 
-// The walk of walk_pairs over a given order of pairs (stage_order).
+// The walk of walk_pairs over the pair table of stage_order:
+// visit_pair(c0, wm0, stage0, c1, wm1, stage1) with each block's wave mask
+// (c1 = -1: no second block).  The next pair's entry is read before the
+// barrier (the table does not change during the walk), so its copies go out
+// right after it.
 template <int kHW, bool kVLikeK, typename Before, typename VisitPair>
-__device__ __forceinline__ void walk_ordered(const Ring<kHW, kVLikeK> &ring, const int16_t *order, int npairs,
+__device__ __forceinline__ void walk_ordered(const Ring<kHW, kVLikeK> &ring, const u32x4 *pairs, int npairs,
                                              Before before_visit, VisitPair visit_pair) {
-  auto blk = [&](int i) { return __builtin_amdgcn_readfirstlane((int)order[i]); };
-  int a0 = blk(0), a1 = blk(1);  // a0: never -1 (every query selects its own block)
-  ring.copy(a0, 0);
-  ring.copy(a1 >= 0 ? a1 : a0, 1);
+  auto uni = [](uint32_t v) { return __builtin_amdgcn_readfirstlane((int)v); };
+  const u32x4 e0 = pairs[0];
+  int x0 = uni(e0.x), x1 = uni(e0.y);  // x0's block: never missing (every query selects its own block)
+  ring.copy_page(uni(e0.z), 0);
+  ring.copy_page(uni(e0.w), 1);  // a missing second block: a filler copy of the first, fixed count
   for (int k = 0; k < npairs; ++k) {
     const int s0 = (2 * k) & (kStages - 1), s1 = (2 * k + 1) & (kStages - 1);
+    const u32x4 nx = pairs[k + 1 < npairs ? k + 1 : k];  // after the last pair: filler copies
     wait_vm<0>();   // this wave's copies of the pair landed (nothing else is in flight)
     lds_barrier();  // ... and every other wave's; the previous pair's stages are free
+    const int a0 = x0 & 0xFFFF, a1 = (x1 & 0xFFFF) == 0xFFFF ? -1 : x1 & 0xFFFF;
     before_visit(a0, s0);
     if (a1 >= 0) before_visit(a1, s1);
-    const bool more = k + 1 < npairs;
-    const int b0 = more ? blk(2 * k + 2) : -1;
-    const int b1 = more ? blk(2 * k + 3) : -1;
-    ring.copy(b0 >= 0 ? b0 : a0, (2 * k + 2) & (kStages - 1));  // a missing block: a filler copy, fixed count
-    ring.copy(b1 >= 0 ? b1 : a0, (2 * k + 3) & (kStages - 1));
-    visit_pair(a0, s0, a1, s1);
-    a0 = b0;
-    a1 = b1;
+    const int y0 = uni(nx.x), y1 = uni(nx.y);
+    ring.copy_page(uni(nx.z), (2 * k + 2) & (kStages - 1));
+    ring.copy_page(uni(nx.w), (2 * k + 3) & (kStages - 1));
+    visit_pair(a0, (uint32_t)x0 >> 16, s0, a1, (uint32_t)x1 >> 16, s1);
+    x0 = y0;
+    x1 = y1;
   }
   wait_vm<0>();  // the trailing filler copies land before the workgroup ends
 }
@@ -433,7 +460,7 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kerne
   if constexpr (kOrdered) {
     __syncthreads();
     stage_query_bits<Lay::kThreads>(L, qbits, qpre);
-    npairs = stage_order<Lay::kThreads, Lay::kQW>(L, qbits, wpre, nwords);
+    npairs = stage_order<Lay::kThreads, Lay::kQW>(L, qbits, wpre, nwords, p.block_table);
   }
 
   // B operand of S^T = K Q^T: lane l holds q[its column][32ks + 8(l/16) .. +7]
@@ -478,7 +505,10 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kerne
            lds_barrier();
          }
        };
-  auto visit = [&](int c, int st) {
+  // wm: the waves with a query that selected c (the paired order; all ones
+  // for the ascending walk, whose waves test their queries' pointers)
+  auto visit = [&](int c, uint32_t wm, int st) {
+         if (kOrdered && ((wm >> wave) & 1u) == 0u) return;
          bool s_l;
          float g_l = 0.f;
          if constexpr (kOrdered) {
@@ -499,8 +529,8 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kerne
              ++ptr;
              nxt_c = ptr < cq ? L.sel[qi][ptr] : INT_MAX;
            }
+           if (__builtin_amdgcn_ballot_w64(s_l) == 0) return;
          }
-         if (__builtin_amdgcn_ballot_w64(s_l) == 0) return;
          const uint8_t *kt = L.ring[st];
          const uint8_t *vt = L.ring[st] + kTile;
          f32x4 sacc[4];  // [key tile]
@@ -603,14 +633,18 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_attend_kerne
          }
        };
   // the two blocks of a pair in turn (c1 = -1: no second block)
-  auto visit_pair = [&](int c0, int st0, int c1, int st1) {
-    visit(c0, st0);
-    if (c1 >= 0) visit(c1, st1);
+  auto visit_pair_m = [&](int c0, uint32_t wm0, int st0, int c1, uint32_t wm1, int st1) {
+    visit(c0, wm0, st0);
+    if (c1 >= 0) visit(c1, wm1, st1);
   };
-  if constexpr (kOrdered) walk_ordered(ring, reinterpret_cast<const int16_t *>(&L.sel[0][0]) + kOrdBlocks, npairs,
-                                       before, visit_pair);
-  else if (kWalkPairs) walk_pairs(ring, cur, before, visit, visit_pair);
-  else walk(ring, cur, before, visit);
+  if constexpr (kOrdered) {
+    walk_ordered(ring, pair_table(L), npairs, before, visit_pair_m);
+  } else {
+    auto visit1 = [&](int c, int st) { visit(c, ~0u, st); };
+    auto visit_pair = [&](int c0, int st0, int c1, int st1) { visit_pair_m(c0, ~0u, st0, c1, ~0u, st1); };
+    if (kWalkPairs) walk_pairs(ring, cur, before, visit1, visit_pair);
+    else walk(ring, cur, before, visit1);
+  }
 
   // ---- normalise and store: lane holds dims 16dt + 4(l/16) .. +3 of its column
   const float l = rows_sum(ls);
@@ -683,7 +717,7 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_grad_kernel(
   int npairs = 0;
   if constexpr (kOrdered) {
     stage_query_bits<Lay::kThreads>(L, qbits, qpre);
-    npairs = stage_order<Lay::kThreads, Lay::kQW>(L, qbits, wpre, nwords);
+    npairs = stage_order<Lay::kThreads, Lay::kQW>(L, qbits, wpre, nwords, p.block_table);
     __syncthreads();
   }
   const int cq = kOrdered ? 0 : L.cnt[qi];
@@ -765,13 +799,17 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_grad_kernel(
     const bool s_l = advance(c, slot);
     if (__builtin_amdgcn_ballot_w64(s_l) != 0) finish(block_sum(c, st), s_l, slot);
   };
-  // two blocks (c0 < c1: only c1 can be a query's own block); a wave with
-  // queries in both whole blocks works on the two key tiles side by side
-  auto visit_pair = [&](int c0, int st0, int c1, int st1) {
+  // two blocks (c0 < c1: only c1 can be a query's own block) with their wave
+  // masks (m: the waves with a query that selected the block; all ones for
+  // the ascending walk, whose waves test their queries' pointers); a wave
+  // with queries in both whole blocks works on the two key tiles side by side
+  auto visit_pair_m = [&](int c0, uint32_t wm0, int st0, int c1, uint32_t wm1, int st1) {
+    if (kOrdered && ((wm0 >> wave) & 1u) == 0u && (c1 < 0 || ((wm1 >> wave) & 1u) == 0u)) return;
     int slot0, slot1;
     const bool s0 = advance(c0, slot0);
     const bool s1 = advance(c1, slot1);
-    const bool any0 = __builtin_amdgcn_ballot_w64(s0) != 0, any1 = __builtin_amdgcn_ballot_w64(s1) != 0;
+    const bool any0 = kOrdered ? ((wm0 >> wave) & 1u) != 0u : __builtin_amdgcn_ballot_w64(s0) != 0;
+    const bool any1 = kOrdered ? c1 >= 0 && ((wm1 >> wave) & 1u) != 0u : __builtin_amdgcn_ballot_w64(s1) != 0;
     if (!any0 || !any1 || c0 == w.qb || c1 == w.qb) {
       if (any0) finish(block_sum(c0, st0), s0, slot0);
       if (any1) finish(block_sum(c1, st1), s1, slot1);
@@ -786,9 +824,9 @@ __global__ __launch_bounds__(Layout<kHW>::kThreads, 1) void prefill_grad_kernel(
     finish(acc0, s0, slot0);
     finish(acc1, s1, slot1);
   };
+  auto visit_pair = [&](int c0, int st0, int c1, int st1) { visit_pair_m(c0, ~0u, st0, c1, ~0u, st1); };
   if constexpr (kOrdered)
-    walk_ordered(ring, reinterpret_cast<const int16_t *>(&L.sel[0][0]) + kOrdBlocks, npairs, [&](int, int) {},
-                 visit_pair);
+    walk_ordered(ring, pair_table(L), npairs, [&](int, int) {}, visit_pair_m);
   else if (kWalkPairs) walk_pairs(ring, cur, [&](int, int) {}, visit, visit_pair);
   else walk(ring, cur, [&](int, int) {}, visit);
   __syncthreads();
