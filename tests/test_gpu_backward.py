@@ -108,6 +108,8 @@ PREFILL_BWD_CASES = [
     dict(name="paged_g16_t300", T=300, Hq=16, Hkv=1, budget=192, layout="paged", seed=75),
     dict(name="one_block_t50", T=50, Hq=4, Hkv=1, budget=128, layout="paged", seed=76),
     dict(name="g2_full_budget_t1100_b4096", T=1100, Hq=4, Hkv=2, budget=4096, layout="contiguous", seed=77),
+    # unions over two 64-block pairing chunks (66 blocks, ragged last one)
+    dict(name="two_chunks_t4200", T=4200, Hq=4, Hkv=1, budget=512, layout="paged", seed=78),
 ]
 
 

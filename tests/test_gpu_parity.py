@@ -143,6 +143,10 @@ PREFILL_CASES = [
     dict(name="paged_g16_tail1", T=577, Hq=16, Hkv=1, budget=320, layout="paged"),
     dict(name="full_budget", T=300, Hq=4, Hkv=1, budget=320, layout="paged"),
     dict(name="b4096_g2", T=1500, Hq=4, Hkv=2, budget=4096, layout="paged"),
+    # 66 blocks, a ragged last one: the later query blocks' unions span two
+    # 64-block pairing chunks, the second with one or two blocks (a pair
+    # without its second block)
+    dict(name="two_chunks_t4200", T=4200, Hq=4, Hkv=1, budget=512, layout="paged"),
 ]
 
 
