@@ -8,17 +8,18 @@
 // size 128, Qproj, Q/K normalization, gate RoPE; "Tencent Hunyuan
 // open-sources SAS ...": per-query block selection).  The 64 positions of a
 // block share their candidate set (blocks 0 .. b-1 for block b), so one
-// 512-thread workgroup (8 waves) per (64-position block, KV head) does:
+// 1,024-thread workgroup (16 waves) per (64-position block, KV head) does:
 //   1. the RoPE table of its 64 positions (angles reduced in fp64);
-//   2. per query head, U^T = W_q[h] . Q^T on v_mfma_f32_16x16x32_bf16 (bf16
-//      products are exact, sums fp32), RMSNorm, * w_qnorm and RoPE on the
-//      accumulator lanes, added into the mean gate query in LDS in head order
-//      (deterministic); with fewer heads than waves, a head's positions are
-//      split over several waves;
+//   2. per query head and 16-position tile (one work item per wave),
+//      U^T = W_q[h] . Q^T on v_mfma_f32_16x16x32_bf16 (bf16 products are
+//      exact, sums fp32), RMSNorm, * w_qnorm and RoPE on the accumulator
+//      lanes, added into the mean gate query in LDS in head order
+//      (deterministic);
 //   3. the scores S^T = GK . ghat^T / sqrt(128) on MFMA with ghat split into
 //      bf16 high and low parts (about 16 significant bits: the scores keep
-//      fp32-level accuracy), gate keys gathered through the block table;
-//   4. one exact Top-K per position (wave_select), eight waves in parallel
+//      fp32-level accuracy), gate keys gathered through the block table; a
+//      wave takes candidate tiles of one half of the positions;
+//   4. one exact Top-K per position (wave_select), sixteen waves in parallel
 //      (the score keys' 132 KiB of LDS leave room for one workgroup per CU,
 //      and the selections are latency-bound: more waves, more in flight).
 // It replaces 64 per-position gate workgroups, each of which re-read W_q and
@@ -31,7 +32,7 @@ namespace sas {
 namespace {
 
 constexpr int kPos = 64;                 // positions per workgroup
-constexpr int kWavesSel = 8;             // waves per workgroup
+constexpr int kWavesSel = 16;            // waves per workgroup (128 VGPRs each)
 constexpr int kThreadsSel = 64 * kWavesSel;
 constexpr int kRowWords = kMaxCandBatched + 4;  // LDS row of score keys: 16-byte aligned, staggered banks
 constexpr int kGhatPitch = kGateDim + 4;  // LDS row of the mean gate query (floats)
@@ -72,35 +73,26 @@ __global__ __launch_bounds__(kThreadsSel, 1) void prefill_select_kernel(PrefillS
   if (t < kGateDim) wqn_l[t] = p.w_qnorm[t];
   __syncthreads();
 
-  // ---- 2. gate queries.  Work items (head, group of position tiles): with
-  // fewer heads than waves, each head's 4 tiles of 16 positions are split
-  // over S = 4, 2 or 1 waves (G <= 2, G <= 4, else), so that more waves share
-  // the projections; rounds of kWavesSel / S heads (wave w: head h0 + w %
-  // (kWavesSel / S), tiles of part w / (kWavesSel / S)).
+  // ---- 2. gate queries.  Work item i = (head i / 4, position tile i % 4),
+  // one per wave, in rounds of kWavesSel items (whole heads: kHpr per round)
   const float inv_g = 1.0f / (float)G;
-  const int S = G <= 2 ? 4 : G <= 4 ? 2 : 1;
-  const int ntw = 4 / S;          // position tiles per work item
-  const int hpr = kWavesSel / S;  // heads per round
-  const int hr = wave % hpr, part = wave / hpr;
-  for (int h0 = 0; h0 < G; h0 += hpr) {
-    const int h = h0 + hr;
+  constexpr int kHpr = kWavesSel / 4;  // heads per round
+  for (int i0 = 0; i0 < 4 * G; i0 += kWavesSel) {
+    const int h = (i0 + wave) >> 2, nt = wave & 3;
     const bool active = h < G;
     const int head = kvh * G + (active ? h : 0);
+    const int pos = 16 * nt + j;
     // B operand: lane l holds q[position 16nt + l%16][head][32ks + 8(l/16) .. +7]
-    bf16x8 qB[4][4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int pos = 16 * nt + j;
-      const bool ok = active && nt / ntw == part && pos < nq;
+    bf16x8 qB[4];
+    {
+      const bool ok = active && pos < nq;
       const uint16_t *qrow = p.q + ((int64_t)(t0 + (ok ? pos : 0)) * p.n_q_heads + head) * kHeadDim + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qB[nt][ks] = b8(ok ? ld16(qrow + 32 * ks) : u32x4{0, 0, 0, 0});
+      for (int ks = 0; ks < 4; ++ks) qB[ks] = b8(ok ? ld16(qrow + 32 * ks) : u32x4{0, 0, 0, 0});
     }
-    f32x4 acc[4][8];  // [position tile][row tile]: lane holds rows 16mt + 4g + r of position 16nt + l%16
+    f32x4 acc[8];  // [row tile]: lane holds rows 16mt + 4g + r of position 16nt + l%16
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (active) {
       const uint16_t *wrow = p.w_q + (int64_t)head * kGateDim * kHeadDim + 8 * g;
 #pragma unroll
@@ -109,63 +101,54 @@ __global__ __launch_bounds__(kThreadsSel, 1) void prefill_select_kernel(PrefillS
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) a[ks] = ld16(wrow + (16 * mt + j) * kHeadDim + 32 * ks);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          if (nt / ntw != part) continue;  // uniform: not this item's tile
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-            acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b8(a[ks]), qB[nt][ks], acc[nt][mt], 0, 0, 0);
-        }
+        for (int ks = 0; ks < 4; ++ks)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b8(a[ks]), qB[ks], acc[mt], 0, 0, 0);
       }
       // RMSNorm (the 128 rows of a position sit in the 4 lanes l%16 == const),
       // * w_qnorm, rotate-half RoPE: row i < 64 pairs with row i + 64 (tile mt + 4)
+      float ss = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        if (nt / ntw != part) continue;
-        float ss = 0.f;
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ss = fmaf(acc[mt][r], acc[mt][r], ss);
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      const float inv = 1.0f / sqrtf(ss * (1.0f / kGateDim) + 1e-6f);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * mt + 4 * g + r;
+          const float na = acc[mt][r] * inv * wqn_l[i];
+          const float nb = acc[mt + 4][r] * inv * wqn_l[i + 64];
+          const float c = cosv[pos * 64 + i], s = sinv[pos * 64 + i];
+          acc[mt][r] = na * c - nb * s;
+          acc[mt + 4][r] = nb * c + na * s;
+        }
+    }
+    // add into the mean gate query in head order (the 4 items of one head
+    // cover disjoint positions and add at the same time)
+    for (int hh = 0; hh < kHpr; ++hh) {
+      if (wave >> 2 == hh && active) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ss = fmaf(acc[nt][mt][r], acc[nt][mt][r], ss);
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
-        const float inv = 1.0f / sqrtf(ss * (1.0f / kGateDim) + 1e-6f);
-        const int pos = 16 * nt + j;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 16 * mt + 4 * g + r;
-            const float na = acc[nt][mt][r] * inv * wqn_l[i];
-            const float nb = acc[nt][mt + 4][r] * inv * wqn_l[i + 64];
-            const float c = cosv[pos * 64 + i], s = sinv[pos * 64 + i];
-            acc[nt][mt][r] = na * c - nb * s;
-            acc[nt][mt + 4][r] = nb * c + na * s;
-          }
-      }
-    }
-    // add into the mean gate query in head order (the items of one head
-    // cover disjoint positions and add at the same time)
-    for (int hh = 0; hh < hpr; ++hh) {
-      if (hr == hh && active) {
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          if (nt / ntw != part) continue;
-#pragma unroll
-          for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ghat[(16 * nt + j) * kGhatPitch + 16 * mt + 4 * g + r] += acc[nt][mt][r] * inv_g;
-        }
+          for (int r = 0; r < 4; ++r) ghat[pos * kGhatPitch + 16 * mt + 4 * g + r] += acc[mt][r] * inv_g;
       }
       __syncthreads();
     }
   }
 
-  // ---- 3. scores.  B operands: ghat of position 16nt + l%16, dims 32ks + 8(l/16) .. +7, as bf16 high + low
-  u32x4 bh[4][4], bl[4][4];
+  // ---- 3. scores.  Wave w takes the position tiles 2 half .. 2 half + 1
+  // (half = w / 8) of candidate tiles w % 8, w % 8 + 8, ...  B operands: ghat
+  // of position 16nt + l%16, dims 32ks + 8(l/16) .. +7, as bf16 high + low
+  const int half = wave >> 3;
+  u32x4 bh[2][4], bl[2][4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
+  for (int n2 = 0; n2 < 2; ++n2)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+      const int nt = 2 * half + n2;
       const float *gp = ghat + (16 * nt + j) * kGhatPitch + 32 * ks + 8 * g;
       float hi[8], lo[8];
 #pragma unroll
@@ -174,31 +157,31 @@ __global__ __launch_bounds__(kThreadsSel, 1) void prefill_select_kernel(PrefillS
         hi[e] = __uint_as_float(hb << 16);
         lo[e] = gp[e] - hi[e];
       }
-      bh[nt][ks] = u32x4{pack_bf16_rne(hi[0], hi[1]), pack_bf16_rne(hi[2], hi[3]), pack_bf16_rne(hi[4], hi[5]),
+      bh[n2][ks] = u32x4{pack_bf16_rne(hi[0], hi[1]), pack_bf16_rne(hi[2], hi[3]), pack_bf16_rne(hi[4], hi[5]),
                          pack_bf16_rne(hi[6], hi[7])};
-      bl[nt][ks] = u32x4{pack_bf16_rne(lo[0], lo[1]), pack_bf16_rne(lo[2], lo[3]), pack_bf16_rne(lo[4], lo[5]),
+      bl[n2][ks] = u32x4{pack_bf16_rne(lo[0], lo[1]), pack_bf16_rne(lo[2], lo[3]), pack_bf16_rne(lo[4], lo[5]),
                          pack_bf16_rne(lo[6], lo[7])};
     }
   __syncthreads();  // the tables are consumed: the LDS becomes the score-key rows
   const float inv_sqrt_dg = 0.08838834764831845f;  // 1/sqrt(128)
   const uint16_t *gkh = p.gate_keys + (int64_t)kvh * kGateDim + 8 * g;
   const int64_t page_stride = (int64_t)p.n_kv_heads * kGateDim;
-  for (int ct = wave; 16 * ct < nc; ct += kWavesSel) {
+  for (int ct = wave & 7; 16 * ct < nc; ct += 8) {
     const int c_lane = min(16 * ct + j, nc - 1);  // A operand row: candidate 16ct + l%16
     const uint16_t *krow = gkh + (int64_t)bt_l[c_lane] * page_stride;
     u32x4 a[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) a[ks] = ld16(krow + 32 * ks);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int n2 = 0; n2 < 2; ++n2) {
       f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b8(a[ks]), b8(bh[nt][ks]), sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b8(a[ks]), b8(bl[nt][ks]), sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b8(a[ks]), b8(bh[n2][ks]), sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b8(a[ks]), b8(bl[n2][ks]), sacc, 0, 0, 0);
       }
       // lane: position 16nt + l%16, candidates 16ct + 4(l/16) + r
-      const int pos = 16 * nt + j;
+      const int pos = 16 * (2 * half + n2) + j;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int c = 16 * ct + 4 * g + r;
