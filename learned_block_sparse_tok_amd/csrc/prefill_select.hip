@@ -1,4 +1,4 @@
-// Selection of the training-time forward, batched per 64-position block.
+// Selection of the training-time forward, batched per half of a 64-token block.
 //
 // Every position t of one sequence selects as a decode step of length t+1
 // would: gate query at position t (Qproj, RMSNorm, RoPE, mean over the KV
@@ -6,10 +6,11 @@
 // Top-K, its own block last ("Tencent released Simple-Attention-
 // Sparsification ...", aigc.news: Top-K of 31 historical blocks, gate hidden
 // size 128, Qproj, Q/K normalization, gate RoPE; "Tencent Hunyuan
-// open-sources SAS ...": per-query block selection).  The 64 positions of a
-// block share their candidate set (blocks 0 .. b-1 for block b), so one
-// 1,024-thread workgroup (16 waves) per (64-position block, KV head) does:
-//   1. the RoPE table of its 64 positions (angles reduced in fp64);
+// open-sources SAS ...": per-query block selection).  The positions of a
+// 64-token block share their candidate set (blocks 0 .. b-1 for block b), so
+// one 512-thread workgroup (8 waves of at most 128 VGPRs) per (32 positions
+// of one block, KV head) does:
+//   1. the RoPE table of its 32 positions (angles reduced in fp64);
 //   2. per query head and 16-position tile (one work item per wave),
 //      U^T = W_q[h] . Q^T on v_mfma_f32_16x16x32_bf16 (bf16 products are
 //      exact, sums fp32), RMSNorm, * w_qnorm and RoPE on the accumulator
@@ -17,12 +18,12 @@
 //      (deterministic);
 //   3. the scores S^T = GK . ghat^T / sqrt(128) on MFMA with ghat split into
 //      bf16 high and low parts (about 16 significant bits: the scores keep
-//      fp32-level accuracy), gate keys gathered through the block table; a
-//      wave takes candidate tiles of one half of the positions;
-//   4. one exact Top-K per position (wave_select), sixteen waves in parallel
-//      (the score keys' 132 KiB of LDS leave room for one workgroup per CU,
-//      and the selections are latency-bound: more waves, more in flight).
-// It replaces 64 per-position gate workgroups, each of which re-read W_q and
+//      fp32-level accuracy), gate keys gathered through the block table;
+//   4. one exact Top-K per position (wave_select), eight waves in parallel.
+// Its LDS (the score keys of 32 positions, 66 KiB) leaves room for two
+// workgroups per CU, so one workgroup's latency-bound phases (projection,
+// gathers, radix selects) overlap the other's.
+// It replaces per-position gate workgroups, each of which re-read W_q and
 // the candidates' gate keys.
 #include "sas_device.h"
 #include "sas_kernels.h"
@@ -31,8 +32,9 @@
 namespace sas {
 namespace {
 
-constexpr int kPos = 64;                 // positions per workgroup
-constexpr int kWavesSel = 16;            // waves per workgroup (128 VGPRs each)
+constexpr int kPos = 32;                 // positions per workgroup (half a 64-token block)
+constexpr int kTiles = kPos / 16;        // 16-position MFMA tiles
+constexpr int kWavesSel = 8;             // waves per workgroup (128 VGPRs each: two workgroups per CU)
 constexpr int kThreadsSel = 64 * kWavesSel;
 constexpr int kRowWords = kMaxCandBatched + 4;  // LDS row of score keys: 16-byte aligned, staggered banks
 constexpr int kGhatPitch = kGateDim + 4;  // LDS row of the mean gate query (floats)
@@ -41,24 +43,25 @@ __device__ __forceinline__ bf16x8 b8(u32x4 v) { return __builtin_bit_cast(bf16x8
 
 }  // namespace
 
-__global__ __launch_bounds__(kThreadsSel, 1) void prefill_select_kernel(PrefillSelectParams p) {
+__global__ __launch_bounds__(kThreadsSel, 2) void prefill_select_kernel(PrefillSelectParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t big[kPos * kRowWords];  // phases 1-2 tables, then score keys
   __shared__ __attribute__((aligned(16))) uint32_t hist[kWavesSel][256];
   __shared__ int32_t bt_l[kMaxCandBatched];
   __shared__ float wqn_l[kGateDim];
-  float *cosv = reinterpret_cast<float *>(big);  // [64 positions][64 frequencies]
+  float *cosv = reinterpret_cast<float *>(big);  // [kPos positions][64 frequencies]
   float *sinv = cosv + kPos * 64;
-  float *ghat = sinv + kPos * 64;                 // [64 positions][kGhatPitch]
-  uint32_t *keys = big;                           // [64 positions][kRowWords]
+  float *ghat = sinv + kPos * 64;                 // [kPos positions][kGhatPitch]
+  uint32_t *keys = big;                           // [kPos positions][kRowWords]
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63, g = lane >> 4, j = lane & 15;
   const int kvh = blockIdx.x % p.n_kv_heads;
-  const int qb = p.n_qblocks - 1 - (int)(blockIdx.x / p.n_kv_heads);
-  const int t0 = qb * kPos;
-  const int nq = min(kPos, p.seq_len - t0);
-  const int nc = qb;  // candidates of every position of this block: blocks 0 .. qb-1
+  // heaviest (latest) positions first
+  const int qh = 2 * p.n_qblocks - 1 - (int)(blockIdx.x / p.n_kv_heads);  // half block
+  const int t0 = qh * kPos;
+  const int nq = max(0, min(kPos, p.seq_len - t0));
+  const int nc = qh >> 1;  // candidates of every position here: blocks 0 .. b-1 of its block b
   const int G = p.group;
 
   // ---- 1. RoPE table, block-table row, zeroed mean gate query
@@ -73,12 +76,13 @@ __global__ __launch_bounds__(kThreadsSel, 1) void prefill_select_kernel(PrefillS
   if (t < kGateDim) wqn_l[t] = p.w_qnorm[t];
   __syncthreads();
 
-  // ---- 2. gate queries.  Work item i = (head i / 4, position tile i % 4),
-  // one per wave, in rounds of kWavesSel items (whole heads: kHpr per round)
+  // ---- 2. gate queries.  Work item i = (head i / kTiles, position tile
+  // i % kTiles), one per wave, in rounds of kWavesSel items (whole heads:
+  // kHpr per round)
   const float inv_g = 1.0f / (float)G;
-  constexpr int kHpr = kWavesSel / 4;  // heads per round
-  for (int i0 = 0; i0 < 4 * G; i0 += kWavesSel) {
-    const int h = (i0 + wave) >> 2, nt = wave & 3;
+  constexpr int kHpr = kWavesSel / kTiles;  // heads per round
+  for (int i0 = 0; i0 < kTiles * G; i0 += kWavesSel) {
+    const int h = (i0 + wave) / kTiles, nt = wave % kTiles;
     const bool active = h < G;
     const int head = kvh * G + (active ? h : 0);
     const int pos = 16 * nt + j;
@@ -126,10 +130,10 @@ __global__ __launch_bounds__(kThreadsSel, 1) void prefill_select_kernel(PrefillS
           acc[mt + 4][r] = nb * c + na * s;
         }
     }
-    // add into the mean gate query in head order (the 4 items of one head
+    // add into the mean gate query in head order (the items of one head
     // cover disjoint positions and add at the same time)
     for (int hh = 0; hh < kHpr; ++hh) {
-      if (wave >> 2 == hh && active) {
+      if (wave / kTiles == hh && active) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -139,16 +143,15 @@ __global__ __launch_bounds__(kThreadsSel, 1) void prefill_select_kernel(PrefillS
     }
   }
 
-  // ---- 3. scores.  Wave w takes the position tiles 2 half .. 2 half + 1
-  // (half = w / 8) of candidate tiles w % 8, w % 8 + 8, ...  B operands: ghat
-  // of position 16nt + l%16, dims 32ks + 8(l/16) .. +7, as bf16 high + low
-  const int half = wave >> 3;
-  u32x4 bh[2][4], bl[2][4];
+  // ---- 3. scores.  Wave w takes both position tiles of candidate tiles w,
+  // w + kWavesSel, ...  B operands: ghat of position 16nt + l%16, dims
+  // 32ks + 8(l/16) .. +7, as bf16 high + low
+  u32x4 bh[kTiles][4], bl[kTiles][4];
 #pragma unroll
-  for (int n2 = 0; n2 < 2; ++n2)
+  for (int n2 = 0; n2 < kTiles; ++n2)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int nt = 2 * half + n2;
+      const int nt = n2;
       const float *gp = ghat + (16 * nt + j) * kGhatPitch + 32 * ks + 8 * g;
       float hi[8], lo[8];
 #pragma unroll
@@ -166,14 +169,14 @@ __global__ __launch_bounds__(kThreadsSel, 1) void prefill_select_kernel(PrefillS
   const float inv_sqrt_dg = 0.08838834764831845f;  // 1/sqrt(128)
   const uint16_t *gkh = p.gate_keys + (int64_t)kvh * kGateDim + 8 * g;
   const int64_t page_stride = (int64_t)p.n_kv_heads * kGateDim;
-  for (int ct = wave & 7; 16 * ct < nc; ct += 8) {
+  for (int ct = wave; 16 * ct < nc; ct += kWavesSel) {
     const int c_lane = min(16 * ct + j, nc - 1);  // A operand row: candidate 16ct + l%16
     const uint16_t *krow = gkh + (int64_t)bt_l[c_lane] * page_stride;
     u32x4 a[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) a[ks] = ld16(krow + 32 * ks);
 #pragma unroll
-    for (int n2 = 0; n2 < 2; ++n2) {
+    for (int n2 = 0; n2 < kTiles; ++n2) {
       f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(kThreadsSel, 1) void prefill_select_kernel(PrefillS
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b8(a[ks]), b8(bl[n2][ks]), sacc, 0, 0, 0);
       }
       // lane: position 16nt + l%16, candidates 16ct + 4(l/16) + r
-      const int pos = 16 * (2 * half + n2) + j;
+      const int pos = 16 * n2 + j;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int c = 16 * ct + 4 * g + r;
@@ -210,7 +213,8 @@ __global__ __launch_bounds__(kThreadsSel, 1) void prefill_select_kernel(PrefillS
 }
 
 hipError_t launch_prefill_select(const PrefillSelectParams &p, hipStream_t st) {
-  hipLaunchKernelGGL(prefill_select_kernel, dim3((unsigned)(p.n_qblocks * p.n_kv_heads)), dim3(kThreadsSel), 0, st, p);
+  hipLaunchKernelGGL(prefill_select_kernel, dim3((unsigned)(2 * p.n_qblocks * p.n_kv_heads)), dim3(kThreadsSel), 0, st,
+                     p);
   return hipGetLastError();
 }
 
