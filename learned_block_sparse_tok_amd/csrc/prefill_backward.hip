@@ -219,10 +219,9 @@ __global__ __launch_bounds__(256) void prefill_chain_kernel(PrefillBackwardParam
     const int nh = valid ? nh_l[pp] : 0;
     const uint16_t *gk0 = p.gate_keys + (int64_t)kvh * kGateDim + 16 * o;
     const int64_t gk_page = (int64_t)Hkv * kGateDim;
-    for (int i = 0; i < nh; ++i) {
-      const uint16_t *gk = gk0 + page_l[pp][i] * gk_page;
-      const u32x4 w[4] = {ld16(gk), ld16(gk + 8), ld16(gk + 64), ld16(gk + 72)};
-      const float dsv = ds_l[pp][i];
+    // four selections' keys loaded together (one round trip per four), then
+    // added in slot order
+    auto add_key = [&](const u32x4 (&w)[4], float dsv) {
 #pragma unroll
       for (int k = 0; k < 4; ++k)
 #pragma unroll
@@ -231,6 +230,25 @@ __global__ __launch_bounds__(256) void prefill_chain_kernel(PrefillBackwardParam
           dgh[e] = fmaf(dsv, bf16_lo(w[k][v]), dgh[e]);
           dgh[e + 1] = fmaf(dsv, bf16_hi(w[k][v]), dgh[e + 1]);
         }
+    };
+    int i = 0;
+    for (; i + 4 <= nh; i += 4) {
+      u32x4 w[4][4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint16_t *gk = gk0 + page_l[pp][i + b] * gk_page;
+        w[b][0] = ld16(gk);
+        w[b][1] = ld16(gk + 8);
+        w[b][2] = ld16(gk + 64);
+        w[b][3] = ld16(gk + 72);
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) add_key(w[b], ds_l[pp][i + b]);
+    }
+    for (; i < nh; ++i) {
+      const uint16_t *gk = gk0 + page_l[pp][i] * gk_page;
+      const u32x4 w[4] = {ld16(gk), ld16(gk + 8), ld16(gk + 64), ld16(gk + 72)};
+      add_key(w, ds_l[pp][i]);
     }
   }
 
