@@ -197,23 +197,49 @@ def decode_step_workspace_bytes(shape: SasShape, budget_tokens: int, path="auto"
     return int(lib().sas_decode_step_workspace_bytes(ctypes.byref(shape), int(budget_tokens), STEP_PATH[path]))
 
 
+def _decode_step_args(shape: SasShape, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens, theta,
+                      budget_tokens, sel, gates, cnt, scores, out, workspace, sm_scale, gated, stream=None,
+                      aggregate="mean", gate_mode="scale", path="auto"):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return (ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"), _ptr(w_q, torch.bfloat16, "w_q"),
+            _ptr(w_qnorm, torch.float32, "w_qnorm"), _ptr(gate_keys, torch.bfloat16, "gate_keys"),
+            _ptr(k_pool, torch.bfloat16, "k_pool"), _ptr(v_pool, torch.bfloat16, "v_pool"),
+            _ptr(block_table, torch.int32, "block_table"), _ptr(seq_lens, torch.int32, "seq_lens"),
+            float(theta), int(budget_tokens), AGGREGATE[aggregate], int(bool(gated)),
+            GATE_MODE[gate_mode], float(sm_scale), STEP_PATH[path], _ptr(sel, torch.int32, "sel"),
+            _ptr(gates, torch.float32, "gates"), _ptr(cnt, torch.int32, "cnt"),
+            _ptr(scores, torch.float32, "scores"), _ptr(out, torch.bfloat16, "out"),
+            _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream))
+
+
 def decode_step(shape: SasShape, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens, theta,
                 budget_tokens, sel, gates, cnt, scores, out, workspace, sm_scale, gated, stream=None,
                 aggregate="mean", gate_mode="scale", path="auto"):
     """sas_decode_step: selection then attention in one call (one fused launch
     on the "fused" path); gates / scores / workspace may be None where the
     header allows."""
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().sas_decode_step(ctypes.byref(shape), _ptr(q, torch.bfloat16, "q"), _ptr(w_q, torch.bfloat16, "w_q"),
-                               _ptr(w_qnorm, torch.float32, "w_qnorm"), _ptr(gate_keys, torch.bfloat16, "gate_keys"),
-                               _ptr(k_pool, torch.bfloat16, "k_pool"), _ptr(v_pool, torch.bfloat16, "v_pool"),
-                               _ptr(block_table, torch.int32, "block_table"), _ptr(seq_lens, torch.int32, "seq_lens"),
-                               float(theta), int(budget_tokens), AGGREGATE[aggregate], int(bool(gated)),
-                               GATE_MODE[gate_mode], float(sm_scale), STEP_PATH[path], _ptr(sel, torch.int32, "sel"),
-                               _ptr(gates, torch.float32, "gates"), _ptr(cnt, torch.int32, "cnt"),
-                               _ptr(scores, torch.float32, "scores"), _ptr(out, torch.bfloat16, "out"),
-                               _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream))
-    _check(st, "sas_decode_step")
+    args = _decode_step_args(shape, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens, theta,
+                             budget_tokens, sel, gates, cnt, scores, out, workspace, sm_scale, gated, stream,
+                             aggregate, gate_mode, path)
+    _check(lib().sas_decode_step(*args), "sas_decode_step")
+
+
+class PreparedCall:
+    """One C-ABI call whose arguments were checked and marshalled once: each
+    call() passes the same pointers and sizes again, as a serving loop that
+    keeps its buffers does, on the given stream or, if none was given, on the
+    stream current at the call (so that the call can be captured into a graph).
+    It keeps the tensors it points to alive."""
+
+    def __init__(self, fn, name, args, keep, stream=None):
+        self._fn, self._name, self._keep = fn, name, keep
+        self._args = args[:-1]
+        self._stream = None if stream is None else args[-1]
+
+    def __call__(self):
+        st = self._fn(*self._args, self._stream if self._stream is not None else _stream(None))
+        if st != SAS_OK:
+            _check(st, self._name)
 
 
 NOALLOC_SCRATCH_BYTES = 16 << 20  # SAS_NOALLOC_SCRATCH_BYTES
@@ -281,6 +307,17 @@ class SparseDecoder:
                     self.budget, self.sel, self.gates, self.cnt, self.scores, self.out, self.ws_step, self.sm_scale,
                     self.gated, stream, aggregate=self.aggregate, gate_mode=self.gate_mode, path=self.path)
         return self.out
+
+    def prepare_step(self, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens, stream=None):
+        """step() with its arguments checked and marshalled once: the returned
+        call launches sas_decode_step on these tensors (and the stream current
+        now) each time it is called."""
+        keep = (q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens)
+        args = _decode_step_args(self.shape, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens,
+                                 self.theta, self.budget, self.sel, self.gates, self.cnt, self.scores, self.out,
+                                 self.ws_step, self.sm_scale, self.gated, stream, aggregate=self.aggregate,
+                                 gate_mode=self.gate_mode, path=self.path)
+        return PreparedCall(lib().sas_decode_step, "sas_decode_step", args, keep, stream)
 
 
 def prefill_select(shape: SasShape, q, w_q, w_qnorm, gate_keys, block_table_row, seq_len, theta, budget_tokens,

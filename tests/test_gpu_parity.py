@@ -567,3 +567,36 @@ def test_graph_replay_matches_eager(path):
             torch.cuda.synchronize()
             for a, b in zip(ref, (dec.sel, dec.gates, dec.cnt, dec.out, dec.scores)):
                 assert torch.equal(a, b), f"replay {r}"
+
+
+@pytest.mark.parametrize("path", ["auto", "two_launches"])
+def test_prepared_step_matches_step(path):
+    # the step with its arguments marshalled once (as bench.py times it):
+    # the same outputs as step(), eagerly and captured into a graph
+    w = wl.make(4, 32, 8, [8192, 5000, 3000, 8192], 2048, "paged", 83, DEV, max_blocks=128)
+    gk = gpu_pool(w)
+    dec = ops.SparseDecoder(w.batch, w.n_q_heads, w.n_kv_heads, w.max_blocks, w.strides, 2048, w.theta, True,
+                            device=DEV, path=path)
+    args = (w.q, w.w_q, w.w_qnorm, gk, w.k_pool, w.v_pool, w.block_table, w.seq_lens)
+    dec.step(*args)
+    torch.cuda.synchronize()
+    outs = (dec.sel, dec.gates, dec.cnt, dec.out, dec.scores)
+    ref = [t.clone() for t in outs]
+    call = dec.prepare_step(*args)
+    for t in outs:
+        t.zero_()
+    call()
+    torch.cuda.synchronize()
+    for a, b in zip(ref, outs):
+        assert torch.equal(a, b)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for r in range(3):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, outs):
+            assert torch.equal(a, b), f"replay {r}"
