@@ -312,7 +312,7 @@ class SparseDecoder:
         """step() with its arguments checked and marshalled once: the returned
         call launches sas_decode_step on these tensors (and the stream current
         now) each time it is called."""
-        keep = (q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens)
+        keep = (self, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens)  # outputs live in self
         args = _decode_step_args(self.shape, q, w_q, w_qnorm, gate_keys, k_pool, v_pool, block_table, seq_lens,
                                  self.theta, self.budget, self.sel, self.gates, self.cnt, self.scores, self.out,
                                  self.ws_step, self.sm_scale, self.gated, stream, aggregate=self.aggregate,
