@@ -66,3 +66,18 @@ def test_prefill_issued_flops_when_every_query_selects_the_same_blocks():
     waves = T // (16 // 4)
     mfma = 16 * 16 * 32 * 2  # flops of one 16x16x32 MFMA
     assert bench.prefill_executed_flops(sel, cnt, group) == float(waves * 3 * 32 * mfma)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the path runs on one GPU: --gpus 2 (or a WORLD_SIZE above 1) exits with
+    # a message and status 2 before touching any device
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for args, env in [(["--gpus", "2"], {}), ([], {"WORLD_SIZE": "2", "RANK": "0"})]:
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *args], capture_output=True, text=True,
+                           env={**os.environ, **env}, timeout=120)
+        assert r.returncode == 2
+        assert "one GPU only" in r.stderr
+        assert r.stdout == ""
